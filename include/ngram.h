@@ -1,0 +1,195 @@
+/*
+ * ngram.h -- C ABI of the hashed bigram + trigram embedding table with sparse
+ * row-wise updates, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (modded-nanogpt README, technique list: a hashed bigram +
+ * trigram embedding table of 84.6M rows with a sign trick, and sparse
+ * row-wise embedding updates with beta1 = 0, one second moment per row,
+ * every 4 steps; the @classiclarryd post quoted on the airebao.com item about
+ * the 39.9 s record: only rows seen in the batch get an optimizer step, beta2
+ * is applied retroactively when a row is next used, one optimizer float per
+ * 768 parameters; agentic-affairs "NanoGPT Training Record", ablation section:
+ * 84.6M rows across a bigram and a trigram channel; amund.blog "My 2nd
+ * modded-nanogpt world record attempt", The four improvements, item 4: the
+ * accumulated n-gram gradients can be added as each step produces them or in
+ * one burst every fourth step, with the same result):
+ *
+ *   per position i of a micro-step, with n-gram context reset at each EoS,
+ *     r_b, s_b = hash_b(t[i-1], t[i]);  r_t, s_t = hash_t(t[i-2], t[i-1], t[i])
+ *     out[i]   = s_b W_b[r_b] + s_t W_t[r_t]
+ *   per accumulation window (accum_steps micro-steps), per touched row r:
+ *     G[r]     = sum of s dY[i] over the window's positions hashed to r
+ *   sparse step t (t = 1, 2, ... counts optimizer steps), per touched row:
+ *     v[r]     = beta2^(t - t_last[r]) v[r] + (1 - beta2) mean(G[r]^2)
+ *     W[r]    -= lr G[r] / (sqrt(v[r]) + eps);   t_last[r] = t
+ *
+ * Readings of what the pages leave open (the CPU oracle shares them):
+ *   hash      SplitMix64 finaliser of (key ^ seed) + 0x9E3779B97F4A7C15; row =
+ *             ((z >> 32) * R) >> 32 (Lemire); sign negative iff z & 1.
+ *   keys      bigram p1*(V+1) + t, trigram (p2*(V+1) + p1)*(V+1) + t in 64-bit
+ *             unsigned arithmetic, V = vocab, a missing token written as V.
+ *   context   p1 = t[i-1] unless i == 0 or t[i] is EoS; p2 = t[i-2] unless
+ *             i < 2 or t[i] or t[i-1] is EoS.  Every micro-step starts afresh.
+ *   forward   one fp32 addition of the two signed rows, then one rounding to
+ *             the table dtype (bf16: nearest, ties to even; NaN -> 0x7FC0).
+ *   update    no bias correction (fold it into lr and eps), eps outside the
+ *             root, no weight decay, gradients summed (not averaged) over the
+ *             window.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device pointers unless marked "host".  The caller owns
+ *     every buffer; the library never allocates, frees or synchronises in the
+ *     hot calls (ngram_hash, ngram_embed_fwd, ngram_embed_bwd_accum,
+ *     ngram_window_reduce, ngram_sparse_step, ngram_window_export).  Those
+ *     calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return; they are safe to capture in a HIP graph.
+ *   - A negative return value is a host-detected error and nothing was
+ *     enqueued.  NGRAM_EHIP reports a failed launch.
+ *   - Faults only the device can see (token ids outside [0, vocab), more
+ *     distinct rows than the window holds, step numbers that do not increase)
+ *     set sticky bits in the workspace, read with ngram_device_status.
+ *   - Tables and row-major activations are [rows][dim] with dim = 768; all
+ *     row bases must be 16-byte aligned.  Row counts must be below 2^31.
+ *   - One workspace serves one table pair and one stream at a time; distinct
+ *     workspaces are independent (the library keeps no global state).
+ */
+#ifndef NGRAM_H
+#define NGRAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NGRAM_ABI_VERSION 1
+
+/* dtypes of the tables (and of the forward output) */
+#define NGRAM_DTYPE_F32 0
+#define NGRAM_DTYPE_BF16 1
+
+/* how micro-step gradients enter the window (amund.blog, The four
+ * improvements, item 4) */
+#define NGRAM_MODE_SPREAD 0 /* reduce each micro-step into the window now */
+#define NGRAM_MODE_BURST 1  /* keep micro-steps; reduce all at step time  */
+
+/* status codes */
+#define NGRAM_OK 0
+#define NGRAM_ENULL -1    /* a required pointer is NULL                     */
+#define NGRAM_EALIGN -2   /* a pointer is not aligned as documented         */
+#define NGRAM_ECONFIG -3  /* the config is invalid (see ngram_config_check) */
+#define NGRAM_ESIZE -4    /* a size is out of range                         */
+#define NGRAM_EARG -5     /* a scalar argument is out of range              */
+#define NGRAM_EHIP -6     /* the HIP runtime reported an error              */
+
+/* sticky device flags */
+#define NGRAM_FLAG_BAD_TOKEN 0x1u   /* a token id outside [0, vocab)          */
+#define NGRAM_FLAG_WINDOW_FULL 0x2u /* more distinct rows than window_rows;
+                                       the excess rows were dropped          */
+#define NGRAM_FLAG_STASH_FULL 0x4u  /* burst mode: more than accum_steps *
+                                       max_tokens positions before a step;
+                                       the excess micro-step was dropped     */
+#define NGRAM_FLAG_STEP_ORDER 0x8u  /* sparse step t <= t_last of a touched
+                                       row; that row decays by beta2^0       */
+
+typedef struct ngram_config {
+    int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the
+                            speedrun (agentic-affairs, benchmark definition) */
+    int32_t eos_id;      /* the EoS id that opens each document             */
+    int32_t dim;         /* row width; must be 768                          */
+    int32_t dtype;       /* NGRAM_DTYPE_F32 or NGRAM_DTYPE_BF16             */
+    int64_t rows[2];     /* rows of the bigram [0] and trigram [1] tables,
+                            each in [1, 2^31)                               */
+    uint64_t seed[2];    /* hash seeds of the two channels                  */
+    int64_t max_tokens;  /* largest T of one micro-step, in [1, 2^28]       */
+    int32_t accum_steps; /* micro-steps per window, in [1, 64]              */
+    int32_t mode;        /* NGRAM_MODE_SPREAD or NGRAM_MODE_BURST           */
+    int64_t window_rows; /* distinct rows one window can hold per channel;
+                            0 = min(max(rows[0], rows[1]),
+                                    accum_steps * max_tokens)              */
+} ngram_config;
+
+/* Version of this ABI (NGRAM_ABI_VERSION). */
+int ngram_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *ngram_status_string(int status);
+
+/* Validates a config on the host.  Returns NGRAM_OK or NGRAM_ECONFIG. */
+int ngram_config_check(const ngram_config *cfg);
+
+/* Bytes of device workspace the config needs (host output `bytes`).  The
+ * workspace holds the window accumulator (window_rows x 768 fp32 per
+ * channel), a row->slot map (4 B per table row), sort buffers, and in burst
+ * mode a copy of the window's upstream gradients. */
+int ngram_workspace_bytes(const ngram_config *cfg, uint64_t *bytes);
+
+/* Prepares a workspace of `ws_bytes` bytes (256-byte aligned) on `stream`:
+ * empty window, no flags.  Must be called once before any other use of `ws`
+ * and may be called again to discard a window. */
+int ngram_workspace_init(const ngram_config *cfg, void *ws, uint64_t ws_bytes,
+                         void *stream);
+
+/* Context + hash of one micro-step (modded-nanogpt README, technique list:
+ * hashed bigram + trigram table with sign trick; EoS-aligned batches).
+ * tokens: int32 [T], 4-byte aligned.  idx: uint32 [2][T] (bigram row block,
+ * then trigram), each entry row | (negative << 31).  ws may be NULL; if not,
+ * bad token ids set NGRAM_FLAG_BAD_TOKEN there.  0 <= T <= max_tokens. */
+int ngram_hash(const ngram_config *cfg, const int32_t *tokens, int64_t T,
+               uint32_t *idx, void *ws, void *stream);
+
+/* Forward of one micro-step: out[i] = s_b W_b[r_b(i)] + s_t W_t[r_t(i)]
+ * (same passages as ngram_hash).  W_b, W_t: [rows[c]][768] of cfg->dtype.
+ * out: [T][768] of cfg->dtype; must not overlap the tables.  ws may be NULL
+ * (bad token ids then go unreported; their rows are still valid rows). */
+int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t,
+                    const int32_t *tokens, int64_t T, void *out, void *ws,
+                    void *stream);
+
+/* Backward of one micro-step into the window accumulator (gradients are
+ * accumulated over accum_steps micro-steps and applied once: the
+ * @classiclarryd post; README technique list).  dY: fp32 [T][768], the
+ * gradient of `out` for the same tokens.  Spread mode reduces now (dY may be
+ * reused once the stream passes this call); burst mode copies tokens' rows
+ * and dY into the workspace and reduces at ngram_window_reduce /
+ * ngram_sparse_step. */
+int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws,
+                          const int32_t *tokens, const float *dY, int64_t T,
+                          void *stream);
+
+/* Burst mode: reduce every micro-step kept since the last step into the
+ * window accumulator now (ngram_sparse_step does this itself).  Spread mode:
+ * nothing to do.  Calling it twice is harmless. */
+int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream);
+
+/* Sparse step number t >= 1 on every row the window touched, then empties the
+ * window (the @classiclarryd post: optimizer step only for n-gram rows that
+ * occurred, beta1 = 0, beta2 applied retroactively, one float per 768
+ * parameters).  W_b, W_t: tables of cfg->dtype, updated in place.  v_b, v_t:
+ * fp32 [rows[c]] second moments (start at 0).  t_last_b, t_last_t: int32
+ * [rows[c]] step of each row's last update (start at 0).  Requires
+ * 0 <= beta2 < 1, eps > 0 and finite, lr finite. */
+int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t,
+                      float *v_b, float *v_t, int32_t *t_last_b,
+                      int32_t *t_last_t, int32_t t, float lr, float beta2,
+                      float eps, void *stream);
+
+/* Copies the current window of one channel (0 bigram, 1 trigram) to caller
+ * buffers: the first min(n, max_rows) rows (uint32, first-touch order:
+ * ascending within each reduced micro-step), their gradients G (fp32
+ * [max_rows][768], 16-byte aligned; may be NULL), and n itself (uint32,
+ * device).  In burst mode call ngram_window_reduce first. */
+int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
+                        uint32_t *rows, float *G, int64_t max_rows,
+                        uint32_t *count, void *stream);
+
+/* Synchronises `stream` and writes the sticky device flags to the host word
+ * `flags`; clears them if `clear` is nonzero.  Not for use under capture. */
+int ngram_device_status(const ngram_config *cfg, const void *ws,
+                        uint32_t *flags, int clear, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGRAM_H */

@@ -1,0 +1,329 @@
+// C ABI of libngram: argument checks, workspace layout, launches.
+//
+// Host code only.  Every entry point validates its arguments before touching
+// the HIP runtime, so a rejected call enqueues nothing.  The hot calls never
+// allocate, free or synchronise: device-side counts (distinct rows, kept
+// positions) stay in the workspace header and kernels read them, with grids
+// sized from host-known bounds.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/ngram.h"
+#include "ngram_dev.hpp"
+
+using namespace ngram;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_cfg(const ngram_config *c)
+{
+    if (!c)
+        return NGRAM_ENULL;
+    if (c->vocab < 1 || c->vocab > (1 << 30))
+        return NGRAM_ECONFIG;
+    if (c->eos_id < 0 || c->eos_id >= c->vocab)
+        return NGRAM_ECONFIG;
+    if (c->dim != kDim)
+        return NGRAM_ECONFIG;
+    if (c->dtype != NGRAM_DTYPE_F32 && c->dtype != NGRAM_DTYPE_BF16)
+        return NGRAM_ECONFIG;
+    for (int k = 0; k < 2; ++k)
+        if (c->rows[k] < 1 || c->rows[k] > INT32_MAX)
+            return NGRAM_ECONFIG;
+    if (c->max_tokens < 1 || c->max_tokens > (int64_t(1) << 28))
+        return NGRAM_ECONFIG;
+    if (c->accum_steps < 1 || c->accum_steps > 64)
+        return NGRAM_ECONFIG;
+    if (c->mode != NGRAM_MODE_SPREAD && c->mode != NGRAM_MODE_BURST)
+        return NGRAM_ECONFIG;
+    if (c->mode == NGRAM_MODE_BURST && (int64_t)c->accum_steps * c->max_tokens > (int64_t(1) << 30))
+        return NGRAM_ECONFIG;
+    if (c->window_rows < 0 || c->window_rows > INT32_MAX)
+        return NGRAM_ECONFIG;
+    return NGRAM_OK;
+}
+
+WsLayout layout(const ngram_config *c)
+{
+    WsLayout L;
+    memset(&L, 0, sizeof(L));
+    L.burst = c->mode == NGRAM_MODE_BURST;
+    L.rows[0] = c->rows[0];
+    L.rows[1] = c->rows[1];
+    const int64_t window_keys = (int64_t)c->accum_steps * c->max_tokens;
+    const int64_t rmax = c->rows[0] > c->rows[1] ? c->rows[0] : c->rows[1];
+    L.wrows = c->window_rows > 0 ? c->window_rows : (window_keys < rmax ? window_keys : rmax);
+    L.nk = L.burst ? window_keys : c->max_tokens;
+    L.nblk = (L.nk + kSortTile - 1) / kSortTile;
+    L.nchunk = (L.nk + kChunk - 1) / kChunk;
+    int bits = 0;
+    while (bits < 31 && ((int64_t(1) << bits) < rmax))
+        ++bits;
+    L.passes = bits == 0 ? 1 : (bits + kRadixBits - 1) / kRadixBits;
+
+    uint64_t o = 0;
+    L.hdr = o;
+    o = up(o + sizeof(WsHeader));
+    for (int k = 0; k < 2; ++k) {
+        L.slot_map[k] = o;
+        o = up(o + 4ull * (uint64_t)c->rows[k]);
+    }
+    for (int k = 0; k < 2; ++k) {
+        L.slot_rows[k] = o;
+        o = up(o + 4ull * (uint64_t)L.wrows);
+    }
+    L.gacc = o;
+    o = up(o + 4ull * 2 * (uint64_t)L.wrows * kDim);
+    for (int k = 0; k < 2; ++k) {
+        L.keys[k] = o;
+        o = up(o + 4ull * 2 * (uint64_t)L.nk);
+        L.vals[k] = o;
+        o = up(o + 4ull * 2 * (uint64_t)L.nk);
+    }
+    L.seg_info = o;
+    o = up(o + 4ull * 2 * (uint64_t)L.nk);
+    L.hist = o;
+    o = up(o + 4ull * 2 * kRadix * (uint64_t)L.nblk);
+    L.blk = o;
+    o = up(o + 4ull * 2 * (uint64_t)L.nblk);
+    L.partial = o;
+    o = up(o + 4ull * 2 * (uint64_t)L.nchunk * 2 * kDim);
+    L.owners = o;
+    o = up(o + 8ull * 2 * (uint64_t)L.nchunk);
+    if (L.burst) {
+        L.stash_idx = o;
+        o = up(o + 4ull * 2 * (uint64_t)L.nk);
+        L.stash_dy = o;
+        o = up(o + 4ull * (uint64_t)L.nk * kDim);
+    }
+    L.total = o;
+    return L;
+}
+
+HashParams hash_params(const ngram_config *c)
+{
+    HashParams hp;
+    hp.vocab = (uint32_t)c->vocab;
+    hp.eos = c->eos_id;
+    hp.rows[0] = (uint32_t)c->rows[0];
+    hp.rows[1] = (uint32_t)c->rows[1];
+    hp.seed[0] = c->seed[0];
+    hp.seed[1] = c->seed[1];
+    return hp;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NGRAM_OK : NGRAM_EHIP; }
+
+int check_tokens(const ngram_config *c, const int32_t *tok, int64_t T)
+{
+    if (T < 0 || T > c->max_tokens)
+        return NGRAM_ESIZE;
+    if (T > 0 && !tok)
+        return NGRAM_ENULL;
+    if (!aligned(tok, 4))
+        return NGRAM_EALIGN;
+    return NGRAM_OK;
+}
+
+uint32_t *flags_of(void *ws) { return ws ? &reinterpret_cast<WsHeader *>(ws)->flags : nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+int ngram_abi_version(void) { return NGRAM_ABI_VERSION; }
+
+const char *ngram_status_string(int s)
+{
+    switch (s) {
+    case NGRAM_OK: return "ok";
+    case NGRAM_ENULL: return "a required pointer is NULL";
+    case NGRAM_EALIGN: return "a pointer is not aligned as required";
+    case NGRAM_ECONFIG: return "invalid ngram_config";
+    case NGRAM_ESIZE: return "a size is out of range";
+    case NGRAM_EARG: return "a scalar argument is out of range";
+    case NGRAM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int ngram_config_check(const ngram_config *cfg) { return check_cfg(cfg); }
+
+int ngram_workspace_bytes(const ngram_config *cfg, uint64_t *bytes)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!bytes)
+        return NGRAM_ENULL;
+    *bytes = layout(cfg).total;
+    return NGRAM_OK;
+}
+
+int ngram_workspace_init(const ngram_config *cfg, void *ws, uint64_t ws_bytes, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    if (ws_bytes < L.total)
+        return NGRAM_ESIZE;
+    return hip_status(launch_init(L, (uint8_t *)ws, (hipStream_t)stream));
+}
+
+int ngram_hash(const ngram_config *cfg, const int32_t *tokens, int64_t T, uint32_t *idx, void *ws,
+               void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_tokens(cfg, tokens, T)))
+        return rc;
+    if (T > 0 && !idx)
+        return NGRAM_ENULL;
+    if (!aligned(idx, 4) || !aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    return hip_status(launch_hash(hash_params(cfg), tokens, T, idx, flags_of(ws), (hipStream_t)stream));
+}
+
+int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t, const int32_t *tokens,
+                    int64_t T, void *out, void *ws, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_tokens(cfg, tokens, T)))
+        return rc;
+    if (!W_b || !W_t || (T > 0 && !out))
+        return NGRAM_ENULL;
+    if (!aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(out, 16) || !aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    return hip_status(launch_fwd(cfg->dtype, hash_params(cfg), W_b, W_t, tokens, T, out, flags_of(ws),
+                                 (hipStream_t)stream));
+}
+
+int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws, const int32_t *tokens, const float *dY,
+                          int64_t T, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_tokens(cfg, tokens, T)))
+        return rc;
+    if (!ws || (T > 0 && !dY))
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign) || !aligned(dY, 16))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    uint8_t *w = (uint8_t *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    const HashParams hp = hash_params(cfg);
+    if (L.burst)
+        return hip_status(launch_stash(L, w, hp, tokens, dY, T, s));
+    if (T == 0)
+        return NGRAM_OK;
+    hipError_t e = launch_keys_from_tokens(L, w, hp, tokens, T, s);
+    if (e == hipSuccess)
+        e = launch_reduce(L, w, nullptr, (uint32_t)T, dY, s);
+    return hip_status(e);
+}
+
+int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    if (!L.burst)
+        return NGRAM_OK;
+    uint8_t *w = (uint8_t *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t *n_dev = &reinterpret_cast<const WsHeader *>(w + L.hdr)->n_stash;
+    hipError_t e = launch_keys_from_stash(L, w, s);
+    if (e == hipSuccess)
+        e = launch_reduce(L, w, n_dev, (uint32_t)L.nk, reinterpret_cast<const float *>(w + L.stash_dy), s);
+    if (e == hipSuccess)
+        e = launch_stash_clear(L, w, s);
+    return hip_status(e);
+}
+
+int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, float *v_b, float *v_t,
+                      int32_t *t_last_b, int32_t *t_last_t, int32_t t, float lr, float beta2, float eps,
+                      void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !W_b || !W_t || !v_b || !v_t || !t_last_b || !t_last_t)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(v_b, 4) ||
+        !aligned(v_t, 4) || !aligned(t_last_b, 4) || !aligned(t_last_t, 4))
+        return NGRAM_EALIGN;
+    if (t < 1 || !isfinite(lr) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !isfinite(eps))
+        return NGRAM_EARG;
+    if ((rc = ngram_window_reduce(cfg, ws, stream)))
+        return rc;
+    const WsLayout L = layout(cfg);
+    return hip_status(launch_step(L, (uint8_t *)ws, cfg->dtype, W_b, W_t, v_b, v_t, t_last_b, t_last_t, t,
+                                  lr, beta2, eps, (hipStream_t)stream));
+}
+
+int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, uint32_t *rows, float *G,
+                        int64_t max_rows, uint32_t *count, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !rows || !count)
+        return NGRAM_ENULL;
+    if (channel != 0 && channel != 1)
+        return NGRAM_EARG;
+    if (max_rows < 0 || max_rows > INT32_MAX)
+        return NGRAM_ESIZE;
+    if (!aligned(ws, kAlign) || !aligned(rows, 4) || !aligned(G, 16) || !aligned(count, 4))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    return hip_status(launch_export(L, (const uint8_t *)ws, channel, rows, G, (uint32_t)max_rows, count,
+                                    (hipStream_t)stream));
+}
+
+int ngram_device_status(const ngram_config *cfg, const void *ws, uint32_t *flags, int clear, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !flags)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    hipStream_t s = (hipStream_t)stream;
+    const WsHeader *hdr = reinterpret_cast<const WsHeader *>((const uint8_t *)ws + L.hdr);
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return NGRAM_EHIP;
+    if (hipMemcpy(flags, &hdr->flags, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return NGRAM_EHIP;
+    if (clear) {
+        if (launch_flags_clear((uint8_t *)ws, L, s) != hipSuccess)
+            return NGRAM_EHIP;
+        if (hipStreamSynchronize(s) != hipSuccess)
+            return NGRAM_EHIP;
+    }
+    return NGRAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,178 @@
+// Device helpers, workspace layout and kernel launchers of libngram (gfx950).
+//
+// Everything here is HIP for CDNA4 only: 64-lane wavefronts, 16-byte row
+// accesses, LDS tiles.  No host code of the C ABI lives here; ngram_abi.hip
+// validates arguments and calls the launchers declared at the bottom.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ngram {
+
+constexpr int kDim = 768;
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- hashing
+//
+// Hashed bigram/trigram rows with a +/-1 sign (modded-nanogpt README,
+// technique list).  The pages give no hash; this is the SplitMix64 finaliser
+// (Steele, Lea & Flood 2014, Stafford's Mix13 multipliers) of (key ^ seed)
+// advanced by the golden gamma, reduced to [0, R) by Lemire's multiply-shift
+// of the upper 32 bits, with the sign in bit 0.
+
+struct HashParams {
+    uint32_t vocab;   // V; V itself encodes "no token"
+    int32_t eos;
+    uint32_t rows[2];
+    uint64_t seed[2];
+};
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Packed index: row | (negative << 31).
+__device__ __forceinline__ uint32_t hash_pack(uint64_t key, uint64_t seed, uint32_t R)
+{
+    const uint64_t z = mix64((key ^ seed) + 0x9E3779B97F4A7C15ull);
+    const uint32_t hi = (uint32_t)(z >> 32);
+    const uint32_t row = (uint32_t)(((uint64_t)hi * (uint64_t)R) >> 32);
+    return row | ((uint32_t)z << 31);
+}
+
+// Context of position i (micro-step local) and both channels' packed
+// indices.  The EoS opens its document: no n-gram reaches back across it, and
+// the micro-step start has no context.  Returns true if t[i] is not a valid id.
+__device__ __forceinline__ bool ngram_index(const int32_t *__restrict__ tok, int64_t i,
+                                            const HashParams &hp, uint32_t &ib, uint32_t &it)
+{
+    const int32_t t0 = tok[i];
+    const int32_t t1 = i >= 1 ? tok[i - 1] : 0;
+    const int32_t t2 = i >= 2 ? tok[i - 2] : 0;
+    const uint64_t none = hp.vocab;
+    const bool opens = (t0 == hp.eos);
+    const uint64_t p1 = (i >= 1 && !opens) ? (uint64_t)(uint32_t)t1 : none;
+    const uint64_t p2 = (i >= 2 && !opens && t1 != hp.eos) ? (uint64_t)(uint32_t)t2 : none;
+    const uint64_t B = none + 1;
+    const uint64_t tt = (uint64_t)(uint32_t)t0;
+    const uint64_t kb = p1 * B + tt;
+    const uint64_t kt = (p2 * B + p1) * B + tt;
+    ib = hash_pack(kb, hp.seed[0], hp.rows[0]);
+    it = hash_pack(kt, hp.seed[1], hp.rows[1]);
+    return (uint32_t)t0 >= hp.vocab;
+}
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi)
+{
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// ------------------------------------------------------------ workspace
+//
+// One device allocation, carved by the host (WsLayout).  All mutable state
+// of a window lives here so the hot calls never need a host round trip.
+
+struct WsHeader {
+    uint32_t magic;
+    uint32_t flags;        // NGRAM_FLAG_* (sticky)
+    uint32_t n_slots[2];   // distinct rows in the window, per channel
+    uint32_t n_prev[2];    // n_slots before the micro-step being reduced
+    uint32_t n_owner[2];   // long-segment fix-up records of the current reduce
+    uint32_t n_stash;      // burst mode: positions kept since the last reduce
+    uint32_t pad[55];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+constexpr uint32_t kMagic = 0x6E677231u;
+
+// Sort tiles: 256 threads x 8 keys.
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 8;
+constexpr int kSortTile = kSortThreads * kSortItems;
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+
+// Segment-reduce chunks: one wavefront per 64 sorted keys.
+constexpr int kChunk = 64;
+
+struct WsLayout {
+    uint64_t hdr;
+    uint64_t slot_map[2];   // int32 [rows[c]]: slot of a row in the window, -1 if none
+    uint64_t slot_rows[2];  // uint32 [wrows]: row of each slot
+    uint64_t gacc;          // fp32 [2][wrows][768]: window gradient
+    uint64_t keys[2];       // uint32 [2][nk]: sort key buffers A/B (row)
+    uint64_t vals[2];       // uint32 [2][nk]: sort payload A/B (position | neg << 31)
+    uint64_t seg_info;      // uint32 [2][nk]: slot | new << 31 at segment heads
+    uint64_t hist;          // uint32 [2][256][nblk]
+    uint64_t blk;           // uint32 [2][nblk]
+    uint64_t partial;       // fp32 [2][nchunk][2][768]
+    uint64_t owners;        // uint64 [2][nchunk]
+    uint64_t stash_idx;     // uint32 [2][nk] (burst)
+    uint64_t stash_dy;      // fp32 [nk][768] (burst)
+    uint64_t total;
+
+    int64_t rows[2];
+    int64_t wrows;          // window capacity per channel
+    int64_t nk;             // keys per channel one reduce can hold
+    int64_t nblk;           // sort tiles for nk keys
+    int64_t nchunk;         // 64-key chunks for nk keys
+    int passes;             // radix passes (8 bits each)
+    bool burst;
+};
+
+// ---------------------------------------------------------------- launchers
+// Implemented in the .hip files of this directory; all enqueue on `s`.
+
+hipError_t launch_init(const WsLayout &L, uint8_t *ws, hipStream_t s);
+hipError_t launch_hash(const HashParams &hp, const int32_t *tok, int64_t T, uint32_t *idx,
+                       uint32_t *flags, hipStream_t s);
+hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const void *wt,
+                      const int32_t *tok, int64_t T, void *out, uint32_t *flags, hipStream_t s);
+
+// Spread: keys of one micro-step straight from the tokens.
+hipError_t launch_keys_from_tokens(const WsLayout &L, uint8_t *ws, const HashParams &hp,
+                                   const int32_t *tok, int64_t T, hipStream_t s);
+// Burst: keep one micro-step (packed indices + dY rows) in the stash.
+hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp,
+                        const int32_t *tok, const float *dY, int64_t T, hipStream_t s);
+// Burst: keys of every kept position.
+hipError_t launch_keys_from_stash(const WsLayout &L, uint8_t *ws, hipStream_t s);
+
+// Sort the keys of both channels by row, find segments, assign window slots,
+// reduce signed dY rows into the window.  n_dev (device count) may be null;
+// n_host bounds it.
+hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host,
+                         const float *dY, hipStream_t s);
+
+// Burst: mark the stash empty after a reduce.
+hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);
+
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, float *vb,
+                       float *vt, int32_t *tlb, int32_t *tlt, int32_t t, float lr, float beta2,
+                       float eps, hipStream_t s);
+
+hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s);
+
+hipError_t launch_export(const WsLayout &L, const uint8_t *ws, int channel, uint32_t *rows,
+                         float *G, uint32_t max_rows, uint32_t *count, hipStream_t s);
+
+}  // namespace ngram

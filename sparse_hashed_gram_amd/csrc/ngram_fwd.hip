@@ -1,0 +1,293 @@
+// Hash, forward gather-sum, and the backward's key build (gfx950).
+//
+// Forward (modded-nanogpt README, technique list: hashed bigram + trigram
+// table with sign trick): out[i] = s_b W_b[r_b(i)] + s_t W_t[r_t(i)].
+// A 768-wide row is 96 (bf16) or 192 (fp32) 16-byte chunks.  A block owns 64
+// consecutive positions: 64 threads hash them into LDS, then all 256 threads
+// sweep the 64 x chunks grid so that consecutive lanes read consecutive
+// 16-byte pieces of a row (coalesced 1.5 KB / 3 KB row reads) and write the
+// output rows contiguously.  Each thread keeps several chunks' loads in
+// flight before it consumes any of them.
+#include "ngram_dev.hpp"
+
+#include "../../include/ngram.h"
+
+namespace ngram {
+
+namespace {
+
+constexpr int kFwdTok = 64;
+constexpr int kFwdThreads = 256;
+
+__device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b)
+{
+    uint4 r;
+    r.x = bf16_pack(bf16_lo(a.x) + bf16_lo(b.x), bf16_hi(a.x) + bf16_hi(b.x));
+    r.y = bf16_pack(bf16_lo(a.y) + bf16_lo(b.y), bf16_hi(a.y) + bf16_hi(b.y));
+    r.z = bf16_pack(bf16_lo(a.z) + bf16_lo(b.z), bf16_hi(a.z) + bf16_hi(b.z));
+    r.w = bf16_pack(bf16_lo(a.w) + bf16_lo(b.w), bf16_hi(a.w) + bf16_hi(b.w));
+    return r;
+}
+
+__device__ __forceinline__ uint4 add_f32x4(uint4 a, uint4 b)
+{
+    uint4 r;
+    r.x = __float_as_uint(__uint_as_float(a.x) + __uint_as_float(b.x));
+    r.y = __float_as_uint(__uint_as_float(a.y) + __uint_as_float(b.y));
+    r.z = __float_as_uint(__uint_as_float(a.z) + __uint_as_float(b.z));
+    r.w = __float_as_uint(__uint_as_float(a.w) + __uint_as_float(b.w));
+    return r;
+}
+
+// Negation is a sign-bit flip of every element: exact for both dtypes.
+__device__ __forceinline__ uint4 flip(uint4 a, uint32_t m)
+{
+    return make_uint4(a.x ^ m, a.y ^ m, a.z ^ m, a.w ^ m);
+}
+
+template <int ELT>
+__global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restrict__ tok, int64_t T,
+                                                          HashParams hp,
+                                                          const uint8_t *__restrict__ wb,
+                                                          const uint8_t *__restrict__ wt,
+                                                          uint8_t *__restrict__ out,
+                                                          uint32_t *__restrict__ flags)
+{
+    constexpr int kRowBytes = kDim * ELT;
+    constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
+    constexpr int kIter = kFwdTok * kCpr / kFwdThreads;   // 24 (bf16) or 48 (fp32)
+    constexpr int kU = 4;                                 // chunks in flight per thread
+    constexpr uint32_t kSign = ELT == 2 ? 0x80008000u : 0x80000000u;
+    static_assert(kIter % kU == 0, "unroll must divide the sweep");
+
+    __shared__ uint32_t s_idx[2][kFwdTok];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kFwdTok;
+    if (tid < kFwdTok) {
+        uint32_t ib = 0, it = 0;
+        const int64_t i = t0 + tid;
+        if (i < T) {
+            if (ngram_index(tok, i, hp, ib, it) && flags)
+                atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
+        }
+        s_idx[0][tid] = ib;
+        s_idx[1][tid] = it;
+    }
+    __syncthreads();
+    const int ntok = (int)min<int64_t>(kFwdTok, T - t0);
+    uint4 *orow = reinterpret_cast<uint4 *>(out + (size_t)t0 * kRowBytes);
+
+#pragma unroll
+    for (int g = 0; g < kIter; g += kU) {
+        uint4 a[kU], b[kU];
+        int e[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            e[u] = tid + (g + u) * kFwdThreads;
+            const int lt = e[u] / kCpr;
+            const int c = e[u] - lt * kCpr;
+            if (lt < ntok) {
+                const uint32_t ib = s_idx[0][lt], it = s_idx[1][lt];
+                const uint4 *pb = reinterpret_cast<const uint4 *>(wb + (size_t)(ib & 0x7FFFFFFFu) * kRowBytes) + c;
+                const uint4 *pt = reinterpret_cast<const uint4 *>(wt + (size_t)(it & 0x7FFFFFFFu) * kRowBytes) + c;
+                a[u] = flip(*pb, (ib >> 31) ? kSign : 0u);
+                b[u] = flip(*pt, (it >> 31) ? kSign : 0u);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int lt = e[u] / kCpr;
+            if (lt < ntok)
+                orow[e[u]] = ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]);
+        }
+    }
+}
+
+__global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashParams hp,
+                            uint32_t *__restrict__ idx, uint32_t *__restrict__ flags)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T)
+        return;
+    uint32_t ib, it;
+    if (ngram_index(tok, i, hp, ib, it) && flags)
+        atomicOr(flags, NGRAM_FLAG_BAD_TOKEN);
+    idx[i] = ib;
+    idx[T + i] = it;
+}
+
+// Spread mode: sort keys (row) and payloads (position | neg << 31) of both
+// channels for one micro-step.  Also resets the fix-up record counts.
+__global__ void keys_tokens_kernel(const int32_t *__restrict__ tok, int64_t T, HashParams hp,
+                                   uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
+                                   int64_t nk, WsHeader *__restrict__ hdr)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) {
+        hdr->n_owner[0] = 0;
+        hdr->n_owner[1] = 0;
+    }
+    if (i >= T)
+        return;
+    uint32_t ib, it;
+    if (ngram_index(tok, i, hp, ib, it))
+        atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
+    keys[i] = ib & 0x7FFFFFFFu;
+    vals[i] = (uint32_t)i | (ib & 0x80000000u);
+    keys[nk + i] = it & 0x7FFFFFFFu;
+    vals[nk + i] = (uint32_t)i | (it & 0x80000000u);
+}
+
+// Burst mode: keep the packed indices and the dY rows of one micro-step at
+// the end of the stash.  One block per 16 positions: 16 threads hash, all
+// 256 threads copy the 16 x 192 float4 of dY.
+constexpr int kStashTok = 16;
+__global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const float *__restrict__ dY,
+                                                    int64_t T, HashParams hp, uint32_t *__restrict__ sidx,
+                                                    float *__restrict__ sdy, int64_t nk,
+                                                    WsHeader *__restrict__ hdr)
+{
+    const uint32_t base = hdr->n_stash;
+    if ((int64_t)base + T > nk)
+        return;   // flagged by stash_advance_kernel
+    const int64_t t0 = (int64_t)blockIdx.x * kStashTok;
+    const int tid = threadIdx.x;
+    if (tid < kStashTok && t0 + tid < T) {
+        const int64_t i = t0 + tid;
+        uint32_t ib, it;
+        if (ngram_index(tok, i, hp, ib, it))
+            atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
+        sidx[base + i] = ib;
+        sidx[nk + base + i] = it;
+    }
+    const int ntok = (int)min<int64_t>(kStashTok, T - t0);
+    const float4 *src = reinterpret_cast<const float4 *>(dY + (size_t)t0 * kDim);
+    float4 *dst = reinterpret_cast<float4 *>(sdy + ((size_t)base + t0) * kDim);
+    for (int e = tid; e < ntok * (kDim / 4); e += 256)
+        dst[e] = src[e];
+}
+
+__global__ void stash_advance_kernel(int64_t T, int64_t nk, WsHeader *__restrict__ hdr)
+{
+    const uint32_t base = hdr->n_stash;
+    if ((int64_t)base + T > nk)
+        atomicOr(&hdr->flags, NGRAM_FLAG_STASH_FULL);
+    else
+        hdr->n_stash = base + (uint32_t)T;
+}
+
+__global__ void keys_stash_kernel(const uint32_t *__restrict__ sidx, int64_t nk,
+                                  uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
+                                  WsHeader *__restrict__ hdr)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) {
+        hdr->n_owner[0] = 0;
+        hdr->n_owner[1] = 0;
+    }
+    const uint32_t n = hdr->n_stash;
+    if (i >= n)
+        return;
+    const uint32_t ib = sidx[i], it = sidx[nk + i];
+    keys[i] = ib & 0x7FFFFFFFu;
+    vals[i] = (uint32_t)i | (ib & 0x80000000u);
+    keys[nk + i] = it & 0x7FFFFFFFu;
+    vals[nk + i] = (uint32_t)i | (it & 0x80000000u);
+}
+
+__global__ void stash_clear_kernel(WsHeader *__restrict__ hdr) { hdr->n_stash = 0; }
+
+__global__ void flags_clear_kernel(WsHeader *__restrict__ hdr) { hdr->flags = 0; }
+
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, uint64_t n, uint32_t v)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+unsigned grid_for(int64_t n, int per)
+{
+    return (unsigned)((n + per - 1) / per);
+}
+
+}  // namespace
+
+hipError_t launch_init(const WsLayout &L, uint8_t *ws, hipStream_t s)
+{
+    // header: zero everything, then the magic word
+    fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.hdr), sizeof(WsHeader) / 4, 0u);
+    fill_u32_kernel<<<1, 1, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.hdr), 1, kMagic);
+    for (int c = 0; c < 2; ++c)
+        fill_u32_kernel<<<2048, 256, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.slot_map[c]),
+                                             (uint64_t)L.rows[c], 0xFFFFFFFFu);
+    return hipGetLastError();
+}
+
+hipError_t launch_hash(const HashParams &hp, const int32_t *tok, int64_t T, uint32_t *idx,
+                       uint32_t *flags, hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    hash_kernel<<<grid_for(T, 256), 256, 0, s>>>(tok, T, hp, idx, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const void *wt,
+                      const int32_t *tok, int64_t T, void *out, uint32_t *flags, hipStream_t s)
+{
+    if (T == 0)
+        return hipSuccess;
+    const unsigned g = grid_for(T, kFwdTok);
+    if (dtype == NGRAM_DTYPE_BF16)
+        fwd_kernel<2><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
+                                                (uint8_t *)out, flags);
+    else
+        fwd_kernel<4><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
+                                                (uint8_t *)out, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_keys_from_tokens(const WsLayout &L, uint8_t *ws, const HashParams &hp,
+                                   const int32_t *tok, int64_t T, hipStream_t s)
+{
+    keys_tokens_kernel<<<grid_for(T > 0 ? T : 1, 256), 256, 0, s>>>(
+        tok, T, hp, reinterpret_cast<uint32_t *>(ws + L.keys[0]),
+        reinterpret_cast<uint32_t *>(ws + L.vals[0]), L.nk, reinterpret_cast<WsHeader *>(ws + L.hdr));
+    return hipGetLastError();
+}
+
+hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
+                        const float *dY, int64_t T, hipStream_t s)
+{
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    if (T > 0)
+        stash_kernel<<<grid_for(T, kStashTok), 256, 0, s>>>(
+            tok, dY, T, hp, reinterpret_cast<uint32_t *>(ws + L.stash_idx),
+            reinterpret_cast<float *>(ws + L.stash_dy), L.nk, hdr);
+    stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, hdr);
+    return hipGetLastError();
+}
+
+hipError_t launch_keys_from_stash(const WsLayout &L, uint8_t *ws, hipStream_t s)
+{
+    keys_stash_kernel<<<grid_for(L.nk, 256), 256, 0, s>>>(
+        reinterpret_cast<const uint32_t *>(ws + L.stash_idx), L.nk,
+        reinterpret_cast<uint32_t *>(ws + L.keys[0]), reinterpret_cast<uint32_t *>(ws + L.vals[0]),
+        reinterpret_cast<WsHeader *>(ws + L.hdr));
+    return hipGetLastError();
+}
+
+hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s)
+{
+    stash_clear_kernel<<<1, 1, 0, s>>>(reinterpret_cast<WsHeader *>(ws + L.hdr));
+    return hipGetLastError();
+}
+
+hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s)
+{
+    flags_clear_kernel<<<1, 1, 0, s>>>(reinterpret_cast<WsHeader *>(ws + L.hdr));
+    return hipGetLastError();
+}
+
+}  // namespace ngram

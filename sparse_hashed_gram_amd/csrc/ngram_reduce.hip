@@ -1,0 +1,632 @@
+// Backward of the hashed n-gram table: sort, dedupe, window slots and the
+// signed segment reduction (gfx950).
+//
+// Only rows that occur in the batch receive a gradient and an optimizer step,
+// and gradients are accumulated over 4 steps before the update (the
+// @classiclarryd post quoted on the airebao.com item; modded-nanogpt README,
+// technique list).  For one micro-step (spread mode) or one whole window
+// (burst mode) this file computes, per channel and per distinct row r,
+//     S[r] = sum over positions i hashed to r, in position order, of s_i dY[i]
+// and adds it to the window accumulator G[slot(r)].
+//
+// Pipeline per call, both channels in every launch (blockIdx.y = channel):
+//   1. LSD radix sort of (row, position|sign) pairs, 8-bit digits.  Each pass
+//      is a per-tile LDS histogram, one digit-major scan, and a stable
+//      scatter: ranks within a tile come from wavefront ballots (64-lane
+//      match of the digit), the tile is reordered in LDS, then written out in
+//      digit runs so global writes stay contiguous.
+//   2. Segment heads; rows new to the window get the next slots in ascending
+//      row order (tile counts, one scan, tile-local prefix: no atomics, so the
+//      slot layout is deterministic).
+//   3. Segment reduction: one wavefront per 64 sorted keys.  A lane holds 12
+//      floats of a 768-wide row; each key costs three coalesced 1 KB loads of
+//      dY.  A segment that ends in the chunk is written straight to G; one that
+//      spills into the next chunk only is finished by the chunk where it
+//      starts; longer ones (hot n-grams: thousands of keys) leave one partial
+//      row per chunk, which a 16-wavefront block sums in a fixed order.
+//      Every sum therefore has a fixed association and results are bitwise
+//      reproducible; there are no floating-point atomics.
+#include "ngram_dev.hpp"
+
+#include "../../include/ngram.h"
+
+namespace ngram {
+
+namespace {
+
+__device__ __forceinline__ uint32_t count_of(const uint32_t *n_dev, uint32_t n_host)
+{
+    return n_dev ? min(*n_dev, n_host) : n_host;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+// Exclusive scan over a block of NT threads; *total (if given) gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave, uint32_t *total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane == kWave - 1)
+        s_wave[w] = inc;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+        const uint32_t x = s_wave[i];
+        off += (i < w) ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    if (total)
+        *total = tot;
+    return off + inc - v;
+}
+
+// ------------------------------------------------------------ radix sort
+
+__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
+    const uint32_t *__restrict__ keys, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
+    uint32_t *__restrict__ hist, uint32_t nblk)
+{
+    __shared__ uint32_t h[kRadix];
+    const int c = blockIdx.y;
+    const uint32_t b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint32_t n = count_of(n_dev, n_host);
+    h[tid] = 0;
+    __syncthreads();
+    const uint32_t *k = keys + (size_t)c * nk;
+    const uint32_t base = b * kSortTile;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = base + j * kSortThreads + tid;
+        if (i < n)
+            atomicAdd(&h[(k[i] >> shift) & (kRadix - 1)], 1u);
+    }
+    __syncthreads();
+    hist[((size_t)c * kRadix + tid) * nblk + b] = h[tid];
+}
+
+// In-place exclusive scan of `len` words per channel (channel = blockIdx.x).
+// With hdr non-null the total becomes the number of new window slots.
+__global__ __launch_bounds__(1024) void scan_kernel(uint32_t *__restrict__ data, uint32_t len,
+                                                    WsHeader *__restrict__ hdr, uint32_t wrows)
+{
+    __shared__ uint32_t s_wave[1024 / kWave];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    uint32_t *d = data + (size_t)c * len;
+    const uint32_t per = (len + 1023) / 1024;
+    const uint32_t lo = min(tid * per, len), hi = min(lo + per, len);
+    uint32_t sum = 0;
+    for (uint32_t j = lo; j < hi; ++j)
+        sum += d[j];
+    uint32_t total;
+    uint32_t run = block_excl_scan<1024>(sum, s_wave, &total);
+    for (uint32_t j = lo; j < hi; ++j) {
+        const uint32_t x = d[j];
+        d[j] = run;
+        run += x;
+    }
+    if (hdr && tid == 0) {
+        const uint32_t old = hdr->n_slots[c];
+        hdr->n_prev[c] = old;
+        uint64_t now = (uint64_t)old + total;
+        if (now > wrows) {
+            atomicOr(&hdr->flags, NGRAM_FLAG_WINDOW_FULL);
+            now = wrows;
+        }
+        hdr->n_slots[c] = (uint32_t)now;
+    }
+}
+
+// Stable scatter of one tile by the current digit.  Wave w owns tile keys
+// [w*512, w*512+512), processed 64 at a time in index order.
+__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
+    const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
+    uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
+    const uint32_t *__restrict__ hist, uint32_t nblk)
+{
+    constexpr int kPerWave = kSortTile / (kSortThreads / kWave);
+    __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
+    __shared__ uint32_t s_tile[kRadix];
+    __shared__ uint32_t s_glob[kRadix];
+    __shared__ uint32_t s_k[kSortTile];
+    __shared__ uint32_t s_v[kSortTile];
+    __shared__ uint32_t s_wave[kSortThreads / kWave];
+
+    const int c = blockIdx.y;
+    const uint32_t b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const uint32_t n = count_of(n_dev, n_host);
+    const uint32_t base = b * kSortTile;
+    if (base >= n)
+        return;
+    const uint32_t *ki = kin + (size_t)c * nk;
+    const uint32_t *vi = vin + (size_t)c * nk;
+
+    for (int r = tid; r < (kSortThreads / kWave) * kRadix; r += kSortThreads)
+        (&s_cnt[0][0])[r] = 0;
+    s_glob[tid] = hist[((size_t)c * kRadix + tid) * nblk + b];
+    __syncthreads();
+
+    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = base + w * kPerWave + j * kWave + lane;
+        const bool ok = i < n;
+        key[j] = ok ? ki[i] : 0u;
+        val[j] = ok ? vi[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const bool ok = base + w * kPerWave + j * kWave + lane < n;
+        const uint32_t d = (key[j] >> shift) & (kRadix - 1);
+        uint64_t m = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < kRadixBits; ++bit) {
+            const bool on = (d >> bit) & 1u;
+            const uint64_t bb = __ballot(on);
+            m &= on ? bb : ~bb;
+        }
+        const uint32_t before = s_cnt[w][d];
+        if (ok && lane == 63 - __clzll(m))
+            s_cnt[w][d] = before + (uint32_t)__popcll(m);
+        rank[j] = before + (uint32_t)__popcll(m & below);
+    }
+    __syncthreads();
+    {
+        uint32_t run = 0;
+#pragma unroll
+        for (int ww = 0; ww < kSortThreads / kWave; ++ww) {
+            const uint32_t x = s_cnt[ww][tid];
+            s_cnt[ww][tid] = run;
+            run += x;
+        }
+        s_tile[tid] = block_excl_scan<kSortThreads>(run, s_wave, nullptr);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const bool ok = base + w * kPerWave + j * kWave + lane < n;
+        if (ok) {
+            const uint32_t d = (key[j] >> shift) & (kRadix - 1);
+            const uint32_t pos = s_tile[d] + s_cnt[w][d] + rank[j];
+            s_k[pos] = key[j];
+            s_v[pos] = val[j];
+        }
+    }
+    __syncthreads();
+    uint32_t *ko = kout + (size_t)c * nk;
+    uint32_t *vo = vout + (size_t)c * nk;
+    const uint32_t nv = min((uint32_t)kSortTile, n - base);
+    for (uint32_t p = tid; p < nv; p += kSortThreads) {
+        const uint32_t k = s_k[p];
+        const uint32_t d = (k >> shift) & (kRadix - 1);
+        const uint32_t dst = s_glob[d] + (p - s_tile[d]);
+        ko[dst] = k;
+        vo[dst] = s_v[p];
+    }
+}
+
+// ------------------------------------------------- heads and window slots
+
+struct SlotArgs {
+    const uint32_t *rows;   // sorted keys [2][nk]
+    int64_t nk;
+    const uint32_t *n_dev;
+    uint32_t n_host;
+    int32_t *slot_map[2];
+    uint32_t *slot_rows[2];
+    uint32_t *seg_info;     // [2][nk]
+    uint32_t *blk;          // [2][nblk]
+    uint32_t nblk;
+    uint32_t wrows;
+    WsHeader *hdr;
+};
+
+// Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
+__device__ __forceinline__ uint32_t new_heads(const SlotArgs &a, int c, uint32_t n, uint32_t i0,
+                                              uint32_t &mask)
+{
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const int32_t *sm = a.slot_map[c];
+    uint32_t cnt = 0;
+    mask = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = i0 + j;
+        if (i < n) {
+            const uint32_t r = R[i];
+            const bool head = (i == 0) || (R[i - 1] != r);
+            if (head && sm[r] < 0) {
+                mask |= 1u << j;
+                ++cnt;
+            }
+        }
+    }
+    return cnt;
+}
+
+__global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
+{
+    __shared__ uint32_t s_wave[kSortThreads / kWave];
+    const int c = blockIdx.y;
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t i0 = blockIdx.x * kSortTile + threadIdx.x * kSortItems;
+    uint32_t mask;
+    const uint32_t cnt = new_heads(a, c, n, i0, mask);
+    uint32_t total;
+    block_excl_scan<kSortThreads>(cnt, s_wave, &total);
+    if (threadIdx.x == 0)
+        a.blk[(size_t)c * a.nblk + blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
+{
+    __shared__ uint32_t s_wave[kSortThreads / kWave];
+    const int c = blockIdx.y;
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t i0 = blockIdx.x * kSortTile + threadIdx.x * kSortItems;
+    uint32_t mask;
+    const uint32_t cnt = new_heads(a, c, n, i0, mask);
+    const uint32_t off = block_excl_scan<kSortThreads>(cnt, s_wave, nullptr);
+    uint32_t slot = a.hdr->n_prev[c] + a.blk[(size_t)c * a.nblk + blockIdx.x] + off;
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    int32_t *sm = a.slot_map[c];
+    uint32_t *info = a.seg_info + (size_t)c * a.nk;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = i0 + j;
+        if (i >= n)
+            break;
+        const uint32_t r = R[i];
+        const bool head = (i == 0) || (R[i - 1] != r);
+        if (!head)
+            continue;
+        if (mask & (1u << j)) {
+            if (slot < a.wrows) {
+                sm[r] = (int32_t)slot;
+                a.slot_rows[c][slot] = r;
+                info[i] = slot | 0x80000000u;
+            } else {
+                info[i] = 0xFFFFFFFFu;   // window full: row dropped (flagged)
+            }
+            ++slot;
+        } else {
+            info[i] = (uint32_t)sm[r];
+        }
+    }
+}
+
+// ------------------------------------------------------ segment reduction
+
+constexpr int kRedThreads = 256;
+constexpr int kRedU = 4;   // dY rows in flight per wavefront
+
+struct RedArgs {
+    const uint32_t *rows;   // sorted [2][nk]
+    const uint32_t *vals;   // sorted [2][nk]: position | neg << 31
+    const uint32_t *info;   // [2][nk] at heads
+    int64_t nk;
+    const uint32_t *n_dev;
+    uint32_t n_host;
+    const float *dY;        // [positions][768]
+    float *gacc;            // [2][wrows][768]
+    int64_t wrows;
+    float *partial;         // [2][nchunk][2][768]
+    uint64_t *owners;       // [2][nchunk]: chunk | info << 32
+    int64_t nchunk;
+    WsHeader *hdr;
+};
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b)
+{
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+__device__ __forceinline__ float4 flip4(float4 a, uint32_t s)
+{
+    return make_float4(__uint_as_float(__float_as_uint(a.x) ^ s), __uint_as_float(__float_as_uint(a.y) ^ s),
+                       __uint_as_float(__float_as_uint(a.z) ^ s), __uint_as_float(__float_as_uint(a.w) ^ s));
+}
+
+__device__ __forceinline__ uint32_t lane_val(uint32_t v0, uint32_t v1, int j)
+{
+    return j < kWave ? (uint32_t)__builtin_amdgcn_readlane((int)v0, j)
+                     : (uint32_t)__builtin_amdgcn_readlane((int)v1, j - kWave);
+}
+
+// acc += s_j dY[pos_j] for keys j in [ja, jb), in key order.  Keys below 64
+// come from this chunk's lanes (v0), keys from 64 on from the next chunk's (v1).
+__device__ __forceinline__ void accumulate(float4 (&acc)[3], const float *__restrict__ dY, uint32_t v0,
+                                           uint32_t v1, int ja, int jb, int lane)
+{
+    for (int j = ja; j < jb; j += kRedU) {
+        float4 x[kRedU][3];
+        uint32_t sg[kRedU];
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u) {
+            if (j + u < jb) {
+                const uint32_t v = lane_val(v0, v1, j + u);
+                sg[u] = v & 0x80000000u;
+                const float4 *p = reinterpret_cast<const float4 *>(dY + (size_t)(v & 0x7FFFFFFFu) * kDim) + lane;
+                x[u][0] = p[0];
+                x[u][1] = p[kWave];
+                x[u][2] = p[2 * kWave];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u) {
+            if (j + u < jb) {
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    acc[q] = add4(acc[q], flip4(x[u][q], sg[u]));
+            }
+        }
+    }
+}
+
+// G[slot] = (new row ? 0 : G[slot]) + acc
+__device__ __forceinline__ void flush_row(float4 (&acc)[3], float *gacc, int64_t wrows, int c,
+                                          uint32_t info, int lane)
+{
+    if (info == 0xFFFFFFFFu)
+        return;
+    const uint32_t slot = info & 0x7FFFFFFFu;
+    float4 *g = reinterpret_cast<float4 *>(gacc + ((size_t)c * wrows + slot) * kDim) + lane;
+    if (!(info >> 31)) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            acc[q] = add4(g[q * kWave], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        g[q * kWave] = acc[q];
+}
+
+__device__ __forceinline__ void store_partial(const float4 (&acc)[3], float *partial, int64_t nchunk, int c,
+                                              int64_t chunk, int which, int lane)
+{
+    float4 *p = reinterpret_cast<float4 *>(partial + (((size_t)c * nchunk + chunk) * 2 + which) * kDim) + lane;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        p[q * kWave] = acc[q];
+}
+
+__global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
+{
+    const int c = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const int64_t c0 = chunk * kChunk;
+    if (c0 >= n)
+        return;
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const uint32_t *V = a.vals + (size_t)c * a.nk;
+    const uint32_t *I = a.info + (size_t)c * a.nk;
+    const int nv = (int)min<int64_t>(kChunk, (int64_t)n - c0);
+    const bool valid = lane < nv;
+    const uint32_t r0 = valid ? R[c0 + lane] : 0xFFFFFFFFu;
+    const uint32_t v0 = valid ? V[c0 + lane] : 0u;
+    uint32_t prev = __shfl_up(r0, 1);
+    if (lane == 0)
+        prev = c0 > 0 ? R[c0 - 1] : 0xFFFFFFFFu;
+    const bool head = valid && (r0 != prev);
+    const uint64_t hm = __ballot(head);
+    const uint32_t i0 = head ? I[c0 + lane] : 0u;
+    const uint32_t row_last = (uint32_t)__builtin_amdgcn_readlane((int)r0, nv - 1);
+    const bool cont_after = nv == kChunk && c0 + kChunk < n && R[c0 + kChunk] == row_last;
+
+    // First piece continuing a segment from the previous chunk: skipped when
+    // that chunk (where the segment starts) finishes it because it ends here.
+    bool skip_first = false;
+    if (!(hm & 1ull)) {
+        const uint32_t row0 = (uint32_t)__builtin_amdgcn_readlane((int)r0, 0);
+        const int e0 = hm ? (int)__builtin_ctzll(hm) : nv;
+        const bool piece0_cont = (e0 == nv) && cont_after;
+        const bool head_in_prev = (c0 == kChunk) || (R[c0 - kChunk - 1] != row0);
+        skip_first = head_in_prev && !piece0_cont;
+    }
+    // Last piece starting here and spilling over: finish it here if it ends
+    // within the next chunk (load that chunk's keys), else leave a partial.
+    bool owner_full = false;
+    uint32_t v1 = 0;
+    int extra = 0;
+    if (hm && cont_after) {
+        owner_full = !(c0 + 2 * kChunk < n && R[c0 + 2 * kChunk] == row_last);
+        if (owner_full) {
+            const int64_t i1 = c0 + kChunk + lane;
+            const bool ok1 = i1 < n;
+            const uint32_t r1 = ok1 ? R[i1] : 0xFFFFFFFFu;
+            v1 = ok1 ? V[i1] : 0u;
+            extra = __popcll(__ballot(ok1 && r1 == row_last));
+        }
+    }
+
+    int pa = 0;
+    while (pa < nv) {
+        const uint64_t later = pa >= kChunk - 1 ? 0ull : (hm & (~0ull << (pa + 1)));
+        const int pb = later ? (int)__builtin_ctzll(later) : nv;
+        const bool is_head = (hm >> pa) & 1ull;
+        float4 acc[3] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
+                         make_float4(0.f, 0.f, 0.f, 0.f)};
+        if (!is_head) {
+            if (!skip_first) {
+                accumulate(acc, a.dY, v0, 0u, 0, pb, lane);
+                store_partial(acc, a.partial, a.nchunk, c, chunk, 0, lane);
+            }
+        } else if (pb == nv && cont_after) {
+            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, pa);
+            if (owner_full) {
+                accumulate(acc, a.dY, v0, v1, pa, kChunk + extra, lane);
+                flush_row(acc, a.gacc, a.wrows, c, info, lane);
+            } else {
+                accumulate(acc, a.dY, v0, 0u, pa, kChunk, lane);
+                store_partial(acc, a.partial, a.nchunk, c, chunk, 1, lane);
+                if (lane == 0) {
+                    const uint32_t k = atomicAdd(&a.hdr->n_owner[c], 1u);
+                    a.owners[(size_t)c * a.nchunk + k] = (uint64_t)chunk | ((uint64_t)info << 32);
+                }
+            }
+        } else {
+            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, pa);
+            accumulate(acc, a.dY, v0, 0u, pa, pb, lane);
+            flush_row(acc, a.gacc, a.wrows, c, info, lane);
+        }
+        pa = pb;
+    }
+}
+
+// Sums the partial rows of each segment longer than two chunks: the starting
+// chunk's tail piece, then every following chunk's head piece, split into 16
+// contiguous runs (one per wavefront) that are added in run order.
+constexpr int kFixThreads = 1024;
+__global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
+{
+    constexpr int kW = kFixThreads / kWave;
+    __shared__ float4 s_part[kW][kDim / 4];
+    const int c = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const uint32_t nown = a.hdr->n_owner[c];
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
+    for (uint32_t k = blockIdx.x; k < nown; k += gridDim.x) {
+        const uint64_t rec = a.owners[(size_t)c * a.nchunk + k];
+        const int64_t chunk = (int64_t)(uint32_t)rec;
+        const uint32_t info = (uint32_t)(rec >> 32);
+        const uint32_t row = R[chunk * kChunk + kChunk - 1];
+        int64_t m = 0;   // following chunks that start inside the segment
+        for (;;) {
+            const int64_t cc = chunk + 1 + m + tid;
+            const bool hit = cc * kChunk < (int64_t)n && R[cc * kChunk] == row;
+            const int cnt = __syncthreads_count(hit);
+            m += cnt;
+            if (cnt < kFixThreads)
+                break;
+        }
+        const int64_t np = m + 1;
+        const int64_t lo = np * w / kW, hi = np * (w + 1) / kW;
+        float4 acc[3] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
+                         make_float4(0.f, 0.f, 0.f, 0.f)};
+        for (int64_t p = lo; p < hi; p += kRedU) {
+            float4 x[kRedU][3];
+#pragma unroll
+            for (int u = 0; u < kRedU; ++u) {
+                if (p + u < hi) {
+                    const int64_t src = p + u == 0 ? chunk * 2 + 1 : (chunk + p + u) * 2;
+                    const float4 *s = P + src * (kDim / 4) + lane;
+                    x[u][0] = s[0];
+                    x[u][1] = s[kWave];
+                    x[u][2] = s[2 * kWave];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kRedU; ++u) {
+                if (p + u < hi) {
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        acc[q] = add4(acc[q], x[u][q]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            s_part[w][lane + q * kWave] = acc[q];
+        __syncthreads();
+        if (tid < kDim / 4 && info != 0xFFFFFFFFu) {
+            float4 s = s_part[0][tid];
+#pragma unroll
+            for (int ww = 1; ww < kW; ++ww)
+                s = add4(s, s_part[ww][tid]);
+            float4 *g = reinterpret_cast<float4 *>(a.gacc + ((size_t)c * a.wrows + (info & 0x7FFFFFFFu)) * kDim) + tid;
+            if (!(info >> 31))
+                s = add4(*g, s);
+            *g = s;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host,
+                         const float *dY, hipStream_t s)
+{
+    if (n_host == 0)
+        return hipSuccess;
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+    int cur = 0;
+    for (int p = 0; p < L.passes; ++p) {
+        const int shift = p * kRadixBits;
+        uint32_t *kin = reinterpret_cast<uint32_t *>(ws + L.keys[cur]);
+        uint32_t *vin = reinterpret_cast<uint32_t *>(ws + L.vals[cur]);
+        uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
+        uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
+        radix_hist_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nblk);
+        scan_kernel<<<2, 1024, 0, s>>>(hist, kRadix * nblk, nullptr, 0);
+        radix_scatter_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
+                                                                    shift, hist, nblk);
+        cur ^= 1;
+    }
+    SlotArgs sa;
+    sa.rows = reinterpret_cast<const uint32_t *>(ws + L.keys[cur]);
+    sa.nk = L.nk;
+    sa.n_dev = n_dev;
+    sa.n_host = n_host;
+    for (int c = 0; c < 2; ++c) {
+        sa.slot_map[c] = reinterpret_cast<int32_t *>(ws + L.slot_map[c]);
+        sa.slot_rows[c] = reinterpret_cast<uint32_t *>(ws + L.slot_rows[c]);
+    }
+    sa.seg_info = reinterpret_cast<uint32_t *>(ws + L.seg_info);
+    sa.blk = reinterpret_cast<uint32_t *>(ws + L.blk);
+    sa.nblk = nblk;
+    sa.wrows = (uint32_t)L.wrows;
+    sa.hdr = hdr;
+    mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+    scan_kernel<<<2, 1024, 0, s>>>(sa.blk, nblk, hdr, (uint32_t)L.wrows);
+    assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+
+    RedArgs ra;
+    ra.rows = sa.rows;
+    ra.vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
+    ra.info = sa.seg_info;
+    ra.nk = L.nk;
+    ra.n_dev = n_dev;
+    ra.n_host = n_host;
+    ra.dY = dY;
+    ra.gacc = reinterpret_cast<float *>(ws + L.gacc);
+    ra.wrows = L.wrows;
+    ra.partial = reinterpret_cast<float *>(ws + L.partial);
+    ra.owners = reinterpret_cast<uint64_t *>(ws + L.owners);
+    ra.nchunk = L.nchunk;
+    ra.hdr = hdr;
+    const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
+    const uint32_t per_block = kRedThreads / kWave;
+    seg_reduce_kernel<<<dim3((nchunk + per_block - 1) / per_block, 2), kRedThreads, 0, s>>>(ra);
+    fixup_kernel<<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    return hipGetLastError();
+}
+
+}  // namespace ngram

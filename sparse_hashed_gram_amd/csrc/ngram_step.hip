@@ -1,0 +1,213 @@
+// Fused lazy sparse row-wise step and window export (gfx950).
+//
+// Adam with beta1 = 0 on the n-gram rows a window touched, one second-moment
+// float per 768-wide row, beta2 applied retroactively when a row comes back
+// (the @classiclarryd post quoted on the airebao.com item; modded-nanogpt
+// README technique list: sparse row-wise embedding updates).  Per touched row
+// r with window gradient G and optimizer step number t:
+//     k = t - t_last[r];   v[r] = beta2^k v[r] + (1 - beta2) mean(G^2)
+//     W[r] -= lr G / (sqrt(v[r]) + eps);   t_last[r] = t
+// One wavefront per row: a lane holds 12 of the 768 values (three 16-byte G
+// loads and three 8-byte bf16 loads, all coalesced), mean(G^2) is a butterfly
+// sum over the wavefront (every lane ends with the same bits), and the row's
+// slot-map entry is cleared in the same pass so the window is empty after it.
+#include "ngram_dev.hpp"
+
+#include "../../include/ngram.h"
+
+namespace ngram {
+
+namespace {
+
+struct StepArgs {
+    const uint32_t *slot_rows[2];
+    const float *gacc;      // [2][wrows][768]
+    int64_t wrows;
+    uint8_t *w[2];
+    float *v[2];
+    int32_t *tl[2];
+    int32_t *slot_map[2];
+    WsHeader *hdr;
+    int32_t t;
+    float lr, beta2, eps;
+};
+
+// beta2^k by square-and-multiply in fp64 (relative error below k * 2^-52).
+__device__ __forceinline__ double pow_steps(double b, int32_t k)
+{
+    double r = 1.0;
+    while (k > 0) {
+        if (k & 1)
+            r *= b;
+        b *= b;
+        k >>= 1;
+    }
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        x += __shfl_xor(x, d);
+    return x;
+}
+
+template <int ELT>
+__global__ __launch_bounds__(256) void step_kernel(StepArgs a)
+{
+    const int c = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wid = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    const uint32_t stride = gridDim.x * (256 / kWave);
+    const uint32_t n = a.hdr->n_slots[c];
+    const uint32_t *rows = a.slot_rows[c];
+    const float *G = a.gacc + (size_t)c * a.wrows * kDim;
+    uint8_t *W = a.w[c];
+    float *V = a.v[c];
+    int32_t *TL = a.tl[c];
+    int32_t *SM = a.slot_map[c];
+    const double one_minus_b2 = 1.0 - (double)a.beta2;
+
+    for (uint32_t slot = wid; slot < n; slot += stride) {
+        const uint32_t row = rows[slot];
+        const float4 *g4 = reinterpret_cast<const float4 *>(G + (size_t)slot * kDim) + lane;
+        const float4 g[3] = {g4[0], g4[kWave], g4[2 * kWave]};
+        float w[3][4];
+        if (ELT == 2) {
+            const uint2 *wp = reinterpret_cast<const uint2 *>(W + (size_t)row * kDim * 2) + lane;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const uint2 x = wp[q * kWave];
+                w[q][0] = bf16_lo(x.x);
+                w[q][1] = bf16_hi(x.x);
+                w[q][2] = bf16_lo(x.y);
+                w[q][3] = bf16_hi(x.y);
+            }
+        } else {
+            const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)row * kDim * 4) + lane;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const float4 x = wp[q * kWave];
+                w[q][0] = x.x;
+                w[q][1] = x.y;
+                w[q][2] = x.z;
+                w[q][3] = x.w;
+            }
+        }
+        const int32_t tlast = TL[row];
+        const float vold = V[row];
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            ss += g[q].x * g[q].x + g[q].y * g[q].y + g[q].z * g[q].z + g[q].w * g[q].w;
+        ss = wave_sum(ss);
+        int32_t k = a.t - tlast;
+        if (k < 1) {
+            if (lane == 0)
+                atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+            k = 0;
+        }
+        const double decay = pow_steps((double)a.beta2, k);
+        const float vn = (float)(decay * (double)vold + one_minus_b2 * ((double)ss / (double)kDim));
+        const float scale = a.lr / (sqrtf(vn) + a.eps);
+        const float gg[3][4] = {{g[0].x, g[0].y, g[0].z, g[0].w},
+                                {g[1].x, g[1].y, g[1].z, g[1].w},
+                                {g[2].x, g[2].y, g[2].z, g[2].w}};
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[q][e] = w[q][e] - scale * gg[q][e];
+        if (ELT == 2) {
+            uint2 *wp = reinterpret_cast<uint2 *>(W + (size_t)row * kDim * 2) + lane;
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                wp[q * kWave] = make_uint2(bf16_pack(w[q][0], w[q][1]), bf16_pack(w[q][2], w[q][3]));
+        } else {
+            float4 *wp = reinterpret_cast<float4 *>(W + (size_t)row * kDim * 4) + lane;
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                wp[q * kWave] = make_float4(w[q][0], w[q][1], w[q][2], w[q][3]);
+        }
+        if (lane == 0) {
+            V[row] = vn;
+            TL[row] = a.t;
+            SM[row] = -1;
+        }
+    }
+}
+
+__global__ void window_clear_kernel(WsHeader *__restrict__ hdr)
+{
+    hdr->n_slots[0] = 0;
+    hdr->n_slots[1] = 0;
+    hdr->n_prev[0] = 0;
+    hdr->n_prev[1] = 0;
+}
+
+__global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uint32_t *__restrict__ slot_rows,
+                              const float *__restrict__ G, uint32_t *__restrict__ rows_out,
+                              float *__restrict__ g_out, uint32_t max_rows, uint32_t *__restrict__ count)
+{
+    const uint32_t total = hdr->n_slots[c];
+    const uint32_t n = min(total, max_rows);
+    const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t nthr = (uint64_t)gridDim.x * blockDim.x;
+    if (tid == 0)
+        *count = total;
+    for (uint64_t i = tid; i < n; i += nthr)
+        rows_out[i] = slot_rows[i];
+    if (g_out) {
+        const float4 *src = reinterpret_cast<const float4 *>(G);
+        float4 *dst = reinterpret_cast<float4 *>(g_out);
+        for (uint64_t i = tid; i < (uint64_t)n * (kDim / 4); i += nthr)
+            dst[i] = src[i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, float *vb, float *vt,
+                       int32_t *tlb, int32_t *tlt, int32_t t, float lr, float beta2, float eps, hipStream_t s)
+{
+    StepArgs a;
+    for (int c = 0; c < 2; ++c) {
+        a.slot_rows[c] = reinterpret_cast<const uint32_t *>(ws + L.slot_rows[c]);
+        a.slot_map[c] = reinterpret_cast<int32_t *>(ws + L.slot_map[c]);
+    }
+    a.gacc = reinterpret_cast<const float *>(ws + L.gacc);
+    a.wrows = L.wrows;
+    a.w[0] = (uint8_t *)wb;
+    a.w[1] = (uint8_t *)wt;
+    a.v[0] = vb;
+    a.v[1] = vt;
+    a.tl[0] = tlb;
+    a.tl[1] = tlt;
+    a.hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    a.t = t;
+    a.lr = lr;
+    a.beta2 = beta2;
+    a.eps = eps;
+    const int64_t want = (L.wrows + 3) / 4;
+    const unsigned gx = (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+    if (dtype == NGRAM_DTYPE_BF16)
+        step_kernel<2><<<dim3(gx, 2), 256, 0, s>>>(a);
+    else
+        step_kernel<4><<<dim3(gx, 2), 256, 0, s>>>(a);
+    window_clear_kernel<<<1, 1, 0, s>>>(a.hdr);
+    return hipGetLastError();
+}
+
+hipError_t launch_export(const WsLayout &L, const uint8_t *ws, int channel, uint32_t *rows, float *G,
+                         uint32_t max_rows, uint32_t *count, hipStream_t s)
+{
+    const WsHeader *hdr = reinterpret_cast<const WsHeader *>(ws + L.hdr);
+    const float *src = reinterpret_cast<const float *>(ws + L.gacc) + (size_t)channel * L.wrows * kDim;
+    export_kernel<<<1024, 256, 0, s>>>(hdr, channel,
+                                       reinterpret_cast<const uint32_t *>(ws + L.slot_rows[channel]), src,
+                                       rows, G, max_rows, count);
+    return hipGetLastError();
+}
+
+}  // namespace ngram

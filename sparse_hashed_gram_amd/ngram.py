@@ -1,0 +1,256 @@
+"""Python binding of libngram (ctypes).  Argument marshalling only.
+
+Every function here forwards to the C ABI in ``include/ngram.h`` of the same
+name; PyTorch only supplies device memory and the current HIP stream.  There
+is no fallback: if the HIP library has not been built, importing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libngram.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MODE_SPREAD = 0
+MODE_BURST = 1
+
+FLAG_BAD_TOKEN = 0x1
+FLAG_WINDOW_FULL = 0x2
+FLAG_STASH_FULL = 0x4
+FLAG_STEP_ORDER = 0x8
+
+DIM = 768
+
+
+class NgramConfig(ctypes.Structure):
+    _fields_ = [
+        ("vocab", ctypes.c_int32),
+        ("eos_id", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rows", ctypes.c_int64 * 2),
+        ("seed", ctypes.c_uint64 * 2),
+        ("max_tokens", ctypes.c_int64),
+        ("accum_steps", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("window_rows", ctypes.c_int64),
+    ]
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == DTYPE_F32 else torch.bfloat16
+
+    @property
+    def window_capacity(self) -> int:
+        if self.window_rows > 0:
+            return int(self.window_rows)
+        return int(min(max(self.rows[0], self.rows[1]), self.accum_steps * self.max_tokens))
+
+
+def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
+           max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
+           window_rows: int = 0) -> NgramConfig:
+    c = NgramConfig()
+    c.vocab = vocab
+    c.eos_id = eos_id
+    c.dim = DIM
+    c.dtype = DTYPE_F32 if dtype == "f32" else DTYPE_BF16
+    c.rows[0], c.rows[1] = int(rows[0]), int(rows[1])
+    c.seed[0], c.seed[1] = int(seeds[0]), int(seeds[1])
+    c.max_tokens = int(max_tokens)
+    c.accum_steps = int(accum_steps)
+    c.mode = MODE_SPREAD if mode == "spread" else MODE_BURST
+    c.window_rows = int(window_rows)
+    return c
+
+
+class NgramError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libngram is not built ({_LIB_PATH} missing): run "
+                               "`python -m sparse_hashed_gram_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, u64p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        cp = ctypes.POINTER(NgramConfig)
+        sig = {
+            "ngram_abi_version": ([], ctypes.c_int),
+            "ngram_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "ngram_config_check": ([cp], ctypes.c_int),
+            "ngram_workspace_bytes": ([cp, u64p], ctypes.c_int),
+            "ngram_workspace_init": ([cp, vp, ctypes.c_uint64, vp], ctypes.c_int),
+            "ngram_hash": ([cp, vp, i64, vp, vp, vp], ctypes.c_int),
+            "ngram_embed_fwd": ([cp, vp, vp, vp, i64, vp, vp, vp], ctypes.c_int),
+            "ngram_embed_bwd_accum": ([cp, vp, vp, vp, i64, vp], ctypes.c_int),
+            "ngram_window_reduce": ([cp, vp, vp], ctypes.c_int),
+            "ngram_sparse_step": ([cp, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
+                                   ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+            "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
+            "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+lib()   # fail at import time if the HIP library is missing: there is no fallback
+
+
+def status_string(status: int) -> str:
+    return lib().ngram_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise NgramError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def config_check(cfg: NgramConfig) -> int:
+    return lib().ngram_config_check(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg: NgramConfig) -> int:
+    n = ctypes.c_uint64()
+    _check("ngram_workspace_bytes", lib().ngram_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return int(n.value)
+
+
+class Workspace:
+    """Device workspace of one table pair (a uint8 tensor, 256-byte aligned)."""
+
+    def __init__(self, cfg: NgramConfig, device="cuda"):
+        self.cfg = cfg
+        self.nbytes = workspace_bytes(cfg)
+        self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self._buf.data_ptr()) % 256
+        self.tensor = self._buf[off:off + self.nbytes]
+        self.reset()
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+    def reset(self):
+        _check("ngram_workspace_init",
+               lib().ngram_workspace_init(ctypes.byref(self.cfg), self.ptr, self.nbytes, _stream()))
+
+
+def _ws(ws: Workspace | None):
+    return None if ws is None else ws.ptr
+
+
+def hash(cfg: NgramConfig, tokens: torch.Tensor, ws: Workspace | None = None) -> torch.Tensor:
+    """Packed indices int32 [2, T] (bit pattern row | neg << 31)."""
+    T = tokens.numel()
+    idx = torch.empty((2, T), dtype=torch.int32, device=tokens.device)
+    _check("ngram_hash", lib().ngram_hash(ctypes.byref(cfg), _dev(tokens, "tokens", torch.int32), T,
+                                          idx.data_ptr(), _ws(ws), _stream()))
+    return idx
+
+
+def _check_tables(cfg: NgramConfig, W_b, W_t):
+    for c, W in ((0, W_b), (1, W_t)):
+        if tuple(W.shape) != (cfg.rows[c], DIM):
+            raise ValueError(f"table {c} must be [{cfg.rows[c]}, {DIM}], got {tuple(W.shape)}")
+
+
+def _check_state(cfg: NgramConfig, v_b, v_t, t_last_b, t_last_t):
+    for c, x in ((0, v_b), (1, v_t), (0, t_last_b), (1, t_last_t)):
+        if x.numel() != cfg.rows[c]:
+            raise ValueError(f"optimizer state of channel {c} must have {cfg.rows[c]} entries")
+
+
+def embed_fwd(cfg: NgramConfig, W_b: torch.Tensor, W_t: torch.Tensor, tokens: torch.Tensor,
+              out: torch.Tensor | None = None, ws: Workspace | None = None) -> torch.Tensor:
+    T = tokens.numel()
+    _check_tables(cfg, W_b, W_t)
+    if out is None:
+        out = torch.empty((T, DIM), dtype=cfg.torch_dtype, device=tokens.device)
+    if tuple(out.shape) != (T, DIM):
+        raise ValueError(f"out must be [{T}, {DIM}]")
+    _check("ngram_embed_fwd", lib().ngram_embed_fwd(
+        ctypes.byref(cfg), _dev(W_b, "W_b", cfg.torch_dtype), _dev(W_t, "W_t", cfg.torch_dtype),
+        _dev(tokens, "tokens", torch.int32), T, _dev(out, "out", cfg.torch_dtype), _ws(ws), _stream()))
+    return out
+
+
+def embed_bwd_accum(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: torch.Tensor):
+    T = tokens.numel()
+    if dY.shape != (T, DIM):
+        raise ValueError(f"dY must be [{T}, {DIM}], got {tuple(dY.shape)}")
+    _check("ngram_embed_bwd_accum", lib().ngram_embed_bwd_accum(
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", torch.float32),
+        T, _stream()))
+
+
+def window_reduce(cfg: NgramConfig, ws: Workspace):
+    _check("ngram_window_reduce", lib().ngram_window_reduce(ctypes.byref(cfg), ws.ptr, _stream()))
+
+
+def sparse_step(cfg: NgramConfig, ws: Workspace, W_b, W_t, v_b, v_t, t_last_b, t_last_t, t: int,
+                lr: float, beta2: float, eps: float):
+    dt = cfg.torch_dtype
+    _check_tables(cfg, W_b, W_t)
+    _check_state(cfg, v_b, v_t, t_last_b, t_last_t)
+    _check("ngram_sparse_step", lib().ngram_sparse_step(
+        ctypes.byref(cfg), ws.ptr, _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt),
+        _dev(v_b, "v_b", torch.float32), _dev(v_t, "v_t", torch.float32),
+        _dev(t_last_b, "t_last_b", torch.int32), _dev(t_last_t, "t_last_t", torch.int32),
+        int(t), float(lr), float(beta2), float(eps), _stream()))
+
+
+def window_export(cfg: NgramConfig, ws: Workspace, channel: int, with_grad: bool = True):
+    """(rows int64 [n], G float32 [n, 768] or None) of the current window.
+    Synchronises the stream to read n."""
+    cap = cfg.window_capacity
+    dev = ws.tensor.device
+    rows = torch.empty(cap, dtype=torch.int32, device=dev)
+    G = torch.empty((cap, DIM), dtype=torch.float32, device=dev) if with_grad else None
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check("ngram_window_export", lib().ngram_window_export(
+        ctypes.byref(cfg), ws.ptr, int(channel), rows.data_ptr(),
+        None if G is None else G.data_ptr(), cap, cnt.data_ptr(), _stream()))
+    n = int(cnt.item())
+    n = min(n, cap)
+    r = rows[:n].to(torch.int64) & 0xFFFFFFFF
+    return r, (G[:n] if G is not None else None)
+
+
+def device_status(cfg: NgramConfig, ws: Workspace, clear: bool = False) -> int:
+    f = ctypes.c_uint32()
+    _check("ngram_device_status", lib().ngram_device_status(
+        ctypes.byref(cfg), ws.ptr, ctypes.byref(f), int(bool(clear)), _stream()))
+    return int(f.value)

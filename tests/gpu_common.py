@@ -1,0 +1,135 @@
+"""GPU-side helpers shared by the GPU tests (tables, state snapshots, a window
+driver that checks every step against the oracle).  Test infrastructure."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import helpers
+import oracle
+from sparse_hashed_gram_amd import synth
+
+
+def ng():
+    from sparse_hashed_gram_amd import ngram
+    return ngram
+
+
+def device_table(R: int, dtype: str, seed: int, chunk: int = 1 << 20) -> torch.Tensor:
+    """N(0, 0.02) table generated on the device in row chunks."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    W = torch.empty((R, 768), dtype=tdt, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for s in range(0, R, chunk):
+        e = min(R, s + chunk)
+        W[s:e] = (torch.randn((e - s, 768), generator=g, device="cuda") * 0.02).to(tdt)
+    return W
+
+
+def host_rows(W: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    """Rows of a device table as numpy (float32, or uint16 bf16 bits)."""
+    idx = torch.from_numpy(np.ascontiguousarray(rows, np.int64)).cuda()
+    x = W.index_select(0, idx)
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()
+
+
+def host_vec(x: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    idx = torch.from_numpy(np.ascontiguousarray(rows, np.int64)).cuda()
+    return x.index_select(0, idx).cpu().numpy()
+
+
+class State:
+    """Tables and optimizer state of both channels on the device."""
+
+    def __init__(self, cfg, W_b, W_t):
+        self.cfg = cfg
+        self.W = [W_b, W_t]
+        self.v = [torch.zeros(cfg.rows[c], dtype=torch.float32, device="cuda") for c in range(2)]
+        self.tl = [torch.zeros(cfg.rows[c], dtype=torch.int32, device="cuda") for c in range(2)]
+
+    def clone(self):
+        s = State(self.cfg, self.W[0].clone(), self.W[1].clone())
+        s.v = [x.clone() for x in self.v]
+        s.tl = [x.clone() for x in self.tl]
+        return s
+
+    def step(self, ws, t, lr, beta2, eps):
+        ng().sparse_step(self.cfg, ws, self.W[0], self.W[1], self.v[0], self.v[1], self.tl[0],
+                         self.tl[1], t, lr, beta2, eps)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2),
+                 sample_untouched=512, keep_rows=None, rng_seed=0):
+    """Feeds one window (lists of numpy tokens / dY) through the GPU path,
+    checks the window gradient, the touched sets and the step against the
+    oracle, and a sample of untouched rows for bitwise stability."""
+    N = ng()
+    cfg = st.cfg
+    for tok, dy in zip(toks, dys):
+        N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
+    N.window_reduce(cfg, ws)
+    orc = helpers.oracle_window(cfg.vocab, cfg.eos_id, (cfg.rows[0], cfg.rows[1]), toks, dys,
+                                seeds, keep_rows=keep_rows)
+    rs = np.random.default_rng(rng_seed)
+    touched_all = []
+    snaps = []
+    for c in range(2):
+        rows_g, G_g = N.window_export(cfg, ws, c)
+        rows_g = rows_g.cpu().numpy()
+        G_g = G_g.cpu().numpy()
+        assert len(np.unique(rows_g)) == len(rows_g), "duplicate rows in the window"
+        order = np.argsort(rows_g, kind="stable")
+        rows_g, G_g = rows_g[order], G_g[order]
+        touched, G_o, A_o = orc[c]
+        if keep_rows is None:
+            np.testing.assert_array_equal(rows_g, touched)
+            G_cmp = G_g
+        else:
+            # the oracle saw only the sampled rows: they must all be touched
+            pos = np.searchsorted(rows_g, touched)
+            assert np.all(pos < len(rows_g)) and np.array_equal(rows_g[pos], touched)
+            G_cmp = G_g[pos]
+        helpers.assert_grad_close(G_cmp, G_o, A_o)
+        touched_all.append(rows_g)
+        # state snapshot of the rows the oracle will step
+        Wb = host_rows(st.W[c], touched)
+        vb = host_vec(st.v[c], touched)
+        tb = host_vec(st.tl[c], touched)
+        # untouched sample
+        cand = rs.integers(0, cfg.rows[c], size=4 * sample_untouched)
+        cand = np.setdiff1d(cand, rows_g)[:sample_untouched]
+        snaps.append((touched, G_o, Wb, vb, tb, cand, host_rows(st.W[c], cand),
+                      host_vec(st.v[c], cand), host_vec(st.tl[c], cand)))
+    st.step(ws, t, lr, beta2, eps)
+    for c in range(2):
+        touched, G_o, Wb, vb, tb, cand, Wc, vc, tc = snaps[c]
+        W_o, v_o, t_o = oracle.sparse_step(G_o, Wb, vb, tb, t, lr, beta2, eps)
+        W_g = host_rows(st.W[c], touched)
+        v_g = host_vec(st.v[c], touched)
+        t_g = host_vec(st.tl[c], touched)
+        np.testing.assert_array_equal(t_g, t_o)
+        helpers.assert_v_close(v_g, v_o)
+        helpers.assert_rows_close(W_g, W_o, Wb, dtype)
+        np.testing.assert_array_equal(host_rows(st.W[c], cand), Wc)
+        np.testing.assert_array_equal(host_vec(st.v[c], cand), vc)
+        np.testing.assert_array_equal(host_vec(st.tl[c], cand), tc)
+    # the window is empty afterwards
+    for c in range(2):
+        r, _ = N.window_export(cfg, ws, c, with_grad=False)
+        assert len(r) == 0
+    return touched_all
+
+
+def window_inputs(w, first_step, T=None, n=4, tok_fn=None):
+    toks, dys = [], []
+    for s in range(first_step, first_step + n):
+        toks.append(synth.tokens(w, s, T) if tok_fn is None else tok_fn(s))
+        dys.append(synth.dY(w, s, len(toks[-1])))
+    return toks, dys

@@ -1,0 +1,109 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host (before any HIP call,
+so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ngram.h")
+
+
+@pytest.fixture(scope="module")
+def N():
+    from sparse_hashed_gram_amd import ngram
+    return ngram
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ngram_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(N):
+    names = _declared()
+    assert len(names) >= 12
+    L = ctypes.CDLL(N._LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in ngram.h but not exported"
+
+
+def test_version_and_status_strings(N):
+    assert N.lib().ngram_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert N.status_string(s) not in ("", "unknown status")
+    assert N.status_string(-99) == "unknown status"
+
+
+def _good(N, **kw):
+    args = dict(vocab=50304, eos_id=50256, rows=(4096, 4096), dtype="f32", max_tokens=2048)
+    args.update(kw)
+    return N.config(**args)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
+    ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
+    ("mode", 2), ("window_rows", -1)])
+def test_config_rejects(N, field, value):
+    c = _good(N)
+    setattr(c, field, value)
+    assert N.config_check(c) == -3
+
+
+def test_config_rejects_rows(N):
+    for r in (0, -1, 2**31):
+        c = _good(N)
+        c.rows[1] = r
+        assert N.config_check(c) == -3
+    c = _good(N, max_tokens=1 << 28, accum_steps=8, mode="burst")
+    assert N.config_check(c) == -3       # burst positions must fit 30 bits
+    assert N.config_check(_good(N, max_tokens=1 << 28, accum_steps=8)) == 0
+
+
+def test_workspace_bytes_scale(N):
+    small = N.workspace_bytes(_good(N))
+    full = N.workspace_bytes(_good(N, rows=(42_300_000, 42_300_000), dtype="bf16", max_tokens=393_216))
+    burst = N.workspace_bytes(_good(N, rows=(42_300_000, 42_300_000), dtype="bf16", max_tokens=393_216,
+                                    mode="burst"))
+    assert small < 64 << 20
+    # window accumulator 2 x 1,572,864 x 3 KB dominates; slot maps 2 x 169 MB
+    assert 9.8e9 < full < 10.5e9
+    # burst keeps the window's dY (1,572,864 x 3 KB more)
+    assert burst - full > 4.8e9
+
+
+def test_host_rejections_enqueue_nothing(N):
+    L = N.lib()
+    c = _good(N)
+    cp = ctypes.byref(c)
+    fake = ctypes.c_void_p(1 << 40)           # never dereferenced: rejected first
+    # T out of range
+    assert L.ngram_hash(cp, fake, 4096, fake, None, None) == -4
+    assert L.ngram_hash(cp, fake, -1, fake, None, None) == -4
+    # null pointers
+    assert L.ngram_hash(cp, None, 5, fake, None, None) == -1
+    assert L.ngram_embed_fwd(cp, None, fake, fake, 5, fake, None, None) == -1
+    assert L.ngram_embed_bwd_accum(cp, None, fake, fake, 5, None) == -1
+    # misalignment
+    assert L.ngram_embed_fwd(cp, ctypes.c_void_p((1 << 40) + 8), fake, fake, 5, fake, None, None) == -2
+    assert L.ngram_workspace_init(cp, ctypes.c_void_p((1 << 40) + 128), 1 << 30, None) == -2
+    # workspace too small
+    assert L.ngram_workspace_init(cp, fake, 1024, None) == -4
+    # step arguments
+    ok = [fake] * 7
+    assert L.ngram_sparse_step(cp, *ok, 0, 0.01, 0.95, 1e-8, None) == -5      # t < 1
+    assert L.ngram_sparse_step(cp, *ok, 1, 0.01, 1.0, 1e-8, None) == -5       # beta2 = 1
+    assert L.ngram_sparse_step(cp, *ok, 1, 0.01, -0.1, 1e-8, None) == -5
+    assert L.ngram_sparse_step(cp, *ok, 1, 0.01, 0.95, 0.0, None) == -5       # eps = 0
+    assert L.ngram_sparse_step(cp, *ok, 1, float("nan"), 0.95, 1e-8, None) == -5
+    assert L.ngram_sparse_step(cp, *ok, 1, 0.01, 0.95, float("inf"), None) == -5
+    # export arguments
+    assert L.ngram_window_export(cp, fake, 2, fake, None, 10, fake, None) == -5
+    assert L.ngram_window_export(cp, fake, 0, fake, None, -1, fake, None) == -4
+    # bad config short-circuits everything
+    c.dim = 7
+    assert L.ngram_embed_fwd(cp, fake, fake, fake, 5, fake, None, None) == -3

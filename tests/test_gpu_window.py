@@ -1,0 +1,215 @@
+"""GPU parity of the backward (sort + dedupe + signed segment reduction with
+4-step accumulation) and the lazy sparse row-wise step against the oracle,
+in both the spread and the burst mode (amund.blog, The four improvements,
+item 4), through the C ABI.
+
+Tolerances: touched sets and t_last exact; window gradients per element
+within 1e-5 of sum |s dY|; v within 1e-5 relative; bf16 rows within 1 ulp;
+fp32 rows within 1e-5 of the update plus 1 ulp.  Untouched rows must stay
+bitwise unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import helpers
+from gpu_common import State, check_window, device_table, ng, to_dev, window_inputs
+from sparse_hashed_gram_amd import synth, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny_state(cfg, w):
+    return State(cfg, to_dev(synth.init_rows(w, 0, w.rows[0])),
+                 to_dev(synth.init_rows(w, 1, w.rows[1])))
+
+
+@pytest.mark.parametrize("mode", ["spread", "burst"])
+def test_tiny_workload_two_windows(mode):
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode=mode)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    for win in range(w.steps // w.accum_steps):
+        toks, dys = window_inputs(w, win * w.accum_steps)
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "f32")
+    assert N.device_status(cfg, ws) == 0
+
+
+@pytest.mark.parametrize("mode", ["spread", "burst"])
+def test_small_table_long_gaps(mode):
+    # 64-token micro-steps into 3000-row tables: rows skip windows, so the
+    # retroactive beta2^k with k > 1 is exercised; ragged T per micro-step.
+    w = workloads.TINY
+    N = ng()
+    rows = (2000, 3000)
+    cfg = N.config(w.vocab, w.eos_id, rows, "f32", max_tokens=97, mode=mode)
+    st = State(cfg, to_dev(synth.init_rows(w, 0, rows[0])), to_dev(synth.init_rows(w, 1, rows[1])))
+    ws = N.Workspace(cfg)
+    for win in range(8):
+        Ts = [64, 97, 1, 33]
+        toks = [synth.tokens(w, 100 + 4 * win + m, Ts[m]) for m in range(4)]
+        dys = [synth.dY(w, 100 + 4 * win + m, Ts[m]) for m in range(4)]
+        check_window(st, ws, toks, dys, win + 1, 0.02, 0.9, 1e-6, "f32")
+    gaps = st.tl[0].cpu().numpy()
+    assert len(np.unique(gaps[gaps > 0])) > 3
+
+
+@pytest.mark.parametrize("mode", ["spread", "burst"])
+def test_shard_workload_bf16(mode):
+    w = workloads.SHARD
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=w.tokens_per_step, mode=mode)
+    st = State(cfg, device_table(w.rows[0], "bf16", 21), device_table(w.rows[1], "bf16", 22))
+    ws = N.Workspace(cfg)
+    for win in range(3):
+        toks, dys = window_inputs(w, 4 * win)
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "bf16")
+    assert N.device_status(cfg, ws) == 0
+    del st, ws
+    torch.cuda.empty_cache()
+
+
+def test_collision_skew_at_shard_scale():
+    # Zipf 1.4 with 20% of tokens from a 256-id hot set: segments of thousands
+    # of keys, so the cross-chunk partial sums and the fix-up pass are used.
+    w = workloads.COLLISION
+    N = ng()
+    rows = workloads.SHARD.rows
+    T = 49_152
+    cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=T)
+    st = State(cfg, device_table(rows[0], "bf16", 31), device_table(rows[1], "bf16", 32))
+    ws = N.Workspace(cfg)
+    for win in range(2):
+        toks, dys = window_inputs(w, 4 * win, T=T)
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "bf16")
+    del st, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 127, 128, 129, 4096, 20_000])
+def test_single_hot_row(T):
+    # every position is the same bigram and trigram (after the first two):
+    # one segment spanning up to hundreds of 64-key chunks
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    tok = np.full(T, 42, np.int32)
+    toks = [tok] * 4
+    dys = [synth.dY(w, 500 + m, T) for m in range(4)]
+    check_window(st, ws, toks, dys, 1, w.lr, w.beta2, w.eps, "f32")
+
+
+def test_spread_equals_burst():
+    # same window in both modes from the same state: equal within tolerance
+    w = workloads.SHARD
+    N = ng()
+    T = 49_152
+    cfgs = {m: N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode=m)
+            for m in ("spread", "burst")}
+    base = State(cfgs["spread"], device_table(w.rows[0], "bf16", 41), device_table(w.rows[1], "bf16", 42))
+    toks, dys = window_inputs(w, 8)
+    out = {}
+    for m, cfg in cfgs.items():
+        st = base.clone()
+        st.cfg = cfg
+        ws = N.Workspace(cfg)
+        for tok, dy in zip(toks, dys):
+            N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
+        N.window_reduce(cfg, ws)
+        ex = [N.window_export(cfg, ws, c) for c in range(2)]
+        st.step(ws, 1, w.lr, w.beta2, w.eps)
+        out[m] = (ex, st)
+    for c in range(2):
+        (rs, Gs), (rb, Gb) = out["spread"][0][c], out["burst"][0][c]
+        os_, ob = torch.argsort(rs), torch.argsort(rb)
+        assert torch.equal(rs[os_], rb[ob])
+        orc = helpers.oracle_window(w.vocab, w.eos_id, w.rows, toks, dys)[c]
+        helpers.assert_grad_close(Gs[os_].cpu().numpy(), Gb[ob].cpu().numpy(), orc[2])
+        rows = rs[os_]
+        Ws = out["spread"][1].W[c].index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+        Wb = out["burst"][1].W[c].index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert helpers.ulp_bf16(Ws, Wb).max() <= 1
+        assert torch.equal(out["spread"][1].tl[c], out["burst"][1].tl[c])
+
+
+@pytest.mark.parametrize("mode", ["spread", "burst"])
+def test_bitwise_deterministic(mode):
+    w = workloads.SHARD
+    N = ng()
+    T = 49_152
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode=mode)
+    base = State(cfg, device_table(w.rows[0], "bf16", 51), device_table(w.rows[1], "bf16", 52))
+    toks, dys = window_inputs(workloads.COLLISION, 0, T=T)
+    res = []
+    for rep in range(2):
+        st = base.clone()
+        ws = N.Workspace(cfg)
+        for tok, dy in zip(toks, dys):
+            N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
+        N.window_reduce(cfg, ws)
+        ex = [N.window_export(cfg, ws, c) for c in range(2)]
+        st.step(ws, 3, w.lr, w.beta2, w.eps)
+        res.append((ex, st))
+    for c in range(2):
+        assert torch.equal(res[0][0][c][0], res[1][0][c][0])
+        assert torch.equal(res[0][0][c][1].view(torch.int32), res[1][0][c][1].view(torch.int32))
+        assert torch.equal(res[0][1].W[c].view(torch.int16), res[1][1].W[c].view(torch.int16))
+        assert torch.equal(res[0][1].v[c].view(torch.int32), res[1][1].v[c].view(torch.int32))
+
+
+def test_empty_window_step_is_noop():
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=64)
+    st = _tiny_state(cfg, w)
+    before = st.clone()
+    ws = N.Workspace(cfg)
+    N.embed_bwd_accum(cfg, ws, torch.zeros(0, dtype=torch.int32, device="cuda"),
+                      torch.zeros((0, 768), device="cuda"))
+    st.step(ws, 1, 0.01, 0.95, 1e-8)
+    for c in range(2):
+        assert torch.equal(st.W[c], before.W[c])
+        assert torch.equal(st.v[c], before.v[c])
+        assert torch.equal(st.tl[c], before.tl[c])
+    assert N.device_status(cfg, ws) == 0
+
+
+def test_window_full_flag():
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=2048, window_rows=100)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    tok = synth.tokens(w, 0)
+    N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(synth.dY(w, 0)))
+    rows, G = N.window_export(cfg, ws, 0)
+    assert len(rows) == 100
+    st.step(ws, 1, 0.01, 0.95, 1e-8)
+    assert N.device_status(cfg, ws, clear=True) & N.FLAG_WINDOW_FULL
+    assert int((st.tl[0] == 1).sum()) == 100
+
+
+def test_stash_full_flag_burst():
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=256, accum_steps=2, mode="burst")
+    ws = N.Workspace(cfg)
+    for s in range(3):   # one micro-step more than the window holds
+        N.embed_bwd_accum(cfg, ws, to_dev(synth.tokens(w, s, 256)), to_dev(synth.dY(w, s, 256)))
+    assert N.device_status(cfg, ws, clear=True) & N.FLAG_STASH_FULL
+
+
+def test_step_order_flag():
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=64)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    for t in (5, 5):   # the second step does not advance t
+        N.embed_bwd_accum(cfg, ws, to_dev(synth.tokens(w, 0, 64)), to_dev(synth.dY(w, 0, 64)))
+        st.step(ws, t, 0.01, 0.95, 1e-8)
+    assert N.device_status(cfg, ws, clear=True) & N.FLAG_STEP_ORDER
