@@ -79,6 +79,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
                                 seeds, keep_rows=keep_rows)
     rs = np.random.default_rng(rng_seed)
     touched_all = []
+    grads = []
     snaps = []
     for c in range(2):
         rows_g, G_g = N.window_export(cfg, ws, c)
@@ -98,6 +99,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
             G_cmp = G_g[pos]
         helpers.assert_grad_close(G_cmp, G_o, A_o)
         touched_all.append(rows_g)
+        grads.append(G_g)
         # state snapshot of the rows the oracle will step
         Wb = host_rows(st.W[c], touched)
         vb = host_vec(st.v[c], touched)
@@ -105,18 +107,19 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
         # untouched sample
         cand = rs.integers(0, cfg.rows[c], size=4 * sample_untouched)
         cand = np.setdiff1d(cand, rows_g)[:sample_untouched]
-        snaps.append((touched, G_o, Wb, vb, tb, cand, host_rows(st.W[c], cand),
+        snaps.append((touched, G_o, A_o, Wb, vb, tb, cand, host_rows(st.W[c], cand),
                       host_vec(st.v[c], cand), host_vec(st.tl[c], cand)))
     st.step(ws, t, lr, beta2, eps)
     for c in range(2):
-        touched, G_o, Wb, vb, tb, cand, Wc, vc, tc = snaps[c]
+        touched, G_o, A_o, Wb, vb, tb, cand, Wc, vc, tc = snaps[c]
         W_o, v_o, t_o = oracle.sparse_step(G_o, Wb, vb, tb, t, lr, beta2, eps)
         W_g = host_rows(st.W[c], touched)
         v_g = host_vec(st.v[c], touched)
         t_g = host_vec(st.tl[c], touched)
         np.testing.assert_array_equal(t_g, t_o)
-        helpers.assert_v_close(v_g, v_o)
-        helpers.assert_rows_close(W_g, W_o, Wb, dtype)
+        helpers.assert_v_close(v_g, v_o, G=G_o, absbound=A_o, beta2=beta2)
+        helpers.assert_rows_close(W_g, W_o, Wb, dtype, G=G_o, absbound=A_o, v_orc=v_o, lr=lr,
+                                  eps=eps)
         np.testing.assert_array_equal(host_rows(st.W[c], cand), Wc)
         np.testing.assert_array_equal(host_vec(st.v[c], cand), vc)
         np.testing.assert_array_equal(host_vec(st.tl[c], cand), tc)
@@ -124,7 +127,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
     for c in range(2):
         r, _ = N.window_export(cfg, ws, c, with_grad=False)
         assert len(r) == 0
-    return touched_all
+    return touched_all, grads, orc
 
 
 def window_inputs(w, first_step, T=None, n=4, tok_fn=None):

@@ -4,9 +4,11 @@ in both the spread and the burst mode (amund.blog, The four improvements,
 item 4), through the C ABI.
 
 Tolerances: touched sets and t_last exact; window gradients per element
-within 1e-5 of sum |s dY|; v within 1e-5 relative; bf16 rows within 1 ulp;
-fp32 rows within 1e-5 of the update plus 1 ulp.  Untouched rows must stay
-bitwise unchanged.
+within 1e-5 of sum |s dY|; v within 1e-5 relative plus what that gradient
+error can move (1 - beta2) mean(G^2); table rows within one ulp of the result
+plus 1e-5 of the update plus the gradient error carried through
+lr G / (sqrt(v) + eps) (which matters only where W - update cancels).
+Untouched rows must stay bitwise unchanged.
 """
 import numpy as np
 import pytest
@@ -104,36 +106,35 @@ def test_single_hot_row(T):
 
 
 def test_spread_equals_burst():
-    # same window in both modes from the same state: equal within tolerance
+    # The same window in both modes from the same state: each matches the
+    # oracle, and the two agree with each other within twice the tolerance.
     w = workloads.SHARD
     N = ng()
     T = 49_152
-    cfgs = {m: N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode=m)
-            for m in ("spread", "burst")}
-    base = State(cfgs["spread"], device_table(w.rows[0], "bf16", 41), device_table(w.rows[1], "bf16", 42))
+    base = State(N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T),
+                 device_table(w.rows[0], "bf16", 41), device_table(w.rows[1], "bf16", 42))
     toks, dys = window_inputs(w, 8)
-    out = {}
-    for m, cfg in cfgs.items():
+    res = {}
+    for m in ("spread", "burst"):
+        cfg = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode=m)
         st = base.clone()
         st.cfg = cfg
         ws = N.Workspace(cfg)
-        for tok, dy in zip(toks, dys):
-            N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
-        N.window_reduce(cfg, ws)
-        ex = [N.window_export(cfg, ws, c) for c in range(2)]
-        st.step(ws, 1, w.lr, w.beta2, w.eps)
-        out[m] = (ex, st)
+        rows, grads, orc = check_window(st, ws, toks, dys, 1, w.lr, w.beta2, w.eps, "bf16")
+        res[m] = (rows, grads, orc, st)
     for c in range(2):
-        (rs, Gs), (rb, Gb) = out["spread"][0][c], out["burst"][0][c]
-        os_, ob = torch.argsort(rs), torch.argsort(rb)
-        assert torch.equal(rs[os_], rb[ob])
-        orc = helpers.oracle_window(w.vocab, w.eos_id, w.rows, toks, dys)[c]
-        helpers.assert_grad_close(Gs[os_].cpu().numpy(), Gb[ob].cpu().numpy(), orc[2])
-        rows = rs[os_]
-        Ws = out["spread"][1].W[c].index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
-        Wb = out["burst"][1].W[c].index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
-        assert helpers.ulp_bf16(Ws, Wb).max() <= 1
-        assert torch.equal(out["spread"][1].tl[c], out["burst"][1].tl[c])
+        rs, Gs, orc, ss = res["spread"][0][c], res["spread"][1][c], res["spread"][2][c], res["spread"][3]
+        rb, Gb, sb = res["burst"][0][c], res["burst"][1][c], res["burst"][3]
+        np.testing.assert_array_equal(rs, rb)
+        helpers.assert_grad_close(Gs, Gb, 2 * orc[2])
+        assert torch.equal(ss.tl[c], sb.tl[c])
+        idx = torch.from_numpy(rs).cuda()
+        Ws = ss.W[c].index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        Wb_ = sb.W[c].index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        W0 = base.W[c].index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+        v = sb.v[c].index_select(0, idx).cpu().numpy()
+        err, lim = helpers.rows_limit(Ws, Wb_, W0, "bf16", 2 * orc[2], v, w.lr, w.eps)
+        assert np.all(err <= 2 * lim)
 
 
 @pytest.mark.parametrize("mode", ["spread", "burst"])
