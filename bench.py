@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the hashed bigram + trigram embedding path on one MI355X.
+
+One step = one accumulation window of the whole hot path: 4 micro-steps of
+(context + hash + signed gather-sum forward, then backward: sort, dedupe,
+segment reduction into the window) followed by one fused lazy sparse step on
+every touched row.  Workload (default): the full 84.6M-row table (2 x
+42,300,000 x 768 bf16, about 130 GB) resident on one GPU, 393,216 tokens per
+micro-step drawn from Zipf(1.1) over a 50,304-id vocabulary with EoS-aligned
+documents (synthetic stand-in for FineWeb), upstream gradients N(0, 1).
+
+Prints one JSON line.  `value` is the window's tokens per second through the
+whole path with all inputs resident in HBM; per-kernel-group times come from
+HIP events recorded on the launch stream around each group inside the timed
+region; `roofline` reports the dominant group's algorithmic bytes per launch
+over its mean launch time against the 8 TB/s HBM3E peak; `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "updated rows/s + fwd tokens/s; achieved HBM GB/s vs peak, 84.6M-row table"
+HBM_PEAK_GBPS = 8000.0
+ROW_BF16 = 768 * 2
+ROW_F32 = 768 * 4
+GROUPS = ("fwd", "sort", "reduce", "step", "stash")
+KERNEL_SRC = {"fwd": "ngram_fwd.hip", "sort": "ngram_reduce.hip", "reduce": "ngram_reduce.hip",
+              "step": "ngram_step.hip", "stash": "ngram_fwd.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=6, help="timed windows")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed windows")
+    ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
+    ap.add_argument("--mode", default="spread", choices=["spread", "burst"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=65_536,
+                    help="tokens per micro-step in the oracle's bounded sample (0 = all)")
+    ap.add_argument("--distinct-windows", type=int, default=4,
+                    help="distinct token windows cycled through (inputs stay resident)")
+    return ap.parse_args()
+
+
+def workload(name):
+    from sparse_hashed_gram_amd import workloads
+    return {"tiny": workloads.TINY, "shard": workloads.SHARD, "full": workloads.FULL,
+            "collision": workloads.COLLISION}[name]
+
+
+def device_table(torch, R, dtype, seed, chunk=1 << 21):
+    W = torch.empty((R, 768), dtype=dtype, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for s in range(0, R, chunk):
+        e = min(R, s + chunk)
+        W[s:e] = (torch.randn((e - s, 768), generator=g, device="cuda") * 0.02).to(dtype)
+    return W
+
+
+def window_stats(torch, N, cfg, toks):
+    """Per micro-step and channel: distinct rows and rows new to the window;
+    distinct rows of the whole window.  Uses the library's own hash."""
+    steps = []
+    seen = [None, None]
+    for tok in toks:
+        idx = N.hash(cfg, tok)
+        per = []
+        for c in range(2):
+            u = torch.unique(idx[c] & 0x7FFFFFFF)
+            new = int(u.numel()) if seen[c] is None else int((~torch.isin(u, seen[c])).sum())
+            seen[c] = u if seen[c] is None else torch.unique(torch.cat([seen[c], u]))
+            per.append((int(u.numel()), new))
+        steps.append(per)
+    return steps, [int(s.numel()) for s in seen]
+
+
+def algorithmic_bytes(w, T, stats, row_bytes):
+    """Bytes each kernel group must move by definition."""
+    steps, uwin = stats
+    fwd = T * (3 * row_bytes + 4)                       # 2 rows read + 1 row written + id
+    reduce_ = []
+    for per in steps:
+        b = 0
+        for (u, new) in per:
+            b += T * ROW_F32                            # every key reads its dY row
+            b += new * ROW_F32 + (u - new) * 2 * ROW_F32  # window row: write new / RMW old
+        reduce_.append(b)
+    sort = 2 * T * 4 * 2 * 4                            # keys+vals, read+write, ~4 passes
+    step = sum(uwin) * (2 * row_bytes + ROW_F32 + 8 + 8 + 4)
+    stash = T * (2 * ROW_F32 + 4 + 8)                   # dY row copied, id read, 2 indices written
+    return {"fwd": fwd, "reduce": float(np.mean(reduce_)), "sort": sort, "step": step,
+            "stash": stash}
+
+
+def src_hash(name):
+    p = os.path.join(ROOT, "sparse_hashed_gram_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic(group, per_launch_units):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the kernel source as it is now; else None."""
+    p = os.path.join(ROOT, "profiles", f"pmc_{group}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+        if d.get("source_sha256_16") != src_hash(KERNEL_SRC[group]):
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, toks_np, T_sample, dys_fn):
+    """The oracle on a bounded sample of the same workload: one window of
+    4 micro-steps of T_sample tokens (hash, forward, window gradient, sparse
+    step on touched rows).  Table rows are a snapshot of the rows it touches."""
+    import oracle
+    toks = [t[:T_sample] for t in toks_np]
+    dys = [dys_fn(m, T_sample) for m in range(len(toks))]
+    rows = [oracle.ngram_rows(t, w.vocab, w.eos_id, w.rows) for t in toks]
+    rs = np.random.default_rng(0)
+    ids = []
+    snaps = []
+    for c in range(2):
+        u = np.unique(np.concatenate([r[2 * c] for r in rows]))
+        ids.append(u)
+        snaps.append(rs.integers(0x3C00, 0x3CFF, size=(len(u), 768)).astype(np.uint16)
+                     ^ (rs.integers(0, 2, size=(len(u), 768)).astype(np.uint16) << 15))
+    t0 = time.perf_counter()
+    for m in range(len(toks)):
+        rb, nb, rt, nt, _ = oracle.ngram_rows(toks[m], w.vocab, w.eos_id, w.rows)
+        oracle.forward(snaps[0], snaps[1], rb, nb, rt, nt, ids_b=ids[0], ids_t=ids[1],
+                       out_dtype="bf16")
+    dY = np.concatenate(dys)
+    n_upd = 0
+    for c in range(2):
+        r = np.concatenate([x[2 * c] for x in rows])
+        n = np.concatenate([x[2 * c + 1] for x in rows])
+        touched, G = oracle.window_grad(r, n, dY)
+        pos = np.searchsorted(ids[c], touched)
+        oracle.sparse_step(G, snaps[c][pos], np.zeros(len(touched), np.float32),
+                           np.zeros(len(touched), np.int32), 1, w.lr, w.beta2, w.eps)
+        n_upd += len(touched)
+    el = time.perf_counter() - t0
+    ntok = sum(len(t) for t in toks)
+    return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "seconds": el, "updated_rows_per_s": n_upd / el,
+            "sample": (f"one window: 4 micro-steps x {T_sample} tokens of the same stream "
+                       f"(hash, forward, window gradient, sparse step on {n_upd} touched rows; "
+                       f"table rows as a snapshot of the touched rows)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "table lives whole on one MI355X and there is no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_hashed_gram_amd import ngram as N
+    from sparse_hashed_gram_amd import synth
+    from sparse_hashed_gram_amd.hipevents import Event
+
+    w = workload(args.workload)
+    T = w.tokens_per_step
+    A = w.accum_steps
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    row_bytes = ROW_BF16 if w.dtype == "bf16" else ROW_F32
+    torch.cuda.set_device(0)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode)
+
+    W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(2)]
+    v = [torch.zeros(w.rows[c], dtype=torch.float32, device="cuda") for c in range(2)]
+    tl = [torch.zeros(w.rows[c], dtype=torch.int32, device="cuda") for c in range(2)]
+    ws = N.Workspace(cfg)
+    out = torch.empty((T, 768), dtype=tdt, device="cuda")
+    nwin = max(1, args.distinct_windows)
+    toks_np = [[synth.tokens(w, win * A + m) for m in range(A)] for win in range(nwin)]
+    toks = [[torch.from_numpy(t).cuda() for t in win] for win in toks_np]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dys = [torch.randn((T, 768), generator=g, device="cuda") for _ in range(A)]
+    stats = [window_stats(torch, N, cfg, toks[k]) for k in range(nwin)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    t_step = [0]
+    burst = args.mode == "burst"
+    gid = {"fwd": N.PROF_FWD, "sort": N.PROF_SORT, "reduce": N.PROF_REDUCE, "step": N.PROF_STEP,
+           "stash": N.PROF_STASH}
+
+    def arm(ev, groups):
+        if ev is None:
+            return
+        for grp in groups:
+            a, b = Event(), Event()
+            ev[grp].append((a, b))
+            N.profile_events(gid[grp], a.handle, b.handle)
+
+    def disarm():
+        for k in range(N.PROF_GROUPS):
+            N.profile_events(k, None, None)
+
+    def run_window(k, ev=None):
+        for m in range(A):
+            arm(ev, ("fwd",))
+            N.embed_fwd(cfg, W[0], W[1], toks[k][m], out=out)
+            disarm()
+            arm(ev, ("stash",) if burst else ("sort", "reduce"))
+            N.embed_bwd_accum(cfg, ws, toks[k][m], dys[m])
+            disarm()
+        arm(ev, ("sort", "reduce", "step") if burst else ("step",))
+        t_step[0] += 1
+        N.sparse_step(cfg, ws, W[0], W[1], v[0], v[1], tl[0], tl[1], t_step[0], w.lr, w.beta2, w.eps)
+        disarm()
+
+    for i in range(args.warmup):
+        run_window(i % nwin)
+    torch.cuda.synchronize()
+
+    ev = {g_: [] for g_ in GROUPS}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_window(i % nwin, ev)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    flags = N.device_status(cfg, ws)
+    if flags:
+        print(f"bench.py: device flags {flags:#x} set", file=sys.stderr)
+        sys.exit(1)
+
+    used = [g_ for g_ in GROUPS if ev[g_]]
+    ms = {g_: float(np.mean([a.elapsed_ms(b) for a, b in ev[g_]])) for g_ in used}
+    per_step = {g_: len(ev[g_]) // args.steps for g_ in used}
+    timed_stats = [stats[i % nwin] for i in range(args.steps)]
+    bytes_ = [algorithmic_bytes(w, T, s, row_bytes) for s in timed_stats]
+    abytes = {g_: float(np.mean([b[g_] for b in bytes_])) for g_ in used}
+    if burst:   # one reduction of the whole window per step
+        abytes["reduce"] *= A
+        abytes["sort"] *= A
+    upd_rows = float(np.mean([sum(s[1]) for s in timed_stats]))
+    total_ms = {g_: ms[g_] * per_step[g_] for g_ in used}
+    dom = max([g_ for g_ in ("fwd", "reduce", "step") if g_ in used], key=lambda g_: total_ms[g_])
+    kernels = {}
+    for g_ in used:
+        gbps = abytes[g_] / (ms[g_] * 1e-3) / 1e9
+        kernels[g_] = {"ms_per_launch": round(ms[g_], 4), "launches_per_step": per_step[g_],
+                       "ms_per_step": round(total_ms[g_], 4),
+                       "algorithmic_bytes_per_launch": int(abytes[g_]),
+                       "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    traffic = pmc_traffic(dom, None)
+    achieved = abytes[dom] / (ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic}
+
+    res = {
+        "metric": METRIC,
+        "value": round(A * T * args.steps / el, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: Zipf token streams with EoS-aligned documents, N(0,1) upstream gradients",
+        "config": {"workload": w.name, "table_rows": w.rows[0] + w.rows[1], "dim": 768,
+                   "table_dtype": w.dtype, "tokens_per_micro_step": T, "accum_steps": A,
+                   "mode": args.mode, "global_batch": A * T},
+        "fwd_tokens_per_s": round(T / (ms["fwd"] * 1e-3), 1),
+        "updated_rows_per_s": round(upd_rows / (ms["step"] * 1e-3), 1),
+        "updated_rows_per_step": int(upd_rows),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del W, v, tl, ws, out, dys
+        torch.cuda.empty_cache()
+        Ts = T if args.cpu_tokens <= 0 else min(T, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(w, toks_np[0], Ts, lambda m, n: synth.dY(w, m, n))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -183,6 +183,21 @@ int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
                         uint32_t *rows, float *G, int64_t max_rows,
                         uint32_t *count, void *stream);
 
+/* Kernel groups for ngram_profile_events. */
+#define NGRAM_PROF_FWD 0    /* the forward gather-sum kernel              */
+#define NGRAM_PROF_SORT 1   /* key build, radix sort, heads and slots     */
+#define NGRAM_PROF_REDUCE 2 /* signed segment reduction + long-row fix-up */
+#define NGRAM_PROF_STEP 3   /* the fused sparse step (and window reset)   */
+#define NGRAM_PROF_STASH 4  /* burst mode: keeping a micro-step           */
+#define NGRAM_PROF_GROUPS 5
+
+/* Measurement hook for benchmarks and profilers: until changed, every call
+ * made by this host thread that launches kernels of `group` records
+ * `start_event` just before that group's first launch and `stop_event` just
+ * after its last one, on the call's stream (both are hipEvent_t; NULL stops
+ * recording).  Thread-local; never used by the library itself. */
+int ngram_profile_events(int group, void *start_event, void *stop_event);
+
 /* Synchronises `stream` and writes the sticky device flags to the host word
  * `flags`; clears them if `clear` is nonzero.  Not for use under capture. */
 int ngram_device_status(const ngram_config *cfg, const void *ws,

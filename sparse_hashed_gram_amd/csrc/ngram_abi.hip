@@ -13,6 +13,10 @@
 
 using namespace ngram;
 
+namespace ngram {
+thread_local ProfSlot g_prof[kProfGroups] = {};
+}
+
 namespace {
 
 constexpr uint64_t kAlign = 256;
@@ -299,6 +303,15 @@ int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, ui
     const WsLayout L = layout(cfg);
     return hip_status(launch_export(L, (const uint8_t *)ws, channel, rows, G, (uint32_t)max_rows, count,
                                     (hipStream_t)stream));
+}
+
+int ngram_profile_events(int group, void *start_event, void *stop_event)
+{
+    if (group < 0 || group >= kProfGroups)
+        return NGRAM_EARG;
+    g_prof[group].start = (hipEvent_t)start_event;
+    g_prof[group].stop = (hipEvent_t)stop_event;
+    return NGRAM_OK;
 }
 
 int ngram_device_status(const ngram_config *cfg, const void *ws, uint32_t *flags, int clear, void *stream)

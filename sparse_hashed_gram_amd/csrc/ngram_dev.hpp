@@ -139,6 +139,27 @@ struct WsLayout {
     bool burst;
 };
 
+// ------------------------------------------------------------- profiling
+// Optional event pairs per kernel group (ngram_profile_events); thread-local.
+
+struct ProfSlot {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+constexpr int kProfGroups = 5;
+extern thread_local ProfSlot g_prof[kProfGroups];
+
+inline void prof_begin(int group, hipStream_t s)
+{
+    if (g_prof[group].start)
+        (void)hipEventRecord(g_prof[group].start, s);
+}
+inline void prof_end(int group, hipStream_t s)
+{
+    if (g_prof[group].stop)
+        (void)hipEventRecord(g_prof[group].stop, s);
+}
+
 // ---------------------------------------------------------------- launchers
 // Implemented in the .hip files of this directory; all enqueue on `s`.
 

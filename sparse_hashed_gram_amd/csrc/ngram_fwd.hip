@@ -239,18 +239,21 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
     if (T == 0)
         return hipSuccess;
     const unsigned g = grid_for(T, kFwdTok);
+    prof_begin(NGRAM_PROF_FWD, s);
     if (dtype == NGRAM_DTYPE_BF16)
         fwd_kernel<2><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
                                                 (uint8_t *)out, flags);
     else
         fwd_kernel<4><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
                                                 (uint8_t *)out, flags);
+    prof_end(NGRAM_PROF_FWD, s);
     return hipGetLastError();
 }
 
 hipError_t launch_keys_from_tokens(const WsLayout &L, uint8_t *ws, const HashParams &hp,
                                    const int32_t *tok, int64_t T, hipStream_t s)
 {
+    prof_begin(NGRAM_PROF_SORT, s);
     keys_tokens_kernel<<<grid_for(T > 0 ? T : 1, 256), 256, 0, s>>>(
         tok, T, hp, reinterpret_cast<uint32_t *>(ws + L.keys[0]),
         reinterpret_cast<uint32_t *>(ws + L.vals[0]), L.nk, reinterpret_cast<WsHeader *>(ws + L.hdr));
@@ -261,16 +264,19 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
                         const float *dY, int64_t T, hipStream_t s)
 {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    prof_begin(NGRAM_PROF_STASH, s);
     if (T > 0)
         stash_kernel<<<grid_for(T, kStashTok), 256, 0, s>>>(
             tok, dY, T, hp, reinterpret_cast<uint32_t *>(ws + L.stash_idx),
             reinterpret_cast<float *>(ws + L.stash_dy), L.nk, hdr);
     stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, hdr);
+    prof_end(NGRAM_PROF_STASH, s);
     return hipGetLastError();
 }
 
 hipError_t launch_keys_from_stash(const WsLayout &L, uint8_t *ws, hipStream_t s)
 {
+    prof_begin(NGRAM_PROF_SORT, s);
     keys_stash_kernel<<<grid_for(L.nk, 256), 256, 0, s>>>(
         reinterpret_cast<const uint32_t *>(ws + L.stash_idx), L.nk,
         reinterpret_cast<uint32_t *>(ws + L.keys[0]), reinterpret_cast<uint32_t *>(ws + L.vals[0]),

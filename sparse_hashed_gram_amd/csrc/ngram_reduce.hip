@@ -572,8 +572,10 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host,
                          const float *dY, hipStream_t s)
 {
-    if (n_host == 0)
+    if (n_host == 0) {
+        prof_end(NGRAM_PROF_SORT, s);
         return hipSuccess;
+    }
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
@@ -607,6 +609,7 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     scan_kernel<<<2, 1024, 0, s>>>(sa.blk, nblk, hdr, (uint32_t)L.wrows);
     assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+    prof_end(NGRAM_PROF_SORT, s);
 
     RedArgs ra;
     ra.rows = sa.rows;
@@ -624,8 +627,10 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     ra.hdr = hdr;
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
     const uint32_t per_block = kRedThreads / kWave;
+    prof_begin(NGRAM_PROF_REDUCE, s);
     seg_reduce_kernel<<<dim3((nchunk + per_block - 1) / per_block, 2), kRedThreads, 0, s>>>(ra);
     fixup_kernel<<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    prof_end(NGRAM_PROF_REDUCE, s);
     return hipGetLastError();
 }
 

@@ -191,11 +191,13 @@ hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void
     a.eps = eps;
     const int64_t want = (L.wrows + 3) / 4;
     const unsigned gx = (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+    prof_begin(NGRAM_PROF_STEP, s);
     if (dtype == NGRAM_DTYPE_BF16)
         step_kernel<2><<<dim3(gx, 2), 256, 0, s>>>(a);
     else
         step_kernel<4><<<dim3(gx, 2), 256, 0, s>>>(a);
     window_clear_kernel<<<1, 1, 0, s>>>(a.hdr);
+    prof_end(NGRAM_PROF_STEP, s);
     return hipGetLastError();
 }
 

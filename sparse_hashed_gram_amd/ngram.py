@@ -24,6 +24,13 @@ FLAG_WINDOW_FULL = 0x2
 FLAG_STASH_FULL = 0x4
 FLAG_STEP_ORDER = 0x8
 
+PROF_FWD = 0
+PROF_SORT = 1
+PROF_REDUCE = 2
+PROF_STEP = 3
+PROF_STASH = 4
+PROF_GROUPS = 5
+
 DIM = 768
 
 
@@ -101,6 +108,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
+            "ngram_profile_events": ([ctypes.c_int, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -254,3 +262,9 @@ def device_status(cfg: NgramConfig, ws: Workspace, clear: bool = False) -> int:
     _check("ngram_device_status", lib().ngram_device_status(
         ctypes.byref(cfg), ws.ptr, ctypes.byref(f), int(bool(clear)), _stream()))
     return int(f.value)
+
+
+def profile_events(group: int, start, stop):
+    """Record two HIP events (raw hipEvent_t handles, or None) around the
+    kernels of `group` in this thread's later calls."""
+    _check("ngram_profile_events", lib().ngram_profile_events(int(group), start, stop))
