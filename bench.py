@@ -111,20 +111,26 @@ def src_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(group, per_launch_units):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
-    taken on the kernel source as it is now; else None."""
-    p = os.path.join(ROOT, "profiles", f"pmc_{group}.json")
-    if not os.path.exists(p):
-        return None
-    try:
+def pmc_traffic(group):
+    """HBM bytes per launch of a kernel group from a committed rocprofv3 PMC
+    summary (profiles/pmc_*.md, FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy's reading), if it was taken on the kernel source as it is now;
+    else None."""
+    import glob
+    want = src_hash(KERNEL_SRC[group])
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_*.md"))):
+        kv = {}
         with open(p) as f:
-            d = json.load(f)
-        if d.get("source_sha256_16") != src_hash(KERNEL_SRC[group]):
-            return None
-        return float(d["hbm_bytes_per_launch"])
-    except Exception:
-        return None
+            for line in f:
+                if ":" in line and not line.startswith(("#", "|", "rocprofv3")):
+                    k, _, v = line.partition(":")
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel") == group and kv.get("source_sha256_16") == want:
+            try:
+                return float(kv["hbm_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def cpu_baseline(w, toks_np, T_sample, dys_fn):
@@ -267,7 +273,7 @@ def main():
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    traffic = pmc_traffic(dom, None)
+    traffic = pmc_traffic(dom)
     achieved = abytes[dom] / (ms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -186,7 +186,7 @@ int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
 /* Kernel groups for ngram_profile_events. */
 #define NGRAM_PROF_FWD 0    /* the forward gather-sum kernel              */
 #define NGRAM_PROF_SORT 1   /* key build, radix sort, heads and slots     */
-#define NGRAM_PROF_REDUCE 2 /* signed segment reduction + long-row fix-up */
+#define NGRAM_PROF_REDUCE 2 /* the signed segment-reduction kernel        */
 #define NGRAM_PROF_STEP 3   /* the fused sparse step (and window reset)   */
 #define NGRAM_PROF_STASH 4  /* burst mode: keeping a micro-step           */
 #define NGRAM_PROF_GROUPS 5

@@ -99,26 +99,78 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     hist[((size_t)c * kRadix + tid) * nblk + b] = h[tid];
 }
 
-// In-place exclusive scan of `len` words per channel (channel = blockIdx.x).
-// With hdr non-null the total becomes the number of new window slots.
-__global__ __launch_bounds__(1024) void scan_kernel(uint32_t *__restrict__ data, uint32_t len,
-                                                    WsHeader *__restrict__ hdr, uint32_t wrows)
+// In-place exclusive scan of `len` words per channel (channel = blockIdx.x),
+// one 1024-thread block per channel.  Each thread owns a contiguous run of
+// words; when `len` is a multiple of 4 the run is read and written as 16-byte
+// vectors with eight loads in flight, so the scan costs a few memory
+// latencies instead of one per word.  With hdr non-null the total becomes the
+// number of new window slots of the channel.
+constexpr int kScanThreads = 1024;
+constexpr int kScanU = 8;
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint32_t *__restrict__ data, uint32_t len,
+                                                            WsHeader *__restrict__ hdr, uint32_t wrows)
 {
-    __shared__ uint32_t s_wave[1024 / kWave];
+    __shared__ uint32_t s_wave[kScanThreads / kWave];
     const int c = blockIdx.x;
     const int tid = threadIdx.x;
     uint32_t *d = data + (size_t)c * len;
-    const uint32_t per = (len + 1023) / 1024;
+    const bool vec = (len % 4) == 0;
+    uint32_t per = (len + kScanThreads - 1) / kScanThreads;
+    if (vec)
+        per = (per + 3) & ~3u;
     const uint32_t lo = min(tid * per, len), hi = min(lo + per, len);
     uint32_t sum = 0;
-    for (uint32_t j = lo; j < hi; ++j)
-        sum += d[j];
+    if (vec) {
+        const uint4 *v = reinterpret_cast<const uint4 *>(d + lo);
+        const uint32_t nv = (hi - lo) / 4;
+        for (uint32_t k = 0; k < nv; k += kScanU) {
+            uint4 x[kScanU];
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u)
+                if (k + u < nv)
+                    x[u] = v[k + u];
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u)
+                if (k + u < nv)
+                    sum += x[u].x + x[u].y + x[u].z + x[u].w;
+        }
+    } else {
+        for (uint32_t j = lo; j < hi; ++j)
+            sum += d[j];
+    }
     uint32_t total;
-    uint32_t run = block_excl_scan<1024>(sum, s_wave, &total);
-    for (uint32_t j = lo; j < hi; ++j) {
-        const uint32_t x = d[j];
-        d[j] = run;
-        run += x;
+    uint32_t run = block_excl_scan<kScanThreads>(sum, s_wave, &total);
+    if (vec) {
+        uint4 *v = reinterpret_cast<uint4 *>(d + lo);
+        const uint32_t nv = (hi - lo) / 4;
+        for (uint32_t k = 0; k < nv; k += kScanU) {
+            uint4 x[kScanU];
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u)
+                if (k + u < nv)
+                    x[u] = v[k + u];
+#pragma unroll
+            for (int u = 0; u < kScanU; ++u) {
+                if (k + u < nv) {
+                    uint4 y;
+                    y.x = run;
+                    run += x[u].x;
+                    y.y = run;
+                    run += x[u].y;
+                    y.z = run;
+                    run += x[u].z;
+                    y.w = run;
+                    run += x[u].w;
+                    v[k + u] = y;
+                }
+            }
+        }
+    } else {
+        for (uint32_t j = lo; j < hi; ++j) {
+            const uint32_t x = d[j];
+            d[j] = run;
+            run += x;
+        }
     }
     if (hdr && tid == 0) {
         const uint32_t old = hdr->n_slots[c];
@@ -340,75 +392,54 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b)
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-__device__ __forceinline__ float4 flip4(float4 a, uint32_t s)
-{
-    return make_float4(__uint_as_float(__float_as_uint(a.x) ^ s), __uint_as_float(__float_as_uint(a.y) ^ s),
-                       __uint_as_float(__float_as_uint(a.z) ^ s), __uint_as_float(__float_as_uint(a.w) ^ s));
-}
-
 __device__ __forceinline__ uint32_t lane_val(uint32_t v0, uint32_t v1, int j)
 {
     return j < kWave ? (uint32_t)__builtin_amdgcn_readlane((int)v0, j)
                      : (uint32_t)__builtin_amdgcn_readlane((int)v1, j - kWave);
 }
 
-// acc += s_j dY[pos_j] for keys j in [ja, jb), in key order.  Keys below 64
-// come from this chunk's lanes (v0), keys from 64 on from the next chunk's (v1).
-__device__ __forceinline__ void accumulate(float4 (&acc)[3], const float *__restrict__ dY, uint32_t v0,
-                                           uint32_t v1, int ja, int jb, int lane)
+// Lane l of a wavefront holds elements l + 64 m (m = 0..11) of a 768-wide
+// row, so every load, store and atomic of a row is twelve 256-byte contiguous
+// wavefront accesses.
+constexpr int kPer = kDim / kWave;   // 12
+
+__device__ __forceinline__ void store_row(float *dst, const float (&acc)[kPer], int lane)
 {
-    for (int j = ja; j < jb; j += kRedU) {
-        float4 x[kRedU][3];
-        uint32_t sg[kRedU];
 #pragma unroll
-        for (int u = 0; u < kRedU; ++u) {
-            if (j + u < jb) {
-                const uint32_t v = lane_val(v0, v1, j + u);
-                sg[u] = v & 0x80000000u;
-                const float4 *p = reinterpret_cast<const float4 *>(dY + (size_t)(v & 0x7FFFFFFFu) * kDim) + lane;
-                x[u][0] = p[0];
-                x[u][1] = p[kWave];
-                x[u][2] = p[2 * kWave];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kRedU; ++u) {
-            if (j + u < jb) {
-#pragma unroll
-                for (int q = 0; q < 3; ++q)
-                    acc[q] = add4(acc[q], flip4(x[u][q], sg[u]));
-            }
-        }
-    }
+    for (int m = 0; m < kPer; ++m)
+        dst[lane + m * kWave] = acc[m];
 }
 
-// G[slot] = (new row ? 0 : G[slot]) + acc
-__device__ __forceinline__ void flush_row(float4 (&acc)[3], float *gacc, int64_t wrows, int c,
-                                          uint32_t info, int lane)
+// Adds a micro-step's sum into its window row.  A row new to the window is
+// written; an existing one gets G += S through fire-and-forget atomic adds
+// (the read-modify-write happens in L2 and the wavefront does not wait for
+// it).  Every window row has exactly one segment, hence exactly one writer,
+// per launch, so each element sees a single addition: the result is the
+// plain fp32 sum G + S and does not depend on timing.
+__device__ __forceinline__ void flush_window_row(const float (&acc)[kPer], float *gacc, int64_t wrows, int c,
+                                                 uint32_t info, int lane)
 {
     if (info == 0xFFFFFFFFu)
-        return;
-    const uint32_t slot = info & 0x7FFFFFFFu;
-    float4 *g = reinterpret_cast<float4 *>(gacc + ((size_t)c * wrows + slot) * kDim) + lane;
-    if (!(info >> 31)) {
+        return;   // window full: row dropped (flagged when slots were assigned)
+    float *g = gacc + ((size_t)c * wrows + (info & 0x7FFFFFFFu)) * kDim;
+    if (info >> 31) {
+        store_row(g, acc, lane);
+    } else {
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-            acc[q] = add4(g[q * kWave], acc[q]);
+        for (int m = 0; m < kPer; ++m)
+            unsafeAtomicAdd(g + lane + m * kWave, acc[m]);
     }
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-        g[q * kWave] = acc[q];
 }
 
-__device__ __forceinline__ void store_partial(const float4 (&acc)[3], float *partial, int64_t nchunk, int c,
-                                              int64_t chunk, int which, int lane)
-{
-    float4 *p = reinterpret_cast<float4 *>(partial + (((size_t)c * nchunk + chunk) * 2 + which) * kDim) + lane;
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-        p[q * kWave] = acc[q];
-}
-
+// One wavefront per 64 sorted keys.  Keys are consumed in order, kRedU dY rows
+// in flight at a time, whatever the segment boundaries.  A segment's sum is
+// reset at its first key and flushed at its last:
+//   - a segment that starts and ends here goes to the window;
+//   - the first piece, if it continues a segment from the previous chunk, is
+//     skipped when that chunk finishes it, else left as partial row 0;
+//   - the last piece, if it spills into the next chunk, is finished here when
+//     it ends within that chunk (its keys are loaded as lanes 64..127), else
+//     left as partial row 1 with a fix-up record.
 __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
@@ -434,22 +465,23 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     const uint32_t row_last = (uint32_t)__builtin_amdgcn_readlane((int)r0, nv - 1);
     const bool cont_after = nv == kChunk && c0 + kChunk < n && R[c0 + kChunk] == row_last;
 
-    // First piece continuing a segment from the previous chunk: skipped when
-    // that chunk (where the segment starts) finishes it because it ends here.
+    // first piece: continuation of the previous chunk's last segment?
+    const bool first_cont = !(hm & 1ull);
+    const int e0 = hm ? (int)__builtin_ctzll(hm) : nv;   // end of the first piece
     bool skip_first = false;
-    if (!(hm & 1ull)) {
+    if (first_cont) {
         const uint32_t row0 = (uint32_t)__builtin_amdgcn_readlane((int)r0, 0);
-        const int e0 = hm ? (int)__builtin_ctzll(hm) : nv;
         const bool piece0_cont = (e0 == nv) && cont_after;
         const bool head_in_prev = (c0 == kChunk) || (R[c0 - kChunk - 1] != row0);
         skip_first = head_in_prev && !piece0_cont;
     }
-    // Last piece starting here and spilling over: finish it here if it ends
-    // within the next chunk (load that chunk's keys), else leave a partial.
+    // last piece: starts at the highest head; spills over if cont_after
+    const int la = hm ? 63 - (int)__builtin_clzll(hm) : -1;
+    const bool last_spills = hm && cont_after;
     bool owner_full = false;
     uint32_t v1 = 0;
     int extra = 0;
-    if (hm && cont_after) {
+    if (last_spills) {
         owner_full = !(c0 + 2 * kChunk < n && R[c0 + 2 * kChunk] == row_last);
         if (owner_full) {
             const int64_t i1 = c0 + kChunk + lane;
@@ -459,38 +491,66 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
             extra = __popcll(__ballot(ok1 && r1 == row_last));
         }
     }
+    const int j0 = skip_first ? e0 : 0;
+    const int jend = owner_full ? kChunk + extra : nv;
 
-    int pa = 0;
-    while (pa < nv) {
-        const uint64_t later = pa >= kChunk - 1 ? 0ull : (hm & (~0ull << (pa + 1)));
-        const int pb = later ? (int)__builtin_ctzll(later) : nv;
-        const bool is_head = (hm >> pa) & 1ull;
-        float4 acc[3] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
-                         make_float4(0.f, 0.f, 0.f, 0.f)};
-        if (!is_head) {
-            if (!skip_first) {
-                accumulate(acc, a.dY, v0, 0u, 0, pb, lane);
-                store_partial(acc, a.partial, a.nchunk, c, chunk, 0, lane);
+    float acc[kPer];
+    int ps = j0;   // start key of the open segment
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+        acc[m] = 0.f;
+    for (int j = j0; j < jend; j += kRedU) {
+        float x[kRedU][kPer];
+        uint32_t sg[kRedU];
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u) {
+            if (j + u < jend) {
+                const uint32_t v = lane_val(v0, v1, j + u);
+                sg[u] = v & 0x80000000u;
+                const float *p = a.dY + (size_t)(v & 0x7FFFFFFFu) * kDim + lane;
+#pragma unroll
+                for (int m = 0; m < kPer; ++m)
+                    x[u][m] = p[m * kWave];
             }
-        } else if (pb == nv && cont_after) {
-            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, pa);
-            if (owner_full) {
-                accumulate(acc, a.dY, v0, v1, pa, kChunk + extra, lane);
-                flush_row(acc, a.gacc, a.wrows, c, info, lane);
-            } else {
-                accumulate(acc, a.dY, v0, 0u, pa, kChunk, lane);
-                store_partial(acc, a.partial, a.nchunk, c, chunk, 1, lane);
-                if (lane == 0) {
-                    const uint32_t k = atomicAdd(&a.hdr->n_owner[c], 1u);
-                    a.owners[(size_t)c * a.nchunk + k] = (uint64_t)chunk | ((uint64_t)info << 32);
-                }
-            }
-        } else {
-            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, pa);
-            accumulate(acc, a.dY, v0, 0u, pa, pb, lane);
-            flush_row(acc, a.gacc, a.wrows, c, info, lane);
         }
-        pa = pb;
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u) {
+            const int k = j + u;
+            if (k >= jend)
+                break;
+            if (k < kChunk && k != j0 && ((hm >> k) & 1ull)) {
+                ps = k;
+#pragma unroll
+                for (int m = 0; m < kPer; ++m)
+                    acc[m] = 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < kPer; ++m)
+                acc[m] += __uint_as_float(__float_as_uint(x[u][m]) ^ sg[u]);
+            // does the open segment end at key k?
+            bool ends;
+            if (k >= kChunk - 1 && owner_full)
+                ends = (k == jend - 1);
+            else if (k == nv - 1)
+                ends = true;
+            else
+                ends = (k + 1 < kChunk) && ((hm >> (k + 1)) & 1ull);
+            if (!ends)
+                continue;
+            if (ps == 0 && first_cont) {
+                store_row(a.partial + (((size_t)c * a.nchunk + chunk) * 2 + 0) * kDim, acc, lane);
+            } else if (ps == la && last_spills && !owner_full) {
+                const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, ps);
+                store_row(a.partial + (((size_t)c * a.nchunk + chunk) * 2 + 1) * kDim, acc, lane);
+                if (lane == 0) {
+                    const uint32_t k2 = atomicAdd(&a.hdr->n_owner[c], 1u);
+                    a.owners[(size_t)c * a.nchunk + k2] = (uint64_t)chunk | ((uint64_t)info << 32);
+                }
+            } else {
+                const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, ps);
+                flush_window_row(acc, a.gacc, a.wrows, c, info, lane);
+            }
+        }
     }
 }
 
@@ -587,7 +647,7 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
         uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
         uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
         radix_hist_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nblk);
-        scan_kernel<<<2, 1024, 0, s>>>(hist, kRadix * nblk, nullptr, 0);
+        scan_kernel<<<2, kScanThreads, 0, s>>>(hist, kRadix * nblk, nullptr, 0);
         radix_scatter_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
                                                                     shift, hist, nblk);
         cur ^= 1;
@@ -607,7 +667,7 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     sa.wrows = (uint32_t)L.wrows;
     sa.hdr = hdr;
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    scan_kernel<<<2, 1024, 0, s>>>(sa.blk, nblk, hdr, (uint32_t)L.wrows);
+    scan_kernel<<<2, kScanThreads, 0, s>>>(sa.blk, nblk, hdr, (uint32_t)L.wrows);
     assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     prof_end(NGRAM_PROF_SORT, s);
 
@@ -629,8 +689,8 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     const uint32_t per_block = kRedThreads / kWave;
     prof_begin(NGRAM_PROF_REDUCE, s);
     seg_reduce_kernel<<<dim3((nchunk + per_block - 1) / per_block, 2), kRedThreads, 0, s>>>(ra);
-    fixup_kernel<<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     prof_end(NGRAM_PROF_REDUCE, s);
+    fixup_kernel<<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     return hipGetLastError();
 }
 

@@ -53,13 +53,102 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// Row state of one touched row while it is being stepped.
+struct RowIn {
+    uint32_t row;
+    float4 g[3];
+    float w[3][4];
+    float v;
+    int32_t tl;
+};
+
+template <int ELT>
+__device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot, const uint8_t *W,
+                                         const float *V, const int32_t *TL, int lane)
+{
+    const float4 *g4 = reinterpret_cast<const float4 *>(G + (size_t)slot * kDim) + lane;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        r.g[q] = g4[q * kWave];
+    if (ELT == 2) {
+        const uint2 *wp = reinterpret_cast<const uint2 *>(W + (size_t)r.row * kDim * 2) + lane;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const uint2 x = wp[q * kWave];
+            r.w[q][0] = bf16_lo(x.x);
+            r.w[q][1] = bf16_hi(x.x);
+            r.w[q][2] = bf16_lo(x.y);
+            r.w[q][3] = bf16_hi(x.y);
+        }
+    } else {
+        const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)r.row * kDim * 4) + lane;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const float4 x = wp[q * kWave];
+            r.w[q][0] = x.x;
+            r.w[q][1] = x.y;
+            r.w[q][2] = x.z;
+            r.w[q][3] = x.w;
+        }
+    }
+    r.v = V[r.row];
+    r.tl = TL[r.row];
+}
+
+template <int ELT>
+__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, float *V, int32_t *TL,
+                                         int32_t *SM, double one_minus_b2, int lane)
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        ss += r.g[q].x * r.g[q].x + r.g[q].y * r.g[q].y + r.g[q].z * r.g[q].z + r.g[q].w * r.g[q].w;
+    ss = wave_sum(ss);
+    int32_t k = a.t - r.tl;
+    if (k < 1) {
+        if (lane == 0)
+            atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+        k = 0;
+    }
+    const double decay = pow_steps((double)a.beta2, k);
+    const float vn = (float)(decay * (double)r.v + one_minus_b2 * ((double)ss / (double)kDim));
+    const float scale = a.lr / (sqrtf(vn) + a.eps);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        r.w[q][0] -= scale * r.g[q].x;
+        r.w[q][1] -= scale * r.g[q].y;
+        r.w[q][2] -= scale * r.g[q].z;
+        r.w[q][3] -= scale * r.g[q].w;
+    }
+    if (ELT == 2) {
+        uint2 *wp = reinterpret_cast<uint2 *>(W + (size_t)r.row * kDim * 2) + lane;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            wp[q * kWave] = make_uint2(bf16_pack(r.w[q][0], r.w[q][1]), bf16_pack(r.w[q][2], r.w[q][3]));
+    } else {
+        float4 *wp = reinterpret_cast<float4 *>(W + (size_t)r.row * kDim * 4) + lane;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            wp[q * kWave] = make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]);
+    }
+    if (lane == 0) {
+        V[r.row] = vn;
+        TL[r.row] = a.t;
+        SM[r.row] = -1;
+    }
+}
+
+// Each wavefront takes 64 consecutive window slots at a time (one coalesced
+// load of their row ids), then steps them two rows per iteration with both
+// rows' loads in flight together.
+constexpr int kStepRows = 2;
 template <int ELT>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
 {
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wid = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-    const uint32_t stride = gridDim.x * (256 / kWave);
+    const uint32_t nwaves = gridDim.x * (256 / kWave);
     const uint32_t n = a.hdr->n_slots[c];
     const uint32_t *rows = a.slot_rows[c];
     const float *G = a.gacc + (size_t)c * a.wrows * kDim;
@@ -69,71 +158,22 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     int32_t *SM = a.slot_map[c];
     const double one_minus_b2 = 1.0 - (double)a.beta2;
 
-    for (uint32_t slot = wid; slot < n; slot += stride) {
-        const uint32_t row = rows[slot];
-        const float4 *g4 = reinterpret_cast<const float4 *>(G + (size_t)slot * kDim) + lane;
-        const float4 g[3] = {g4[0], g4[kWave], g4[2 * kWave]};
-        float w[3][4];
-        if (ELT == 2) {
-            const uint2 *wp = reinterpret_cast<const uint2 *>(W + (size_t)row * kDim * 2) + lane;
+    for (uint32_t base = wid * kWave; base < n; base += nwaves * kWave) {
+        const uint32_t cnt = min((uint32_t)kWave, n - base);
+        const uint32_t my_row = lane < (int)cnt ? rows[base + lane] : 0u;
+        for (uint32_t u = 0; u < cnt; u += kStepRows) {
+            RowIn r[kStepRows];
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const uint2 x = wp[q * kWave];
-                w[q][0] = bf16_lo(x.x);
-                w[q][1] = bf16_hi(x.x);
-                w[q][2] = bf16_lo(x.y);
-                w[q][3] = bf16_hi(x.y);
+            for (int k = 0; k < kStepRows; ++k) {
+                if (u + k < cnt) {
+                    r[k].row = (uint32_t)__builtin_amdgcn_readlane((int)my_row, (int)(u + k));
+                    load_row<ELT>(r[k], G, base + u + k, W, V, TL, lane);
+                }
             }
-        } else {
-            const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)row * kDim * 4) + lane;
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const float4 x = wp[q * kWave];
-                w[q][0] = x.x;
-                w[q][1] = x.y;
-                w[q][2] = x.z;
-                w[q][3] = x.w;
-            }
-        }
-        const int32_t tlast = TL[row];
-        const float vold = V[row];
-        float ss = 0.f;
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-            ss += g[q].x * g[q].x + g[q].y * g[q].y + g[q].z * g[q].z + g[q].w * g[q].w;
-        ss = wave_sum(ss);
-        int32_t k = a.t - tlast;
-        if (k < 1) {
-            if (lane == 0)
-                atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
-            k = 0;
-        }
-        const double decay = pow_steps((double)a.beta2, k);
-        const float vn = (float)(decay * (double)vold + one_minus_b2 * ((double)ss / (double)kDim));
-        const float scale = a.lr / (sqrtf(vn) + a.eps);
-        const float gg[3][4] = {{g[0].x, g[0].y, g[0].z, g[0].w},
-                                {g[1].x, g[1].y, g[1].z, g[1].w},
-                                {g[2].x, g[2].y, g[2].z, g[2].w}};
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[q][e] = w[q][e] - scale * gg[q][e];
-        if (ELT == 2) {
-            uint2 *wp = reinterpret_cast<uint2 *>(W + (size_t)row * kDim * 2) + lane;
-#pragma unroll
-            for (int q = 0; q < 3; ++q)
-                wp[q * kWave] = make_uint2(bf16_pack(w[q][0], w[q][1]), bf16_pack(w[q][2], w[q][3]));
-        } else {
-            float4 *wp = reinterpret_cast<float4 *>(W + (size_t)row * kDim * 4) + lane;
-#pragma unroll
-            for (int q = 0; q < 3; ++q)
-                wp[q * kWave] = make_float4(w[q][0], w[q][1], w[q][2], w[q][3]);
-        }
-        if (lane == 0) {
-            V[row] = vn;
-            TL[row] = a.t;
-            SM[row] = -1;
+            for (int k = 0; k < kStepRows; ++k)
+                if (u + k < cnt)
+                    step_row<ELT>(r[k], a, W, V, TL, SM, one_minus_b2, lane);
         }
     }
 }
@@ -189,8 +229,9 @@ hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void
     a.lr = lr;
     a.beta2 = beta2;
     a.eps = eps;
-    const int64_t want = (L.wrows + 3) / 4;
-    const unsigned gx = (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+    // about one resident wavefront per SIMD slot; each walks 64-slot blocks
+    const int64_t want = (L.wrows + 255) / 256;
+    const unsigned gx = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);
     prof_begin(NGRAM_PROF_STEP, s);
     if (dtype == NGRAM_DTYPE_BF16)
         step_kernel<2><<<dim3(gx, 2), 256, 0, s>>>(a);
