@@ -194,8 +194,7 @@ def main():
     cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode)
 
     W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(2)]
-    v = [torch.zeros(w.rows[c], dtype=torch.float32, device="cuda") for c in range(2)]
-    tl = [torch.zeros(w.rows[c], dtype=torch.int32, device="cuda") for c in range(2)]
+    state = [N.new_state(w.rows[c]) for c in range(2)]
     ws = N.Workspace(cfg)
     out = torch.empty((T, 768), dtype=tdt, device="cuda")
     nwin = max(1, args.distinct_windows)
@@ -235,7 +234,7 @@ def main():
             disarm()
         arm(ev, ("sort", "reduce", "step") if burst else ("step",))
         t_step[0] += 1
-        N.sparse_step(cfg, ws, W[0], W[1], v[0], v[1], tl[0], tl[1], t_step[0], w.lr, w.beta2, w.eps)
+        N.sparse_step(cfg, ws, W[0], W[1], state[0], state[1], t_step[0], w.lr, w.beta2, w.eps)
         disarm()
 
     for i in range(args.warmup):
@@ -303,7 +302,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del W, v, tl, ws, out, dys
+        del W, state, ws, out, dys
         torch.cuda.empty_cache()
         Ts = T if args.cpu_tokens <= 0 else min(T, args.cpu_tokens)
         res["cpu_baseline"] = cpu_baseline(w, toks_np[0], Ts, lambda m, n: synth.dY(w, m, n))

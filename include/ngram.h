@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 1
+#define NGRAM_ABI_VERSION 2
 
 /* dtypes of the tables (and of the forward output) */
 #define NGRAM_DTYPE_F32 0
@@ -109,6 +109,15 @@ typedef struct ngram_config {
                                     accum_steps * max_tokens)              */
 } ngram_config;
 
+/* Optimizer state of one table row (8 bytes, 8-byte aligned arrays): the
+ * second moment v (one float per 768-wide row, the @classiclarryd post) and
+ * the optimizer step at which the row was last updated (its pending beta2
+ * decay is beta2^(t - t_last)).  Start at {0, 0}. */
+typedef struct ngram_row_state {
+    float v;
+    int32_t t_last;
+} ngram_row_state;
+
 /* Version of this ABI (NGRAM_ABI_VERSION). */
 int ngram_abi_version(void);
 
@@ -120,7 +129,7 @@ int ngram_config_check(const ngram_config *cfg);
 
 /* Bytes of device workspace the config needs (host output `bytes`).  The
  * workspace holds the window accumulator (window_rows x 768 fp32 per
- * channel), a row->slot map (4 B per table row), sort buffers, and in burst
+ * channel), a row->slot map (8 B per table row), sort buffers, and in burst
  * mode a copy of the window's upstream gradients. */
 int ngram_workspace_bytes(const ngram_config *cfg, uint64_t *bytes);
 
@@ -165,14 +174,14 @@ int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream);
 /* Sparse step number t >= 1 on every row the window touched, then empties the
  * window (the @classiclarryd post: optimizer step only for n-gram rows that
  * occurred, beta1 = 0, beta2 applied retroactively, one float per 768
- * parameters).  W_b, W_t: tables of cfg->dtype, updated in place.  v_b, v_t:
- * fp32 [rows[c]] second moments (start at 0).  t_last_b, t_last_t: int32
- * [rows[c]] step of each row's last update (start at 0).  Requires
- * 0 <= beta2 < 1, eps > 0 and finite, lr finite. */
+ * parameters).  W_b, W_t: tables of cfg->dtype, updated in place.  state_b,
+ * state_t: ngram_row_state [rows[c]] (v and t_last of every row), updated for
+ * the touched rows only.  Requires 0 <= beta2 < 1, eps > 0 and finite, lr
+ * finite. */
 int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t,
-                      float *v_b, float *v_t, int32_t *t_last_b,
-                      int32_t *t_last_t, int32_t t, float lr, float beta2,
-                      float eps, void *stream);
+                      ngram_row_state *state_b, ngram_row_state *state_t,
+                      int32_t t, float lr, float beta2, float eps,
+                      void *stream);
 
 /* Copies the current window of one channel (0 bigram, 1 trigram) to caller
  * buffers: the first min(n, max_rows) rows (uint32, first-touch order:

@@ -76,7 +76,7 @@ WsLayout layout(const ngram_config *c)
     o = up(o + sizeof(WsHeader));
     for (int k = 0; k < 2; ++k) {
         L.slot_map[k] = o;
-        o = up(o + 4ull * (uint64_t)c->rows[k]);
+        o = up(o + sizeof(SlotEntry) * (uint64_t)c->rows[k]);
     }
     for (int k = 0; k < 2; ++k) {
         L.slot_rows[k] = o;
@@ -94,6 +94,8 @@ WsLayout layout(const ngram_config *c)
     o = up(o + 4ull * 2 * (uint64_t)L.nk);
     L.hist = o;
     o = up(o + 4ull * 2 * kRadix * (uint64_t)L.nblk);
+    L.tot = o;
+    o = up(o + 4ull * 2 * kRadix);
     L.blk = o;
     o = up(o + 4ull * 2 * (uint64_t)L.nblk);
     L.partial = o;
@@ -236,10 +238,7 @@ int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws, const int32_t *toke
         return hip_status(launch_stash(L, w, hp, tokens, dY, T, s));
     if (T == 0)
         return NGRAM_OK;
-    hipError_t e = launch_keys_from_tokens(L, w, hp, tokens, T, s);
-    if (e == hipSuccess)
-        e = launch_reduce(L, w, nullptr, (uint32_t)T, dY, s);
-    return hip_status(e);
+    return hip_status(launch_reduce(L, w, hp, tokens, T, dY, s));
 }
 
 int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
@@ -256,34 +255,33 @@ int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
         return NGRAM_OK;
     uint8_t *w = (uint8_t *)ws;
     hipStream_t s = (hipStream_t)stream;
-    const uint32_t *n_dev = &reinterpret_cast<const WsHeader *>(w + L.hdr)->n_stash;
-    hipError_t e = launch_keys_from_stash(L, w, s);
-    if (e == hipSuccess)
-        e = launch_reduce(L, w, n_dev, (uint32_t)L.nk, reinterpret_cast<const float *>(w + L.stash_dy), s);
+    hipError_t e = launch_reduce(L, w, hash_params(cfg), nullptr, L.nk,
+                                 reinterpret_cast<const float *>(w + L.stash_dy), s);
     if (e == hipSuccess)
         e = launch_stash_clear(L, w, s);
     return hip_status(e);
 }
 
-int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, float *v_b, float *v_t,
-                      int32_t *t_last_b, int32_t *t_last_t, int32_t t, float lr, float beta2, float eps,
-                      void *stream)
+int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
+                      ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps, void *stream)
 {
+    static_assert(sizeof(ngram_row_state) == sizeof(RowState), "row state layout");
     int rc = check_cfg(cfg);
     if (rc)
         return rc;
-    if (!ws || !W_b || !W_t || !v_b || !v_t || !t_last_b || !t_last_t)
+    if (!ws || !W_b || !W_t || !state_b || !state_t)
         return NGRAM_ENULL;
-    if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(v_b, 4) ||
-        !aligned(v_t, 4) || !aligned(t_last_b, 4) || !aligned(t_last_t, 4))
+    if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) ||
+        !aligned(state_t, 8))
         return NGRAM_EALIGN;
     if (t < 1 || !isfinite(lr) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !isfinite(eps))
         return NGRAM_EARG;
     if ((rc = ngram_window_reduce(cfg, ws, stream)))
         return rc;
     const WsLayout L = layout(cfg);
-    return hip_status(launch_step(L, (uint8_t *)ws, cfg->dtype, W_b, W_t, v_b, v_t, t_last_b, t_last_t, t,
-                                  lr, beta2, eps, (hipStream_t)stream));
+    return hip_status(launch_step(L, (uint8_t *)ws, cfg->dtype, W_b, W_t, reinterpret_cast<RowState *>(state_b),
+                                  reinterpret_cast<RowState *>(state_t), t, lr, beta2, eps,
+                                  (hipStream_t)stream));
 }
 
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, uint32_t *rows, float *G,

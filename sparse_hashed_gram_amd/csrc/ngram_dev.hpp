@@ -95,14 +95,29 @@ struct WsHeader {
     uint32_t magic;
     uint32_t flags;        // NGRAM_FLAG_* (sticky)
     uint32_t n_slots[2];   // distinct rows in the window, per channel
-    uint32_t n_prev[2];    // n_slots before the micro-step being reduced
+    uint32_t n_next[2];    // n_slots once the micro-step being reduced is in
     uint32_t n_owner[2];   // long-segment fix-up records of the current reduce
     uint32_t n_stash;      // burst mode: positions kept since the last reduce
-    uint32_t pad[55];
+    uint32_t epoch;        // window number; slot-map entries of other windows are stale
+    uint32_t pad[54];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
 constexpr uint32_t kMagic = 0x6E677231u;
+
+// Row -> window slot map entry.  A row is in the current window iff its
+// epoch equals the header's; ending a window just advances the epoch, so the
+// sparse step never has to clear entries.
+struct SlotEntry {
+    uint32_t epoch;
+    uint32_t slot;
+};
+
+// Per-row optimizer state, as the caller stores it (ngram_row_state).
+struct RowState {
+    float v;
+    int32_t t_last;
+};
 
 // Sort tiles: 256 threads x 8 keys.
 constexpr int kSortThreads = 256;
@@ -116,13 +131,14 @@ constexpr int kChunk = 64;
 
 struct WsLayout {
     uint64_t hdr;
-    uint64_t slot_map[2];   // int32 [rows[c]]: slot of a row in the window, -1 if none
+    uint64_t slot_map[2];   // SlotEntry [rows[c]]: {window epoch, slot} of each row
     uint64_t slot_rows[2];  // uint32 [wrows]: row of each slot
     uint64_t gacc;          // fp32 [2][wrows][768]: window gradient
     uint64_t keys[2];       // uint32 [2][nk]: sort key buffers A/B (row)
     uint64_t vals[2];       // uint32 [2][nk]: sort payload A/B (position | neg << 31)
     uint64_t seg_info;      // uint32 [2][nk]: slot | new << 31 at segment heads
-    uint64_t hist;          // uint32 [2][256][nblk]
+    uint64_t hist;          // uint32 [2][256][nblk]: per-tile digit counts, then offsets
+    uint64_t tot;           // uint32 [2][256]: digit totals of a pass
     uint64_t blk;           // uint32 [2][nblk]
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
@@ -169,27 +185,22 @@ hipError_t launch_hash(const HashParams &hp, const int32_t *tok, int64_t T, uint
 hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const void *wt,
                       const int32_t *tok, int64_t T, void *out, uint32_t *flags, hipStream_t s);
 
-// Spread: keys of one micro-step straight from the tokens.
-hipError_t launch_keys_from_tokens(const WsLayout &L, uint8_t *ws, const HashParams &hp,
-                                   const int32_t *tok, int64_t T, hipStream_t s);
 // Burst: keep one micro-step (packed indices + dY rows) in the stash.
 hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp,
                         const int32_t *tok, const float *dY, int64_t T, hipStream_t s);
-// Burst: keys of every kept position.
-hipError_t launch_keys_from_stash(const WsLayout &L, uint8_t *ws, hipStream_t s);
 
-// Sort the keys of both channels by row, find segments, assign window slots,
-// reduce signed dY rows into the window.  n_dev (device count) may be null;
-// n_host bounds it.
-hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host,
-                         const float *dY, hipStream_t s);
+// Build the sort keys of both channels (spread: hashed from `tok`, T of them;
+// burst: from every kept stash position, a device count bounded by nk), sort
+// them by row, find segments, assign window slots and reduce the signed dY
+// rows into the window.
+hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
+                         int64_t T, const float *dY, hipStream_t s);
 
 // Burst: mark the stash empty after a reduce.
 hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);
 
-hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, float *vb,
-                       float *vt, int32_t *tlb, int32_t *tlt, int32_t t, float lr, float beta2,
-                       float eps, hipStream_t s);
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, RowState *sb,
+                       RowState *st, int32_t t, float lr, float beta2, float eps, hipStream_t s);
 
 hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s);
 

@@ -1,4 +1,4 @@
-// Hash, forward gather-sum, and the backward's key build (gfx950).
+// Hash, forward gather-sum, and the burst-mode stash (gfx950).
 //
 // Forward (modded-nanogpt README, technique list: hashed bigram + trigram
 // table with sign trick): out[i] = s_b W_b[r_b(i)] + s_t W_t[r_t(i)].
@@ -116,28 +116,6 @@ __global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashPara
     idx[T + i] = it;
 }
 
-// Spread mode: sort keys (row) and payloads (position | neg << 31) of both
-// channels for one micro-step.  Also resets the fix-up record counts.
-__global__ void keys_tokens_kernel(const int32_t *__restrict__ tok, int64_t T, HashParams hp,
-                                   uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
-                                   int64_t nk, WsHeader *__restrict__ hdr)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) {
-        hdr->n_owner[0] = 0;
-        hdr->n_owner[1] = 0;
-    }
-    if (i >= T)
-        return;
-    uint32_t ib, it;
-    if (ngram_index(tok, i, hp, ib, it))
-        atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
-    keys[i] = ib & 0x7FFFFFFFu;
-    vals[i] = (uint32_t)i | (ib & 0x80000000u);
-    keys[nk + i] = it & 0x7FFFFFFFu;
-    vals[nk + i] = (uint32_t)i | (it & 0x80000000u);
-}
-
 // Burst mode: keep the packed indices and the dY rows of one micro-step at
 // the end of the stash.  One block per 16 positions: 16 threads hash, all
 // 256 threads copy the 16 x 192 float4 of dY.
@@ -176,25 +154,6 @@ __global__ void stash_advance_kernel(int64_t T, int64_t nk, WsHeader *__restrict
         hdr->n_stash = base + (uint32_t)T;
 }
 
-__global__ void keys_stash_kernel(const uint32_t *__restrict__ sidx, int64_t nk,
-                                  uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
-                                  WsHeader *__restrict__ hdr)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) {
-        hdr->n_owner[0] = 0;
-        hdr->n_owner[1] = 0;
-    }
-    const uint32_t n = hdr->n_stash;
-    if (i >= n)
-        return;
-    const uint32_t ib = sidx[i], it = sidx[nk + i];
-    keys[i] = ib & 0x7FFFFFFFu;
-    vals[i] = (uint32_t)i | (ib & 0x80000000u);
-    keys[nk + i] = it & 0x7FFFFFFFu;
-    vals[nk + i] = (uint32_t)i | (it & 0x80000000u);
-}
-
 __global__ void stash_clear_kernel(WsHeader *__restrict__ hdr) { hdr->n_stash = 0; }
 
 __global__ void flags_clear_kernel(WsHeader *__restrict__ hdr) { hdr->flags = 0; }
@@ -215,12 +174,15 @@ unsigned grid_for(int64_t n, int per)
 
 hipError_t launch_init(const WsLayout &L, uint8_t *ws, hipStream_t s)
 {
-    // header: zero everything, then the magic word
-    fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.hdr), sizeof(WsHeader) / 4, 0u);
-    fill_u32_kernel<<<1, 1, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.hdr), 1, kMagic);
+    // header: zero everything, then the magic word and window epoch 1; slot
+    // map entries start at epoch 0, i.e. in no window
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(hdr), sizeof(WsHeader) / 4, 0u);
+    fill_u32_kernel<<<1, 1, 0, s>>>(&hdr->magic, 1, kMagic);
+    fill_u32_kernel<<<1, 1, 0, s>>>(&hdr->epoch, 1, 1u);
     for (int c = 0; c < 2; ++c)
         fill_u32_kernel<<<2048, 256, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.slot_map[c]),
-                                             (uint64_t)L.rows[c], 0xFFFFFFFFu);
+                                             2 * (uint64_t)L.rows[c], 0u);
     return hipGetLastError();
 }
 
@@ -250,16 +212,6 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
     return hipGetLastError();
 }
 
-hipError_t launch_keys_from_tokens(const WsLayout &L, uint8_t *ws, const HashParams &hp,
-                                   const int32_t *tok, int64_t T, hipStream_t s)
-{
-    prof_begin(NGRAM_PROF_SORT, s);
-    keys_tokens_kernel<<<grid_for(T > 0 ? T : 1, 256), 256, 0, s>>>(
-        tok, T, hp, reinterpret_cast<uint32_t *>(ws + L.keys[0]),
-        reinterpret_cast<uint32_t *>(ws + L.vals[0]), L.nk, reinterpret_cast<WsHeader *>(ws + L.hdr));
-    return hipGetLastError();
-}
-
 hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
                         const float *dY, int64_t T, hipStream_t s)
 {
@@ -271,16 +223,6 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
             reinterpret_cast<float *>(ws + L.stash_dy), L.nk, hdr);
     stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, hdr);
     prof_end(NGRAM_PROF_STASH, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_keys_from_stash(const WsLayout &L, uint8_t *ws, hipStream_t s)
-{
-    prof_begin(NGRAM_PROF_SORT, s);
-    keys_stash_kernel<<<grid_for(L.nk, 256), 256, 0, s>>>(
-        reinterpret_cast<const uint32_t *>(ws + L.stash_idx), L.nk,
-        reinterpret_cast<uint32_t *>(ws + L.keys[0]), reinterpret_cast<uint32_t *>(ws + L.vals[0]),
-        reinterpret_cast<WsHeader *>(ws + L.hdr));
     return hipGetLastError();
 }
 

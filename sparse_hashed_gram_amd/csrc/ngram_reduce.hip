@@ -75,6 +75,61 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave
 }
 
 // ------------------------------------------------------------ radix sort
+//
+// Tiles of 2048 keys (256 threads x 8).  Per pass: per-tile digit counts
+// (hist[c][d][tile], digit-major), then one block per (digit, channel) turns
+// its row of tile counts into exclusive tile offsets and a digit total, then
+// the scatter adds the exclusive scan of the digit totals (done per block in
+// LDS) to get each tile's global digit offsets.
+
+// Key build for one tile, fused with the first pass's digit counts.  Spread:
+// position i of the micro-step is hashed from the tokens.  Burst: every
+// position kept in the stash, whose packed indices were hashed when kept.
+// Also clears the fix-up record counts of the reduce that follows.
+template <bool FROM_STASH>
+__global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
+    const int32_t *__restrict__ tok, const uint32_t *__restrict__ sidx, HashParams hp, uint32_t n_host,
+    uint32_t *__restrict__ keys, uint32_t *__restrict__ vals, int64_t nk, uint32_t *__restrict__ hist,
+    uint32_t nblk, WsHeader *__restrict__ hdr)
+{
+    __shared__ uint32_t h[2][kRadix];
+    const int tid = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t n = FROM_STASH ? min(hdr->n_stash, n_host) : n_host;
+    if (b == 0 && tid == 0) {
+        hdr->n_owner[0] = 0;
+        hdr->n_owner[1] = 0;
+    }
+    h[0][tid] = 0;
+    h[1][tid] = 0;
+    __syncthreads();
+    const uint32_t base = b * kSortTile;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = base + j * kSortThreads + tid;
+        if (i < n) {
+            uint32_t ib, it;
+            if (FROM_STASH) {
+                ib = sidx[i];
+                it = sidx[nk + i];
+            } else {
+                bad |= ngram_index(tok, i, hp, ib, it);
+            }
+            keys[i] = ib & 0x7FFFFFFFu;
+            vals[i] = i | (ib & 0x80000000u);
+            keys[nk + i] = it & 0x7FFFFFFFu;
+            vals[nk + i] = i | (it & 0x80000000u);
+            atomicAdd(&h[0][ib & (kRadix - 1)], 1u);
+            atomicAdd(&h[1][it & (kRadix - 1)], 1u);
+        }
+    }
+    if (bad)
+        atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
+    __syncthreads();
+    hist[((size_t)0 * kRadix + tid) * nblk + b] = h[0][tid];
+    hist[((size_t)1 * kRadix + tid) * nblk + b] = h[1][tid];
+}
 
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const uint32_t *__restrict__ keys, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
@@ -99,89 +154,28 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     hist[((size_t)c * kRadix + tid) * nblk + b] = h[tid];
 }
 
-// In-place exclusive scan of `len` words per channel (channel = blockIdx.x),
-// one 1024-thread block per channel.  Each thread owns a contiguous run of
-// words; when `len` is a multiple of 4 the run is read and written as 16-byte
-// vectors with eight loads in flight, so the scan costs a few memory
-// latencies instead of one per word.  With hdr non-null the total becomes the
-// number of new window slots of the channel.
-constexpr int kScanThreads = 1024;
-constexpr int kScanU = 8;
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint32_t *__restrict__ data, uint32_t len,
-                                                            WsHeader *__restrict__ hdr, uint32_t wrows)
+// Block (d, c): exclusive scan of digit d's tile counts in place, total to
+// tot[c][d].  Each thread owns a contiguous run of tiles.
+__global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__restrict__ hist, uint32_t nblk,
+                                                                   uint32_t *__restrict__ tot)
 {
-    __shared__ uint32_t s_wave[kScanThreads / kWave];
-    const int c = blockIdx.x;
-    const int tid = threadIdx.x;
-    uint32_t *d = data + (size_t)c * len;
-    const bool vec = (len % 4) == 0;
-    uint32_t per = (len + kScanThreads - 1) / kScanThreads;
-    if (vec)
-        per = (per + 3) & ~3u;
-    const uint32_t lo = min(tid * per, len), hi = min(lo + per, len);
+    __shared__ uint32_t s_wave[kSortThreads / kWave];
+    const int d = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+    uint32_t *row = hist + ((size_t)c * kRadix + d) * nblk;
+    const uint32_t per = (nblk + kSortThreads - 1) / kSortThreads;
+    const uint32_t lo = min(tid * per, nblk), hi = min(lo + per, nblk);
     uint32_t sum = 0;
-    if (vec) {
-        const uint4 *v = reinterpret_cast<const uint4 *>(d + lo);
-        const uint32_t nv = (hi - lo) / 4;
-        for (uint32_t k = 0; k < nv; k += kScanU) {
-            uint4 x[kScanU];
-#pragma unroll
-            for (int u = 0; u < kScanU; ++u)
-                if (k + u < nv)
-                    x[u] = v[k + u];
-#pragma unroll
-            for (int u = 0; u < kScanU; ++u)
-                if (k + u < nv)
-                    sum += x[u].x + x[u].y + x[u].z + x[u].w;
-        }
-    } else {
-        for (uint32_t j = lo; j < hi; ++j)
-            sum += d[j];
-    }
+    for (uint32_t j = lo; j < hi; ++j)
+        sum += row[j];
     uint32_t total;
-    uint32_t run = block_excl_scan<kScanThreads>(sum, s_wave, &total);
-    if (vec) {
-        uint4 *v = reinterpret_cast<uint4 *>(d + lo);
-        const uint32_t nv = (hi - lo) / 4;
-        for (uint32_t k = 0; k < nv; k += kScanU) {
-            uint4 x[kScanU];
-#pragma unroll
-            for (int u = 0; u < kScanU; ++u)
-                if (k + u < nv)
-                    x[u] = v[k + u];
-#pragma unroll
-            for (int u = 0; u < kScanU; ++u) {
-                if (k + u < nv) {
-                    uint4 y;
-                    y.x = run;
-                    run += x[u].x;
-                    y.y = run;
-                    run += x[u].y;
-                    y.z = run;
-                    run += x[u].z;
-                    y.w = run;
-                    run += x[u].w;
-                    v[k + u] = y;
-                }
-            }
-        }
-    } else {
-        for (uint32_t j = lo; j < hi; ++j) {
-            const uint32_t x = d[j];
-            d[j] = run;
-            run += x;
-        }
+    uint32_t run = block_excl_scan<kSortThreads>(sum, s_wave, &total);
+    for (uint32_t j = lo; j < hi; ++j) {
+        const uint32_t x = row[j];
+        row[j] = run;
+        run += x;
     }
-    if (hdr && tid == 0) {
-        const uint32_t old = hdr->n_slots[c];
-        hdr->n_prev[c] = old;
-        uint64_t now = (uint64_t)old + total;
-        if (now > wrows) {
-            atomicOr(&hdr->flags, NGRAM_FLAG_WINDOW_FULL);
-            now = wrows;
-        }
-        hdr->n_slots[c] = (uint32_t)now;
-    }
+    if (tid == 0)
+        tot[c * kRadix + d] = total;
 }
 
 // Stable scatter of one tile by the current digit.  Wave w owns tile keys
@@ -189,7 +183,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(uint32_t *__restrict
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
-    const uint32_t *__restrict__ hist, uint32_t nblk)
+    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk)
 {
     constexpr int kPerWave = kSortTile / (kSortThreads / kWave);
     __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
@@ -213,7 +207,10 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 
     for (int r = tid; r < (kSortThreads / kWave) * kRadix; r += kSortThreads)
         (&s_cnt[0][0])[r] = 0;
-    s_glob[tid] = hist[((size_t)c * kRadix + tid) * nblk + b];
+    {
+        const uint32_t digit_base = block_excl_scan<kSortThreads>(tot[c * kRadix + tid], s_wave, nullptr);
+        s_glob[tid] = digit_base + hist[((size_t)c * kRadix + tid) * nblk + b];
+    }
     __syncthreads();
 
     uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
@@ -277,52 +274,54 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 }
 
 // ------------------------------------------------- heads and window slots
+//
+// mark: every segment head looks its row up in the slot map once; a row
+// already in this window records its slot, a new one the marker kNewHead.
+// assign: new heads get the next free slots in ascending row order (tile
+// prefix + thread prefix: no atomics, deterministic layout).
+
+constexpr uint32_t kNewHead = 0xFFFFFFFEu;
+constexpr uint32_t kDropped = 0xFFFFFFFFu;
 
 struct SlotArgs {
     const uint32_t *rows;   // sorted keys [2][nk]
     int64_t nk;
     const uint32_t *n_dev;
     uint32_t n_host;
-    int32_t *slot_map[2];
+    SlotEntry *slot_map[2];
     uint32_t *slot_rows[2];
-    uint32_t *seg_info;     // [2][nk]
-    uint32_t *blk;          // [2][nblk]
+    uint32_t *seg_info;     // [2][nk]: at heads, slot | new << 31
+    uint32_t *blk;          // [2][nblk]: new heads per tile
     uint32_t nblk;
     uint32_t wrows;
     WsHeader *hdr;
 };
 
 // Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
-__device__ __forceinline__ uint32_t new_heads(const SlotArgs &a, int c, uint32_t n, uint32_t i0,
-                                              uint32_t &mask)
-{
-    const uint32_t *R = a.rows + (size_t)c * a.nk;
-    const int32_t *sm = a.slot_map[c];
-    uint32_t cnt = 0;
-    mask = 0;
-#pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const uint32_t i = i0 + j;
-        if (i < n) {
-            const uint32_t r = R[i];
-            const bool head = (i == 0) || (R[i - 1] != r);
-            if (head && sm[r] < 0) {
-                mask |= 1u << j;
-                ++cnt;
-            }
-        }
-    }
-    return cnt;
-}
-
 __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
     const int c = blockIdx.y;
     const uint32_t n = count_of(a.n_dev, a.n_host);
     const uint32_t i0 = blockIdx.x * kSortTile + threadIdx.x * kSortItems;
-    uint32_t mask;
-    const uint32_t cnt = new_heads(a, c, n, i0, mask);
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const SlotEntry *sm = a.slot_map[c];
+    uint32_t *info = a.seg_info + (size_t)c * a.nk;
+    const uint32_t epoch = a.hdr->epoch;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = i0 + j;
+        if (i < n) {
+            const uint32_t r = R[i];
+            if (i == 0 || R[i - 1] != r) {
+                const SlotEntry e = sm[r];
+                const bool known = e.epoch == epoch;
+                info[i] = known ? e.slot : kNewHead;
+                cnt += known ? 0u : 1u;
+            }
+        }
+    }
     uint32_t total;
     block_excl_scan<kSortThreads>(cnt, s_wave, &total);
     if (threadIdx.x == 0)
@@ -333,35 +332,58 @@ __global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
     const int c = blockIdx.y;
+    const uint32_t b = blockIdx.x;
+    const int tid = threadIdx.x;
     const uint32_t n = count_of(a.n_dev, a.n_host);
-    const uint32_t i0 = blockIdx.x * kSortTile + threadIdx.x * kSortItems;
-    uint32_t mask;
-    const uint32_t cnt = new_heads(a, c, n, i0, mask);
-    const uint32_t off = block_excl_scan<kSortThreads>(cnt, s_wave, nullptr);
-    uint32_t slot = a.hdr->n_prev[c] + a.blk[(size_t)c * a.nblk + blockIdx.x] + off;
+    const uint32_t *blk = a.blk + (size_t)c * a.nblk;
+    // new heads in earlier tiles (block 0 also counts all tiles)
+    const uint32_t upto = b == 0 ? a.nblk : b;
+    uint32_t part = 0, part_before = 0;
+    for (uint32_t k = tid; k < upto; k += kSortThreads) {
+        const uint32_t x = blk[k];
+        part += x;
+        part_before += k < b ? x : 0u;
+    }
+    uint32_t before_tiles, all_tiles;
+    block_excl_scan<kSortThreads>(part_before, s_wave, &before_tiles);
+    block_excl_scan<kSortThreads>(part, s_wave, &all_tiles);
+    const uint32_t old = a.hdr->n_slots[c];
+    if (b == 0 && tid == 0) {
+        uint64_t now = (uint64_t)old + all_tiles;
+        if (now > a.wrows) {
+            atomicOr(&a.hdr->flags, NGRAM_FLAG_WINDOW_FULL);
+            now = a.wrows;
+        }
+        a.hdr->n_next[c] = (uint32_t)now;
+    }
+    const uint32_t i0 = b * kSortTile + tid * kSortItems;
     const uint32_t *R = a.rows + (size_t)c * a.nk;
-    int32_t *sm = a.slot_map[c];
     uint32_t *info = a.seg_info + (size_t)c * a.nk;
+    uint32_t mask = 0, cnt = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
-        if (i >= n)
-            break;
-        const uint32_t r = R[i];
-        const bool head = (i == 0) || (R[i - 1] != r);
-        if (!head)
-            continue;
+        if (i < n && (i == 0 || R[i - 1] != R[i]) && info[i] == kNewHead) {
+            mask |= 1u << j;
+            ++cnt;
+        }
+    }
+    uint32_t slot = old + before_tiles + block_excl_scan<kSortThreads>(cnt, s_wave, nullptr);
+    SlotEntry *sm = a.slot_map[c];
+    const uint32_t epoch = a.hdr->epoch;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
         if (mask & (1u << j)) {
+            const uint32_t i = i0 + j;
+            const uint32_t r = R[i];
             if (slot < a.wrows) {
-                sm[r] = (int32_t)slot;
+                sm[r] = SlotEntry{epoch, slot};
                 a.slot_rows[c][slot] = r;
                 info[i] = slot | 0x80000000u;
             } else {
-                info[i] = 0xFFFFFFFFu;   // window full: row dropped (flagged)
+                info[i] = kDropped;   // window full: row dropped (flagged)
             }
             ++slot;
-        } else {
-            info[i] = (uint32_t)sm[r];
         }
     }
 }
@@ -446,6 +468,8 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
     const uint32_t n = count_of(a.n_dev, a.n_host);
+    if (chunk == 0 && lane == 0)
+        a.hdr->n_slots[c] = a.hdr->n_next[c];   // the slots assign_kernel handed out
     const int64_t c0 = chunk * kChunk;
     if (c0 >= n)
         return;
@@ -629,16 +653,31 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 
 }  // namespace
 
-hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host,
+hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
                          const float *dY, hipStream_t s)
 {
-    if (n_host == 0) {
-        prof_end(NGRAM_PROF_SORT, s);
-        return hipSuccess;
-    }
+    // spread: T keys known on the host; burst: the stash count on the device,
+    // bounded by the stash capacity (grids cover the bound, blocks past the
+    // count exit)
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    const bool burst = tok == nullptr;
+    const uint32_t n_host = (uint32_t)T;
+    const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
+    if (n_host == 0)
+        return hipSuccess;
     const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+    uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
+    uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + L.keys[0]);
+    uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + L.vals[0]);
+
+    prof_begin(NGRAM_PROF_SORT, s);
+    if (burst)
+        keys_tile_kernel<true><<<nblk, kSortThreads, 0, s>>>(nullptr, reinterpret_cast<const uint32_t *>(ws + L.stash_idx),
+                                                            hp, n_host, k0, v0, L.nk, hist, nblk, hdr);
+    else
+        keys_tile_kernel<false><<<nblk, kSortThreads, 0, s>>>(tok, nullptr, hp, n_host, k0, v0, L.nk, hist, nblk,
+                                                             hdr);
     int cur = 0;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = p * kRadixBits;
@@ -646,10 +685,11 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
         uint32_t *vin = reinterpret_cast<uint32_t *>(ws + L.vals[cur]);
         uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
         uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
-        radix_hist_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nblk);
-        scan_kernel<<<2, kScanThreads, 0, s>>>(hist, kRadix * nblk, nullptr, 0);
+        if (p > 0)
+            radix_hist_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nblk);
+        scan_digits_kernel<<<dim3(kRadix, 2), kSortThreads, 0, s>>>(hist, nblk, tot);
         radix_scatter_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
-                                                                    shift, hist, nblk);
+                                                                    shift, hist, tot, nblk);
         cur ^= 1;
     }
     SlotArgs sa;
@@ -658,7 +698,7 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     sa.n_dev = n_dev;
     sa.n_host = n_host;
     for (int c = 0; c < 2; ++c) {
-        sa.slot_map[c] = reinterpret_cast<int32_t *>(ws + L.slot_map[c]);
+        sa.slot_map[c] = reinterpret_cast<SlotEntry *>(ws + L.slot_map[c]);
         sa.slot_rows[c] = reinterpret_cast<uint32_t *>(ws + L.slot_rows[c]);
     }
     sa.seg_info = reinterpret_cast<uint32_t *>(ws + L.seg_info);
@@ -667,7 +707,6 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, 
     sa.wrows = (uint32_t)L.wrows;
     sa.hdr = hdr;
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    scan_kernel<<<2, kScanThreads, 0, s>>>(sa.blk, nblk, hdr, (uint32_t)L.wrows);
     assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     prof_end(NGRAM_PROF_SORT, s);
 

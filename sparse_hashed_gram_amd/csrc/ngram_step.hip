@@ -9,8 +9,10 @@
 //     W[r] -= lr G / (sqrt(v[r]) + eps);   t_last[r] = t
 // One wavefront per row: a lane holds 12 of the 768 values (three 16-byte G
 // loads and three 8-byte bf16 loads, all coalesced), mean(G^2) is a butterfly
-// sum over the wavefront (every lane ends with the same bits), and the row's
-// slot-map entry is cleared in the same pass so the window is empty after it.
+// sum over the wavefront (every lane ends with the same bits).  v and t_last
+// of a row share one 8-byte record, so the row's optimizer state costs one
+// small read and one small write; the window is emptied by advancing its
+// epoch afterwards, not by touching the slot map.
 #include "ngram_dev.hpp"
 
 #include "../../include/ngram.h"
@@ -24,9 +26,7 @@ struct StepArgs {
     const float *gacc;      // [2][wrows][768]
     int64_t wrows;
     uint8_t *w[2];
-    float *v[2];
-    int32_t *tl[2];
-    int32_t *slot_map[2];
+    RowState *st[2];
     WsHeader *hdr;
     int32_t t;
     float lr, beta2, eps;
@@ -58,13 +58,12 @@ struct RowIn {
     uint32_t row;
     float4 g[3];
     float w[3][4];
-    float v;
-    int32_t tl;
+    RowState s;
 };
 
 template <int ELT>
 __device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot, const uint8_t *W,
-                                         const float *V, const int32_t *TL, int lane)
+                                         const RowState *S, int lane)
 {
     const float4 *g4 = reinterpret_cast<const float4 *>(G + (size_t)slot * kDim) + lane;
 #pragma unroll
@@ -91,27 +90,26 @@ __device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot
             r.w[q][3] = x.w;
         }
     }
-    r.v = V[r.row];
-    r.tl = TL[r.row];
+    r.s = S[r.row];
 }
 
 template <int ELT>
-__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, float *V, int32_t *TL,
-                                         int32_t *SM, double one_minus_b2, int lane)
+__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, RowState *S,
+                                         double one_minus_b2, int lane)
 {
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
         ss += r.g[q].x * r.g[q].x + r.g[q].y * r.g[q].y + r.g[q].z * r.g[q].z + r.g[q].w * r.g[q].w;
     ss = wave_sum(ss);
-    int32_t k = a.t - r.tl;
+    int32_t k = a.t - r.s.t_last;
     if (k < 1) {
         if (lane == 0)
             atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
         k = 0;
     }
     const double decay = pow_steps((double)a.beta2, k);
-    const float vn = (float)(decay * (double)r.v + one_minus_b2 * ((double)ss / (double)kDim));
+    const float vn = (float)(decay * (double)r.s.v + one_minus_b2 * ((double)ss / (double)kDim));
     const float scale = a.lr / (sqrtf(vn) + a.eps);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
@@ -131,11 +129,8 @@ __device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W
         for (int q = 0; q < 3; ++q)
             wp[q * kWave] = make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]);
     }
-    if (lane == 0) {
-        V[r.row] = vn;
-        TL[r.row] = a.t;
-        SM[r.row] = -1;
-    }
+    if (lane == 0)
+        S[r.row] = RowState{vn, a.t};
 }
 
 // Each wavefront takes 64 consecutive window slots at a time (one coalesced
@@ -153,9 +148,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const uint32_t *rows = a.slot_rows[c];
     const float *G = a.gacc + (size_t)c * a.wrows * kDim;
     uint8_t *W = a.w[c];
-    float *V = a.v[c];
-    int32_t *TL = a.tl[c];
-    int32_t *SM = a.slot_map[c];
+    RowState *S = a.st[c];
     const double one_minus_b2 = 1.0 - (double)a.beta2;
 
     for (uint32_t base = wid * kWave; base < n; base += nwaves * kWave) {
@@ -167,23 +160,24 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
             for (int k = 0; k < kStepRows; ++k) {
                 if (u + k < cnt) {
                     r[k].row = (uint32_t)__builtin_amdgcn_readlane((int)my_row, (int)(u + k));
-                    load_row<ELT>(r[k], G, base + u + k, W, V, TL, lane);
+                    load_row<ELT>(r[k], G, base + u + k, W, S, lane);
                 }
             }
 #pragma unroll
             for (int k = 0; k < kStepRows; ++k)
                 if (u + k < cnt)
-                    step_row<ELT>(r[k], a, W, V, TL, SM, one_minus_b2, lane);
+                    step_row<ELT>(r[k], a, W, S, one_minus_b2, lane);
         }
     }
 }
 
 __global__ void window_clear_kernel(WsHeader *__restrict__ hdr)
 {
+    hdr->epoch += 1;
     hdr->n_slots[0] = 0;
     hdr->n_slots[1] = 0;
-    hdr->n_prev[0] = 0;
-    hdr->n_prev[1] = 0;
+    hdr->n_next[0] = 0;
+    hdr->n_next[1] = 0;
 }
 
 __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uint32_t *__restrict__ slot_rows,
@@ -208,22 +202,18 @@ __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uin
 
 }  // namespace
 
-hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, float *vb, float *vt,
-                       int32_t *tlb, int32_t *tlt, int32_t t, float lr, float beta2, float eps, hipStream_t s)
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, RowState *sb, RowState *st,
+                       int32_t t, float lr, float beta2, float eps, hipStream_t s)
 {
     StepArgs a;
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c)
         a.slot_rows[c] = reinterpret_cast<const uint32_t *>(ws + L.slot_rows[c]);
-        a.slot_map[c] = reinterpret_cast<int32_t *>(ws + L.slot_map[c]);
-    }
     a.gacc = reinterpret_cast<const float *>(ws + L.gacc);
     a.wrows = L.wrows;
     a.w[0] = (uint8_t *)wb;
     a.w[1] = (uint8_t *)wt;
-    a.v[0] = vb;
-    a.v[1] = vt;
-    a.tl[0] = tlb;
-    a.tl[1] = tlt;
+    a.st[0] = sb;
+    a.st[1] = st;
     a.hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     a.t = t;
     a.lr = lr;

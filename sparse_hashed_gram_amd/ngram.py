@@ -104,7 +104,7 @@ def lib() -> ctypes.CDLL:
             "ngram_embed_fwd": ([cp, vp, vp, vp, i64, vp, vp, vp], ctypes.c_int),
             "ngram_embed_bwd_accum": ([cp, vp, vp, vp, i64, vp], ctypes.c_int),
             "ngram_window_reduce": ([cp, vp, vp], ctypes.c_int),
-            "ngram_sparse_step": ([cp, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
+            "ngram_sparse_step": ([cp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
                                    ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
@@ -195,10 +195,26 @@ def _check_tables(cfg: NgramConfig, W_b, W_t):
             raise ValueError(f"table {c} must be [{cfg.rows[c]}, {DIM}], got {tuple(W.shape)}")
 
 
-def _check_state(cfg: NgramConfig, v_b, v_t, t_last_b, t_last_t):
-    for c, x in ((0, v_b), (1, v_t), (0, t_last_b), (1, t_last_t)):
-        if x.numel() != cfg.rows[c]:
-            raise ValueError(f"optimizer state of channel {c} must have {cfg.rows[c]} entries")
+def new_state(rows: int, device="cuda") -> torch.Tensor:
+    """Optimizer state of a table: float32 [rows, 2], one 8-byte record
+    (v, t_last) per row (ngram_row_state); column 1 holds int32 bits."""
+    return torch.zeros((rows, 2), dtype=torch.float32, device=device)
+
+
+def state_v(st: torch.Tensor) -> torch.Tensor:
+    """The second moments v (a strided float32 view)."""
+    return st[:, 0]
+
+
+def state_t_last(st: torch.Tensor) -> torch.Tensor:
+    """The last-update steps t_last (a strided int32 view)."""
+    return st.view(torch.int32)[:, 1]
+
+
+def _check_state(cfg: NgramConfig, st_b, st_t):
+    for c, x in ((0, st_b), (1, st_t)):
+        if tuple(x.shape) != (cfg.rows[c], 2) or x.dtype != torch.float32:
+            raise ValueError(f"optimizer state of channel {c} must be float32 [{cfg.rows[c]}, 2]")
 
 
 def embed_fwd(cfg: NgramConfig, W_b: torch.Tensor, W_t: torch.Tensor, tokens: torch.Tensor,
@@ -228,15 +244,15 @@ def window_reduce(cfg: NgramConfig, ws: Workspace):
     _check("ngram_window_reduce", lib().ngram_window_reduce(ctypes.byref(cfg), ws.ptr, _stream()))
 
 
-def sparse_step(cfg: NgramConfig, ws: Workspace, W_b, W_t, v_b, v_t, t_last_b, t_last_t, t: int,
+def sparse_step(cfg: NgramConfig, ws: Workspace, W_b, W_t, state_b, state_t, t: int,
                 lr: float, beta2: float, eps: float):
+    """state_b / state_t: float32 [rows, 2] from new_state()."""
     dt = cfg.torch_dtype
     _check_tables(cfg, W_b, W_t)
-    _check_state(cfg, v_b, v_t, t_last_b, t_last_t)
+    _check_state(cfg, state_b, state_t)
     _check("ngram_sparse_step", lib().ngram_sparse_step(
         ctypes.byref(cfg), ws.ptr, _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt),
-        _dev(v_b, "v_b", torch.float32), _dev(v_t, "v_t", torch.float32),
-        _dev(t_last_b, "t_last_b", torch.int32), _dev(t_last_t, "t_last_t", torch.int32),
+        _dev(state_b, "state_b", torch.float32), _dev(state_t, "state_t", torch.float32),
         int(t), float(lr), float(beta2), float(eps), _stream()))
 
 

@@ -42,23 +42,28 @@ def host_vec(x: torch.Tensor, rows: np.ndarray) -> np.ndarray:
 
 
 class State:
-    """Tables and optimizer state of both channels on the device."""
+    """Tables and optimizer state (packed v, t_last records) of both channels."""
 
     def __init__(self, cfg, W_b, W_t):
         self.cfg = cfg
         self.W = [W_b, W_t]
-        self.v = [torch.zeros(cfg.rows[c], dtype=torch.float32, device="cuda") for c in range(2)]
-        self.tl = [torch.zeros(cfg.rows[c], dtype=torch.int32, device="cuda") for c in range(2)]
+        self.st = [ng().new_state(cfg.rows[c]) for c in range(2)]
+
+    @property
+    def v(self):
+        return [ng().state_v(x) for x in self.st]
+
+    @property
+    def tl(self):
+        return [ng().state_t_last(x) for x in self.st]
 
     def clone(self):
         s = State(self.cfg, self.W[0].clone(), self.W[1].clone())
-        s.v = [x.clone() for x in self.v]
-        s.tl = [x.clone() for x in self.tl]
+        s.st = [x.clone() for x in self.st]
         return s
 
     def step(self, ws, t, lr, beta2, eps):
-        ng().sparse_step(self.cfg, ws, self.W[0], self.W[1], self.v[0], self.v[1], self.tl[0],
-                         self.tl[1], t, lr, beta2, eps)
+        ng().sparse_step(self.cfg, ws, self.W[0], self.W[1], self.st[0], self.st[1], t, lr, beta2, eps)
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:

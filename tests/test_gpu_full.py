@@ -50,10 +50,9 @@ def big_state():
             e = min(FULL.rows[c], s + (1 << 21))
             t[s:e] = (torch.randn((e - s, 768), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
         W.append(t)
-    st = {"cfg": cfg, "W": W,
-          "v": [torch.zeros(FULL.rows[c], device="cuda") for c in range(2)],
-          "tl": [torch.zeros(FULL.rows[c], dtype=torch.int32, device="cuda") for c in range(2)],
-          "t": 0}
+    state = [N.new_state(FULL.rows[c]) for c in range(2)]
+    st = {"cfg": cfg, "W": W, "state": state,
+          "v": [N.state_v(x) for x in state], "tl": [N.state_t_last(x) for x in state], "t": 0}
     yield st
     del st
     torch.cuda.empty_cache()
@@ -132,8 +131,8 @@ def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True):
         del G_g
     st["t"] += 1
     t = st["t"]
-    N.sparse_step(cfg, ws, st["W"][0], st["W"][1], st["v"][0], st["v"][1], st["tl"][0], st["tl"][1],
-                  t, FULL.lr, FULL.beta2, FULL.eps)
+    N.sparse_step(cfg, ws, st["W"][0], st["W"][1], st["state"][0], st["state"][1], t, FULL.lr,
+                  FULL.beta2, FULL.eps)
     for c in range(2):
         s = snaps[c]
         W_o, v_o, t_o = oracle.sparse_step(s["G"], s["W"], s["v"], s["tl"], t, FULL.lr, FULL.beta2,
@@ -183,8 +182,8 @@ def test_spread_vs_burst_full_table(big_state):
         seeds = [500 + 4 * win + m for m in range(4)]
         idx = [[N.hash(cfg_s, to_dev(tok))[c] & 0x7FFFFFFF for tok in toks] for c in range(2)]
         rows = [torch.unique(torch.cat(idx[c]).long()) for c in range(2)]
-        keep = [(big_state["W"][c].index_select(0, rows[c]), big_state["v"][c].index_select(0, rows[c]),
-                 big_state["tl"][c].index_select(0, rows[c])) for c in range(2)]
+        keep = [(big_state["W"][c].index_select(0, rows[c]),
+                 big_state["state"][c].index_select(0, rows[c])) for c in range(2)]
         t0 = big_state["t"]
         big_state["cfg"] = cfg_s
         _run_and_check_window(big_state, ws_s, toks, seeds, rs, check_fwd=False)
@@ -192,8 +191,7 @@ def test_spread_vs_burst_full_table(big_state):
                   for c in range(2)]
         for c in range(2):   # restore the touched rows: the state is as before the window
             big_state["W"][c].index_copy_(0, rows[c], keep[c][0])
-            big_state["v"][c].index_copy_(0, rows[c], keep[c][1])
-            big_state["tl"][c].index_copy_(0, rows[c], keep[c][2])
+            big_state["state"][c].index_copy_(0, rows[c], keep[c][1])
         big_state["t"] = t0
         big_state["cfg"] = cfg_b
         _run_and_check_window(big_state, ws_b, toks, seeds, rs, check_fwd=False)
