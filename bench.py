@@ -45,12 +45,22 @@ def parse():
     ap.add_argument("--steps", type=int, default=6, help="timed windows")
     ap.add_argument("--warmup", type=int, default=2, help="untimed windows")
     ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
-    ap.add_argument("--mode", default="spread", choices=["spread", "burst"])
+    ap.add_argument("--mode", default="spread", choices=["spread", "burst", "burst_ref"],
+                    help="spread: each micro-step reduced into the window at once; burst: micro-steps "
+                         "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
+                         "in place at step time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65_536,
                     help="tokens per micro-step in the oracle's bounded sample (0 = all)")
     ap.add_argument("--distinct-windows", type=int, default=4,
                     help="distinct token windows cycled through (inputs stay resident)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 4 GiB fp32 tensor 3 times (the known-size kernel that scales "
+                         "rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes), then exit")
+    ap.add_argument("--path", default="fused", choices=["fused", "accum"],
+                    help="fused: the window's last micro-step goes through ngram_embed_bwd_step "
+                         "(reduction fused with the step); accum: every micro-step through "
+                         "ngram_embed_bwd_accum, then ngram_sparse_step")
     return ap.parse_args()
 
 
@@ -87,22 +97,50 @@ def window_stats(torch, N, cfg, toks):
     return steps, [int(s.numel()) for s in seen]
 
 
-def algorithmic_bytes(w, T, stats, row_bytes):
-    """Bytes each kernel group must move by definition."""
+STATE = 8     # one (v, t_last) record per row
+
+
+def algorithmic_bytes(T, stats, row_bytes, mode, path):
+    """Bytes each kernel group must move per window, by definition (the design doc
+    gives the per-unit figures), and its launches per window.
+
+    accumulate reduction, per micro-step and channel: every key reads its dY
+      row; a row new to the window writes its window row, one already there
+      reads and writes it;
+    fused reduction (last micro-step, or the whole window in burst mode): dY
+      rows; a row already in the window reads its window row; every touched
+      row reads and writes its table row and its state;
+    step: per row left to it, window row read + table row read and written +
+      state read and written + slot id;
+    stash (burst): dY row read and written, token id, two indices, row code;
+    stash (burst by reference): token id, two indices, row code."""
     steps, uwin = stats
-    fwd = T * (3 * row_bytes + 4)                       # 2 rows read + 1 row written + id
-    reduce_ = []
-    for per in steps:
+    A = len(steps)
+    fwd = T * (3 * row_bytes + 4)
+    step_row = ROW_F32 + 2 * row_bytes + 2 * STATE + 4
+    out = {"fwd": [fwd] * A, "sort": [2 * T * 4 * 2 * 4] * A}
+    if mode in ("burst", "burst_ref"):
+        n = A * T
+        copy = 2 * ROW_F32 if mode == "burst" else 0
+        out["stash"] = [T * (copy + 4 + 8 + 4)] * A
+        out["sort"] = [2 * n * 4 * 2 * 4]
+        out["reduce"] = [2 * n * ROW_F32 + sum(uwin) * (2 * row_bytes + 2 * STATE)]
+        out["step"] = [0]
+        return out
+    red = []
+    last = A - 1 if path == "fused" else A
+    for m in range(last):
+        red.append(sum(T * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32 for (u, new) in steps[m]))
+    fused_rows = 0
+    if path == "fused":
         b = 0
-        for (u, new) in per:
-            b += T * ROW_F32                            # every key reads its dY row
-            b += new * ROW_F32 + (u - new) * 2 * ROW_F32  # window row: write new / RMW old
-        reduce_.append(b)
-    sort = 2 * T * 4 * 2 * 4                            # keys+vals, read+write, ~4 passes
-    step = sum(uwin) * (2 * row_bytes + ROW_F32 + 8 + 8 + 4)
-    stash = T * (2 * ROW_F32 + 4 + 8)                   # dY row copied, id read, 2 indices written
-    return {"fwd": fwd, "reduce": float(np.mean(reduce_)), "sort": sort, "step": step,
-            "stash": stash}
+        for (u, new) in steps[-1]:
+            b += T * ROW_F32 + (u - new) * ROW_F32 + u * (2 * row_bytes + 2 * STATE)
+            fused_rows += u
+        red.append(b)
+    out["reduce"] = red
+    out["step"] = [(sum(uwin) - fused_rows) * step_row]
+    return out
 
 
 def src_hash(name):
@@ -181,6 +219,17 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        n = 1 << 30   # 1 Gi floats = 4 GiB read and 4 GiB written per copy
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": 4 * n, "copies": 3}))
+        return
+
     from sparse_hashed_gram_amd import ngram as N
     from sparse_hashed_gram_amd import synth
     from sparse_hashed_gram_amd.hipevents import Event
@@ -208,7 +257,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
 
     t_step = [0]
-    burst = args.mode == "burst"
+    burst = args.mode in ("burst", "burst_ref")
     gid = {"fwd": N.PROF_FWD, "sort": N.PROF_SORT, "reduce": N.PROF_REDUCE, "step": N.PROF_STEP,
            "stash": N.PROF_STASH}
 
@@ -224,16 +273,24 @@ def main():
         for k in range(N.PROF_GROUPS):
             N.profile_events(k, None, None)
 
+    fused_last = args.path == "fused" and not burst
+
     def run_window(k, ev=None):
+        t_step[0] += 1
         for m in range(A):
             arm(ev, ("fwd",))
             N.embed_fwd(cfg, W[0], W[1], toks[k][m], out=out)
             disarm()
+            if fused_last and m == A - 1:
+                arm(ev, ("sort", "reduce", "step"))
+                N.embed_bwd_step(cfg, ws, toks[k][m], dys[m], W[0], W[1], state[0], state[1], t_step[0],
+                                 w.lr, w.beta2, w.eps)
+                disarm()
+                return
             arm(ev, ("stash",) if burst else ("sort", "reduce"))
             N.embed_bwd_accum(cfg, ws, toks[k][m], dys[m])
             disarm()
         arm(ev, ("sort", "reduce", "step") if burst else ("step",))
-        t_step[0] += 1
         N.sparse_step(cfg, ws, W[0], W[1], state[0], state[1], t_step[0], w.lr, w.beta2, w.eps)
         disarm()
 
@@ -254,17 +311,22 @@ def main():
         sys.exit(1)
 
     used = [g_ for g_ in GROUPS if ev[g_]]
-    ms = {g_: float(np.mean([a.elapsed_ms(b) for a, b in ev[g_]])) for g_ in used}
+    ms_all = {g_: [a.elapsed_ms(b) for a, b in ev[g_]] for g_ in used}
     per_step = {g_: len(ev[g_]) // args.steps for g_ in used}
+    ms = {g_: float(np.mean(ms_all[g_])) for g_ in used}
     timed_stats = [stats[i % nwin] for i in range(args.steps)]
-    bytes_ = [algorithmic_bytes(w, T, s, row_bytes) for s in timed_stats]
-    abytes = {g_: float(np.mean([b[g_] for b in bytes_])) for g_ in used}
-    if burst:   # one reduction of the whole window per step
-        abytes["reduce"] *= A
-        abytes["sort"] *= A
+    bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path) for s in timed_stats]
+    # per group: all bytes of its timed launches over all their time
+    abytes = {g_: float(np.sum([sum(b[g_]) for b in bytes_])) / len(ms_all[g_]) for g_ in used}
     upd_rows = float(np.mean([sum(s[1]) for s in timed_stats]))
     total_ms = {g_: ms[g_] * per_step[g_] for g_ in used}
     dom = max([g_ for g_ in ("fwd", "reduce", "step") if g_ in used], key=lambda g_: total_ms[g_])
+    if burst or args.path == "fused":
+        # the step runs (partly) inside the last reduction launch
+        step_ms_per_window = total_ms["step"] + (ms["reduce"] if burst else
+                                                 float(np.mean(ms_all["reduce"][A - 1::A])))
+    else:
+        step_ms_per_window = total_ms["step"]
     kernels = {}
     for g_ in used:
         gbps = abytes[g_] / (ms[g_] * 1e-3) / 1e9
@@ -293,9 +355,11 @@ def main():
         "data": "synthetic: Zipf token streams with EoS-aligned documents, N(0,1) upstream gradients",
         "config": {"workload": w.name, "table_rows": w.rows[0] + w.rows[1], "dim": 768,
                    "table_dtype": w.dtype, "tokens_per_micro_step": T, "accum_steps": A,
-                   "mode": args.mode, "global_batch": A * T},
+                   "mode": args.mode, "path": args.path, "global_batch": A * T},
         "fwd_tokens_per_s": round(T / (ms["fwd"] * 1e-3), 1),
-        "updated_rows_per_s": round(upd_rows / (ms["step"] * 1e-3), 1),
+        # rows stepped per second of the kernels that step them (the step, plus
+        # the fused reduction when the step is fused into it)
+        "updated_rows_per_s": round(upd_rows / (step_ms_per_window * 1e-3), 1),
         "updated_rows_per_step": int(upd_rows),
         "kernels": kernels,
         "roofline": roof,

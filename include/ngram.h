@@ -40,9 +40,10 @@
  *   - All pointers are device pointers unless marked "host".  The caller owns
  *     every buffer; the library never allocates, frees or synchronises in the
  *     hot calls (ngram_hash, ngram_embed_fwd, ngram_embed_bwd_accum,
- *     ngram_window_reduce, ngram_sparse_step, ngram_window_export).  Those
- *     calls only enqueue work on `stream` (a hipStream_t; NULL = the null
- *     stream) and return; they are safe to capture in a HIP graph.
+ *     ngram_embed_bwd_step, ngram_window_reduce, ngram_sparse_step,
+ *     ngram_window_export).  Those calls only enqueue work on `stream` (a
+ *     hipStream_t; NULL = the null stream) and return; they are safe to
+ *     capture in a HIP graph.
  *   - A negative return value is a host-detected error and nothing was
  *     enqueued.  NGRAM_EHIP reports a failed launch.
  *   - Faults only the device can see (token ids outside [0, vocab), more
@@ -70,8 +71,12 @@ extern "C" {
 
 /* how micro-step gradients enter the window (amund.blog, The four
  * improvements, item 4) */
-#define NGRAM_MODE_SPREAD 0 /* reduce each micro-step into the window now */
-#define NGRAM_MODE_BURST 1  /* keep micro-steps; reduce all at step time  */
+#define NGRAM_MODE_SPREAD 0     /* reduce each micro-step into the window now */
+#define NGRAM_MODE_BURST 1      /* keep micro-steps (dY copied into the
+                                   workspace); reduce all at step time       */
+#define NGRAM_MODE_BURST_REF 2  /* as BURST, but dY is not copied: the caller
+                                   keeps every micro-step's dY unchanged until
+                                   the window's step (max_tokens <= 2^25)    */
 
 /* status codes */
 #define NGRAM_OK 0
@@ -103,7 +108,7 @@ typedef struct ngram_config {
     uint64_t seed[2];    /* hash seeds of the two channels                  */
     int64_t max_tokens;  /* largest T of one micro-step, in [1, 2^28]       */
     int32_t accum_steps; /* micro-steps per window, in [1, 64]              */
-    int32_t mode;        /* NGRAM_MODE_SPREAD or NGRAM_MODE_BURST           */
+    int32_t mode;        /* NGRAM_MODE_SPREAD, _BURST or _BURST_REF         */
     int64_t window_rows; /* distinct rows one window can hold per channel;
                             0 = min(max(rows[0], rows[1]),
                                     accum_steps * max_tokens)              */
@@ -159,9 +164,10 @@ int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t,
  * accumulated over accum_steps micro-steps and applied once: the
  * @classiclarryd post; README technique list).  dY: fp32 [T][768], the
  * gradient of `out` for the same tokens.  Spread mode reduces now (dY may be
- * reused once the stream passes this call); burst mode copies tokens' rows
- * and dY into the workspace and reduces at ngram_window_reduce /
- * ngram_sparse_step. */
+ * reused once the stream passes this call); burst mode keeps the tokens' rows
+ * and a copy of dY in the workspace and reduces at ngram_window_reduce /
+ * ngram_sparse_step; burst-by-reference mode keeps the rows and only the
+ * address of dY, which must stay unchanged until the window's step. */
 int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws,
                           const int32_t *tokens, const float *dY, int64_t T,
                           void *stream);
@@ -182,6 +188,19 @@ int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t,
                       ngram_row_state *state_b, ngram_row_state *state_t,
                       int32_t t, float lr, float beta2, float eps,
                       void *stream);
+
+/* The last micro-step of a window fused with the sparse step: the same as
+ * ngram_embed_bwd_accum(tokens, dY, T) followed by ngram_sparse_step(t, ...),
+ * but every row this micro-step touches gets its window gradient completed
+ * and its step applied in the reduction itself, so its gradient never goes
+ * back to memory; the other rows of the window are stepped as usual.  In
+ * burst mode the whole window is reduced this way.  Arguments as for those
+ * two calls; the window is empty afterwards. */
+int ngram_embed_bwd_step(const ngram_config *cfg, void *ws,
+                         const int32_t *tokens, const float *dY, int64_t T,
+                         void *W_b, void *W_t, ngram_row_state *state_b,
+                         ngram_row_state *state_t, int32_t t, float lr,
+                         float beta2, float eps, void *stream);
 
 /* Copies the current window of one channel (0 bigram, 1 trigram) to caller
  * buffers: the first min(n, max_rows) rows (uint32, first-touch order:

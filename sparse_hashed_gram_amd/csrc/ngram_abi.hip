@@ -44,9 +44,11 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->accum_steps < 1 || c->accum_steps > 64)
         return NGRAM_ECONFIG;
-    if (c->mode != NGRAM_MODE_SPREAD && c->mode != NGRAM_MODE_BURST)
+    if (c->mode != NGRAM_MODE_SPREAD && c->mode != NGRAM_MODE_BURST && c->mode != NGRAM_MODE_BURST_REF)
         return NGRAM_ECONFIG;
-    if (c->mode == NGRAM_MODE_BURST && (int64_t)c->accum_steps * c->max_tokens > (int64_t(1) << 30))
+    if (c->mode != NGRAM_MODE_SPREAD && (int64_t)c->accum_steps * c->max_tokens > (int64_t(1) << 30))
+        return NGRAM_ECONFIG;
+    if (c->mode == NGRAM_MODE_BURST_REF && c->max_tokens > (int64_t(1) << 25))
         return NGRAM_ECONFIG;
     if (c->window_rows < 0 || c->window_rows > INT32_MAX)
         return NGRAM_ECONFIG;
@@ -57,7 +59,12 @@ WsLayout layout(const ngram_config *c)
 {
     WsLayout L;
     memset(&L, 0, sizeof(L));
-    L.burst = c->mode == NGRAM_MODE_BURST;
+    L.burst = c->mode != NGRAM_MODE_SPREAD;
+    L.by_ref = c->mode == NGRAM_MODE_BURST_REF;
+    L.accum = c->accum_steps;
+    L.pos_bits = 0;
+    while ((int64_t(1) << L.pos_bits) < c->max_tokens)
+        ++L.pos_bits;
     L.rows[0] = c->rows[0];
     L.rows[1] = c->rows[1];
     const int64_t window_keys = (int64_t)c->accum_steps * c->max_tokens;
@@ -105,8 +112,15 @@ WsLayout layout(const ngram_config *c)
     if (L.burst) {
         L.stash_idx = o;
         o = up(o + 4ull * 2 * (uint64_t)L.nk);
-        L.stash_dy = o;
-        o = up(o + 4ull * (uint64_t)L.nk * kDim);
+        L.stash_pos = o;
+        o = up(o + 4ull * (uint64_t)L.nk);
+        if (L.by_ref) {
+            L.dy_ptrs = o;
+            o = up(o + 8ull * 64);
+        } else {
+            L.stash_dy = o;
+            o = up(o + 4ull * (uint64_t)L.nk * kDim);
+        }
     }
     L.total = o;
     return L;
@@ -255,12 +269,55 @@ int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
         return NGRAM_OK;
     uint8_t *w = (uint8_t *)ws;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_reduce(L, w, hash_params(cfg), nullptr, L.nk,
-                                 reinterpret_cast<const float *>(w + L.stash_dy), s);
+    hipError_t e = launch_reduce(L, w, hash_params(cfg), nullptr, L.nk, nullptr, s);
     if (e == hipSuccess)
         e = launch_stash_clear(L, w, s);
     return hip_status(e);
 }
+
+namespace {
+
+int check_step_args(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
+                    ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps)
+{
+    if (!ws || !W_b || !W_t || !state_b || !state_t)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) ||
+        !aligned(state_t, 8))
+        return NGRAM_EALIGN;
+    if (t < 1 || !isfinite(lr) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !isfinite(eps))
+        return NGRAM_EARG;
+    (void)cfg;
+    return NGRAM_OK;
+}
+
+FuseArgs fuse_args(const ngram_config *cfg, void *W_b, void *W_t, ngram_row_state *state_b,
+                   ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps)
+{
+    FuseArgs f;
+    f.w[0] = (uint8_t *)W_b;
+    f.w[1] = (uint8_t *)W_t;
+    f.st[0] = reinterpret_cast<RowState *>(state_b);
+    f.st[1] = reinterpret_cast<RowState *>(state_t);
+    f.p = StepParams{t, lr, beta2, eps};
+    f.dtype = cfg->dtype;
+    return f;
+}
+
+// Burst mode: reduce the kept micro-steps fused with the step, then step the
+// rows the window held from an earlier explicit reduce (if any) and end the
+// window.
+int burst_step(const ngram_config *cfg, const WsLayout &L, uint8_t *w, const FuseArgs &f, hipStream_t s)
+{
+    hipError_t e = launch_reduce_step(L, w, hash_params(cfg), nullptr, L.nk, nullptr, f, s);
+    if (e == hipSuccess)
+        e = launch_stash_clear(L, w, s);
+    if (e == hipSuccess)
+        e = launch_step(L, w, cfg->dtype, f.w[0], f.w[1], f.st[0], f.st[1], f.p.t, f.p.lr, f.p.beta2, f.p.eps, s);
+    return hip_status(e);
+}
+
+}  // namespace
 
 int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
                       ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps, void *stream)
@@ -269,19 +326,49 @@ int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, n
     int rc = check_cfg(cfg);
     if (rc)
         return rc;
-    if (!ws || !W_b || !W_t || !state_b || !state_t)
-        return NGRAM_ENULL;
-    if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) ||
-        !aligned(state_t, 8))
-        return NGRAM_EALIGN;
-    if (t < 1 || !isfinite(lr) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !isfinite(eps))
-        return NGRAM_EARG;
-    if ((rc = ngram_window_reduce(cfg, ws, stream)))
+    if ((rc = check_step_args(cfg, ws, W_b, W_t, state_b, state_t, t, lr, beta2, eps)))
         return rc;
     const WsLayout L = layout(cfg);
-    return hip_status(launch_step(L, (uint8_t *)ws, cfg->dtype, W_b, W_t, reinterpret_cast<RowState *>(state_b),
-                                  reinterpret_cast<RowState *>(state_t), t, lr, beta2, eps,
-                                  (hipStream_t)stream));
+    uint8_t *w = (uint8_t *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    const FuseArgs f = fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps);
+    if (L.burst)
+        return burst_step(cfg, L, w, f, s);
+    return hip_status(launch_step(L, w, cfg->dtype, W_b, W_t, f.st[0], f.st[1], t, lr, beta2, eps, s));
+}
+
+int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *tokens, const float *dY, int64_t T,
+                         void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t, int32_t t,
+                         float lr, float beta2, float eps, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_tokens(cfg, tokens, T)))
+        return rc;
+    if (T > 0 && !dY)
+        return NGRAM_ENULL;
+    if (!aligned(dY, 16))
+        return NGRAM_EALIGN;
+    if ((rc = check_step_args(cfg, ws, W_b, W_t, state_b, state_t, t, lr, beta2, eps)))
+        return rc;
+    const WsLayout L = layout(cfg);
+    uint8_t *w = (uint8_t *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    const FuseArgs f = fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps);
+    const HashParams hp = hash_params(cfg);
+    if (L.burst) {
+        hipError_t e = launch_stash(L, w, hp, tokens, dY, T, s);
+        if (e != hipSuccess)
+            return NGRAM_EHIP;
+        return burst_step(cfg, L, w, f, s);
+    }
+    hipError_t e = hipSuccess;
+    if (T > 0)
+        e = launch_reduce_step(L, w, hp, tokens, T, dY, f, s);
+    if (e == hipSuccess)
+        e = launch_step(L, w, cfg->dtype, W_b, W_t, f.st[0], f.st[1], t, lr, beta2, eps, s);
+    return hip_status(e);
 }
 
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, uint32_t *rows, float *G,

@@ -99,7 +99,8 @@ struct WsHeader {
     uint32_t n_owner[2];   // long-segment fix-up records of the current reduce
     uint32_t n_stash;      // burst mode: positions kept since the last reduce
     uint32_t epoch;        // window number; slot-map entries of other windows are stale
-    uint32_t pad[54];
+    uint32_t n_micro;      // burst modes: micro-steps kept since the last reduce
+    uint32_t pad[53];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
@@ -142,8 +143,10 @@ struct WsLayout {
     uint64_t blk;           // uint32 [2][nblk]
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
-    uint64_t stash_idx;     // uint32 [2][nk] (burst)
-    uint64_t stash_dy;      // fp32 [nk][768] (burst)
+    uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
+    uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
+    uint64_t stash_dy;      // fp32 [nk][768] (burst, copying): the kept dY rows
+    uint64_t dy_ptrs;       // const float * [64] (burst by reference): dY of each micro-step
     uint64_t total;
 
     int64_t rows[2];
@@ -152,8 +155,70 @@ struct WsLayout {
     int64_t nblk;           // sort tiles for nk keys
     int64_t nchunk;         // 64-key chunks for nk keys
     int passes;             // radix passes (8 bits each)
-    bool burst;
+    bool burst;             // micro-steps are kept and reduced at step time
+    bool by_ref;            // ... and their dY is read where the caller keeps it
+    int pos_bits;           // by_ref: dY row code = micro-step << pos_bits | position
+    int accum;              // micro-steps per window
 };
+
+// -------------------------------------------------------------- row step
+//
+// The lazy row-wise step (Adam with beta1 = 0, one second moment per row,
+// beta2 applied for every optimizer step the row missed): given the row's
+// window gradient G (its sum of squares sum_g2) and its state, returns the
+// factor lr / (sqrt(v') + eps) that multiplies G, and v' itself.
+
+struct StepParams {
+    int32_t t;
+    float lr;
+    float beta2;
+    float eps;
+};
+
+// beta2^k by square-and-multiply in fp64 (relative error below k * 2^-52).
+__device__ __forceinline__ double pow_steps(double b, int32_t k)
+{
+    double r = 1.0;
+    while (k > 0) {
+        if (k & 1)
+            r *= b;
+        b *= b;
+        k >>= 1;
+    }
+    return r;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1)
+        x += __shfl_xor(x, d);
+    return x;
+}
+
+// order_bad: t does not exceed t_last (the row then decays by beta2^0).
+__device__ __forceinline__ float step_scale(float sum_g2, RowState s, const StepParams &p, float &vn,
+                                            bool &order_bad)
+{
+    int32_t k = p.t - s.t_last;
+    order_bad = k < 1;
+    if (k < 1)
+        k = 0;
+    const double decay = pow_steps((double)p.beta2, k);
+    vn = (float)(decay * (double)s.v + (1.0 - (double)p.beta2) * ((double)sum_g2 / (double)kDim));
+    return p.lr / (sqrtf(vn) + p.eps);
+}
+
+// Tables and state the fused reduce + step writes.
+struct FuseArgs {
+    uint8_t *w[2];
+    RowState *st[2];
+    StepParams p;
+    int dtype;
+};
+
+// Slot rows whose step already ran inside the fused reduction carry this bit.
+constexpr uint32_t kSlotStepped = 0x80000000u;
 
 // ------------------------------------------------------------- profiling
 // Optional event pairs per kernel group (ngram_profile_events); thread-local.
@@ -195,6 +260,12 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp,
 // rows into the window.
 hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
                          int64_t T, const float *dY, hipStream_t s);
+// The same reduction fused with the sparse step: each row's gradient of the
+// window is completed (with what the window already holds for it) and the
+// row is stepped at once; rows only the window holds are left for
+// launch_step, which skips the stepped ones.
+hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
+                              int64_t T, const float *dY, const FuseArgs &f, hipStream_t s);
 
 // Burst: mark the stash empty after a reduce.
 hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);

@@ -116,17 +116,22 @@ __global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashPara
     idx[T + i] = it;
 }
 
-// Burst mode: keep the packed indices and the dY rows of one micro-step at
-// the end of the stash.  One block per 16 positions: 16 threads hash, all
-// 256 threads copy the 16 x 192 float4 of dY.
+// Burst modes: keep the packed indices of one micro-step at the end of the
+// stash, with each position's dY row code: the stash position itself when the
+// dY rows are copied next to it (copying burst), or micro-step << pos_bits |
+// position when dY stays where the caller keeps it (burst by reference).
+// One block per 16 positions: 16 threads hash; when copying, all 256 threads
+// copy the 16 x 192 float4 of dY.
 constexpr int kStashTok = 16;
+template <bool BY_REF>
 __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const float *__restrict__ dY,
                                                     int64_t T, HashParams hp, uint32_t *__restrict__ sidx,
-                                                    float *__restrict__ sdy, int64_t nk,
-                                                    WsHeader *__restrict__ hdr)
+                                                    uint32_t *__restrict__ spos, float *__restrict__ sdy, int64_t nk,
+                                                    int pos_bits, int accum, WsHeader *__restrict__ hdr)
 {
     const uint32_t base = hdr->n_stash;
-    if ((int64_t)base + T > nk)
+    const uint32_t m = hdr->n_micro;
+    if ((int64_t)base + T > nk || (BY_REF && (int)m >= accum))
         return;   // flagged by stash_advance_kernel
     const int64_t t0 = (int64_t)blockIdx.x * kStashTok;
     const int tid = threadIdx.x;
@@ -137,24 +142,37 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
             atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
         sidx[base + i] = ib;
         sidx[nk + base + i] = it;
+        spos[base + i] = BY_REF ? (m << pos_bits) | (uint32_t)i : base + (uint32_t)i;
     }
-    const int ntok = (int)min<int64_t>(kStashTok, T - t0);
-    const float4 *src = reinterpret_cast<const float4 *>(dY + (size_t)t0 * kDim);
-    float4 *dst = reinterpret_cast<float4 *>(sdy + ((size_t)base + t0) * kDim);
-    for (int e = tid; e < ntok * (kDim / 4); e += 256)
-        dst[e] = src[e];
+    if (!BY_REF) {
+        const int ntok = (int)min<int64_t>(kStashTok, T - t0);
+        const float4 *src = reinterpret_cast<const float4 *>(dY + (size_t)t0 * kDim);
+        float4 *dst = reinterpret_cast<float4 *>(sdy + ((size_t)base + t0) * kDim);
+        for (int e = tid; e < ntok * (kDim / 4); e += 256)
+            dst[e] = src[e];
+    }
 }
 
-__global__ void stash_advance_kernel(int64_t T, int64_t nk, WsHeader *__restrict__ hdr)
+__global__ void stash_advance_kernel(int64_t T, int64_t nk, int accum, const float *dY,
+                                     const float **__restrict__ dy_ptrs, WsHeader *__restrict__ hdr)
 {
     const uint32_t base = hdr->n_stash;
-    if ((int64_t)base + T > nk)
+    const uint32_t m = hdr->n_micro;
+    if ((int64_t)base + T > nk || (dy_ptrs && (int)m >= accum)) {
         atomicOr(&hdr->flags, NGRAM_FLAG_STASH_FULL);
-    else
-        hdr->n_stash = base + (uint32_t)T;
+        return;
+    }
+    if (dy_ptrs)
+        dy_ptrs[m] = dY;
+    hdr->n_stash = base + (uint32_t)T;
+    hdr->n_micro = m + 1;
 }
 
-__global__ void stash_clear_kernel(WsHeader *__restrict__ hdr) { hdr->n_stash = 0; }
+__global__ void stash_clear_kernel(WsHeader *__restrict__ hdr)
+{
+    hdr->n_stash = 0;
+    hdr->n_micro = 0;
+}
 
 __global__ void flags_clear_kernel(WsHeader *__restrict__ hdr) { hdr->flags = 0; }
 
@@ -216,12 +234,20 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
                         const float *dY, int64_t T, hipStream_t s)
 {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
+    uint32_t *spos = reinterpret_cast<uint32_t *>(ws + L.stash_pos);
     prof_begin(NGRAM_PROF_STASH, s);
-    if (T > 0)
-        stash_kernel<<<grid_for(T, kStashTok), 256, 0, s>>>(
-            tok, dY, T, hp, reinterpret_cast<uint32_t *>(ws + L.stash_idx),
-            reinterpret_cast<float *>(ws + L.stash_dy), L.nk, hdr);
-    stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, hdr);
+    if (T > 0) {
+        if (L.by_ref)
+            stash_kernel<true><<<grid_for(T, kStashTok), 256, 0, s>>>(tok, dY, T, hp, sidx, spos, nullptr, L.nk,
+                                                                      L.pos_bits, L.accum, hdr);
+        else
+            stash_kernel<false><<<grid_for(T, kStashTok), 256, 0, s>>>(
+                tok, dY, T, hp, sidx, spos, reinterpret_cast<float *>(ws + L.stash_dy), L.nk, L.pos_bits, L.accum,
+                hdr);
+    }
+    stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, L.accum, dY,
+                                         L.by_ref ? reinterpret_cast<const float **>(ws + L.dy_ptrs) : nullptr, hdr);
     prof_end(NGRAM_PROF_STASH, s);
     return hipGetLastError();
 }

@@ -88,9 +88,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave
 // Also clears the fix-up record counts of the reduce that follows.
 template <bool FROM_STASH>
 __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
-    const int32_t *__restrict__ tok, const uint32_t *__restrict__ sidx, HashParams hp, uint32_t n_host,
-    uint32_t *__restrict__ keys, uint32_t *__restrict__ vals, int64_t nk, uint32_t *__restrict__ hist,
-    uint32_t nblk, WsHeader *__restrict__ hdr)
+    const int32_t *__restrict__ tok, const uint32_t *__restrict__ sidx, const uint32_t *__restrict__ spos,
+    HashParams hp, uint32_t n_host, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals, int64_t nk,
+    uint32_t *__restrict__ hist, uint32_t nblk, WsHeader *__restrict__ hdr)
 {
     __shared__ uint32_t h[2][kRadix];
     const int tid = threadIdx.x;
@@ -109,17 +109,18 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = base + j * kSortThreads + tid;
         if (i < n) {
-            uint32_t ib, it;
+            uint32_t ib, it, pos = i;
             if (FROM_STASH) {
                 ib = sidx[i];
                 it = sidx[nk + i];
+                pos = spos[i];
             } else {
                 bad |= ngram_index(tok, i, hp, ib, it);
             }
             keys[i] = ib & 0x7FFFFFFFu;
-            vals[i] = i | (ib & 0x80000000u);
+            vals[i] = pos | (ib & 0x80000000u);
             keys[nk + i] = it & 0x7FFFFFFFu;
-            vals[nk + i] = i | (it & 0x80000000u);
+            vals[nk + i] = pos | (it & 0x80000000u);
             atomicAdd(&h[0][ib & (kRadix - 1)], 1u);
             atomicAdd(&h[1][it & (kRadix - 1)], 1u);
         }
@@ -393,25 +394,43 @@ __global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
 constexpr int kRedThreads = 256;
 constexpr int kRedU = 4;   // dY rows in flight per wavefront
 
+// Reduction modes: accumulate into the window, or fused with the step on a
+// bf16 / fp32 table.
+constexpr int kAccum = 0;
+constexpr int kFuseBf16 = 2;
+constexpr int kFuseF32 = 4;
+
 struct RedArgs {
     const uint32_t *rows;   // sorted [2][nk]
-    const uint32_t *vals;   // sorted [2][nk]: position | neg << 31
+    const uint32_t *vals;   // sorted [2][nk]: dY row code | neg << 31
     const uint32_t *info;   // [2][nk] at heads
     int64_t nk;
     const uint32_t *n_dev;
     uint32_t n_host;
-    const float *dY;        // [positions][768]
+    const float *dY;        // [positions][768], indexed by the row code
+    const float *const *dy_ptrs;   // burst by reference: dY of each micro-step
+    int pos_bits;           // burst by reference: row code = micro-step << pos_bits | position
     float *gacc;            // [2][wrows][768]
+    uint32_t *slot_rows[2];
     int64_t wrows;
     float *partial;         // [2][nchunk][2][768]
     uint64_t *owners;       // [2][nchunk]: chunk | info << 32
     int64_t nchunk;
     WsHeader *hdr;
+    FuseArgs f;             // fused modes only
 };
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b)
 {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Start of the dY row a key refers to.
+__device__ __forceinline__ const float *dy_row(const RedArgs &a, uint32_t code)
+{
+    if (a.dy_ptrs)
+        return a.dy_ptrs[code >> a.pos_bits] + (size_t)(code & ((1u << a.pos_bits) - 1u)) * kDim;
+    return a.dY + (size_t)code * kDim;
 }
 
 __device__ __forceinline__ uint32_t lane_val(uint32_t v0, uint32_t v1, int j)
@@ -421,8 +440,8 @@ __device__ __forceinline__ uint32_t lane_val(uint32_t v0, uint32_t v1, int j)
 }
 
 // Lane l of a wavefront holds elements l + 64 m (m = 0..11) of a 768-wide
-// row, so every load, store and atomic of a row is twelve 256-byte contiguous
-// wavefront accesses.
+// row, so every load, store and atomic of a row is twelve 256-byte (fp32) or
+// 128-byte (bf16) contiguous wavefront accesses.
 constexpr int kPer = kDim / kWave;   // 12
 
 __device__ __forceinline__ void store_row(float *dst, const float (&acc)[kPer], int lane)
@@ -441,7 +460,7 @@ __device__ __forceinline__ void store_row(float *dst, const float (&acc)[kPer], 
 __device__ __forceinline__ void flush_window_row(const float (&acc)[kPer], float *gacc, int64_t wrows, int c,
                                                  uint32_t info, int lane)
 {
-    if (info == 0xFFFFFFFFu)
+    if (info == kDropped)
         return;   // window full: row dropped (flagged when slots were assigned)
     float *g = gacc + ((size_t)c * wrows + (info & 0x7FFFFFFFu)) * kDim;
     if (info >> 31) {
@@ -453,22 +472,79 @@ __device__ __forceinline__ void flush_window_row(const float (&acc)[kPer], float
     }
 }
 
+// Fused flush: the row's window gradient is complete.  A row the window
+// already holds adds its stored gradient first (G = G_window + S, the same
+// addition the accumulate path would make) and its slot is marked stepped;
+// then the row is stepped in place.
+template <int MODE>
+__device__ __forceinline__ void flush_fused(float (&acc)[kPer], const RedArgs &a, int c, uint32_t row,
+                                            uint32_t info, int lane)
+{
+    if (info != kNewHead) {
+        const float *g = a.gacc + ((size_t)c * a.wrows + info) * kDim + lane;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            acc[m] = g[m * kWave] + acc[m];
+        if (lane == 0)
+            a.slot_rows[c][info] = row | kSlotStepped;
+    }
+    float w[kPer];
+    if (MODE == kFuseBf16) {
+        const uint16_t *wp = reinterpret_cast<const uint16_t *>(a.f.w[c]) + (size_t)row * kDim + lane;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            w[m] = __uint_as_float((uint32_t)wp[m * kWave] << 16);
+    } else {
+        const float *wp = reinterpret_cast<const float *>(a.f.w[c]) + (size_t)row * kDim + lane;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            w[m] = wp[m * kWave];
+    }
+    const RowState st = a.f.st[c][row];
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+        ss += acc[m] * acc[m];
+    ss = wave_sum(ss);
+    float vn;
+    bool order_bad;
+    const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
+    if (MODE == kFuseBf16) {
+        uint16_t *wp = reinterpret_cast<uint16_t *>(a.f.w[c]) + (size_t)row * kDim + lane;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            wp[m * kWave] = (uint16_t)bf16_rne(w[m] - scale * acc[m]);
+    } else {
+        float *wp = reinterpret_cast<float *>(a.f.w[c]) + (size_t)row * kDim + lane;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            wp[m * kWave] = w[m] - scale * acc[m];
+    }
+    if (lane == 0) {
+        a.f.st[c][row] = RowState{vn, a.f.p.t};
+        if (order_bad)
+            atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+    }
+}
+
 // One wavefront per 64 sorted keys.  Keys are consumed in order, kRedU dY rows
 // in flight at a time, whatever the segment boundaries.  A segment's sum is
 // reset at its first key and flushed at its last:
-//   - a segment that starts and ends here goes to the window;
+//   - a segment that starts and ends here goes to the window (or, fused, is
+//     completed and stepped);
 //   - the first piece, if it continues a segment from the previous chunk, is
 //     skipped when that chunk finishes it, else left as partial row 0;
 //   - the last piece, if it spills into the next chunk, is finished here when
 //     it ends within that chunk (its keys are loaded as lanes 64..127), else
 //     left as partial row 1 with a fix-up record.
+template <int MODE>
 __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
     const uint32_t n = count_of(a.n_dev, a.n_host);
-    if (chunk == 0 && lane == 0)
+    if (MODE == kAccum && chunk == 0 && lane == 0)
         a.hdr->n_slots[c] = a.hdr->n_next[c];   // the slots assign_kernel handed out
     const int64_t c0 = chunk * kChunk;
     if (c0 >= n)
@@ -531,7 +607,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
             if (j + u < jend) {
                 const uint32_t v = lane_val(v0, v1, j + u);
                 sg[u] = v & 0x80000000u;
-                const float *p = a.dY + (size_t)(v & 0x7FFFFFFFu) * kDim + lane;
+                const float *p = dy_row(a, v & 0x7FFFFFFFu) + lane;
 #pragma unroll
                 for (int m = 0; m < kPer; ++m)
                     x[u][m] = p[m * kWave];
@@ -572,7 +648,10 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
                 }
             } else {
                 const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, ps);
-                flush_window_row(acc, a.gacc, a.wrows, c, info, lane);
+                if (MODE == kAccum)
+                    flush_window_row(acc, a.gacc, a.wrows, c, info, lane);
+                else
+                    flush_fused<MODE>(acc, a, c, (uint32_t)__builtin_amdgcn_readlane((int)r0, ps), info, lane);
             }
         }
     }
@@ -580,12 +659,15 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 
 // Sums the partial rows of each segment longer than two chunks: the starting
 // chunk's tail piece, then every following chunk's head piece, split into 16
-// contiguous runs (one per wavefront) that are added in run order.
+// contiguous runs (one per wavefront) that are added in run order.  Then the
+// row goes to the window, or (fused) is completed and stepped by the block.
 constexpr int kFixThreads = 1024;
+template <int MODE>
 __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 {
     constexpr int kW = kFixThreads / kWave;
     __shared__ float4 s_part[kW][kDim / 4];
+    __shared__ float s_ss[kW];
     const int c = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -637,15 +719,58 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
         for (int q = 0; q < 3; ++q)
             s_part[w][lane + q * kWave] = acc[q];
         __syncthreads();
-        if (tid < kDim / 4 && info != 0xFFFFFFFFu) {
-            float4 s = s_part[0][tid];
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tid < kDim / 4) {
+            sum = s_part[0][tid];
 #pragma unroll
             for (int ww = 1; ww < kW; ++ww)
-                s = add4(s, s_part[ww][tid]);
-            float4 *g = reinterpret_cast<float4 *>(a.gacc + ((size_t)c * a.wrows + (info & 0x7FFFFFFFu)) * kDim) + tid;
-            if (!(info >> 31))
-                s = add4(*g, s);
-            *g = s;
+                sum = add4(sum, s_part[ww][tid]);
+        }
+        if (MODE == kAccum) {
+            if (tid < kDim / 4 && info != kDropped) {
+                float4 *g = reinterpret_cast<float4 *>(a.gacc + ((size_t)c * a.wrows + (info & 0x7FFFFFFFu)) * kDim) + tid;
+                if (!(info >> 31))
+                    sum = add4(*g, sum);
+                *g = sum;
+            }
+        } else {
+            // complete the row's window gradient, then step it with the block:
+            // thread t < 192 owns elements 4t .. 4t+3
+            if (tid < kDim / 4 && info != kNewHead)
+                sum = add4(reinterpret_cast<const float4 *>(a.gacc + ((size_t)c * a.wrows + info) * kDim)[tid], sum);
+            if (tid == 0 && info != kNewHead)
+                a.slot_rows[c][info] = row | kSlotStepped;
+            float ss = tid < kDim / 4 ? sum.x * sum.x + sum.y * sum.y + sum.z * sum.z + sum.w * sum.w : 0.f;
+            ss = wave_sum(ss);
+            if (lane == 0)
+                s_ss[w] = ss;
+            __syncthreads();
+            ss = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kW; ++ww)
+                ss += s_ss[ww];
+            const RowState st = a.f.st[c][row];
+            float vn;
+            bool order_bad;
+            const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
+            if (tid < kDim / 4) {
+                if (MODE == kFuseBf16) {
+                    uint2 *wp = reinterpret_cast<uint2 *>(a.f.w[c] + (size_t)row * kDim * 2) + tid;
+                    const uint2 x = *wp;
+                    *wp = make_uint2(bf16_pack(bf16_lo(x.x) - scale * sum.x, bf16_hi(x.x) - scale * sum.y),
+                                     bf16_pack(bf16_lo(x.y) - scale * sum.z, bf16_hi(x.y) - scale * sum.w));
+                } else {
+                    float4 *wp = reinterpret_cast<float4 *>(a.f.w[c] + (size_t)row * kDim * 4) + tid;
+                    const float4 x = *wp;
+                    *wp = make_float4(x.x - scale * sum.x, x.y - scale * sum.y, x.z - scale * sum.z,
+                                      x.w - scale * sum.w);
+                }
+            }
+            if (tid == 0) {
+                a.f.st[c][row] = RowState{vn, a.f.p.t};
+                if (order_bad)
+                    atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+            }
         }
         __syncthreads();
     }
@@ -653,8 +778,10 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 
 }  // namespace
 
-hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
-                         const float *dY, hipStream_t s)
+namespace {
+
+hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                       const float *dY, const FuseArgs *f, hipStream_t s)
 {
     // spread: T keys known on the host; burst: the stash count on the device,
     // bounded by the stash capacity (grids cover the bound, blocks past the
@@ -673,11 +800,12 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, c
 
     prof_begin(NGRAM_PROF_SORT, s);
     if (burst)
-        keys_tile_kernel<true><<<nblk, kSortThreads, 0, s>>>(nullptr, reinterpret_cast<const uint32_t *>(ws + L.stash_idx),
-                                                            hp, n_host, k0, v0, L.nk, hist, nblk, hdr);
+        keys_tile_kernel<true><<<nblk, kSortThreads, 0, s>>>(
+            nullptr, reinterpret_cast<const uint32_t *>(ws + L.stash_idx),
+            reinterpret_cast<const uint32_t *>(ws + L.stash_pos), hp, n_host, k0, v0, L.nk, hist, nblk, hdr);
     else
-        keys_tile_kernel<false><<<nblk, kSortThreads, 0, s>>>(tok, nullptr, hp, n_host, k0, v0, L.nk, hist, nblk,
-                                                             hdr);
+        keys_tile_kernel<false><<<nblk, kSortThreads, 0, s>>>(tok, nullptr, nullptr, hp, n_host, k0, v0, L.nk, hist,
+                                                             nblk, hdr);
     int cur = 0;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = p * kRadixBits;
@@ -707,7 +835,8 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, c
     sa.wrows = (uint32_t)L.wrows;
     sa.hdr = hdr;
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+    if (!f)   // fused: rows new to the window are stepped at once and need no slot
+        assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     prof_end(NGRAM_PROF_SORT, s);
 
     RedArgs ra;
@@ -717,20 +846,51 @@ hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, c
     ra.nk = L.nk;
     ra.n_dev = n_dev;
     ra.n_host = n_host;
-    ra.dY = dY;
+    ra.dY = burst && !L.by_ref ? reinterpret_cast<const float *>(ws + L.stash_dy) : dY;
+    ra.dy_ptrs = L.by_ref ? reinterpret_cast<const float *const *>(ws + L.dy_ptrs) : nullptr;
+    ra.pos_bits = L.pos_bits;
     ra.gacc = reinterpret_cast<float *>(ws + L.gacc);
+    ra.slot_rows[0] = sa.slot_rows[0];
+    ra.slot_rows[1] = sa.slot_rows[1];
     ra.wrows = L.wrows;
     ra.partial = reinterpret_cast<float *>(ws + L.partial);
     ra.owners = reinterpret_cast<uint64_t *>(ws + L.owners);
     ra.nchunk = L.nchunk;
     ra.hdr = hdr;
+    if (f)
+        ra.f = *f;
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
     const uint32_t per_block = kRedThreads / kWave;
+    const dim3 grid((nchunk + per_block - 1) / per_block, 2);
     prof_begin(NGRAM_PROF_REDUCE, s);
-    seg_reduce_kernel<<<dim3((nchunk + per_block - 1) / per_block, 2), kRedThreads, 0, s>>>(ra);
-    prof_end(NGRAM_PROF_REDUCE, s);
-    fixup_kernel<<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    if (!f) {
+        seg_reduce_kernel<kAccum><<<grid, kRedThreads, 0, s>>>(ra);
+        prof_end(NGRAM_PROF_REDUCE, s);
+        fixup_kernel<kAccum><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    } else if (f->dtype == NGRAM_DTYPE_BF16) {
+        seg_reduce_kernel<kFuseBf16><<<grid, kRedThreads, 0, s>>>(ra);
+        prof_end(NGRAM_PROF_REDUCE, s);
+        fixup_kernel<kFuseBf16><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    } else {
+        seg_reduce_kernel<kFuseF32><<<grid, kRedThreads, 0, s>>>(ra);
+        prof_end(NGRAM_PROF_REDUCE, s);
+        fixup_kernel<kFuseF32><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+    }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                         const float *dY, hipStream_t s)
+{
+    return reduce_impl(L, ws, hp, tok, T, dY, nullptr, s);
+}
+
+hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                              const float *dY, const FuseArgs &f, hipStream_t s)
+{
+    return reduce_impl(L, ws, hp, tok, T, dY, &f, s);
 }
 
 }  // namespace ngram

@@ -28,30 +28,8 @@ struct StepArgs {
     uint8_t *w[2];
     RowState *st[2];
     WsHeader *hdr;
-    int32_t t;
-    float lr, beta2, eps;
+    StepParams p;
 };
-
-// beta2^k by square-and-multiply in fp64 (relative error below k * 2^-52).
-__device__ __forceinline__ double pow_steps(double b, int32_t k)
-{
-    double r = 1.0;
-    while (k > 0) {
-        if (k & 1)
-            r *= b;
-        b *= b;
-        k >>= 1;
-    }
-    return r;
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1)
-        x += __shfl_xor(x, d);
-    return x;
-}
 
 // Row state of one touched row while it is being stepped.
 struct RowIn {
@@ -94,23 +72,18 @@ __device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot
 }
 
 template <int ELT>
-__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, RowState *S,
-                                         double one_minus_b2, int lane)
+__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, RowState *S, int lane)
 {
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
         ss += r.g[q].x * r.g[q].x + r.g[q].y * r.g[q].y + r.g[q].z * r.g[q].z + r.g[q].w * r.g[q].w;
     ss = wave_sum(ss);
-    int32_t k = a.t - r.s.t_last;
-    if (k < 1) {
-        if (lane == 0)
-            atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
-        k = 0;
-    }
-    const double decay = pow_steps((double)a.beta2, k);
-    const float vn = (float)(decay * (double)r.s.v + one_minus_b2 * ((double)ss / (double)kDim));
-    const float scale = a.lr / (sqrtf(vn) + a.eps);
+    float vn;
+    bool order_bad;
+    const float scale = step_scale(ss, r.s, a.p, vn, order_bad);
+    if (order_bad && lane == 0)
+        atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         r.w[q][0] -= scale * r.g[q].x;
@@ -130,12 +103,13 @@ __device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W
             wp[q * kWave] = make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]);
     }
     if (lane == 0)
-        S[r.row] = RowState{vn, a.t};
+        S[r.row] = RowState{vn, a.p.t};
 }
 
 // Each wavefront takes 64 consecutive window slots at a time (one coalesced
 // load of their row ids), then steps them two rows per iteration with both
-// rows' loads in flight together.
+// rows' loads in flight together.  Slots whose row was already stepped by
+// the fused reduction (kSlotStepped) are skipped.
 constexpr int kStepRows = 2;
 template <int ELT>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
@@ -149,24 +123,27 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const float *G = a.gacc + (size_t)c * a.wrows * kDim;
     uint8_t *W = a.w[c];
     RowState *S = a.st[c];
-    const double one_minus_b2 = 1.0 - (double)a.beta2;
 
     for (uint32_t base = wid * kWave; base < n; base += nwaves * kWave) {
         const uint32_t cnt = min((uint32_t)kWave, n - base);
         const uint32_t my_row = lane < (int)cnt ? rows[base + lane] : 0u;
         for (uint32_t u = 0; u < cnt; u += kStepRows) {
             RowIn r[kStepRows];
+            bool live[kStepRows];
 #pragma unroll
             for (int k = 0; k < kStepRows; ++k) {
+                live[k] = false;
                 if (u + k < cnt) {
                     r[k].row = (uint32_t)__builtin_amdgcn_readlane((int)my_row, (int)(u + k));
-                    load_row<ELT>(r[k], G, base + u + k, W, S, lane);
+                    live[k] = !(r[k].row & kSlotStepped);
+                    if (live[k])
+                        load_row<ELT>(r[k], G, base + u + k, W, S, lane);
                 }
             }
 #pragma unroll
             for (int k = 0; k < kStepRows; ++k)
-                if (u + k < cnt)
-                    step_row<ELT>(r[k], a, W, S, one_minus_b2, lane);
+                if (live[k])
+                    step_row<ELT>(r[k], a, W, S, lane);
         }
     }
 }
@@ -191,7 +168,7 @@ __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uin
     if (tid == 0)
         *count = total;
     for (uint64_t i = tid; i < n; i += nthr)
-        rows_out[i] = slot_rows[i];
+        rows_out[i] = slot_rows[i] & ~kSlotStepped;
     if (g_out) {
         const float4 *src = reinterpret_cast<const float4 *>(G);
         float4 *dst = reinterpret_cast<float4 *>(g_out);
@@ -215,10 +192,7 @@ hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void
     a.st[0] = sb;
     a.st[1] = st;
     a.hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
-    a.t = t;
-    a.lr = lr;
-    a.beta2 = beta2;
-    a.eps = eps;
+    a.p = StepParams{t, lr, beta2, eps};
     // about one resident wavefront per SIMD slot; each walks 64-slot blocks
     const int64_t want = (L.wrows + 255) / 256;
     const unsigned gx = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);

@@ -18,6 +18,8 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MODE_SPREAD = 0
 MODE_BURST = 1
+MODE_BURST_REF = 2
+_MODES = {"spread": MODE_SPREAD, "burst": MODE_BURST, "burst_ref": MODE_BURST_REF}
 
 FLAG_BAD_TOKEN = 0x1
 FLAG_WINDOW_FULL = 0x2
@@ -71,7 +73,7 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.seed[0], c.seed[1] = int(seeds[0]), int(seeds[1])
     c.max_tokens = int(max_tokens)
     c.accum_steps = int(accum_steps)
-    c.mode = MODE_SPREAD if mode == "spread" else MODE_BURST
+    c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
     return c
 
@@ -106,6 +108,8 @@ def lib() -> ctypes.CDLL:
             "ngram_window_reduce": ([cp, vp, vp], ctypes.c_int),
             "ngram_sparse_step": ([cp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
                                    ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+            "ngram_embed_bwd_step": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, i32, ctypes.c_float,
+                                      ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
             "ngram_profile_events": ([ctypes.c_int, vp, vp], ctypes.c_int),
@@ -232,6 +236,7 @@ def embed_fwd(cfg: NgramConfig, W_b: torch.Tensor, W_t: torch.Tensor, tokens: to
 
 
 def embed_bwd_accum(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: torch.Tensor):
+    """In burst_ref mode dY must stay alive and unchanged until the window's step."""
     T = tokens.numel()
     if dY.shape != (T, DIM):
         raise ValueError(f"dY must be [{T}, {DIM}], got {tuple(dY.shape)}")
@@ -254,6 +259,21 @@ def sparse_step(cfg: NgramConfig, ws: Workspace, W_b, W_t, state_b, state_t, t: 
         ctypes.byref(cfg), ws.ptr, _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt),
         _dev(state_b, "state_b", torch.float32), _dev(state_t, "state_t", torch.float32),
         int(t), float(lr), float(beta2), float(eps), _stream()))
+
+
+def embed_bwd_step(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: torch.Tensor,
+                   W_b, W_t, state_b, state_t, t: int, lr: float, beta2: float, eps: float):
+    """The window's last micro-step fused with its sparse step."""
+    T = tokens.numel()
+    if dY.shape != (T, DIM):
+        raise ValueError(f"dY must be [{T}, {DIM}], got {tuple(dY.shape)}")
+    dt = cfg.torch_dtype
+    _check_tables(cfg, W_b, W_t)
+    _check_state(cfg, state_b, state_t)
+    _check("ngram_embed_bwd_step", lib().ngram_embed_bwd_step(
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", torch.float32), T,
+        _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
+        _dev(state_t, "state_t", torch.float32), int(t), float(lr), float(beta2), float(eps), _stream()))
 
 
 def window_export(cfg: NgramConfig, ws: Workspace, channel: int, with_grad: bool = True):

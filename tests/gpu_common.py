@@ -65,23 +65,38 @@ class State:
     def step(self, ws, t, lr, beta2, eps):
         ng().sparse_step(self.cfg, ws, self.W[0], self.W[1], self.st[0], self.st[1], t, lr, beta2, eps)
 
+    def bwd_step(self, ws, tok, dy, t, lr, beta2, eps):
+        ng().embed_bwd_step(self.cfg, ws, tok, dy, self.W[0], self.W[1], self.st[0], self.st[1], t, lr,
+                            beta2, eps)
+
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2),
-                 sample_untouched=512, keep_rows=None, rng_seed=0):
+                 sample_untouched=512, keep_rows=None, rng_seed=0, how="export"):
     """Feeds one window (lists of numpy tokens / dY) through the GPU path,
-    checks the window gradient, the touched sets and the step against the
-    oracle, and a sample of untouched rows for bitwise stability."""
+    checks the touched sets and the step against the oracle, and a sample of
+    untouched rows for bitwise stability.  how:
+      "export"     reduce, export and check the window gradient, then step;
+      "step"       sparse_step straight after the micro-steps (burst mode:
+                   the reduction fused with the step);
+      "fused_last" the last micro-step through embed_bwd_step."""
     N = ng()
     cfg = st.cfg
-    for tok, dy in zip(toks, dys):
-        N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
-    N.window_reduce(cfg, ws)
+    last = len(toks) - 1 if how == "fused_last" else len(toks)
+    keep = []   # burst by reference reads dY at step time: keep it alive
+    for tok, dy in zip(toks[:last], dys[:last]):
+        keep.append(to_dev(dy))
+        N.embed_bwd_accum(cfg, ws, to_dev(tok), keep[-1])
+    if how == "export":
+        N.window_reduce(cfg, ws)
     orc = helpers.oracle_window(cfg.vocab, cfg.eos_id, (cfg.rows[0], cfg.rows[1]), toks, dys,
                                 seeds, keep_rows=keep_rows)
+    if how != "export":
+        return _check_step_only(st, ws, toks, dys, t, lr, beta2, eps, dtype, orc, how, last,
+                                sample_untouched, rng_seed, keep)
     rs = np.random.default_rng(rng_seed)
     touched_all = []
     grads = []
@@ -115,6 +130,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
         snaps.append((touched, G_o, A_o, Wb, vb, tb, cand, host_rows(st.W[c], cand),
                       host_vec(st.v[c], cand), host_vec(st.tl[c], cand)))
     st.step(ws, t, lr, beta2, eps)
+    del keep
     for c in range(2):
         touched, G_o, A_o, Wb, vb, tb, cand, Wc, vc, tc = snaps[c]
         W_o, v_o, t_o = oracle.sparse_step(G_o, Wb, vb, tb, t, lr, beta2, eps)
@@ -141,3 +157,37 @@ def window_inputs(w, first_step, T=None, n=4, tok_fn=None):
         toks.append(synth.tokens(w, s, T) if tok_fn is None else tok_fn(s))
         dys.append(synth.dY(w, s, len(toks[-1])))
     return toks, dys
+
+
+def _check_step_only(st, ws, toks, dys, t, lr, beta2, eps, dtype, orc, how, last, sample_untouched,
+                     rng_seed, keep):
+    """check_window without the exported gradient: the step's results alone."""
+    N = ng()
+    cfg = st.cfg
+    rs = np.random.default_rng(rng_seed)
+    snaps = []
+    for c in range(2):
+        touched, G_o, A_o = orc[c]
+        cand = rs.integers(0, cfg.rows[c], size=4 * sample_untouched)
+        cand = np.setdiff1d(cand, touched)[:sample_untouched]
+        snaps.append((touched, G_o, A_o, host_rows(st.W[c], touched), host_vec(st.v[c], touched),
+                      host_vec(st.tl[c], touched), cand, host_rows(st.W[c], cand)))
+    if how == "fused_last":
+        st.bwd_step(ws, to_dev(toks[last]), to_dev(dys[last]), t, lr, beta2, eps)
+    else:
+        st.step(ws, t, lr, beta2, eps)
+    torch.cuda.synchronize()
+    keep.clear()
+    for c in range(2):
+        touched, G_o, A_o, Wb, vb, tb, cand, Wc = snaps[c]
+        W_o, v_o, t_o = oracle.sparse_step(G_o, Wb, vb, tb, t, lr, beta2, eps)
+        np.testing.assert_array_equal(host_vec(st.tl[c], touched), t_o)
+        assert int((st.tl[c] == t).sum()) == len(touched)
+        helpers.assert_v_close(host_vec(st.v[c], touched), v_o, G=G_o, absbound=A_o, beta2=beta2)
+        helpers.assert_rows_close(host_rows(st.W[c], touched), W_o, Wb, dtype, G=G_o, absbound=A_o,
+                                  v_orc=v_o, lr=lr, eps=eps)
+        np.testing.assert_array_equal(host_rows(st.W[c], cand), Wc)
+    for c in range(2):
+        r, _ = N.window_export(cfg, ws, c, with_grad=False)
+        assert len(r) == 0
+    return [s[0] for s in snaps], None, orc

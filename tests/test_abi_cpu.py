@@ -47,7 +47,7 @@ def _good(N, **kw):
 @pytest.mark.parametrize("field,value", [
     ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
     ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
-    ("mode", 2), ("window_rows", -1)])
+    ("mode", 3), ("window_rows", -1)])
 def test_config_rejects(N, field, value):
     c = _good(N)
     setattr(c, field, value)

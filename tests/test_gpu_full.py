@@ -89,7 +89,11 @@ def _oracle_grad_for(rows_all, neg_all, dys, sample):
     return touched, G, A
 
 
-def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True):
+def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True, fused_last=False):
+    """One window through the GPU path, checked on sampled rows.  fused_last:
+    the last micro-step goes through ngram_embed_bwd_step (the reduction
+    fused with the step), so the window gradient is only seen through the
+    step's results."""
     N = ng()
     cfg = st["cfg"]
     dys = [_dy(s) for s in dy_seeds]
@@ -107,32 +111,43 @@ def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True):
                                  ids_b=ib, ids_t=it, out_dtype="bf16")
             got = out.index_select(0, torch.from_numpy(sp).cuda()).view(torch.int16).cpu().numpy()
             np.testing.assert_array_equal(got.view(np.uint16), ref)
+        if fused_last and m == len(toks) - 1:
+            last_tok = tok_d
+            break
         N.embed_bwd_accum(cfg, ws, tok_d, dys[m])
-    N.window_reduce(cfg, ws)
+    if not fused_last:
+        N.window_reduce(cfg, ws)
     snaps = []
     for c in range(2):
         rows_all = np.concatenate([p[2 * c] for p in per])
         neg_all = np.concatenate([p[2 * c + 1] for p in per])
-        rows_g, G_g = N.window_export(cfg, ws, c)
-        order = torch.argsort(rows_g)
-        rows_g, G_g = rows_g[order], G_g[order]
-        np.testing.assert_array_equal(rows_g.cpu().numpy(), np.unique(rows_all))
         sample, hottest = _sample_rows(rows_all, rs)
         touched, G_o, A_o = _oracle_grad_for(rows_all, neg_all, dys, sample)
         assert np.array_equal(touched, sample)
-        pos = torch.searchsorted(rows_g, torch.from_numpy(sample).cuda())
-        helpers.assert_grad_close(G_g.index_select(0, pos).cpu().numpy(), G_o, A_o)
+        if fused_last:
+            rows_g = torch.from_numpy(np.unique(rows_all)).cuda()
+        else:
+            rows_g, G_g = N.window_export(cfg, ws, c)
+            order = torch.argsort(rows_g)
+            rows_g, G_g = rows_g[order], G_g[order]
+            np.testing.assert_array_equal(rows_g.cpu().numpy(), np.unique(rows_all))
+            pos = torch.searchsorted(rows_g, torch.from_numpy(sample).cuda())
+            helpers.assert_grad_close(G_g.index_select(0, pos).cpu().numpy(), G_o, A_o)
+            del G_g
         cand = rs.integers(0, FULL.rows[c], size=4096)
         cand = np.setdiff1d(cand, rows_g.cpu().numpy())[:1024]
         snaps.append(dict(sample=sample, G=G_o, A=A_o, hottest=hottest, rows_g=rows_g,
                           W=host_rows(st["W"][c], sample), v=host_vec(st["v"][c], sample),
                           tl=host_vec(st["tl"][c], sample), cand=cand,
                           Wc=host_rows(st["W"][c], cand)))
-        del G_g
     st["t"] += 1
     t = st["t"]
-    N.sparse_step(cfg, ws, st["W"][0], st["W"][1], st["state"][0], st["state"][1], t, FULL.lr,
-                  FULL.beta2, FULL.eps)
+    if fused_last:
+        N.embed_bwd_step(cfg, ws, last_tok, dys[-1], st["W"][0], st["W"][1], st["state"][0],
+                         st["state"][1], t, FULL.lr, FULL.beta2, FULL.eps)
+    else:
+        N.sparse_step(cfg, ws, st["W"][0], st["W"][1], st["state"][0], st["state"][1], t, FULL.lr,
+                      FULL.beta2, FULL.eps)
     for c in range(2):
         s = snaps[c]
         W_o, v_o, t_o = oracle.sparse_step(s["G"], s["W"], s["v"], s["tl"], t, FULL.lr, FULL.beta2,
@@ -144,6 +159,8 @@ def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True):
         assert int((st["tl"][c] == t).sum()) == len(s["rows_g"])
         assert bool((st["tl"][c].index_select(0, s["rows_g"]) == t).all())
         np.testing.assert_array_equal(host_rows(st["W"][c], s["cand"]), s["Wc"])
+    for c in range(2):   # the window is empty after the step
+        assert len(N.window_export(cfg, ws, c, with_grad=False)[0]) == 0
     assert N.device_status(cfg, ws) == 0
     return snaps
 
@@ -155,6 +172,19 @@ def test_full_table_window_spread(big_state):
     toks = [synth.tokens(FULL, s) for s in range(4)]
     snaps = _run_and_check_window(big_state, ws, toks, [31, 32, 33, 34], rs)
     assert snaps[0]["hottest"] > 10_000   # hot bigram segments span hundreds of chunks
+
+
+def test_full_table_window_fused_step(big_state):
+    # the launch sequence bench.py times: three micro-steps accumulated, the
+    # last one reduced together with the sparse step
+    N = ng()
+    ws = N.Workspace(big_state["cfg"])
+    rs = np.random.default_rng(6)
+    for win in range(2):
+        toks = [synth.tokens(FULL, 40 + 4 * win + m) for m in range(4)]
+        snaps = _run_and_check_window(big_state, ws, toks, [61 + 4 * win + m for m in range(4)], rs,
+                                      check_fwd=win == 0, fused_last=True)
+        assert snaps[0]["hottest"] > 10_000
 
 
 def test_collision_workload_full_table(big_state):

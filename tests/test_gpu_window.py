@@ -26,7 +26,7 @@ def _tiny_state(cfg, w):
                  to_dev(synth.init_rows(w, 1, w.rows[1])))
 
 
-@pytest.mark.parametrize("mode", ["spread", "burst"])
+@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
 def test_tiny_workload_two_windows(mode):
     w = workloads.TINY
     N = ng()
@@ -39,7 +39,54 @@ def test_tiny_workload_two_windows(mode):
     assert N.device_status(cfg, ws) == 0
 
 
-@pytest.mark.parametrize("mode", ["spread", "burst"])
+@pytest.mark.parametrize("mode,how", [("spread", "fused_last"), ("burst", "step"),
+                                      ("burst", "fused_last"), ("spread", "step"),
+                                      ("burst_ref", "step"), ("burst_ref", "fused_last")])
+def test_tiny_workload_fused_step(mode, how):
+    # the step fused into the reduction: the last micro-step (spread) or the
+    # whole window (burst); gradients are checked through the step results
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode=mode)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    for win in range(w.steps // w.accum_steps):
+        toks, dys = window_inputs(w, win * w.accum_steps)
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "f32", how=how)
+    assert N.device_status(cfg, ws) == 0
+
+
+@pytest.mark.parametrize("how", ["fused_last", "step"])
+@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
+def test_shard_workload_fused(mode, how):
+    w = workloads.COLLISION
+    N = ng()
+    rows = workloads.SHARD.rows
+    T = 49_152
+    cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=T, mode=mode)
+    st = State(cfg, device_table(rows[0], "bf16", 61), device_table(rows[1], "bf16", 62))
+    ws = N.Workspace(cfg)
+    for win in range(2):
+        toks, dys = window_inputs(w, 4 * win, T=T)
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "bf16", how=how)
+    assert N.device_status(cfg, ws) == 0
+    del st, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [65, 129, 20_000])
+def test_single_hot_row_fused(T):
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T)
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    tok = np.full(T, 42, np.int32)
+    dys = [synth.dY(w, 600 + m, T) for m in range(4)]
+    check_window(st, ws, [tok] * 4, dys, 1, w.lr, w.beta2, w.eps, "f32", how="fused_last")
+
+
+@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
 def test_small_table_long_gaps(mode):
     # 64-token micro-steps into 3000-row tables: rows skip windows, so the
     # retroactive beta2^k with k > 1 is exercised; ragged T per micro-step.
@@ -53,7 +100,8 @@ def test_small_table_long_gaps(mode):
         Ts = [64, 97, 1, 33]
         toks = [synth.tokens(w, 100 + 4 * win + m, Ts[m]) for m in range(4)]
         dys = [synth.dY(w, 100 + 4 * win + m, Ts[m]) for m in range(4)]
-        check_window(st, ws, toks, dys, win + 1, 0.02, 0.9, 1e-6, "f32")
+        how = ("export", "fused_last", "step")[win % 3]
+        check_window(st, ws, toks, dys, win + 1, 0.02, 0.9, 1e-6, "f32", how=how)
     gaps = st.tl[0].cpu().numpy()
     assert len(np.unique(gaps[gaps > 0])) > 3
 
@@ -137,7 +185,7 @@ def test_spread_equals_burst():
         assert np.all(err <= 2 * lim)
 
 
-@pytest.mark.parametrize("mode", ["spread", "burst"])
+@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
 def test_bitwise_deterministic(mode):
     w = workloads.SHARD
     N = ng()
@@ -149,11 +197,14 @@ def test_bitwise_deterministic(mode):
     for rep in range(2):
         st = base.clone()
         ws = N.Workspace(cfg)
-        for tok, dy in zip(toks, dys):
-            N.embed_bwd_accum(cfg, ws, to_dev(tok), to_dev(dy))
+        dys_d = [to_dev(dy) for dy in dys]   # burst_ref reads dY at reduce time
+        for tok, dy in zip(toks, dys_d):
+            N.embed_bwd_accum(cfg, ws, to_dev(tok), dy)
         N.window_reduce(cfg, ws)
         ex = [N.window_export(cfg, ws, c) for c in range(2)]
         st.step(ws, 3, w.lr, w.beta2, w.eps)
+        torch.cuda.synchronize()
+        del dys_d
         res.append((ex, st))
     for c in range(2):
         assert torch.equal(res[0][0][c][0], res[1][0][c][0])
