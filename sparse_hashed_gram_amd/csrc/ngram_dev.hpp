@@ -86,6 +86,75 @@ __device__ __forceinline__ uint32_t bf16_pack(float lo, float hi)
     return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// The same rounding by gfx950's pair conversion (v_cvt_pk_bf16_f32); equal to
+// bf16_pack except for NaN inputs, whose sign and payload it may keep.
+__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &b, 4);
+    return u;
+}
+
+// ------------------------------------------------------- memory access
+//
+// Accesses through the global address space.  An address formed at run time
+// (taken from another lane, or read from memory) would otherwise be used
+// with flat instructions, and a wait for LDS results (lgkmcnt) then also has
+// to drain every flat load in flight.
+
+template <int BYTES>
+struct RawWord;
+template <>
+struct RawWord<4> {
+    typedef uint32_t type;
+};
+template <>
+struct RawWord<8> {
+    typedef uint32_t type __attribute__((ext_vector_type(2)));
+};
+template <>
+struct RawWord<16> {
+    typedef uint32_t type __attribute__((ext_vector_type(4)));
+};
+
+template <typename T>
+__device__ __forceinline__ T ld_global(uint64_t addr)
+{
+    typedef typename RawWord<sizeof(T)>::type W;
+    const W w = *(const __attribute__((address_space(1))) W *)addr;
+    T v;
+    __builtin_memcpy(&v, &w, sizeof(T));
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_global(uint64_t addr, const T &v)
+{
+    typedef typename RawWord<sizeof(T)>::type W;
+    W w;
+    __builtin_memcpy(&w, &v, sizeof(T));
+    *(__attribute__((address_space(1))) W *)addr = w;
+}
+
+__device__ __forceinline__ void atomic_add_global(uint64_t addr, float v)
+{
+    __hip_atomic_fetch_add((__attribute__((address_space(1))) float *)addr, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Marks x as produced here.  Used on per-lane values loaded before a loop and
+// read inside it through readlane: the wait for their loads then happens once,
+// here, and not as a full drain of the loop's own loads at every use.
+template <typename T>
+__device__ __forceinline__ void settle(T &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
 // ------------------------------------------------------------ workspace
 //
 // One device allocation, carved by the host (WsLayout).  All mutable state
@@ -188,12 +257,21 @@ __device__ __forceinline__ double pow_steps(double b, int32_t k)
     return r;
 }
 
+// Sum over the 64 lanes, the same bits in every lane: butterflies inside each
+// row of 16 lanes through DPP (xor 1, xor 2, half-row mirror, row mirror),
+// then the four row sums read as scalars and added in a fixed order.  No LDS
+// traffic, so it does not wait on outstanding memory operations.
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1)
-        x += __shfl_xor(x, d);
-    return x;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));   // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));   // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // order_bad: t does not exceed t_last (the row then decays by beta2^0).
@@ -205,7 +283,7 @@ __device__ __forceinline__ float step_scale(float sum_g2, RowState s, const Step
     if (k < 1)
         k = 0;
     const double decay = pow_steps((double)p.beta2, k);
-    vn = (float)(decay * (double)s.v + (1.0 - (double)p.beta2) * ((double)sum_g2 / (double)kDim));
+    vn = (float)(decay * (double)s.v + (1.0 - (double)p.beta2) * ((double)sum_g2 * (1.0 / kDim)));
     return p.lr / (sqrtf(vn) + p.eps);
 }
 

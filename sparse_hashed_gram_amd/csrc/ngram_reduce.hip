@@ -409,7 +409,7 @@ struct RedArgs {
     uint32_t n_host;
     const float *dY;        // [positions][768], indexed by the row code
     const float *const *dy_ptrs;   // burst by reference: dY of each micro-step
-    int pos_bits;           // burst by reference: row code = micro-step << pos_bits | position
+    int pos_bits;           // row code = micro-step << pos_bits | position (31: one dY buffer)
     float *gacc;            // [2][wrows][768]
     uint32_t *slot_rows[2];
     int64_t wrows;
@@ -425,233 +425,422 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b)
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// Start of the dY row a key refers to.
-__device__ __forceinline__ const float *dy_row(const RedArgs &a, uint32_t code)
-{
-    if (a.dy_ptrs)
-        return a.dy_ptrs[code >> a.pos_bits] + (size_t)(code & ((1u << a.pos_bits) - 1u)) * kDim;
-    return a.dY + (size_t)code * kDim;
-}
-
 __device__ __forceinline__ uint32_t lane_val(uint32_t v0, uint32_t v1, int j)
 {
     return j < kWave ? (uint32_t)__builtin_amdgcn_readlane((int)v0, j)
                      : (uint32_t)__builtin_amdgcn_readlane((int)v1, j - kWave);
 }
 
-// Lane l of a wavefront holds elements l + 64 m (m = 0..11) of a 768-wide
-// row, so every load, store and atomic of a row is twelve 256-byte (fp32) or
-// 128-byte (bf16) contiguous wavefront accesses.
-constexpr int kPer = kDim / kWave;   // 12
+constexpr int kPer = kDim / kWave;   // 12 elements of a row per lane
 
-__device__ __forceinline__ void store_row(float *dst, const float (&acc)[kPer], int lane)
-{
-#pragma unroll
-    for (int m = 0; m < kPer; ++m)
-        dst[lane + m * kWave] = acc[m];
-}
-
-// Adds a micro-step's sum into its window row.  A row new to the window is
-// written; an existing one gets G += S through fire-and-forget atomic adds
-// (the read-modify-write happens in L2 and the wavefront does not wait for
-// it).  Every window row has exactly one segment, hence exactly one writer,
-// per launch, so each element sees a single addition: the result is the
-// plain fp32 sum G + S and does not depend on timing.
-__device__ __forceinline__ void flush_window_row(const float (&acc)[kPer], float *gacc, int64_t wrows, int c,
-                                                 uint32_t info, int lane)
-{
-    if (info == kDropped)
-        return;   // window full: row dropped (flagged when slots were assigned)
-    float *g = gacc + ((size_t)c * wrows + (info & 0x7FFFFFFFu)) * kDim;
-    if (info >> 31) {
-        store_row(g, acc, lane);
-    } else {
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            unsafeAtomicAdd(g + lane + m * kWave, acc[m]);
-    }
-}
-
-// Fused flush: the row's window gradient is complete.  A row the window
-// already holds adds its stored gradient first (G = G_window + S, the same
-// addition the accumulate path would make) and its slot is marked stepped;
-// then the row is stepped in place.
-template <int MODE>
-__device__ __forceinline__ void flush_fused(float (&acc)[kPer], const RedArgs &a, int c, uint32_t row,
-                                            uint32_t info, int lane)
-{
-    if (info != kNewHead) {
-        const float *g = a.gacc + ((size_t)c * a.wrows + info) * kDim + lane;
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            acc[m] = g[m * kWave] + acc[m];
-        if (lane == 0)
-            a.slot_rows[c][info] = row | kSlotStepped;
-    }
-    float w[kPer];
-    if (MODE == kFuseBf16) {
-        const uint16_t *wp = reinterpret_cast<const uint16_t *>(a.f.w[c]) + (size_t)row * kDim + lane;
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            w[m] = __uint_as_float((uint32_t)wp[m * kWave] << 16);
-    } else {
-        const float *wp = reinterpret_cast<const float *>(a.f.w[c]) + (size_t)row * kDim + lane;
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            w[m] = wp[m * kWave];
-    }
-    const RowState st = a.f.st[c][row];
-    float ss = 0.f;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m)
-        ss += acc[m] * acc[m];
-    ss = wave_sum(ss);
-    float vn;
-    bool order_bad;
-    const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
-    if (MODE == kFuseBf16) {
-        uint16_t *wp = reinterpret_cast<uint16_t *>(a.f.w[c]) + (size_t)row * kDim + lane;
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            wp[m * kWave] = (uint16_t)bf16_rne(w[m] - scale * acc[m]);
-    } else {
-        float *wp = reinterpret_cast<float *>(a.f.w[c]) + (size_t)row * kDim + lane;
-#pragma unroll
-        for (int m = 0; m < kPer; ++m)
-            wp[m * kWave] = w[m] - scale * acc[m];
-    }
-    if (lane == 0) {
-        a.f.st[c][row] = RowState{vn, a.f.p.t};
-        if (order_bad)
-            atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
-    }
-}
-
-// One wavefront per 64 sorted keys.  Keys are consumed in order, kRedU dY rows
-// in flight at a time, whatever the segment boundaries.  A segment's sum is
+// Which keys of its 64-key chunk a wavefront consumes, and how its first and
+// last pieces are finished.  Keys are consumed in order; a segment's sum is
 // reset at its first key and flushed at its last:
-//   - a segment that starts and ends here goes to the window (or, fused, is
-//     completed and stepped);
+//   - a segment that starts and ends here is finished here;
 //   - the first piece, if it continues a segment from the previous chunk, is
 //     skipped when that chunk finishes it, else left as partial row 0;
 //   - the last piece, if it spills into the next chunk, is finished here when
 //     it ends within that chunk (its keys are loaded as lanes 64..127), else
 //     left as partial row 1 with a fix-up record.
-template <int MODE>
+struct ChunkPlan {
+    uint32_t r0, v0, i0;   // this lane's key: row, dY row code | sign, head info
+    uint32_t v1;           // lanes 64..127: keys of an owned spill-over
+    uint64_t hm;           // segment heads among the chunk's keys
+    int nv;                // keys in the chunk
+    int j0, jend;          // keys this wavefront consumes
+    int la;                // first key of the last piece (-1: no head)
+    bool first_cont;       // key 0 continues the previous chunk's segment
+    bool last_spills;      // the last piece continues into the next chunk
+    bool owner_full;       // ... and this chunk finishes it
+    uint32_t row_last;
+};
+
+// False if the chunk is past the end of the keys.
+__device__ __forceinline__ bool chunk_plan(const RedArgs &a, int c, int64_t chunk, uint32_t n, int lane,
+                                           ChunkPlan &p)
+{
+    const int64_t c0 = chunk * kChunk;
+    if (c0 >= n)
+        return false;
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const uint32_t *V = a.vals + (size_t)c * a.nk;
+    const uint32_t *I = a.info + (size_t)c * a.nk;
+    p.nv = (int)min<int64_t>(kChunk, (int64_t)n - c0);
+    const bool valid = lane < p.nv;
+    p.r0 = valid ? R[c0 + lane] : 0xFFFFFFFFu;
+    p.v0 = valid ? V[c0 + lane] : 0u;
+    uint32_t prev = __shfl_up(p.r0, 1);
+    if (lane == 0)
+        prev = c0 > 0 ? R[c0 - 1] : 0xFFFFFFFFu;
+    const bool head = valid && (p.r0 != prev);
+    p.hm = __ballot(head);
+    p.i0 = head ? I[c0 + lane] : 0u;
+    p.row_last = (uint32_t)__builtin_amdgcn_readlane((int)p.r0, p.nv - 1);
+    const bool cont_after = p.nv == kChunk && c0 + kChunk < n && R[c0 + kChunk] == p.row_last;
+
+    p.first_cont = !(p.hm & 1ull);
+    const int e0 = p.hm ? (int)__builtin_ctzll(p.hm) : p.nv;   // end of the first piece
+    bool skip_first = false;
+    if (p.first_cont) {
+        const uint32_t row0 = (uint32_t)__builtin_amdgcn_readlane((int)p.r0, 0);
+        const bool piece0_cont = (e0 == p.nv) && cont_after;
+        const bool head_in_prev = (c0 == kChunk) || (R[c0 - kChunk - 1] != row0);
+        skip_first = head_in_prev && !piece0_cont;
+    }
+    p.la = p.hm ? 63 - (int)__builtin_clzll(p.hm) : -1;
+    p.last_spills = p.hm && cont_after;
+    p.owner_full = false;
+    p.v1 = 0;
+    int extra = 0;
+    if (p.last_spills) {
+        p.owner_full = !(c0 + 2 * kChunk < n && R[c0 + 2 * kChunk] == p.row_last);
+        if (p.owner_full) {
+            const int64_t i1 = c0 + kChunk + lane;
+            const bool ok1 = i1 < n;
+            const uint32_t r1 = ok1 ? R[i1] : 0xFFFFFFFFu;
+            p.v1 = ok1 ? V[i1] : 0u;
+            extra = __popcll(__ballot(ok1 && r1 == p.row_last));
+        }
+    }
+    p.j0 = skip_first ? e0 : 0;
+    p.jend = p.owner_full ? kChunk + extra : p.nv;
+    return true;
+}
+
+// Does the open segment end at key k?
+__device__ __forceinline__ bool seg_ends(const ChunkPlan &p, int k)
+{
+    if (k >= kChunk - 1 && p.owner_full)
+        return k == p.jend - 1;
+    if (k == p.nv - 1)
+        return true;
+    return (k + 1 < kChunk) && ((p.hm >> (k + 1)) & 1ull);
+}
+
+// Lane m < 64 holds the base address of micro-step m's dY (burst by
+// reference) or, with one dY buffer, every lane holds that buffer's address;
+// a key's dY row address then needs no dependent load and no branch.
+__device__ __forceinline__ uint64_t dy_lane_base(const RedArgs &a, int lane)
+{
+    return a.dy_ptrs ? (uint64_t)a.dy_ptrs[lane] : (uint64_t)a.dY;
+}
+
+__device__ __forceinline__ uint64_t dy_row_addr(const RedArgs &a, uint64_t lane_base, uint32_t code)
+{
+    const int m = (int)(code >> a.pos_bits);   // uniform across the wavefront
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lane_base, m);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lane_base >> 32), m);
+    const uint32_t pos = code & (uint32_t)((1ull << a.pos_bits) - 1u);
+    return ((uint64_t)lo | ((uint64_t)hi << 32)) + (uint64_t)pos * (kDim * 4);
+}
+
+// The chunk's per-lane values are read through readlane inside the key loop.
+__device__ __forceinline__ void settle_plan(ChunkPlan &p)
+{
+    settle(p.r0);
+    settle(p.v0);
+    settle(p.i0);
+    settle(p.v1);
+}
+
+// Partial row of a piece that another chunk or the fix-up finishes.
+template <typename Store>
+__device__ __forceinline__ void flush_partial(const RedArgs &a, const ChunkPlan &p, int c, int64_t chunk, int ps,
+                                              int lane, Store store)
+{
+    const uint64_t base = (uint64_t)a.partial + (((uint64_t)c * a.nchunk + chunk) * 2) * (kDim * 4);
+    if (ps == 0 && p.first_cont) {
+        store(base);
+    } else {
+        const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
+        store(base + kDim * 4);
+        if (lane == 0) {
+            const uint32_t k2 = atomicAdd(&a.hdr->n_owner[c], 1u);
+            a.owners[(size_t)c * a.nchunk + k2] = (uint64_t)chunk | ((uint64_t)info << 32);
+        }
+    }
+}
+
+// Accumulating reduction (one wavefront per 64 sorted keys, kRedU dY rows in
+// flight whatever the segment boundaries): each finished segment goes to its
+// window row.  Lane l holds elements l + 64 m (m = 0..11), so every load,
+// store and atomic of a row is twelve 256-byte contiguous wavefront accesses.
 __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
     const uint32_t n = count_of(a.n_dev, a.n_host);
-    if (MODE == kAccum && chunk == 0 && lane == 0)
+    if (chunk == 0 && lane == 0)
         a.hdr->n_slots[c] = a.hdr->n_next[c];   // the slots assign_kernel handed out
-    const int64_t c0 = chunk * kChunk;
-    if (c0 >= n)
+    ChunkPlan p;
+    if (!chunk_plan(a, c, chunk, n, lane, p))
         return;
-    const uint32_t *R = a.rows + (size_t)c * a.nk;
-    const uint32_t *V = a.vals + (size_t)c * a.nk;
-    const uint32_t *I = a.info + (size_t)c * a.nk;
-    const int nv = (int)min<int64_t>(kChunk, (int64_t)n - c0);
-    const bool valid = lane < nv;
-    const uint32_t r0 = valid ? R[c0 + lane] : 0xFFFFFFFFu;
-    const uint32_t v0 = valid ? V[c0 + lane] : 0u;
-    uint32_t prev = __shfl_up(r0, 1);
-    if (lane == 0)
-        prev = c0 > 0 ? R[c0 - 1] : 0xFFFFFFFFu;
-    const bool head = valid && (r0 != prev);
-    const uint64_t hm = __ballot(head);
-    const uint32_t i0 = head ? I[c0 + lane] : 0u;
-    const uint32_t row_last = (uint32_t)__builtin_amdgcn_readlane((int)r0, nv - 1);
-    const bool cont_after = nv == kChunk && c0 + kChunk < n && R[c0 + kChunk] == row_last;
-
-    // first piece: continuation of the previous chunk's last segment?
-    const bool first_cont = !(hm & 1ull);
-    const int e0 = hm ? (int)__builtin_ctzll(hm) : nv;   // end of the first piece
-    bool skip_first = false;
-    if (first_cont) {
-        const uint32_t row0 = (uint32_t)__builtin_amdgcn_readlane((int)r0, 0);
-        const bool piece0_cont = (e0 == nv) && cont_after;
-        const bool head_in_prev = (c0 == kChunk) || (R[c0 - kChunk - 1] != row0);
-        skip_first = head_in_prev && !piece0_cont;
-    }
-    // last piece: starts at the highest head; spills over if cont_after
-    const int la = hm ? 63 - (int)__builtin_clzll(hm) : -1;
-    const bool last_spills = hm && cont_after;
-    bool owner_full = false;
-    uint32_t v1 = 0;
-    int extra = 0;
-    if (last_spills) {
-        owner_full = !(c0 + 2 * kChunk < n && R[c0 + 2 * kChunk] == row_last);
-        if (owner_full) {
-            const int64_t i1 = c0 + kChunk + lane;
-            const bool ok1 = i1 < n;
-            const uint32_t r1 = ok1 ? R[i1] : 0xFFFFFFFFu;
-            v1 = ok1 ? V[i1] : 0u;
-            extra = __popcll(__ballot(ok1 && r1 == row_last));
-        }
-    }
-    const int j0 = skip_first ? e0 : 0;
-    const int jend = owner_full ? kChunk + extra : nv;
+    uint64_t lane_base = dy_lane_base(a, lane);
+    settle_plan(p);
+    settle(lane_base);
+    const uint64_t gacc = (uint64_t)a.gacc + (uint64_t)c * a.wrows * (kDim * 4) + 4 * lane;
 
     float acc[kPer];
-    int ps = j0;   // start key of the open segment
+    int ps = p.j0;   // start key of the open segment
 #pragma unroll
     for (int m = 0; m < kPer; ++m)
         acc[m] = 0.f;
-    for (int j = j0; j < jend; j += kRedU) {
+    for (int j = p.j0; j < p.jend; j += kRedU) {
         float x[kRedU][kPer];
         uint32_t sg[kRedU];
 #pragma unroll
         for (int u = 0; u < kRedU; ++u) {
-            if (j + u < jend) {
-                const uint32_t v = lane_val(v0, v1, j + u);
+            if (j + u < p.jend) {
+                const uint32_t v = lane_val(p.v0, p.v1, j + u);
                 sg[u] = v & 0x80000000u;
-                const float *p = dy_row(a, v & 0x7FFFFFFFu) + lane;
+                const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 4 * lane;
 #pragma unroll
                 for (int m = 0; m < kPer; ++m)
-                    x[u][m] = p[m * kWave];
+                    x[u][m] = ld_global<float>(q + m * kWave * 4);
             }
         }
 #pragma unroll
         for (int u = 0; u < kRedU; ++u) {
             const int k = j + u;
-            if (k >= jend)
+            if (k >= p.jend)
                 break;
-            if (k < kChunk && k != j0 && ((hm >> k) & 1ull)) {
+            if (k < kChunk && k != p.j0 && ((p.hm >> k) & 1ull)) {
                 ps = k;
 #pragma unroll
                 for (int m = 0; m < kPer; ++m)
                     acc[m] = 0.f;
             }
+            const float sgn = sg[u] ? -1.f : 1.f;   // acc +- dY, one rounding
 #pragma unroll
             for (int m = 0; m < kPer; ++m)
-                acc[m] += __uint_as_float(__float_as_uint(x[u][m]) ^ sg[u]);
-            // does the open segment end at key k?
-            bool ends;
-            if (k >= kChunk - 1 && owner_full)
-                ends = (k == jend - 1);
-            else if (k == nv - 1)
-                ends = true;
-            else
-                ends = (k + 1 < kChunk) && ((hm >> (k + 1)) & 1ull);
-            if (!ends)
+                acc[m] = fmaf(x[u][m], sgn, acc[m]);
+            if (!seg_ends(p, k))
                 continue;
-            if (ps == 0 && first_cont) {
-                store_row(a.partial + (((size_t)c * a.nchunk + chunk) * 2 + 0) * kDim, acc, lane);
-            } else if (ps == la && last_spills && !owner_full) {
-                const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, ps);
-                store_row(a.partial + (((size_t)c * a.nchunk + chunk) * 2 + 1) * kDim, acc, lane);
-                if (lane == 0) {
-                    const uint32_t k2 = atomicAdd(&a.hdr->n_owner[c], 1u);
-                    a.owners[(size_t)c * a.nchunk + k2] = (uint64_t)chunk | ((uint64_t)info << 32);
-                }
+            if ((ps == 0 && p.first_cont) || (ps == p.la && p.last_spills && !p.owner_full)) {
+                flush_partial(a, p, c, chunk, ps, lane, [&](uint64_t dst) {
+#pragma unroll
+                    for (int m = 0; m < kPer; ++m)
+                        st_global<float>(dst + 4 * (lane + m * kWave), acc[m]);
+                });
+                continue;
+            }
+            // A row new to the window is written; an existing one gets G += S
+            // through fire-and-forget atomic adds executed in L2 (the
+            // wavefront does not wait for the old row).  Every window row has
+            // exactly one segment, hence one writer, per launch, so each
+            // element sees a single addition and the result is the plain fp32
+            // sum G + S, whatever the timing.
+            const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
+            if (info == kDropped)
+                continue;   // window full: row dropped (flagged when slots were assigned)
+            const uint64_t g = gacc + (uint64_t)(info & 0x7FFFFFFFu) * (kDim * 4);
+            if (info >> 31) {
+#pragma unroll
+                for (int m = 0; m < kPer; ++m)
+                    st_global<float>(g + m * kWave * 4, acc[m]);
             } else {
-                const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)i0, ps);
-                if (MODE == kAccum)
-                    flush_window_row(acc, a.gacc, a.wrows, c, info, lane);
-                else
-                    flush_fused<MODE>(acc, a, c, (uint32_t)__builtin_amdgcn_readlane((int)r0, ps), info, lane);
+#pragma unroll
+                for (int m = 0; m < kPer; ++m)
+                    atomic_add_global(g + m * kWave * 4, acc[m]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------- reduction fused with step
+//
+// The same walk over the sorted keys, but a finished segment is the row's
+// complete window gradient G (plus what the window already holds for it, if
+// anything): the row is stepped at once and G never goes to memory.  Here
+// lane l holds elements 4l..4l+3 of each 256-wide third of a row, so a dY
+// row is three 1 KB wavefront loads and a bf16 table row three 512 B ones.
+// The table row and state of every segment that ends among the keys of a
+// batch are loaded together with the batch's dY rows, so a short segment
+// costs one memory round trip, not two.
+
+constexpr int kQ = kDim / (4 * kWave);   // 3 float4 per lane
+#ifndef NGRAM_STEP_U
+#define NGRAM_STEP_U 4
+#endif
+constexpr int kStepU = NGRAM_STEP_U;     // keys per batch
+
+template <int ELT>
+struct WRow;
+template <>
+struct WRow<2> {   // 4 bf16
+    uint2 q[kQ];
+};
+template <>
+struct WRow<4> {   // 4 fp32
+    float4 q[kQ];
+};
+
+// addr: the row's start + this lane's offset (ELT * 4 * lane).
+template <int ELT>
+__device__ __forceinline__ void load_wrow(WRow<ELT> &w, uint64_t addr)
+{
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+        if constexpr (ELT == 2)
+            w.q[q] = ld_global<uint2>(addr + q * kWave * 8);
+        else
+            w.q[q] = ld_global<float4>(addr + q * kWave * 16);
+    }
+}
+
+// W <- W - scale * G, rounded once to the table dtype.  bf16: the hardware's
+// round-to-nearest-even pair conversion; if any lane holds a NaN the whole
+// wavefront takes the bitwise rounding instead, which writes NaN as 0x7FC0.
+template <int ELT>
+__device__ __forceinline__ void store_stepped(const WRow<ELT> &w, const float4 (&g)[kQ], float scale, uint64_t addr)
+{
+    if constexpr (ELT == 2) {
+        float r[kQ][4];
+        bool nan = false;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const uint2 x = w.q[q];
+            r[q][0] = bf16_lo(x.x) - scale * g[q].x;
+            r[q][1] = bf16_hi(x.x) - scale * g[q].y;
+            r[q][2] = bf16_lo(x.y) - scale * g[q].z;
+            r[q][3] = bf16_hi(x.y) - scale * g[q].w;
+            nan |= __builtin_isunordered(r[q][0], r[q][1]) | __builtin_isunordered(r[q][2], r[q][3]);
+        }
+        if (!__any(nan)) {
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                st_global<uint2>(addr + q * kWave * 8,
+                                 make_uint2(bf16_pack_rne(r[q][0], r[q][1]), bf16_pack_rne(r[q][2], r[q][3])));
+        } else {
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                st_global<uint2>(addr + q * kWave * 8,
+                                 make_uint2(bf16_pack(r[q][0], r[q][1]), bf16_pack(r[q][2], r[q][3])));
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const float4 x = w.q[q];
+            st_global<float4>(addr + q * kWave * 16, make_float4(x.x - scale * g[q].x, x.y - scale * g[q].y,
+                                                                 x.z - scale * g[q].z, x.w - scale * g[q].w));
+        }
+    }
+}
+
+template <int ELT>
+__global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
+{
+    const int c = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    ChunkPlan p;
+    if (!chunk_plan(a, c, chunk, n, lane, p))
+        return;
+    uint64_t lane_base = dy_lane_base(a, lane);
+    settle_plan(p);
+    settle(lane_base);
+    const uint64_t table = (uint64_t)a.f.w[c] + (uint64_t)ELT * 4 * lane;
+    const uint64_t state = (uint64_t)a.f.st[c];
+    const uint64_t gacc = (uint64_t)a.gacc + (uint64_t)c * a.wrows * (kDim * 4) + 16 * lane;
+
+    // keys 0..63 that end a segment stepped here (not a partial piece); an
+    // owned spill-over ends at jend - 1 >= 64
+    uint64_t fin = (p.hm >> 1) | (1ull << (p.nv - 1));
+    if (p.first_cont && p.j0 == 0) {
+        const int e0 = p.hm ? (int)__builtin_ctzll(p.hm) : p.nv;
+        fin &= ~(1ull << (e0 - 1));
+    }
+    if (p.last_spills)
+        fin &= ~(1ull << 63);   // nv == 64: finished past the chunk or left partial
+
+    float4 acc[kQ];
+    int ps = p.j0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+        acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = p.j0; j < p.jend; j += kStepU) {
+        float4 x[kStepU][kQ];
+        uint32_t sg[kStepU];
+        WRow<ELT> w[kStepU];
+        RowState st[kStepU];
+        uint32_t row[kStepU];
+        bool ends_here[kStepU];
+#pragma unroll
+        for (int u = 0; u < kStepU; ++u) {
+            const int k = j + u;
+            ends_here[u] = false;
+            if (k < p.jend) {
+                const uint32_t v = lane_val(p.v0, p.v1, k);
+                sg[u] = v & 0x80000000u;
+                const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 16 * lane;
+#pragma unroll
+                for (int qq = 0; qq < kQ; ++qq)
+                    x[u][qq] = ld_global<float4>(q + qq * kWave * 16);
+                ends_here[u] = k < kChunk ? ((fin >> k) & 1ull) != 0 : (p.owner_full && k == p.jend - 1);
+                if (ends_here[u]) {
+                    row[u] = k < kChunk ? (uint32_t)__builtin_amdgcn_readlane((int)p.r0, k) : p.row_last;
+                    load_wrow<ELT>(w[u], table + (uint64_t)row[u] * (kDim * ELT));
+                    st[u] = ld_global<RowState>(state + (uint64_t)row[u] * sizeof(RowState));
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStepU; ++u) {
+            const int k = j + u;
+            if (k >= p.jend)
+                break;
+            if (k < kChunk && k != p.j0 && ((p.hm >> k) & 1ull)) {
+                ps = k;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            // s dY + acc: the product by +-1 is exact, so this is acc +- dY
+            // with a single rounding
+            const float sgn = sg[u] ? -1.f : 1.f;
+#pragma unroll
+            for (int q = 0; q < kQ; ++q) {
+                acc[q].x = fmaf(x[u][q].x, sgn, acc[q].x);
+                acc[q].y = fmaf(x[u][q].y, sgn, acc[q].y);
+                acc[q].z = fmaf(x[u][q].z, sgn, acc[q].z);
+                acc[q].w = fmaf(x[u][q].w, sgn, acc[q].w);
+            }
+            if (ends_here[u]) {
+                const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
+                float4 g[kQ];
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    g[q] = acc[q];
+                if (info != kNewHead) {   // G = G_window + S, as the accumulating path adds it
+                    const uint64_t gw = gacc + (uint64_t)info * (kDim * 4);
+#pragma unroll
+                    for (int q = 0; q < kQ; ++q)
+                        g[q] = add4(ld_global<float4>(gw + q * kWave * 16), g[q]);
+                    if (lane == 0)
+                        a.slot_rows[c][info] = row[u] | kSlotStepped;
+                }
+                float ss = 0.f;
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    ss += g[q].x * g[q].x + g[q].y * g[q].y + g[q].z * g[q].z + g[q].w * g[q].w;
+                ss = wave_sum(ss);
+                float vn;
+                bool order_bad;
+                const float scale = step_scale(ss, st[u], a.f.p, vn, order_bad);
+                store_stepped<ELT>(w[u], g, scale, table + (uint64_t)row[u] * (kDim * ELT));
+                if (lane == 0) {
+                    st_global<RowState>(state + (uint64_t)row[u] * sizeof(RowState), RowState{vn, a.f.p.t});
+                    if (order_bad)
+                        atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+                }
+            } else if (seg_ends(p, k)) {
+                flush_partial(a, p, c, chunk, ps, lane, [&](uint64_t dst) {
+#pragma unroll
+                    for (int q = 0; q < kQ; ++q)
+                        st_global<float4>(dst + 16 * (lane + q * kWave), acc[q]);
+                });
             }
         }
     }
@@ -848,7 +1037,7 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     ra.n_host = n_host;
     ra.dY = burst && !L.by_ref ? reinterpret_cast<const float *>(ws + L.stash_dy) : dY;
     ra.dy_ptrs = L.by_ref ? reinterpret_cast<const float *const *>(ws + L.dy_ptrs) : nullptr;
-    ra.pos_bits = L.pos_bits;
+    ra.pos_bits = L.by_ref ? L.pos_bits : 31;
     ra.gacc = reinterpret_cast<float *>(ws + L.gacc);
     ra.slot_rows[0] = sa.slot_rows[0];
     ra.slot_rows[1] = sa.slot_rows[1];
@@ -864,15 +1053,15 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     const dim3 grid((nchunk + per_block - 1) / per_block, 2);
     prof_begin(NGRAM_PROF_REDUCE, s);
     if (!f) {
-        seg_reduce_kernel<kAccum><<<grid, kRedThreads, 0, s>>>(ra);
+        seg_reduce_kernel<<<grid, kRedThreads, 0, s>>>(ra);
         prof_end(NGRAM_PROF_REDUCE, s);
         fixup_kernel<kAccum><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else if (f->dtype == NGRAM_DTYPE_BF16) {
-        seg_reduce_kernel<kFuseBf16><<<grid, kRedThreads, 0, s>>>(ra);
+        seg_step_kernel<2><<<grid, kRedThreads, 0, s>>>(ra);
         prof_end(NGRAM_PROF_REDUCE, s);
         fixup_kernel<kFuseBf16><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else {
-        seg_reduce_kernel<kFuseF32><<<grid, kRedThreads, 0, s>>>(ra);
+        seg_step_kernel<4><<<grid, kRedThreads, 0, s>>>(ra);
         prof_end(NGRAM_PROF_REDUCE, s);
         fixup_kernel<kFuseF32><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     }
