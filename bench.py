@@ -2,12 +2,15 @@
 """Benchmark of the hashed bigram + trigram embedding path on one MI355X.
 
 One step = one accumulation window of the whole hot path: 4 micro-steps of
-(context + hash + signed gather-sum forward, then backward: sort, dedupe,
-segment reduction into the window) followed by one fused lazy sparse step on
-every touched row.  Workload (default): the full 84.6M-row table (2 x
-42,300,000 x 768 bf16, about 130 GB) resident on one GPU, 393,216 tokens per
-micro-step drawn from Zipf(1.1) over a 50,304-id vocabulary with EoS-aligned
-documents (synthetic stand-in for FineWeb), upstream gradients N(0, 1).
+the forward (context + hash + signed gather-sum) and the backward (keys
+kept), then the window's reduction fused with the lazy sparse step (sort,
+dedupe, signed segment reduction, step of every touched row).  --mode
+spread reduces each micro-step into the window accumulator as it comes and
+fuses the step into the last one instead.  Workload (default): the full
+84.6M-row table (2 x 42,300,000 x 768 bf16, about 130 GB) resident on one
+GPU, 393,216 tokens per micro-step drawn from Zipf(1.1) over a 50,304-id
+vocabulary with EoS-aligned documents (synthetic stand-in for FineWeb),
+upstream gradients N(0, 1).
 
 Prints one JSON line.  `value` is the window's tokens per second through the
 whole path with all inputs resident in HBM; per-kernel-group times come from
@@ -45,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=6, help="timed windows")
     ap.add_argument("--warmup", type=int, default=2, help="untimed windows")
     ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
-    ap.add_argument("--mode", default="spread", choices=["spread", "burst", "burst_ref"],
+    ap.add_argument("--mode", default="burst_ref", choices=["spread", "burst", "burst_ref"],
                     help="spread: each micro-step reduced into the window at once; burst: micro-steps "
                          "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
                          "in place at step time")
@@ -81,61 +84,73 @@ def device_table(torch, R, dtype, seed, chunk=1 << 21):
 
 
 def window_stats(torch, N, cfg, toks):
-    """Per micro-step and channel: distinct rows and rows new to the window;
-    distinct rows of the whole window.  Uses the library's own hash."""
+    """From the library's own hash, per micro-step and channel: distinct rows
+    and rows new to the window, and (trigram) rows that occur once in the
+    micro-step and are new to the window; distinct rows of the whole window;
+    trigram rows that occur once in the whole window."""
     steps = []
     seen = [None, None]
+    all_t = []
     for tok in toks:
         idx = N.hash(cfg, tok)
         per = []
         for c in range(2):
-            u = torch.unique(idx[c] & 0x7FFFFFFF)
-            new = int(u.numel()) if seen[c] is None else int((~torch.isin(u, seen[c])).sum())
+            r = (idx[c] & 0x7FFFFFFF).long()
+            u, cnt = torch.unique(r, return_counts=True)
+            fresh = torch.ones_like(u, dtype=torch.bool) if seen[c] is None else ~torch.isin(u, seen[c])
+            single_new = int(((cnt == 1) & fresh).sum()) if c == 1 else 0
+            per.append((int(u.numel()), int(fresh.sum()), single_new))
             seen[c] = u if seen[c] is None else torch.unique(torch.cat([seen[c], u]))
-            per.append((int(u.numel()), new))
+            if c == 1:
+                all_t.append(r)
         steps.append(per)
-    return steps, [int(s.numel()) for s in seen]
+    _, cnt = torch.unique(torch.cat(all_t), return_counts=True)
+    return steps, [int(s.numel()) for s in seen], int((cnt == 1).sum())
 
 
 STATE = 8     # one (v, t_last) record per row
 
 
 def algorithmic_bytes(T, stats, row_bytes, mode, path):
-    """Bytes each kernel group must move per window, by definition (the design doc
-    gives the per-unit figures), and its launches per window.
+    """Bytes each kernel group must move per window (the design doc gives the
+    per-unit figures), listed per launch.
 
     accumulate reduction, per micro-step and channel: every key reads its dY
       row; a row new to the window writes its window row, one already there
       reads and writes it;
-    fused reduction (last micro-step, or the whole window in burst mode): dY
-      rows; a row already in the window reads its window row; every touched
-      row reads and writes its table row and its state;
+    fused reduction (last micro-step, or the whole window in burst modes):
+      the bigram pass reads the dY row of every key; the trigram pass reads
+      those of the keys whose row is not a singleton new to the window (the
+      others are stepped by the bigram pass from the dY row it holds); a row
+      already in the window reads its window row; every touched row reads and
+      writes its table row and its state;
     step: per row left to it, window row read + table row read and written +
       state read and written + slot id;
     stash (burst): dY row read and written, token id, two indices, row code;
     stash (burst by reference): token id, two indices, row code."""
-    steps, uwin = stats
+    steps, uwin, tsingle_win = stats
     A = len(steps)
     fwd = T * (3 * row_bytes + 4)
-    step_row = ROW_F32 + 2 * row_bytes + 2 * STATE + 4
+    table_state = 2 * row_bytes + 2 * STATE
+    step_row = ROW_F32 + table_state + 4
     out = {"fwd": [fwd] * A, "sort": [2 * T * 4 * 2 * 4] * A}
     if mode in ("burst", "burst_ref"):
         n = A * T
         copy = 2 * ROW_F32 if mode == "burst" else 0
         out["stash"] = [T * (copy + 4 + 8 + 4)] * A
         out["sort"] = [2 * n * 4 * 2 * 4]
-        out["reduce"] = [2 * n * ROW_F32 + sum(uwin) * (2 * row_bytes + 2 * STATE)]
+        out["reduce"] = [(2 * n - tsingle_win) * ROW_F32 + sum(uwin) * table_state]
         out["step"] = [0]
         return out
     red = []
     last = A - 1 if path == "fused" else A
     for m in range(last):
-        red.append(sum(T * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32 for (u, new) in steps[m]))
+        red.append(sum(T * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32 for (u, new, _) in steps[m]))
     fused_rows = 0
     if path == "fused":
         b = 0
-        for (u, new) in steps[-1]:
-            b += T * ROW_F32 + (u - new) * ROW_F32 + u * (2 * row_bytes + 2 * STATE)
+        for (u, new, single_new) in steps[-1]:
+            b += (T - single_new) * ROW_F32 + (u - new) * ROW_F32 + u * table_state
             fused_rows += u
         red.append(b)
     out["reduce"] = red

@@ -169,7 +169,8 @@ struct WsHeader {
     uint32_t n_stash;      // burst mode: positions kept since the last reduce
     uint32_t epoch;        // window number; slot-map entries of other windows are stale
     uint32_t n_micro;      // burst modes: micro-steps kept since the last reduce
-    uint32_t pad[53];
+    uint32_t n_multi;      // fused reduction: trigram keys left after the singleton split
+    uint32_t pad[52];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
@@ -212,6 +213,8 @@ struct WsLayout {
     uint64_t blk;           // uint32 [2][nblk]
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
+    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row | neg << 31
+                            // if that row is a singleton of the reduction, else kNotSingle
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
     uint64_t stash_dy;      // fp32 [nk][768] (burst, copying): the kept dY rows
@@ -227,6 +230,7 @@ struct WsLayout {
     bool burst;             // micro-steps are kept and reduced at step time
     bool by_ref;            // ... and their dY is read where the caller keeps it
     int pos_bits;           // by_ref: dY row code = micro-step << pos_bits | position
+    int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
 };
 

@@ -286,19 +286,33 @@ constexpr uint32_t kDropped = 0xFFFFFFFFu;
 
 struct SlotArgs {
     const uint32_t *rows;   // sorted keys [2][nk]
+    const uint32_t *vals;   // sorted payloads [2][nk]: dY row code | neg << 31
     int64_t nk;
     const uint32_t *n_dev;
     uint32_t n_host;
     SlotEntry *slot_map[2];
     uint32_t *slot_rows[2];
     uint32_t *seg_info;     // [2][nk]: at heads, slot | new << 31
-    uint32_t *blk;          // [2][nblk]: new heads per tile
+    uint32_t *blk;          // [2][nblk]: new heads per tile; singleton split: kept trigram keys per tile
     uint32_t nblk;
     uint32_t wrows;
     WsHeader *hdr;
+    uint32_t *tinfo;        // singleton split only (fused reduction), else null
+    uint32_t *split_rows;   // compacted trigram keys, payloads and head info
+    uint32_t *split_vals;
+    uint32_t *split_info;
 };
 
+// A trigram row is handed to the bigram pass when the reduction is fused with
+// the step, the row occurs at exactly one position of the reduced keys, and
+// the window holds nothing for it yet: its gradient is then s dY of that one
+// position, which the bigram pass has in registers anyway.
+constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
+
 // Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
+// With the singleton split (trigram channel), every key also records in
+// tinfo whether its row is a singleton, and the tile's kept (non-singleton)
+// keys are counted.
 __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
@@ -309,24 +323,81 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
     const SlotEntry *sm = a.slot_map[c];
     uint32_t *info = a.seg_info + (size_t)c * a.nk;
     const uint32_t epoch = a.hdr->epoch;
-    uint32_t cnt = 0;
+    const bool split = a.tinfo != nullptr && c == 1;
+    uint32_t cnt = 0, kept = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
         if (i < n) {
             const uint32_t r = R[i];
+            bool single = false;
             if (i == 0 || R[i - 1] != r) {
                 const SlotEntry e = sm[r];
                 const bool known = e.epoch == epoch;
                 info[i] = known ? e.slot : kNewHead;
                 cnt += known ? 0u : 1u;
+                single = split && !known && (i + 1 == n || R[i + 1] != r);
+            }
+            if (split) {
+                const uint32_t v = a.vals[(size_t)c * a.nk + i];
+                a.tinfo[v & 0x7FFFFFFFu] = single ? (r | (v & 0x80000000u)) : kNotSingle;
+                kept += single ? 0u : 1u;
             }
         }
     }
     uint32_t total;
-    block_excl_scan<kSortThreads>(cnt, s_wave, &total);
+    block_excl_scan<kSortThreads>(split ? kept : cnt, s_wave, &total);
     if (threadIdx.x == 0)
         a.blk[(size_t)c * a.nblk + blockIdx.x] = total;
+}
+
+// Singleton split: the trigram keys that stay in the trigram pass (rows with
+// more than one position, or already in the window) are copied, in order,
+// with their head info to the split arrays; hdr->n_multi gets their count.
+__global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
+{
+    __shared__ uint32_t s_wave[kSortThreads / kWave];
+    constexpr int c = 1;
+    const uint32_t b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t *blk = a.blk + (size_t)c * a.nblk;
+    const uint32_t upto = b == 0 ? a.nblk : b;
+    uint32_t part = 0, part_before = 0;
+    for (uint32_t k = tid; k < upto; k += kSortThreads) {
+        const uint32_t x = blk[k];
+        part += x;
+        part_before += k < b ? x : 0u;
+    }
+    uint32_t before_tiles, all_tiles;
+    block_excl_scan<kSortThreads>(part_before, s_wave, &before_tiles);
+    block_excl_scan<kSortThreads>(part, s_wave, &all_tiles);
+    if (b == 0 && tid == 0)
+        a.hdr->n_multi = all_tiles;
+    const uint32_t i0 = b * kSortTile + tid * kSortItems;
+    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const uint32_t *V = a.vals + (size_t)c * a.nk;
+    const uint32_t *info = a.seg_info + (size_t)c * a.nk;
+    uint32_t keep = 0, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t i = i0 + j;
+        if (i < n && a.tinfo[V[i] & 0x7FFFFFFFu] == kNotSingle) {
+            keep |= 1u << j;
+            ++cnt;
+        }
+    }
+    uint32_t o = before_tiles + block_excl_scan<kSortThreads>(cnt, s_wave, nullptr);
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        if (keep & (1u << j)) {
+            const uint32_t i = i0 + j;
+            a.split_rows[o] = R[i];
+            a.split_vals[o] = V[i];
+            a.split_info[o] = info[i];
+            ++o;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
@@ -401,13 +472,12 @@ constexpr int kFuseBf16 = 2;
 constexpr int kFuseF32 = 4;
 
 struct RedArgs {
-    const uint32_t *rows;   // sorted [2][nk]
-    const uint32_t *vals;   // sorted [2][nk]: dY row code | neg << 31
-    const uint32_t *info;   // [2][nk] at heads
-    int64_t nk;
-    const uint32_t *n_dev;
-    uint32_t n_host;
-    const float *dY;        // [positions][768], indexed by the row code
+    const uint32_t *rows[2];    // per channel: sorted row keys
+    const uint32_t *vals[2];    // per channel: dY row code | neg << 31
+    const uint32_t *info[2];    // per channel: at segment heads, slot (| new << 31) or kNewHead
+    const uint32_t *n_dev[2];   // per channel: device key count (null: n_host)
+    uint32_t n_host;            // key count bound (grids cover it)
+    const float *dY;            // [positions][768], indexed by the row code
     const float *const *dy_ptrs;   // burst by reference: dY of each micro-step
     int pos_bits;           // row code = micro-step << pos_bits | position (31: one dY buffer)
     float *gacc;            // [2][wrows][768]
@@ -417,6 +487,7 @@ struct RedArgs {
     uint64_t *owners;       // [2][nchunk]: chunk | info << 32
     int64_t nchunk;
     WsHeader *hdr;
+    const uint32_t *tinfo;  // fused with the singleton split: trigram singleton of each dY row code
     FuseArgs f;             // fused modes only
 };
 
@@ -462,9 +533,9 @@ __device__ __forceinline__ bool chunk_plan(const RedArgs &a, int c, int64_t chun
     const int64_t c0 = chunk * kChunk;
     if (c0 >= n)
         return false;
-    const uint32_t *R = a.rows + (size_t)c * a.nk;
-    const uint32_t *V = a.vals + (size_t)c * a.nk;
-    const uint32_t *I = a.info + (size_t)c * a.nk;
+    const uint32_t *R = a.rows[c];
+    const uint32_t *V = a.vals[c];
+    const uint32_t *I = a.info[c];
     p.nv = (int)min<int64_t>(kChunk, (int64_t)n - c0);
     const bool valid = lane < p.nv;
     p.r0 = valid ? R[c0 + lane] : 0xFFFFFFFFu;
@@ -570,7 +641,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
-    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t n = count_of(a.n_dev[c], a.n_host);
     if (chunk == 0 && lane == 0)
         a.hdr->n_slots[c] = a.hdr->n_next[c];   // the slots assign_kernel handed out
     ChunkPlan p;
@@ -728,21 +799,59 @@ __device__ __forceinline__ void store_stepped(const WRow<ELT> &w, const float4 (
     }
 }
 
+// One row's step from its complete window gradient g (sum of squares by the
+// wavefront), its prefetched table row w and state st.
+template <int ELT>
+__device__ __forceinline__ void step_one(const float4 (&g)[kQ], const WRow<ELT> &w, RowState st, uint32_t row,
+                                         uint64_t table, uint64_t state, const RedArgs &a, int lane)
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+        ss += g[q].x * g[q].x + g[q].y * g[q].y + g[q].z * g[q].z + g[q].w * g[q].w;
+    ss = wave_sum(ss);
+    float vn;
+    bool order_bad;
+    const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
+    store_stepped<ELT>(w, g, scale, table + (uint64_t)row * (kDim * ELT));
+    if (lane == 0) {
+        st_global<RowState>(state + (uint64_t)row * sizeof(RowState), RowState{vn, a.f.p.t});
+        if (order_bad)
+            atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
+    }
+}
+
+// With the singleton split, the bigram pass (channel 0) also steps, for every
+// key it reads, the trigram row of that key's position when tinfo marks it a
+// singleton: its gradient is s_t dY of this very row of dY.  The trigram pass
+// then only walks the keys the split kept.
 template <int ELT>
 __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
-    const uint32_t n = count_of(a.n_dev, a.n_host);
+    const uint32_t n = count_of(a.n_dev[c], a.n_host);
     ChunkPlan p;
     if (!chunk_plan(a, c, chunk, n, lane, p))
         return;
+    const bool tsplit = a.tinfo != nullptr && c == 0;
+    uint32_t t0 = kNotSingle, t1 = kNotSingle;   // trigram singleton of keys lane, 64 + lane
+    if (tsplit) {
+        if (lane < p.nv)
+            t0 = a.tinfo[p.v0 & 0x7FFFFFFFu];
+        if (p.owner_full && kChunk + lane < p.jend)
+            t1 = a.tinfo[p.v1 & 0x7FFFFFFFu];
+    }
     uint64_t lane_base = dy_lane_base(a, lane);
     settle_plan(p);
     settle(lane_base);
+    settle(t0);
+    settle(t1);
     const uint64_t table = (uint64_t)a.f.w[c] + (uint64_t)ELT * 4 * lane;
     const uint64_t state = (uint64_t)a.f.st[c];
+    const uint64_t table_t = (uint64_t)a.f.w[1] + (uint64_t)ELT * 4 * lane;
+    const uint64_t state_t = (uint64_t)a.f.st[1];
     const uint64_t gacc = (uint64_t)a.gacc + (uint64_t)c * a.wrows * (kDim * 4) + 16 * lane;
 
     // keys 0..63 that end a segment stepped here (not a partial piece); an
@@ -763,14 +872,15 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
     for (int j = p.j0; j < p.jend; j += kStepU) {
         float4 x[kStepU][kQ];
         uint32_t sg[kStepU];
-        WRow<ELT> w[kStepU];
-        RowState st[kStepU];
-        uint32_t row[kStepU];
+        WRow<ELT> w[kStepU], wt[kStepU];
+        RowState st[kStepU], stt[kStepU];
+        uint32_t row[kStepU], tv[kStepU];
         bool ends_here[kStepU];
 #pragma unroll
         for (int u = 0; u < kStepU; ++u) {
             const int k = j + u;
             ends_here[u] = false;
+            tv[u] = kNotSingle;
             if (k < p.jend) {
                 const uint32_t v = lane_val(p.v0, p.v1, k);
                 sg[u] = v & 0x80000000u;
@@ -783,6 +893,14 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                     row[u] = k < kChunk ? (uint32_t)__builtin_amdgcn_readlane((int)p.r0, k) : p.row_last;
                     load_wrow<ELT>(w[u], table + (uint64_t)row[u] * (kDim * ELT));
                     st[u] = ld_global<RowState>(state + (uint64_t)row[u] * sizeof(RowState));
+                }
+                if (tsplit) {
+                    tv[u] = lane_val(t0, t1, k);
+                    if (tv[u] != kNotSingle) {
+                        const uint32_t tr = tv[u] & 0x7FFFFFFFu;
+                        load_wrow<ELT>(wt[u], table_t + (uint64_t)tr * (kDim * ELT));
+                        stt[u] = ld_global<RowState>(state_t + (uint64_t)tr * sizeof(RowState));
+                    }
                 }
             }
         }
@@ -807,6 +925,14 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                 acc[q].z = fmaf(x[u][q].z, sgn, acc[q].z);
                 acc[q].w = fmaf(x[u][q].w, sgn, acc[q].w);
             }
+            if (tv[u] != kNotSingle) {   // the trigram singleton of this position: G = s_t dY
+                const float ts = (tv[u] & 0x80000000u) ? -1.f : 1.f;
+                float4 g[kQ];
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    g[q] = make_float4(ts * x[u][q].x, ts * x[u][q].y, ts * x[u][q].z, ts * x[u][q].w);
+                step_one<ELT>(g, wt[u], stt[u], tv[u] & 0x7FFFFFFFu, table_t, state_t, a, lane);
+            }
             if (ends_here[u]) {
                 const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
                 float4 g[kQ];
@@ -821,20 +947,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                     if (lane == 0)
                         a.slot_rows[c][info] = row[u] | kSlotStepped;
                 }
-                float ss = 0.f;
-#pragma unroll
-                for (int q = 0; q < kQ; ++q)
-                    ss += g[q].x * g[q].x + g[q].y * g[q].y + g[q].z * g[q].z + g[q].w * g[q].w;
-                ss = wave_sum(ss);
-                float vn;
-                bool order_bad;
-                const float scale = step_scale(ss, st[u], a.f.p, vn, order_bad);
-                store_stepped<ELT>(w[u], g, scale, table + (uint64_t)row[u] * (kDim * ELT));
-                if (lane == 0) {
-                    st_global<RowState>(state + (uint64_t)row[u] * sizeof(RowState), RowState{vn, a.f.p.t});
-                    if (order_bad)
-                        atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
-                }
+                step_one<ELT>(g, w[u], st[u], row[u], table, state, a, lane);
             } else if (seg_ends(p, k)) {
                 flush_partial(a, p, c, chunk, ps, lane, [&](uint64_t dst) {
 #pragma unroll
@@ -862,8 +975,8 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint32_t nown = a.hdr->n_owner[c];
-    const uint32_t n = count_of(a.n_dev, a.n_host);
-    const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const uint32_t n = count_of(a.n_dev[c], a.n_host);
+    const uint32_t *R = a.rows[c];
     const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
     for (uint32_t k = blockIdx.x; k < nown; k += gridDim.x) {
         const uint64_t rec = a.owners[(size_t)c * a.nchunk + k];
@@ -1011,6 +1124,7 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     }
     SlotArgs sa;
     sa.rows = reinterpret_cast<const uint32_t *>(ws + L.keys[cur]);
+    sa.vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
     sa.nk = L.nk;
     sa.n_dev = n_dev;
     sa.n_host = n_host;
@@ -1023,18 +1137,37 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     sa.nblk = nblk;
     sa.wrows = (uint32_t)L.wrows;
     sa.hdr = hdr;
+    // fused: trigram singletons go to the bigram pass; the kept trigram keys
+    // are compacted into the sort's spare buffers (free once it is done)
+    uint32_t *spare_k = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
+    uint32_t *spare_v = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
+    sa.tinfo = f ? reinterpret_cast<uint32_t *>(ws + L.tinfo) : nullptr;
+    sa.split_rows = spare_k + L.nk;
+    sa.split_vals = spare_v + L.nk;
+    sa.split_info = spare_k;
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    if (!f)   // fused: rows new to the window are stepped at once and need no slot
+    if (f)
+        split_kernel<<<nblk, kSortThreads, 0, s>>>(sa);
+    else   // fused: rows new to the window are stepped at once and need no slot
         assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     prof_end(NGRAM_PROF_SORT, s);
 
     RedArgs ra;
-    ra.rows = sa.rows;
-    ra.vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
-    ra.info = sa.seg_info;
-    ra.nk = L.nk;
-    ra.n_dev = n_dev;
+    const uint32_t *vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
+    for (int c = 0; c < 2; ++c) {
+        ra.rows[c] = sa.rows + (size_t)c * L.nk;
+        ra.vals[c] = vals + (size_t)c * L.nk;
+        ra.info[c] = sa.seg_info + (size_t)c * L.nk;
+        ra.n_dev[c] = n_dev;
+    }
+    if (f) {
+        ra.rows[1] = sa.split_rows;
+        ra.vals[1] = sa.split_vals;
+        ra.info[1] = sa.split_info;
+        ra.n_dev[1] = &hdr->n_multi;
+    }
     ra.n_host = n_host;
+    ra.tinfo = sa.tinfo;
     ra.dY = burst && !L.by_ref ? reinterpret_cast<const float *>(ws + L.stash_dy) : dY;
     ra.dy_ptrs = L.by_ref ? reinterpret_cast<const float *const *>(ws + L.dy_ptrs) : nullptr;
     ra.pos_bits = L.by_ref ? L.pos_bits : 31;
