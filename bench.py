@@ -239,10 +239,15 @@ def main():
         x = torch.ones(n, dtype=torch.float32, device="cuda")
         y = torch.empty_like(x)
         torch.cuda.synchronize()
-        for _ in range(3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        for k in range(3):
             y.copy_(x)
+            ev[k + 1].record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_per_copy": 4 * n, "copies": 3}))
+        ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(3)]
+        print(json.dumps({"copy_calibration_bytes_per_copy": 4 * n, "copies": 3, "ms_per_copy": ms,
+                          "copy_gbps_read_plus_write": round(8 * n / (min(ms) * 1e-3) / 1e9, 1)}))
         return
 
     from sparse_hashed_gram_amd import ngram as N
