@@ -84,10 +84,11 @@ def device_table(torch, R, dtype, seed, chunk=1 << 21):
 
 
 def window_stats(torch, N, cfg, toks):
-    """From the library's own hash, per micro-step and channel: distinct rows
-    and rows new to the window, and (trigram) rows that occur once in the
-    micro-step and are new to the window; distinct rows of the whole window;
-    trigram rows that occur once in the whole window."""
+    """From the library's own hash, per micro-step and channel: distinct rows,
+    rows new to the window, and (trigram) rows that occur once in the
+    micro-step and are new to the window, and rows that occur once in it;
+    distinct rows of the whole window; trigram rows that occur once in the
+    whole window."""
     steps = []
     seen = [None, None]
     all_t = []
@@ -99,7 +100,8 @@ def window_stats(torch, N, cfg, toks):
             u, cnt = torch.unique(r, return_counts=True)
             fresh = torch.ones_like(u, dtype=torch.bool) if seen[c] is None else ~torch.isin(u, seen[c])
             single_new = int(((cnt == 1) & fresh).sum()) if c == 1 else 0
-            per.append((int(u.numel()), int(fresh.sum()), single_new))
+            single = int((cnt == 1).sum()) if c == 1 else 0
+            per.append((int(u.numel()), int(fresh.sum()), single_new, single))
             seen[c] = u if seen[c] is None else torch.unique(torch.cat([seen[c], u]))
             if c == 1:
                 all_t.append(r)
@@ -115,9 +117,11 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path):
     """Bytes each kernel group must move per window (the design doc gives the
     per-unit figures), listed per launch.
 
-    accumulate reduction, per micro-step and channel: every key reads its dY
-      row; a row new to the window writes its window row, one already there
-      reads and writes it;
+    accumulate reduction, per micro-step: the bigram pass reads the dY row of
+      every key, the trigram pass those of keys whose row occurs more than
+      once in the micro-step (a singleton's row is written by the bigram
+      pass from the dY row it holds); per channel, a row new to the window
+      writes its window row, one already there reads and writes it;
     fused reduction (last micro-step, or the whole window in burst modes):
       the bigram pass reads the dY row of every key; the trigram pass reads
       those of the keys whose row is not a singleton new to the window (the
@@ -145,11 +149,12 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path):
     red = []
     last = A - 1 if path == "fused" else A
     for m in range(last):
-        red.append(sum(T * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32 for (u, new, _) in steps[m]))
+        red.append(sum((T - single) * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32
+                       for (u, new, _, single) in steps[m]))
     fused_rows = 0
     if path == "fused":
         b = 0
-        for (u, new, single_new) in steps[-1]:
+        for (u, new, single_new, _) in steps[-1]:
             b += (T - single_new) * ROW_F32 + (u - new) * ROW_F32 + u * table_state
             fused_rows += u
         red.append(b)

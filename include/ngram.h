@@ -111,7 +111,8 @@ typedef struct ngram_config {
     int32_t mode;        /* NGRAM_MODE_SPREAD, _BURST or _BURST_REF         */
     int64_t window_rows; /* distinct rows one window can hold per channel;
                             0 = min(max(rows[0], rows[1]),
-                                    accum_steps * max_tokens)              */
+                                    accum_steps * max_tokens); the result
+                            must be below 2^30 - 1                         */
 } ngram_config;
 
 /* Optimizer state of one table row (8 bytes, 8-byte aligned arrays): the

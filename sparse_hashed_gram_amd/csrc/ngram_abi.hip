@@ -50,8 +50,15 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->mode == NGRAM_MODE_BURST_REF && c->max_tokens > (int64_t(1) << 25))
         return NGRAM_ECONFIG;
-    if (c->window_rows < 0 || c->window_rows > INT32_MAX)
+    if (c->window_rows < 0)
         return NGRAM_ECONFIG;
+    {   // window slots must fit 30 bits (the singleton map packs new and sign bits above them)
+        const int64_t window_keys = (int64_t)c->accum_steps * c->max_tokens;
+        const int64_t rmax = c->rows[0] > c->rows[1] ? c->rows[0] : c->rows[1];
+        const int64_t wrows = c->window_rows > 0 ? c->window_rows : (window_keys < rmax ? window_keys : rmax);
+        if (wrows >= kMaxWindowRows)
+            return NGRAM_ECONFIG;
+    }
     return NGRAM_OK;
 }
 
@@ -105,6 +112,8 @@ WsLayout layout(const ngram_config *c)
     o = up(o + 4ull * 2 * kRadix);
     L.blk = o;
     o = up(o + 4ull * 2 * (uint64_t)L.nblk);
+    L.kept = o;
+    o = up(o + 4ull * (uint64_t)L.nblk);
     L.partial = o;
     o = up(o + 4ull * 2 * (uint64_t)L.nchunk * 2 * kDim);
     L.owners = o;

@@ -176,6 +176,9 @@ static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
 constexpr uint32_t kMagic = 0x6E677231u;
 
+// Window slots stay below this (the singleton map keeps two flag bits above a slot).
+constexpr int64_t kMaxWindowRows = (int64_t(1) << 30) - 1;
+
 // Row -> window slot map entry.  A row is in the current window iff its
 // epoch equals the header's; ending a window just advances the epoch, so the
 // sparse step never has to clear entries.
@@ -211,10 +214,11 @@ struct WsLayout {
     uint64_t hist;          // uint32 [2][256][nblk]: per-tile digit counts, then offsets
     uint64_t tot;           // uint32 [2][256]: digit totals of a pass
     uint64_t blk;           // uint32 [2][nblk]
+    uint64_t kept;          // uint32 [nblk]: trigram keys kept per sort tile by the singleton split
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
-    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row | neg << 31
-                            // if that row is a singleton of the reduction, else kNotSingle
+    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row's singleton
+                            // record (see the singleton split), else kNotSingle
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
     uint64_t stash_dy;      // fp32 [nk][768] (burst, copying): the kept dY rows

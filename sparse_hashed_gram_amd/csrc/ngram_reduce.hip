@@ -293,26 +293,35 @@ struct SlotArgs {
     SlotEntry *slot_map[2];
     uint32_t *slot_rows[2];
     uint32_t *seg_info;     // [2][nk]: at heads, slot | new << 31
-    uint32_t *blk;          // [2][nblk]: new heads per tile; singleton split: kept trigram keys per tile
+    uint32_t *blk;          // [2][nblk]: new heads per tile
+    uint32_t *kept;         // [nblk]: trigram keys the singleton split keeps, per tile
     uint32_t nblk;
     uint32_t wrows;
     WsHeader *hdr;
-    uint32_t *tinfo;        // singleton split only (fused reduction), else null
+    bool fused;             // the reduction is fused with the step
+    uint32_t *tinfo;        // singleton map, per dY row code
     uint32_t *split_rows;   // compacted trigram keys, payloads and head info
     uint32_t *split_vals;
     uint32_t *split_info;
 };
 
-// A trigram row is handed to the bigram pass when the reduction is fused with
-// the step, the row occurs at exactly one position of the reduced keys, and
-// the window holds nothing for it yet: its gradient is then s dY of that one
-// position, which the bigram pass has in registers anyway.
+// Singleton split.  A trigram row that occurs at exactly one position of the
+// reduced keys has the sum s_t dY of that one position, and the bigram pass
+// holds that dY row in registers anyway: it applies the row there, and the
+// trigram pass only walks the other keys.  The singleton map records, per dY
+// row code:
+//   fused reduction (rows new to the window only): row | neg << 31, and the
+//     bigram pass steps the row;
+//   accumulating reduction: slot | new << 31 | neg << 30 (kDropSingle if the
+//     window had no slot left), and the bigram pass stores (new) or adds the
+//     signed row into that window slot;
+//   kNotSingle otherwise.
 constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
+constexpr uint32_t kDropSingle = 0x3FFFFFFFu;   // slot field of all ones: never a slot
 
 // Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
-// With the singleton split (trigram channel), every key also records in
-// tinfo whether its row is a singleton, and the tile's kept (non-singleton)
-// keys are counted.
+// For the trigram channel it also counts, per tile, the keys the singleton
+// split keeps (split_kernel's layout).
 __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
     const SlotEntry *sm = a.slot_map[c];
     uint32_t *info = a.seg_info + (size_t)c * a.nk;
     const uint32_t epoch = a.hdr->epoch;
-    const bool split = a.tinfo != nullptr && c == 1;
+    const bool empty = a.hdr->n_slots[c] == 0;   // the window holds no row yet: no lookups
     uint32_t cnt = 0, kept = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
@@ -332,28 +341,35 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
             const uint32_t r = R[i];
             bool single = false;
             if (i == 0 || R[i - 1] != r) {
-                const SlotEntry e = sm[r];
-                const bool known = e.epoch == epoch;
-                info[i] = known ? e.slot : kNewHead;
+                bool known = false;
+                uint32_t slot = 0;
+                if (!empty) {
+                    const SlotEntry e = sm[r];
+                    known = e.epoch == epoch;
+                    slot = e.slot;
+                }
+                info[i] = known ? slot : kNewHead;
                 cnt += known ? 0u : 1u;
-                single = split && !known && (i + 1 == n || R[i + 1] != r);
+                single = (i + 1 == n || R[i + 1] != r) && !(a.fused && known);
             }
-            if (split) {
-                const uint32_t v = a.vals[(size_t)c * a.nk + i];
-                a.tinfo[v & 0x7FFFFFFFu] = single ? (r | (v & 0x80000000u)) : kNotSingle;
-                kept += single ? 0u : 1u;
-            }
+            kept += single ? 0u : 1u;
         }
     }
     uint32_t total;
-    block_excl_scan<kSortThreads>(split ? kept : cnt, s_wave, &total);
+    block_excl_scan<kSortThreads>(cnt, s_wave, &total);
     if (threadIdx.x == 0)
         a.blk[(size_t)c * a.nblk + blockIdx.x] = total;
+    if (c == 1) {
+        block_excl_scan<kSortThreads>(kept, s_wave, &total);
+        if (threadIdx.x == 0)
+            a.kept[blockIdx.x] = total;
+    }
 }
 
-// Singleton split: the trigram keys that stay in the trigram pass (rows with
-// more than one position, or already in the window) are copied, in order,
-// with their head info to the split arrays; hdr->n_multi gets their count.
+// Singleton split of the trigram keys, once the heads have their final info:
+// writes every key's singleton-map entry and copies the keys that stay in the
+// trigram pass, in order, with their head info to the split arrays;
+// hdr->n_multi gets their count.
 __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
@@ -361,11 +377,10 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
     const uint32_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const uint32_t n = count_of(a.n_dev, a.n_host);
-    const uint32_t *blk = a.blk + (size_t)c * a.nblk;
     const uint32_t upto = b == 0 ? a.nblk : b;
     uint32_t part = 0, part_before = 0;
     for (uint32_t k = tid; k < upto; k += kSortThreads) {
-        const uint32_t x = blk[k];
+        const uint32_t x = a.kept[k];
         part += x;
         part_before += k < b ? x : 0u;
     }
@@ -382,9 +397,24 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
-        if (i < n && a.tinfo[V[i] & 0x7FFFFFFFu] == kNotSingle) {
-            keep |= 1u << j;
-            ++cnt;
+        if (i < n) {
+            const uint32_t r = R[i];
+            const uint32_t v = V[i];
+            uint32_t rec = kNotSingle;
+            if ((i == 0 || R[i - 1] != r) && (i + 1 == n || R[i + 1] != r)) {
+                const uint32_t in = info[i];
+                if (a.fused) {
+                    if (in == kNewHead)
+                        rec = r | (v & 0x80000000u);
+                } else {
+                    rec = in == kDropped ? kDropSingle : (in | ((v & 0x80000000u) >> 1));
+                }
+            }
+            a.tinfo[v & 0x7FFFFFFFu] = rec;
+            if (rec == kNotSingle) {
+                keep |= 1u << j;
+                ++cnt;
+            }
         }
     }
     uint32_t o = before_tiles + block_excl_scan<kSortThreads>(cnt, s_wave, nullptr);
@@ -487,7 +517,7 @@ struct RedArgs {
     uint64_t *owners;       // [2][nchunk]: chunk | info << 32
     int64_t nchunk;
     WsHeader *hdr;
-    const uint32_t *tinfo;  // fused with the singleton split: trigram singleton of each dY row code
+    const uint32_t *tinfo;  // singleton map per dY row code
     FuseArgs f;             // fused modes only
 };
 
@@ -634,7 +664,9 @@ __device__ __forceinline__ void flush_partial(const RedArgs &a, const ChunkPlan 
 
 // Accumulating reduction (one wavefront per 64 sorted keys, kRedU dY rows in
 // flight whatever the segment boundaries): each finished segment goes to its
-// window row.  Lane l holds elements l + 64 m (m = 0..11), so every load,
+// window row.  With the singleton split the bigram pass also writes, for
+// every key it reads, the signed dY row into the window slot of that
+// position's trigram row when the singleton map names one.  Lane l holds elements l + 64 m (m = 0..11), so every load,
 // store and atomic of a row is twelve 256-byte contiguous wavefront accesses.
 __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 {
@@ -647,10 +679,21 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     ChunkPlan p;
     if (!chunk_plan(a, c, chunk, n, lane, p))
         return;
+    const bool tsplit = a.tinfo != nullptr && c == 0;
+    uint32_t t0 = kNotSingle, t1 = kNotSingle;   // singleton-map entries of keys lane, 64 + lane
+    if (tsplit) {
+        if (lane < p.nv)
+            t0 = a.tinfo[p.v0 & 0x7FFFFFFFu];
+        if (p.owner_full && kChunk + lane < p.jend)
+            t1 = a.tinfo[p.v1 & 0x7FFFFFFFu];
+    }
     uint64_t lane_base = dy_lane_base(a, lane);
     settle_plan(p);
     settle(lane_base);
+    settle(t0);
+    settle(t1);
     const uint64_t gacc = (uint64_t)a.gacc + (uint64_t)c * a.wrows * (kDim * 4) + 4 * lane;
+    const uint64_t gacc_t = (uint64_t)a.gacc + (uint64_t)a.wrows * (kDim * 4) + 4 * lane;
 
     float acc[kPer];
     int ps = p.j0;   // start key of the open segment
@@ -686,6 +729,25 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 #pragma unroll
             for (int m = 0; m < kPer; ++m)
                 acc[m] = fmaf(x[u][m], sgn, acc[m]);
+            if (tsplit) {
+                // this position's trigram row, if a singleton: its whole sum is
+                // s_t dY, stored into a new slot or added (its one addition of
+                // this launch) into an existing one
+                const uint32_t tv = lane_val(t0, t1, k);
+                if (tv != kNotSingle && tv != kDropSingle) {
+                    const float ts = (tv & 0x40000000u) ? -1.f : 1.f;
+                    const uint64_t g = gacc_t + (uint64_t)(tv & 0x3FFFFFFFu) * (kDim * 4);
+                    if (tv >> 31) {
+#pragma unroll
+                        for (int m = 0; m < kPer; ++m)
+                            st_global<float>(g + m * kWave * 4, ts * x[u][m]);
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < kPer; ++m)
+                            atomic_add_global(g + m * kWave * 4, ts * x[u][m]);
+                    }
+                }
+            }
             if (!seg_ends(p, k))
                 continue;
             if ((ps == 0 && p.first_cont) || (ps == p.la && p.last_spills && !p.owner_full)) {
@@ -1137,19 +1199,21 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     sa.nblk = nblk;
     sa.wrows = (uint32_t)L.wrows;
     sa.hdr = hdr;
-    // fused: trigram singletons go to the bigram pass; the kept trigram keys
-    // are compacted into the sort's spare buffers (free once it is done)
+    // singleton split: trigram singletons go to the bigram pass; the kept
+    // trigram keys are compacted into the sort's spare buffers (free once it
+    // is done)
     uint32_t *spare_k = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
     uint32_t *spare_v = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
-    sa.tinfo = f ? reinterpret_cast<uint32_t *>(ws + L.tinfo) : nullptr;
+    sa.kept = reinterpret_cast<uint32_t *>(ws + L.kept);
+    sa.fused = f != nullptr;
+    sa.tinfo = reinterpret_cast<uint32_t *>(ws + L.tinfo);
     sa.split_rows = spare_k + L.nk;
     sa.split_vals = spare_v + L.nk;
     sa.split_info = spare_k;
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    if (f)
-        split_kernel<<<nblk, kSortThreads, 0, s>>>(sa);
-    else   // fused: rows new to the window are stepped at once and need no slot
+    if (!f)   // fused: rows new to the window are stepped at once and need no slot
         assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+    split_kernel<<<nblk, kSortThreads, 0, s>>>(sa);
     prof_end(NGRAM_PROF_SORT, s);
 
     RedArgs ra;
@@ -1160,12 +1224,10 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
         ra.info[c] = sa.seg_info + (size_t)c * L.nk;
         ra.n_dev[c] = n_dev;
     }
-    if (f) {
-        ra.rows[1] = sa.split_rows;
-        ra.vals[1] = sa.split_vals;
-        ra.info[1] = sa.split_info;
-        ra.n_dev[1] = &hdr->n_multi;
-    }
+    ra.rows[1] = sa.split_rows;
+    ra.vals[1] = sa.split_vals;
+    ra.info[1] = sa.split_info;
+    ra.n_dev[1] = &hdr->n_multi;
     ra.n_host = n_host;
     ra.tinfo = sa.tinfo;
     ra.dY = burst && !L.by_ref ? reinterpret_cast<const float *>(ws + L.stash_dy) : dY;

@@ -10,9 +10,10 @@ outputs are checked on samples it computes one by one:
 - step: the sampled rows' W, v, t_last against the oracle's step from the
   GPU's pre-step state, every touched row's t_last, untouched samples bitwise
   unchanged;
-- spread vs burst over several windows from the same state (restoring the
-  touched rows between the two runs), each against the oracle and the two
-  against each other on every touched row.
+- spread, copying burst and burst by reference (fused entry point) over 8
+  windows = 32 steps from the same state (restoring the touched rows between
+  the runs), each against the oracle and the bursts against spread on every
+  touched row.
 """
 import numpy as np
 import pytest
@@ -198,16 +199,21 @@ def test_collision_workload_full_table(big_state):
 
 
 def test_spread_vs_burst_full_table(big_state):
-    """Several windows of the spread-vs-burst workload: each window runs in
-    both modes from the same state; each is checked against the oracle on
-    sampled rows, and the two are compared on every touched row."""
+    """The spread-vs-burst workload, 32 steps = 8 windows: each window runs in
+    spread mode (micro-steps reduced as they come, then the step), in copying
+    burst mode, and in burst-by-reference mode through the fused entry point,
+    each from the same state; each is checked against the oracle on sampled
+    rows, and both burst runs are compared with the spread run on every
+    touched row."""
     N = ng()
     w = workloads.SPREAD_BURST
     cfg_s = big_state["cfg"]
-    cfg_b = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode="burst")
-    ws_s, ws_b = N.Workspace(cfg_s), N.Workspace(cfg_b)
+    cfgs = {"burst": N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode="burst"),
+            "burst_ref": N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=T, mode="burst_ref")}
+    ws_s = N.Workspace(cfg_s)
+    wss = {m: N.Workspace(c) for m, c in cfgs.items()}
     rs = np.random.default_rng(5)
-    for win in range(3):
+    for win in range(8):
         toks = [synth.tokens(w, 4 * win + m) for m in range(4)]
         seeds = [500 + 4 * win + m for m in range(4)]
         idx = [[N.hash(cfg_s, to_dev(tok))[c] & 0x7FFFFFFF for tok in toks] for c in range(2)]
@@ -219,22 +225,24 @@ def test_spread_vs_burst_full_table(big_state):
         _run_and_check_window(big_state, ws_s, toks, seeds, rs, check_fwd=False)
         spread = [(big_state["W"][c].index_select(0, rows[c]), big_state["v"][c].index_select(0, rows[c]))
                   for c in range(2)]
-        for c in range(2):   # restore the touched rows: the state is as before the window
-            big_state["W"][c].index_copy_(0, rows[c], keep[c][0])
-            big_state["state"][c].index_copy_(0, rows[c], keep[c][1])
-        big_state["t"] = t0
-        big_state["cfg"] = cfg_b
-        _run_and_check_window(big_state, ws_b, toks, seeds, rs, check_fwd=False)
-        big_state["cfg"] = cfg_s
-        for c in range(2):
-            Wb = big_state["W"][c].index_select(0, rows[c])
-            vb = big_state["v"][c].index_select(0, rows[c])
-            Ws, vs = spread[c]
-            # every touched row: bf16 values within 2 ulp + a small absolute
-            # floor for cancellations (the sampled rows are held to the full
-            # oracle tolerance above)
-            a, b = Ws.float(), Wb.float()
-            ulp = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7
-            upd = (b - keep[c][0].float()).abs()
-            assert bool(((a - b).abs() <= 2 * ulp + 2e-5 * upd + 1e-5).all())
-            assert bool(((vs - vb).abs() <= 1e-3 * vb.abs() + 1e-12).all())
+        for mode in ("burst", "burst_ref"):
+            for c in range(2):   # restore the touched rows: the state is as before the window
+                big_state["W"][c].index_copy_(0, rows[c], keep[c][0])
+                big_state["state"][c].index_copy_(0, rows[c], keep[c][1])
+            big_state["t"] = t0
+            big_state["cfg"] = cfgs[mode]
+            _run_and_check_window(big_state, wss[mode], toks, seeds, rs, check_fwd=False,
+                                  fused_last=mode == "burst_ref")
+            big_state["cfg"] = cfg_s
+            for c in range(2):
+                Wb = big_state["W"][c].index_select(0, rows[c])
+                vb = big_state["v"][c].index_select(0, rows[c])
+                Ws, vs = spread[c]
+                # every touched row: bf16 values within 2 ulp + a small absolute
+                # floor for cancellations (the sampled rows are held to the full
+                # oracle tolerance above)
+                a, b = Ws.float(), Wb.float()
+                ulp = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7
+                upd = (b - keep[c][0].float()).abs()
+                assert bool(((a - b).abs() <= 2 * ulp + 2e-5 * upd + 1e-5).all()), (win, mode, c)
+                assert bool(((vs - vb).abs() <= 1e-3 * vb.abs() + 1e-12).all()), (win, mode, c)
