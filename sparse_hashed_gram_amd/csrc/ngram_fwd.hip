@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restr
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int lt = e[u] / kCpr;
-            if (lt < ntok)
-                orow[e[u]] = ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]);
+            if (lt < ntok)   // output rows are written once: streaming stores
+                st_global_nt<uint4>((uint64_t)(orow + e[u]), ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]));
         }
     }
 }
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
         const float4 *src = reinterpret_cast<const float4 *>(dY + (size_t)t0 * kDim);
         float4 *dst = reinterpret_cast<float4 *>(sdy + ((size_t)base + t0) * kDim);
         for (int e = tid; e < ntok * (kDim / 4); e += 256)
-            dst[e] = src[e];
+            st_global_nt<float4>((uint64_t)(dst + e), ld_global_nt<float4>((uint64_t)(src + e)));
     }
 }
 

@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
                 const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 4 * lane;
 #pragma unroll
                 for (int m = 0; m < kPer; ++m)
-                    x[u][m] = ld_global<float>(q + m * kWave * 4);
+                    x[u][m] = ld_global_nt<float>(q + m * kWave * 4);
             }
         }
 #pragma unroll
@@ -816,9 +816,9 @@ __device__ __forceinline__ void load_wrow(WRow<ELT> &w, uint64_t addr)
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
         if constexpr (ELT == 2)
-            w.q[q] = ld_global<uint2>(addr + q * kWave * 8);
+            w.q[q] = ld_global_nt<uint2>(addr + q * kWave * 8);
         else
-            w.q[q] = ld_global<float4>(addr + q * kWave * 16);
+            w.q[q] = ld_global_nt<float4>(addr + q * kWave * 16);
     }
 }
 
@@ -843,19 +843,19 @@ __device__ __forceinline__ void store_stepped(const WRow<ELT> &w, const float4 (
         if (!__any(nan)) {
 #pragma unroll
             for (int q = 0; q < kQ; ++q)
-                st_global<uint2>(addr + q * kWave * 8,
+                st_global_nt<uint2>(addr + q * kWave * 8,
                                  make_uint2(bf16_pack_rne(r[q][0], r[q][1]), bf16_pack_rne(r[q][2], r[q][3])));
         } else {
 #pragma unroll
             for (int q = 0; q < kQ; ++q)
-                st_global<uint2>(addr + q * kWave * 8,
+                st_global_nt<uint2>(addr + q * kWave * 8,
                                  make_uint2(bf16_pack(r[q][0], r[q][1]), bf16_pack(r[q][2], r[q][3])));
         }
     } else {
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             const float4 x = w.q[q];
-            st_global<float4>(addr + q * kWave * 16, make_float4(x.x - scale * g[q].x, x.y - scale * g[q].y,
+            st_global_nt<float4>(addr + q * kWave * 16, make_float4(x.x - scale * g[q].x, x.y - scale * g[q].y,
                                                                  x.z - scale * g[q].z, x.w - scale * g[q].w));
         }
     }
@@ -949,19 +949,19 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                 const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 16 * lane;
 #pragma unroll
                 for (int qq = 0; qq < kQ; ++qq)
-                    x[u][qq] = ld_global<float4>(q + qq * kWave * 16);
+                    x[u][qq] = ld_global_nt<float4>(q + qq * kWave * 16);
                 ends_here[u] = k < kChunk ? ((fin >> k) & 1ull) != 0 : (p.owner_full && k == p.jend - 1);
                 if (ends_here[u]) {
                     row[u] = k < kChunk ? (uint32_t)__builtin_amdgcn_readlane((int)p.r0, k) : p.row_last;
                     load_wrow<ELT>(w[u], table + (uint64_t)row[u] * (kDim * ELT));
-                    st[u] = ld_global<RowState>(state + (uint64_t)row[u] * sizeof(RowState));
+                    st[u] = ld_global_nt<RowState>(state + (uint64_t)row[u] * sizeof(RowState));
                 }
                 if (tsplit) {
                     tv[u] = lane_val(t0, t1, k);
                     if (tv[u] != kNotSingle) {
                         const uint32_t tr = tv[u] & 0x7FFFFFFFu;
                         load_wrow<ELT>(wt[u], table_t + (uint64_t)tr * (kDim * ELT));
-                        stt[u] = ld_global<RowState>(state_t + (uint64_t)tr * sizeof(RowState));
+                        stt[u] = ld_global_nt<RowState>(state_t + (uint64_t)tr * sizeof(RowState));
                     }
                 }
             }
@@ -1005,7 +1005,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                     const uint64_t gw = gacc + (uint64_t)info * (kDim * 4);
 #pragma unroll
                     for (int q = 0; q < kQ; ++q)
-                        g[q] = add4(ld_global<float4>(gw + q * kWave * 16), g[q]);
+                        g[q] = add4(ld_global_nt<float4>(gw + q * kWave * 16), g[q]);
                     if (lane == 0)
                         a.slot_rows[c][info] = row[u] | kSlotStepped;
                 }

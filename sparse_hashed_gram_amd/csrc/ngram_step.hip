@@ -43,32 +43,33 @@ template <int ELT>
 __device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot, const uint8_t *W,
                                          const RowState *S, int lane)
 {
-    const float4 *g4 = reinterpret_cast<const float4 *>(G + (size_t)slot * kDim) + lane;
+    // every access here touches its row once: streaming (non-temporal) forms
+    const uint64_t g4 = (uint64_t)(G + (size_t)slot * kDim) + 16 * lane;
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-        r.g[q] = g4[q * kWave];
+        r.g[q] = ld_global_nt<float4>(g4 + q * kWave * 16);
     if (ELT == 2) {
-        const uint2 *wp = reinterpret_cast<const uint2 *>(W + (size_t)r.row * kDim * 2) + lane;
+        const uint64_t wp = (uint64_t)(W + (size_t)r.row * kDim * 2) + 8 * lane;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const uint2 x = wp[q * kWave];
+            const uint2 x = ld_global_nt<uint2>(wp + q * kWave * 8);
             r.w[q][0] = bf16_lo(x.x);
             r.w[q][1] = bf16_hi(x.x);
             r.w[q][2] = bf16_lo(x.y);
             r.w[q][3] = bf16_hi(x.y);
         }
     } else {
-        const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)r.row * kDim * 4) + lane;
+        const uint64_t wp = (uint64_t)(W + (size_t)r.row * kDim * 4) + 16 * lane;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const float4 x = wp[q * kWave];
+            const float4 x = ld_global_nt<float4>(wp + q * kWave * 16);
             r.w[q][0] = x.x;
             r.w[q][1] = x.y;
             r.w[q][2] = x.z;
             r.w[q][3] = x.w;
         }
     }
-    r.s = S[r.row];
+    r.s = ld_global_nt<RowState>((uint64_t)(S + r.row));
 }
 
 template <int ELT>
@@ -92,15 +93,16 @@ __device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W
         r.w[q][3] -= scale * r.g[q].w;
     }
     if (ELT == 2) {
-        uint2 *wp = reinterpret_cast<uint2 *>(W + (size_t)r.row * kDim * 2) + lane;
+        const uint64_t wp = (uint64_t)(W + (size_t)r.row * kDim * 2) + 8 * lane;
 #pragma unroll
         for (int q = 0; q < 3; ++q)
-            wp[q * kWave] = make_uint2(bf16_pack(r.w[q][0], r.w[q][1]), bf16_pack(r.w[q][2], r.w[q][3]));
+            st_global_nt<uint2>(wp + q * kWave * 8,
+                                make_uint2(bf16_pack(r.w[q][0], r.w[q][1]), bf16_pack(r.w[q][2], r.w[q][3])));
     } else {
-        float4 *wp = reinterpret_cast<float4 *>(W + (size_t)r.row * kDim * 4) + lane;
+        const uint64_t wp = (uint64_t)(W + (size_t)r.row * kDim * 4) + 16 * lane;
 #pragma unroll
         for (int q = 0; q < 3; ++q)
-            wp[q * kWave] = make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]);
+            st_global_nt<float4>(wp + q * kWave * 16, make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]));
     }
     if (lane == 0)
         S[r.row] = RowState{vn, a.p.t};
