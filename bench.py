@@ -45,7 +45,7 @@ KERNEL_SRC = {"fwd": "ngram_fwd.hip", "sort": "ngram_reduce.hip", "reduce": "ngr
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=6, help="timed windows")
+    ap.add_argument("--steps", type=int, default=16, help="timed windows")
     ap.add_argument("--warmup", type=int, default=2, help="untimed windows")
     ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
     ap.add_argument("--mode", default="burst_ref", choices=["spread", "burst", "burst_ref"],
@@ -53,13 +53,19 @@ def parse():
                          "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
                          "in place at step time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=65_536,
+    ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per micro-step in the oracle's bounded sample (0 = all)")
+    ap.add_argument("--cpu-windows", type=int, default=3,
+                    help="windows in the oracle's bounded sample (at most --distinct-windows)")
     ap.add_argument("--distinct-windows", type=int, default=4,
                     help="distinct token windows cycled through (inputs stay resident)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 4 GiB fp32 tensor 3 times (the known-size kernel that scales "
                          "rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes), then exit")
+    ap.add_argument("--events-all", action="store_true",
+                    help="HIP events on every launch of every kernel group (each event-carrying kernel "
+                         "leaves the stream idle for a few microseconds; the default times the reduction "
+                         "and sort of every window, one forward per window and the spread step)")
     ap.add_argument("--path", default="fused", choices=["fused", "accum"],
                     help="fused: the window's last micro-step goes through ngram_embed_bwd_step "
                          "(reduction fused with the step); accum: every micro-step through "
@@ -192,43 +198,49 @@ def pmc_traffic(group):
 
 
 def cpu_baseline(w, toks_np, T_sample, dys_fn):
-    """The oracle on a bounded sample of the same workload: one window of
-    4 micro-steps of T_sample tokens (hash, forward, window gradient, sparse
-    step on touched rows).  Table rows are a snapshot of the rows it touches."""
+    """The oracle on a bounded sample of the same workload: whole windows of
+    4 micro-steps of T_sample tokens each (hash, forward, window gradient,
+    sparse step on the touched rows).  Table rows are a snapshot of the rows
+    a window touches; preparing inputs (dY, snapshots) is not timed."""
     import oracle
-    toks = [t[:T_sample] for t in toks_np]
-    dys = [dys_fn(m, T_sample) for m in range(len(toks))]
-    rows = [oracle.ngram_rows(t, w.vocab, w.eos_id, w.rows) for t in toks]
-    rs = np.random.default_rng(0)
-    ids = []
-    snaps = []
-    for c in range(2):
-        u = np.unique(np.concatenate([r[2 * c] for r in rows]))
-        ids.append(u)
-        snaps.append(rs.integers(0x3C00, 0x3CFF, size=(len(u), 768)).astype(np.uint16)
-                     ^ (rs.integers(0, 2, size=(len(u), 768)).astype(np.uint16) << 15))
-    t0 = time.perf_counter()
-    for m in range(len(toks)):
-        rb, nb, rt, nt, _ = oracle.ngram_rows(toks[m], w.vocab, w.eos_id, w.rows)
-        oracle.forward(snaps[0], snaps[1], rb, nb, rt, nt, ids_b=ids[0], ids_t=ids[1],
-                       out_dtype="bf16")
-    dY = np.concatenate(dys)
+    el = 0.0
+    ntok = 0
     n_upd = 0
-    for c in range(2):
-        r = np.concatenate([x[2 * c] for x in rows])
-        n = np.concatenate([x[2 * c + 1] for x in rows])
-        touched, G = oracle.window_grad(r, n, dY)
-        pos = np.searchsorted(ids[c], touched)
-        oracle.sparse_step(G, snaps[c][pos], np.zeros(len(touched), np.float32),
-                           np.zeros(len(touched), np.int32), 1, w.lr, w.beta2, w.eps)
-        n_upd += len(touched)
-    el = time.perf_counter() - t0
-    ntok = sum(len(t) for t in toks)
+    for win, wtoks in enumerate(toks_np):
+        toks = [t[:T_sample] for t in wtoks]
+        A = len(toks)
+        dY = np.concatenate([dys_fn(win * A + m, T_sample) for m in range(A)])
+        rows = [oracle.ngram_rows(t, w.vocab, w.eos_id, w.rows) for t in toks]
+        rs = np.random.default_rng(win)
+        ids = []
+        snaps = []
+        for c in range(2):
+            u = np.unique(np.concatenate([r[2 * c] for r in rows]))
+            ids.append(u)
+            snaps.append(rs.integers(0x3C00, 0x3CFF, size=(len(u), 768)).astype(np.uint16)
+                         ^ (rs.integers(0, 2, size=(len(u), 768)).astype(np.uint16) << 15))
+        t0 = time.perf_counter()
+        for m in range(A):
+            rb, nb, rt, nt, _ = oracle.ngram_rows(toks[m], w.vocab, w.eos_id, w.rows)
+            oracle.forward(snaps[0], snaps[1], rb, nb, rt, nt, ids_b=ids[0], ids_t=ids[1],
+                           out_dtype="bf16")
+        for c in range(2):
+            r = np.concatenate([x[2 * c] for x in rows])
+            n = np.concatenate([x[2 * c + 1] for x in rows])
+            touched, G = oracle.window_grad(r, n, dY)
+            pos = np.searchsorted(ids[c], touched)
+            oracle.sparse_step(G, snaps[c][pos], np.zeros(len(touched), np.float32),
+                               np.zeros(len(touched), np.int32), 1, w.lr, w.beta2, w.eps)
+            n_upd += len(touched)
+        el += time.perf_counter() - t0
+        ntok += sum(len(t) for t in toks)
+        del dY, rows, snaps
+    nw = len(toks_np)
     return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "seconds": el, "updated_rows_per_s": n_upd / el,
-            "sample": (f"one window: 4 micro-steps x {T_sample} tokens of the same stream "
-                       f"(hash, forward, window gradient, sparse step on {n_upd} touched rows; "
-                       f"table rows as a snapshot of the touched rows)")}
+            "sample": (f"{nw} window(s) of 4 micro-steps x {T_sample} tokens of the same streams "
+                       f"(hash, forward, window gradient, sparse step on {n_upd} touched rows in "
+                       f"all; table rows as a snapshot of the touched rows)")}
 
 
 def main():
@@ -286,12 +298,22 @@ def main():
     gid = {"fwd": N.PROF_FWD, "sort": N.PROF_SORT, "reduce": N.PROF_REDUCE, "step": N.PROF_STEP,
            "stash": N.PROF_STASH}
 
-    def arm(ev, groups):
+    # Events ride on the timed kernels' own dispatches, but every kernel that
+    # carries one still leaves the stream idle for a few microseconds around
+    # it.  So they go on a sample of launches that covers every group's
+    # launch kinds: the reduction and sort of every window (the dominant
+    # kernels), one forward per window (micro-step i mod 4 in window i, so
+    # every micro-step's forward is sampled equally), and the spread path's
+    # step; --events-all times every launch of every group.
+    def arm(ev, groups, win, m):
         if ev is None:
             return
         for grp in groups:
+            if not args.events_all and (grp == "stash" or (grp == "fwd" and m != win % A)
+                                        or (grp == "step" and burst)):
+                continue
             a, b = Event(), Event()
-            ev[grp].append((a, b))
+            ev[grp].append((a, b, win, m))
             N.profile_events(gid[grp], a.handle, b.handle)
 
     def disarm():
@@ -300,22 +322,22 @@ def main():
 
     fused_last = args.path == "fused" and not burst
 
-    def run_window(k, ev=None):
+    def run_window(k, ev=None, win=0):
         t_step[0] += 1
         for m in range(A):
-            arm(ev, ("fwd",))
+            arm(ev, ("fwd",), win, m)
             N.embed_fwd(cfg, W[0], W[1], toks[k][m], out=out)
             disarm()
             if fused_last and m == A - 1:
-                arm(ev, ("sort", "reduce", "step"))
+                arm(ev, ("sort", "reduce", "step"), win, m)
                 N.embed_bwd_step(cfg, ws, toks[k][m], dys[m], W[0], W[1], state[0], state[1], t_step[0],
                                  w.lr, w.beta2, w.eps)
                 disarm()
                 return
-            arm(ev, ("stash",) if burst else ("sort", "reduce"))
+            arm(ev, ("stash",) if burst else ("sort", "reduce"), win, m)
             N.embed_bwd_accum(cfg, ws, toks[k][m], dys[m])
             disarm()
-        arm(ev, ("sort", "reduce", "step") if burst else ("step",))
+        arm(ev, ("sort", "reduce", "step") if burst else ("step",), win, 0 if burst else A)
         N.sparse_step(cfg, ws, W[0], W[1], state[0], state[1], t_step[0], w.lr, w.beta2, w.eps)
         disarm()
 
@@ -327,7 +349,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_window(i % nwin, ev)
+        run_window(i % nwin, ev, i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     flags = N.device_status(cfg, ws)
@@ -336,20 +358,23 @@ def main():
         sys.exit(1)
 
     used = [g_ for g_ in GROUPS if ev[g_]]
-    ms_all = {g_: [a.elapsed_ms(b) for a, b in ev[g_]] for g_ in used}
-    per_step = {g_: len(ev[g_]) // args.steps for g_ in used}
-    ms = {g_: float(np.mean(ms_all[g_])) for g_ in used}
     timed_stats = [stats[i % nwin] for i in range(args.steps)]
     bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path) for s in timed_stats]
+    ms_all = {g_: [a.elapsed_ms(b) for a, b, _, _ in ev[g_]] for g_ in used}
+    # algorithmic bytes of each timed launch: launch m of the window's list
+    # (groups with one launch per window have a one-entry list)
+    by_all = {g_: [bytes_[win][g_][min(m, len(bytes_[win][g_]) - 1)] for _, _, win, m in ev[g_]] for g_ in used}
+    per_step = {g_: len(bytes_[0][g_]) for g_ in used}
+    ms = {g_: float(np.mean(ms_all[g_])) for g_ in used}
     # per group: all bytes of its timed launches over all their time
-    abytes = {g_: float(np.sum([sum(b[g_]) for b in bytes_])) / len(ms_all[g_]) for g_ in used}
+    abytes = {g_: float(np.sum(by_all[g_])) / len(ms_all[g_]) for g_ in used}
     upd_rows = float(np.mean([sum(s[1]) for s in timed_stats]))
     total_ms = {g_: ms[g_] * per_step[g_] for g_ in used}
     dom = max([g_ for g_ in ("fwd", "reduce", "step") if g_ in used], key=lambda g_: total_ms[g_])
     if burst or args.path == "fused":
         # the step runs (partly) inside the last reduction launch
-        step_ms_per_window = total_ms["step"] + (ms["reduce"] if burst else
-                                                 float(np.mean(ms_all["reduce"][A - 1::A])))
+        last = [t for t, (_, _, _, m) in zip(ms_all["reduce"], ev["reduce"]) if burst or m == A - 1]
+        step_ms_per_window = total_ms.get("step", 0.0) + float(np.mean(last))
     else:
         step_ms_per_window = total_ms["step"]
     kernels = {}
@@ -394,7 +419,8 @@ def main():
         del W, state, ws, out, dys
         torch.cuda.empty_cache()
         Ts = T if args.cpu_tokens <= 0 else min(T, args.cpu_tokens)
-        res["cpu_baseline"] = cpu_baseline(w, toks_np[0], Ts, lambda m, n: synth.dY(w, m, n))
+        nw = max(1, min(args.cpu_windows, len(toks_np)))
+        res["cpu_baseline"] = cpu_baseline(w, toks_np[:nw], Ts, lambda m, n: synth.dY(w, m, n))
     print(json.dumps(res))
 
 

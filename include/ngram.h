@@ -222,9 +222,11 @@ int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
 
 /* Measurement hook for benchmarks and profilers: until changed, every call
  * made by this host thread that launches kernels of `group` records
- * `start_event` just before that group's first launch and `stop_event` just
- * after its last one, on the call's stream (both are hipEvent_t; NULL stops
- * recording).  Thread-local; never used by the library itself. */
+ * `start_event` at the start of that group's first kernel and `stop_event` at
+ * the end of its last one (both are hipEvent_t; NULL stops recording).  The
+ * events are attached to those kernels' own dispatches on the call's stream
+ * (hipExtLaunchKernelGGL), so recording them adds no work to the stream.
+ * Thread-local; never used by the library itself. */
 int ngram_profile_events(int group, void *start_event, void *stop_event);
 
 /* Synchronises `stream` and writes the sticky device flags to the host word

@@ -5,6 +5,7 @@
 // validates arguments and calls the launchers declared at the bottom.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -334,6 +335,10 @@ constexpr uint32_t kSlotStepped = 0x80000000u;
 
 // ------------------------------------------------------------- profiling
 // Optional event pairs per kernel group (ngram_profile_events); thread-local.
+// The group's first kernel carries the start event and its last kernel the
+// stop event through hipExtLaunchKernelGGL, which takes them from that
+// dispatch's own start and end timestamps: no marker packet enters the
+// stream, so measuring adds no idle time between kernels.
 
 struct ProfSlot {
     hipEvent_t start;
@@ -342,15 +347,18 @@ struct ProfSlot {
 constexpr int kProfGroups = 5;
 extern thread_local ProfSlot g_prof[kProfGroups];
 
-inline void prof_begin(int group, hipStream_t s)
+// Launches kernel<<<grid, block, shmem, s>>>(args...); `first` / `last` mark
+// it as the first / last kernel of `group` for the events above.
+template <typename... KArgs, typename... Args>
+inline void launch_prof(int group, bool first, bool last, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                        uint32_t shmem, hipStream_t s, Args... args)
 {
-    if (g_prof[group].start)
-        (void)hipEventRecord(g_prof[group].start, s);
-}
-inline void prof_end(int group, hipStream_t s)
-{
-    if (g_prof[group].stop)
-        (void)hipEventRecord(g_prof[group].stop, s);
+    hipEvent_t a = first ? g_prof[group].start : nullptr;
+    hipEvent_t b = last ? g_prof[group].stop : nullptr;
+    if (a || b)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, a, b, 0u, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
 }
 
 // ---------------------------------------------------------------- launchers

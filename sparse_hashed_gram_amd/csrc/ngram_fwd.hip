@@ -219,14 +219,8 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
     if (T == 0)
         return hipSuccess;
     const unsigned g = grid_for(T, kFwdTok);
-    prof_begin(NGRAM_PROF_FWD, s);
-    if (dtype == NGRAM_DTYPE_BF16)
-        fwd_kernel<2><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
-                                                (uint8_t *)out, flags);
-    else
-        fwd_kernel<4><<<g, kFwdThreads, 0, s>>>(tok, T, hp, (const uint8_t *)wb, (const uint8_t *)wt,
-                                                (uint8_t *)out, flags);
-    prof_end(NGRAM_PROF_FWD, s);
+    launch_prof(NGRAM_PROF_FWD, true, true, dtype == NGRAM_DTYPE_BF16 ? fwd_kernel<2> : fwd_kernel<4>, dim3(g),
+                dim3(kFwdThreads), 0, s, tok, T, hp, wb, wt, out, flags);
     return hipGetLastError();
 }
 
@@ -236,19 +230,12 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
     uint32_t *spos = reinterpret_cast<uint32_t *>(ws + L.stash_pos);
-    prof_begin(NGRAM_PROF_STASH, s);
-    if (T > 0) {
-        if (L.by_ref)
-            stash_kernel<true><<<grid_for(T, kStashTok), 256, 0, s>>>(tok, dY, T, hp, sidx, spos, nullptr, L.nk,
-                                                                      L.pos_bits, L.accum, hdr);
-        else
-            stash_kernel<false><<<grid_for(T, kStashTok), 256, 0, s>>>(
-                tok, dY, T, hp, sidx, spos, reinterpret_cast<float *>(ws + L.stash_dy), L.nk, L.pos_bits, L.accum,
-                hdr);
-    }
-    stash_advance_kernel<<<1, 1, 0, s>>>(T, L.nk, L.accum, dY,
-                                         L.by_ref ? reinterpret_cast<const float **>(ws + L.dy_ptrs) : nullptr, hdr);
-    prof_end(NGRAM_PROF_STASH, s);
+    if (T > 0)
+        launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true> : stash_kernel<false>,
+                    dim3(grid_for(T, kStashTok)), dim3(256), 0, s, tok, dY, T, hp, sidx, spos,
+                    L.by_ref ? nullptr : reinterpret_cast<float *>(ws + L.stash_dy), L.nk, L.pos_bits, L.accum, hdr);
+    launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel, dim3(1), dim3(1), 0, s, T, L.nk, L.accum, dY,
+                L.by_ref ? reinterpret_cast<const float **>(ws + L.dy_ptrs) : nullptr, hdr);
     return hipGetLastError();
 }
 

@@ -1162,14 +1162,10 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + L.keys[0]);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + L.vals[0]);
 
-    prof_begin(NGRAM_PROF_SORT, s);
-    if (burst)
-        keys_tile_kernel<true><<<nblk, kSortThreads, 0, s>>>(
-            nullptr, reinterpret_cast<const uint32_t *>(ws + L.stash_idx),
-            reinterpret_cast<const uint32_t *>(ws + L.stash_pos), hp, n_host, k0, v0, L.nk, hist, nblk, hdr);
-    else
-        keys_tile_kernel<false><<<nblk, kSortThreads, 0, s>>>(tok, nullptr, nullptr, hp, n_host, k0, v0, L.nk, hist,
-                                                             nblk, hdr);
+    launch_prof(NGRAM_PROF_SORT, true, false, burst ? keys_tile_kernel<true> : keys_tile_kernel<false>, dim3(nblk),
+                dim3(kSortThreads), 0, s, tok, burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) : nullptr,
+                burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
+                hist, nblk, hdr);
     int cur = 0;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = p * kRadixBits;
@@ -1213,8 +1209,7 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     if (!f)   // fused: rows new to the window are stepped at once and need no slot
         assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    split_kernel<<<nblk, kSortThreads, 0, s>>>(sa);
-    prof_end(NGRAM_PROF_SORT, s);
+    launch_prof(NGRAM_PROF_SORT, false, true, split_kernel, dim3(nblk), dim3(kSortThreads), 0, s, sa);
 
     RedArgs ra;
     const uint32_t *vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
@@ -1246,18 +1241,14 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
     const uint32_t per_block = kRedThreads / kWave;
     const dim3 grid((nchunk + per_block - 1) / per_block, 2);
-    prof_begin(NGRAM_PROF_REDUCE, s);
     if (!f) {
-        seg_reduce_kernel<<<grid, kRedThreads, 0, s>>>(ra);
-        prof_end(NGRAM_PROF_REDUCE, s);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_reduce_kernel, grid, dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kAccum><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else if (f->dtype == NGRAM_DTYPE_BF16) {
-        seg_step_kernel<2><<<grid, kRedThreads, 0, s>>>(ra);
-        prof_end(NGRAM_PROF_REDUCE, s);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_step_kernel<2>, grid, dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kFuseBf16><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else {
-        seg_step_kernel<4><<<grid, kRedThreads, 0, s>>>(ra);
-        prof_end(NGRAM_PROF_REDUCE, s);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_step_kernel<4>, grid, dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kFuseF32><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     }
     return hipGetLastError();
