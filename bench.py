@@ -52,6 +52,8 @@ def parse():
                     help="spread: each micro-step reduced into the window at once; burst: micro-steps "
                          "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
                          "in place at step time")
+    ap.add_argument("--dy-dtype", default="f32", choices=["f32", "bf16"],
+                    help="dtype of the upstream gradients dY (the window sums are fp32 either way)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per micro-step in the oracle's bounded sample (0 = all)")
@@ -119,7 +121,7 @@ def window_stats(torch, N, cfg, toks):
 STATE = 8     # one (v, t_last) record per row
 
 
-def algorithmic_bytes(T, stats, row_bytes, mode, path):
+def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4):
     """Bytes each kernel group must move per window (the design doc gives the
     per-unit figures), listed per launch.
 
@@ -137,7 +139,8 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path):
     step: per row left to it, window row read + table row read and written +
       state read and written + slot id;
     stash (burst): dY row read and written, token id, two indices, row code;
-    stash (burst by reference): token id, two indices, row code."""
+    stash (burst by reference): token id, two indices, row code.
+    dY rows count dy_row bytes (3,072 fp32, 1,536 bf16); window rows are fp32."""
     steps, uwin, tsingle_win = stats
     A = len(steps)
     fwd = T * (3 * row_bytes + 4)
@@ -146,22 +149,22 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path):
     out = {"fwd": [fwd] * A, "sort": [2 * T * 4 * 2 * 4] * A}
     if mode in ("burst", "burst_ref"):
         n = A * T
-        copy = 2 * ROW_F32 if mode == "burst" else 0
+        copy = 2 * dy_row if mode == "burst" else 0
         out["stash"] = [T * (copy + 4 + 8 + 4)] * A
         out["sort"] = [2 * n * 4 * 2 * 4]
-        out["reduce"] = [(2 * n - tsingle_win) * ROW_F32 + sum(uwin) * table_state]
+        out["reduce"] = [(2 * n - tsingle_win) * dy_row + sum(uwin) * table_state]
         out["step"] = [0]
         return out
     red = []
     last = A - 1 if path == "fused" else A
     for m in range(last):
-        red.append(sum((T - single) * ROW_F32 + new * ROW_F32 + (u - new) * 2 * ROW_F32
+        red.append(sum((T - single) * dy_row + new * ROW_F32 + (u - new) * 2 * ROW_F32
                        for (u, new, _, single) in steps[m]))
     fused_rows = 0
     if path == "fused":
         b = 0
         for (u, new, single_new, _) in steps[-1]:
-            b += (T - single_new) * ROW_F32 + (u - new) * ROW_F32 + u * table_state
+            b += (T - single_new) * dy_row + (u - new) * ROW_F32 + u * table_state
             fused_rows += u
         red.append(b)
     out["reduce"] = red
@@ -277,7 +280,9 @@ def main():
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     row_bytes = ROW_BF16 if w.dtype == "bf16" else ROW_F32
     torch.cuda.set_device(0)
-    cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode,
+                   dy_dtype=args.dy_dtype)
+    dy_row = 768 * (2 if args.dy_dtype == "bf16" else 4)
 
     W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(2)]
     state = [N.new_state(w.rows[c]) for c in range(2)]
@@ -288,7 +293,7 @@ def main():
     toks = [[torch.from_numpy(t).cuda() for t in win] for win in toks_np]
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
-    dys = [torch.randn((T, 768), generator=g, device="cuda") for _ in range(A)]
+    dys = [torch.randn((T, 768), generator=g, device="cuda").to(cfg.dy_torch_dtype) for _ in range(A)]
     stats = [window_stats(torch, N, cfg, toks[k]) for k in range(nwin)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream().cuda_stream
@@ -359,7 +364,7 @@ def main():
 
     used = [g_ for g_ in GROUPS if ev[g_]]
     timed_stats = [stats[i % nwin] for i in range(args.steps)]
-    bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path) for s in timed_stats]
+    bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path, dy_row) for s in timed_stats]
     ms_all = {g_: [a.elapsed_ms(b) for a, b, _, _ in ev[g_]] for g_ in used}
     # algorithmic bytes of each timed launch: launch m of the window's list
     # (groups with one launch per window have a one-entry list)
@@ -405,7 +410,8 @@ def main():
         "data": "synthetic: Zipf token streams with EoS-aligned documents, N(0,1) upstream gradients",
         "config": {"workload": w.name, "table_rows": w.rows[0] + w.rows[1], "dim": 768,
                    "table_dtype": w.dtype, "tokens_per_micro_step": T, "accum_steps": A,
-                   "mode": args.mode, "path": args.path, "global_batch": A * T},
+                   "mode": args.mode, "path": args.path, "dy_dtype": args.dy_dtype,
+                   "global_batch": A * T},
         "fwd_tokens_per_s": round(T / (ms["fwd"] * 1e-3), 1),
         # rows stepped per second of the kernels that step them (the step, plus
         # the fused reduction when the step is fused into it)

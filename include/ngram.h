@@ -63,9 +63,10 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 2
+#define NGRAM_ABI_VERSION 3
 
-/* dtypes of the tables (and of the forward output) */
+/* dtypes of the tables (and of the forward output), and of the upstream
+ * gradients dY */
 #define NGRAM_DTYPE_F32 0
 #define NGRAM_DTYPE_BF16 1
 
@@ -113,6 +114,11 @@ typedef struct ngram_config {
                             0 = min(max(rows[0], rows[1]),
                                     accum_steps * max_tokens); the result
                             must be below 2^30 - 1                         */
+    int32_t dy_dtype;    /* dtype of dY: NGRAM_DTYPE_F32 (0) or
+                            NGRAM_DTYPE_BF16 (the gradient a bf16 model
+                            returns for a bf16 forward output); window sums
+                            are fp32 either way                             */
+    int32_t reserved;    /* must be 0                                       */
 } ngram_config;
 
 /* Optimizer state of one table row (8 bytes, 8-byte aligned arrays): the
@@ -163,14 +169,15 @@ int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t,
 
 /* Backward of one micro-step into the window accumulator (gradients are
  * accumulated over accum_steps micro-steps and applied once: the
- * @classiclarryd post; README technique list).  dY: fp32 [T][768], the
- * gradient of `out` for the same tokens.  Spread mode reduces now (dY may be
+ * @classiclarryd post; README technique list).  dY: [T][768] of
+ * cfg->dy_dtype, 16-byte aligned, the gradient of `out` for the same tokens.
+ * Each position's signed dY row is added to its rows' window sums in fp32.  Spread mode reduces now (dY may be
  * reused once the stream passes this call); burst mode keeps the tokens' rows
  * and a copy of dY in the workspace and reduces at ngram_window_reduce /
  * ngram_sparse_step; burst-by-reference mode keeps the rows and only the
  * address of dY, which must stay unchanged until the window's step. */
 int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws,
-                          const int32_t *tokens, const float *dY, int64_t T,
+                          const int32_t *tokens, const void *dY, int64_t T,
                           void *stream);
 
 /* Burst mode: reduce every micro-step kept since the last step into the
@@ -198,7 +205,7 @@ int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t,
  * burst mode the whole window is reduced this way.  Arguments as for those
  * two calls; the window is empty afterwards. */
 int ngram_embed_bwd_step(const ngram_config *cfg, void *ws,
-                         const int32_t *tokens, const float *dY, int64_t T,
+                         const int32_t *tokens, const void *dY, int64_t T,
                          void *W_b, void *W_t, ngram_row_state *state_b,
                          ngram_row_state *state_t, int32_t t, float lr,
                          float beta2, float eps, void *stream);

@@ -17,6 +17,8 @@ namespace ngram {
 thread_local ProfSlot g_prof[kProfGroups] = {};
 }
 
+static_assert(sizeof(ngram_config) == 80, "ngram_config layout (the Python binding mirrors it)");
+
 namespace {
 
 constexpr uint64_t kAlign = 256;
@@ -52,6 +54,8 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->window_rows < 0)
         return NGRAM_ECONFIG;
+    if ((c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16) || c->reserved != 0)
+        return NGRAM_ECONFIG;
     {   // window slots must fit 30 bits (the singleton map packs new and sign bits above them)
         const int64_t window_keys = (int64_t)c->accum_steps * c->max_tokens;
         const int64_t rmax = c->rows[0] > c->rows[1] ? c->rows[0] : c->rows[1];
@@ -69,6 +73,7 @@ WsLayout layout(const ngram_config *c)
     L.burst = c->mode != NGRAM_MODE_SPREAD;
     L.by_ref = c->mode == NGRAM_MODE_BURST_REF;
     L.accum = c->accum_steps;
+    L.dy_elt = c->dy_dtype == NGRAM_DTYPE_BF16 ? 2 : 4;
     L.pos_bits = 0;
     while ((int64_t(1) << L.pos_bits) < c->max_tokens)
         ++L.pos_bits;
@@ -131,7 +136,7 @@ WsLayout layout(const ngram_config *c)
             o = up(o + 8ull * 64);
         } else {
             L.stash_dy = o;
-            o = up(o + 4ull * (uint64_t)L.nk * kDim);
+            o = up(o + (uint64_t)L.dy_elt * (uint64_t)L.nk * kDim);
         }
     }
     L.total = o;
@@ -244,7 +249,7 @@ int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t, c
                                  (hipStream_t)stream));
 }
 
-int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws, const int32_t *tokens, const float *dY,
+int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY,
                           int64_t T, void *stream)
 {
     int rc = check_cfg(cfg);
@@ -349,7 +354,7 @@ int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, n
     return hip_status(launch_step(L, w, cfg->dtype, W_b, W_t, f.st[0], f.st[1], t, lr, beta2, eps, s));
 }
 
-int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *tokens, const float *dY, int64_t T,
+int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY, int64_t T,
                          void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t, int32_t t,
                          float lr, float beta2, float eps, void *stream)
 {

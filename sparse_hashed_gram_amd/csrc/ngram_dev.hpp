@@ -110,6 +110,10 @@ __device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi)
 template <int BYTES>
 struct RawWord;
 template <>
+struct RawWord<2> {
+    typedef uint16_t type;
+};
+template <>
 struct RawWord<4> {
     typedef uint32_t type;
 };
@@ -248,8 +252,8 @@ struct WsLayout {
                             // record (see the singleton split), else kNotSingle
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
-    uint64_t stash_dy;      // fp32 [nk][768] (burst, copying): the kept dY rows
-    uint64_t dy_ptrs;       // const float * [64] (burst by reference): dY of each micro-step
+    uint64_t stash_dy;      // dY dtype [nk][768] (burst, copying): the kept dY rows
+    uint64_t dy_ptrs;       // const void * [64] (burst by reference): dY of each micro-step
     uint64_t total;
 
     int64_t rows[2];
@@ -261,6 +265,7 @@ struct WsLayout {
     bool burst;             // micro-steps are kept and reduced at step time
     bool by_ref;            // ... and their dY is read where the caller keeps it
     int pos_bits;           // by_ref: dY row code = micro-step << pos_bits | position
+    int dy_elt;             // bytes per dY element: 4 (fp32) or 2 (bf16)
     int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
 };
@@ -372,20 +377,20 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
 
 // Burst: keep one micro-step (packed indices + dY rows) in the stash.
 hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp,
-                        const int32_t *tok, const float *dY, int64_t T, hipStream_t s);
+                        const int32_t *tok, const void *dY, int64_t T, hipStream_t s);
 
 // Build the sort keys of both channels (spread: hashed from `tok`, T of them;
 // burst: from every kept stash position, a device count bounded by nk), sort
 // them by row, find segments, assign window slots and reduce the signed dY
 // rows into the window.
 hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
-                         int64_t T, const float *dY, hipStream_t s);
+                         int64_t T, const void *dY, hipStream_t s);
 // The same reduction fused with the sparse step: each row's gradient of the
 // window is completed (with what the window already holds for it) and the
 // row is stepped at once; rows only the window holds are left for
 // launch_step, which skips the stepped ones.
 hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
-                              int64_t T, const float *dY, const FuseArgs &f, hipStream_t s);
+                              int64_t T, const void *dY, const FuseArgs &f, hipStream_t s);
 
 // Burst: mark the stash empty after a reduce.
 hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);

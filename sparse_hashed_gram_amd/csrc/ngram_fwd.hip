@@ -121,13 +121,15 @@ __global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashPara
 // dY rows are copied next to it (copying burst), or micro-step << pos_bits |
 // position when dY stays where the caller keeps it (burst by reference).
 // One block per 16 positions: 16 threads hash; when copying, all 256 threads
-// copy the 16 x 192 float4 of dY.
+// copy the 16 dY rows in 16-byte pieces (row_bytes = 768 x the dY element
+// size).
 constexpr int kStashTok = 16;
 template <bool BY_REF>
-__global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const float *__restrict__ dY,
+__global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const uint8_t *__restrict__ dY,
                                                     int64_t T, HashParams hp, uint32_t *__restrict__ sidx,
-                                                    uint32_t *__restrict__ spos, float *__restrict__ sdy, int64_t nk,
-                                                    int pos_bits, int accum, WsHeader *__restrict__ hdr)
+                                                    uint32_t *__restrict__ spos, uint8_t *__restrict__ sdy,
+                                                    int row_bytes, int64_t nk, int pos_bits, int accum,
+                                                    WsHeader *__restrict__ hdr)
 {
     const uint32_t base = hdr->n_stash;
     const uint32_t m = hdr->n_micro;
@@ -146,15 +148,15 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
     }
     if (!BY_REF) {
         const int ntok = (int)min<int64_t>(kStashTok, T - t0);
-        const float4 *src = reinterpret_cast<const float4 *>(dY + (size_t)t0 * kDim);
-        float4 *dst = reinterpret_cast<float4 *>(sdy + ((size_t)base + t0) * kDim);
-        for (int e = tid; e < ntok * (kDim / 4); e += 256)
-            st_global_nt<float4>((uint64_t)(dst + e), ld_global_nt<float4>((uint64_t)(src + e)));
+        const uint4 *src = reinterpret_cast<const uint4 *>(dY + (size_t)t0 * row_bytes);
+        uint4 *dst = reinterpret_cast<uint4 *>(sdy + ((size_t)base + t0) * row_bytes);
+        for (int e = tid; e < ntok * (row_bytes / 16); e += 256)
+            st_global_nt<uint4>((uint64_t)(dst + e), ld_global_nt<uint4>((uint64_t)(src + e)));
     }
 }
 
-__global__ void stash_advance_kernel(int64_t T, int64_t nk, int accum, const float *dY,
-                                     const float **__restrict__ dy_ptrs, WsHeader *__restrict__ hdr)
+__global__ void stash_advance_kernel(int64_t T, int64_t nk, int accum, const uint8_t *dY,
+                                     const uint8_t **__restrict__ dy_ptrs, WsHeader *__restrict__ hdr)
 {
     const uint32_t base = hdr->n_stash;
     const uint32_t m = hdr->n_micro;
@@ -225,7 +227,7 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
 }
 
 hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok,
-                        const float *dY, int64_t T, hipStream_t s)
+                        const void *dY, int64_t T, hipStream_t s)
 {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
@@ -233,9 +235,9 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
     if (T > 0)
         launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true> : stash_kernel<false>,
                     dim3(grid_for(T, kStashTok)), dim3(256), 0, s, tok, dY, T, hp, sidx, spos,
-                    L.by_ref ? nullptr : reinterpret_cast<float *>(ws + L.stash_dy), L.nk, L.pos_bits, L.accum, hdr);
+                    L.by_ref ? nullptr : ws + L.stash_dy, L.dy_elt * kDim, L.nk, L.pos_bits, L.accum, hdr);
     launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel, dim3(1), dim3(1), 0, s, T, L.nk, L.accum, dY,
-                L.by_ref ? reinterpret_cast<const float **>(ws + L.dy_ptrs) : nullptr, hdr);
+                L.by_ref ? reinterpret_cast<const uint8_t **>(ws + L.dy_ptrs) : nullptr, hdr);
     return hipGetLastError();
 }
 

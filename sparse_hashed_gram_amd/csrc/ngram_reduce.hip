@@ -507,8 +507,8 @@ struct RedArgs {
     const uint32_t *info[2];    // per channel: at segment heads, slot (| new << 31) or kNewHead
     const uint32_t *n_dev[2];   // per channel: device key count (null: n_host)
     uint32_t n_host;            // key count bound (grids cover it)
-    const float *dY;            // [positions][768], indexed by the row code
-    const float *const *dy_ptrs;   // burst by reference: dY of each micro-step
+    const uint8_t *dY;          // [positions][768] of the dY dtype, indexed by the row code
+    const uint8_t *const *dy_ptrs;   // burst by reference: dY of each micro-step
     int pos_bits;           // row code = micro-step << pos_bits | position (31: one dY buffer)
     float *gacc;            // [2][wrows][768]
     uint32_t *slot_rows[2];
@@ -626,13 +626,23 @@ __device__ __forceinline__ uint64_t dy_lane_base(const RedArgs &a, int lane)
     return a.dy_ptrs ? (uint64_t)a.dy_ptrs[lane] : (uint64_t)a.dY;
 }
 
+template <int DYE>
 __device__ __forceinline__ uint64_t dy_row_addr(const RedArgs &a, uint64_t lane_base, uint32_t code)
 {
     const int m = (int)(code >> a.pos_bits);   // uniform across the wavefront
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lane_base, m);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lane_base >> 32), m);
     const uint32_t pos = code & (uint32_t)((1ull << a.pos_bits) - 1u);
-    return ((uint64_t)lo | ((uint64_t)hi << 32)) + (uint64_t)pos * (kDim * 4);
+    return ((uint64_t)lo | ((uint64_t)hi << 32)) + (uint64_t)pos * (kDim * DYE);
+}
+
+// dY elements are loaded as raw bits (DYE bytes each) and widened to fp32 only
+// where they are used, so a batch's loads stay in flight together; a bf16
+// value widens exactly.
+template <int DYE>
+__device__ __forceinline__ float dy_f32(uint32_t raw)
+{
+    return DYE == 4 ? __uint_as_float(raw) : __uint_as_float(raw << 16);
 }
 
 // The chunk's per-lane values are read through readlane inside the key loop.
@@ -668,6 +678,7 @@ __device__ __forceinline__ void flush_partial(const RedArgs &a, const ChunkPlan 
 // every key it reads, the signed dY row into the window slot of that
 // position's trigram row when the singleton map names one.  Lane l holds elements l + 64 m (m = 0..11), so every load,
 // store and atomic of a row is twelve 256-byte contiguous wavefront accesses.
+template <int DYE>
 __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
@@ -701,17 +712,18 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     for (int m = 0; m < kPer; ++m)
         acc[m] = 0.f;
     for (int j = p.j0; j < p.jend; j += kRedU) {
-        float x[kRedU][kPer];
+        uint32_t x[kRedU][kPer];   // raw dY bits
         uint32_t sg[kRedU];
 #pragma unroll
         for (int u = 0; u < kRedU; ++u) {
             if (j + u < p.jend) {
                 const uint32_t v = lane_val(p.v0, p.v1, j + u);
                 sg[u] = v & 0x80000000u;
-                const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 4 * lane;
+                const uint64_t q = dy_row_addr<DYE>(a, lane_base, v & 0x7FFFFFFFu) + DYE * lane;
 #pragma unroll
                 for (int m = 0; m < kPer; ++m)
-                    x[u][m] = ld_global_nt<float>(q + m * kWave * 4);
+                    x[u][m] = DYE == 4 ? ld_global_nt<uint32_t>(q + m * kWave * 4)
+                                       : (uint32_t)ld_global_nt<uint16_t>(q + m * kWave * 2);
             }
         }
 #pragma unroll
@@ -728,7 +740,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
             const float sgn = sg[u] ? -1.f : 1.f;   // acc +- dY, one rounding
 #pragma unroll
             for (int m = 0; m < kPer; ++m)
-                acc[m] = fmaf(x[u][m], sgn, acc[m]);
+                acc[m] = fmaf(dy_f32<DYE>(x[u][m]), sgn, acc[m]);
             if (tsplit) {
                 // this position's trigram row, if a singleton: its whole sum is
                 // s_t dY, stored into a new slot or added (its one addition of
@@ -740,11 +752,11 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
                     if (tv >> 31) {
 #pragma unroll
                         for (int m = 0; m < kPer; ++m)
-                            st_global<float>(g + m * kWave * 4, ts * x[u][m]);
+                            st_global<float>(g + m * kWave * 4, ts * dy_f32<DYE>(x[u][m]));
                     } else {
 #pragma unroll
                         for (int m = 0; m < kPer; ++m)
-                            atomic_add_global(g + m * kWave * 4, ts * x[u][m]);
+                            atomic_add_global(g + m * kWave * 4, ts * dy_f32<DYE>(x[u][m]));
                     }
                 }
             }
@@ -887,7 +899,30 @@ __device__ __forceinline__ void step_one(const float4 (&g)[kQ], const WRow<ELT> 
 // key it reads, the trigram row of that key's position when tinfo marks it a
 // singleton: its gradient is s_t dY of this very row of dY.  The trigram pass
 // then only walks the keys the split kept.
-template <int ELT>
+// Four consecutive dY elements of one lane: raw bits as loaded (16 bytes of
+// fp32 or 8 bytes of bf16), widened where they are used.
+template <int DYE>
+struct DyQuad;
+template <>
+struct DyQuad<4> {
+    typedef uint4 type;
+};
+template <>
+struct DyQuad<2> {
+    typedef uint2 type;
+};
+
+__device__ __forceinline__ float4 dy_quad_f32(uint4 x)
+{
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+}
+
+__device__ __forceinline__ float4 dy_quad_f32(uint2 x)
+{
+    return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+}
+
+template <int ELT, int DYE>
 __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
@@ -932,7 +967,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
     for (int q = 0; q < kQ; ++q)
         acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = p.j0; j < p.jend; j += kStepU) {
-        float4 x[kStepU][kQ];
+        typename DyQuad<DYE>::type x[kStepU][kQ];   // raw dY bits
         uint32_t sg[kStepU];
         WRow<ELT> w[kStepU], wt[kStepU];
         RowState st[kStepU], stt[kStepU];
@@ -946,10 +981,10 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
             if (k < p.jend) {
                 const uint32_t v = lane_val(p.v0, p.v1, k);
                 sg[u] = v & 0x80000000u;
-                const uint64_t q = dy_row_addr(a, lane_base, v & 0x7FFFFFFFu) + 16 * lane;
+                const uint64_t q = dy_row_addr<DYE>(a, lane_base, v & 0x7FFFFFFFu) + 4 * DYE * lane;
 #pragma unroll
                 for (int qq = 0; qq < kQ; ++qq)
-                    x[u][qq] = ld_global_nt<float4>(q + qq * kWave * 16);
+                    x[u][qq] = ld_global_nt<typename DyQuad<DYE>::type>(q + qq * kWave * 4 * DYE);
                 ends_here[u] = k < kChunk ? ((fin >> k) & 1ull) != 0 : (p.owner_full && k == p.jend - 1);
                 if (ends_here[u]) {
                     row[u] = k < kChunk ? (uint32_t)__builtin_amdgcn_readlane((int)p.r0, k) : p.row_last;
@@ -982,17 +1017,20 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
             const float sgn = sg[u] ? -1.f : 1.f;
 #pragma unroll
             for (int q = 0; q < kQ; ++q) {
-                acc[q].x = fmaf(x[u][q].x, sgn, acc[q].x);
-                acc[q].y = fmaf(x[u][q].y, sgn, acc[q].y);
-                acc[q].z = fmaf(x[u][q].z, sgn, acc[q].z);
-                acc[q].w = fmaf(x[u][q].w, sgn, acc[q].w);
+                const float4 d = dy_quad_f32(x[u][q]);
+                acc[q].x = fmaf(d.x, sgn, acc[q].x);
+                acc[q].y = fmaf(d.y, sgn, acc[q].y);
+                acc[q].z = fmaf(d.z, sgn, acc[q].z);
+                acc[q].w = fmaf(d.w, sgn, acc[q].w);
             }
             if (tv[u] != kNotSingle) {   // the trigram singleton of this position: G = s_t dY
                 const float ts = (tv[u] & 0x80000000u) ? -1.f : 1.f;
                 float4 g[kQ];
 #pragma unroll
-                for (int q = 0; q < kQ; ++q)
-                    g[q] = make_float4(ts * x[u][q].x, ts * x[u][q].y, ts * x[u][q].z, ts * x[u][q].w);
+                for (int q = 0; q < kQ; ++q) {
+                    const float4 d = dy_quad_f32(x[u][q]);
+                    g[q] = make_float4(ts * d.x, ts * d.y, ts * d.z, ts * d.w);
+                }
                 step_one<ELT>(g, wt[u], stt[u], tv[u] & 0x7FFFFFFFu, table_t, state_t, a, lane);
             }
             if (ends_here[u]) {
@@ -1145,7 +1183,7 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 namespace {
 
 hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
-                       const float *dY, const FuseArgs *f, hipStream_t s)
+                       const void *dY, const FuseArgs *f, hipStream_t s)
 {
     // spread: T keys known on the host; burst: the stash count on the device,
     // bounded by the stash capacity (grids cover the bound, blocks past the
@@ -1225,8 +1263,8 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     ra.n_dev[1] = &hdr->n_multi;
     ra.n_host = n_host;
     ra.tinfo = sa.tinfo;
-    ra.dY = burst && !L.by_ref ? reinterpret_cast<const float *>(ws + L.stash_dy) : dY;
-    ra.dy_ptrs = L.by_ref ? reinterpret_cast<const float *const *>(ws + L.dy_ptrs) : nullptr;
+    ra.dY = burst && !L.by_ref ? ws + L.stash_dy : static_cast<const uint8_t *>(dY);
+    ra.dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t *const *>(ws + L.dy_ptrs) : nullptr;
     ra.pos_bits = L.by_ref ? L.pos_bits : 31;
     ra.gacc = reinterpret_cast<float *>(ws + L.gacc);
     ra.slot_rows[0] = sa.slot_rows[0];
@@ -1241,14 +1279,18 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
     const uint32_t per_block = kRedThreads / kWave;
     const dim3 grid((nchunk + per_block - 1) / per_block, 2);
+    const bool dy16 = L.dy_elt == 2;
     if (!f) {
-        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_reduce_kernel, grid, dim3(kRedThreads), 0, s, ra);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_reduce_kernel<2> : seg_reduce_kernel<4>, grid,
+                    dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kAccum><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else if (f->dtype == NGRAM_DTYPE_BF16) {
-        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_step_kernel<2>, grid, dim3(kRedThreads), 0, s, ra);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<2, 2> : seg_step_kernel<2, 4>, grid,
+                    dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kFuseBf16><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     } else {
-        launch_prof(NGRAM_PROF_REDUCE, true, true, seg_step_kernel<4>, grid, dim3(kRedThreads), 0, s, ra);
+        launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<4, 2> : seg_step_kernel<4, 4>, grid,
+                    dim3(kRedThreads), 0, s, ra);
         fixup_kernel<kFuseF32><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
     }
     return hipGetLastError();
@@ -1257,13 +1299,13 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
 }  // namespace
 
 hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
-                         const float *dY, hipStream_t s)
+                         const void *dY, hipStream_t s)
 {
     return reduce_impl(L, ws, hp, tok, T, dY, nullptr, s);
 }
 
 hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
-                              const float *dY, const FuseArgs &f, hipStream_t s)
+                              const void *dY, const FuseArgs &f, hipStream_t s)
 {
     return reduce_impl(L, ws, hp, tok, T, dY, &f, s);
 }

@@ -48,11 +48,17 @@ class NgramConfig(ctypes.Structure):
         ("accum_steps", ctypes.c_int32),
         ("mode", ctypes.c_int32),
         ("window_rows", ctypes.c_int64),
+        ("dy_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
     @property
     def torch_dtype(self):
         return torch.float32 if self.dtype == DTYPE_F32 else torch.bfloat16
+
+    @property
+    def dy_torch_dtype(self):
+        return torch.float32 if self.dy_dtype == DTYPE_F32 else torch.bfloat16
 
     @property
     def window_capacity(self) -> int:
@@ -63,7 +69,7 @@ class NgramConfig(ctypes.Structure):
 
 def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
            max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
-           window_rows: int = 0) -> NgramConfig:
+           window_rows: int = 0, dy_dtype: str = "f32") -> NgramConfig:
     c = NgramConfig()
     c.vocab = vocab
     c.eos_id = eos_id
@@ -75,6 +81,8 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.accum_steps = int(accum_steps)
     c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
+    c.dy_dtype = DTYPE_F32 if dy_dtype == "f32" else DTYPE_BF16
+    c.reserved = 0
     return c
 
 
@@ -241,7 +249,7 @@ def embed_bwd_accum(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: t
     if dY.shape != (T, DIM):
         raise ValueError(f"dY must be [{T}, {DIM}], got {tuple(dY.shape)}")
     _check("ngram_embed_bwd_accum", lib().ngram_embed_bwd_accum(
-        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", torch.float32),
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype),
         T, _stream()))
 
 
@@ -271,7 +279,7 @@ def embed_bwd_step(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: to
     _check_tables(cfg, W_b, W_t)
     _check_state(cfg, state_b, state_t)
     _check("ngram_embed_bwd_step", lib().ngram_embed_bwd_step(
-        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", torch.float32), T,
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), T,
         _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
         _dev(state_t, "state_t", torch.float32), int(t), float(lr), float(beta2), float(eps), _stream()))
 

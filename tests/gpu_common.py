@@ -74,8 +74,25 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def dy_dev(dy: np.ndarray, dy_dtype: str = "f32") -> torch.Tensor:
+    """dY on the device in the config's dY dtype.  For bf16 the float32
+    values must already be bf16 numbers (bf16_values), so the upload is exact
+    and the oracle sees the same gradients."""
+    t = to_dev(dy)
+    if dy_dtype == "f32":
+        return t
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.to(torch.float32), t), "dY is not made of bf16 values"
+    return b
+
+
+def bf16_values(dy: np.ndarray) -> np.ndarray:
+    """float32 array of the nearest bf16 numbers (test input preparation)."""
+    return torch.from_numpy(np.ascontiguousarray(dy)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
 def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2),
-                 sample_untouched=512, keep_rows=None, rng_seed=0, how="export"):
+                 sample_untouched=512, keep_rows=None, rng_seed=0, how="export", dy_dtype="f32"):
     """Feeds one window (lists of numpy tokens / dY) through the GPU path,
     checks the touched sets and the step against the oracle, and a sample of
     untouched rows for bitwise stability.  how:
@@ -88,7 +105,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
     last = len(toks) - 1 if how == "fused_last" else len(toks)
     keep = []   # burst by reference reads dY at step time: keep it alive
     for tok, dy in zip(toks[:last], dys[:last]):
-        keep.append(to_dev(dy))
+        keep.append(dy_dev(dy, dy_dtype))
         N.embed_bwd_accum(cfg, ws, to_dev(tok), keep[-1])
     if how == "export":
         N.window_reduce(cfg, ws)
@@ -96,7 +113,7 @@ def check_window(st: State, ws, toks, dys, t, lr, beta2, eps, dtype, seeds=(1, 2
                                 seeds, keep_rows=keep_rows)
     if how != "export":
         return _check_step_only(st, ws, toks, dys, t, lr, beta2, eps, dtype, orc, how, last,
-                                sample_untouched, rng_seed, keep)
+                                sample_untouched, rng_seed, keep, dy_dtype)
     rs = np.random.default_rng(rng_seed)
     touched_all = []
     grads = []
@@ -160,7 +177,7 @@ def window_inputs(w, first_step, T=None, n=4, tok_fn=None):
 
 
 def _check_step_only(st, ws, toks, dys, t, lr, beta2, eps, dtype, orc, how, last, sample_untouched,
-                     rng_seed, keep):
+                     rng_seed, keep, dy_dtype="f32"):
     """check_window without the exported gradient: the step's results alone."""
     N = ng()
     cfg = st.cfg
@@ -173,7 +190,7 @@ def _check_step_only(st, ws, toks, dys, t, lr, beta2, eps, dtype, orc, how, last
         snaps.append((touched, G_o, A_o, host_rows(st.W[c], touched), host_vec(st.v[c], touched),
                       host_vec(st.tl[c], touched), cand, host_rows(st.W[c], cand)))
     if how == "fused_last":
-        st.bwd_step(ws, to_dev(toks[last]), to_dev(dys[last]), t, lr, beta2, eps)
+        st.bwd_step(ws, to_dev(toks[last]), dy_dev(dys[last], dy_dtype), t, lr, beta2, eps)
     else:
         st.step(ws, t, lr, beta2, eps)
     torch.cuda.synchronize()

@@ -31,8 +31,14 @@ def test_exports_every_declared_symbol(N):
         assert hasattr(L, n), f"{n} declared in ngram.h but not exported"
 
 
+def test_config_struct_layout(N):
+    # the binding's ctypes mirror of ngram_config must match the C layout
+    assert ctypes.sizeof(N.NgramConfig) == 80
+    assert N.NgramConfig.dy_dtype.offset == 72
+
+
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 2
+    assert N.lib().ngram_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -47,7 +53,7 @@ def _good(N, **kw):
 @pytest.mark.parametrize("field,value", [
     ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
     ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
-    ("mode", 3), ("window_rows", -1)])
+    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("reserved", 1)])
 def test_config_rejects(N, field, value):
     c = _good(N)
     setattr(c, field, value)
@@ -72,8 +78,11 @@ def test_workspace_bytes_scale(N):
     assert small < 64 << 20
     # window accumulator 2 x 1,572,864 x 3 KB dominates; slot maps 2 x 338 MB
     assert 10.2e9 < full < 11.0e9
-    # burst keeps the window's dY (1,572,864 x 3 KB more)
+    # burst keeps the window's dY (1,572,864 x 3 KB more; half that for bf16 dY)
     assert burst - full > 4.8e9
+    burst16 = N.workspace_bytes(_good(N, rows=(42_300_000, 42_300_000), dtype="bf16", max_tokens=393_216,
+                                      mode="burst", dy_dtype="bf16"))
+    assert abs((burst - burst16) - 1_572_864 * 768 * 2) < 1 << 20
 
 
 def test_host_rejections_enqueue_nothing(N):

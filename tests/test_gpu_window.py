@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import helpers
-from gpu_common import State, check_window, device_table, ng, to_dev, window_inputs
+from gpu_common import State, bf16_values, check_window, device_table, ng, to_dev, window_inputs
 from sparse_hashed_gram_amd import synth, workloads
 
 pytestmark = pytest.mark.gpu
@@ -265,3 +265,65 @@ def test_step_order_flag():
         N.embed_bwd_accum(cfg, ws, to_dev(synth.tokens(w, 0, 64)), to_dev(synth.dY(w, 0, 64)))
         st.step(ws, t, 0.01, 0.95, 1e-8)
     assert N.device_status(cfg, ws, clear=True) & N.FLAG_STEP_ORDER
+
+
+@pytest.mark.parametrize("how", ["export", "step", "fused_last"])
+@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
+def test_tiny_workload_bf16_dy(mode, how):
+    # bf16 upstream gradients (the gradient of a bf16 forward output): the
+    # kernels widen each element exactly and sum in fp32, so the oracle gets
+    # the same values as float32
+    w = workloads.TINY
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode=mode,
+                   dy_dtype="bf16")
+    st = _tiny_state(cfg, w)
+    ws = N.Workspace(cfg)
+    for win in range(w.steps // w.accum_steps):
+        toks, dys = window_inputs(w, win * w.accum_steps)
+        dys = [bf16_values(d) for d in dys]
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "f32", how=how, dy_dtype="bf16")
+    assert N.device_status(cfg, ws) == 0
+
+
+@pytest.mark.parametrize("mode,how", [("spread", "fused_last"), ("burst", "step"), ("burst_ref", "step"),
+                                      ("burst_ref", "fused_last")])
+def test_shard_workload_bf16_dy(mode, how):
+    w = workloads.COLLISION
+    N = ng()
+    rows = workloads.SHARD.rows
+    T = 49_152
+    cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=T, mode=mode, dy_dtype="bf16")
+    st = State(cfg, device_table(rows[0], "bf16", 71), device_table(rows[1], "bf16", 72))
+    ws = N.Workspace(cfg)
+    for win in range(2):
+        toks, dys = window_inputs(w, 4 * win, T=T)
+        dys = [bf16_values(d) for d in dys]
+        check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "bf16", how=how, dy_dtype="bf16")
+    assert N.device_status(cfg, ws) == 0
+    del st, ws
+    torch.cuda.empty_cache()
+
+
+def test_bf16_dy_matches_f32_dy_bitwise():
+    # the same bf16-valued gradients given as fp32 or as bf16 take the same
+    # path through the same sums: the results are bitwise equal
+    w = workloads.TINY
+    N = ng()
+    outs = []
+    for dyt in ("f32", "bf16"):
+        cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode="burst_ref",
+                       dy_dtype=dyt)
+        st = _tiny_state(cfg, w)
+        ws = N.Workspace(cfg)
+        toks, dys = window_inputs(w, 0)
+        keep = [to_dev(bf16_values(d)) for d in dys]
+        if dyt == "bf16":
+            keep = [k.to(torch.bfloat16) for k in keep]
+        for tok, dy in zip(toks, keep):
+            N.embed_bwd_accum(cfg, ws, to_dev(tok), dy)
+        st.step(ws, 1, w.lr, w.beta2, w.eps)
+        torch.cuda.synchronize()
+        outs.append((st.W[0].cpu(), st.W[1].cpu(), st.st[0].cpu(), st.st[1].cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
