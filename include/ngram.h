@@ -41,9 +41,10 @@
  *     every buffer; the library never allocates, frees or synchronises in the
  *     hot calls (ngram_hash, ngram_embed_fwd, ngram_embed_bwd_accum,
  *     ngram_embed_bwd_step, ngram_window_reduce, ngram_sparse_step,
- *     ngram_window_export).  Those calls only enqueue work on `stream` (a
- *     hipStream_t; NULL = the null stream) and return; they are safe to
- *     capture in a HIP graph.
+ *     ngram_window_export and the _dev step variants).  Those calls only
+ *     enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return; they are safe to capture in a HIP graph (with the _dev step
+ *     variants, a replay can take a new step number and learning rate).
  *   - A negative return value is a host-detected error and nothing was
  *     enqueued.  NGRAM_EHIP reports a failed launch.
  *   - Faults only the device can see (token ids outside [0, vocab), more
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 3
+#define NGRAM_ABI_VERSION 4
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -97,6 +98,9 @@ extern "C" {
                                        the excess micro-step was dropped     */
 #define NGRAM_FLAG_STEP_ORDER 0x8u  /* sparse step t <= t_last of a touched
                                        row; that row decays by beta2^0       */
+#define NGRAM_FLAG_BAD_PARAMS 0x10u /* step parameters read from device
+                                       memory were out of range; that step
+                                       changed no row and emptied the window */
 
 typedef struct ngram_config {
     int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the
@@ -129,6 +133,19 @@ typedef struct ngram_row_state {
     float v;
     int32_t t_last;
 } ngram_row_state;
+
+/* Step parameters in device memory (16 bytes, 16-byte aligned), for the
+ * _dev step entry points: the kernels read them when they run, so a captured
+ * HIP graph replays with whatever the caller stored there last (the
+ * speedrun's training step is graph-captured: agentic-affairs "NanoGPT
+ * Training Record", ablation section).  Valid values as for
+ * ngram_sparse_step. */
+typedef struct ngram_step_params {
+    int32_t t;
+    float lr;
+    float beta2;
+    float eps;
+} ngram_step_params;
 
 /* Version of this ABI (NGRAM_ABI_VERSION). */
 int ngram_abi_version(void);
@@ -209,6 +226,24 @@ int ngram_embed_bwd_step(const ngram_config *cfg, void *ws,
                          void *W_b, void *W_t, ngram_row_state *state_b,
                          ngram_row_state *state_t, int32_t t, float lr,
                          float beta2, float eps, void *stream);
+
+/* ngram_sparse_step and ngram_embed_bwd_step with the step parameters
+ * (t, lr, beta2, eps) read from `params` in device memory when the kernels
+ * run, for callers that capture a window in a HIP graph and replay it with a
+ * new step number and learning rate each time.  The library cannot check
+ * device-resident values on the host: out-of-range ones set
+ * NGRAM_FLAG_BAD_PARAMS, and that step then writes no table row and no row
+ * state (the window is still emptied). */
+int ngram_sparse_step_dev(const ngram_config *cfg, void *ws, void *W_b,
+                          void *W_t, ngram_row_state *state_b,
+                          ngram_row_state *state_t,
+                          const ngram_step_params *params, void *stream);
+
+int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws,
+                             const int32_t *tokens, const void *dY, int64_t T,
+                             void *W_b, void *W_t, ngram_row_state *state_b,
+                             ngram_row_state *state_t,
+                             const ngram_step_params *params, void *stream);
 
 /* Copies the current window of one channel (0 bigram, 1 trigram) to caller
  * buffers: the first min(n, max_rows) rows (uint32, first-touch order:

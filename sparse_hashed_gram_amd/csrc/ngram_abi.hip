@@ -294,29 +294,44 @@ int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
 
 namespace {
 
-int check_step_args(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
-                    ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps)
+int check_step_ptrs(void *ws, void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t)
 {
     if (!ws || !W_b || !W_t || !state_b || !state_t)
         return NGRAM_ENULL;
     if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) ||
         !aligned(state_t, 8))
         return NGRAM_EALIGN;
+    return NGRAM_OK;
+}
+
+int check_step_scalars(int32_t t, float lr, float beta2, float eps)
+{
     if (t < 1 || !isfinite(lr) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !isfinite(eps))
         return NGRAM_EARG;
-    (void)cfg;
+    return NGRAM_OK;
+}
+
+int check_params_ptr(const ngram_step_params *params)
+{
+    if (!params)
+        return NGRAM_ENULL;
+    if (!aligned(params, 16))
+        return NGRAM_EALIGN;
     return NGRAM_OK;
 }
 
 FuseArgs fuse_args(const ngram_config *cfg, void *W_b, void *W_t, ngram_row_state *state_b,
-                   ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps)
+                   ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps,
+                   const ngram_step_params *params)
 {
+    static_assert(sizeof(ngram_step_params) == sizeof(StepParams), "step parameter layout");
     FuseArgs f;
     f.w[0] = (uint8_t *)W_b;
     f.w[1] = (uint8_t *)W_t;
     f.st[0] = reinterpret_cast<RowState *>(state_b);
     f.st[1] = reinterpret_cast<RowState *>(state_t);
     f.p = StepParams{t, lr, beta2, eps};
+    f.p_dev = reinterpret_cast<const StepParams *>(params);
     f.dtype = cfg->dtype;
     return f;
 }
@@ -330,49 +345,24 @@ int burst_step(const ngram_config *cfg, const WsLayout &L, uint8_t *w, const Fus
     if (e == hipSuccess)
         e = launch_stash_clear(L, w, s);
     if (e == hipSuccess)
-        e = launch_step(L, w, cfg->dtype, f.w[0], f.w[1], f.st[0], f.st[1], f.p.t, f.p.lr, f.p.beta2, f.p.eps, s);
+        e = launch_step(L, w, f, s);
     return hip_status(e);
 }
 
-}  // namespace
-
-int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
-                      ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps, void *stream)
+int sparse_step_impl(const ngram_config *cfg, void *ws, const FuseArgs &f, hipStream_t s)
 {
-    static_assert(sizeof(ngram_row_state) == sizeof(RowState), "row state layout");
-    int rc = check_cfg(cfg);
-    if (rc)
-        return rc;
-    if ((rc = check_step_args(cfg, ws, W_b, W_t, state_b, state_t, t, lr, beta2, eps)))
-        return rc;
     const WsLayout L = layout(cfg);
     uint8_t *w = (uint8_t *)ws;
-    hipStream_t s = (hipStream_t)stream;
-    const FuseArgs f = fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps);
     if (L.burst)
         return burst_step(cfg, L, w, f, s);
-    return hip_status(launch_step(L, w, cfg->dtype, W_b, W_t, f.st[0], f.st[1], t, lr, beta2, eps, s));
+    return hip_status(launch_step(L, w, f, s));
 }
 
-int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY, int64_t T,
-                         void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t, int32_t t,
-                         float lr, float beta2, float eps, void *stream)
+int bwd_step_impl(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY, int64_t T,
+                  const FuseArgs &f, hipStream_t s)
 {
-    int rc = check_cfg(cfg);
-    if (rc)
-        return rc;
-    if ((rc = check_tokens(cfg, tokens, T)))
-        return rc;
-    if (T > 0 && !dY)
-        return NGRAM_ENULL;
-    if (!aligned(dY, 16))
-        return NGRAM_EALIGN;
-    if ((rc = check_step_args(cfg, ws, W_b, W_t, state_b, state_t, t, lr, beta2, eps)))
-        return rc;
     const WsLayout L = layout(cfg);
     uint8_t *w = (uint8_t *)ws;
-    hipStream_t s = (hipStream_t)stream;
-    const FuseArgs f = fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps);
     const HashParams hp = hash_params(cfg);
     if (L.burst) {
         hipError_t e = launch_stash(L, w, hp, tokens, dY, T, s);
@@ -384,8 +374,79 @@ int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *token
     if (T > 0)
         e = launch_reduce_step(L, w, hp, tokens, T, dY, f, s);
     if (e == hipSuccess)
-        e = launch_step(L, w, cfg->dtype, W_b, W_t, f.st[0], f.st[1], t, lr, beta2, eps, s);
+        e = launch_step(L, w, f, s);
     return hip_status(e);
+}
+
+int check_bwd_inputs(const ngram_config *cfg, const int32_t *tokens, const void *dY, int64_t T)
+{
+    int rc = check_tokens(cfg, tokens, T);
+    if (rc)
+        return rc;
+    if (T > 0 && !dY)
+        return NGRAM_ENULL;
+    if (!aligned(dY, 16))
+        return NGRAM_EALIGN;
+    return NGRAM_OK;
+}
+
+}  // namespace
+
+int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
+                      ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps, void *stream)
+{
+    static_assert(sizeof(ngram_row_state) == sizeof(RowState), "row state layout");
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
+        return rc;
+    return sparse_step_impl(cfg, ws, fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps, nullptr),
+                            (hipStream_t)stream);
+}
+
+int ngram_sparse_step_dev(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
+                          ngram_row_state *state_t, const ngram_step_params *params, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
+        return rc;
+    return sparse_step_impl(cfg, ws, fuse_args(cfg, W_b, W_t, state_b, state_t, 0, 0.f, 0.f, 0.f, params),
+                            (hipStream_t)stream);
+}
+
+int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY, int64_t T,
+                         void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t, int32_t t,
+                         float lr, float beta2, float eps, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_bwd_inputs(cfg, tokens, dY, T)))
+        return rc;
+    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
+        return rc;
+    return bwd_step_impl(cfg, ws, tokens, dY, T,
+                         fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps, nullptr),
+                         (hipStream_t)stream);
+}
+
+int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws, const int32_t *tokens, const void *dY, int64_t T,
+                             void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t,
+                             const ngram_step_params *params, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_bwd_inputs(cfg, tokens, dY, T)))
+        return rc;
+    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
+        return rc;
+    return bwd_step_impl(cfg, ws, tokens, dY, T,
+                         fuse_args(cfg, W_b, W_t, state_b, state_t, 0, 0.f, 0.f, 0.f, params),
+                         (hipStream_t)stream);
 }
 
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, uint32_t *rows, float *G,

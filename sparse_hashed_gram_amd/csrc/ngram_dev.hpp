@@ -327,11 +327,29 @@ __device__ __forceinline__ float step_scale(float sum_g2, RowState s, const Step
     return p.lr / (sqrtf(vn) + p.eps);
 }
 
+// The step parameters a kernel uses: the call's own, or (p_dev set) those in
+// device memory, read when the kernel runs, so that a replayed HIP graph picks
+// up new values.  ok is false if device-read values are out of range (t < 1,
+// beta2 outside [0, 1), eps not positive and finite, lr not finite); the
+// kernels then write no table row and no row state.
+__device__ __forceinline__ StepParams step_params(const StepParams &p, const StepParams *p_dev, bool &ok)
+{
+    if (!p_dev) {
+        ok = true;
+        return p;
+    }
+    const StepParams q = *p_dev;
+    ok = q.t >= 1 && __builtin_isfinite(q.lr) && q.beta2 >= 0.f && q.beta2 < 1.f && q.eps > 0.f &&
+         __builtin_isfinite(q.eps);
+    return q;
+}
+
 // Tables and state the fused reduce + step writes.
 struct FuseArgs {
     uint8_t *w[2];
     RowState *st[2];
     StepParams p;
+    const StepParams *p_dev;   // if set, the parameters are read from here
     int dtype;
 };
 
@@ -395,8 +413,7 @@ hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &
 // Burst: mark the stash empty after a reduce.
 hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);
 
-hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, RowState *sb,
-                       RowState *st, int32_t t, float lr, float beta2, float eps, hipStream_t s);
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s);
 
 hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s);
 

@@ -877,7 +877,8 @@ __device__ __forceinline__ void store_stepped(const WRow<ELT> &w, const float4 (
 // wavefront), its prefetched table row w and state st.
 template <int ELT>
 __device__ __forceinline__ void step_one(const float4 (&g)[kQ], const WRow<ELT> &w, RowState st, uint32_t row,
-                                         uint64_t table, uint64_t state, const RedArgs &a, int lane)
+                                         uint64_t table, uint64_t state, const RedArgs &a, const StepParams &sp,
+                                         bool sp_ok, int lane)
 {
     float ss = 0.f;
 #pragma unroll
@@ -886,10 +887,12 @@ __device__ __forceinline__ void step_one(const float4 (&g)[kQ], const WRow<ELT> 
     ss = wave_sum(ss);
     float vn;
     bool order_bad;
-    const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
+    const float scale = step_scale(ss, st, sp, vn, order_bad);
+    if (!sp_ok)
+        return;
     store_stepped<ELT>(w, g, scale, table + (uint64_t)row * (kDim * ELT));
     if (lane == 0) {
-        st_global<RowState>(state + (uint64_t)row * sizeof(RowState), RowState{vn, a.f.p.t});
+        st_global<RowState>(state + (uint64_t)row * sizeof(RowState), RowState{vn, sp.t});
         if (order_bad)
             atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
     }
@@ -950,6 +953,8 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
     const uint64_t table_t = (uint64_t)a.f.w[1] + (uint64_t)ELT * 4 * lane;
     const uint64_t state_t = (uint64_t)a.f.st[1];
     const uint64_t gacc = (uint64_t)a.gacc + (uint64_t)c * a.wrows * (kDim * 4) + 16 * lane;
+    bool sp_ok;
+    const StepParams sp = step_params(a.f.p, a.f.p_dev, sp_ok);
 
     // keys 0..63 that end a segment stepped here (not a partial piece); an
     // owned spill-over ends at jend - 1 >= 64
@@ -1031,7 +1036,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                     const float4 d = dy_quad_f32(x[u][q]);
                     g[q] = make_float4(ts * d.x, ts * d.y, ts * d.z, ts * d.w);
                 }
-                step_one<ELT>(g, wt[u], stt[u], tv[u] & 0x7FFFFFFFu, table_t, state_t, a, lane);
+                step_one<ELT>(g, wt[u], stt[u], tv[u] & 0x7FFFFFFFu, table_t, state_t, a, sp, sp_ok, lane);
             }
             if (ends_here[u]) {
                 const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
@@ -1047,7 +1052,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
                     if (lane == 0)
                         a.slot_rows[c][info] = row[u] | kSlotStepped;
                 }
-                step_one<ELT>(g, w[u], st[u], row[u], table, state, a, lane);
+                step_one<ELT>(g, w[u], st[u], row[u], table, state, a, sp, sp_ok, lane);
             } else if (seg_ends(p, k)) {
                 flush_partial(a, p, c, chunk, ps, lane, [&](uint64_t dst) {
 #pragma unroll
@@ -1153,9 +1158,10 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
                 ss += s_ss[ww];
             const RowState st = a.f.st[c][row];
             float vn;
-            bool order_bad;
-            const float scale = step_scale(ss, st, a.f.p, vn, order_bad);
-            if (tid < kDim / 4) {
+            bool order_bad, sp_ok;
+            const StepParams sp = step_params(a.f.p, a.f.p_dev, sp_ok);
+            const float scale = step_scale(ss, st, sp, vn, order_bad);
+            if (tid < kDim / 4 && sp_ok) {
                 if (MODE == kFuseBf16) {
                     uint2 *wp = reinterpret_cast<uint2 *>(a.f.w[c] + (size_t)row * kDim * 2) + tid;
                     const uint2 x = *wp;
@@ -1168,8 +1174,8 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
                                       x.w - scale * sum.w);
                 }
             }
-            if (tid == 0) {
-                a.f.st[c][row] = RowState{vn, a.f.p.t};
+            if (tid == 0 && sp_ok) {
+                a.f.st[c][row] = RowState{vn, sp.t};
                 if (order_bad)
                     atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
             }

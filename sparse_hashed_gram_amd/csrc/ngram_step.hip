@@ -29,6 +29,7 @@ struct StepArgs {
     RowState *st[2];
     WsHeader *hdr;
     StepParams p;
+    const StepParams *p_dev;   // if set, the parameters are read from here
 };
 
 // Row state of one touched row while it is being stepped.
@@ -73,7 +74,8 @@ __device__ __forceinline__ void load_row(RowIn &r, const float *G, uint32_t slot
 }
 
 template <int ELT>
-__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W, RowState *S, int lane)
+__device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, const StepParams &sp, uint8_t *W,
+                                         RowState *S, int lane)
 {
     float ss = 0.f;
 #pragma unroll
@@ -82,7 +84,7 @@ __device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W
     ss = wave_sum(ss);
     float vn;
     bool order_bad;
-    const float scale = step_scale(ss, r.s, a.p, vn, order_bad);
+    const float scale = step_scale(ss, r.s, sp, vn, order_bad);
     if (order_bad && lane == 0)
         atomicOr(&a.hdr->flags, NGRAM_FLAG_STEP_ORDER);
 #pragma unroll
@@ -105,7 +107,7 @@ __device__ __forceinline__ void step_row(RowIn &r, const StepArgs &a, uint8_t *W
             st_global_nt<float4>(wp + q * kWave * 16, make_float4(r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]));
     }
     if (lane == 0)
-        S[r.row] = RowState{vn, a.p.t};
+        S[r.row] = RowState{vn, sp.t};
 }
 
 // Each wavefront takes 64 consecutive window slots at a time (one coalesced
@@ -125,6 +127,13 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const float *G = a.gacc + (size_t)c * a.wrows * kDim;
     uint8_t *W = a.w[c];
     RowState *S = a.st[c];
+    bool sp_ok;
+    const StepParams sp = step_params(a.p, a.p_dev, sp_ok);
+    if (!sp_ok) {
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+            atomicOr(&a.hdr->flags, NGRAM_FLAG_BAD_PARAMS);
+        return;
+    }
 
     for (uint32_t base = wid * kWave; base < n; base += nwaves * kWave) {
         const uint32_t cnt = min((uint32_t)kWave, n - base);
@@ -145,7 +154,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
 #pragma unroll
             for (int k = 0; k < kStepRows; ++k)
                 if (live[k])
-                    step_row<ELT>(r[k], a, W, S, lane);
+                    step_row<ELT>(r[k], a, sp, W, S, lane);
         }
     }
 }
@@ -181,20 +190,21 @@ __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uin
 
 }  // namespace
 
-hipError_t launch_step(const WsLayout &L, uint8_t *ws, int dtype, void *wb, void *wt, RowState *sb, RowState *st,
-                       int32_t t, float lr, float beta2, float eps, hipStream_t s)
+hipError_t launch_step(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s)
 {
     StepArgs a;
     for (int c = 0; c < 2; ++c)
         a.slot_rows[c] = reinterpret_cast<const uint32_t *>(ws + L.slot_rows[c]);
     a.gacc = reinterpret_cast<const float *>(ws + L.gacc);
     a.wrows = L.wrows;
-    a.w[0] = (uint8_t *)wb;
-    a.w[1] = (uint8_t *)wt;
-    a.st[0] = sb;
-    a.st[1] = st;
+    a.w[0] = f.w[0];
+    a.w[1] = f.w[1];
+    a.st[0] = f.st[0];
+    a.st[1] = f.st[1];
     a.hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
-    a.p = StepParams{t, lr, beta2, eps};
+    a.p = f.p;
+    a.p_dev = f.p_dev;
+    const int dtype = f.dtype;
     // about one resident wavefront per SIMD slot; each walks 64-slot blocks
     const int64_t want = (L.wrows + 255) / 256;
     const unsigned gx = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);

@@ -25,6 +25,7 @@ FLAG_BAD_TOKEN = 0x1
 FLAG_WINDOW_FULL = 0x2
 FLAG_STASH_FULL = 0x4
 FLAG_STEP_ORDER = 0x8
+FLAG_BAD_PARAMS = 0x10
 
 PROF_FWD = 0
 PROF_SORT = 1
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
             "ngram_embed_bwd_step": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, i32, ctypes.c_float,
                                       ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
+            "ngram_sparse_step_dev": ([cp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "ngram_embed_bwd_step_dev": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
             "ngram_profile_events": ([ctypes.c_int, vp, vp], ctypes.c_int),
@@ -282,6 +285,55 @@ def embed_bwd_step(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: to
         ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), T,
         _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
         _dev(state_t, "state_t", torch.float32), int(t), float(lr), float(beta2), float(eps), _stream()))
+
+
+def step_params(t: int, lr: float, beta2: float, eps: float, out: torch.Tensor | None = None,
+                device="cuda") -> torch.Tensor:
+    """Step parameters for the _dev entry points: a 16-byte device tensor
+    (int32 t, then float32 lr, beta2, eps), written in place if `out` is
+    given (an ordinary copy on the current stream)."""
+    host = torch.tensor([float(lr), float(beta2), float(eps)], dtype=torch.float32)
+    rec = torch.empty(4, dtype=torch.int32)
+    rec[0] = int(t)
+    rec[1:] = host.view(torch.int32)
+    if out is None:
+        out = torch.empty(4, dtype=torch.int32, device=device)
+    out.copy_(rec)
+    return out
+
+
+def _check_params(p: torch.Tensor):
+    if p.numel() != 4 or p.element_size() != 4 or p.data_ptr() % 16:
+        raise ValueError("step parameters must be a 16-byte aligned 4 x 32-bit device tensor")
+
+
+def sparse_step_dev(cfg: NgramConfig, ws: Workspace, W_b, W_t, state_b, state_t, params: torch.Tensor):
+    """sparse_step with (t, lr, beta2, eps) read from `params` (step_params)
+    when the kernels run."""
+    dt = cfg.torch_dtype
+    _check_tables(cfg, W_b, W_t)
+    _check_state(cfg, state_b, state_t)
+    _check_params(params)
+    _check("ngram_sparse_step_dev", lib().ngram_sparse_step_dev(
+        ctypes.byref(cfg), ws.ptr, _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt),
+        _dev(state_b, "state_b", torch.float32), _dev(state_t, "state_t", torch.float32),
+        _dev(params, "params"), _stream()))
+
+
+def embed_bwd_step_dev(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: torch.Tensor,
+                       W_b, W_t, state_b, state_t, params: torch.Tensor):
+    """embed_bwd_step with the step parameters in device memory."""
+    T = tokens.numel()
+    if dY.shape != (T, DIM):
+        raise ValueError(f"dY must be [{T}, {DIM}], got {tuple(dY.shape)}")
+    dt = cfg.torch_dtype
+    _check_tables(cfg, W_b, W_t)
+    _check_state(cfg, state_b, state_t)
+    _check_params(params)
+    _check("ngram_embed_bwd_step_dev", lib().ngram_embed_bwd_step_dev(
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), T,
+        _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
+        _dev(state_t, "state_t", torch.float32), _dev(params, "params"), _stream()))
 
 
 def window_export(cfg: NgramConfig, ws: Workspace, channel: int, with_grad: bool = True):

@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 3
+    assert N.lib().ngram_abi_version() == 4
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -110,6 +110,10 @@ def test_host_rejections_enqueue_nothing(N):
     assert L.ngram_sparse_step(cp, *ok, 1, 0.01, 0.95, 0.0, None) == -5       # eps = 0
     assert L.ngram_sparse_step(cp, *ok, 1, float("nan"), 0.95, 1e-8, None) == -5
     assert L.ngram_sparse_step(cp, *ok, 1, 0.01, 0.95, float("inf"), None) == -5
+    # device step parameters: pointer required and 16-byte aligned
+    assert L.ngram_sparse_step_dev(cp, *ok, None, None) == -1
+    assert L.ngram_sparse_step_dev(cp, *ok, ctypes.c_void_p((1 << 40) + 4), None) == -2
+    assert L.ngram_embed_bwd_step_dev(cp, fake, fake, fake, 5, *[fake] * 4, None, None) == -1
     # export arguments
     assert L.ngram_window_export(cp, fake, 2, fake, None, 10, fake, None) == -5
     assert L.ngram_window_export(cp, fake, 0, fake, None, -1, fake, None) == -4
