@@ -338,12 +338,10 @@ FuseArgs fuse_args(const ngram_config *cfg, void *W_b, void *W_t, ngram_row_stat
 
 // Burst mode: reduce the kept micro-steps fused with the step, then step the
 // rows the window held from an earlier explicit reduce (if any) and end the
-// window.
+// window (the step kernel also empties the stash).
 int burst_step(const ngram_config *cfg, const WsLayout &L, uint8_t *w, const FuseArgs &f, hipStream_t s)
 {
     hipError_t e = launch_reduce_step(L, w, hash_params(cfg), nullptr, L.nk, nullptr, f, s);
-    if (e == hipSuccess)
-        e = launch_stash_clear(L, w, s);
     if (e == hipSuccess)
         e = launch_step(L, w, f, s);
     return hip_status(e);

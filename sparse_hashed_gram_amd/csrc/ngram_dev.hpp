@@ -228,8 +228,13 @@ struct RowState {
 constexpr int kSortThreads = 256;
 constexpr int kSortItems = 8;
 constexpr int kSortTile = kSortThreads * kSortItems;
-constexpr int kRadixBits = 8;
+#ifndef NGRAM_RADIX_BITS
+#define NGRAM_RADIX_BITS 9
+#endif
+constexpr int kRadixBits = NGRAM_RADIX_BITS;   // 26-bit rows of the full table: 3 passes
 constexpr int kRadix = 1 << kRadixBits;
+constexpr int kDpt = kRadix / kSortThreads;    // digits per thread in the per-digit loops
+static_assert(kRadix % kSortThreads == 0, "digits are split evenly over the threads");
 
 // Segment-reduce chunks: one wavefront per 64 sorted keys.
 constexpr int kChunk = 64;

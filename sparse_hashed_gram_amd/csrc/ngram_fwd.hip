@@ -120,10 +120,10 @@ __global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashPara
 // stash, with each position's dY row code: the stash position itself when the
 // dY rows are copied next to it (copying burst), or micro-step << pos_bits |
 // position when dY stays where the caller keeps it (burst by reference).
-// One block per 16 positions: 16 threads hash; when copying, all 256 threads
-// copy the 16 dY rows in 16-byte pieces (row_bytes = 768 x the dY element
-// size).
-constexpr int kStashTok = 16;
+// One block per 256 positions: each thread hashes one; when copying, the
+// block then copies its 256 dY rows in 16-byte pieces (row_bytes = 768 x the
+// dY element size).  stash_advance_kernel then moves the stash forward.
+constexpr int kStashTok = 256;
 template <bool BY_REF>
 __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const uint8_t *__restrict__ dY,
                                                     int64_t T, HashParams hp, uint32_t *__restrict__ sidx,
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
         return;   // flagged by stash_advance_kernel
     const int64_t t0 = (int64_t)blockIdx.x * kStashTok;
     const int tid = threadIdx.x;
-    if (tid < kStashTok && t0 + tid < T) {
+    if (t0 + tid < T) {
         const int64_t i = t0 + tid;
         uint32_t ib, it;
         if (ngram_index(tok, i, hp, ib, it))
@@ -232,12 +232,13 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
     uint32_t *spos = reinterpret_cast<uint32_t *>(ws + L.stash_pos);
+    const uint8_t **dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t **>(ws + L.dy_ptrs) : nullptr;
     if (T > 0)
         launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true> : stash_kernel<false>,
                     dim3(grid_for(T, kStashTok)), dim3(256), 0, s, tok, dY, T, hp, sidx, spos,
                     L.by_ref ? nullptr : ws + L.stash_dy, L.dy_elt * kDim, L.nk, L.pos_bits, L.accum, hdr);
     launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel, dim3(1), dim3(1), 0, s, T, L.nk, L.accum, dY,
-                L.by_ref ? reinterpret_cast<const uint8_t **>(ws + L.dy_ptrs) : nullptr, hdr);
+                dy_ptrs, hdr);
     return hipGetLastError();
 }
 

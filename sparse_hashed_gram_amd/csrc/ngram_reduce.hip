@@ -100,8 +100,10 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
         hdr->n_owner[0] = 0;
         hdr->n_owner[1] = 0;
     }
-    h[0][tid] = 0;
-    h[1][tid] = 0;
+    for (int d = tid; d < kRadix; d += kSortThreads) {
+        h[0][d] = 0;
+        h[1][d] = 0;
+    }
     __syncthreads();
     const uint32_t base = b * kSortTile;
     bool bad = false;
@@ -128,8 +130,10 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     if (bad)
         atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
     __syncthreads();
-    hist[((size_t)0 * kRadix + tid) * nblk + b] = h[0][tid];
-    hist[((size_t)1 * kRadix + tid) * nblk + b] = h[1][tid];
+    for (int d = tid; d < kRadix; d += kSortThreads) {
+        hist[((size_t)0 * kRadix + d) * nblk + b] = h[0][d];
+        hist[((size_t)1 * kRadix + d) * nblk + b] = h[1][d];
+    }
 }
 
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
@@ -141,7 +145,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const uint32_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const uint32_t n = count_of(n_dev, n_host);
-    h[tid] = 0;
+    for (int d = tid; d < kRadix; d += kSortThreads)
+        h[d] = 0;
     __syncthreads();
     const uint32_t *k = keys + (size_t)c * nk;
     const uint32_t base = b * kSortTile;
@@ -152,7 +157,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
             atomicAdd(&h[(k[i] >> shift) & (kRadix - 1)], 1u);
     }
     __syncthreads();
-    hist[((size_t)c * kRadix + tid) * nblk + b] = h[tid];
+    for (int d = tid; d < kRadix; d += kSortThreads)
+        hist[((size_t)c * kRadix + d) * nblk + b] = h[d];
 }
 
 // Block (d, c): exclusive scan of digit d's tile counts in place, total to
@@ -209,8 +215,20 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     for (int r = tid; r < (kSortThreads / kWave) * kRadix; r += kSortThreads)
         (&s_cnt[0][0])[r] = 0;
     {
-        const uint32_t digit_base = block_excl_scan<kSortThreads>(tot[c * kRadix + tid], s_wave, nullptr);
-        s_glob[tid] = digit_base + hist[((size_t)c * kRadix + tid) * nblk + b];
+        // thread t owns digits t * kDpt .. t * kDpt + kDpt - 1
+        uint32_t v[kDpt], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kDpt; ++j) {
+            v[j] = tot[c * kRadix + tid * kDpt + j];
+            sum += v[j];
+        }
+        uint32_t run = block_excl_scan<kSortThreads>(sum, s_wave, nullptr);
+#pragma unroll
+        for (int j = 0; j < kDpt; ++j) {
+            const int d = tid * kDpt + j;
+            s_glob[d] = run + hist[((size_t)c * kRadix + d) * nblk + b];
+            run += v[j];
+        }
     }
     __syncthreads();
 
@@ -241,14 +259,28 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     }
     __syncthreads();
     {
-        uint32_t run = 0;
+        // per digit: exclusive offsets of the wavefronts' runs, then the
+        // exclusive scan of the digit totals over the tile
+        uint32_t dtot[kDpt], sum = 0;
 #pragma unroll
-        for (int ww = 0; ww < kSortThreads / kWave; ++ww) {
-            const uint32_t x = s_cnt[ww][tid];
-            s_cnt[ww][tid] = run;
-            run += x;
+        for (int j = 0; j < kDpt; ++j) {
+            const int d = tid * kDpt + j;
+            uint32_t run = 0;
+#pragma unroll
+            for (int ww = 0; ww < kSortThreads / kWave; ++ww) {
+                const uint32_t x = s_cnt[ww][d];
+                s_cnt[ww][d] = run;
+                run += x;
+            }
+            dtot[j] = run;
+            sum += run;
         }
-        s_tile[tid] = block_excl_scan<kSortThreads>(run, s_wave, nullptr);
+        uint32_t run = block_excl_scan<kSortThreads>(sum, s_wave, nullptr);
+#pragma unroll
+        for (int j = 0; j < kDpt; ++j) {
+            s_tile[tid * kDpt + j] = run;
+            run += dtot[j];
+        }
     }
     __syncthreads();
 #pragma unroll

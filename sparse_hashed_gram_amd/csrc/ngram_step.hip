@@ -129,13 +129,10 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     RowState *S = a.st[c];
     bool sp_ok;
     const StepParams sp = step_params(a.p, a.p_dev, sp_ok);
-    if (!sp_ok) {
-        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-            atomicOr(&a.hdr->flags, NGRAM_FLAG_BAD_PARAMS);
-        return;
-    }
+    if (!sp_ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        atomicOr(&a.hdr->flags, NGRAM_FLAG_BAD_PARAMS);
 
-    for (uint32_t base = wid * kWave; base < n; base += nwaves * kWave) {
+    for (uint32_t base = wid * kWave; sp_ok && base < n; base += nwaves * kWave) {
         const uint32_t cnt = min((uint32_t)kWave, n - base);
         const uint32_t my_row = lane < (int)cnt ? rows[base + lane] : 0u;
         for (uint32_t u = 0; u < cnt; u += kStepRows) {
@@ -159,6 +156,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     }
 }
 
+// Ends the window: the epoch advances, so every slot-map entry goes stale, and
+// the window's and the burst stash's counts return to 0.
 __global__ void window_clear_kernel(WsHeader *__restrict__ hdr)
 {
     hdr->epoch += 1;
@@ -166,6 +165,8 @@ __global__ void window_clear_kernel(WsHeader *__restrict__ hdr)
     hdr->n_slots[1] = 0;
     hdr->n_next[0] = 0;
     hdr->n_next[1] = 0;
+    hdr->n_stash = 0;
+    hdr->n_micro = 0;
 }
 
 __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uint32_t *__restrict__ slot_rows,
