@@ -1115,19 +1115,52 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
     const uint32_t n = count_of(a.n_dev[c], a.n_host);
     const uint32_t *R = a.rows[c];
     const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
+    bool sp_ok = true;
+    const StepParams sp = MODE == kAccum ? a.f.p : step_params(a.f.p, a.f.p_dev, sp_ok);
     for (uint32_t k = blockIdx.x; k < nown; k += gridDim.x) {
         const uint64_t rec = a.owners[(size_t)c * a.nchunk + k];
         const int64_t chunk = (int64_t)(uint32_t)rec;
         const uint32_t info = (uint32_t)(rec >> 32);
         const uint32_t row = R[chunk * kChunk + kChunk - 1];
-        int64_t m = 0;   // following chunks that start inside the segment
-        for (;;) {
-            const int64_t cc = chunk + 1 + m + tid;
+        // what the row's completion needs besides the sum, loaded first so
+        // that it arrives while the pieces are found and added: the window
+        // row (if the window holds the row), and (fused) the table row and
+        // the row's state.  Thread t < 192 owns elements 4t .. 4t+3.
+        const bool in_window = MODE == kAccum ? (info != kDropped && !(info >> 31)) : info != kNewHead;
+        const uint32_t slot = MODE == kAccum ? (info & 0x7FFFFFFFu) : info;
+        float4 gw = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint2 wb = make_uint2(0u, 0u);
+        float4 wf = make_float4(0.f, 0.f, 0.f, 0.f);
+        RowState st = RowState{0.f, 0};
+        if (tid < kDim / 4) {
+            if (in_window)
+                gw = ld_global_nt<float4>((uint64_t)(a.gacc + ((size_t)c * a.wrows + slot) * kDim) + 16 * tid);
+            if (MODE == kFuseBf16)
+                wb = ld_global_nt<uint2>((uint64_t)(a.f.w[c] + (size_t)row * kDim * 2) + 8 * tid);
+            else if (MODE == kFuseF32)
+                wf = ld_global_nt<float4>((uint64_t)(a.f.w[c] + (size_t)row * kDim * 4) + 16 * tid);
+        }
+        if (MODE != kAccum)
+            st = ld_global_nt<RowState>((uint64_t)(a.f.st[c] + row));
+        // m = following chunks that start inside the segment (rows are
+        // sorted, so they are consecutive): every wavefront probes the next
+        // 64 chunk heads; a segment longer than that is scanned by the whole
+        // block, 1024 heads at a time
+        int64_t m = 0;
+        {
+            const int64_t cc = chunk + 1 + lane;
             const bool hit = cc * kChunk < (int64_t)n && R[cc * kChunk] == row;
-            const int cnt = __syncthreads_count(hit);
-            m += cnt;
-            if (cnt < kFixThreads)
-                break;
+            m = __popcll(__ballot(hit));
+        }
+        if (m == kWave) {
+            for (;;) {
+                const int64_t cc = chunk + 1 + m + tid;
+                const bool hit = cc * kChunk < (int64_t)n && R[cc * kChunk] == row;
+                const int cnt = __syncthreads_count(hit);
+                m += cnt;
+                if (cnt < kFixThreads)
+                    break;
+            }
         }
         const int64_t np = m + 1;
         const int64_t lo = np * w / kW, hi = np * (w + 1) / kW;
@@ -1164,20 +1197,15 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 #pragma unroll
             for (int ww = 1; ww < kW; ++ww)
                 sum = add4(sum, s_part[ww][tid]);
+            if (in_window)
+                sum = add4(gw, sum);   // G = window row + this reduction's sum
         }
         if (MODE == kAccum) {
-            if (tid < kDim / 4 && info != kDropped) {
-                float4 *g = reinterpret_cast<float4 *>(a.gacc + ((size_t)c * a.wrows + (info & 0x7FFFFFFFu)) * kDim) + tid;
-                if (!(info >> 31))
-                    sum = add4(*g, sum);
-                *g = sum;
-            }
+            if (tid < kDim / 4 && info != kDropped)
+                st_global<float4>((uint64_t)(a.gacc + ((size_t)c * a.wrows + slot) * kDim) + 16 * tid, sum);
         } else {
-            // complete the row's window gradient, then step it with the block:
-            // thread t < 192 owns elements 4t .. 4t+3
-            if (tid < kDim / 4 && info != kNewHead)
-                sum = add4(reinterpret_cast<const float4 *>(a.gacc + ((size_t)c * a.wrows + info) * kDim)[tid], sum);
-            if (tid == 0 && info != kNewHead)
+            // step the row with the block
+            if (tid == 0 && in_window)
                 a.slot_rows[c][info] = row | kSlotStepped;
             float ss = tid < kDim / 4 ? sum.x * sum.x + sum.y * sum.y + sum.z * sum.z + sum.w * sum.w : 0.f;
             ss = wave_sum(ss);
@@ -1188,22 +1216,20 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 #pragma unroll
             for (int ww = 0; ww < kW; ++ww)
                 ss += s_ss[ww];
-            const RowState st = a.f.st[c][row];
             float vn;
-            bool order_bad, sp_ok;
-            const StepParams sp = step_params(a.f.p, a.f.p_dev, sp_ok);
+            bool order_bad;
             const float scale = step_scale(ss, st, sp, vn, order_bad);
             if (tid < kDim / 4 && sp_ok) {
                 if (MODE == kFuseBf16) {
-                    uint2 *wp = reinterpret_cast<uint2 *>(a.f.w[c] + (size_t)row * kDim * 2) + tid;
-                    const uint2 x = *wp;
-                    *wp = make_uint2(bf16_pack(bf16_lo(x.x) - scale * sum.x, bf16_hi(x.x) - scale * sum.y),
-                                     bf16_pack(bf16_lo(x.y) - scale * sum.z, bf16_hi(x.y) - scale * sum.w));
+                    st_global_nt<uint2>((uint64_t)(a.f.w[c] + (size_t)row * kDim * 2) + 8 * tid,
+                                        make_uint2(bf16_pack(bf16_lo(wb.x) - scale * sum.x,
+                                                             bf16_hi(wb.x) - scale * sum.y),
+                                                   bf16_pack(bf16_lo(wb.y) - scale * sum.z,
+                                                             bf16_hi(wb.y) - scale * sum.w)));
                 } else {
-                    float4 *wp = reinterpret_cast<float4 *>(a.f.w[c] + (size_t)row * kDim * 4) + tid;
-                    const float4 x = *wp;
-                    *wp = make_float4(x.x - scale * sum.x, x.y - scale * sum.y, x.z - scale * sum.z,
-                                      x.w - scale * sum.w);
+                    st_global_nt<float4>((uint64_t)(a.f.w[c] + (size_t)row * kDim * 4) + 16 * tid,
+                                         make_float4(wf.x - scale * sum.x, wf.y - scale * sum.y,
+                                                     wf.z - scale * sum.z, wf.w - scale * sum.w));
                 }
             }
             if (tid == 0 && sp_ok) {
