@@ -178,11 +178,11 @@ def src_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(group):
+def pmc_traffic(group, mode, dy_dtype):
     """HBM bytes per launch of a kernel group from a committed rocprofv3 PMC
     summary (profiles/pmc_*.md, FETCH_SIZE and WRITE_SIZE scaled by a plain
-    copy's reading), if it was taken on the kernel source as it is now;
-    else None."""
+    copy's reading), if it was taken on the same mode and dY dtype and on the
+    kernel source as it is now; else None."""
     import glob
     want = src_hash(KERNEL_SRC[group])
     for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_*.md"))):
@@ -192,7 +192,8 @@ def pmc_traffic(group):
                 if ":" in line and not line.startswith(("#", "|", "rocprofv3")):
                     k, _, v = line.partition(":")
                     kv[k.strip()] = v.strip()
-        if kv.get("kernel") == group and kv.get("source_sha256_16") == want:
+        if (kv.get("kernel") == group and kv.get("source_sha256_16") == want and kv.get("mode") == mode
+                and kv.get("dy_dtype") == dy_dtype):
             try:
                 return float(kv["hbm_bytes_per_launch"])
             except (KeyError, ValueError):
@@ -389,7 +390,7 @@ def main():
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    traffic = pmc_traffic(dom)
+    traffic = pmc_traffic(dom, args.mode, args.dy_dtype)
     achieved = abytes[dom] / (ms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
