@@ -121,7 +121,7 @@ def window_stats(torch, N, cfg, toks):
 STATE = 8     # one (v, t_last) record per row
 
 
-def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4):
+def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_passes=3):
     """Bytes each kernel group must move per window (the design doc gives the
     per-unit figures), listed per launch.
 
@@ -146,12 +146,14 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4):
     fwd = T * (3 * row_bytes + 4)
     table_state = 2 * row_bytes + 2 * STATE
     step_row = ROW_F32 + table_state + 4
-    out = {"fwd": [fwd] * A, "sort": [2 * T * 4 * 2 * 4] * A}
+    # sort: each radix pass reads and writes a (row, payload) pair per key of
+    # both channels
+    out = {"fwd": [fwd] * A, "sort": [2 * T * 16 * radix_passes] * A}
     if mode in ("burst", "burst_ref"):
         n = A * T
         copy = 2 * dy_row if mode == "burst" else 0
         out["stash"] = [T * (copy + 4 + 8 + 4)] * A
-        out["sort"] = [2 * n * 4 * 2 * 4]
+        out["sort"] = [2 * n * 16 * radix_passes]
         out["reduce"] = [(2 * n - tsingle_win) * dy_row + sum(uwin) * table_state]
         out["step"] = [0]
         return out
@@ -365,7 +367,9 @@ def main():
 
     used = [g_ for g_ in GROUPS if ev[g_]]
     timed_stats = [stats[i % nwin] for i in range(args.steps)]
-    bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path, dy_row) for s in timed_stats]
+    rbits = max(1, int(max(w.rows) - 1).bit_length())
+    passes = (rbits + 8) // 9   # the library's 9-bit radix digits
+    bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path, dy_row, passes) for s in timed_stats]
     ms_all = {g_: [a.elapsed_ms(b) for a, b, _, _ in ev[g_]] for g_ in used}
     # algorithmic bytes of each timed launch: launch m of the window's list
     # (groups with one launch per window have a one-entry list)

@@ -76,7 +76,7 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 def dy_dev(dy: np.ndarray, dy_dtype: str = "f32") -> torch.Tensor:
     """dY on the device in the config's dY dtype.  For bf16 the float32
-    values must already be bf16 numbers (bf16_values), so the upload is exact
+    values must already be bf16 numbers (round_to_bf16), so the upload is exact
     and the oracle sees the same gradients."""
     t = to_dev(dy)
     if dy_dtype == "f32":
@@ -86,7 +86,7 @@ def dy_dev(dy: np.ndarray, dy_dtype: str = "f32") -> torch.Tensor:
     return b
 
 
-def bf16_values(dy: np.ndarray) -> np.ndarray:
+def round_to_bf16(dy: np.ndarray) -> np.ndarray:
     """float32 array of the nearest bf16 numbers (test input preparation)."""
     return torch.from_numpy(np.ascontiguousarray(dy)).to(torch.bfloat16).to(torch.float32).numpy()
 

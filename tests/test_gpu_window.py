@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import helpers
-from gpu_common import State, bf16_values, check_window, device_table, ng, to_dev, window_inputs
+from gpu_common import State, round_to_bf16, check_window, device_table, ng, to_dev, window_inputs
 from sparse_hashed_gram_amd import synth, workloads
 
 pytestmark = pytest.mark.gpu
@@ -281,7 +281,7 @@ def test_tiny_workload_bf16_dy(mode, how):
     ws = N.Workspace(cfg)
     for win in range(w.steps // w.accum_steps):
         toks, dys = window_inputs(w, win * w.accum_steps)
-        dys = [bf16_values(d) for d in dys]
+        dys = [round_to_bf16(d) for d in dys]
         check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "f32", how=how, dy_dtype="bf16")
     assert N.device_status(cfg, ws) == 0
 
@@ -298,7 +298,7 @@ def test_shard_workload_bf16_dy(mode, how):
     ws = N.Workspace(cfg)
     for win in range(2):
         toks, dys = window_inputs(w, 4 * win, T=T)
-        dys = [bf16_values(d) for d in dys]
+        dys = [round_to_bf16(d) for d in dys]
         check_window(st, ws, toks, dys, win + 1, w.lr, w.beta2, w.eps, "bf16", how=how, dy_dtype="bf16")
     assert N.device_status(cfg, ws) == 0
     del st, ws
@@ -317,7 +317,7 @@ def test_bf16_dy_matches_f32_dy_bitwise():
         st = _tiny_state(cfg, w)
         ws = N.Workspace(cfg)
         toks, dys = window_inputs(w, 0)
-        keep = [to_dev(bf16_values(d)) for d in dys]
+        keep = [to_dev(round_to_bf16(d)) for d in dys]
         if dyt == "bf16":
             keep = [k.to(torch.bfloat16) for k in keep]
         for tok, dy in zip(toks, keep):
