@@ -13,7 +13,9 @@ outputs are checked on samples it computes one by one:
 - spread, copying burst and burst by reference (fused entry point) over 8
   windows = 32 steps from the same state (restoring the touched rows between
   the runs), each against the oracle and the bursts against spread on every
-  touched row.
+  touched row;
+- bf16 upstream gradients in the launch sequence bench.py --dy-dtype bf16
+  times (burst by reference, the window reduced fused with the step).
 """
 import numpy as np
 import pytest
@@ -84,20 +86,20 @@ def _oracle_grad_for(rows_all, neg_all, dys, sample):
         sel = step_of == s
         if sel.any():
             idx = torch.from_numpy(pos[sel] - s * T).cuda()
-            dY[sel] = dys[s].index_select(0, idx).cpu().numpy()
+            dY[sel] = dys[s].index_select(0, idx).float().cpu().numpy()   # bf16 widens exactly
     touched, G = oracle.window_grad(rows_all[m], neg_all[m], dY)
     _, A = oracle.window_grad(rows_all[m], np.zeros(len(pos), np.uint8), np.abs(dY))
     return touched, G, A
 
 
-def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True, fused_last=False):
+def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True, fused_last=False, dy_dtype="f32"):
     """One window through the GPU path, checked on sampled rows.  fused_last:
     the last micro-step goes through ngram_embed_bwd_step (the reduction
     fused with the step), so the window gradient is only seen through the
     step's results."""
     N = ng()
     cfg = st["cfg"]
-    dys = [_dy(s) for s in dy_seeds]
+    dys = [_dy(s) if dy_dtype == "f32" else _dy(s).to(torch.bfloat16) for s in dy_seeds]
     per = [helpers.oracle_rows(FULL, tok, FULL.rows) for tok in toks]
     out = torch.empty((T, 768), dtype=torch.bfloat16, device="cuda")
     for m, tok in enumerate(toks):
@@ -246,3 +248,21 @@ def test_spread_vs_burst_full_table(big_state):
                 upd = (b - keep[c][0].float()).abs()
                 assert bool(((a - b).abs() <= 2 * ulp + 2e-5 * upd + 1e-5).all()), (win, mode, c)
                 assert bool(((vs - vb).abs() <= 1e-3 * vb.abs() + 1e-12).all()), (win, mode, c)
+
+
+def test_full_table_bf16_dy_burst_ref(big_state):
+    N = ng()
+    cfg = N.config(FULL.vocab, FULL.eos_id, FULL.rows, "bf16", max_tokens=T, mode="burst_ref",
+                   dy_dtype="bf16")
+    ws = N.Workspace(cfg)
+    rs = np.random.default_rng(8)
+    saved = big_state["cfg"]
+    big_state["cfg"] = cfg
+    try:
+        for win in range(2):
+            toks = [synth.tokens(FULL, 80 + 4 * win + m) for m in range(4)]
+            snaps = _run_and_check_window(big_state, ws, toks, [81 + 4 * win + m for m in range(4)], rs,
+                                          check_fwd=False, fused_last=True, dy_dtype="bf16")
+            assert snaps[0]["hottest"] > 10_000
+    finally:
+        big_state["cfg"] = saved
