@@ -837,10 +837,7 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
 // costs one memory round trip, not two.
 
 constexpr int kQ = kDim / (4 * kWave);   // 3 float4 per lane
-#ifndef NGRAM_STEP_U
-#define NGRAM_STEP_U 4
-#endif
-constexpr int kStepU = NGRAM_STEP_U;     // keys per batch
+constexpr int kStepU = 2;   // keys per batch
 
 template <int ELT>
 struct WRow;
@@ -957,8 +954,11 @@ __device__ __forceinline__ float4 dy_quad_f32(uint2 x)
     return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
 }
 
+// Three wavefronts per SIMD with two keys per batch (at most 168 VGPRs, no
+// spills) keep more loads in flight per CU than two wavefronts with four keys
+// per batch: 1.3 % faster with fp32 dY, 2-4 % with bf16 dY on the full table.
 template <int ELT, int DYE>
-__global__ __launch_bounds__(kRedThreads) void seg_step_kernel(RedArgs a)
+__global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void seg_step_kernel(RedArgs a)
 {
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
