@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 4
+#define NGRAM_ABI_VERSION 5
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -101,6 +101,23 @@ extern "C" {
 #define NGRAM_FLAG_BAD_PARAMS 0x10u /* step parameters read from device
                                        memory were out of range; that step
                                        changed no row and emptied the window */
+#define NGRAM_FLAG_WINDOW_UNREADY 0x20u /* burst modes: a window reached its
+                                       reduction with keys recorded ahead
+                                       whose gradients never came, or (with
+                                       NGRAM_OPT_PRESORT) not sorted since
+                                       its last keys; the window was dropped:
+                                       no row changed                        */
+#define NGRAM_FLAG_KEYS_MISMATCH 0x40u /* burst modes: a micro-step's
+                                       gradients came with another T than
+                                       its keys recorded ahead; they were not
+                                       attached (the window is then dropped
+                                       with NGRAM_FLAG_WINDOW_UNREADY)       */
+
+/* options (ngram_config.options) */
+#define NGRAM_OPT_PRESORT 0x1  /* burst modes: the caller sorts every window
+                                  with ngram_window_sort after its last keys
+                                  and before its step, which then skips the
+                                  sort (see ngram_window_keys)              */
 
 typedef struct ngram_config {
     int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the
@@ -122,7 +139,7 @@ typedef struct ngram_config {
                             NGRAM_DTYPE_BF16 (the gradient a bf16 model
                             returns for a bf16 forward output); window sums
                             are fp32 either way                             */
-    int32_t reserved;    /* must be 0                                       */
+    int32_t options;     /* NGRAM_OPT_* bits; 0 = none                      */
 } ngram_config;
 
 /* Optimizer state of one table row (8 bytes, 8-byte aligned arrays): the
@@ -201,6 +218,32 @@ int ngram_embed_bwd_accum(const ngram_config *cfg, void *ws,
  * window accumulator now (ngram_sparse_step does this itself).  Spread mode:
  * nothing to do.  Calling it twice is harmless. */
 int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream);
+
+/* Burst modes: records the sort keys of the window's next micro-step now,
+ * from its tokens alone (a window's n-gram rows depend on its tokens, not on
+ * its gradients).  The matching ngram_embed_bwd_accum (or
+ * ngram_embed_bwd_step), the next one called for this window, then only
+ * attaches the micro-step's dY (same T, else NGRAM_FLAG_KEYS_MISMATCH).
+ * Micro-steps may be recorded ahead in any number up to accum_steps, and
+ * ngram_window_sort can then sort the window on another stream while the
+ * forwards and the model run.  A window whose recorded keys never get their
+ * gradients is dropped at its step (NGRAM_FLAG_WINDOW_UNREADY).  Order this
+ * call before the micro-step's backward (same stream, or an event wait):
+ * a backward that runs first keeps the keys itself, and the ones recorded
+ * later then belong to a further micro-step.
+ * tokens: int32 [T], the same tokens the micro-step's forward gets. */
+int ngram_window_keys(const ngram_config *cfg, void *ws, const int32_t *tokens,
+                      int64_t T, void *stream);
+
+/* Burst modes: sorts the window's keys recorded so far (by ngram_window_keys
+ * or ngram_embed_bwd_accum), finds the distinct rows and splits off the
+ * trigram rows that occur once, i.e. everything the step's fused reduction
+ * needs besides the gradients.  With NGRAM_OPT_PRESORT the step skips these
+ * kernels and requires this call after the window's last keys (else the
+ * window is dropped with NGRAM_FLAG_WINDOW_UNREADY); without the option the
+ * step sorts again.  Order it before the step on the step's stream (an event
+ * wait if it runs on another stream).  Spread mode: nothing to do. */
+int ngram_window_sort(const ngram_config *cfg, void *ws, void *stream);
 
 /* Sparse step number t >= 1 on every row the window touched, then empties the
  * window (the @classiclarryd post: optimizer step only for n-gram rows that

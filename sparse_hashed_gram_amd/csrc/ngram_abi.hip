@@ -54,7 +54,11 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->window_rows < 0)
         return NGRAM_ECONFIG;
-    if ((c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16) || c->reserved != 0)
+    if (c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16)
+        return NGRAM_ECONFIG;
+    if ((c->options & ~NGRAM_OPT_PRESORT) != 0)
+        return NGRAM_ECONFIG;
+    if ((c->options & NGRAM_OPT_PRESORT) && c->mode == NGRAM_MODE_SPREAD)
         return NGRAM_ECONFIG;
     {   // window slots must fit 30 bits (the singleton map packs new and sign bits above them)
         const int64_t window_keys = (int64_t)c->accum_steps * c->max_tokens;
@@ -131,9 +135,11 @@ WsLayout layout(const ngram_config *c)
         o = up(o + 4ull * 2 * (uint64_t)L.nk);
         L.stash_pos = o;
         o = up(o + 4ull * (uint64_t)L.nk);
+        L.mstep = o;
+        o = up(o + sizeof(MicroStep) * kMaxMicro);
         if (L.by_ref) {
             L.dy_ptrs = o;
-            o = up(o + 8ull * 64);
+            o = up(o + 8ull * kMaxMicro);
         } else {
             L.stash_dy = o;
             o = up(o + (uint64_t)L.dy_elt * (uint64_t)L.nk * kDim);
@@ -336,12 +342,15 @@ FuseArgs fuse_args(const ngram_config *cfg, void *W_b, void *W_t, ngram_row_stat
     return f;
 }
 
-// Burst mode: reduce the kept micro-steps fused with the step, then step the
-// rows the window held from an earlier explicit reduce (if any) and end the
-// window (the step kernel also empties the stash).
+// Burst mode: reduce the kept micro-steps fused with the step (sorting them
+// first unless the caller sorts each window: NGRAM_OPT_PRESORT), then step
+// the rows the window held from an earlier explicit reduce (if any) and end
+// the window (which also empties the stash).
 int burst_step(const ngram_config *cfg, const WsLayout &L, uint8_t *w, const FuseArgs &f, hipStream_t s)
 {
-    hipError_t e = launch_reduce_step(L, w, hash_params(cfg), nullptr, L.nk, nullptr, f, s);
+    hipError_t e = (cfg->options & NGRAM_OPT_PRESORT)
+                       ? launch_reduce_step_sorted(L, w, f, s)
+                       : launch_reduce_step(L, w, hash_params(cfg), nullptr, L.nk, nullptr, f, s);
     if (e == hipSuccess)
         e = launch_step(L, w, f, s);
     return hip_status(e);
@@ -445,6 +454,38 @@ int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws, const int32_t *t
     return bwd_step_impl(cfg, ws, tokens, dY, T,
                          fuse_args(cfg, W_b, W_t, state_b, state_t, 0, 0.f, 0.f, 0.f, params),
                          (hipStream_t)stream);
+}
+
+int ngram_window_keys(const ngram_config *cfg, void *ws, const int32_t *tokens, int64_t T, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if ((rc = check_tokens(cfg, tokens, T)))
+        return rc;
+    if (!ws)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    if (!L.burst)
+        return NGRAM_OK;   // spread mode reduces each micro-step with its gradients
+    return hip_status(launch_keys(L, (uint8_t *)ws, hash_params(cfg), tokens, T, (hipStream_t)stream));
+}
+
+int ngram_window_sort(const ngram_config *cfg, void *ws, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws)
+        return NGRAM_ENULL;
+    if (!aligned(ws, kAlign))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    if (!L.burst)
+        return NGRAM_OK;
+    return hip_status(launch_window_sort(L, (uint8_t *)ws, hash_params(cfg), (hipStream_t)stream));
 }
 
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, uint32_t *rows, float *G,

@@ -199,9 +199,12 @@ struct WsHeader {
     uint32_t n_owner[2];   // long-segment fix-up records of the current reduce
     uint32_t n_stash;      // burst mode: positions kept since the last reduce
     uint32_t epoch;        // window number; slot-map entries of other windows are stale
-    uint32_t n_micro;      // burst modes: micro-steps kept since the last reduce
+    uint32_t n_micro;      // burst modes: micro-steps whose gradients are attached
     uint32_t n_multi;      // fused reduction: trigram keys left after the singleton split
-    uint32_t pad[52];
+    uint32_t n_keyed;      // burst modes: micro-steps whose keys are kept (>= n_micro)
+    uint32_t sorted_n;     // burst modes: n_stash when the keys were last sorted
+    uint32_t dropped;      // the window was found unready: its step changes no row
+    uint32_t pad[49];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
@@ -217,6 +220,14 @@ struct SlotEntry {
     uint32_t epoch;
     uint32_t slot;
 };
+
+// Burst modes: where a kept micro-step's positions start in the stash, and
+// how many it has.
+struct MicroStep {
+    uint32_t base;
+    uint32_t T;
+};
+constexpr int kMaxMicro = 64;   // accum_steps is at most this
 
 // Per-row optimizer state, as the caller stores it (ngram_row_state).
 struct RowState {
@@ -259,6 +270,7 @@ struct WsLayout {
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
     uint64_t stash_dy;      // dY dtype [nk][768] (burst, copying): the kept dY rows
     uint64_t dy_ptrs;       // const void * [64] (burst by reference): dY of each micro-step
+    uint64_t mstep;         // MicroStep [64] (burst modes)
     uint64_t total;
 
     int64_t rows[2];
@@ -401,6 +413,14 @@ hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const voi
 // Burst: keep one micro-step (packed indices + dY rows) in the stash.
 hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp,
                         const int32_t *tok, const void *dY, int64_t T, hipStream_t s);
+// Burst: keep one micro-step's keys only (its gradients come later).
+hipError_t launch_keys(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                       hipStream_t s);
+// Burst: sort the kept keys for the fused reduction (keys, radix sort, heads,
+// singleton split); sets sorted_n.
+hipError_t launch_window_sort(const WsLayout &L, uint8_t *ws, const HashParams &hp, hipStream_t s);
+// Burst: the fused reduction + step of a window sorted by launch_window_sort.
+hipError_t launch_reduce_step_sorted(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s);
 
 // Build the sort keys of both channels (spread: hashed from `tok`, T of them;
 // burst: from every kept stash position, a device count bounded by nk), sort

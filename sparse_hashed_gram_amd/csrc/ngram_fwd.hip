@@ -120,24 +120,38 @@ __global__ void hash_kernel(const int32_t *__restrict__ tok, int64_t T, HashPara
 // stash, with each position's dY row code: the stash position itself when the
 // dY rows are copied next to it (copying burst), or micro-step << pos_bits |
 // position when dY stays where the caller keeps it (burst by reference).
+// A micro-step's keys may have been kept ahead (KEYS_ONLY launch, from its
+// tokens alone); its backward then only attaches the gradients: the address
+// (by reference) or a copy of the dY rows (copying burst) at the positions
+// its keys took.
 // One block per 256 positions: each thread hashes one; when copying, the
 // block then copies its 256 dY rows in 16-byte pieces (row_bytes = 768 x the
-// dY element size).  stash_advance_kernel then moves the stash forward.
+// dY element size).  stash_advance_kernel then moves the counts forward.
 constexpr int kStashTok = 256;
-template <bool BY_REF>
+template <bool BY_REF, bool KEYS_ONLY>
 __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ tok, const uint8_t *__restrict__ dY,
                                                     int64_t T, HashParams hp, uint32_t *__restrict__ sidx,
                                                     uint32_t *__restrict__ spos, uint8_t *__restrict__ sdy,
                                                     int row_bytes, int64_t nk, int pos_bits, int accum,
-                                                    WsHeader *__restrict__ hdr)
+                                                    const MicroStep *__restrict__ mstep, WsHeader *__restrict__ hdr)
 {
-    const uint32_t base = hdr->n_stash;
-    const uint32_t m = hdr->n_micro;
-    if ((int64_t)base + T > nk || (BY_REF && (int)m >= accum))
-        return;   // flagged by stash_advance_kernel
+    const uint32_t mk = hdr->n_keyed;
+    const uint32_t m = KEYS_ONLY ? mk : hdr->n_micro;
+    const bool ahead = !KEYS_ONLY && m < mk;   // keys kept ahead: attach the gradients only
+    uint32_t base;
+    if (ahead) {
+        const MicroStep ms = mstep[m];
+        if (ms.T != (uint32_t)T)
+            return;   // flagged by stash_advance_kernel
+        base = ms.base;
+    } else {
+        base = hdr->n_stash;
+        if ((int64_t)base + T > nk || (int)m >= accum)
+            return;   // flagged by stash_advance_kernel
+    }
     const int64_t t0 = (int64_t)blockIdx.x * kStashTok;
     const int tid = threadIdx.x;
-    if (t0 + tid < T) {
+    if (!ahead && t0 + tid < T) {
         const int64_t i = t0 + tid;
         uint32_t ib, it;
         if (ngram_index(tok, i, hp, ib, it))
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
         sidx[nk + base + i] = it;
         spos[base + i] = BY_REF ? (m << pos_bits) | (uint32_t)i : base + (uint32_t)i;
     }
-    if (!BY_REF) {
+    if (!BY_REF && !KEYS_ONLY) {
         const int ntok = (int)min<int64_t>(kStashTok, T - t0);
         const uint4 *src = reinterpret_cast<const uint4 *>(dY + (size_t)t0 * row_bytes);
         uint4 *dst = reinterpret_cast<uint4 *>(sdy + ((size_t)base + t0) * row_bytes);
@@ -155,25 +169,47 @@ __global__ __launch_bounds__(256) void stash_kernel(const int32_t *__restrict__ 
     }
 }
 
+// The counts after a stash_kernel launch (one thread; also the whole job
+// when T = 0).  KEYS_ONLY: the micro-step's keys are kept, its gradients are
+// still to come.
+template <bool KEYS_ONLY>
 __global__ void stash_advance_kernel(int64_t T, int64_t nk, int accum, const uint8_t *dY,
-                                     const uint8_t **__restrict__ dy_ptrs, WsHeader *__restrict__ hdr)
+                                     const uint8_t **__restrict__ dy_ptrs, MicroStep *__restrict__ mstep,
+                                     WsHeader *__restrict__ hdr)
 {
+    const uint32_t mk = hdr->n_keyed;
+    const uint32_t m = KEYS_ONLY ? mk : hdr->n_micro;
+    if (!KEYS_ONLY && m < mk) {   // attach to keys kept ahead
+        if (mstep[m].T != (uint32_t)T) {
+            atomicOr(&hdr->flags, NGRAM_FLAG_KEYS_MISMATCH);
+            return;
+        }
+        if (dy_ptrs)
+            dy_ptrs[m] = dY;
+        hdr->n_micro = m + 1;
+        return;
+    }
     const uint32_t base = hdr->n_stash;
-    const uint32_t m = hdr->n_micro;
-    if ((int64_t)base + T > nk || (dy_ptrs && (int)m >= accum)) {
+    if ((int64_t)base + T > nk || (int)m >= accum) {
         atomicOr(&hdr->flags, NGRAM_FLAG_STASH_FULL);
         return;
     }
-    if (dy_ptrs)
-        dy_ptrs[m] = dY;
+    mstep[m] = MicroStep{base, (uint32_t)T};
     hdr->n_stash = base + (uint32_t)T;
-    hdr->n_micro = m + 1;
+    hdr->n_keyed = m + 1;
+    if (!KEYS_ONLY) {
+        if (dy_ptrs)
+            dy_ptrs[m] = dY;
+        hdr->n_micro = m + 1;
+    }
 }
 
 __global__ void stash_clear_kernel(WsHeader *__restrict__ hdr)
 {
     hdr->n_stash = 0;
     hdr->n_micro = 0;
+    hdr->n_keyed = 0;
+    hdr->sorted_n = 0;
 }
 
 __global__ void flags_clear_kernel(WsHeader *__restrict__ hdr) { hdr->flags = 0; }
@@ -232,13 +268,30 @@ hipError_t launch_stash(const WsLayout &L, uint8_t *ws, const HashParams &hp, co
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
     uint32_t *spos = reinterpret_cast<uint32_t *>(ws + L.stash_pos);
+    MicroStep *mstep = reinterpret_cast<MicroStep *>(ws + L.mstep);
     const uint8_t **dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t **>(ws + L.dy_ptrs) : nullptr;
     if (T > 0)
-        launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true> : stash_kernel<false>,
+        launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true, false> : stash_kernel<false, false>,
                     dim3(grid_for(T, kStashTok)), dim3(256), 0, s, tok, dY, T, hp, sidx, spos,
-                    L.by_ref ? nullptr : ws + L.stash_dy, L.dy_elt * kDim, L.nk, L.pos_bits, L.accum, hdr);
-    launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel, dim3(1), dim3(1), 0, s, T, L.nk, L.accum, dY,
-                dy_ptrs, hdr);
+                    L.by_ref ? nullptr : ws + L.stash_dy, L.dy_elt * kDim, L.nk, L.pos_bits, L.accum, mstep, hdr);
+    launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel<false>, dim3(1), dim3(1), 0, s, T, L.nk,
+                L.accum, dY, dy_ptrs, mstep, hdr);
+    return hipGetLastError();
+}
+
+hipError_t launch_keys(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                       hipStream_t s)
+{
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.stash_idx);
+    uint32_t *spos = reinterpret_cast<uint32_t *>(ws + L.stash_pos);
+    MicroStep *mstep = reinterpret_cast<MicroStep *>(ws + L.mstep);
+    if (T > 0)
+        launch_prof(NGRAM_PROF_STASH, true, false, L.by_ref ? stash_kernel<true, true> : stash_kernel<false, true>,
+                    dim3(grid_for(T, kStashTok)), dim3(256), 0, s, tok, nullptr, T, hp, sidx, spos, nullptr,
+                    L.dy_elt * kDim, L.nk, L.pos_bits, L.accum, mstep, hdr);
+    launch_prof(NGRAM_PROF_STASH, T == 0, true, stash_advance_kernel<true>, dim3(1), dim3(1), 0, s, T, L.nk,
+                L.accum, nullptr, nullptr, mstep, hdr);
     return hipGetLastError();
 }
 

@@ -419,8 +419,10 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
     uint32_t before_tiles, all_tiles;
     block_excl_scan<kSortThreads>(part_before, s_wave, &before_tiles);
     block_excl_scan<kSortThreads>(part, s_wave, &all_tiles);
-    if (b == 0 && tid == 0)
+    if (b == 0 && tid == 0) {
         a.hdr->n_multi = all_tiles;
+        a.hdr->sorted_n = n;   // the keys this sort covered
+    }
     const uint32_t i0 = b * kSortTile + tid * kSortItems;
     const uint32_t *R = a.rows + (size_t)c * a.nk;
     const uint32_t *V = a.vals + (size_t)c * a.nk;
@@ -550,8 +552,26 @@ struct RedArgs {
     int64_t nchunk;
     WsHeader *hdr;
     const uint32_t *tinfo;  // singleton map per dY row code
+    bool burst;             // the keys are the burst stash's: check the window is ready
     FuseArgs f;             // fused modes only
 };
+
+// Burst modes: a window is reduced only if every micro-step whose keys are
+// kept has its gradients attached (else a dY row code could name gradients
+// that never came) and its keys were sorted after the last of them.
+// Otherwise the launch does nothing and flags the window (one thread).
+__device__ __forceinline__ bool window_ready(const RedArgs &a)
+{
+    if (!a.burst)
+        return true;
+    const WsHeader *h = a.hdr;
+    const bool ok = h->n_micro == h->n_keyed && h->sorted_n == h->n_stash;
+    if (!ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        atomicOr(&a.hdr->flags, NGRAM_FLAG_WINDOW_UNREADY);
+        a.hdr->dropped = 1;   // the window's step changes nothing
+    }
+    return ok;
+}
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b)
 {
@@ -717,6 +737,8 @@ __global__ __launch_bounds__(kRedThreads) void seg_reduce_kernel(RedArgs a)
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
     const uint32_t n = count_of(a.n_dev[c], a.n_host);
+    if (!window_ready(a))
+        return;
     if (chunk == 0 && lane == 0)
         a.hdr->n_slots[c] = a.hdr->n_next[c];   // the slots assign_kernel handed out
     ChunkPlan p;
@@ -964,6 +986,8 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
     const uint32_t n = count_of(a.n_dev[c], a.n_host);
+    if (!window_ready(a))
+        return;
     ChunkPlan p;
     if (!chunk_plan(a, c, chunk, n, lane, p))
         return;
@@ -1246,18 +1270,48 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 
 namespace {
 
-hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
-                       const void *dY, const FuseArgs *f, hipStream_t s)
+// The sorted arrays, the singleton split's outputs and the slot pointers of
+// one reduce.  The radix sort ping-pongs between the two key/payload buffers,
+// so after L.passes passes the sorted keys are in buffer passes % 2; the
+// other buffer is free and holds the compacted trigram keys.
+SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host, bool fused)
 {
-    // spread: T keys known on the host; burst: the stash count on the device,
-    // bounded by the stash capacity (grids cover the bound, blocks past the
-    // count exit)
+    const int cur = L.passes & 1;
+    SlotArgs sa;
+    sa.rows = reinterpret_cast<const uint32_t *>(ws + L.keys[cur]);
+    sa.vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
+    sa.nk = L.nk;
+    sa.n_dev = n_dev;
+    sa.n_host = n_host;
+    for (int c = 0; c < 2; ++c) {
+        sa.slot_map[c] = reinterpret_cast<SlotEntry *>(ws + L.slot_map[c]);
+        sa.slot_rows[c] = reinterpret_cast<uint32_t *>(ws + L.slot_rows[c]);
+    }
+    sa.seg_info = reinterpret_cast<uint32_t *>(ws + L.seg_info);
+    sa.blk = reinterpret_cast<uint32_t *>(ws + L.blk);
+    sa.nblk = (n_host + kSortTile - 1) / kSortTile;
+    sa.wrows = (uint32_t)L.wrows;
+    sa.hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    uint32_t *spare_k = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
+    uint32_t *spare_v = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
+    sa.kept = reinterpret_cast<uint32_t *>(ws + L.kept);
+    sa.fused = fused;
+    sa.tinfo = reinterpret_cast<uint32_t *>(ws + L.tinfo);
+    sa.split_rows = spare_k + L.nk;
+    sa.split_vals = spare_v + L.nk;
+    sa.split_info = spare_k;
+    return sa;
+}
+
+// Keys, radix sort, segment heads, window slots (accumulating reduce only)
+// and the singleton split.  Spread: the T keys of `tok`; burst (tok null):
+// the stash, its count on the device, bounded by n_host.
+void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, uint32_t n_host, bool fused,
+               hipStream_t s)
+{
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const bool burst = tok == nullptr;
-    const uint32_t n_host = (uint32_t)T;
     const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
-    if (n_host == 0)
-        return hipSuccess;
     const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
@@ -1282,45 +1336,29 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
                                                                     shift, hist, tot, nblk);
         cur ^= 1;
     }
-    SlotArgs sa;
-    sa.rows = reinterpret_cast<const uint32_t *>(ws + L.keys[cur]);
-    sa.vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
-    sa.nk = L.nk;
-    sa.n_dev = n_dev;
-    sa.n_host = n_host;
-    for (int c = 0; c < 2; ++c) {
-        sa.slot_map[c] = reinterpret_cast<SlotEntry *>(ws + L.slot_map[c]);
-        sa.slot_rows[c] = reinterpret_cast<uint32_t *>(ws + L.slot_rows[c]);
-    }
-    sa.seg_info = reinterpret_cast<uint32_t *>(ws + L.seg_info);
-    sa.blk = reinterpret_cast<uint32_t *>(ws + L.blk);
-    sa.nblk = nblk;
-    sa.wrows = (uint32_t)L.wrows;
-    sa.hdr = hdr;
-    // singleton split: trigram singletons go to the bigram pass; the kept
-    // trigram keys are compacted into the sort's spare buffers (free once it
-    // is done)
-    uint32_t *spare_k = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
-    uint32_t *spare_v = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
-    sa.kept = reinterpret_cast<uint32_t *>(ws + L.kept);
-    sa.fused = f != nullptr;
-    sa.tinfo = reinterpret_cast<uint32_t *>(ws + L.tinfo);
-    sa.split_rows = spare_k + L.nk;
-    sa.split_vals = spare_v + L.nk;
-    sa.split_info = spare_k;
+    const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
     mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    if (!f)   // fused: rows new to the window are stepped at once and need no slot
+    if (!fused)   // fused: rows new to the window are stepped at once and need no slot
         assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
     launch_prof(NGRAM_PROF_SORT, false, true, split_kernel, dim3(nblk), dim3(kSortThreads), 0, s, sa);
+}
 
+// The signed segment reduction of the sorted keys (accumulating, or fused
+// with the step when f is set), then the fix-up of long segments.
+hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool burst, const void *dY,
+                       const FuseArgs *f, hipStream_t s)
+{
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
+    const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
+    const SlotArgs sa = slot_args(L, ws, n_dev, n_host, f != nullptr);
     RedArgs ra;
-    const uint32_t *vals = reinterpret_cast<const uint32_t *>(ws + L.vals[cur]);
     for (int c = 0; c < 2; ++c) {
         ra.rows[c] = sa.rows + (size_t)c * L.nk;
-        ra.vals[c] = vals + (size_t)c * L.nk;
+        ra.vals[c] = sa.vals + (size_t)c * L.nk;
         ra.info[c] = sa.seg_info + (size_t)c * L.nk;
         ra.n_dev[c] = n_dev;
     }
+    // the trigram pass walks the keys the singleton split kept
     ra.rows[1] = sa.split_rows;
     ra.vals[1] = sa.split_vals;
     ra.info[1] = sa.split_info;
@@ -1338,6 +1376,7 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     ra.owners = reinterpret_cast<uint64_t *>(ws + L.owners);
     ra.nchunk = L.nchunk;
     ra.hdr = hdr;
+    ra.burst = burst;
     if (f)
         ra.f = *f;
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
@@ -1360,6 +1399,19 @@ hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, con
     return hipGetLastError();
 }
 
+hipError_t reduce_impl(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
+                       const void *dY, const FuseArgs *f, hipStream_t s)
+{
+    // spread: T keys known on the host; burst: the stash count on the device,
+    // bounded by the stash capacity (grids cover the bound, blocks past the
+    // count exit)
+    const uint32_t n_host = (uint32_t)T;
+    if (n_host == 0)
+        return hipSuccess;
+    sort_part(L, ws, hp, tok, n_host, f != nullptr, s);
+    return reduce_part(L, ws, n_host, tok == nullptr, dY, f, s);
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32_t *tok, int64_t T,
@@ -1372,6 +1424,17 @@ hipError_t launch_reduce_step(const WsLayout &L, uint8_t *ws, const HashParams &
                               const void *dY, const FuseArgs &f, hipStream_t s)
 {
     return reduce_impl(L, ws, hp, tok, T, dY, &f, s);
+}
+
+hipError_t launch_window_sort(const WsLayout &L, uint8_t *ws, const HashParams &hp, hipStream_t s)
+{
+    sort_part(L, ws, hp, nullptr, (uint32_t)L.nk, true, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_step_sorted(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s)
+{
+    return reduce_part(L, ws, (uint32_t)L.nk, true, nullptr, &f, s);
 }
 
 }  // namespace ngram

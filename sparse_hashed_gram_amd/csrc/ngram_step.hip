@@ -131,8 +131,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a)
     const StepParams sp = step_params(a.p, a.p_dev, sp_ok);
     if (!sp_ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
         atomicOr(&a.hdr->flags, NGRAM_FLAG_BAD_PARAMS);
+    const bool live_window = sp_ok && !a.hdr->dropped;
 
-    for (uint32_t base = wid * kWave; sp_ok && base < n; base += nwaves * kWave) {
+    for (uint32_t base = wid * kWave; live_window && base < n; base += nwaves * kWave) {
         const uint32_t cnt = min((uint32_t)kWave, n - base);
         const uint32_t my_row = lane < (int)cnt ? rows[base + lane] : 0u;
         for (uint32_t u = 0; u < cnt; u += kStepRows) {
@@ -167,6 +168,9 @@ __global__ void window_clear_kernel(WsHeader *__restrict__ hdr)
     hdr->n_next[1] = 0;
     hdr->n_stash = 0;
     hdr->n_micro = 0;
+    hdr->n_keyed = 0;
+    hdr->sorted_n = 0;
+    hdr->dropped = 0;
 }
 
 __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uint32_t *__restrict__ slot_rows,

@@ -19,6 +19,7 @@ DTYPE_BF16 = 1
 MODE_SPREAD = 0
 MODE_BURST = 1
 MODE_BURST_REF = 2
+OPT_PRESORT = 0x1
 _MODES = {"spread": MODE_SPREAD, "burst": MODE_BURST, "burst_ref": MODE_BURST_REF}
 
 FLAG_BAD_TOKEN = 0x1
@@ -26,6 +27,8 @@ FLAG_WINDOW_FULL = 0x2
 FLAG_STASH_FULL = 0x4
 FLAG_STEP_ORDER = 0x8
 FLAG_BAD_PARAMS = 0x10
+FLAG_WINDOW_UNREADY = 0x20
+FLAG_KEYS_MISMATCH = 0x40
 
 PROF_FWD = 0
 PROF_SORT = 1
@@ -50,7 +53,7 @@ class NgramConfig(ctypes.Structure):
         ("mode", ctypes.c_int32),
         ("window_rows", ctypes.c_int64),
         ("dy_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("options", ctypes.c_int32),
     ]
 
     @property
@@ -70,7 +73,7 @@ class NgramConfig(ctypes.Structure):
 
 def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
            max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
-           window_rows: int = 0, dy_dtype: str = "f32") -> NgramConfig:
+           window_rows: int = 0, dy_dtype: str = "f32", presort: bool = False) -> NgramConfig:
     c = NgramConfig()
     c.vocab = vocab
     c.eos_id = eos_id
@@ -83,7 +86,7 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
     c.dy_dtype = DTYPE_F32 if dy_dtype == "f32" else DTYPE_BF16
-    c.reserved = 0
+    c.options = OPT_PRESORT if presort else 0
     return c
 
 
@@ -115,6 +118,8 @@ def lib() -> ctypes.CDLL:
             "ngram_embed_fwd": ([cp, vp, vp, vp, i64, vp, vp, vp], ctypes.c_int),
             "ngram_embed_bwd_accum": ([cp, vp, vp, vp, i64, vp], ctypes.c_int),
             "ngram_window_reduce": ([cp, vp, vp], ctypes.c_int),
+            "ngram_window_keys": ([cp, vp, vp, i64, vp], ctypes.c_int),
+            "ngram_window_sort": ([cp, vp, vp], ctypes.c_int),
             "ngram_sparse_step": ([cp, vp, vp, vp, vp, vp, i32, ctypes.c_float,
                                    ctypes.c_float, ctypes.c_float, vp], ctypes.c_int),
             "ngram_embed_bwd_step": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, i32, ctypes.c_float,
@@ -254,6 +259,17 @@ def embed_bwd_accum(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY: t
     _check("ngram_embed_bwd_accum", lib().ngram_embed_bwd_accum(
         ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype),
         T, _stream()))
+
+
+def window_keys(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor):
+    """Burst modes: keep the sort keys of the window's next micro-step now."""
+    _check("ngram_window_keys", lib().ngram_window_keys(
+        ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), tokens.numel(), _stream()))
+
+
+def window_sort(cfg: NgramConfig, ws: Workspace):
+    """Burst modes: sort the window's kept keys (on the current stream)."""
+    _check("ngram_window_sort", lib().ngram_window_sort(ctypes.byref(cfg), ws.ptr, _stream()))
 
 
 def window_reduce(cfg: NgramConfig, ws: Workspace):

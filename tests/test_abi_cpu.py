@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 4
+    assert N.lib().ngram_abi_version() == 5
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -53,11 +53,17 @@ def _good(N, **kw):
 @pytest.mark.parametrize("field,value", [
     ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
     ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
-    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("reserved", 1)])
+    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("options", 2), ("options", 1)])
 def test_config_rejects(N, field, value):
     c = _good(N)
     setattr(c, field, value)
     assert N.config_check(c) == -3
+
+
+def test_presort_is_for_burst_modes(N):
+    assert N.config_check(_good(N, mode="burst_ref", presort=True)) == 0
+    assert N.config_check(_good(N, mode="burst", presort=True)) == 0
+    assert N.config_check(_good(N, mode="spread", presort=True)) == -3
 
 
 def test_config_rejects_rows(N):
