@@ -64,6 +64,12 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 4 GiB fp32 tensor 3 times (the known-size kernel that scales "
                          "rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes), then exit")
+    ap.add_argument("--schedule", default="serial", choices=["serial", "overlap"],
+                    help="burst modes: serial sorts each window inside its step; overlap keeps the "
+                         "window's keys ahead and sorts them on a second stream while the forwards run "
+                         "(ngram_window_keys / ngram_window_sort, NGRAM_OPT_PRESORT). With nothing but "
+                         "the forwards to overlap, the sort slows them about as much as it saves. Spread "
+                         "mode is always serial")
     ap.add_argument("--events-all", action="store_true",
                     help="HIP events on every launch of every kernel group (each event-carrying kernel "
                          "leaves the stream idle for a few microseconds; the default times the reduction "
@@ -283,8 +289,9 @@ def main():
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     row_bytes = ROW_BF16 if w.dtype == "bf16" else ROW_F32
     torch.cuda.set_device(0)
+    overlap = args.schedule == "overlap" and args.mode in ("burst", "burst_ref")
     cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode,
-                   dy_dtype=args.dy_dtype)
+                   dy_dtype=args.dy_dtype, presort=overlap)
     dy_row = 768 * (2 if args.dy_dtype == "bf16" else 4)
 
     W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(2)]
@@ -329,13 +336,30 @@ def main():
             N.profile_events(k, None, None)
 
     fused_last = args.path == "fused" and not burst
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
 
     def run_window(k, ev=None, win=0):
         t_step[0] += 1
+        if overlap:
+            # the window's keys depend on its tokens only: keep them and sort
+            # them on the side stream while the forwards run on the main one
+            keys_done, sort_done = torch.cuda.Event(), torch.cuda.Event()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                for m in range(A):
+                    N.window_keys(cfg, ws, toks[k][m])
+                keys_done.record(side)
+                arm(ev, ("sort",), win, 0)
+                N.window_sort(cfg, ws)
+                disarm()
+                sort_done.record(side)
         for m in range(A):
             arm(ev, ("fwd",), win, m)
             N.embed_fwd(cfg, W[0], W[1], toks[k][m], out=out)
             disarm()
+            if overlap and m == 0:
+                main.wait_event(keys_done)   # the backward only attaches dY to the kept keys
             if fused_last and m == A - 1:
                 arm(ev, ("sort", "reduce", "step"), win, m)
                 N.embed_bwd_step(cfg, ws, toks[k][m], dys[m], W[0], W[1], state[0], state[1], t_step[0],
@@ -345,7 +369,10 @@ def main():
             arm(ev, ("stash",) if burst else ("sort", "reduce"), win, m)
             N.embed_bwd_accum(cfg, ws, toks[k][m], dys[m])
             disarm()
-        arm(ev, ("sort", "reduce", "step") if burst else ("step",), win, 0 if burst else A)
+        if overlap:
+            main.wait_event(sort_done)
+        arm(ev, ("reduce", "step") if overlap else ("sort", "reduce", "step") if burst else ("step",), win,
+            0 if burst else A)
         N.sparse_step(cfg, ws, W[0], W[1], state[0], state[1], t_step[0], w.lr, w.beta2, w.eps)
         disarm()
 
@@ -416,6 +443,7 @@ def main():
         "config": {"workload": w.name, "table_rows": w.rows[0] + w.rows[1], "dim": 768,
                    "table_dtype": w.dtype, "tokens_per_micro_step": T, "accum_steps": A,
                    "mode": args.mode, "path": args.path, "dy_dtype": args.dy_dtype,
+                   "schedule": "overlap" if overlap else "serial",
                    "global_batch": A * T},
         "fwd_tokens_per_s": round(T / (ms["fwd"] * 1e-3), 1),
         # rows stepped per second of the kernels that step them (the step, plus
