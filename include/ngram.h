@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 5
+#define NGRAM_ABI_VERSION 6
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -118,6 +118,9 @@ extern "C" {
                                   with ngram_window_sort after its last keys
                                   and before its step, which then skips the
                                   sort (see ngram_window_keys)              */
+#define NGRAM_OPT_OUT_F32 0x2  /* the forward writes fp32 whatever the table
+                                  dtype: the exact fp32 sum of the two
+                                  signed rows, not rounded to bf16          */
 
 typedef struct ngram_config {
     int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the
@@ -195,7 +198,8 @@ int ngram_hash(const ngram_config *cfg, const int32_t *tokens, int64_t T,
 
 /* Forward of one micro-step: out[i] = s_b W_b[r_b(i)] + s_t W_t[r_t(i)]
  * (same passages as ngram_hash).  W_b, W_t: [rows[c]][768] of cfg->dtype.
- * out: [T][768] of cfg->dtype; must not overlap the tables.  ws may be NULL
+ * out: [T][768] of cfg->dtype, or fp32 with NGRAM_OPT_OUT_F32; must not
+ * overlap the tables.  ws may be NULL
  * (bad token ids then go unreported; their rows are still valid rows). */
 int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t,
                     const int32_t *tokens, int64_t T, void *out, void *ws,

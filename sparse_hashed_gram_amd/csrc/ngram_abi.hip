@@ -56,7 +56,7 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16)
         return NGRAM_ECONFIG;
-    if ((c->options & ~NGRAM_OPT_PRESORT) != 0)
+    if ((c->options & ~(NGRAM_OPT_PRESORT | NGRAM_OPT_OUT_F32)) != 0)
         return NGRAM_ECONFIG;
     if ((c->options & NGRAM_OPT_PRESORT) && c->mode == NGRAM_MODE_SPREAD)
         return NGRAM_ECONFIG;
@@ -251,7 +251,8 @@ int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t, c
         return NGRAM_ENULL;
     if (!aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(out, 16) || !aligned(ws, kAlign))
         return NGRAM_EALIGN;
-    return hip_status(launch_fwd(cfg->dtype, hash_params(cfg), W_b, W_t, tokens, T, out, flags_of(ws),
+    return hip_status(launch_fwd(cfg->dtype, (cfg->options & NGRAM_OPT_OUT_F32) != 0, hash_params(cfg), W_b, W_t,
+                                 tokens, T, out, flags_of(ws),
                                  (hipStream_t)stream));
 }
 

@@ -407,7 +407,7 @@ inline void launch_prof(int group, bool first, bool last, void (*kernel)(KArgs..
 hipError_t launch_init(const WsLayout &L, uint8_t *ws, hipStream_t s);
 hipError_t launch_hash(const HashParams &hp, const int32_t *tok, int64_t T, uint32_t *idx,
                        uint32_t *flags, hipStream_t s);
-hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const void *wt,
+hipError_t launch_fwd(int dtype, bool out_f32, const HashParams &hp, const void *wb, const void *wt,
                       const int32_t *tok, int64_t T, void *out, uint32_t *flags, hipStream_t s);
 
 // Burst: keep one micro-step (packed indices + dY rows) in the stash.

@@ -45,7 +45,23 @@ __device__ __forceinline__ uint4 flip(uint4 a, uint32_t m)
     return make_uint4(a.x ^ m, a.y ^ m, a.z ^ m, a.w ^ m);
 }
 
-template <int ELT>
+// The exact fp32 sum of two signed bf16 quads, as two float quads (the
+// forward's fp32 output of a bf16 table: the sum, not rounded again).
+__device__ __forceinline__ void add_bf16x8_f32(uint4 a, uint4 b, uint4 &lo, uint4 &hi)
+{
+    lo.x = __float_as_uint(bf16_lo(a.x) + bf16_lo(b.x));
+    lo.y = __float_as_uint(bf16_hi(a.x) + bf16_hi(b.x));
+    lo.z = __float_as_uint(bf16_lo(a.y) + bf16_lo(b.y));
+    lo.w = __float_as_uint(bf16_hi(a.y) + bf16_hi(b.y));
+    hi.x = __float_as_uint(bf16_lo(a.z) + bf16_lo(b.z));
+    hi.y = __float_as_uint(bf16_hi(a.z) + bf16_hi(b.z));
+    hi.z = __float_as_uint(bf16_lo(a.w) + bf16_lo(b.w));
+    hi.w = __float_as_uint(bf16_hi(a.w) + bf16_hi(b.w));
+}
+
+// ELT: table element bytes; OUT_F32: fp32 output for a bf16 table (else the
+// output has the table's dtype).
+template <int ELT, bool OUT_F32 = false>
 __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restrict__ tok, int64_t T,
                                                           HashParams hp,
                                                           const uint8_t *__restrict__ wb,
@@ -75,7 +91,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restr
     }
     __syncthreads();
     const int ntok = (int)min<int64_t>(kFwdTok, T - t0);
-    uint4 *orow = reinterpret_cast<uint4 *>(out + (size_t)t0 * kRowBytes);
+    constexpr int kOutRowBytes = OUT_F32 ? kDim * 4 : kRowBytes;
+    uint4 *orow = reinterpret_cast<uint4 *>(out + (size_t)t0 * kOutRowBytes);
 
 #pragma unroll
     for (int g = 0; g < kIter; g += kU) {
@@ -97,8 +114,20 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restr
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int lt = e[u] / kCpr;
-            if (lt < ntok)   // output rows are written once: streaming stores
-                st_global_nt<uint4>((uint64_t)(orow + e[u]), ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]));
+            if (lt < ntok) {   // output rows are written once: streaming stores
+                if constexpr (OUT_F32 && ELT == 2) {
+                    // chunk c of a bf16 row holds elements 8c..8c+7: fp32 pieces 2c, 2c+1
+                    uint4 lo, hi;
+                    add_bf16x8_f32(a[u], b[u], lo, hi);
+                    const int c = e[u] - lt * kCpr;
+                    uint4 *o = orow + (size_t)lt * (kOutRowBytes / 16) + 2 * c;
+                    st_global_nt<uint4>((uint64_t)o, lo);
+                    st_global_nt<uint4>((uint64_t)(o + 1), hi);
+                } else {
+                    st_global_nt<uint4>((uint64_t)(orow + e[u]),
+                                        ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]));
+                }
+            }
         }
     }
 }
@@ -251,13 +280,14 @@ hipError_t launch_hash(const HashParams &hp, const int32_t *tok, int64_t T, uint
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(int dtype, const HashParams &hp, const void *wb, const void *wt,
+hipError_t launch_fwd(int dtype, bool out_f32, const HashParams &hp, const void *wb, const void *wt,
                       const int32_t *tok, int64_t T, void *out, uint32_t *flags, hipStream_t s)
 {
     if (T == 0)
         return hipSuccess;
     const unsigned g = grid_for(T, kFwdTok);
-    launch_prof(NGRAM_PROF_FWD, true, true, dtype == NGRAM_DTYPE_BF16 ? fwd_kernel<2> : fwd_kernel<4>, dim3(g),
+    launch_prof(NGRAM_PROF_FWD, true, true,
+                dtype == NGRAM_DTYPE_BF16 ? (out_f32 ? fwd_kernel<2, true> : fwd_kernel<2>) : fwd_kernel<4>, dim3(g),
                 dim3(kFwdThreads), 0, s, tok, T, hp, wb, wt, out, flags);
     return hipGetLastError();
 }

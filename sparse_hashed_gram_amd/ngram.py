@@ -20,6 +20,7 @@ MODE_SPREAD = 0
 MODE_BURST = 1
 MODE_BURST_REF = 2
 OPT_PRESORT = 0x1
+OPT_OUT_F32 = 0x2
 _MODES = {"spread": MODE_SPREAD, "burst": MODE_BURST, "burst_ref": MODE_BURST_REF}
 
 FLAG_BAD_TOKEN = 0x1
@@ -61,6 +62,10 @@ class NgramConfig(ctypes.Structure):
         return torch.float32 if self.dtype == DTYPE_F32 else torch.bfloat16
 
     @property
+    def out_torch_dtype(self):
+        return torch.float32 if (self.dtype == DTYPE_F32 or self.options & OPT_OUT_F32) else torch.bfloat16
+
+    @property
     def dy_torch_dtype(self):
         return torch.float32 if self.dy_dtype == DTYPE_F32 else torch.bfloat16
 
@@ -73,7 +78,8 @@ class NgramConfig(ctypes.Structure):
 
 def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
            max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
-           window_rows: int = 0, dy_dtype: str = "f32", presort: bool = False) -> NgramConfig:
+           window_rows: int = 0, dy_dtype: str = "f32", presort: bool = False,
+           out_f32: bool = False) -> NgramConfig:
     c = NgramConfig()
     c.vocab = vocab
     c.eos_id = eos_id
@@ -86,7 +92,7 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
     c.dy_dtype = DTYPE_F32 if dy_dtype == "f32" else DTYPE_BF16
-    c.options = OPT_PRESORT if presort else 0
+    c.options = (OPT_PRESORT if presort else 0) | (OPT_OUT_F32 if out_f32 else 0)
     return c
 
 
@@ -242,12 +248,12 @@ def embed_fwd(cfg: NgramConfig, W_b: torch.Tensor, W_t: torch.Tensor, tokens: to
     T = tokens.numel()
     _check_tables(cfg, W_b, W_t)
     if out is None:
-        out = torch.empty((T, DIM), dtype=cfg.torch_dtype, device=tokens.device)
+        out = torch.empty((T, DIM), dtype=cfg.out_torch_dtype, device=tokens.device)
     if tuple(out.shape) != (T, DIM):
         raise ValueError(f"out must be [{T}, {DIM}]")
     _check("ngram_embed_fwd", lib().ngram_embed_fwd(
         ctypes.byref(cfg), _dev(W_b, "W_b", cfg.torch_dtype), _dev(W_t, "W_t", cfg.torch_dtype),
-        _dev(tokens, "tokens", torch.int32), T, _dev(out, "out", cfg.torch_dtype), _ws(ws), _stream()))
+        _dev(tokens, "tokens", torch.int32), T, _dev(out, "out", cfg.out_torch_dtype), _ws(ws), _stream()))
     return out
 
 

@@ -136,3 +136,27 @@ def test_forward_empty_is_noop():
     Wt = torch.zeros((w.rows[1], 768), device="cuda")
     out = N.embed_fwd(cfg, Wb, Wt, torch.zeros(0, dtype=torch.int32, device="cuda"))
     assert out.shape == (0, 768)
+
+
+@pytest.mark.parametrize("T", [1, 65, 4097, 49_152])
+def test_forward_shard_bf16_table_fp32_output(T):
+    # NGRAM_OPT_OUT_F32: the exact fp32 sum of the two signed bf16 rows, not
+    # rounded again; its bf16 rounding is the default output
+    w = workloads.SHARD
+    N = ng()
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=w.tokens_per_step, out_f32=True)
+    cfg16 = N.config(w.vocab, w.eos_id, w.rows, "bf16", max_tokens=w.tokens_per_step)
+    Wb = device_table(w.rows[0], "bf16", 13)
+    Wt = device_table(w.rows[1], "bf16", 14)
+    tok = synth.tokens(w, 4)[:T]
+    out = N.embed_fwd(cfg, Wb, Wt, to_dev(tok))
+    assert out.dtype == torch.float32
+    out16 = N.embed_fwd(cfg16, Wb, Wt, to_dev(tok))
+    assert torch.equal(out.to(torch.bfloat16), out16)
+    rb, nb, rt, nt = helpers.oracle_rows(w, tok, w.rows)
+    ib, it = np.unique(rb), np.unique(rt)
+    ref = oracle.forward(host_rows(Wb, ib), host_rows(Wt, it), rb, nb, rt, nt, ids_b=ib, ids_t=it,
+                         out_dtype="f32")
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    del Wb, Wt
+    torch.cuda.empty_cache()
