@@ -40,20 +40,25 @@
  *   - All pointers are device pointers unless marked "host".  The caller owns
  *     every buffer; the library never allocates, frees or synchronises in the
  *     hot calls (ngram_hash, ngram_embed_fwd, ngram_embed_bwd_accum,
- *     ngram_embed_bwd_step, ngram_window_reduce, ngram_sparse_step,
- *     ngram_window_export and the _dev step variants).  Those calls only
- *     enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
- *     return; they are safe to capture in a HIP graph (with the _dev step
- *     variants, a replay can take a new step number and learning rate).
+ *     ngram_embed_bwd_step, ngram_window_keys, ngram_window_sort,
+ *     ngram_window_reduce, ngram_sparse_step, ngram_window_export and the
+ *     _dev step variants).  Those calls only enqueue work on `stream` (a
+ *     hipStream_t; NULL = the null stream) and return; they are safe to
+ *     capture in a HIP graph (with the _dev step variants, a replay can take
+ *     a new step number and learning rate).
  *   - A negative return value is a host-detected error and nothing was
  *     enqueued.  NGRAM_EHIP reports a failed launch.
  *   - Faults only the device can see (token ids outside [0, vocab), more
- *     distinct rows than the window holds, step numbers that do not increase)
- *     set sticky bits in the workspace, read with ngram_device_status.
+ *     distinct rows than the window holds, a full burst stash, step numbers
+ *     that do not increase, out-of-range device step parameters, burst
+ *     windows not ready for their step) set sticky NGRAM_FLAG_* bits in the
+ *     workspace, read with ngram_device_status.
  *   - Tables and row-major activations are [rows][dim] with dim = 768; all
  *     row bases must be 16-byte aligned.  Row counts must be below 2^31.
- *   - One workspace serves one table pair and one stream at a time; distinct
- *     workspaces are independent (the library keeps no global state).
+ *   - One workspace serves one table pair; the calls on it must be ordered
+ *     (one stream, or event waits where ngram_window_keys / ngram_window_sort
+ *     run on another).  Distinct workspaces are independent (the library
+ *     keeps no global state).
  */
 #ifndef NGRAM_H
 #define NGRAM_H
