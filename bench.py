@@ -45,8 +45,8 @@ KERNEL_SRC = {"fwd": "ngram_fwd.hip", "sort": "ngram_reduce.hip", "reduce": "ngr
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=16, help="timed windows")
-    ap.add_argument("--warmup", type=int, default=2, help="untimed windows")
+    ap.add_argument("--steps", type=int, default=20, help="timed windows")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed windows")
     ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
     ap.add_argument("--mode", default="burst_ref", choices=["spread", "burst", "burst_ref"],
                     help="spread: each micro-step reduced into the window at once; burst: micro-steps "
@@ -417,7 +417,10 @@ def main():
     kernels = {}
     for g_ in used:
         gbps = abytes[g_] / (ms[g_] * 1e-3) / 1e9
-        kernels[g_] = {"ms_per_launch": round(ms[g_], 4), "launches_per_step": per_step[g_],
+        q1, med, q3 = (float(x) for x in np.percentile(ms_all[g_], [25, 50, 75]))
+        kernels[g_] = {"ms_per_launch": round(ms[g_], 4), "ms_median": round(med, 4),
+                       "ms_iqr": round(q3 - q1, 4), "timed_launches": len(ms_all[g_]),
+                       "launches_per_step": per_step[g_],
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
