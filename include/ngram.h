@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 6
+#define NGRAM_ABI_VERSION 7
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -126,6 +126,15 @@ extern "C" {
 #define NGRAM_OPT_OUT_F32 0x2  /* the forward writes fp32 whatever the table
                                   dtype: the exact fp32 sum of the two
                                   signed rows, not rounded to bf16          */
+#define NGRAM_OPT_DIRECT 0x4   /* one table indexed by the token id itself
+                                  (value embeddings, updated on the same
+                                  4-step cadence: @classiclarryd post): row
+                                  = id, sign +1, no hashing, no context;
+                                  rows[0] >= vocab; rows[1], W_t and
+                                  state_t are not used (W_t and state_t may
+                                  be NULL).  The forward is out[i] =
+                                  W_b[t[i]]; an id outside [0, vocab) is
+                                  flagged and reads row 0                   */
 
 typedef struct ngram_config {
     int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the

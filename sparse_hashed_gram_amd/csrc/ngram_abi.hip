@@ -56,8 +56,10 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16)
         return NGRAM_ECONFIG;
-    if ((c->options & ~(NGRAM_OPT_PRESORT | NGRAM_OPT_OUT_F32)) != 0)
+    if ((c->options & ~(NGRAM_OPT_PRESORT | NGRAM_OPT_OUT_F32 | NGRAM_OPT_DIRECT)) != 0)
         return NGRAM_ECONFIG;
+    if ((c->options & NGRAM_OPT_DIRECT) && c->rows[0] < c->vocab)
+        return NGRAM_ECONFIG;   // every token id needs its row
     if ((c->options & NGRAM_OPT_PRESORT) && c->mode == NGRAM_MODE_SPREAD)
         return NGRAM_ECONFIG;
     {   // window slots must fit 30 bits (the singleton map packs new and sign bits above them)
@@ -77,6 +79,7 @@ WsLayout layout(const ngram_config *c)
     L.burst = c->mode != NGRAM_MODE_SPREAD;
     L.by_ref = c->mode == NGRAM_MODE_BURST_REF;
     L.accum = c->accum_steps;
+    L.nch = (c->options & NGRAM_OPT_DIRECT) ? 1 : 2;
     L.dy_elt = c->dy_dtype == NGRAM_DTYPE_BF16 ? 2 : 4;
     L.pos_bits = 0;
     while ((int64_t(1) << L.pos_bits) < c->max_tokens)
@@ -158,6 +161,7 @@ HashParams hash_params(const ngram_config *c)
     hp.rows[1] = (uint32_t)c->rows[1];
     hp.seed[0] = c->seed[0];
     hp.seed[1] = c->seed[1];
+    hp.direct = (c->options & NGRAM_OPT_DIRECT) ? 1u : 0u;
     return hp;
 }
 
@@ -247,7 +251,8 @@ int ngram_embed_fwd(const ngram_config *cfg, const void *W_b, const void *W_t, c
         return rc;
     if ((rc = check_tokens(cfg, tokens, T)))
         return rc;
-    if (!W_b || !W_t || (T > 0 && !out))
+    const bool direct = (cfg->options & NGRAM_OPT_DIRECT) != 0;   // W_t is not used then
+    if (!W_b || (!W_t && !direct) || (T > 0 && !out))
         return NGRAM_ENULL;
     if (!aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(out, 16) || !aligned(ws, kAlign))
         return NGRAM_EALIGN;
@@ -301,9 +306,11 @@ int ngram_window_reduce(const ngram_config *cfg, void *ws, void *stream)
 
 namespace {
 
-int check_step_ptrs(void *ws, void *W_b, void *W_t, ngram_row_state *state_b, ngram_row_state *state_t)
+int check_step_ptrs(const ngram_config *cfg, void *ws, void *W_b, void *W_t, ngram_row_state *state_b,
+                    ngram_row_state *state_t)
 {
-    if (!ws || !W_b || !W_t || !state_b || !state_t)
+    const bool direct = (cfg->options & NGRAM_OPT_DIRECT) != 0;   // the second table is not used then
+    if (!ws || !W_b || !state_b || (!direct && (!W_t || !state_t)))
         return NGRAM_ENULL;
     if (!aligned(ws, kAlign) || !aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) ||
         !aligned(state_t, 8))
@@ -407,7 +414,7 @@ int ngram_sparse_step(const ngram_config *cfg, void *ws, void *W_b, void *W_t, n
     int rc = check_cfg(cfg);
     if (rc)
         return rc;
-    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
+    if ((rc = check_step_ptrs(cfg, ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
         return rc;
     return sparse_step_impl(cfg, ws, fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps, nullptr),
                             (hipStream_t)stream);
@@ -419,7 +426,7 @@ int ngram_sparse_step_dev(const ngram_config *cfg, void *ws, void *W_b, void *W_
     int rc = check_cfg(cfg);
     if (rc)
         return rc;
-    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
+    if ((rc = check_step_ptrs(cfg, ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
         return rc;
     return sparse_step_impl(cfg, ws, fuse_args(cfg, W_b, W_t, state_b, state_t, 0, 0.f, 0.f, 0.f, params),
                             (hipStream_t)stream);
@@ -434,7 +441,7 @@ int ngram_embed_bwd_step(const ngram_config *cfg, void *ws, const int32_t *token
         return rc;
     if ((rc = check_bwd_inputs(cfg, tokens, dY, T)))
         return rc;
-    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
+    if ((rc = check_step_ptrs(cfg, ws, W_b, W_t, state_b, state_t)) || (rc = check_step_scalars(t, lr, beta2, eps)))
         return rc;
     return bwd_step_impl(cfg, ws, tokens, dY, T,
                          fuse_args(cfg, W_b, W_t, state_b, state_t, t, lr, beta2, eps, nullptr),
@@ -450,7 +457,7 @@ int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws, const int32_t *t
         return rc;
     if ((rc = check_bwd_inputs(cfg, tokens, dY, T)))
         return rc;
-    if ((rc = check_step_ptrs(ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
+    if ((rc = check_step_ptrs(cfg, ws, W_b, W_t, state_b, state_t)) || (rc = check_params_ptr(params)))
         return rc;
     return bwd_step_impl(cfg, ws, tokens, dY, T,
                          fuse_args(cfg, W_b, W_t, state_b, state_t, 0, 0.f, 0.f, 0.f, params),

@@ -28,6 +28,7 @@ struct HashParams {
     int32_t eos;
     uint32_t rows[2];
     uint64_t seed[2];
+    uint32_t direct;  // one table indexed by the token id itself (no hashing, no sign)
 };
 
 __device__ __forceinline__ uint64_t mix64(uint64_t z)
@@ -53,6 +54,13 @@ __device__ __forceinline__ bool ngram_index(const int32_t *__restrict__ tok, int
                                             const HashParams &hp, uint32_t &ib, uint32_t &it)
 {
     const int32_t t0 = tok[i];
+    if (hp.direct) {
+        // a token-indexed table (value embeddings): row = the id; an id
+        // outside the table takes row 0 (and is flagged: it is outside [0, V))
+        ib = (uint32_t)t0 < hp.rows[0] ? (uint32_t)t0 : 0u;
+        it = 0;
+        return (uint32_t)t0 >= hp.vocab;
+    }
     const int32_t t1 = i >= 1 ? tok[i - 1] : 0;
     const int32_t t2 = i >= 2 ? tok[i - 2] : 0;
     const uint64_t none = hp.vocab;
@@ -285,6 +293,7 @@ struct WsLayout {
     int dy_elt;             // bytes per dY element: 4 (fp32) or 2 (bf16)
     int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
+    int nch;                // tables: 2 (bigram, trigram), or 1 (token-indexed)
 };
 
 // -------------------------------------------------------------- row step

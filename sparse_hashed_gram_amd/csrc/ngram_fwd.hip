@@ -60,8 +60,9 @@ __device__ __forceinline__ void add_bf16x8_f32(uint4 a, uint4 b, uint4 &lo, uint
 }
 
 // ELT: table element bytes; OUT_F32: fp32 output for a bf16 table (else the
-// output has the table's dtype).
-template <int ELT, bool OUT_F32 = false>
+// output has the table's dtype); DIRECT: one token-indexed table, the output
+// is its row as stored (no second row, no sign).
+template <int ELT, bool OUT_F32 = false, bool DIRECT = false>
 __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restrict__ tok, int64_t T,
                                                           HashParams hp,
                                                           const uint8_t *__restrict__ wb,
@@ -108,7 +109,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restr
                 const uint4 *pb = reinterpret_cast<const uint4 *>(wb + (size_t)(ib & 0x7FFFFFFFu) * kRowBytes) + c;
                 const uint4 *pt = reinterpret_cast<const uint4 *>(wt + (size_t)(it & 0x7FFFFFFFu) * kRowBytes) + c;
                 a[u] = flip(*pb, (ib >> 31) ? kSign : 0u);
-                b[u] = flip(*pt, (it >> 31) ? kSign : 0u);
+                if (!DIRECT)
+                    b[u] = flip(*pt, (it >> 31) ? kSign : 0u);
             }
         }
 #pragma unroll
@@ -118,14 +120,17 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(const int32_t *__restr
                 if constexpr (OUT_F32 && ELT == 2) {
                     // chunk c of a bf16 row holds elements 8c..8c+7: fp32 pieces 2c, 2c+1
                     uint4 lo, hi;
-                    add_bf16x8_f32(a[u], b[u], lo, hi);
+                    // x + (-0) = x for every x, signed zeros and NaN included:
+                    // the direct row widens exactly
+                    add_bf16x8_f32(a[u], DIRECT ? make_uint4(0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u) : b[u],
+                                   lo, hi);
                     const int c = e[u] - lt * kCpr;
                     uint4 *o = orow + (size_t)lt * (kOutRowBytes / 16) + 2 * c;
                     st_global_nt<uint4>((uint64_t)o, lo);
                     st_global_nt<uint4>((uint64_t)(o + 1), hi);
                 } else {
                     st_global_nt<uint4>((uint64_t)(orow + e[u]),
-                                        ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]));
+                                        DIRECT ? a[u] : ELT == 2 ? add_bf16x8(a[u], b[u]) : add_f32x4(a[u], b[u]));
                 }
             }
         }
@@ -286,8 +291,11 @@ hipError_t launch_fwd(int dtype, bool out_f32, const HashParams &hp, const void 
     if (T == 0)
         return hipSuccess;
     const unsigned g = grid_for(T, kFwdTok);
-    launch_prof(NGRAM_PROF_FWD, true, true,
-                dtype == NGRAM_DTYPE_BF16 ? (out_f32 ? fwd_kernel<2, true> : fwd_kernel<2>) : fwd_kernel<4>, dim3(g),
+    auto k = dtype == NGRAM_DTYPE_BF16 ? (out_f32 ? fwd_kernel<2, true> : fwd_kernel<2>) : fwd_kernel<4>;
+    if (hp.direct)
+        k = dtype == NGRAM_DTYPE_BF16 ? (out_f32 ? fwd_kernel<2, true, true> : fwd_kernel<2, false, true>)
+                                      : fwd_kernel<4, false, true>;
+    launch_prof(NGRAM_PROF_FWD, true, true, k, dim3(g),
                 dim3(kFwdThreads), 0, s, tok, T, hp, wb, wt, out, flags);
     return hipGetLastError();
 }

@@ -398,6 +398,12 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
     }
 }
 
+// One table: the keys this sort covered (the split records it otherwise).
+__global__ void sorted_count_kernel(WsHeader *__restrict__ hdr, const uint32_t *n_dev, uint32_t n_host)
+{
+    hdr->sorted_n = count_of(n_dev, n_host);
+}
+
 // Singleton split of the trigram keys, once the heads have their final info:
 // writes every key's singleton-map entry and copies the keys that stay in the
 // trigram pass, in order, with their head info to the split arrays;
@@ -1330,17 +1336,24 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
         uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
         uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
         if (p > 0)
-            radix_hist_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nblk);
-        scan_digits_kernel<<<dim3(kRadix, 2), kSortThreads, 0, s>>>(hist, nblk, tot);
-        radix_scatter_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
+            radix_hist_kernel<<<dim3(nblk, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist,
+                                                                          nblk);
+        scan_digits_kernel<<<dim3(kRadix, L.nch), kSortThreads, 0, s>>>(hist, nblk, tot);
+        radix_scatter_kernel<<<dim3(nblk, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
                                                                     shift, hist, tot, nblk);
         cur ^= 1;
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
-    mark_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
+    // one table (token-indexed): no trigram channel, no singleton split
+    launch_prof(NGRAM_PROF_SORT, false, L.nch == 1 && fused, mark_kernel, dim3(nblk, L.nch), dim3(kSortThreads),
+                0, s, sa);
     if (!fused)   // fused: rows new to the window are stepped at once and need no slot
-        assign_kernel<<<dim3(nblk, 2), kSortThreads, 0, s>>>(sa);
-    launch_prof(NGRAM_PROF_SORT, false, true, split_kernel, dim3(nblk), dim3(kSortThreads), 0, s, sa);
+        launch_prof(NGRAM_PROF_SORT, false, L.nch == 1, assign_kernel, dim3(nblk, L.nch), dim3(kSortThreads), 0, s,
+                    sa);
+    if (L.nch == 2)
+        launch_prof(NGRAM_PROF_SORT, false, true, split_kernel, dim3(nblk), dim3(kSortThreads), 0, s, sa);
+    else
+        sorted_count_kernel<<<1, 1, 0, s>>>(reinterpret_cast<WsHeader *>(ws + L.hdr), n_dev, n_host);
 }
 
 // The signed segment reduction of the sorted keys (accumulating, or fused
@@ -1364,7 +1377,7 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     ra.info[1] = sa.split_info;
     ra.n_dev[1] = &hdr->n_multi;
     ra.n_host = n_host;
-    ra.tinfo = sa.tinfo;
+    ra.tinfo = L.nch == 2 ? sa.tinfo : nullptr;
     ra.dY = burst && !L.by_ref ? ws + L.stash_dy : static_cast<const uint8_t *>(dY);
     ra.dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t *const *>(ws + L.dy_ptrs) : nullptr;
     ra.pos_bits = L.by_ref ? L.pos_bits : 31;
@@ -1381,20 +1394,20 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
         ra.f = *f;
     const uint32_t nchunk = (n_host + kChunk - 1) / kChunk;
     const uint32_t per_block = kRedThreads / kWave;
-    const dim3 grid((nchunk + per_block - 1) / per_block, 2);
+    const dim3 grid((nchunk + per_block - 1) / per_block, L.nch);
     const bool dy16 = L.dy_elt == 2;
     if (!f) {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_reduce_kernel<2> : seg_reduce_kernel<4>, grid,
                     dim3(kRedThreads), 0, s, ra);
-        fixup_kernel<kAccum><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+        fixup_kernel<kAccum><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     } else if (f->dtype == NGRAM_DTYPE_BF16) {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<2, 2> : seg_step_kernel<2, 4>, grid,
                     dim3(kRedThreads), 0, s, ra);
-        fixup_kernel<kFuseBf16><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+        fixup_kernel<kFuseBf16><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     } else {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<4, 2> : seg_step_kernel<4, 4>, grid,
                     dim3(kRedThreads), 0, s, ra);
-        fixup_kernel<kFuseF32><<<dim3(256, 2), kFixThreads, 0, s>>>(ra);
+        fixup_kernel<kFuseF32><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     }
     return hipGetLastError();
 }

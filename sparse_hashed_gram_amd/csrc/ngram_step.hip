@@ -214,7 +214,7 @@ hipError_t launch_step(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStr
     const int64_t want = (L.wrows + 255) / 256;
     const unsigned gx = (unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024);
     launch_prof(NGRAM_PROF_STEP, true, false, dtype == NGRAM_DTYPE_BF16 ? step_kernel<2> : step_kernel<4>,
-                dim3(gx, 2), dim3(256), 0, s, a);
+                dim3(gx, L.nch), dim3(256), 0, s, a);
     launch_prof(NGRAM_PROF_STEP, false, true, window_clear_kernel, dim3(1), dim3(1), 0, s, a.hdr);
     return hipGetLastError();
 }

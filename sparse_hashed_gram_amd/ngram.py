@@ -21,6 +21,7 @@ MODE_BURST = 1
 MODE_BURST_REF = 2
 OPT_PRESORT = 0x1
 OPT_OUT_F32 = 0x2
+OPT_DIRECT = 0x4
 _MODES = {"spread": MODE_SPREAD, "burst": MODE_BURST, "burst_ref": MODE_BURST_REF}
 
 FLAG_BAD_TOKEN = 0x1
@@ -79,7 +80,9 @@ class NgramConfig(ctypes.Structure):
 def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
            max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
            window_rows: int = 0, dy_dtype: str = "f32", presort: bool = False,
-           out_f32: bool = False) -> NgramConfig:
+           out_f32: bool = False, direct: bool = False) -> NgramConfig:
+    """direct: one table indexed by the token id (value embeddings); rows
+    is then (rows of that table, 1) and W_t / state_t may be None."""
     c = NgramConfig()
     c.vocab = vocab
     c.eos_id = eos_id
@@ -92,7 +95,7 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
     c.dy_dtype = DTYPE_F32 if dy_dtype == "f32" else DTYPE_BF16
-    c.options = (OPT_PRESORT if presort else 0) | (OPT_OUT_F32 if out_f32 else 0)
+    c.options = (OPT_PRESORT if presort else 0) | (OPT_OUT_F32 if out_f32 else 0) | (OPT_DIRECT if direct else 0)
     return c
 
 
@@ -217,6 +220,8 @@ def hash(cfg: NgramConfig, tokens: torch.Tensor, ws: Workspace | None = None) ->
 
 def _check_tables(cfg: NgramConfig, W_b, W_t):
     for c, W in ((0, W_b), (1, W_t)):
+        if W is None and c == 1 and cfg.options & OPT_DIRECT:
+            continue
         if tuple(W.shape) != (cfg.rows[c], DIM):
             raise ValueError(f"table {c} must be [{cfg.rows[c]}, {DIM}], got {tuple(W.shape)}")
 
@@ -239,6 +244,8 @@ def state_t_last(st: torch.Tensor) -> torch.Tensor:
 
 def _check_state(cfg: NgramConfig, st_b, st_t):
     for c, x in ((0, st_b), (1, st_t)):
+        if x is None and c == 1 and cfg.options & OPT_DIRECT:
+            continue
         if tuple(x.shape) != (cfg.rows[c], 2) or x.dtype != torch.float32:
             raise ValueError(f"optimizer state of channel {c} must be float32 [{cfg.rows[c]}, 2]")
 

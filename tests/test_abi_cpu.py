@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 6
+    assert N.lib().ngram_abi_version() == 7
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -53,7 +53,7 @@ def _good(N, **kw):
 @pytest.mark.parametrize("field,value", [
     ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
     ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
-    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("options", 4), ("options", 1)])
+    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("options", 8), ("options", 1)])
 def test_config_rejects(N, field, value):
     c = _good(N)
     setattr(c, field, value)
@@ -64,6 +64,21 @@ def test_presort_is_for_burst_modes(N):
     assert N.config_check(_good(N, mode="burst_ref", presort=True)) == 0
     assert N.config_check(_good(N, mode="burst", presort=True)) == 0
     assert N.config_check(_good(N, mode="spread", presort=True)) == -3
+
+
+def test_direct_table_needs_a_row_per_id(N):
+    assert N.config_check(_good(N, rows=(50304, 1), direct=True)) == 0
+    assert N.config_check(_good(N, rows=(50303, 1), direct=True)) == -3
+
+
+def test_direct_table_takes_no_second_table(N):
+    L = N.lib()
+    c = _good(N, rows=(50304, 1), direct=True)
+    fake = ctypes.c_void_p(1 << 40)
+    # NULL W_t / state_t pass the host checks in direct mode (T out of range stops the call)
+    assert L.ngram_embed_fwd(ctypes.byref(c), fake, None, fake, 5000, fake, None, None) == -4
+    h = _good(N)
+    assert L.ngram_embed_fwd(ctypes.byref(h), fake, None, fake, 5, fake, None, None) == -1
 
 
 def test_config_rejects_rows(N):
