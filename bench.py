@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed windows")
     ap.add_argument("--warmup", type=int, default=5, help="untimed windows")
-    ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision"])
+    ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision", "value"])
     ap.add_argument("--mode", default="burst_ref", choices=["spread", "burst", "burst_ref"],
                     help="spread: each micro-step reduced into the window at once; burst: micro-steps "
                          "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
@@ -84,7 +84,7 @@ def parse():
 def workload(name):
     from sparse_hashed_gram_amd import workloads
     return {"tiny": workloads.TINY, "shard": workloads.SHARD, "full": workloads.FULL,
-            "collision": workloads.COLLISION}[name]
+            "collision": workloads.COLLISION, "value": workloads.VALUE}[name]
 
 
 def device_table(torch, R, dtype, seed, chunk=1 << 21):
@@ -98,18 +98,19 @@ def device_table(torch, R, dtype, seed, chunk=1 << 21):
 
 
 def window_stats(torch, N, cfg, toks):
-    """From the library's own hash, per micro-step and channel: distinct rows,
-    rows new to the window, and (trigram) rows that occur once in the
+    """From the library's own hash, per micro-step and table in use: distinct
+    rows, rows new to the window, and (trigram) rows that occur once in the
     micro-step and are new to the window, and rows that occur once in it;
     distinct rows of the whole window; trigram rows that occur once in the
-    whole window."""
+    whole window.  A token-indexed table has one channel."""
+    nch = 1 if cfg.options & N.OPT_DIRECT else 2
     steps = []
-    seen = [None, None]
+    seen = [None] * nch
     all_t = []
     for tok in toks:
         idx = N.hash(cfg, tok)
         per = []
-        for c in range(2):
+        for c in range(nch):
             r = (idx[c] & 0x7FFFFFFF).long()
             u, cnt = torch.unique(r, return_counts=True)
             fresh = torch.ones_like(u, dtype=torch.bool) if seen[c] is None else ~torch.isin(u, seen[c])
@@ -120,8 +121,11 @@ def window_stats(torch, N, cfg, toks):
             if c == 1:
                 all_t.append(r)
         steps.append(per)
-    _, cnt = torch.unique(torch.cat(all_t), return_counts=True)
-    return steps, [int(s.numel()) for s in seen], int((cnt == 1).sum())
+    tsingle = 0
+    if all_t:
+        _, cnt = torch.unique(torch.cat(all_t), return_counts=True)
+        tsingle = int((cnt == 1).sum())
+    return steps, [int(s.numel()) for s in seen], tsingle
 
 
 STATE = 8     # one (v, t_last) record per row
@@ -149,18 +153,19 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_pas
     dY rows count dy_row bytes (3,072 fp32, 1,536 bf16); window rows are fp32."""
     steps, uwin, tsingle_win = stats
     A = len(steps)
-    fwd = T * (3 * row_bytes + 4)
+    nch = len(uwin)   # tables in use: 2, or 1 for a token-indexed table
+    fwd = T * ((nch + 1) * row_bytes + 4)
     table_state = 2 * row_bytes + 2 * STATE
     step_row = ROW_F32 + table_state + 4
     # sort: each radix pass reads and writes a (row, payload) pair per key of
-    # both channels
-    out = {"fwd": [fwd] * A, "sort": [2 * T * 16 * radix_passes] * A}
+    # every channel
+    out = {"fwd": [fwd] * A, "sort": [nch * T * 16 * radix_passes] * A}
     if mode in ("burst", "burst_ref"):
         n = A * T
         copy = 2 * dy_row if mode == "burst" else 0
         out["stash"] = [T * (copy + 4 + 8 + 4)] * A
-        out["sort"] = [2 * n * 16 * radix_passes]
-        out["reduce"] = [(2 * n - tsingle_win) * dy_row + sum(uwin) * table_state]
+        out["sort"] = [nch * n * 16 * radix_passes]
+        out["reduce"] = [(nch * n - tsingle_win) * dy_row + sum(uwin) * table_state]
         out["step"] = [0]
         return out
     red = []
@@ -186,11 +191,11 @@ def src_hash(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic(group, mode, dy_dtype):
+def pmc_traffic(group, workload_key, mode, dy_dtype):
     """HBM bytes per launch of a kernel group from a committed rocprofv3 PMC
     summary (profiles/pmc_*.md, FETCH_SIZE and WRITE_SIZE scaled by a plain
-    copy's reading), if it was taken on the same mode and dY dtype and on the
-    kernel source as it is now; else None."""
+    copy's reading), if it was taken on the same workload, mode and dY dtype
+    and on the kernel source as it is now; else None."""
     import glob
     want = src_hash(KERNEL_SRC[group])
     for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_*.md"))):
@@ -201,7 +206,7 @@ def pmc_traffic(group, mode, dy_dtype):
                     k, _, v = line.partition(":")
                     kv[k.strip()] = v.strip()
         if (kv.get("kernel") == group and kv.get("source_sha256_16") == want and kv.get("mode") == mode
-                and kv.get("dy_dtype") == dy_dtype):
+                and kv.get("dy_dtype") == dy_dtype and kv.get("workload") == workload_key):
             try:
                 return float(kv["hbm_bytes_per_launch"])
             except (KeyError, ValueError):
@@ -222,7 +227,11 @@ def cpu_baseline(w, toks_np, T_sample, dys_fn):
         toks = [t[:T_sample] for t in wtoks]
         A = len(toks)
         dY = np.concatenate([dys_fn(win * A + m, T_sample) for m in range(A)])
-        rows = [oracle.ngram_rows(t, w.vocab, w.eos_id, w.rows) for t in toks]
+        if w.direct:   # the token ids are the rows, every sign +1; no second table
+            rows = [(t.astype(np.int64), np.zeros(len(t), np.uint8)) * 2 for t in toks]
+        else:
+            rows = [oracle.ngram_rows(t, w.vocab, w.eos_id, w.rows) for t in toks]
+        nch = 1 if w.direct else 2
         rs = np.random.default_rng(win)
         ids = []
         snaps = []
@@ -233,10 +242,13 @@ def cpu_baseline(w, toks_np, T_sample, dys_fn):
                          ^ (rs.integers(0, 2, size=(len(u), 768)).astype(np.uint16) << 15))
         t0 = time.perf_counter()
         for m in range(A):
+            if w.direct:   # the forward is a gather of the snapshot rows
+                snaps[0][np.searchsorted(ids[0], toks[m])]
+                continue
             rb, nb, rt, nt, _ = oracle.ngram_rows(toks[m], w.vocab, w.eos_id, w.rows)
             oracle.forward(snaps[0], snaps[1], rb, nb, rt, nt, ids_b=ids[0], ids_t=ids[1],
                            out_dtype="bf16")
-        for c in range(2):
+        for c in range(nch):
             r = np.concatenate([x[2 * c] for x in rows])
             n = np.concatenate([x[2 * c + 1] for x in rows])
             touched, G = oracle.window_grad(r, n, dY)
@@ -291,11 +303,12 @@ def main():
     torch.cuda.set_device(0)
     overlap = args.schedule == "overlap" and args.mode in ("burst", "burst_ref")
     cfg = N.config(w.vocab, w.eos_id, w.rows, w.dtype, max_tokens=T, accum_steps=A, mode=args.mode,
-                   dy_dtype=args.dy_dtype, presort=overlap)
+                   dy_dtype=args.dy_dtype, presort=overlap, direct=w.direct)
     dy_row = 768 * (2 if args.dy_dtype == "bf16" else 4)
 
-    W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(2)]
-    state = [N.new_state(w.rows[c]) for c in range(2)]
+    nch = 1 if w.direct else 2   # a token-indexed table has no second table
+    W = [device_table(torch, w.rows[c], tdt, 1000 + c) for c in range(nch)] + [None] * (2 - nch)
+    state = [N.new_state(w.rows[c]) for c in range(nch)] + [None] * (2 - nch)
     ws = N.Workspace(cfg)
     out = torch.empty((T, 768), dtype=tdt, device="cuda")
     nwin = max(1, args.distinct_windows)
@@ -424,7 +437,7 @@ def main():
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    traffic = pmc_traffic(dom, args.mode, args.dy_dtype)
+    traffic = pmc_traffic(dom, args.workload, args.mode, args.dy_dtype)
     achieved = abytes[dom] / (ms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -43,6 +43,7 @@ class Workload:
     vocab: int = VOCAB
     eos_id: int = EOS_ID
     dim: int = DIM
+    direct: bool = False     # one table indexed by the token id (value embeddings)
 
     @property
     def rows(self) -> tuple[int, int]:
@@ -72,6 +73,11 @@ COLLISION = Workload(
     name="collision stress: 84.6M-row bf16 table, 393,216 tokens/step, Zipf 1.4 + 20% hot-256",
     wid=4, rows_bigram=42_300_000, rows_trigram=42_300_000, dtype="bf16",
     tokens_per_step=393_216, steps=8, zipf_s=1.4, hot_frac=0.2)
+
+VALUE = Workload(
+    name="value embeddings: token-indexed 50,304x768 bf16 table, 393,216 tokens/step, Zipf 1.1",
+    wid=6, rows_bigram=VOCAB, rows_trigram=1, dtype="bf16",
+    tokens_per_step=393_216, steps=8, direct=True)
 
 SPREAD_BURST = Workload(
     name="spread vs burst: 84.6M-row bf16 table, 393,216 tokens/step, 32 steps",
