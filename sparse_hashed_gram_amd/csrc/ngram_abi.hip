@@ -130,6 +130,9 @@ WsLayout layout(const ngram_config *c)
     o = up(o + 4ull * 2 * (uint64_t)L.nchunk * 2 * kDim);
     L.owners = o;
     o = up(o + 8ull * 2 * (uint64_t)L.nchunk);
+    L.ngroup = (L.nchunk + kGroup - 1) / kGroup;
+    L.gpart = o;
+    o = up(o + 4ull * 2 * (uint64_t)L.ngroup * kDim);
     L.code_cap = L.by_ref ? ((int64_t)L.accum << L.pos_bits) : L.nk;
     L.tinfo = o;
     o = up(o + 4ull * (uint64_t)L.code_cap);

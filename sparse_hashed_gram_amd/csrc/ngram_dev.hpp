@@ -257,6 +257,8 @@ static_assert(kRadix % kSortThreads == 0, "digits are split evenly over the thre
 
 // Segment-reduce chunks: one wavefront per 64 sorted keys.
 constexpr int kChunk = 64;
+// Chunks per group in the fix-up of long segments.
+constexpr int kGroup = 64;
 
 struct WsLayout {
     uint64_t hdr;
@@ -272,6 +274,7 @@ struct WsLayout {
     uint64_t kept;          // uint32 [nblk]: trigram keys kept per sort tile by the singleton split
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
+    uint64_t gpart;         // fp32 [2][ngroup][768]: sums of 64-chunk groups inside one segment
     uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row's singleton
                             // record (see the singleton split), else kNotSingle
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
@@ -286,6 +289,7 @@ struct WsLayout {
     int64_t nk;             // keys per channel one reduce can hold
     int64_t nblk;           // sort tiles for nk keys
     int64_t nchunk;         // 64-key chunks for nk keys
+    int64_t ngroup;         // groups of 64 chunks
     int passes;             // radix passes (8 bits each)
     bool burst;             // micro-steps are kept and reduced at step time
     bool by_ref;            // ... and their dY is read where the caller keeps it

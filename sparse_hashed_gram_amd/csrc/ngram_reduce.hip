@@ -556,6 +556,8 @@ struct RedArgs {
     float *partial;         // [2][nchunk][2][768]
     uint64_t *owners;       // [2][nchunk]: chunk | info << 32
     int64_t nchunk;
+    float *gpart;           // [2][ngroup][768]: sums of groups of kGroup chunks inside one segment
+    int64_t ngroup;
     WsHeader *hdr;
     const uint32_t *tinfo;  // singleton map per dY row code
     bool burst;             // the keys are the burst stash's: check the window is ready
@@ -1126,10 +1128,70 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
     }
 }
 
+// Long segments (hot n-grams: up to thousands of chunks) leave one partial row
+// per chunk.  A group of kGroup chunks that lies inside one segment -- the
+// keys just before and just after the group have the same row, so every
+// chunk of the group starts and ends inside that segment and its partial row
+// 0 is the whole chunk -- is summed here once, in a fixed order (4 runs of 16
+// chunks, then the runs in order), and the fix-up adds the group's sum
+// instead of its kGroup pieces.
+constexpr int kGroupThreads = 256;
+__global__ __launch_bounds__(kGroupThreads) void group_sum_kernel(RedArgs a)
+{
+    constexpr int kW = kGroupThreads / kWave;
+    constexpr int kRun = kGroup / kW;
+    __shared__ float4 s_part[kW][kDim / 4];
+    const int c = blockIdx.y;
+    const int64_t g = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    const int64_t n = count_of(a.n_dev[c], a.n_host);
+    const int64_t k0 = g * kGroup * kChunk;   // the group's first key
+    const int64_t k1 = k0 + kGroup * kChunk;  // the first key after it
+    if (g == 0 || k1 >= n)
+        return;
+    const uint32_t *R = a.rows[c];
+    if (R[k0 - 1] != R[k1])
+        return;   // not inside one segment
+    const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
+    float4 acc[3] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
+                     make_float4(0.f, 0.f, 0.f, 0.f)};
+    const int64_t c0 = g * kGroup + w * kRun;
+    for (int i = 0; i < kRun; i += kRedU) {
+        float4 x[kRedU][3];
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u) {
+            const float4 *s = P + (c0 + i + u) * 2 * (kDim / 4) + lane;   // partial row 0 of the chunk
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                x[u][q] = s[q * kWave];
+        }
+#pragma unroll
+        for (int u = 0; u < kRedU; ++u)
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                acc[q] = add4(acc[q], x[u][q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        s_part[w][lane + q * kWave] = acc[q];
+    __syncthreads();
+    if (tid < kDim / 4) {
+        float4 sum = s_part[0][tid];
+#pragma unroll
+        for (int ww = 1; ww < kW; ++ww)
+            sum = add4(sum, s_part[ww][tid]);
+        reinterpret_cast<float4 *>(a.gpart + ((size_t)c * a.ngroup + g) * kDim)[tid] = sum;
+    }
+}
+
 // Sums the partial rows of each segment longer than two chunks: the starting
-// chunk's tail piece, then every following chunk's head piece, split into 16
-// contiguous runs (one per wavefront) that are added in run order.  Then the
-// row goes to the window, or (fused) is completed and stepped by the block.
+// chunk's tail piece, then the following chunks' head pieces -- the sums of
+// the whole groups inside the segment in place of their chunks' pieces --
+// split into 16 contiguous runs (one per wavefront) that are added in run
+// order.  Then the row goes to the window, or (fused) is completed and
+// stepped by the block.
 constexpr int kFixThreads = 1024;
 template <int MODE>
 __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
@@ -1192,7 +1254,24 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
                     break;
             }
         }
-        const int64_t np = m + 1;
+        // items: the owner's tail piece; the head pieces of chunks first ..
+        // 64 g_lo - 1; the sums of groups g_lo .. g_hi - 1 (chunks inside
+        // first .. last - 1); the head pieces of chunks 64 g_hi .. last
+        const int64_t first = chunk + 1, last = chunk + m;
+        const int64_t g_lo = (first + kGroup - 1) / kGroup, g_hi = last / kGroup;
+        const int64_t ng = g_hi > g_lo ? g_hi - g_lo : 0;
+        const int64_t n_before = ng ? g_lo * kGroup - first : m;
+        const int64_t np = 1 + n_before + ng + (ng ? last - g_hi * kGroup + 1 : 0);
+        const float4 *G4 = reinterpret_cast<const float4 *>(a.gpart + (size_t)c * a.ngroup * kDim);
+        auto item = [&](int64_t q) -> const float4 * {
+            if (q == 0)
+                return P + (chunk * 2 + 1) * (kDim / 4);
+            if (q <= n_before)
+                return P + (first + q - 1) * 2 * (kDim / 4);
+            if (q <= n_before + ng)
+                return G4 + (g_lo + q - 1 - n_before) * (kDim / 4);
+            return P + (g_hi * kGroup + q - 1 - n_before - ng) * 2 * (kDim / 4);
+        };
         const int64_t lo = np * w / kW, hi = np * (w + 1) / kW;
         float4 acc[3] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f),
                          make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -1201,8 +1280,7 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 #pragma unroll
             for (int u = 0; u < kRedU; ++u) {
                 if (p + u < hi) {
-                    const int64_t src = p + u == 0 ? chunk * 2 + 1 : (chunk + p + u) * 2;
-                    const float4 *s = P + src * (kDim / 4) + lane;
+                    const float4 *s = item(p + u) + lane;
                     x[u][0] = s[0];
                     x[u][1] = s[kWave];
                     x[u][2] = s[2 * kWave];
@@ -1388,6 +1466,8 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     ra.partial = reinterpret_cast<float *>(ws + L.partial);
     ra.owners = reinterpret_cast<uint64_t *>(ws + L.owners);
     ra.nchunk = L.nchunk;
+    ra.gpart = reinterpret_cast<float *>(ws + L.gpart);
+    ra.ngroup = L.ngroup;
     ra.hdr = hdr;
     ra.burst = burst;
     if (f)
@@ -1396,17 +1476,21 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     const uint32_t per_block = kRedThreads / kWave;
     const dim3 grid((nchunk + per_block - 1) / per_block, L.nch);
     const bool dy16 = L.dy_elt == 2;
+    const dim3 ggrid((unsigned)((nchunk + kGroup - 1) / kGroup), L.nch);
     if (!f) {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_reduce_kernel<2> : seg_reduce_kernel<4>, grid,
                     dim3(kRedThreads), 0, s, ra);
+        group_sum_kernel<<<ggrid, kGroupThreads, 0, s>>>(ra);
         fixup_kernel<kAccum><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     } else if (f->dtype == NGRAM_DTYPE_BF16) {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<2, 2> : seg_step_kernel<2, 4>, grid,
                     dim3(kRedThreads), 0, s, ra);
+        group_sum_kernel<<<ggrid, kGroupThreads, 0, s>>>(ra);
         fixup_kernel<kFuseBf16><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     } else {
         launch_prof(NGRAM_PROF_REDUCE, true, true, dy16 ? seg_step_kernel<4, 2> : seg_step_kernel<4, 4>, grid,
                     dim3(kRedThreads), 0, s, ra);
+        group_sum_kernel<<<ggrid, kGroupThreads, 0, s>>>(ra);
         fixup_kernel<kFuseF32><<<dim3(256, L.nch), kFixThreads, 0, s>>>(ra);
     }
     return hipGetLastError();
