@@ -98,3 +98,14 @@ def loss_bwd(X, W, cand, slot, dloss):
     dz = dlogits(X, W, cand, slot, dloss)
     Wc = np.asarray(W, np.float64)[cand]
     return dz @ Wc, dz.T @ np.asarray(X, np.float64)
+
+
+def dW_rows(X, W, cand, slot, dloss, lse, cs):
+    """Rows cs of dWc (what W[cand[cs]] receives), from every position's lse:
+    dWc[c] = sum_i g_i (exp(z_ic - lse_i) - [slot_i = c]) X_i, fp64."""
+    cs = np.asarray(cs, np.int64)
+    X64 = np.asarray(X, np.float64)
+    z = X64 @ np.asarray(W, np.float64)[np.asarray(cand)[cs]].T          # [T, |cs|]
+    p = np.exp(z - np.asarray(lse, np.float64)[:, None])
+    p -= (np.asarray(slot, np.int64)[:, None] == cs[None, :])
+    return (np.asarray(dloss, np.float64)[:, None] * p).T @ X64

@@ -1,4 +1,5 @@
-"""Builds libngram.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libngram.so (HIP, gfx950) in-tree with hipcc: the n-gram table
+(include/ngram.h) and the sampled-softmax loss (include/ssm.h).
 
     python -m sparse_hashed_gram_amd.build
 
@@ -18,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT, "libngram.so")
-SOURCES = ["ngram_abi.hip", "ngram_fwd.hip", "ngram_reduce.hip", "ngram_step.hip"]
+SOURCES = ["ngram_abi.hip", "ngram_fwd.hip", "ngram_reduce.hip", "ngram_step.hip", "ssm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

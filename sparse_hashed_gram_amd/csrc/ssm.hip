@@ -1,0 +1,843 @@
+// Sampled-softmax training loss on gfx950 (the method and readings are in
+// include/ssm.h): the candidate set, then three bf16 contractions on the
+// matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation) with the softmax
+// work fused into their epilogues:
+//
+//   forward   z = X W_S^T per 128 x 128 tile -> per-tile (max, sum exp) of
+//             each position, the target's logit; a per-position pass folds
+//             the tiles into lse and the loss.  z never reaches memory.
+//   backward  z recomputed per tile -> dz = g (exp(z - lse) - onehot), bf16,
+//             written row-major and transposed; dX = dz W_S; dW[S] += dz^T X.
+//
+// Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
+// k-contiguous in memory (the backward's transposed operands are written
+// first), so one main loop serves all three: a 128 x 128 block tile, k-steps
+// of 64 through double-buffered LDS, four wavefronts of 64 x 64 (2 x 2
+// matrix-core tiles of 32 x 32).
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 768;
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdk = kBK + 8;   // bf16 per LDS operand row: 144 B, 16-byte reads conflict-free
+constexpr int kLdt = kBN + 4;   // fp32 per row of the forward's epilogue tile
+constexpr int kLdb = kBN + 8;   // bf16 per row of the dz epilogue tile
+constexpr int kTile = 128;      // T and C are padded to multiples of this
+constexpr uint32_t kSmem = 2u * (kBM + kBN) * kLdk * 2u;   // 73,728 B
+static_assert(kBM * kLdt * 4 + kBM * 8 <= (int)kSmem, "forward epilogue fits");
+static_assert(kBM * kLdb * 2 + 3 * kBM * 4 <= (int)kSmem, "dz epilogue fits");
+constexpr uint32_t kMagic = 0x53534d31u;
+constexpr uint64_t kAlign = 256;
+constexpr int kSelectThreads = 1024;
+
+struct Hdr {
+    uint32_t magic;
+    uint32_t flags;        // sticky SSM_FLAG_*
+    uint32_t void_batch;   // nonzero: the last candidate set is void
+    uint32_t n_present;    // distinct targets of the last candidate set
+    uint32_t pad[60];
+};
+static_assert(sizeof(Hdr) == 256, "header is 256 bytes");
+
+struct Layout {
+    int64_t Tp, Cp;   // padded maxima
+    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, dzt, total;
+};
+
+inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+Layout layout(const ssm_config *c)
+{
+    Layout L{};
+    L.Tp = rup(c->max_tokens, kTile);
+    L.Cp = rup(c->candidates, kTile);
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        uint64_t at = o;
+        o += (bytes + kAlign - 1) / kAlign * kAlign;
+        return at;
+    };
+    L.hdr = take(sizeof(Hdr));
+    L.rank = take(4ull * c->vocab);
+    L.cnt = take(4ull * c->vocab);
+    L.zt = take(4ull * L.Tp);
+    L.part = take(8ull * L.Tp * (L.Cp / kTile));
+    L.xt = take(2ull * kD * L.Tp);
+    L.wst = take(2ull * kD * L.Cp);
+    L.dz = take(2ull * L.Tp * L.Cp);
+    L.dzt = take(2ull * L.Tp * L.Cp);
+    L.total = o;
+    return L;
+}
+
+// ------------------------------------------------------------ candidate set
+
+__global__ void init_kernel(Hdr *h)
+{
+    if (threadIdx.x == 0) {
+        h->magic = kMagic;
+        h->flags = 0;
+        h->void_batch = 0;
+        h->n_present = 0;
+    }
+}
+
+__global__ void flags_clear_kernel(Hdr *h)
+{
+    if (threadIdx.x == 0)
+        h->flags = 0;
+}
+
+__global__ void cand_clear_kernel(int32_t *rank, int32_t *cnt, int32_t V, Hdr *h)
+{
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v < V) {
+        rank[v] = 0;
+        cnt[v] = 0;
+    }
+    if (v == 0)
+        h->void_batch = 0;
+}
+
+// rank[] holds the presence mark (1) until the select kernel ranks it.
+__global__ void cand_mark_kernel(const int32_t *tgt, int64_t T, const int32_t *perm, int32_t V,
+                                 int32_t *rank, int32_t *cnt, Hdr *h)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < T) {
+        const int32_t y = tgt[i];
+        if ((uint32_t)y < (uint32_t)V) {
+            rank[y] = 1;
+        } else {
+            atomicOr(&h->flags, SSM_FLAG_BAD_TARGET);
+            atomicOr(&h->void_batch, 1u);
+        }
+    }
+    if (i < V) {
+        const int32_t p = perm[i];
+        if ((uint32_t)p < (uint32_t)V) {
+            atomicAdd(&cnt[p], 1);
+        } else {
+            atomicOr(&h->flags, SSM_FLAG_BAD_PERM);
+            atomicOr(&h->void_batch, 1u);
+        }
+    }
+}
+
+// Exclusive scan of one value per thread over the block; returns the
+// exclusive prefix and writes the block total to *total (all threads).
+__device__ inline int32_t block_scan(int32_t x, int32_t *wsum, int32_t *total)
+{
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int32_t v = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += o;
+    }
+    if (lane == 63)
+        wsum[w] = v;
+    __syncthreads();
+    if (t == 0) {
+        int32_t s = 0;
+        for (int k = 0; k < kSelectThreads / 64; ++k) {
+            const int32_t e = wsum[k];
+            wsum[k] = s;
+            s += e;
+        }
+        wsum[kSelectThreads / 64] = s;
+    }
+    __syncthreads();
+    const int32_t r = wsum[w] + v - x;
+    *total = wsum[kSelectThreads / 64];
+    __syncthreads();
+    return r;
+}
+
+// One block: ranks the present ids (ascending) into cand[0, n), then fills
+// cand[n, C) with absent ids in permutation order.
+__global__ __launch_bounds__(kSelectThreads) void cand_select_kernel(const int32_t *perm, int32_t V,
+                                                                      int32_t C, int32_t *rank,
+                                                                      const int32_t *cnt, int32_t *cand,
+                                                                      Hdr *h)
+{
+    __shared__ int32_t wsum[kSelectThreads / 64 + 1];
+    __shared__ int32_t s_bad;
+    const int t = threadIdx.x;
+    if (t == 0)
+        s_bad = 0;
+    for (int32_t c = t; c < C; c += kSelectThreads)
+        cand[c] = 0;   // in range whatever follows
+    __syncthreads();
+
+    int32_t base = 0;
+    for (int32_t v0 = 0; v0 < V; v0 += kSelectThreads) {
+        const int32_t v = v0 + t;
+        const int32_t pres = v < V ? rank[v] : 0;
+        if (v < V && cnt[v] != 1)
+            s_bad = 1;
+        int32_t tot;
+        const int32_t r = base + block_scan(pres, wsum, &tot);
+        if (v < V) {
+            rank[v] = pres ? r : -1;
+            if (pres && r < C)
+                cand[r] = v;
+        }
+        base += tot;
+    }
+    const int32_t n = base;
+    __syncthreads();   // ranks visible to the whole block
+    if (n < C) {
+        int32_t filled = 0;
+        for (int32_t j0 = 0; j0 < V && filled < C - n; j0 += kSelectThreads) {
+            const int32_t j = j0 + t;
+            int32_t p = -1;
+            if (j < V) {
+                p = perm[j];
+                if ((uint32_t)p >= (uint32_t)V)
+                    p = -1;
+            }
+            const int32_t absent = (p >= 0 && rank[p] < 0) ? 1 : 0;
+            int32_t tot;
+            const int32_t pos = filled + block_scan(absent, wsum, &tot);
+            if (absent && pos < C - n)
+                cand[n + pos] = p;
+            filled += tot;
+        }
+    }
+    if (t == 0) {
+        h->n_present = (uint32_t)n;
+        uint32_t f = 0;
+        if (n > C)
+            f |= SSM_FLAG_OVERFLOW;
+        if (s_bad)
+            f |= SSM_FLAG_BAD_PERM;
+        if (f) {
+            atomicOr(&h->flags, f);
+            atomicOr(&h->void_batch, 1u);
+        }
+    }
+}
+
+__global__ void cand_slot_kernel(const int32_t *tgt, int64_t T, int32_t V, int32_t C,
+                                 const int32_t *rank, int32_t *slot)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T)
+        return;
+    const int32_t y = tgt[i];
+    int32_t s = 0;
+    if ((uint32_t)y < (uint32_t)V) {
+        const int32_t r = rank[y];
+        s = (r >= 0 && r < C) ? r : 0;
+    }
+    slot[i] = s;
+}
+
+// --------------------------------------------------------- the contraction
+
+// Row i of an operand: base + row * ld, with row = idx[i] for a gathered
+// operand.  Rows at or past n read row n - 1 (their results are masked).
+struct Rows {
+    const uint16_t *base;
+    int64_t ld;            // elements between rows
+    const int32_t *idx;    // gather ids, or nullptr
+    int32_t n;             // rows that exist (>= 1)
+    int32_t V;             // gather ids must be below V
+};
+
+__device__ inline const uint16_t *row_ptr(const Rows &r, int64_t i, uint32_t *flags)
+{
+    int64_t j = i < r.n ? i : r.n - 1;
+    if (r.idx) {
+        int32_t v = r.idx[j];
+        if ((uint32_t)v >= (uint32_t)r.V) {
+            atomicOr(flags, SSM_FLAG_BAD_CAND);
+            v = 0;
+        }
+        j = v;
+    }
+    return r.base + j * r.ld;
+}
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc[mb][nb] = the wavefront's 32 x 32 tiles of C[m0 + ..][n0 + ..]; K is a
+// multiple of kBK.  Ends with a block barrier (LDS free for the epilogue).
+__device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
+                                uint16_t *sm, f32x16 (&acc)[2][2], uint32_t *flags)
+{
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int lr = t >> 3, lc = (t & 7) * 8;   // loader: rows lr + 32 j, 16 bytes at column lc
+    const uint16_t *pa[4], *pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pa[j] = row_ptr(A, m0 + lr + 32 * j, flags) + lc;
+        pb[j] = row_ptr(B, n0 + lr + 32 * j, flags) + lc;
+    }
+    uint16_t *As = sm, *Bs = sm + 2 * kBM * kLdk;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[mb][nb][e] = 0.f;
+
+    u32x4 ra[4], rb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        ra[j] = *(const u32x4 *)pa[j];
+        rb[j] = *(const u32x4 *)pb[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        *(u32x4 *)(As + (lr + 32 * j) * kLdk + lc) = ra[j];
+        *(u32x4 *)(Bs + (lr + 32 * j) * kLdk + lc) = rb[j];
+    }
+    __syncthreads();
+
+    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
+    const int64_t nk = K / kBK;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int64_t k0 = (kt + 1) * kBK;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ra[j] = *(const u32x4 *)(pa[j] + k0);
+                rb[j] = *(const u32x4 *)(pb[j] + k0);
+            }
+        }
+        const uint16_t *as = As + cur * kBM * kLdk, *bs = Bs + cur * kBN * kLdk;
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 16) {
+            const bf16x8 a0 = *(const bf16x8 *)(as + ar * kLdk + kk + kh);
+            const bf16x8 a1 = *(const bf16x8 *)(as + (ar + 32) * kLdk + kk + kh);
+            const bf16x8 b0 = *(const bf16x8 *)(bs + br * kLdk + kk + kh);
+            const bf16x8 b1 = *(const bf16x8 *)(bs + (br + 32) * kLdk + kk + kh);
+            acc[0][0] = mfma(a0, b0, acc[0][0]);
+            acc[0][1] = mfma(a0, b1, acc[0][1]);
+            acc[1][0] = mfma(a1, b0, acc[1][0]);
+            acc[1][1] = mfma(a1, b1, acc[1][1]);
+        }
+        if (more) {
+            uint16_t *an = As + (cur ^ 1) * kBM * kLdk, *bn = Bs + (cur ^ 1) * kBN * kLdk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *(u32x4 *)(an + (lr + 32 * j) * kLdk + lc) = ra[j];
+                *(u32x4 *)(bn + (lr + 32 * j) * kLdk + lc) = rb[j];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Position of acc[mb][nb][e] in the block tile (32 x 32 matrix-core layout:
+// lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4).
+__device__ inline int tile_row(int mb, int e)
+{
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    return wm * 64 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+__device__ inline int tile_col(int nb)
+{
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    return wn * 64 + nb * 32 + (lane & 31);
+}
+
+__device__ inline uint16_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+enum { EPI_FWD = 0, EPI_DZ = 1, EPI_DX = 2, EPI_DW = 3 };
+
+struct GemmArgs {
+    Rows A, B;
+    int64_t K;
+    int64_t T;             // positions
+    int32_t C;             // candidates
+    int32_t V;
+    const int32_t *slot;   // [T]
+    const int32_t *cand;   // [C]
+    const float *lse;      // [T]
+    const float *g;        // [T]
+    float *zt;             // forward: target logits [T]
+    float2 *part;          // forward: per-tile (max, sum exp) [C / 128][T]
+    uint16_t *dz;          // [Tq][Cp] bf16
+    uint16_t *dzt;         // [Cp][Tq] bf16
+    int64_t Tq, Cp;
+    float *out;            // dX [T][768] or dW [V][768]
+    Hdr *h;
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+{
+    __shared__ __align__(16) uint8_t smem[kSmem];
+    const int64_t m0 = (int64_t)blockIdx.x * kBM, n0 = (int64_t)blockIdx.y * kBN;
+    f32x16 acc[2][2];
+    mainloop(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    const int t = threadIdx.x;
+
+    if constexpr (EPI == EPI_FWD) {
+        float *tile = reinterpret_cast<float *>(smem);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    tile[tile_row(mb, e) * kLdt + tile_col(nb)] = acc[mb][nb][e];
+        __syncthreads();
+        // thread: row r, columns hf*64 .. +64; the two halves meet in LDS
+        const int r = t & 127, hf = t >> 7;
+        const int64_t i = m0 + r, c0 = n0 + hf * 64;
+        const int64_t left = (int64_t)a.C - c0;
+        const int nv = left <= 0 ? 0 : (left >= 64 ? 64 : (int)left);
+        const float *zr = tile + r * kLdt + hf * 64;
+        float m = -INFINITY, s = 0.f;
+        if (nv > 0) {
+            for (int k = 0; k < 64; ++k)
+                if (k < nv)
+                    m = fmaxf(m, zr[k]);
+            for (int k = 0; k < 64; ++k)
+                if (k < nv)
+                    s += __expf(zr[k] - m);
+        }
+        if (i < a.T) {
+            const int64_t y = a.slot[i];
+            if (y >= c0 && y < c0 + nv)
+                a.zt[i] = zr[y - c0];
+        }
+        float2 *pr = reinterpret_cast<float2 *>(smem + kBM * kLdt * 4);
+        if (hf == 1)
+            pr[r] = make_float2(m, s);
+        __syncthreads();
+        if (hf == 0 && i < a.T) {
+            const float2 o = pr[r];
+            const float M = fmaxf(m, o.x);
+            float S = s * __expf(m - M);
+            if (o.y > 0.f)
+                S += o.y * __expf(o.x - M);
+            a.part[(int64_t)blockIdx.y * a.T + i] = make_float2(M, S);
+        }
+    } else if constexpr (EPI == EPI_DZ) {
+        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [kBM][kLdb] bf16
+        float *s_l = reinterpret_cast<float *>(smem + kBM * kLdb * 2);
+        float *s_g = s_l + kBM;
+        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + kBM);
+        if (t < kBM) {
+            const int64_t i = m0 + t;
+            const bool ok = i < a.T && a.h->void_batch == 0;
+            s_l[t] = ok ? a.lse[i] : 0.f;
+            s_g[t] = ok ? a.g[i] : 0.f;
+            s_y[t] = ok ? a.slot[i] : -1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int rr = tile_row(mb, e), cc = tile_col(nb);
+                    const int64_t c = n0 + cc;
+                    float d = 0.f;   // padding rows and columns, and a void batch, give 0
+                    if (c < a.C && s_g[rr] != 0.f) {
+                        const float p = __expf(acc[mb][nb][e] - s_l[rr]);
+                        d = s_g[rr] * (p - (s_y[rr] == c ? 1.f : 0.f));
+                    }
+                    bt[rr * kLdb + cc] = bf16_rne(d);
+                }
+        __syncthreads();
+        // row-major: 16 chunks of 16 B per row
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int rr = (t >> 4) + 16 * p, q = t & 15;
+            const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
+            *(u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8) = v;
+        }
+        // transposed: column cc, rows hf*64 .. +64 in chunks of 8
+        const int cc = t & 127, r0 = (t >> 7) * 64;
+#pragma unroll
+        for (int k = 0; k < 64; k += 8) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wv[e] = (uint32_t)bt[(r0 + k + 2 * e) * kLdb + cc] |
+                        ((uint32_t)bt[(r0 + k + 2 * e + 1) * kLdb + cc] << 16);
+            *(u32x4 *)(a.dzt + (n0 + cc) * a.Tq + m0 + r0 + k) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        }
+    } else if constexpr (EPI == EPI_DX) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t i = m0 + tile_row(mb, e);
+                if (i < a.T) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        a.out[i * kD + n0 + tile_col(nb)] = acc[mb][nb][e];
+                }
+            }
+    } else {   // EPI_DW
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t c = m0 + tile_row(mb, e);
+                if (c < a.C) {
+                    const int32_t v = a.cand[c];
+                    if ((uint32_t)v < (uint32_t)a.V) {
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            float *o = a.out + (int64_t)v * kD + n0 + tile_col(nb);
+                            *o += acc[mb][nb][e];
+                        }
+                    }
+                }
+            }
+    }
+}
+
+// Folds the per-tile sums of each position: lse = M + log sum_t s_t e^(m_t - M).
+__global__ void lse_kernel(const float2 *part, int64_t T, int nct, const int32_t *slot, int32_t C,
+                           const float *zt, float *loss, float *lse, Hdr *h)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T)
+        return;
+    float M = -INFINITY;
+    for (int c = 0; c < nct; ++c)
+        M = fmaxf(M, part[(int64_t)c * T + i].x);
+    float S = 0.f;
+    for (int c = 0; c < nct; ++c) {
+        const float2 p = part[(int64_t)c * T + i];
+        S += p.y * expf(p.x - M);
+    }
+    const float l = M + logf(S);
+    const int32_t y = slot[i];
+    const bool ok = (uint32_t)y < (uint32_t)C;
+    if (!ok)
+        atomicOr(&h->flags, SSM_FLAG_BAD_SLOT);
+    const bool bad = h->void_batch != 0;
+    lse[i] = bad ? NAN : l;
+    loss[i] = (bad || !ok) ? NAN : l - zt[i];
+}
+
+// dst[d][j] = element d of source row j for j < n, 0 for n <= j < (grid.x * 64);
+// dst is [768][ldd] bf16.
+__global__ __launch_bounds__(256) void transpose_kernel(Rows src, int64_t n, uint16_t *dst, int64_t ldd,
+                                                        uint32_t *flags)
+{
+    __shared__ __align__(16) uint16_t s[64][72];
+    const int t = threadIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.x * 64;
+    const int d0 = blockIdx.y * 64;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int r = (t >> 3) + 32 * p, q = t & 7;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j0 + r < n)
+            v = *(const u32x4 *)(row_ptr(src, j0 + r, flags) + d0 + q * 8);
+        *(u32x4 *)&s[r][q * 8] = v;
+    }
+    __syncthreads();
+    const int d = t >> 2, rb = (t & 3) * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            wv[e] = (uint32_t)s[rb + 8 * h + 2 * e][d] | ((uint32_t)s[rb + 8 * h + 2 * e + 1][d] << 16);
+        *(u32x4 *)(dst + (int64_t)(d0 + d) * ldd + j0 + rb + 8 * h) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+}
+
+// ------------------------------------------------------------------ launch
+
+struct ProfPair {
+    hipEvent_t start, stop;
+};
+thread_local ProfPair g_prof[SSM_PROF_GROUPS];
+
+template <typename... KArgs, typename... Args>
+void launch(int group, bool first, bool last, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+            hipStream_t s, Args... args)
+{
+    hipEvent_t a = first ? g_prof[group].start : nullptr;
+    hipEvent_t b = last ? g_prof[group].stop : nullptr;
+    if (a || b)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0u, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, 0, s>>>(static_cast<KArgs>(args)...);
+}
+
+int check_cfg(const ssm_config *c)
+{
+    if (!c)
+        return SSM_ENULL;
+    if (c->dim != kD || c->vocab < 1 || c->candidates < 1 || c->candidates > c->vocab ||
+        c->reserved != 0 || c->max_tokens < 1 || c->max_tokens > (1 << 24))
+        return SSM_ECONFIG;
+    return SSM_OK;
+}
+
+bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+int done(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_EHIP; }
+
+uint32_t blocks(int64_t n, int b) { return (uint32_t)((n + b - 1) / b); }
+
+}   // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_status_string(int status)
+{
+    switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ENULL: return "a required pointer is NULL";
+    case SSM_EALIGN: return "a pointer is misaligned";
+    case SSM_ECONFIG: return "invalid config";
+    case SSM_ESIZE: return "size out of range";
+    case SSM_EARG: return "argument out of range";
+    case SSM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int ssm_workspace_bytes(const ssm_config *cfg, uint64_t *bytes)
+{
+    const int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!bytes)
+        return SSM_ENULL;
+    *bytes = layout(cfg).total;
+    return SSM_OK;
+}
+
+int ssm_workspace_init(const ssm_config *cfg, void *ws, uint64_t ws_bytes, void *stream)
+{
+    const int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws)
+        return SSM_ENULL;
+    if (!aligned(ws, kAlign))
+        return SSM_EALIGN;
+    const Layout L = layout(cfg);
+    if (ws_bytes < L.total)
+        return SSM_ESIZE;
+    hipStream_t s = (hipStream_t)stream;
+    init_kernel<<<1, 64, 0, s>>>(reinterpret_cast<Hdr *>((uint8_t *)ws + L.hdr));
+    return done(hipGetLastError());
+}
+
+int ssm_candidates(const ssm_config *cfg, void *ws, const int32_t *targets, int64_t T,
+                   const int32_t *perm, int32_t *cand, int32_t *slot, void *stream)
+{
+    const int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !targets || !perm || !cand || !slot)
+        return SSM_ENULL;
+    if (!aligned(ws, kAlign))
+        return SSM_EALIGN;
+    if (T < 0 || T > cfg->max_tokens)
+        return SSM_ESIZE;
+    if (T == 0)
+        return SSM_OK;
+    const Layout L = layout(cfg);
+    uint8_t *w = (uint8_t *)ws;
+    Hdr *h = reinterpret_cast<Hdr *>(w + L.hdr);
+    int32_t *rank = reinterpret_cast<int32_t *>(w + L.rank);
+    int32_t *cnt = reinterpret_cast<int32_t *>(w + L.cnt);
+    const int32_t V = cfg->vocab, C = cfg->candidates;
+    hipStream_t s = (hipStream_t)stream;
+    launch(SSM_PROF_CAND, true, false, cand_clear_kernel, dim3(blocks(V, 256)), dim3(256), s, rank, cnt, V, h);
+    launch(SSM_PROF_CAND, false, false, cand_mark_kernel, dim3(blocks(T > V ? T : V, 256)), dim3(256), s,
+           targets, T, perm, V, rank, cnt, h);
+    launch(SSM_PROF_CAND, false, false, cand_select_kernel, dim3(1), dim3(kSelectThreads), s, perm, V, C,
+           rank, (const int32_t *)cnt, cand, h);
+    launch(SSM_PROF_CAND, false, true, cand_slot_kernel, dim3(blocks(T, 256)), dim3(256), s, targets, T, V,
+           C, (const int32_t *)rank, slot);
+    return done(hipGetLastError());
+}
+
+static int check_loss_args(const ssm_config *cfg, void *ws, const void *X, const void *W,
+                           const int32_t *cand, const int32_t *slot, int64_t T)
+{
+    const int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !X || !W || !cand || !slot)
+        return SSM_ENULL;
+    if (!aligned(ws, kAlign) || !aligned(X, 16) || !aligned(W, 16))
+        return SSM_EALIGN;
+    if (T < 0 || T > cfg->max_tokens)
+        return SSM_ESIZE;
+    return SSM_OK;
+}
+
+int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, const int32_t *cand,
+                 const int32_t *slot, int64_t T, float *loss, float *lse, void *stream)
+{
+    int rc = check_loss_args(cfg, ws, X, W, cand, slot, T);
+    if (rc)
+        return rc;
+    if (!loss || !lse)
+        return SSM_ENULL;
+    if (T == 0)
+        return SSM_OK;
+    const Layout L = layout(cfg);
+    uint8_t *w = (uint8_t *)ws;
+    Hdr *h = reinterpret_cast<Hdr *>(w + L.hdr);
+    const int32_t V = cfg->vocab, C = cfg->candidates;
+    const int64_t Tq = rup(T, kTile);
+    const int nct = (int)(L.Cp / kTile);
+    GemmArgs a{};
+    a.A = Rows{(const uint16_t *)X, kD, nullptr, (int32_t)T, V};
+    a.B = Rows{(const uint16_t *)W, kD, cand, C, V};
+    a.K = kD;
+    a.T = T;
+    a.C = C;
+    a.V = V;
+    a.slot = slot;
+    a.cand = cand;
+    a.zt = reinterpret_cast<float *>(w + L.zt);
+    a.part = reinterpret_cast<float2 *>(w + L.part);
+    a.Tq = Tq;
+    a.Cp = L.Cp;
+    a.h = h;
+    hipStream_t s = (hipStream_t)stream;
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD>, dim3(blocks(Tq, kBM), nct), dim3(256), s, a);
+    launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
+           (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
+    return done(hipGetLastError());
+}
+
+int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, const int32_t *cand,
+                 const int32_t *slot, const float *lse, const float *dloss, int64_t T, float *dX,
+                 float *dW, void *stream)
+{
+    int rc = check_loss_args(cfg, ws, X, W, cand, slot, T);
+    if (rc)
+        return rc;
+    if (!lse || !dloss || !dX || !dW)
+        return SSM_ENULL;
+    if (!aligned(dX, 16) || !aligned(dW, 16))
+        return SSM_EALIGN;
+    if (T == 0)
+        return SSM_OK;
+    const Layout L = layout(cfg);
+    uint8_t *w = (uint8_t *)ws;
+    Hdr *h = reinterpret_cast<Hdr *>(w + L.hdr);
+    const int32_t V = cfg->vocab, C = cfg->candidates;
+    const int64_t Tq = rup(T, kTile), Cp = L.Cp;
+    uint16_t *xt = reinterpret_cast<uint16_t *>(w + L.xt);
+    uint16_t *wst = reinterpret_cast<uint16_t *>(w + L.wst);
+    uint16_t *dz = reinterpret_cast<uint16_t *>(w + L.dz);
+    uint16_t *dzt = reinterpret_cast<uint16_t *>(w + L.dzt);
+    hipStream_t s = (hipStream_t)stream;
+
+    const Rows xr{(const uint16_t *)X, kD, nullptr, (int32_t)T, V};
+    const Rows wr{(const uint16_t *)W, kD, cand, C, V};
+    launch(SSM_PROF_TRANS, true, false, transpose_kernel, dim3(blocks(Tq, 64), kD / 64), dim3(256), s, xr, T,
+           xt, Tq, &h->flags);
+    launch(SSM_PROF_TRANS, false, true, transpose_kernel, dim3(blocks(Cp, 64), kD / 64), dim3(256), s, wr,
+           (int64_t)C, wst, Cp, &h->flags);
+
+    GemmArgs a{};
+    a.T = T;
+    a.C = C;
+    a.V = V;
+    a.slot = slot;
+    a.cand = cand;
+    a.lse = lse;
+    a.g = dloss;
+    a.dz = dz;
+    a.dzt = dzt;
+    a.Tq = Tq;
+    a.Cp = Cp;
+    a.h = h;
+
+    a.A = xr;
+    a.B = wr;
+    a.K = kD;
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ>, dim3(blocks(Tq, kBM), blocks(Cp, kBN)), dim3(256), s,
+           a);
+
+    a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
+    a.B = Rows{wst, Cp, nullptr, kD, V};
+    a.K = Cp;
+    a.out = dX;
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX>, dim3(blocks(Tq, kBM), kD / kBN), dim3(256), s, a);
+
+    a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
+    a.B = Rows{xt, Tq, nullptr, kD, V};
+    a.K = Tq;
+    a.out = dW;
+    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW>, dim3(blocks(Cp, kBM), kD / kBN), dim3(256), s, a);
+    return done(hipGetLastError());
+}
+
+int ssm_device_status(const ssm_config *cfg, const void *ws, uint32_t *flags, int clear, void *stream)
+{
+    const int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !flags)
+        return SSM_ENULL;
+    if (!aligned(ws, kAlign))
+        return SSM_EALIGN;
+    const Layout L = layout(cfg);
+    hipStream_t s = (hipStream_t)stream;
+    const Hdr *h = reinterpret_cast<const Hdr *>((const uint8_t *)ws + L.hdr);
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return SSM_EHIP;
+    if (hipMemcpy(flags, &h->flags, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return SSM_EHIP;
+    if (clear) {
+        flags_clear_kernel<<<1, 64, 0, s>>>(const_cast<Hdr *>(h));
+        if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+            return SSM_EHIP;
+    }
+    return SSM_OK;
+}
+
+int ssm_profile_events(int group, void *start_event, void *stop_event)
+{
+    if (group < 0 || group >= SSM_PROF_GROUPS)
+        return SSM_EARG;
+    g_prof[group].start = (hipEvent_t)start_event;
+    g_prof[group].stop = (hipEvent_t)stop_event;
+    return SSM_OK;
+}
+
+}   // extern "C"

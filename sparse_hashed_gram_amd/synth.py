@@ -98,3 +98,32 @@ def init_rows(w: Workload, channel: int, n_rows: int) -> np.ndarray:
 
 def doc_starts(tok: np.ndarray, eos_id: int) -> np.ndarray:
     return np.flatnonzero(tok == eos_id)
+
+
+# ------------------------------------------------------- sampled softmax
+
+STREAM_SSM_X = 5
+STREAM_SSM_W = 6
+STREAM_SSM_PERM = 7
+STREAM_SSM_G = 8
+SSM_WID = 100   # seed-space id of the sampled-softmax inputs
+
+
+def ssm_inputs(step: int, T: int, V: int, w: Workload | None = None):
+    """Inputs of one sampled-softmax batch, as float32 arrays holding values
+    the caller rounds to bf16 once (X, W) before both sides see them.
+
+    targets: the next tokens of a Zipf stream (``tokens`` of workload w, the
+    full-table stream by default, shifted by one); X: final hidden states,
+    N(0, 1); W: the lm_head, N(0, 0.05) (logits of standard deviation about
+    1.4 at dim 768); perm: a uniform random permutation of [0, V), the
+    randomness the candidate draw uses; g: per-position upstream gradients,
+    uniform in [0.5, 1.5) / T."""
+    from .workloads import FULL
+    w = w or FULL
+    tgt = tokens(w, step, T + 1)[1:].astype(np.int32) % V
+    X = rng(SSM_WID, STREAM_SSM_X, step).standard_normal((T, 768), dtype=np.float32)
+    W = rng(SSM_WID, STREAM_SSM_W, 0).standard_normal((V, 768), dtype=np.float32) * np.float32(0.05)
+    perm = rng(SSM_WID, STREAM_SSM_PERM, step).permutation(V).astype(np.int32)
+    g = (rng(SSM_WID, STREAM_SSM_G, step).random(T) + 0.5).astype(np.float32) / np.float32(max(T, 1))
+    return tgt, X, W, perm, g

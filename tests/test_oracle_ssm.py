@@ -173,3 +173,17 @@ def test_dlogits_rows_sum_to_zero():
     dz = ssm.dlogits(X, W, cand, slot, g)
     np.testing.assert_allclose(dz.sum(1), 0.0, atol=1e-13)
     assert np.all(np.sign(dz[np.arange(len(tgt)), slot]) == -np.sign(g))
+
+
+def test_dW_rows_are_torch_autograd_rows():
+    # the sampled-row form used at full size, against autograd of the loss
+    tgt, perm, X, W, g, C = _case(9)
+    cand, slot, _, _ = ssm.candidates(tgt, perm, len(W), C)
+    _, lse = ssm.loss_fwd(X, W, cand, slot)
+    cs = np.array([0, 3, C // 2, C - 1])
+    rows = ssm.dW_rows(X, W, cand, slot, g, lse, cs)
+    Wt = torch.from_numpy(W).requires_grad_()
+    z = torch.from_numpy(X) @ Wt[torch.from_numpy(cand)].T
+    l = torch.nn.functional.cross_entropy(z, torch.from_numpy(slot), reduction="none")
+    (l * torch.from_numpy(g)).sum().backward()
+    np.testing.assert_allclose(rows, Wt.grad.numpy()[cand[cs]], rtol=1e-12, atol=1e-13)
