@@ -47,7 +47,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed windows")
     ap.add_argument("--warmup", type=int, default=5, help="untimed windows")
-    ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision", "value"])
+    ap.add_argument("--workload", default="full", choices=["tiny", "shard", "full", "collision", "value", "ssm"],
+                    help="ssm: the sampled-softmax loss (include/ssm.h) instead of the n-gram table; "
+                         "one step = candidate set + loss forward + backward of one micro-batch")
+    ap.add_argument("--candidates", type=int, default=10240,
+                    help="ssm: candidate-set size (10240, 14336, 24576 or 50304 in the speedrun)")
+    ap.add_argument("--ssm-tokens", type=int, default=49152,
+                    help="ssm: positions per micro-batch (one GPU's share of the 393,216-token batch)")
     ap.add_argument("--mode", default="burst_ref", choices=["spread", "burst", "burst_ref"],
                     help="spread: each micro-step reduced into the window at once; burst: micro-steps "
                          "kept (dY copied) and reduced with the step; burst_ref: as burst, dY read "
@@ -267,6 +273,136 @@ def cpu_baseline(w, toks_np, T_sample, dys_fn):
                        f"all; table rows as a snapshot of the touched rows)")}
 
 
+SSM_METRIC = "sampled-softmax loss tokens/s (forward + backward); achieved TFLOP/s vs bf16 matrix-core peak"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+SSM_GROUPS = ("cand", "fwd", "lse", "trans", "dz", "dx", "dw")
+
+
+def cpu_baseline_ssm(batches, C, T_sample):
+    """The sampled-softmax oracle (fp64 numpy) on a bounded sample: the first
+    T_sample positions of each batch, all C candidates (candidate set, loss
+    forward, backward)."""
+    import oracle.ssm as orc
+    el = 0.0
+    n = 0
+    for tgt, X, W, perm, g in batches:
+        t, x, gg = tgt[:T_sample], X[:T_sample], g[:T_sample]
+        t0 = time.perf_counter()
+        cand, slot, _, ok = orc.candidates(t, perm, len(W), C)
+        if not ok:
+            continue
+        orc.loss_fwd(x, W, cand, slot)
+        orc.loss_bwd(x, W, cand, slot, gg)
+        el += time.perf_counter() - t0
+        n += len(t)
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    return {"value": n / el if el else None, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": el,
+            "sample": (f"{len(batches)} batch(es) x first {T_sample} positions, all {C} candidates "
+                       f"(candidate set, fp64 loss forward and backward; numpy BLAS threads = {threads})")}
+
+
+def main_ssm(args, torch):
+    """One step = one micro-batch through the sampled-softmax loss: the
+    candidate set, the forward (loss, lse) and the backward (dX, dW[S] +=).
+    Inputs resident in HBM; a few distinct batches cycled."""
+    from sparse_hashed_gram_amd import ssm as S
+    from sparse_hashed_gram_amd import synth
+    from sparse_hashed_gram_amd.hipevents import Event
+
+    torch.cuda.set_device(0)
+    V, T, C, D = 50304, args.ssm_tokens, args.candidates, 768
+    nb = max(1, min(args.distinct_windows, 4))
+    cfg = S.config(V, C, T)
+    ws = S.Workspace(cfg)
+    host = [synth.ssm_inputs(b, T, V) for b in range(nb)]
+    W = torch.from_numpy(host[0][2]).to(torch.bfloat16).cuda()
+    batches = []
+    for tgt, X, _, perm, g in host:
+        batches.append((torch.from_numpy(tgt).cuda(), torch.from_numpy(X).to(torch.bfloat16).cuda(),
+                        torch.from_numpy(perm).cuda(), torch.from_numpy(g).cuda()))
+    cand = torch.empty(C, dtype=torch.int32, device="cuda")
+    slot = torch.empty(T, dtype=torch.int32, device="cuda")
+    loss = torch.empty(T, dtype=torch.float32, device="cuda")
+    lse = torch.empty(T, dtype=torch.float32, device="cuda")
+    dX = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    dW = torch.zeros((V, D), dtype=torch.float32, device="cuda")
+
+    def run(k, ev=None):
+        if ev is not None:
+            for gi, name in enumerate(SSM_GROUPS):
+                a, b = Event(), Event()
+                ev[name].append((a, b))
+                S.profile_events(gi, a.handle, b.handle)
+        tgt, X, perm, g = batches[k]
+        S.candidates(cfg, ws, tgt, perm, cand, slot)
+        S.loss_fwd(cfg, ws, X, W, cand, slot, loss, lse)
+        S.loss_bwd(cfg, ws, X, W, cand, slot, lse, g, dW, dX)
+        if ev is not None:
+            for gi in range(S.PROF_GROUPS):
+                S.profile_events(gi, None, None)
+
+    for i in range(args.warmup):
+        run(i % nb)
+    torch.cuda.synchronize()
+    ev = {n: [] for n in SSM_GROUPS}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i % nb, ev)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    flags = S.device_status(cfg, ws)
+    if flags:
+        print(f"bench.py: sampled-softmax device flags {flags:#x} set", file=sys.stderr)
+        sys.exit(1)
+    flop = 2.0 * T * C * D   # one contraction over the batch and the candidate set
+    kflop = {"fwd": flop, "dz": flop, "dx": flop, "dw": flop}
+    kernels = {}
+    for name in SSM_GROUPS:
+        ms_l = [a.elapsed_ms(b) for a, b in ev[name]]
+        q1, med, q3 = (float(x) for x in np.percentile(ms_l, [25, 50, 75]))
+        k = {"ms_per_launch": round(float(np.mean(ms_l)), 4), "ms_median": round(med, 4),
+             "ms_iqr": round(q3 - q1, 4), "timed_launches": len(ms_l)}
+        if name in kflop:
+            tf = kflop[name] / (np.mean(ms_l) * 1e-3) / 1e12
+            k.update({"flop_per_launch": kflop[name], "achieved_tflops": round(tf, 1),
+                      "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        kernels[name] = k
+    dom = max(kflop, key=lambda n: kernels[n]["ms_per_launch"])
+    ms_step = el / args.steps * 1e3
+    res = {
+        "metric": SSM_METRIC,
+        "value": round(T * args.steps / el, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Zipf next-token targets, N(0,1) hidden states, N(0,0.05) lm_head",
+        "config": {"workload": f"sampled softmax: {T} positions x {C} candidates of a {V}-id vocabulary, "
+                               f"dim {D}", "tokens_per_micro_step": T, "candidates": C, "vocab": V,
+                   "dim": D},
+        # forward + backward contractions the method needs (the backward's
+        # recomputed logits are not counted)
+        "path_tflops": round(3 * flop / (ms_step * 1e-3) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved_tflops"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": kernels[dom]["frac_of_mfma_peak"], "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del ws, dW, dX, batches
+        torch.cuda.empty_cache()
+        Ts = args.cpu_tokens if args.cpu_tokens > 0 else 4096
+        res["cpu_baseline"] = cpu_baseline_ssm(host[:2], C, min(T, Ts))
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +426,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_copy": 4 * n, "copies": 3, "ms_per_copy": ms,
                           "copy_gbps_read_plus_write": round(8 * n / (min(ms) * 1e-3) / 1e9, 1)}))
         return
+
+    if args.workload == "ssm":
+        return main_ssm(args, torch)
 
     from sparse_hashed_gram_amd import ngram as N
     from sparse_hashed_gram_amd import synth
