@@ -11,9 +11,9 @@
 //
 // Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // k-contiguous in memory (the backward's transposed operands are written
-// first), so one main loop serves all three: a 128 x 128 block tile, k-steps
-// of 64 through double-buffered LDS, four wavefronts of 64 x 64 (2 x 2
-// matrix-core tiles of 32 x 32).
+// first), so one main loop serves all three: a 128 x 128 block tile staged
+// through double-buffered LDS, four wavefronts of 64 x 64 (2 x 2 matrix-core
+// tiles of 32 x 32).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -28,14 +28,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdk = kBK + 8;   // bf16 per LDS operand row: 144 B, 16-byte reads conflict-free
-constexpr int kLdt = kBN + 4;   // fp32 per row of the forward's epilogue tile
-constexpr int kLdb = kBN + 8;   // bf16 per row of the dz epilogue tile
+constexpr int kLdt = 128 + 4;   // fp32 per row of the forward's epilogue tile
+constexpr int kLdb = 128 + 8;   // bf16 per row of the dz epilogue tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
-constexpr uint32_t kSmem = 2u * (kBM + kBN) * kLdk * 2u;   // 73,728 B
-static_assert(kBM * kLdt * 4 + kBM * 8 <= (int)kSmem, "forward epilogue fits");
-static_assert(kBM * kLdb * 2 + 3 * kBM * 4 <= (int)kSmem, "dz epilogue fits");
+// Tile shapes per contraction (measured on MI355X at 49,152 x 10,240 x 768):
+// the forward and dz contractions run k = 768 only, so their prologue and
+// softmax epilogue weigh more; k-steps of 32 (40 KB of LDS, three blocks per
+// CU) hide them best.  dX and dW run k = C and k = T; k-steps of 64 (two
+// blocks per CU) halve their barriers.
+constexpr int kFwdBK = 32, kDzBK = 32, kDxBK = 64, kDwBK = 64;
+
+// Block tile of a contraction: four wavefronts, 2 along M x 2 along N; a
+// wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
+// by 64 columns).  BK: k-elements staged per LDS buffer (two buffers).
+template <int WMB, int BK>
+struct Tile {
+    static constexpr int BM = 2 * WMB * 32, BN = 128;
+    static constexpr int LDK = BK + 8;                  // bf16 per LDS operand row (16-byte reads conflict-free)
+    static constexpr int CH = BK / 8;                   // 16-byte chunks per row per k-step
+    static constexpr int RP = 256 / CH;                 // rows one pass of the block's loads covers
+    static constexpr int LA = BM / RP, LB = BN / RP;    // 16-byte loads per thread per operand
+    static constexpr uint32_t SMEM = 2u * (BM + BN) * LDK * 2u;
+};
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
 constexpr int kSelectThreads = 1024;
@@ -277,84 +291,90 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 }
 
 // acc[mb][nb] = the wavefront's 32 x 32 tiles of C[m0 + ..][n0 + ..]; K is a
-// multiple of kBK.  Ends with a block barrier (LDS free for the epilogue).
+// multiple of BK.  Ends with a block barrier (LDS free for the epilogue).
+template <int WMB, int BK>
 __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
-                                uint16_t *sm, f32x16 (&acc)[2][2], uint32_t *flags)
+                                uint16_t *sm, f32x16 (&acc)[WMB][2], uint32_t *flags)
 {
+    using TL = Tile<WMB, BK>;
+    constexpr int LDK = TL::LDK;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int wm = w >> 1, wn = w & 1;
-    const int lr = t >> 3, lc = (t & 7) * 8;   // loader: rows lr + 32 j, 16 bytes at column lc
-    const uint16_t *pa[4], *pb[4];
+    const int lr = t / TL::CH, lc = (t % TL::CH) * 8;   // loader: rows lr + RP j, 16 bytes at column lc
+    const uint16_t *pa[TL::LA], *pb[TL::LB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        pa[j] = row_ptr(A, m0 + lr + 32 * j, flags) + lc;
-        pb[j] = row_ptr(B, n0 + lr + 32 * j, flags) + lc;
-    }
-    uint16_t *As = sm, *Bs = sm + 2 * kBM * kLdk;
+    for (int j = 0; j < TL::LA; ++j)
+        pa[j] = row_ptr(A, m0 + lr + TL::RP * j, flags) + lc;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int j = 0; j < TL::LB; ++j)
+        pb[j] = row_ptr(B, n0 + lr + TL::RP * j, flags) + lc;
+    uint16_t *As = sm, *Bs = sm + 2 * TL::BM * LDK;
+#pragma unroll
+    for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[mb][nb][e] = 0.f;
 
-    u32x4 ra[4], rb[4];
+    u32x4 ra[TL::LA], rb[TL::LB];
+    auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        ra[j] = *(const u32x4 *)pa[j];
-        rb[j] = *(const u32x4 *)pb[j];
-    }
+        for (int j = 0; j < TL::LA; ++j)
+            ra[j] = *(const u32x4 *)(pa[j] + k0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        *(u32x4 *)(As + (lr + 32 * j) * kLdk + lc) = ra[j];
-        *(u32x4 *)(Bs + (lr + 32 * j) * kLdk + lc) = rb[j];
-    }
+        for (int j = 0; j < TL::LB; ++j)
+            rb[j] = *(const u32x4 *)(pb[j] + k0);
+    };
+    auto sstore = [&](int buf) {
+        uint16_t *an = As + buf * TL::BM * LDK, *bn = Bs + buf * TL::BN * LDK;
+#pragma unroll
+        for (int j = 0; j < TL::LA; ++j)
+            *(u32x4 *)(an + (lr + TL::RP * j) * LDK + lc) = ra[j];
+#pragma unroll
+        for (int j = 0; j < TL::LB; ++j)
+            *(u32x4 *)(bn + (lr + TL::RP * j) * LDK + lc) = rb[j];
+    };
+    gload(0);
+    sstore(0);
     __syncthreads();
 
-    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
-    const int64_t nk = K / kBK;
+    const int ar = wm * WMB * 32 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
+    const int64_t nk = K / BK;
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int cur = (int)(kt & 1);
         const bool more = kt + 1 < nk;
-        if (more) {
-            const int64_t k0 = (kt + 1) * kBK;
+        if (more)
+            gload((kt + 1) * BK);
+        const uint16_t *as = As + cur * TL::BM * LDK, *bs = Bs + cur * TL::BN * LDK;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                ra[j] = *(const u32x4 *)(pa[j] + k0);
-                rb[j] = *(const u32x4 *)(pb[j] + k0);
-            }
-        }
-        const uint16_t *as = As + cur * kBM * kLdk, *bs = Bs + cur * kBN * kLdk;
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8 a[WMB], b[2];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 16) {
-            const bf16x8 a0 = *(const bf16x8 *)(as + ar * kLdk + kk + kh);
-            const bf16x8 a1 = *(const bf16x8 *)(as + (ar + 32) * kLdk + kk + kh);
-            const bf16x8 b0 = *(const bf16x8 *)(bs + br * kLdk + kk + kh);
-            const bf16x8 b1 = *(const bf16x8 *)(bs + (br + 32) * kLdk + kk + kh);
-            acc[0][0] = mfma(a0, b0, acc[0][0]);
-            acc[0][1] = mfma(a0, b1, acc[0][1]);
-            acc[1][0] = mfma(a1, b0, acc[1][0]);
-            acc[1][1] = mfma(a1, b1, acc[1][1]);
-        }
-        if (more) {
-            uint16_t *an = As + (cur ^ 1) * kBM * kLdk, *bn = Bs + (cur ^ 1) * kBN * kLdk;
+            for (int mb = 0; mb < WMB; ++mb)
+                a[mb] = *(const bf16x8 *)(as + (ar + 32 * mb) * LDK + kk + kh);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *(u32x4 *)(an + (lr + 32 * j) * kLdk + lc) = ra[j];
-                *(u32x4 *)(bn + (lr + 32 * j) * kLdk + lc) = rb[j];
-            }
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb] = *(const bf16x8 *)(bs + (br + 32 * nb) * LDK + kk + kh);
+#pragma unroll
+            for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
         }
+        if (more)
+            sstore(cur ^ 1);
         __syncthreads();
     }
 }
 
 // Position of acc[mb][nb][e] in the block tile (32 x 32 matrix-core layout:
 // lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4).
+template <int WMB>
 __device__ inline int tile_row(int mb, int e)
 {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return wm * 64 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    return wm * WMB * 32 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
 __device__ inline int tile_col(int nb)
 {
@@ -392,63 +412,86 @@ struct GemmArgs {
     Hdr *h;
 };
 
-template <int EPI>
+constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
+
+template <int EPI, int WMB, int BK>
+constexpr uint32_t smem_bytes()
+{
+    return EPI == EPI_FWD ? cmax(Tile<WMB, BK>::SMEM, 64 * kLdt * 4 + 4 * 64 * 8)
+         : EPI == EPI_DZ  ? cmax(Tile<WMB, BK>::SMEM, 128 * kLdb * 2 + 3 * 128 * 4)
+                          : Tile<WMB, BK>::SMEM;
+}
+
+template <int EPI, int WMB, int BK>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
-    __shared__ __align__(16) uint8_t smem[kSmem];
-    const int64_t m0 = (int64_t)blockIdx.x * kBM, n0 = (int64_t)blockIdx.y * kBN;
-    f32x16 acc[2][2];
-    mainloop(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    static_assert(EPI == EPI_DX || EPI == EPI_DW || WMB == 2, "the softmax epilogues take 128-row tiles");
+    using TL = Tile<WMB, BK>;
+    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK>()];
+    const int64_t m0 = (int64_t)blockIdx.x * TL::BM, n0 = (int64_t)blockIdx.y * TL::BN;
+    f32x16 acc[WMB][2];
+    mainloop<WMB, BK>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
-        float *tile = reinterpret_cast<float *>(smem);
+        // two halves of 64 rows; wavefront q takes columns 32q .. 32q + 32 of
+        // every row of the half, and the four quarters meet in LDS
+        float *tile = reinterpret_cast<float *>(smem);                      // [64][kLdt]
+        float2 *pq = reinterpret_cast<float2 *>(smem + 64 * kLdt * 4);      // [4][64]
+        const int w = t >> 6, r = t & 63, q = w, wm = w >> 1;
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    tile[tile_row(mb, e) * kLdt + tile_col(nb)] = acc[mb][nb][e];
-        __syncthreads();
-        // thread: row r, columns hf*64 .. +64; the two halves meet in LDS
-        const int r = t & 127, hf = t >> 7;
-        const int64_t i = m0 + r, c0 = n0 + hf * 64;
-        const int64_t left = (int64_t)a.C - c0;
-        const int nv = left <= 0 ? 0 : (left >= 64 ? 64 : (int)left);
-        const float *zr = tile + r * kLdt + hf * 64;
-        float m = -INFINITY, s = 0.f;
-        if (nv > 0) {
-            for (int k = 0; k < 64; ++k)
-                if (k < nv)
-                    m = fmaxf(m, zr[k]);
-            for (int k = 0; k < 64; ++k)
-                if (k < nv)
-                    s += __expf(zr[k] - m);
-        }
-        if (i < a.T) {
-            const int64_t y = a.slot[i];
-            if (y >= c0 && y < c0 + nv)
-                a.zt[i] = zr[y - c0];
-        }
-        float2 *pr = reinterpret_cast<float2 *>(smem + kBM * kLdt * 4);
-        if (hf == 1)
-            pr[r] = make_float2(m, s);
-        __syncthreads();
-        if (hf == 0 && i < a.T) {
-            const float2 o = pr[r];
-            const float M = fmaxf(m, o.x);
-            float S = s * __expf(m - M);
-            if (o.y > 0.f)
-                S += o.y * __expf(o.x - M);
-            a.part[(int64_t)blockIdx.y * a.T + i] = make_float2(M, S);
+                        for (int e = 0; e < 16; ++e)
+                            tile[(tile_row<2>(mb, e) - 64 * h) * kLdt + tile_col(nb)] = acc[mb][nb][e];
+            }
+            __syncthreads();
+            const int64_t i = m0 + 64 * h + r, c0 = n0 + 32 * q;
+            const int64_t left = (int64_t)a.C - c0;
+            const int nv = left <= 0 ? 0 : (left >= 32 ? 32 : (int)left);
+            const float *zr = tile + r * kLdt + 32 * q;
+            float m = -INFINITY, s = 0.f;
+            if (nv > 0) {
+                for (int k = 0; k < 32; ++k)
+                    if (k < nv)
+                        m = fmaxf(m, zr[k]);
+                for (int k = 0; k < 32; ++k)
+                    if (k < nv)
+                        s += __expf(zr[k] - m);
+            }
+            if (i < a.T) {
+                const int64_t y = a.slot[i];
+                if (y >= c0 && y < c0 + nv)
+                    a.zt[i] = zr[y - c0];
+            }
+            pq[q * 64 + r] = make_float2(m, s);
+            __syncthreads();
+            if (q == 0 && i < a.T) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    M = fmaxf(M, pq[k * 64 + r].x);
+                float S = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float2 o = pq[k * 64 + r];
+                    if (o.y > 0.f)
+                        S += o.y * __expf(o.x - M);
+                }
+                a.part[(int64_t)blockIdx.y * a.T + i] = make_float2(M, S);
+            }
+            __syncthreads();
         }
     } else if constexpr (EPI == EPI_DZ) {
-        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [kBM][kLdb] bf16
-        float *s_l = reinterpret_cast<float *>(smem + kBM * kLdb * 2);
-        float *s_g = s_l + kBM;
-        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + kBM);
-        if (t < kBM) {
+        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
+        float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
+        float *s_g = s_l + 128;
+        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
+        if (t < 128) {
             const int64_t i = m0 + t;
             const bool ok = i < a.T && a.h->void_batch == 0;
             s_l[t] = ok ? a.lse[i] : 0.f;
@@ -457,12 +500,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         }
         __syncthreads();
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int rr = tile_row(mb, e), cc = tile_col(nb);
+                    const int rr = tile_row<WMB>(mb, e), cc = tile_col(nb);
                     const int64_t c = n0 + cc;
                     float d = 0.f;   // padding rows and columns, and a void batch, give 0
                     if (c < a.C && s_g[rr] != 0.f) {
@@ -492,10 +535,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t i = m0 + tile_row(mb, e);
+                const int64_t i = m0 + tile_row<WMB>(mb, e);
                 if (i < a.T) {
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
@@ -504,10 +547,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             }
     } else {   // EPI_DW
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t c = m0 + tile_row(mb, e);
+                const int64_t c = m0 + tile_row<WMB>(mb, e);
                 if (c < a.C) {
                     const int32_t v = a.cand[c];
                     if ((uint32_t)v < (uint32_t)a.V) {
@@ -736,7 +779,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.Cp = L.Cp;
     a.h = h;
     hipStream_t s = (hipStream_t)stream;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD>, dim3(blocks(Tq, kBM), nct), dim3(256), s, a);
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK>, dim3(blocks(Tq, 128), nct), dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
     return done(hipGetLastError());
@@ -790,20 +833,20 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.A = xr;
     a.B = wr;
     a.K = kD;
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ>, dim3(blocks(Tq, kBM), blocks(Cp, kBN)), dim3(256), s,
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK>, dim3(blocks(Tq, 128), blocks(Cp, 128)), dim3(256), s,
            a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
     a.B = Rows{wst, Cp, nullptr, kD, V};
     a.K = Cp;
     a.out = dX;
-    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX>, dim3(blocks(Tq, kBM), kD / kBN), dim3(256), s, a);
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK>, dim3(blocks(Tq, Tile<2, kDxBK>::BM), kD / 128), dim3(256), s, a);
 
     a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
     a.B = Rows{xt, Tq, nullptr, kD, V};
     a.K = Tq;
     a.out = dW;
-    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW>, dim3(blocks(Cp, kBM), kD / kBN), dim3(256), s, a);
+    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK>, dim3(blocks(Cp, Tile<2, kDwBK>::BM), kD / 128), dim3(256), s, a);
     return done(hipGetLastError());
 }
 
