@@ -391,6 +391,42 @@ __device__ inline uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Block -> output tile.  The hardware hands consecutive workgroups to the 8
+// XCDs in turn; each XCD is given a contiguous range of tiles instead, walked
+// in groups of 8 M-tiles (all N-tiles of a group before the next group), so
+// the blocks resident on one XCD share their A and B tiles in its L2 and the
+// last-level cache sees each operand tile while its users still run.
+constexpr uint32_t kXcds = 8, kGroupM = 8;
+
+__host__ __device__ inline uint32_t grid_blocks(uint32_t nM, uint32_t nN)
+{
+    return kXcds * ((nM * nN + kXcds - 1) / kXcds);
+}
+
+// The dz kernel keeps the plain order (M-tiles fastest): its two bf16 output
+// layouts were written faster that way (measured).
+template <bool GROUPED>
+__device__ inline bool tile_of(uint32_t nM, uint32_t nN, uint32_t &mt, uint32_t &nt)
+{
+    if (!GROUPED) {
+        if (blockIdx.x >= nM * nN)
+            return false;
+        mt = blockIdx.x % nM;
+        nt = blockIdx.x / nM;
+        return true;
+    }
+    const uint32_t total = nM * nN, per = (total + kXcds - 1) / kXcds;
+    const uint32_t tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (tile >= total)
+        return false;
+    const uint32_t span = kGroupM * nN, g = tile / span, first = g * kGroupM;
+    const uint32_t gm = nM - first < kGroupM ? nM - first : kGroupM;
+    const uint32_t r = tile - g * span;
+    mt = first + r % gm;
+    nt = r / gm;
+    return true;
+}
+
 enum { EPI_FWD = 0, EPI_DZ = 1, EPI_DX = 2, EPI_DW = 3 };
 
 struct GemmArgs {
@@ -408,6 +444,7 @@ struct GemmArgs {
     uint16_t *dz;          // [Tq][Cp] bf16
     uint16_t *dzt;         // [Cp][Tq] bf16
     int64_t Tq, Cp;
+    uint32_t tiles_m, tiles_n;   // output tiles (block tile BM x 128)
     float *out;            // dX [T][768] or dW [V][768]
     Hdr *h;
 };
@@ -428,7 +465,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     static_assert(EPI == EPI_DX || EPI == EPI_DW || WMB == 2, "the softmax epilogues take 128-row tiles");
     using TL = Tile<WMB, BK>;
     __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK>()];
-    const int64_t m0 = (int64_t)blockIdx.x * TL::BM, n0 = (int64_t)blockIdx.y * TL::BN;
+    uint32_t mt, nt;
+    if (!tile_of<EPI != EPI_DZ>(a.tiles_m, a.tiles_n, mt, nt))
+        return;   // the whole block: no barrier is reached
+    const int64_t m0 = (int64_t)mt * TL::BM, n0 = (int64_t)nt * TL::BN;
     f32x16 acc[WMB][2];
     mainloop<WMB, BK>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
     const int t = threadIdx.x;
@@ -482,7 +522,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                     if (o.y > 0.f)
                         S += o.y * __expf(o.x - M);
                 }
-                a.part[(int64_t)blockIdx.y * a.T + i] = make_float2(M, S);
+                a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
             }
             __syncthreads();
         }
@@ -779,7 +819,10 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.Cp = L.Cp;
     a.h = h;
     hipStream_t s = (hipStream_t)stream;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK>, dim3(blocks(Tq, 128), nct), dim3(256), s, a);
+    a.tiles_m = blocks(Tq, 128);
+    a.tiles_n = (uint32_t)nct;
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+           dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
     return done(hipGetLastError());
@@ -833,20 +876,28 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.A = xr;
     a.B = wr;
     a.K = kD;
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK>, dim3(blocks(Tq, 128), blocks(Cp, 128)), dim3(256), s,
-           a);
+    a.tiles_m = blocks(Tq, 128);
+    a.tiles_n = blocks(Cp, 128);
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+           dim3(256), s, a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
     a.B = Rows{wst, Cp, nullptr, kD, V};
     a.K = Cp;
     a.out = dX;
-    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK>, dim3(blocks(Tq, Tile<2, kDxBK>::BM), kD / 128), dim3(256), s, a);
+    a.tiles_m = blocks(Tq, Tile<2, kDxBK>::BM);
+    a.tiles_n = kD / 128;
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+           dim3(256), s, a);
 
     a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
     a.B = Rows{xt, Tq, nullptr, kD, V};
     a.K = Tq;
     a.out = dW;
-    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK>, dim3(blocks(Cp, Tile<2, kDwBK>::BM), kD / 128), dim3(256), s, a);
+    a.tiles_m = blocks(Cp, Tile<2, kDwBK>::BM);
+    a.tiles_n = kD / 128;
+    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+           dim3(256), s, a);
     return done(hipGetLastError());
 }
 
