@@ -539,20 +539,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             s_y[t] = ok ? a.slot[i] : -1;
         }
         __syncthreads();
+        // a lane holds 4 consecutive rows of one column per group of 4
+        // accumulator entries: 4 adjacent elements of a transposed row, stored
+        // from registers; the row-major copy goes through LDS
 #pragma unroll
         for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int rr = tile_row<WMB>(mb, e), cc = tile_col(nb);
+                for (int e4 = 0; e4 < 16; e4 += 4) {
+                    const int cc = tile_col(nb), r4 = tile_row<WMB>(mb, e4);
                     const int64_t c = n0 + cc;
-                    float d = 0.f;   // padding rows and columns, and a void batch, give 0
-                    if (c < a.C && s_g[rr] != 0.f) {
-                        const float p = __expf(acc[mb][nb][e] - s_l[rr]);
-                        d = s_g[rr] * (p - (s_y[rr] == c ? 1.f : 0.f));
+                    uint16_t h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int rr = r4 + j;
+                        float d = 0.f;   // padding rows and columns, and a void batch, give 0
+                        if (c < a.C && s_g[rr] != 0.f) {
+                            const float p = __expf(acc[mb][nb][e4 + j] - s_l[rr]);
+                            d = s_g[rr] * (p - (s_y[rr] == c ? 1.f : 0.f));
+                        }
+                        h[j] = bf16_rne(d);
+                        bt[rr * kLdb + cc] = h[j];
                     }
-                    bt[rr * kLdb + cc] = bf16_rne(d);
+                    *(uint2 *)(a.dzt + (n0 + cc) * a.Tq + m0 + r4) =
+                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
                 }
         __syncthreads();
         // row-major: 16 chunks of 16 B per row
@@ -561,17 +572,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             const int rr = (t >> 4) + 16 * p, q = t & 15;
             const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
             *(u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8) = v;
-        }
-        // transposed: column cc, rows hf*64 .. +64 in chunks of 8
-        const int cc = t & 127, r0 = (t >> 7) * 64;
-#pragma unroll
-        for (int k = 0; k < 64; k += 8) {
-            uint32_t wv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                wv[e] = (uint32_t)bt[(r0 + k + 2 * e) * kLdb + cc] |
-                        ((uint32_t)bt[(r0 + k + 2 * e + 1) * kLdb + cc] << 16);
-            *(u32x4 *)(a.dzt + (n0 + cc) * a.Tq + m0 + r0 + k) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
