@@ -300,3 +300,49 @@ def test_full_size_sampled(C):
     # rows outside the candidate set stay zero
     out = np.setdiff1d(rs.integers(0, V, 4000), cand_o)[:500]
     assert not np.any(dW.cpu().numpy()[out])
+
+
+def test_graph_replay_equals_eager():
+    # candidate set, forward and backward captured once in a HIP graph and
+    # replayed on new batches copied into the captured buffers; every replay
+    # equals the same calls run eagerly, bitwise (dW accumulates in both)
+    N = S()
+    T, C, V = 1000, 1500, V_SMALL
+    cfg = N.config(V, C, T)
+    ws_g, ws_e = N.Workspace(cfg), N.Workspace(cfg)
+    _, _, W, _, _ = _inputs(0, T, V)
+    Wd = _dev_bf16(W)
+    tgt_s = torch.zeros(T, dtype=torch.int32, device="cuda")
+    perm_s = torch.zeros(V, dtype=torch.int32, device="cuda")
+    X_s = torch.zeros((T, 768), dtype=torch.bfloat16, device="cuda")
+    g_s = torch.zeros(T, dtype=torch.float32, device="cuda")
+    cand_s = torch.empty(C, dtype=torch.int32, device="cuda")
+    slot_s = torch.empty(T, dtype=torch.int32, device="cuda")
+    loss_s = torch.empty(T, dtype=torch.float32, device="cuda")
+    lse_s = torch.empty(T, dtype=torch.float32, device="cuda")
+    dX_s = torch.empty((T, 768), dtype=torch.float32, device="cuda")
+    dW_g = torch.zeros((V, 768), dtype=torch.float32, device="cuda")
+    dW_e = torch.zeros((V, 768), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        N.candidates(cfg, ws_g, tgt_s, perm_s, cand_s, slot_s)
+        N.loss_fwd(cfg, ws_g, X_s, Wd, cand_s, slot_s, loss_s, lse_s)
+        N.loss_bwd(cfg, ws_g, X_s, Wd, cand_s, slot_s, lse_s, g_s, dW_g, dX_s)
+    for step in range(3):
+        tgt, X, _, perm, g = _inputs(400 + step, T, V)
+        tgt_s.copy_(_dev(tgt))
+        perm_s.copy_(_dev(perm))
+        X_s.copy_(_dev_bf16(X))
+        g_s.copy_(_dev(g))
+        graph.replay()
+        cand, slot = N.candidates(cfg, ws_e, _dev(tgt), _dev(perm))
+        loss, lse = N.loss_fwd(cfg, ws_e, _dev_bf16(X), Wd, cand, slot)
+        dX = N.loss_bwd(cfg, ws_e, _dev_bf16(X), Wd, cand, slot, lse, _dev(g), dW_e)
+        torch.cuda.synchronize()
+        for a, b in ((cand_s, cand), (slot_s, slot), (loss_s, loss), (lse_s, lse), (dX_s, dX), (dW_g, dW_e)):
+            assert torch.equal(a, b), f"replay {step} differs"
+        junk = torch.randn(1 << 16, device="cuda").sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
+    assert N.device_status(cfg, ws_g) == 0 and N.device_status(cfg, ws_e) == 0
