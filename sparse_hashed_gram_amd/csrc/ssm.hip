@@ -12,8 +12,8 @@
 // Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // k-contiguous in memory (the backward's transposed operands are written
 // first), so one main loop serves all three: a 128 x 128 block tile staged
-// through double-buffered LDS, four wavefronts of 64 x 64 (2 x 2 matrix-core
-// tiles of 32 x 32).
+// through LDS (one or two buffers), four wavefronts of 64 x 64 (2 x 2
+// matrix-core tiles of 32 x 32).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,23 +32,25 @@ constexpr int kLdt = 128 + 4;   // fp32 per row of the forward's epilogue tile
 constexpr int kLdb = 128 + 8;   // bf16 per row of the dz epilogue tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Tile shapes per contraction (measured on MI355X at 49,152 x 10,240 x 768):
-// the forward and dz contractions run k = 768 only, so their prologue and
-// softmax epilogue weigh more; k-steps of 32 (40 KB of LDS, three blocks per
-// CU) hide them best.  dX and dW run k = C and k = T; k-steps of 64 (two
-// blocks per CU) halve their barriers.
-constexpr int kFwdBK = 32, kDzBK = 32, kDxBK = 64, kDwBK = 64;
+// the forward runs k = 768 with a heavy softmax epilogue; k-steps of 32 in
+// two LDS buffers (40 KB, three blocks per CU) suit it best.  dz and dX take
+// k-steps of 64 in one LDS buffer (37 KB, three blocks per CU, two barriers
+// per step); dW, k = T, keeps two buffers of 64.
+constexpr int kFwdBK = 32, kDzBK = 64, kDxBK = 64, kDwBK = 64;
+constexpr bool kFwdSingle = false, kDzSingle = true, kDxSingle = true, kDwSingle = false;
 
 // Block tile of a contraction: four wavefronts, 2 along M x 2 along N; a
 // wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
 // by 64 columns).  BK: k-elements staged per LDS buffer (two buffers).
-template <int WMB, int BK>
+template <int WMB, int BK, bool SINGLE = false>   // SINGLE: one LDS buffer (register prefetch only)
 struct Tile {
     static constexpr int BM = 2 * WMB * 32, BN = 128;
+    static constexpr int NBUF = SINGLE ? 1 : 2;
     static constexpr int LDK = BK + 8;                  // bf16 per LDS operand row (16-byte reads conflict-free)
     static constexpr int CH = BK / 8;                   // 16-byte chunks per row per k-step
     static constexpr int RP = 256 / CH;                 // rows one pass of the block's loads covers
     static constexpr int LA = BM / RP, LB = BN / RP;    // 16-byte loads per thread per operand
-    static constexpr uint32_t SMEM = 2u * (BM + BN) * LDK * 2u;
+    static constexpr uint32_t SMEM = NBUF * (BM + BN) * LDK * 2u;
 };
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
@@ -292,11 +294,11 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 
 // acc[mb][nb] = the wavefront's 32 x 32 tiles of C[m0 + ..][n0 + ..]; K is a
 // multiple of BK.  Ends with a block barrier (LDS free for the epilogue).
-template <int WMB, int BK>
+template <int WMB, int BK, bool SINGLE>
 __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
                                 uint16_t *sm, f32x16 (&acc)[WMB][2], uint32_t *flags)
 {
-    using TL = Tile<WMB, BK>;
+    using TL = Tile<WMB, BK, SINGLE>;
     constexpr int LDK = TL::LDK;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int wm = w >> 1, wn = w & 1;
@@ -308,7 +310,7 @@ __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t
 #pragma unroll
     for (int j = 0; j < TL::LB; ++j)
         pb[j] = row_ptr(B, n0 + lr + TL::RP * j, flags) + lc;
-    uint16_t *As = sm, *Bs = sm + 2 * TL::BM * LDK;
+    uint16_t *As = sm, *Bs = sm + TL::NBUF * TL::BM * LDK;
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
@@ -341,6 +343,34 @@ __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t
 
     const int ar = wm * WMB * 32 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
     const int64_t nk = K / BK;
+    if constexpr (SINGLE) {
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk;
+            if (more)
+                gload((kt + 1) * BK);
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 16) {
+                bf16x8 a[WMB], b[2];
+#pragma unroll
+                for (int mb = 0; mb < WMB; ++mb)
+                    a[mb] = *(const bf16x8 *)(As + (ar + 32 * mb) * LDK + kk + kh);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    b[nb] = *(const bf16x8 *)(Bs + (br + 32 * nb) * LDK + kk + kh);
+#pragma unroll
+                for (int mb = 0; mb < WMB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+            }
+            __syncthreads();   // every wavefront is done reading the buffer
+            if (more) {
+                sstore(0);
+                __syncthreads();
+            }
+        }
+        return;
+    }
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int cur = (int)(kt & 1);
         const bool more = kt + 1 < nk;
@@ -451,26 +481,26 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
-template <int EPI, int WMB, int BK>
+template <int EPI, int WMB, int BK, bool SINGLE>
 constexpr uint32_t smem_bytes()
 {
-    return EPI == EPI_FWD ? cmax(Tile<WMB, BK>::SMEM, 64 * kLdt * 4 + 4 * 64 * 8)
-         : EPI == EPI_DZ  ? cmax(Tile<WMB, BK>::SMEM, 128 * kLdb * 2 + 3 * 128 * 4)
-                          : Tile<WMB, BK>::SMEM;
+    return EPI == EPI_FWD ? cmax(Tile<WMB, BK, SINGLE>::SMEM, 64 * kLdt * 4 + 4 * 64 * 8)
+         : EPI == EPI_DZ  ? cmax(Tile<WMB, BK, SINGLE>::SMEM, 128 * kLdb * 2 + 3 * 128 * 4)
+                          : Tile<WMB, BK, SINGLE>::SMEM;
 }
 
-template <int EPI, int WMB, int BK>
+template <int EPI, int WMB, int BK, bool SINGLE = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
     static_assert(EPI == EPI_DX || EPI == EPI_DW || WMB == 2, "the softmax epilogues take 128-row tiles");
-    using TL = Tile<WMB, BK>;
-    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK>()];
+    using TL = Tile<WMB, BK, SINGLE>;
+    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK, SINGLE>()];
     uint32_t mt, nt;
     if (!tile_of<EPI != EPI_DZ>(a.tiles_m, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
     const int64_t m0 = (int64_t)mt * TL::BM, n0 = (int64_t)nt * TL::BN;
     f32x16 acc[WMB][2];
-    mainloop<WMB, BK>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    mainloop<WMB, BK, SINGLE>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
@@ -821,7 +851,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     hipStream_t s = (hipStream_t)stream;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = (uint32_t)nct;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK, kFwdSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
@@ -878,7 +908,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.K = kD;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = blocks(Cp, 128);
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK, kDzSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
@@ -887,7 +917,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.out = dX;
     a.tiles_m = blocks(Tq, Tile<2, kDxBK>::BM);
     a.tiles_n = kD / 128;
-    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK, kDxSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
 
     a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
@@ -896,7 +926,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.out = dW;
     a.tiles_m = blocks(Cp, Tile<2, kDwBK>::BM);
     a.tiles_n = kD / 128;
-    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     return done(hipGetLastError());
 }
