@@ -91,6 +91,7 @@ WsLayout layout(const ngram_config *c)
     L.wrows = c->window_rows > 0 ? c->window_rows : (window_keys < rmax ? window_keys : rmax);
     L.nk = L.burst ? window_keys : c->max_tokens;
     L.nblk = (L.nk + kSortTile - 1) / kSortTile;
+    L.nrblk = (L.nk + kRadixTile - 1) / kRadixTile;
     L.nchunk = (L.nk + kChunk - 1) / kChunk;
     int bits = 0;
     while (bits < 31 && ((int64_t(1) << bits) < rmax))
@@ -119,7 +120,7 @@ WsLayout layout(const ngram_config *c)
     L.seg_info = o;
     o = up(o + 4ull * 2 * (uint64_t)L.nk);
     L.hist = o;
-    o = up(o + 4ull * 2 * kRadix * (uint64_t)L.nblk);
+    o = up(o + 4ull * 2 * kRadix * (uint64_t)L.nrblk);
     L.tot = o;
     o = up(o + 4ull * 2 * kRadix);
     L.blk = o;

@@ -105,10 +105,10 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
         h[1][d] = 0;
     }
     __syncthreads();
-    const uint32_t base = b * kSortTile;
+    const uint32_t base = b * kRadixTile;
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kRadixItems; ++j) {
         const uint32_t i = base + j * kSortThreads + tid;
         if (i < n) {
             uint32_t ib, it, pos = i;
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
         h[d] = 0;
     __syncthreads();
     const uint32_t *k = keys + (size_t)c * nk;
-    const uint32_t base = b * kSortTile;
+    const uint32_t base = b * kRadixTile;
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kRadixItems; ++j) {
         const uint32_t i = base + j * kSortThreads + tid;
         if (i < n)
             atomicAdd(&h[(k[i] >> shift) & (kRadix - 1)], 1u);
@@ -185,19 +185,19 @@ __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__r
         tot[c * kRadix + d] = total;
 }
 
-// Stable scatter of one tile by the current digit.  Wave w owns tile keys
-// [w*512, w*512+512), processed 64 at a time in index order.
+// Stable scatter of one tile by the current digit.  Wave w owns the w-th
+// quarter of the tile's keys, processed 64 at a time in index order.
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
     const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk)
 {
-    constexpr int kPerWave = kSortTile / (kSortThreads / kWave);
+    constexpr int kPerWave = kRadixTile / (kSortThreads / kWave);
     __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
     __shared__ uint32_t s_tile[kRadix];
     __shared__ uint32_t s_glob[kRadix];
-    __shared__ uint32_t s_k[kSortTile];
-    __shared__ uint32_t s_v[kSortTile];
+    __shared__ uint32_t s_k[kRadixTile];
+    __shared__ uint32_t s_v[kRadixTile];
     __shared__ uint32_t s_wave[kSortThreads / kWave];
 
     const int c = blockIdx.y;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint32_t n = count_of(n_dev, n_host);
-    const uint32_t base = b * kSortTile;
+    const uint32_t base = b * kRadixTile;
     if (base >= n)
         return;
     const uint32_t *ki = kin + (size_t)c * nk;
@@ -232,17 +232,17 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     }
     __syncthreads();
 
-    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kRadixItems; ++j) {
         const uint32_t i = base + w * kPerWave + j * kWave + lane;
         const bool ok = i < n;
         key[j] = ok ? ki[i] : 0u;
         val[j] = ok ? vi[i] : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kRadixItems; ++j) {
         const bool ok = base + w * kPerWave + j * kWave + lane < n;
         const uint32_t d = (key[j] >> shift) & (kRadix - 1);
         uint64_t m = __ballot(ok);
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
+    for (int j = 0; j < kRadixItems; ++j) {
         const bool ok = base + w * kPerWave + j * kWave + lane < n;
         if (ok) {
             const uint32_t d = (key[j] >> shift) & (kRadix - 1);
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     __syncthreads();
     uint32_t *ko = kout + (size_t)c * nk;
     uint32_t *vo = vout + (size_t)c * nk;
-    const uint32_t nv = min((uint32_t)kSortTile, n - base);
+    const uint32_t nv = min((uint32_t)kRadixTile, n - base);
     for (uint32_t p = tid; p < nv; p += kSortThreads) {
         const uint32_t k = s_k[p];
         const uint32_t d = (k >> shift) & (kRadix - 1);
@@ -1396,16 +1396,17 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const bool burst = tok == nullptr;
     const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
-    const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;
+    const uint32_t nrb = (n_host + kRadixTile - 1) / kRadixTile;   // radix tiles
+    const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;     // slot / split tiles
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + L.keys[0]);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + L.vals[0]);
 
-    launch_prof(NGRAM_PROF_SORT, true, false, burst ? keys_tile_kernel<true> : keys_tile_kernel<false>, dim3(nblk),
+    launch_prof(NGRAM_PROF_SORT, true, false, burst ? keys_tile_kernel<true> : keys_tile_kernel<false>, dim3(nrb),
                 dim3(kSortThreads), 0, s, tok, burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) : nullptr,
                 burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
-                hist, nblk, hdr);
+                hist, nrb, hdr);
     int cur = 0;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = p * kRadixBits;
@@ -1414,11 +1415,11 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
         uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
         uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
         if (p > 0)
-            radix_hist_kernel<<<dim3(nblk, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist,
-                                                                          nblk);
-        scan_digits_kernel<<<dim3(kRadix, L.nch), kSortThreads, 0, s>>>(hist, nblk, tot);
-        radix_scatter_kernel<<<dim3(nblk, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
-                                                                    shift, hist, tot, nblk);
+            radix_hist_kernel<<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist,
+                                                                         nrb);
+        scan_digits_kernel<<<dim3(kRadix, L.nch), kSortThreads, 0, s>>>(hist, nrb, tot);
+        radix_scatter_kernel<<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
+                                                                   shift, hist, tot, nrb);
         cur ^= 1;
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
