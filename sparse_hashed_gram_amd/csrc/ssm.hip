@@ -12,8 +12,9 @@
 // Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // k-contiguous in memory (the backward's transposed operands are written
 // first), so one main loop serves all three: a 128 x 128 block tile staged
-// through LDS (one or two buffers), four wavefronts of 64 x 64 (2 x 2
-// matrix-core tiles of 32 x 32).
+// through LDS (one or two buffers, filled from registers or by direct
+// global -> LDS loads), four wavefronts of 64 x 64 (2 x 2 matrix-core tiles
+// of 32 x 32).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -32,12 +33,13 @@ constexpr int kLdt = 128 + 4;   // fp32 per row of the forward's epilogue tile
 constexpr int kLdb = 128 + 8;   // bf16 per row of the dz epilogue tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Tile shapes per contraction (measured on MI355X at 49,152 x 10,240 x 768):
-// the forward runs k = 768 with a heavy softmax epilogue; k-steps of 32 in
-// two LDS buffers (40 KB, three blocks per CU) suit it best.  dz and dX take
-// k-steps of 64 in one LDS buffer (37 KB, three blocks per CU, two barriers
-// per step); dW, k = T, keeps two buffers of 64.
+// the forward (k = 768, heavy softmax epilogue) takes k-steps of 32 with
+// direct global -> LDS loads (four blocks per CU); dz and dX k-steps of 64 in
+// one LDS buffer filled from registers (three blocks per CU, two barriers per
+// step); dW (k = T) k-steps of 64 with direct loads into two buffers.
 constexpr int kFwdBK = 32, kDzBK = 64, kDxBK = 64, kDwBK = 64;
 constexpr bool kFwdSingle = false, kDzSingle = true, kDxSingle = true, kDwSingle = false;
+constexpr bool kFwdDirect = true, kDzDirect = false, kDxDirect = false, kDwDirect = true;
 
 // Block tile of a contraction: four wavefronts, 2 along M x 2 along N; a
 // wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
@@ -398,6 +400,90 @@ __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t
     }
 }
 
+
+// Direct global -> LDS form of the main loop (global_load_lds_dwordx4: lane l
+// of a wavefront lands its 16 bytes at LDS base + 16 l, so one load fills a
+// contiguous 1 KB block).  Rows are stored unpadded, BK / 8 chunks of 16
+// bytes each, chunk c of row r at position c ^ ((r >> SH) & (CH - 1)): the
+// 16 lanes of a ds_read_b128 group (16 consecutive rows, one chunk) then hit
+// 16 different 16-byte bank groups.  Each lane fetches the source chunk that
+// belongs at its position.  Two buffers; no staging registers, no ds_write.
+template <int BK>
+struct DirectTile {
+    static constexpr int CH = BK / 8, RB = CH * 16, RPI = 1024 / RB, NI = 32 / RPI;
+    static constexpr int SH = CH == 8 ? 1 : (CH == 4 ? 2 : 3);
+    static constexpr uint32_t OPB = 128 * RB;              // one operand tile, bytes
+    static constexpr uint32_t SMEM = 2u * 2u * OPB;
+};
+
+__device__ inline void lds_load16(const uint16_t *g, uint8_t *lds)
+{
+    __builtin_amdgcn_global_load_lds((const void *)g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int BK>
+__device__ inline void mainloop_direct(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
+                                       uint8_t *sm, f32x16 (&acc)[2][2], uint32_t *flags)
+{
+    using DT = DirectTile<BK>;
+    constexpr int CH = DT::CH, RB = DT::RB, RPI = DT::RPI, NI = DT::NI, SH = DT::SH;
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int lrow = lane / CH, lpos = lane % CH;
+    const uint16_t *pa[NI], *pb[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int r = w * 32 + j * RPI + lrow;
+        const int c = lpos ^ ((r >> SH) & (CH - 1));
+        pa[j] = row_ptr(A, m0 + r, flags) + 8 * c;
+        pb[j] = row_ptr(B, n0 + r, flags) + 8 * c;
+    }
+    auto issue = [&](int buf, int64_t k0) {
+        uint8_t *ab = sm + buf * 2 * DT::OPB, *bb = ab + DT::OPB;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int r0 = w * 32 + j * RPI;
+            lds_load16(pa[j] + k0, ab + r0 * RB);
+            lds_load16(pb[j] + k0, bb + r0 * RB);
+        }
+    };
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[mb][nb][e] = 0.f;
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31), kq = lane >> 5;
+    const int sa0 = (ar >> SH) & (CH - 1), sa1 = ((ar + 32) >> SH) & (CH - 1);
+    const int sb0 = (br >> SH) & (CH - 1), sb1 = ((br + 32) >> SH) & (CH - 1);
+    const int64_t nk = K / BK;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        if (kt + 1 < nk)
+            issue(cur ^ 1, (kt + 1) * BK);
+        const uint8_t *ab = sm + cur * 2 * DT::OPB, *bb = ab + DT::OPB;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int c = 2 * kk + kq;
+            const bf16x8 a0 = *(const bf16x8 *)(ab + ar * RB + 16 * (c ^ sa0));
+            const bf16x8 a1 = *(const bf16x8 *)(ab + (ar + 32) * RB + 16 * (c ^ sa1));
+            const bf16x8 b0 = *(const bf16x8 *)(bb + br * RB + 16 * (c ^ sb0));
+            const bf16x8 b1 = *(const bf16x8 *)(bb + (br + 32) * RB + 16 * (c ^ sb1));
+            acc[0][0] = mfma(a0, b0, acc[0][0]);
+            acc[0][1] = mfma(a0, b1, acc[0][1]);
+            acc[1][0] = mfma(a1, b0, acc[1][0]);
+            acc[1][1] = mfma(a1, b1, acc[1][1]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next tile have landed
+        __syncthreads();
+    }
+}
+
 // Position of acc[mb][nb][e] in the block tile (32 x 32 matrix-core layout:
 // lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4).
 template <int WMB>
@@ -481,26 +567,32 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
-template <int EPI, int WMB, int BK, bool SINGLE>
+template <int EPI, int WMB, int BK, bool SINGLE, bool DIRECT>
 constexpr uint32_t smem_bytes()
 {
-    return EPI == EPI_FWD ? cmax(Tile<WMB, BK, SINGLE>::SMEM, 64 * kLdt * 4 + 4 * 64 * 8)
-         : EPI == EPI_DZ  ? cmax(Tile<WMB, BK, SINGLE>::SMEM, 128 * kLdb * 2 + 3 * 128 * 4)
-                          : Tile<WMB, BK, SINGLE>::SMEM;
+    constexpr uint32_t main = DIRECT ? DirectTile<BK>::SMEM : Tile<WMB, BK, SINGLE>::SMEM;
+    return EPI == EPI_FWD ? cmax(main, 64 * kLdt * 4 + 4 * 64 * 8)
+         : EPI == EPI_DZ  ? cmax(main, 128 * kLdb * 2 + 3 * 128 * 4)
+                          : main;
 }
 
-template <int EPI, int WMB, int BK, bool SINGLE = false>
+template <int EPI, int WMB, int BK, bool SINGLE, bool DIRECT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
     static_assert(EPI == EPI_DX || EPI == EPI_DW || WMB == 2, "the softmax epilogues take 128-row tiles");
     using TL = Tile<WMB, BK, SINGLE>;
-    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK, SINGLE>()];
+    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK, SINGLE, DIRECT>()];
     uint32_t mt, nt;
     if (!tile_of<EPI != EPI_DZ>(a.tiles_m, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
     const int64_t m0 = (int64_t)mt * TL::BM, n0 = (int64_t)nt * TL::BN;
     f32x16 acc[WMB][2];
-    mainloop<WMB, BK, SINGLE>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    if constexpr (DIRECT) {
+        static_assert(WMB == 2 && !SINGLE, "direct loads: 64 x 64 wave tiles, two buffers");
+        mainloop_direct<BK>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
+    } else {
+        mainloop<WMB, BK, SINGLE>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    }
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
@@ -851,7 +943,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     hipStream_t s = (hipStream_t)stream;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = (uint32_t)nct;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK, kFwdSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK, kFwdSingle, kFwdDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
@@ -908,7 +1000,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.K = kD;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = blocks(Cp, 128);
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK, kDzSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK, kDzSingle, kDzDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
@@ -917,7 +1009,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.out = dX;
     a.tiles_m = blocks(Tq, Tile<2, kDxBK>::BM);
     a.tiles_n = kD / 128;
-    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK, kDxSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK, kDxSingle, kDxDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
 
     a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
@@ -926,7 +1018,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.out = dW;
     a.tiles_m = blocks(Cp, Tile<2, kDwBK>::BM);
     a.tiles_n = kD / 128;
-    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle, kDwDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     return done(hipGetLastError());
 }
