@@ -728,19 +728,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 }
 
 // Folds the per-tile sums of each position: lse = M + log sum_t s_t e^(m_t - M).
+// (Every tile has a finite maximum: its first column is a candidate.)
 __global__ void lse_kernel(const float2 *part, int64_t T, int nct, const int32_t *slot, int32_t C,
                            const float *zt, float *loss, float *lse, Hdr *h)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= T)
         return;
-    float M = -INFINITY;
-    for (int c = 0; c < nct; ++c)
-        M = fmaxf(M, part[(int64_t)c * T + i].x);
-    float S = 0.f;
+    // one pass, rescaling the running sum whenever the running maximum grows
+    float M = -INFINITY, S = 0.f;
     for (int c = 0; c < nct; ++c) {
         const float2 p = part[(int64_t)c * T + i];
-        S += p.y * expf(p.x - M);
+        if (p.x > M) {
+            S = S * expf(M - p.x) + p.y;
+            M = p.x;
+        } else {
+            S += p.y * expf(p.x - M);
+        }
     }
     const float l = M + logf(S);
     const int32_t y = slot[i];
