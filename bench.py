@@ -138,8 +138,10 @@ STATE = 8     # one (v, t_last) record per row
 
 
 def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_passes=3):
-    """Bytes each kernel group must move per window (the design doc gives the
-    per-unit figures), listed per launch.
+    """Bytes each kernel group must move per window, listed per launch.  Per
+    unit: a token's forward reads two table rows and writes one output row
+    (plus its id); a reduced key reads its dY row; a stepped row reads and
+    writes its table row and its 8-byte state.
 
     accumulate reduction, per micro-step: the bigram pass reads the dY row of
       every key, the trigram pass those of keys whose row occurs more than
@@ -406,7 +408,7 @@ def main_ssm(args, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); the "
               "table lives whole on one MI355X and there is no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
