@@ -222,11 +222,53 @@ def pmc_traffic(group, workload_key, mode, dy_dtype):
     return None
 
 
+def host_info():
+    """Core count, CPU model and RAM of the machine the oracle ran on."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["ram_gib"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(w, toks_np, T_sample, dys_fn):
     """The oracle on a bounded sample of the same workload: whole windows of
     4 micro-steps of T_sample tokens each (hash, forward, window gradient,
-    sparse step on the touched rows).  Table rows are a snapshot of the rows
-    a window touches; preparing inputs (dY, snapshots) is not timed."""
+    sparse step on the touched rows), on all threads; then the first window
+    at an eighth of the tokens on one thread.  Table rows are a snapshot of
+    the rows a window touches; preparing inputs (dY, snapshots) is not
+    timed."""
+    import oracle
+    el, ntok, n_upd = _oracle_windows(w, toks_np, T_sample, dys_fn)
+    threads = oracle.threads()
+    T1 = max(1, T_sample // 8)
+    oracle.set_threads(1)
+    try:
+        el1, ntok1, _ = _oracle_windows(w, toks_np[:1], T1, dys_fn)
+    finally:
+        oracle.set_threads(threads)
+    nw = len(toks_np)
+    return {"value": ntok / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": el, "updated_rows_per_s": n_upd / el,
+            "sample": (f"{nw} window(s) of 4 micro-steps x {T_sample} tokens of the same streams "
+                       f"(hash, forward, window gradient, sparse step on {n_upd} touched rows in "
+                       f"all; table rows as a snapshot of the touched rows)"),
+            "one_thread": {"value": ntok1 / el1, "unit": "tokens/s", "seconds": el1,
+                           "sample": f"the first window at 4 micro-steps x {T1} tokens, one thread"},
+            "host": host_info()}
+
+
+def _oracle_windows(w, toks_np, T_sample, dys_fn):
     import oracle
     el = 0.0
     ntok = 0
@@ -267,12 +309,7 @@ def cpu_baseline(w, toks_np, T_sample, dys_fn):
         el += time.perf_counter() - t0
         ntok += sum(len(t) for t in toks)
         del dY, rows, snaps
-    nw = len(toks_np)
-    return {"value": ntok / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "seconds": el, "updated_rows_per_s": n_upd / el,
-            "sample": (f"{nw} window(s) of 4 micro-steps x {T_sample} tokens of the same streams "
-                       f"(hash, forward, window gradient, sparse step on {n_upd} touched rows in "
-                       f"all; table rows as a snapshot of the touched rows)")}
+    return el, ntok, n_upd
 
 
 SSM_METRIC = "sampled-softmax loss tokens/s (forward + backward); achieved TFLOP/s vs bf16 matrix-core peak"
@@ -299,7 +336,7 @@ def cpu_baseline_ssm(batches, C, T_sample):
         n += len(t)
     threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
     return {"value": n / el if el else None, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": el,
+            "seconds": el, "host": host_info(),
             "sample": (f"{len(batches)} batch(es) x first {T_sample} positions, all {C} candidates "
                        f"(candidate set, fp64 loss forward and backward; numpy BLAS threads = {threads})")}
 
@@ -568,6 +605,10 @@ def main():
         step_ms_per_window = total_ms.get("step", 0.0) + float(np.mean(last))
     else:
         step_ms_per_window = total_ms["step"]
+    # the forward's compulsory bytes: each distinct row of a micro-step read
+    # once (repeats could come from the caches), every output row written
+    comp_fwd = [sum(u[0] for u in timed_stats[win][0][m]) * row_bytes + T * (row_bytes + 4)
+                for _, _, win, m in ev["fwd"]] if "fwd" in used else []
     kernels = {}
     for g_ in used:
         gbps = abytes[g_] / (ms[g_] * 1e-3) / 1e9
@@ -578,6 +619,10 @@ def main():
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if g_ == "fwd" and comp_fwd:
+            cb = float(np.mean(comp_fwd))
+            kernels[g_]["compulsory_bytes_per_launch"] = int(cb)
+            kernels[g_]["compulsory_frac_of_hbm_peak"] = round(cb / (ms[g_] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
     traffic = pmc_traffic(dom, args.workload, args.mode, args.dy_dtype)
     achieved = abytes[dom] / (ms[dom] * 1e-3) / 1e9
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

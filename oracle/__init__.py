@@ -76,6 +76,8 @@ def lib():
                                       ctypes.c_float, ctypes.c_float, ctypes.c_float]
         L.orc_threads.restype = ctypes.c_int
         L.orc_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -199,3 +201,8 @@ def sparse_step(G: np.ndarray, W: np.ndarray, v: np.ndarray, t_last: np.ndarray,
 
 def threads() -> int:
     return int(lib().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (n <= 0: all processors)."""
+    lib().orc_set_threads(int(n))

@@ -356,4 +356,14 @@ int orc_threads(void)
 #endif
 }
 
+/* Sets the threads of the OpenMP loops (n <= 0: all processors). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+#else
+    (void)n;
+#endif
+}
+
 int orc_rounding_is_nearest(void) { return fegetround() == FE_TONEAREST; }
