@@ -43,7 +43,7 @@ constexpr bool kFwdDirect = true, kDzDirect = false, kDxDirect = false, kDwDirec
 
 // Block tile of a contraction: four wavefronts, 2 along M x 2 along N; a
 // wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
-// by 64 columns).  BK: k-elements staged per LDS buffer (two buffers).
+// by 64 columns).  BK: k-elements staged per LDS buffer.
 template <int WMB, int BK, bool SINGLE = false>   // SINGLE: one LDS buffer (register prefetch only)
 struct Tile {
     static constexpr int BM = 2 * WMB * 32, BN = 128;
