@@ -91,7 +91,7 @@ WsLayout layout(const ngram_config *c)
     L.wrows = c->window_rows > 0 ? c->window_rows : (window_keys < rmax ? window_keys : rmax);
     L.nk = L.burst ? window_keys : c->max_tokens;
     L.nblk = (L.nk + kSortTile - 1) / kSortTile;
-    L.nrblk = (L.nk + kRadixTile - 1) / kRadixTile;
+    L.nrblk = (L.nk + radix_tile(kRadixItemsSmall) - 1) / radix_tile(kRadixItemsSmall);   // the most radix tiles
     L.nchunk = (L.nk + kChunk - 1) / kChunk;
     int bits = 0;
     while (bits < 31 && ((int64_t(1) << bits) < rmax))

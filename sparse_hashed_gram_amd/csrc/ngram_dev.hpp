@@ -254,15 +254,14 @@ constexpr int kRadixBits = NGRAM_RADIX_BITS;   // 26-bit rows of the full table:
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kDpt = kRadix / kSortThreads;    // digits per thread in the per-digit loops
 static_assert(kRadix % kSortThreads == 0, "digits are split evenly over the threads");
-// Radix tiles (key build, digit counts, scatter): 256 threads x kRadixItems
-// keys.  A larger tile gives the scatter longer runs of each digit to write:
-// 16 keys per thread took the full window's sort from 0.217 to 0.191 ms
-// (8: 2,048-key tiles; 32: 0.202 ms).
-#ifndef NGRAM_RADIX_ITEMS
-#define NGRAM_RADIX_ITEMS 16
-#endif
-constexpr int kRadixItems = NGRAM_RADIX_ITEMS;
-constexpr int kRadixTile = kSortThreads * kRadixItems;
+// Radix tiles (key build, digit counts, scatter): 256 threads x ITEMS keys.
+// A larger tile gives the scatter longer runs of each digit to write, but
+// fewer blocks: 16 keys per thread when a channel has at least 1M keys to
+// sort (the full burst window's sort: 0.217 -> 0.191 ms), else 8 (a spread
+// micro-step or a shard window would leave CUs idle).
+constexpr int kRadixItemsBig = 16, kRadixItemsSmall = 8;
+constexpr uint32_t kRadixBigKeys = 1u << 20;
+__host__ __device__ constexpr int radix_tile(int items) { return kSortThreads * items; }
 
 // Segment-reduce chunks: one wavefront per 64 sorted keys.
 constexpr int kChunk = 64;

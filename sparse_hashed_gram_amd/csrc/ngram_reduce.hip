@@ -86,7 +86,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave
 // position i of the micro-step is hashed from the tokens.  Burst: every
 // position kept in the stash, whose packed indices were hashed when kept.
 // Also clears the fix-up record counts of the reduce that follows.
-template <bool FROM_STASH>
+template <bool FROM_STASH, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     const int32_t *__restrict__ tok, const uint32_t *__restrict__ sidx, const uint32_t *__restrict__ spos,
     HashParams hp, uint32_t n_host, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals, int64_t nk,
@@ -105,10 +105,10 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
         h[1][d] = 0;
     }
     __syncthreads();
-    const uint32_t base = b * kRadixTile;
+    const uint32_t base = b * radix_tile(ITEMS);
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kRadixItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const uint32_t i = base + j * kSortThreads + tid;
         if (i < n) {
             uint32_t ib, it, pos = i;
@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     }
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const uint32_t *__restrict__ keys, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
     uint32_t *__restrict__ hist, uint32_t nblk)
@@ -149,9 +150,9 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
         h[d] = 0;
     __syncthreads();
     const uint32_t *k = keys + (size_t)c * nk;
-    const uint32_t base = b * kRadixTile;
+    const uint32_t base = b * radix_tile(ITEMS);
 #pragma unroll
-    for (int j = 0; j < kRadixItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const uint32_t i = base + j * kSortThreads + tid;
         if (i < n)
             atomicAdd(&h[(k[i] >> shift) & (kRadix - 1)], 1u);
@@ -187,17 +188,18 @@ __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__r
 
 // Stable scatter of one tile by the current digit.  Wave w owns the w-th
 // quarter of the tile's keys, processed 64 at a time in index order.
+template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
     const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk)
 {
-    constexpr int kPerWave = kRadixTile / (kSortThreads / kWave);
+    constexpr int kPerWave = radix_tile(ITEMS) / (kSortThreads / kWave);
     __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
     __shared__ uint32_t s_tile[kRadix];
     __shared__ uint32_t s_glob[kRadix];
-    __shared__ uint32_t s_k[kRadixTile];
-    __shared__ uint32_t s_v[kRadixTile];
+    __shared__ uint32_t s_k[radix_tile(ITEMS)];
+    __shared__ uint32_t s_v[radix_tile(ITEMS)];
     __shared__ uint32_t s_wave[kSortThreads / kWave];
 
     const int c = blockIdx.y;
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint32_t n = count_of(n_dev, n_host);
-    const uint32_t base = b * kRadixTile;
+    const uint32_t base = b * radix_tile(ITEMS);
     if (base >= n)
         return;
     const uint32_t *ki = kin + (size_t)c * nk;
@@ -232,17 +234,17 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     }
     __syncthreads();
 
-    uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
+    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = 0; j < kRadixItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const uint32_t i = base + w * kPerWave + j * kWave + lane;
         const bool ok = i < n;
         key[j] = ok ? ki[i] : 0u;
         val[j] = ok ? vi[i] : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kRadixItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const bool ok = base + w * kPerWave + j * kWave + lane < n;
         const uint32_t d = (key[j] >> shift) & (kRadix - 1);
         uint64_t m = __ballot(ok);
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kRadixItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const bool ok = base + w * kPerWave + j * kWave + lane < n;
         if (ok) {
             const uint32_t d = (key[j] >> shift) & (kRadix - 1);
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     __syncthreads();
     uint32_t *ko = kout + (size_t)c * nk;
     uint32_t *vo = vout + (size_t)c * nk;
-    const uint32_t nv = min((uint32_t)kRadixTile, n - base);
+    const uint32_t nv = min((uint32_t)radix_tile(ITEMS), n - base);
     for (uint32_t p = tid; p < nv; p += kSortThreads) {
         const uint32_t k = s_k[p];
         const uint32_t d = (k >> shift) & (kRadix - 1);
@@ -1396,14 +1398,18 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const bool burst = tok == nullptr;
     const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
-    const uint32_t nrb = (n_host + kRadixTile - 1) / kRadixTile;   // radix tiles
+    const bool big = n_host >= kRadixBigKeys;
+    const uint32_t tile = radix_tile(big ? kRadixItemsBig : kRadixItemsSmall);
+    const uint32_t nrb = (n_host + tile - 1) / tile;   // radix tiles
     const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;     // slot / split tiles
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + L.keys[0]);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + L.vals[0]);
 
-    launch_prof(NGRAM_PROF_SORT, true, false, burst ? keys_tile_kernel<true> : keys_tile_kernel<false>, dim3(nrb),
+    launch_prof(NGRAM_PROF_SORT, true, false, burst ? (big ? keys_tile_kernel<true, kRadixItemsBig> : keys_tile_kernel<true, kRadixItemsSmall>)
+                      : (big ? keys_tile_kernel<false, kRadixItemsBig> : keys_tile_kernel<false, kRadixItemsSmall>),
+                dim3(nrb),
                 dim3(kSortThreads), 0, s, tok, burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) : nullptr,
                 burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
                 hist, nrb, hdr);
@@ -1415,11 +1421,12 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
         uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
         uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
         if (p > 0)
-            radix_hist_kernel<<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist,
-                                                                         nrb);
+            (big ? radix_hist_kernel<kRadixItemsBig> : radix_hist_kernel<kRadixItemsSmall>)
+                <<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nrb);
         scan_digits_kernel<<<dim3(kRadix, L.nch), kSortThreads, 0, s>>>(hist, nrb, tot);
-        radix_scatter_kernel<<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host,
-                                                                   shift, hist, tot, nrb);
+        (big ? radix_scatter_kernel<kRadixItemsBig> : radix_scatter_kernel<kRadixItemsSmall>)
+            <<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist, tot,
+                                                       nrb);
         cur ^= 1;
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
