@@ -327,3 +327,36 @@ def test_bf16_dy_matches_f32_dy_bitwise():
         outs.append((st.W[0].cpu(), st.W[1].cpu(), st.st[0].cpu(), st.st[1].cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["burst", "burst_ref"])
+def test_radix_tile_size_does_not_change_results(mode):
+    # burst windows sort 4 x max_tokens keys per channel: from 2^20 keys on
+    # the radix kernels take 4,096-key tiles, below it 2,048-key tiles.  The
+    # sort is stable either way, so a ragged window stepped through both
+    # configurations must give the same bits.
+    N = ng()
+    w = workloads.FULL
+    rows = (1 << 20, 1 << 20)
+    Ts = [262143, 100000, 7, 150001]
+    inputs = [[(to_dev(synth.tokens(w, 700 + 4 * win + m, T)), to_dev(synth.dY(w, 700 + 4 * win + m, T)))
+               for m, T in enumerate(Ts)] for win in range(2)]
+    states = []
+    for max_tokens in (262144, 262143):   # 4 x 262,144 = 2^20 keys; 4 x 262,143 just below
+        cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=max_tokens, mode=mode)
+        st = State(cfg, device_table(rows[0], "bf16", 41), device_table(rows[1], "bf16", 42))
+        ws = N.Workspace(cfg)
+        for win in range(2):
+            for m, (tok, dy) in enumerate(inputs[win]):
+                if m == len(Ts) - 1:
+                    st.bwd_step(ws, tok, dy, win + 1, w.lr, w.beta2, w.eps)
+                else:
+                    N.embed_bwd_accum(cfg, ws, tok, dy)
+        torch.cuda.synchronize()
+        assert N.device_status(cfg, ws) == 0
+        assert int((st.tl[0] == 2).sum()) > 0
+        states.append(st)
+        del ws
+    for c in range(2):
+        assert torch.equal(states[0].W[c], states[1].W[c]), c
+        assert torch.equal(states[0].st[c], states[1].st[c]), c
