@@ -50,7 +50,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        L = ctypes.CDLL(build())
+        # NGRAM_ORACLE_LIB: another build of this source (the mutation tests
+        # load deliberately broken copies this way, in their own processes)
+        L = ctypes.CDLL(os.environ.get("NGRAM_ORACLE_LIB") or build())
         u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
         L.orc_hash64.restype = u64
         L.orc_hash64.argtypes = [u64, u64]
