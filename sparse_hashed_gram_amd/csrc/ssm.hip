@@ -36,7 +36,8 @@ constexpr int kTile = 128;      // T and C are padded to multiples of this
 // the forward (k = 768, heavy softmax epilogue) takes k-steps of 32 with
 // direct global -> LDS loads (four blocks per CU); dz and dX k-steps of 64 in
 // one LDS buffer filled from registers (three blocks per CU, two barriers per
-// step); dW (k = T) k-steps of 64 with direct loads into two buffers.
+// step); dW (k = T) k-steps of 64 with direct loads into two buffers, or the
+// dX form when its three blocks per CU fill the last round better.
 constexpr int kFwdBK = 32, kDzBK = 64, kDxBK = 64, kDwBK = 64;
 constexpr bool kFwdSingle = false, kDzSingle = true, kDxSingle = true, kDwSingle = false;
 constexpr bool kFwdDirect = true, kDzDirect = false, kDxDirect = false, kDwDirect = true;
@@ -816,6 +817,15 @@ int check_cfg(const ssm_config *c)
 
 bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
 
+constexpr uint32_t kCUs = 256;   // MI355X compute units
+
+// Share of the resident slots busy over all rounds of a launch of nb blocks.
+double round_fill(uint32_t nb, uint32_t slots)
+{
+    const uint32_t rounds = (nb + slots - 1) / slots;
+    return rounds ? (double)nb / ((double)rounds * slots) : 1.0;
+}
+
 int done(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_EHIP; }
 
 uint32_t blocks(int64_t n, int b) { return (uint32_t)((n + b - 1) / b); }
@@ -1022,8 +1032,15 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.out = dW;
     a.tiles_m = blocks(Cp, Tile<2, kDwBK>::BM);
     a.tiles_n = kD / 128;
-    launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle, kDwDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
-           dim3(256), s, a);
+    // dW's blocks are few and long (k = T): take the form whose resident
+    // slots (two or three blocks per CU) leave less of the last round idle
+    const uint32_t nb = a.tiles_m * a.tiles_n;
+    if (round_fill(nb, 3 * kCUs) > round_fill(nb, 2 * kCUs))
+        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, true, false>,
+               dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
+    else
+        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle, kDwDirect>,
+               dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
     return done(hipGetLastError());
 }
 

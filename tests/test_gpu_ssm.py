@@ -346,3 +346,21 @@ def test_graph_replay_equals_eager():
         torch.cuda.synchronize()
         del junk
     assert N.device_status(cfg, ws_g) == 0 and N.device_status(cfg, ws_e) == 0
+
+
+def test_backward_dw_three_blocks_per_cu_form():
+    # 14,336 candidates: dW's 672 blocks fill three-per-CU slots better than
+    # two-per-CU ones, so the library takes the other dW form; same bar
+    N = S()
+    T, V, C = 700, 50304, 14336
+    tgt, X, W, perm, g = _inputs(33, T, V)
+    cand_o, slot_o, _, ok = orc.candidates(tgt, perm, V, C)
+    assert ok
+    cfg, ws, cand, slot = _run_cand(N, V, C, T, tgt, perm)
+    Xd, Wd = _dev_bf16(X), _dev_bf16(W)
+    loss, lse = N.loss_fwd(cfg, ws, Xd, Wd, cand, slot)
+    dW0 = np.random.default_rng(5).standard_normal((V, 768)).astype(np.float32)
+    dW = _dev(dW0)
+    dX = N.loss_bwd(cfg, ws, Xd, Wd, cand, slot, lse, _dev(g), dW)
+    _check_bwd(X, W, cand_o, slot_o, g, dX, dW, dW0, C)
+    assert N.device_status(cfg, ws) == 0
