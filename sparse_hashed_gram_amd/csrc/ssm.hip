@@ -11,10 +11,10 @@
 //
 // Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // k-contiguous in memory (the backward's transposed operands are written
-// first), so one main loop serves all three: a 128 x 128 block tile staged
-// through LDS (one or two buffers, filled from registers or by direct
-// global -> LDS loads), four wavefronts of 64 x 64 (2 x 2 matrix-core tiles
-// of 32 x 32).
+// first), so one kernel template serves all four: four wavefronts per block,
+// each owning WM x WN matrix-core tiles of 32 x 32, and one of two main
+// loops, staged through registers into one LDS buffer or pipelined with
+// direct global -> LDS loads.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -29,31 +29,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
-constexpr int kLdt = 128 + 4;   // fp32 per row of the forward's epilogue tile
+constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
 constexpr int kLdb = 128 + 8;   // bf16 per row of the dz epilogue tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
-// Tile shapes per contraction (measured on MI355X at 49,152 x 10,240 x 768):
-// the forward (k = 768, heavy softmax epilogue) takes k-steps of 32 with
-// direct global -> LDS loads (four blocks per CU); dz and dX k-steps of 64 in
-// one LDS buffer filled from registers (three blocks per CU, two barriers per
-// step); dW (k = T) k-steps of 64 with direct loads into two buffers, or the
-// dX form when its three blocks per CU fill the last round better.
-constexpr int kFwdBK = 32, kDzBK = 64, kDxBK = 64, kDwBK = 64;
-constexpr bool kFwdSingle = false, kDzSingle = true, kDxSingle = true, kDwSingle = false;
-constexpr bool kFwdDirect = true, kDzDirect = false, kDxDirect = false, kDwDirect = true;
+// Per contraction: the k-step BK and the main-loop form, NS = 0 for the
+// loop staged through registers into one LDS buffer (three blocks per CU),
+// NS > 0 for direct global -> LDS loads into NS pipelined stages (two blocks
+// per CU); and the block tile, four wavefronts of WM x WN matrix-core tiles
+// of 32 x 32.  Chosen by measurement on MI355X (49,152 positions x 10,240
+// candidates x 768).
+constexpr int kFwdBK = 64, kFwdS = 2;                        // forward, 128 x 128
+constexpr int kDzBK = 64, kDzS = 0;                          // dz, 128 x 128
+constexpr int kDxWM = 2, kDxWN = 3, kDxBK = 64, kDxS = 2;    // dX, 128 x 192
+constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 128 (or staged: three blocks per CU)
 
-// Block tile of a contraction: four wavefronts, 2 along M x 2 along N; a
+// Staged form's block tile: four wavefronts, 2 along M x 2 along N; a
 // wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
-// by 64 columns).  BK: k-elements staged per LDS buffer.
-template <int WMB, int BK, bool SINGLE = false>   // SINGLE: one LDS buffer (register prefetch only)
+// by 64 columns).  BK: k-elements per LDS buffer (one buffer; the next k-step
+// is prefetched into registers).
+template <int WMB, int BK>
 struct Tile {
     static constexpr int BM = 2 * WMB * 32, BN = 128;
-    static constexpr int NBUF = SINGLE ? 1 : 2;
     static constexpr int LDK = BK + 8;                  // bf16 per LDS operand row (16-byte reads conflict-free)
     static constexpr int CH = BK / 8;                   // 16-byte chunks per row per k-step
     static constexpr int RP = 256 / CH;                 // rows one pass of the block's loads covers
     static constexpr int LA = BM / RP, LB = BN / RP;    // 16-byte loads per thread per operand
-    static constexpr uint32_t SMEM = NBUF * (BM + BN) * LDK * 2u;
+    static constexpr uint32_t SMEM = (BM + BN) * LDK * 2u;
 };
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
@@ -297,11 +298,11 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 
 // acc[mb][nb] = the wavefront's 32 x 32 tiles of C[m0 + ..][n0 + ..]; K is a
 // multiple of BK.  Ends with a block barrier (LDS free for the epilogue).
-template <int WMB, int BK, bool SINGLE>
+template <int WMB, int BK>
 __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
                                 uint16_t *sm, f32x16 (&acc)[WMB][2], uint32_t *flags)
 {
-    using TL = Tile<WMB, BK, SINGLE>;
+    using TL = Tile<WMB, BK>;
     constexpr int LDK = TL::LDK;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int wm = w >> 1, wn = w & 1;
@@ -313,7 +314,7 @@ __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t
 #pragma unroll
     for (int j = 0; j < TL::LB; ++j)
         pb[j] = row_ptr(B, n0 + lr + TL::RP * j, flags) + lc;
-    uint16_t *As = sm, *Bs = sm + TL::NBUF * TL::BM * LDK;
+    uint16_t *As = sm, *Bs = sm + TL::BM * LDK;
 #pragma unroll
     for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
@@ -331,172 +332,68 @@ __device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t
         for (int j = 0; j < TL::LB; ++j)
             rb[j] = *(const u32x4 *)(pb[j] + k0);
     };
-    auto sstore = [&](int buf) {
-        uint16_t *an = As + buf * TL::BM * LDK, *bn = Bs + buf * TL::BN * LDK;
+    auto sstore = [&]() {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j)
-            *(u32x4 *)(an + (lr + TL::RP * j) * LDK + lc) = ra[j];
+            *(u32x4 *)(As + (lr + TL::RP * j) * LDK + lc) = ra[j];
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j)
-            *(u32x4 *)(bn + (lr + TL::RP * j) * LDK + lc) = rb[j];
+            *(u32x4 *)(Bs + (lr + TL::RP * j) * LDK + lc) = rb[j];
     };
     gload(0);
-    sstore(0);
+    sstore();
     __syncthreads();
 
     const int ar = wm * WMB * 32 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
     const int64_t nk = K / BK;
-    if constexpr (SINGLE) {
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more)
-                gload((kt + 1) * BK);
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 16) {
-                bf16x8 a[WMB], b[2];
-#pragma unroll
-                for (int mb = 0; mb < WMB; ++mb)
-                    a[mb] = *(const bf16x8 *)(As + (ar + 32 * mb) * LDK + kk + kh);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    b[nb] = *(const bf16x8 *)(Bs + (br + 32 * nb) * LDK + kk + kh);
-#pragma unroll
-                for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
-            }
-            __syncthreads();   // every wavefront is done reading the buffer
-            if (more) {
-                sstore(0);
-                __syncthreads();
-            }
-        }
-        return;
-    }
     for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
         const bool more = kt + 1 < nk;
         if (more)
             gload((kt + 1) * BK);
-        const uint16_t *as = As + cur * TL::BM * LDK, *bs = Bs + cur * TL::BN * LDK;
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
             bf16x8 a[WMB], b[2];
 #pragma unroll
             for (int mb = 0; mb < WMB; ++mb)
-                a[mb] = *(const bf16x8 *)(as + (ar + 32 * mb) * LDK + kk + kh);
+                a[mb] = *(const bf16x8 *)(As + (ar + 32 * mb) * LDK + kk + kh);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
-                b[nb] = *(const bf16x8 *)(bs + (br + 32 * nb) * LDK + kk + kh);
+                b[nb] = *(const bf16x8 *)(Bs + (br + 32 * nb) * LDK + kk + kh);
 #pragma unroll
             for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
         }
-        if (more)
-            sstore(cur ^ 1);
-        __syncthreads();
+        __syncthreads();   // every wavefront is done reading the buffer
+        if (more) {
+            sstore();
+            __syncthreads();
+        }
     }
 }
 
-
-// Direct global -> LDS form of the main loop (global_load_lds_dwordx4: lane l
-// of a wavefront lands its 16 bytes at LDS base + 16 l, so one load fills a
-// contiguous 1 KB block).  Rows are stored unpadded, BK / 8 chunks of 16
-// bytes each, chunk c of row r at position c ^ ((r >> SH) & (CH - 1)): the
-// 16 lanes of a ds_read_b128 group (16 consecutive rows, one chunk) then hit
-// 16 different 16-byte bank groups.  Each lane fetches the source chunk that
-// belongs at its position.  Two buffers; no staging registers, no ds_write.
-template <int BK>
-struct DirectTile {
-    static constexpr int CH = BK / 8, RB = CH * 16, RPI = 1024 / RB, NI = 32 / RPI;
-    static constexpr int SH = CH == 8 ? 1 : (CH == 4 ? 2 : 3);
-    static constexpr uint32_t OPB = 128 * RB;              // one operand tile, bytes
-    static constexpr uint32_t SMEM = 2u * 2u * OPB;
-};
-
+// Direct global -> LDS load (global_load_lds_dwordx4): lane l of a wavefront
+// lands its 16 bytes at LDS base + 16 l (probed on the GPU), so one load
+// fills a contiguous 1 KB block; the LDS base must be wavefront-uniform.
 __device__ inline void lds_load16(const uint16_t *g, uint8_t *lds)
 {
     __builtin_amdgcn_global_load_lds((const void *)g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
 
-template <int BK>
-__device__ inline void mainloop_direct(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
-                                       uint8_t *sm, f32x16 (&acc)[2][2], uint32_t *flags)
-{
-    using DT = DirectTile<BK>;
-    constexpr int CH = DT::CH, RB = DT::RB, RPI = DT::RPI, NI = DT::NI, SH = DT::SH;
-    const int t = threadIdx.x, lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = w >> 1, wn = w & 1;
-    const int lrow = lane / CH, lpos = lane % CH;
-    const uint16_t *pa[NI], *pb[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int r = w * 32 + j * RPI + lrow;
-        const int c = lpos ^ ((r >> SH) & (CH - 1));
-        pa[j] = row_ptr(A, m0 + r, flags) + 8 * c;
-        pb[j] = row_ptr(B, n0 + r, flags) + 8 * c;
-    }
-    auto issue = [&](int buf, int64_t k0) {
-        uint8_t *ab = sm + buf * 2 * DT::OPB, *bb = ab + DT::OPB;
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int r0 = w * 32 + j * RPI;
-            lds_load16(pa[j] + k0, ab + r0 * RB);
-            lds_load16(pb[j] + k0, bb + r0 * RB);
-        }
-    };
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[mb][nb][e] = 0.f;
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31), kq = lane >> 5;
-    const int sa0 = (ar >> SH) & (CH - 1), sa1 = ((ar + 32) >> SH) & (CH - 1);
-    const int sb0 = (br >> SH) & (CH - 1), sb1 = ((br + 32) >> SH) & (CH - 1);
-    const int64_t nk = K / BK;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk)
-            issue(cur ^ 1, (kt + 1) * BK);
-        const uint8_t *ab = sm + cur * 2 * DT::OPB, *bb = ab + DT::OPB;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + kq;
-            const bf16x8 a0 = *(const bf16x8 *)(ab + ar * RB + 16 * (c ^ sa0));
-            const bf16x8 a1 = *(const bf16x8 *)(ab + (ar + 32) * RB + 16 * (c ^ sa1));
-            const bf16x8 b0 = *(const bf16x8 *)(bb + br * RB + 16 * (c ^ sb0));
-            const bf16x8 b1 = *(const bf16x8 *)(bb + (br + 32) * RB + 16 * (c ^ sb1));
-            acc[0][0] = mfma(a0, b0, acc[0][0]);
-            acc[0][1] = mfma(a0, b1, acc[0][1]);
-            acc[1][0] = mfma(a1, b0, acc[1][0]);
-            acc[1][1] = mfma(a1, b1, acc[1][1]);
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next tile have landed
-        __syncthreads();
-    }
-}
-
 // Position of acc[mb][nb][e] in the block tile (32 x 32 matrix-core layout:
 // lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4).
-template <int WMB>
+template <int WM>
 __device__ inline int tile_row(int mb, int e)
 {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return wm * WMB * 32 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    return wm * WM * 32 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
+template <int WN>
 __device__ inline int tile_col(int nb)
 {
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-    return wn * 64 + nb * 32 + (lane & 31);
+    return wn * WN * 32 + nb * 32 + (lane & 31);
 }
 
 __device__ inline uint16_t bf16_rne(float f)
@@ -544,6 +441,172 @@ __device__ inline bool tile_of(uint32_t nM, uint32_t nN, uint32_t &mt, uint32_t 
     return true;
 }
 
+// Pipelined form of the main loop: block tile (64 WM) x (64 WN), four
+// wavefronts of (32 WM) x (32 WN) (WM, WN > 2 let each operand fragment read
+// from LDS feed more matrix-core ops).  Direct global -> LDS loads into S
+// stages of BK; S - 1 stages are in flight while one is read, and one barrier
+// per k-step both publishes the stage that landed and frees the one read last.
+// Rows are stored unpadded, BK / 8 chunks of 16 bytes each, chunk c of row r
+// at position c ^ ((r >> SH) & (CH - 1)), so the lanes of one ds_read_b128
+// (consecutive rows, one chunk) spread over the banks (the PMC bank-conflict
+// counter reads 0); each lane fetches the source chunk that belongs at its
+// position.  The next sub-step's fragments are read while the current one's
+// products run.
+template <int WM, int WN, int BK, int S>
+struct WideTile {
+    static constexpr int BM = 64 * WM, BN = 64 * WN;
+    static constexpr int CH = BK / 8, RB = CH * 16, RPI = 1024 / RB;
+    static constexpr int SH = CH == 8 ? 1 : (CH == 4 ? 2 : 3);
+    static constexpr int LA = BM / (4 * RPI), LB = BN / (4 * RPI);   // loads per thread per stage
+    static constexpr uint32_t STAGE = (uint32_t)(BM + BN) * RB;
+    static constexpr uint32_t SMEM = S * STAGE;
+    static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "whole loads per wavefront");
+    static_assert(S >= 2 && (S - 2) * (LA + LB) < 64, "outstanding loads fit the counter");
+};
+
+// s_waitcnt that waits for this wavefront's vector-memory count to drop to N
+// and leaves the other counters alone (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Block barrier with no memory fence.  A fence would make the compiler wait
+// for every outstanding LDS-bound load (they count as vector-memory ops), which
+// defeats the stages; the caller waits for exactly the loads it needs, this
+// waits for the wavefront's LDS reads, and the empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ inline void barrier_nofence()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt left alone
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int WM, int WN, int BK, int S>
+__device__ inline void mainloop_wide(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
+                                     uint8_t *sm, f32x16 (&acc)[WM][WN], uint32_t *flags)
+{
+    using WT = WideTile<WM, WN, BK, S>;
+    constexpr int CH = WT::CH, RB = WT::RB, RPI = WT::RPI, SH = WT::SH, LA = WT::LA, LB = WT::LB;
+    const int t = threadIdx.x, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int lrow = lane / CH, lpos = lane % CH;
+    // load j of wavefront w fills rows (4 j + w) RPI .. + RPI of its operand
+    const uint16_t *pa[LA], *pb[LB];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int r = (4 * j + w) * RPI + lrow;
+        pa[j] = row_ptr(A, m0 + r, flags) + 8 * (lpos ^ ((r >> SH) & (CH - 1)));
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int r = (4 * j + w) * RPI + lrow;
+        pb[j] = row_ptr(B, n0 + r, flags) + 8 * (lpos ^ ((r >> SH) & (CH - 1)));
+    }
+    auto issue = [&](int stage, int64_t k0) {
+        uint8_t *ab = sm + stage * WT::STAGE, *bb = ab + WT::BM * RB;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            lds_load16(pa[j] + k0, ab + (4 * j + w) * RPI * RB);
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            lds_load16(pb[j] + k0, bb + (4 * j + w) * RPI * RB);
+    };
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[mb][nb][e] = 0.f;
+    const int64_t nk = K / BK;
+    constexpr int KK = BK / 16, L = LA + LB;
+    static_assert(KK % 2 == 0, "fragment buffers alternate within a stage");
+    // every buffer starts filling at once; buffer kt % S is refilled with
+    // stage kt + S as soon as all wavefronts have read stage kt
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+        if (st < nk)
+            issue(st, st * BK);
+    // rows of one fragment start at a multiple of 32, so every fragment of a
+    // lane has the same swizzle
+    const int ar = wm * WM * 32 + (lane & 31), br = wn * WN * 32 + (lane & 31), kq = lane >> 5;
+    const int sa = (ar >> SH) & (CH - 1), sb = (br >> SH) & (CH - 1);
+    bf16x8 fa[2][WM], fb[2][WN];
+    auto rd = [&](int stage, int kk, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
+        const uint8_t *ab = sm + stage * WT::STAGE, *bb = ab + WT::BM * RB;
+        const int c = 2 * kk + kq;
+#pragma unroll
+        for (int mb = 0; mb < WM; ++mb)
+            a[mb] = *(const bf16x8 *)(ab + (ar + 32 * mb) * RB + 16 * (c ^ sa));
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+            b[nb] = *(const bf16x8 *)(bb + (br + 32 * nb) * RB + 16 * (c ^ sb));
+    };
+    auto mm = [&](int mb0, int mb1, const bf16x8 (&a)[WM], const bf16x8 (&b)[WN]) {
+#pragma unroll
+        for (int mb = mb0; mb < mb1; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < WN; ++nb)
+                acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
+    };
+    // one phase: the reads of the next fragments interleaved with the
+    // products of the current ones (read, product, read, ... then the rest of
+    // the products), fenced off from the phases around it
+    auto phase = [&](bool more, int stage, int kk, const bf16x8 (&a)[WM], const bf16x8 (&b)[WN],
+                     bf16x8 (&na)[WM], bf16x8 (&nb)[WN]) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (more)
+            rd(stage, kk, na, nb);
+        mm(0, WM, a, b);
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < WM + WN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix-core op
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, WM * WN - WM - WN, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nk >= S)
+        wait_vmcnt<(S - 1) * L>();
+    else
+        wait_vmcnt<0>();
+    barrier_nofence();
+    rd(0, 0, fa[0], fb[0]);
+    int cur = 0;
+    constexpr int last = (KK - 1) & 1;
+    // all but the last sub-step of a k-step; fragments of its sub-step 0 are
+    // in fa[0], fb[0]
+    auto inner = [&]() {
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk)
+            phase(true, cur, kk + 1, fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+    };
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        inner();
+        if (kt + S - 1 < nk)
+            wait_vmcnt<(S - 2) * L>();   // stage kt + 1 has landed; later ones may still fly
+        else
+            wait_vmcnt<0>();
+        barrier_nofence();               // ... for every wavefront, which are all done with stage kt
+        if (kt + S < nk)
+            issue(cur, (kt + S) * BK);
+        cur = cur + 1 == S ? 0 : cur + 1;
+        phase(true, cur, 0, fa[last], fb[last], fa[0], fb[0]);
+    }
+    inner();
+    phase(false, cur, 0, fa[last], fb[last], fa[0], fb[0]);
+    __syncthreads();   // LDS free for whatever follows
+}
+
 enum { EPI_FWD = 0, EPI_DZ = 1, EPI_DX = 2, EPI_DW = 3 };
 
 struct GemmArgs {
@@ -568,40 +631,48 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
-template <int EPI, int WMB, int BK, bool SINGLE, bool DIRECT>
+template <int EPI, int WM, int WN, int BK, int NS>
 constexpr uint32_t smem_bytes()
 {
-    constexpr uint32_t main = DIRECT ? DirectTile<BK>::SMEM : Tile<WMB, BK, SINGLE>::SMEM;
-    return EPI == EPI_FWD ? cmax(main, 64 * kLdt * 4 + 4 * 64 * 8)
+    constexpr uint32_t main = NS ? WideTile<WM, WN, BK, NS ? NS : 2>::SMEM : Tile<WM, BK>::SMEM;
+    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 64 * 8)
          : EPI == EPI_DZ  ? cmax(main, 128 * kLdb * 2 + 3 * 128 * 4)
                           : main;
 }
 
-template <int EPI, int WMB, int BK, bool SINGLE, bool DIRECT>
+// One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile, then the
+// epilogue EPI.  NS = 0: staged loop (WN = 2); NS > 0: pipelined loop with NS
+// stages.  The softmax epilogues take 128 x 128 tiles.
+template <int EPI, int WM, int WN, int BK, int NS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
-    static_assert(EPI == EPI_DX || EPI == EPI_DW || WMB == 2, "the softmax epilogues take 128-row tiles");
-    using TL = Tile<WMB, BK, SINGLE>;
-    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WMB, BK, SINGLE, DIRECT>()];
+    static_assert(EPI == EPI_DX || EPI == EPI_DW || (WM == 2 && WN == 2), "the softmax epilogues take 128 x 128 tiles");
+    static_assert(NS > 0 || WN == 2, "the staged loop takes 64-column wavefront tiles");
+    constexpr int BM = 64 * WM, BN = 64 * WN;
+    __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WM, WN, BK, NS>()];
     uint32_t mt, nt;
     if (!tile_of<EPI != EPI_DZ>(a.tiles_m, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
-    const int64_t m0 = (int64_t)mt * TL::BM, n0 = (int64_t)nt * TL::BN;
-    f32x16 acc[WMB][2];
-    if constexpr (DIRECT) {
-        static_assert(WMB == 2 && !SINGLE, "direct loads: 64 x 64 wave tiles, two buffers");
-        mainloop_direct<BK>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
-    } else {
-        mainloop<WMB, BK, SINGLE>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
-    }
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+    f32x16 acc[WM][WN];
+    if constexpr (NS > 0)
+        mainloop_wide<WM, WN, BK, NS ? NS : 2>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
+    else
+        mainloop<WM, BK>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
-        // two halves of 64 rows; wavefront q takes columns 32q .. 32q + 32 of
-        // every row of the half, and the four quarters meet in LDS
-        float *tile = reinterpret_cast<float *>(smem);                      // [64][kLdt]
-        float2 *pq = reinterpret_cast<float2 *>(smem + 64 * kLdt * 4);      // [4][64]
+        // two halves of 64 rows.  The half's two wavefronts store their
+        // accumulators column-major (a lane's 4 consecutive rows of one column
+        // are one 16-byte store); wavefront q then folds columns 32q .. 32q + 32
+        // of every row of the half, a row per lane (reads of consecutive rows),
+        // and the four quarters meet in LDS
+        float *tile = reinterpret_cast<float *>(smem);                      // [128][kLdt]
+        float2 *pq = reinterpret_cast<float2 *>(smem + 128 * kLdt * 4);     // [4][64]
         const int w = t >> 6, r = t & 63, q = w, wm = w >> 1;
+        const int64_t c0 = n0 + 32 * q;
+        const int64_t left = (int64_t)a.C - c0;
+        const int nv = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 32 ? 32 : (int)left));
         for (int h = 0; h < 2; ++h) {
             if (wm == h) {
 #pragma unroll
@@ -609,27 +680,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            tile[(tile_row<2>(mb, e) - 64 * h) * kLdt + tile_col(nb)] = acc[mb][nb][e];
+                        for (int g = 0; g < 4; ++g)
+                            *(float4 *)(tile + tile_col<2>(nb) * kLdt + tile_row<2>(mb, 4 * g) - 64 * h) =
+                                make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                            acc[mb][nb][4 * g + 3]);
             }
             __syncthreads();
-            const int64_t i = m0 + 64 * h + r, c0 = n0 + 32 * q;
-            const int64_t left = (int64_t)a.C - c0;
-            const int nv = left <= 0 ? 0 : (left >= 32 ? 32 : (int)left);
-            const float *zr = tile + r * kLdt + 32 * q;
+            const int64_t i = m0 + 64 * h + r;
+            const float *zc = tile + 32 * q * kLdt + r;   // column 32q + k at zc[k kLdt]
             float m = -INFINITY, s = 0.f;
-            if (nv > 0) {
+            if (nv == 32) {
+                float v[32];
+#pragma unroll
                 for (int k = 0; k < 32; ++k)
-                    if (k < nv)
-                        m = fmaxf(m, zr[k]);
+                    v[k] = zc[k * kLdt];
+#pragma unroll
                 for (int k = 0; k < 32; ++k)
-                    if (k < nv)
-                        s += __expf(zr[k] - m);
+                    m = fmaxf(m, v[k]);
+#pragma unroll
+                for (int k = 0; k < 32; ++k)
+                    s += __expf(v[k] - m);
+            } else if (nv > 0) {
+                for (int k = 0; k < nv; ++k)
+                    m = fmaxf(m, zc[k * kLdt]);
+                for (int k = 0; k < nv; ++k)
+                    s += __expf(zc[k * kLdt] - m);
             }
             if (i < a.T) {
                 const int64_t y = a.slot[i];
                 if (y >= c0 && y < c0 + nv)
-                    a.zt[i] = zr[y - c0];
+                    a.zt[i] = zc[(y - c0) * kLdt];
             }
             pq[q * 64 + r] = make_float2(m, s);
             __syncthreads();
@@ -666,12 +746,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         // accumulator entries: 4 adjacent elements of a transposed row, stored
         // from registers; the row-major copy goes through LDS
 #pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                 for (int e4 = 0; e4 < 16; e4 += 4) {
-                    const int cc = tile_col(nb), r4 = tile_row<WMB>(mb, e4);
+                    const int cc = tile_col<2>(nb), r4 = tile_row<2>(mb, e4);
                     const int64_t c = n0 + cc;
                     uint16_t h[4];
 #pragma unroll
@@ -698,28 +778,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
+        for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t i = m0 + tile_row<WMB>(mb, e);
+                const int64_t i = m0 + tile_row<WM>(mb, e);
                 if (i < a.T) {
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        a.out[i * kD + n0 + tile_col(nb)] = acc[mb][nb][e];
+                    for (int nb = 0; nb < WN; ++nb)
+                        a.out[i * kD + n0 + tile_col<WN>(nb)] = acc[mb][nb][e];
                 }
             }
     } else {   // EPI_DW
 #pragma unroll
-        for (int mb = 0; mb < WMB; ++mb)
+        for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t c = m0 + tile_row<WMB>(mb, e);
+                const int64_t c = m0 + tile_row<WM>(mb, e);
                 if (c < a.C) {
                     const int32_t v = a.cand[c];
                     if ((uint32_t)v < (uint32_t)a.V) {
 #pragma unroll
-                        for (int nb = 0; nb < 2; ++nb) {
-                            float *o = a.out + (int64_t)v * kD + n0 + tile_col(nb);
+                        for (int nb = 0; nb < WN; ++nb) {
+                            float *o = a.out + (int64_t)v * kD + n0 + tile_col<WN>(nb);
                             *o += acc[mb][nb][e];
                         }
                     }
@@ -957,7 +1037,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     hipStream_t s = (hipStream_t)stream;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = (uint32_t)nct;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdBK, kFwdSingle, kFwdDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, 2, kFwdBK, kFwdS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
@@ -1014,32 +1094,33 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.K = kD;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = blocks(Cp, 128);
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, kDzBK, kDzSingle, kDzDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, 2, kDzBK, kDzS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
     a.B = Rows{wst, Cp, nullptr, kD, V};
     a.K = Cp;
     a.out = dX;
-    a.tiles_m = blocks(Tq, Tile<2, kDxBK>::BM);
-    a.tiles_n = kD / 128;
-    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, 2, kDxBK, kDxSingle, kDxDirect>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
-           dim3(256), s, a);
+    a.tiles_m = blocks(Tq, 64 * kDxWM);
+    a.tiles_n = kD / (64 * kDxWN);
+    launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, kDxWM, kDxWN, kDxBK, kDxS>,
+           dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
 
     a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
     a.B = Rows{xt, Tq, nullptr, kD, V};
     a.K = Tq;
     a.out = dW;
-    a.tiles_m = blocks(Cp, Tile<2, kDwBK>::BM);
+    a.tiles_m = blocks(Cp, 128);
     a.tiles_n = kD / 128;
     // dW's blocks are few and long (k = T): take the form whose resident
-    // slots (two or three blocks per CU) leave less of the last round idle
+    // slots (two blocks per CU pipelined, three staged) leave less of the
+    // last round idle
     const uint32_t nb = a.tiles_m * a.tiles_n;
     if (round_fill(nb, 3 * kCUs) > round_fill(nb, 2 * kCUs))
-        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, true, false>,
+        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 2, kDwBK, 0>,
                dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
     else
-        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, kDwBK, kDwSingle, kDwDirect>,
+        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 2, kDwBK, kDwS>,
                dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
     return done(hipGetLastError());
 }
