@@ -30,7 +30,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
 constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
-constexpr int kLdb = 128 + 8;   // bf16 per row of the dz epilogue tile
+constexpr int kLdb = 128 + 16;  // bf16 per row of the dz epilogue's row-major tile (paired 4-byte writes conflict-free)
+constexpr int kLdbT = 128 + 8;  // bf16 per row of its transposed tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Per contraction: the k-step BK and the main-loop form, NS = 0 for the
 // loop staged through registers into one LDS buffer (three blocks per CU),
@@ -742,31 +743,58 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             s_y[t] = ok ? a.slot[i] : -1;
         }
         __syncthreads();
-        // a lane holds 4 consecutive rows of one column per group of 4
-        // accumulator entries: 4 adjacent elements of a transposed row, stored
-        // from registers; the row-major copy goes through LDS
+        // dz of the tile as bf16, kept packed in registers (a lane holds 4
+        // consecutive rows of one column per group of 4 accumulator entries)
+        // and written through LDS twice: row-major, then transposed, so both
+        // copies leave as whole 256-byte rows
+        uint32_t hp[2][2][4][2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
+                const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
+                const int4 y4 = *(const int4 *)(s_y + r4);
+                const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
+                const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int cc = tile_col<2>(nb);
+                    const int c = (int)n0 + cc;        // candidates < 2^31
+                    const bool col_ok = c < a.C;
+                    uint16_t h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // padding rows and columns, and a void batch, give 0
+                        // (masked, not branched around: no divergence)
+                        const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
+                        const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
+                        const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
+                        const float d = __uint_as_float(__float_as_uint(dv) & keep);
+                        h[j] = bf16_rne(d);
+                    }
+                    hp[mb][nb][g][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    hp[mb][nb][g][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                }
+            }
+        // row-major tile: lanes l and l ^ 1 hold adjacent columns, so they swap
+        // halves and each writes two rows of a column pair (4-byte writes):
+        // even lanes rows r4, r4 + 1 of columns cc, cc + 1, odd lanes rows
+        // r4 + 2, r4 + 3 of columns cc - 1, cc
+        const int odd = t & 1;
+        uint16_t *bp = bt + odd * (2 * kLdb - 1);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int e4 = 0; e4 < 16; e4 += 4) {
-                    const int cc = tile_col<2>(nb), r4 = tile_row<2>(mb, e4);
-                    const int64_t c = n0 + cc;
-                    uint16_t h[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int rr = r4 + j;
-                        float d = 0.f;   // padding rows and columns, and a void batch, give 0
-                        if (c < a.C && s_g[rr] != 0.f) {
-                            const float p = __expf(acc[mb][nb][e4 + j] - s_l[rr]);
-                            d = s_g[rr] * (p - (s_y[rr] == c ? 1.f : 0.f));
-                        }
-                        h[j] = bf16_rne(d);
-                        bt[rr * kLdb + cc] = h[j];
-                    }
-                    *(uint2 *)(a.dzt + (n0 + cc) * a.Tq + m0 + r4) =
-                        make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t x = hp[mb][nb][g][0], y = hp[mb][nb][g][1];   // rows r4, r4 + 1 | r4 + 2, r4 + 3
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x : y), 0xB1, 0xF, 0xF, false);
+                    const uint32_t lo = odd ? o : x, hi = odd ? y : o;   // left and right column
+                    uint16_t *q = bp + tile_row<2>(mb, 4 * g) * kLdb + tile_col<2>(nb);
+                    *(uint32_t *)q = (lo & 0xffffu) | (hi << 16);
+                    *(uint32_t *)(q + kLdb) = (lo >> 16) | (hi & 0xffff0000u);
                 }
         __syncthreads();
         // row-major: 16 chunks of 16 B per row
@@ -775,6 +803,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             const int rr = (t >> 4) + 16 * p, q = t & 15;
             const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
             *(u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8) = v;
+        }
+        __syncthreads();
+        // transposed: row cc of the LDS tile holds column cc of dz
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(uint2 *)(bt + tile_col<2>(nb) * kLdbT + tile_row<2>(mb, 4 * g)) =
+                        make_uint2(hp[mb][nb][g][0], hp[mb][nb][g][1]);
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int cr = (t >> 4) + 16 * p, q = t & 15;
+            const u32x4 v = *(const u32x4 *)(bt + cr * kLdbT + q * 8);
+            *(u32x4 *)(a.dzt + (n0 + cr) * a.Tq + m0 + q * 8) = v;
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
