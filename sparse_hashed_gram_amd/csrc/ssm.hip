@@ -42,7 +42,7 @@ constexpr int kTile = 128;      // T and C are padded to multiples of this
 constexpr int kFwdBK = 64, kFwdS = 2;                        // forward, 128 x 128
 constexpr int kDzBK = 64, kDzS = 0;                          // dz, 128 x 128
 constexpr int kDxWM = 2, kDxWN = 3, kDxBK = 64, kDxS = 2;    // dX, 128 x 192
-constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 128 (or staged: three blocks per CU)
+constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 192 or 128 x 128 by round fill
 
 // Staged form's block tile: four wavefronts, 2 along M x 2 along N; a
 // wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
@@ -1156,17 +1156,21 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.K = Tq;
     a.out = dW;
     a.tiles_m = blocks(Cp, 128);
-    a.tiles_n = kD / 128;
-    // dW's blocks are few and long (k = T): take the form whose resident
-    // slots (two blocks per CU pipelined, three staged) leave less of the
-    // last round idle
-    const uint32_t nb = a.tiles_m * a.tiles_n;
-    if (round_fill(nb, 3 * kCUs) > round_fill(nb, 2 * kCUs))
-        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 2, kDwBK, 0>,
+    // dW's blocks are few and long (k = T), so the last round of resident
+    // blocks (two per CU) decides much of its time: 128 x 192 tiles do about
+    // 1.25x the work per unit time of 128 x 128 ones (measured at equal
+    // fill), and the 128 x 128 form wins only where it fills its rounds that
+    // much better (10,240 candidates: 480 blocks in 512 slots)
+    const uint32_t nb2 = a.tiles_m * (kD / 128), nb3 = a.tiles_m * (kD / 192);
+    if (1.25 * round_fill(nb3, 2 * kCUs) >= round_fill(nb2, 2 * kCUs)) {
+        a.tiles_n = kD / 192;
+        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 3, kDwBK, kDwS>,
                dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
-    else
+    } else {
+        a.tiles_n = kD / 128;
         launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 2, kDwBK, kDwS>,
                dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
+    }
     return done(hipGetLastError());
 }
 

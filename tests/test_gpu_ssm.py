@@ -348,9 +348,10 @@ def test_graph_replay_equals_eager():
     assert N.device_status(cfg, ws_g) == 0 and N.device_status(cfg, ws_e) == 0
 
 
-def test_backward_dw_three_blocks_per_cu_form():
-    # 14,336 candidates: dW's 672 blocks fill three-per-CU slots better than
-    # two-per-CU ones, so the library takes the other dW form; same bar
+def test_backward_dw_wide_tile_form():
+    # 14,336 candidates: dW's 128 x 192 tiles (448 blocks in 512 slots) beat
+    # the 128 x 128 ones (672 blocks, two rounds), so the library takes the
+    # other dW form; same bar
     N = S()
     T, V, C = 700, 50304, 14336
     tgt, X, W, perm, g = _inputs(33, T, V)
