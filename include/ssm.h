@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 #define SSM_OK 0
 #define SSM_ENULL -1    /* a required pointer is NULL                          */
@@ -62,13 +62,16 @@ extern "C" {
                                      was read in its place                   */
 #define SSM_FLAG_BAD_SLOT 0x10u   /* a slot outside [0, C): that position's
                                      loss is NaN and its one-hot term absent */
+#define SSM_FLAG_NO_LOGITS 0x20u  /* ssm_loss_bwd found no logits stored by an
+                                     ssm_loss_fwd of the same T since the last
+                                     ssm_candidates: gradients are zero      */
 
 /* kernel groups for ssm_profile_events */
 #define SSM_PROF_CAND 0   /* the candidate-set kernels                        */
 #define SSM_PROF_FWD 1    /* forward contraction + per-tile softmax sums      */
 #define SSM_PROF_LSE 2    /* per-position log-sum-exp and loss                */
 #define SSM_PROF_TRANS 3  /* the backward's operand transposes                */
-#define SSM_PROF_DZ 4     /* recomputed logits -> dz (bf16)                   */
+#define SSM_PROF_DZ 4     /* stored logits -> dz (bf16)                       */
 #define SSM_PROF_DX 5     /* dX = dz W_S                                      */
 #define SSM_PROF_DW 6     /* dW[S] += dz^T X                                  */
 #define SSM_PROF_GROUPS 7
@@ -84,9 +87,10 @@ typedef struct ssm_config {
 int ssm_abi_version(void);
 const char *ssm_status_string(int status);
 
-/* Workspace size for cfg (host).  About 4 (T+128)(C+128) bytes for the two
- * layouts of dz, plus 2 D (T + C + 256) bytes of transposed operands and 8
- * T C/128 bytes of per-tile sums. */
+/* Workspace size for cfg (host).  About 4 (T+128)(C+128) bytes for the
+ * forward's fp32 logits, 4 (T+128)(C+128) for the two layouts of dz, plus
+ * 2 D (T + C + 256) bytes of transposed operands and 8 T C/128 bytes of
+ * per-tile sums (about 4 GB at T = 49,152, C = 10,240). */
 int ssm_workspace_bytes(const ssm_config *cfg, uint64_t *bytes);
 
 /* Prepares a workspace (256-byte aligned, ws_bytes from ssm_workspace_bytes)
@@ -107,7 +111,8 @@ int ssm_candidates(const ssm_config *cfg, void *ws, const int32_t *targets, int6
 
 /* Forward: loss and lse (fp32 [T] each) of every position over the
  * candidate set.  X: bf16 [T][768]; W: bf16 [V][768] (the lm_head);
- * cand, slot as from ssm_candidates.  T = 0 enqueues nothing. */
+ * cand, slot as from ssm_candidates.  The fp32 logits stay in the workspace
+ * for ssm_loss_bwd.  T = 0 enqueues nothing. */
 int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W,
                  const int32_t *cand, const int32_t *slot, int64_t T, float *loss,
                  float *lse, void *stream);
@@ -115,7 +120,11 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W,
 /* Backward: dX = dz W_S (fp32 [T][768], overwritten) and dW[cand[c]] +=
  * (dz^T X)[c] (fp32 [V][768]; rows outside the candidate set are not
  * touched).  lse: the forward's; dloss: fp32 [T], the upstream gradient g.
- * The logits are recomputed, not stored.  dX must not overlap X or dW. */
+ * dz comes from the logits the last ssm_loss_fwd on this workspace stored:
+ * call it after that forward with the same X, W, cand, slot and T (the
+ * library checks T and that no ssm_candidates came between, see
+ * SSM_FLAG_NO_LOGITS; X and W are the caller's to keep).  dX must not
+ * overlap X or dW. */
 int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W,
                  const int32_t *cand, const int32_t *slot, const float *lse,
                  const float *dloss, int64_t T, float *dX, float *dW, void *stream);

@@ -4,17 +4,18 @@
 // work fused into their epilogues:
 //
 //   forward   z = X W_S^T per 128 x 128 tile -> per-tile (max, sum exp) of
-//             each position, the target's logit; a per-position pass folds
-//             the tiles into lse and the loss.  z never reaches memory.
-//   backward  z recomputed per tile -> dz = g (exp(z - lse) - onehot), bf16,
-//             written row-major and transposed; dX = dz W_S; dW[S] += dz^T X.
+//             each position, the target's logit, and z itself (fp32, kept
+//             in the workspace); a per-position pass folds the tiles into
+//             lse and the loss.
+//   backward  a streaming pass over the stored z -> dz = g (exp(z - lse) -
+//             onehot), bf16, written row-major and transposed; dX = dz W_S;
+//             dW[S] += dz^T X.
 //
 // Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // k-contiguous in memory (the backward's transposed operands are written
-// first), so one kernel template serves all four: four wavefronts per block,
-// each owning WM x WN matrix-core tiles of 32 x 32, and one of two main
-// loops, staged through registers into one LDS buffer or pipelined with
-// direct global -> LDS loads.
+// first), so one kernel template serves all three: four wavefronts per
+// block, each owning WM x WN matrix-core tiles of 32 x 32, and a pipelined
+// main loop with direct global -> LDS loads.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -27,36 +28,21 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
 constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
 constexpr int kLdb = 128 + 16;  // bf16 per row of the dz epilogue's row-major tile (paired 4-byte writes conflict-free)
 constexpr int kLdbT = 128 + 8;  // bf16 per row of its transposed tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
-// Per contraction: the k-step BK and the main-loop form, NS = 0 for the
-// loop staged through registers into one LDS buffer (three blocks per CU),
-// NS > 0 for direct global -> LDS loads into NS pipelined stages (two blocks
-// per CU); and the block tile, four wavefronts of WM x WN matrix-core tiles
-// of 32 x 32.  Chosen by measurement on MI355X (49,152 positions x 10,240
-// candidates x 768).
+// Per contraction: the k-step BK, the number NS of pipelined stages (two
+// blocks per CU), and the block tile, four wavefronts of WM x WN matrix-core
+// tiles of 32 x 32.  Chosen by measurement on MI355X (49,152 positions x
+// 10,240 candidates x 768).
 constexpr int kFwdBK = 64, kFwdS = 2;                        // forward, 128 x 128
-constexpr int kDzBK = 64, kDzS = 0;                          // dz, 128 x 128
 constexpr int kDxWM = 2, kDxWN = 3, kDxBK = 64, kDxS = 2;    // dX, 128 x 192
 constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 192 or 128 x 128 by round fill
 
-// Staged form's block tile: four wavefronts, 2 along M x 2 along N; a
-// wavefront owns WMB x 2 matrix-core tiles of 32 x 32 (WMB 32 x 32 row blocks
-// by 64 columns).  BK: k-elements per LDS buffer (one buffer; the next k-step
-// is prefetched into registers).
-template <int WMB, int BK>
-struct Tile {
-    static constexpr int BM = 2 * WMB * 32, BN = 128;
-    static constexpr int LDK = BK + 8;                  // bf16 per LDS operand row (16-byte reads conflict-free)
-    static constexpr int CH = BK / 8;                   // 16-byte chunks per row per k-step
-    static constexpr int RP = 256 / CH;                 // rows one pass of the block's loads covers
-    static constexpr int LA = BM / RP, LB = BN / RP;    // 16-byte loads per thread per operand
-    static constexpr uint32_t SMEM = (BM + BN) * LDK * 2u;
-};
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
 constexpr int kSelectThreads = 1024;
@@ -66,13 +52,14 @@ struct Hdr {
     uint32_t flags;        // sticky SSM_FLAG_*
     uint32_t void_batch;   // nonzero: the last candidate set is void
     uint32_t n_present;    // distinct targets of the last candidate set
-    uint32_t pad[60];
+    int32_t z_T;           // T of the logits the last forward stored; -1: none for this candidate set
+    uint32_t pad[59];
 };
 static_assert(sizeof(Hdr) == 256, "header is 256 bytes");
 
 struct Layout {
     int64_t Tp, Cp;   // padded maxima
-    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, dzt, total;
+    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, dzt, zb, total;
 };
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -97,6 +84,7 @@ Layout layout(const ssm_config *c)
     L.wst = take(2ull * kD * L.Cp);
     L.dz = take(2ull * L.Tp * L.Cp);
     L.dzt = take(2ull * L.Tp * L.Cp);
+    L.zb = take(4ull * L.Tp * L.Cp);
     L.total = o;
     return L;
 }
@@ -110,6 +98,7 @@ __global__ void init_kernel(Hdr *h)
         h->flags = 0;
         h->void_batch = 0;
         h->n_present = 0;
+        h->z_T = -1;
     }
 }
 
@@ -126,8 +115,10 @@ __global__ void cand_clear_kernel(int32_t *rank, int32_t *cnt, int32_t V, Hdr *h
         rank[v] = 0;
         cnt[v] = 0;
     }
-    if (v == 0)
+    if (v == 0) {
         h->void_batch = 0;
+        h->z_T = -1;   // a new candidate set: no stored logits belong to it yet
+    }
 }
 
 // rank[] holds the presence mark (1) until the select kernel ranks it.
@@ -295,83 +286,6 @@ __device__ inline const uint16_t *row_ptr(const Rows &r, int64_t i, uint32_t *fl
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// acc[mb][nb] = the wavefront's 32 x 32 tiles of C[m0 + ..][n0 + ..]; K is a
-// multiple of BK.  Ends with a block barrier (LDS free for the epilogue).
-template <int WMB, int BK>
-__device__ inline void mainloop(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
-                                uint16_t *sm, f32x16 (&acc)[WMB][2], uint32_t *flags)
-{
-    using TL = Tile<WMB, BK>;
-    constexpr int LDK = TL::LDK;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int lr = t / TL::CH, lc = (t % TL::CH) * 8;   // loader: rows lr + RP j, 16 bytes at column lc
-    const uint16_t *pa[TL::LA], *pb[TL::LB];
-#pragma unroll
-    for (int j = 0; j < TL::LA; ++j)
-        pa[j] = row_ptr(A, m0 + lr + TL::RP * j, flags) + lc;
-#pragma unroll
-    for (int j = 0; j < TL::LB; ++j)
-        pb[j] = row_ptr(B, n0 + lr + TL::RP * j, flags) + lc;
-    uint16_t *As = sm, *Bs = sm + TL::BM * LDK;
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[mb][nb][e] = 0.f;
-
-    u32x4 ra[TL::LA], rb[TL::LB];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int j = 0; j < TL::LA; ++j)
-            ra[j] = *(const u32x4 *)(pa[j] + k0);
-#pragma unroll
-        for (int j = 0; j < TL::LB; ++j)
-            rb[j] = *(const u32x4 *)(pb[j] + k0);
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int j = 0; j < TL::LA; ++j)
-            *(u32x4 *)(As + (lr + TL::RP * j) * LDK + lc) = ra[j];
-#pragma unroll
-        for (int j = 0; j < TL::LB; ++j)
-            *(u32x4 *)(Bs + (lr + TL::RP * j) * LDK + lc) = rb[j];
-    };
-    gload(0);
-    sstore();
-    __syncthreads();
-
-    const int ar = wm * WMB * 32 + (lane & 31), br = wn * 64 + (lane & 31), kh = 8 * (lane >> 5);
-    const int64_t nk = K / BK;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more)
-            gload((kt + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8 a[WMB], b[2];
-#pragma unroll
-            for (int mb = 0; mb < WMB; ++mb)
-                a[mb] = *(const bf16x8 *)(As + (ar + 32 * mb) * LDK + kk + kh);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                b[nb] = *(const bf16x8 *)(Bs + (br + 32 * nb) * LDK + kk + kh);
-#pragma unroll
-            for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = mfma(a[mb], b[nb], acc[mb][nb]);
-        }
-        __syncthreads();   // every wavefront is done reading the buffer
-        if (more) {
-            sstore();
-            __syncthreads();
-        }
-    }
 }
 
 // Direct global -> LDS load (global_load_lds_dwordx4): lane l of a wavefront
@@ -622,6 +536,7 @@ struct GemmArgs {
     const float *g;        // [T]
     float *zt;             // forward: target logits [T]
     float2 *part;          // forward: per-tile (max, sum exp) [C / 128][T]
+    float *zb;             // forward -> dz: fp32 logits, one 64 KB block per 128 x 128 tile
     uint16_t *dz;          // [Tq][Cp] bf16
     uint16_t *dzt;         // [Cp][Tq] bf16
     int64_t Tq, Cp;
@@ -632,37 +547,182 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
+// Logits buffer: one block of 128 x 128 fp32 per tile (mt, nt), holding the
+// accumulators as the 256 threads of a block have them: entry 4 g + j of
+// matrix-core tile (mb, nb) of thread t at float4 ((2 mb + nb) 4 + g) 256 + t.
+__device__ inline f32x4 *logits_block(const GemmArgs &a, uint32_t mt, uint32_t nt)
+{
+    return reinterpret_cast<f32x4 *>(a.zb) + ((int64_t)mt * a.tiles_n + nt) * (128 * 128 / 4);
+}
+__device__ inline void store_logits(const GemmArgs &a, uint32_t mt, uint32_t nt, const f32x16 (&acc)[2][2])
+{
+    f32x4 *zb = logits_block(a, mt, nt);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                __builtin_nontemporal_store(
+                    f32x4{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]},
+                    zb + ((2 * mb + nb) * 4 + g) * 256 + threadIdx.x);
+}
+
+// dz from the stored logits, one 128 x 128 tile per block:
+// dz = g (exp(z - lse) - onehot) rounded to bf16, written row-major [Tq][Cp]
+// and transposed [Cp][Tq].  Logits that the last forward did not store for
+// this candidate set and T give zeros and SSM_FLAG_NO_LOGITS.
+__global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
+{
+    __shared__ __align__(16) uint8_t smem[128 * kLdb * 2 + 3 * 128 * 4];
+    uint32_t mt, nt;
+    if (!tile_of<false>(a.tiles_m, a.tiles_n, mt, nt))
+        return;
+    const int64_t m0 = (int64_t)mt * 128, n0 = (int64_t)nt * 128;
+    const int t = threadIdx.x;
+    f32x16 acc[2][2];
+    {
+        const f32x4 *zb = logits_block(a, mt, nt);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v = __builtin_nontemporal_load(zb + ((2 * mb + nb) * 4 + g) * 256 + t);
+                    acc[mb][nb][4 * g] = v[0];
+                    acc[mb][nb][4 * g + 1] = v[1];
+                    acc[mb][nb][4 * g + 2] = v[2];
+                    acc[mb][nb][4 * g + 3] = v[3];
+                }
+    }
+    const bool have = a.h->z_T == (int32_t)a.T;
+    if (!have && blockIdx.x == 0 && t == 0)
+        atomicOr(&a.h->flags, SSM_FLAG_NO_LOGITS);
+        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
+        float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
+        float *s_g = s_l + 128;
+        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
+        if (t < 128) {
+            const int64_t i = m0 + t;
+            const bool ok = have && i < a.T && a.h->void_batch == 0;
+            s_l[t] = ok ? a.lse[i] : 0.f;
+            s_g[t] = ok ? a.g[i] : 0.f;
+            s_y[t] = ok ? a.slot[i] : -1;
+        }
+        __syncthreads();
+        // dz of the tile as bf16, kept packed in registers (a lane holds 4
+        // consecutive rows of one column per group of 4 accumulator entries)
+        // and written through LDS twice: row-major, then transposed, so both
+        // copies leave as whole 256-byte rows
+        uint32_t hp[2][2][4][2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
+                const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
+                const int4 y4 = *(const int4 *)(s_y + r4);
+                const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
+                const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int cc = tile_col<2>(nb);
+                    const int c = (int)n0 + cc;        // candidates < 2^31
+                    const bool col_ok = c < a.C;
+                    uint16_t h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // padding rows and columns, and a void batch, give 0
+                        // (masked, not branched around: no divergence)
+                        const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
+                        const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
+                        const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
+                        const float d = __uint_as_float(__float_as_uint(dv) & keep);
+                        h[j] = bf16_rne(d);
+                    }
+                    hp[mb][nb][g][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    hp[mb][nb][g][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                }
+            }
+        // row-major tile: lanes l and l ^ 1 hold adjacent columns, so they swap
+        // halves and each writes two rows of a column pair (4-byte writes):
+        // even lanes rows r4, r4 + 1 of columns cc, cc + 1, odd lanes rows
+        // r4 + 2, r4 + 3 of columns cc - 1, cc
+        const int odd = t & 1;
+        uint16_t *bp = bt + odd * (2 * kLdb - 1);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t x = hp[mb][nb][g][0], y = hp[mb][nb][g][1];   // rows r4, r4 + 1 | r4 + 2, r4 + 3
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x : y), 0xB1, 0xF, 0xF, false);
+                    const uint32_t lo = odd ? o : x, hi = odd ? y : o;   // left and right column
+                    uint16_t *q = bp + tile_row<2>(mb, 4 * g) * kLdb + tile_col<2>(nb);
+                    *(uint32_t *)q = (lo & 0xffffu) | (hi << 16);
+                    *(uint32_t *)(q + kLdb) = (lo >> 16) | (hi & 0xffff0000u);
+                }
+        __syncthreads();
+        // row-major: 16 chunks of 16 B per row
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int rr = (t >> 4) + 16 * p, q = t & 15;
+            const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
+            __builtin_nontemporal_store(v, (u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8));
+        }
+        __syncthreads();
+        // transposed: row cc of the LDS tile holds column cc of dz
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(uint2 *)(bt + tile_col<2>(nb) * kLdbT + tile_row<2>(mb, 4 * g)) =
+                        make_uint2(hp[mb][nb][g][0], hp[mb][nb][g][1]);
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int cr = (t >> 4) + 16 * p, q = t & 15;
+            const u32x4 v = *(const u32x4 *)(bt + cr * kLdbT + q * 8);
+            __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + (n0 + cr) * a.Tq + m0 + q * 8));
+        }
+}
+
+
 template <int EPI, int WM, int WN, int BK, int NS>
 constexpr uint32_t smem_bytes()
 {
-    constexpr uint32_t main = NS ? WideTile<WM, WN, BK, NS ? NS : 2>::SMEM : Tile<WM, BK>::SMEM;
-    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 64 * 8)
-         : EPI == EPI_DZ  ? cmax(main, 128 * kLdb * 2 + 3 * 128 * 4)
-                          : main;
+    constexpr uint32_t main = WideTile<WM, WN, BK, NS>::SMEM;
+    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 64 * 8) : main;
 }
 
-// One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile, then the
-// epilogue EPI.  NS = 0: staged loop (WN = 2); NS > 0: pipelined loop with NS
-// stages.  The softmax epilogues take 128 x 128 tiles.
+// One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile (the
+// pipelined loop, NS stages), then the epilogue EPI.  The forward's softmax
+// epilogue takes 128 x 128 tiles.
 template <int EPI, int WM, int WN, int BK, int NS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
-    static_assert(EPI == EPI_DX || EPI == EPI_DW || (WM == 2 && WN == 2), "the softmax epilogues take 128 x 128 tiles");
-    static_assert(NS > 0 || WN == 2, "the staged loop takes 64-column wavefront tiles");
+    static_assert(EPI == EPI_FWD || EPI == EPI_DX || EPI == EPI_DW, "contraction epilogues");
+    static_assert(EPI != EPI_FWD || (WM == 2 && WN == 2), "the forward's epilogue takes 128 x 128 tiles");
+    static_assert(NS >= 2, "pipelined loop");
     constexpr int BM = 64 * WM, BN = 64 * WN;
     __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WM, WN, BK, NS>()];
     uint32_t mt, nt;
-    if (!tile_of<EPI != EPI_DZ>(a.tiles_m, a.tiles_n, mt, nt))
+    if (!tile_of<true>(a.tiles_m, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
     const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
     f32x16 acc[WM][WN];
-    if constexpr (NS > 0)
-        mainloop_wide<WM, WN, BK, NS ? NS : 2>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
-    else
-        mainloop<WM, BK>(a.A, a.B, a.K, m0, n0, reinterpret_cast<uint16_t *>(smem), acc, &a.h->flags);
+    mainloop_wide<WM, WN, BK, NS>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
+        // the tile's fp32 logits for the dz kernel, in the accumulators' own
+        // layout (each store: 256 lanes x 16 bytes, contiguous; non-temporal:
+        // 4 T C bytes would otherwise push the operands out of the caches)
+        store_logits(a, mt, nt, acc);
         // two halves of 64 rows.  The half's two wavefronts store their
         // accumulators column-major (a lane's 4 consecutive rows of one column
         // are one 16-byte store); wavefront q then folds columns 32q .. 32q + 32
@@ -730,97 +790,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             }
             __syncthreads();
         }
-    } else if constexpr (EPI == EPI_DZ) {
-        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
-        float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
-        float *s_g = s_l + 128;
-        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
-        if (t < 128) {
-            const int64_t i = m0 + t;
-            const bool ok = i < a.T && a.h->void_batch == 0;
-            s_l[t] = ok ? a.lse[i] : 0.f;
-            s_g[t] = ok ? a.g[i] : 0.f;
-            s_y[t] = ok ? a.slot[i] : -1;
-        }
-        __syncthreads();
-        // dz of the tile as bf16, kept packed in registers (a lane holds 4
-        // consecutive rows of one column per group of 4 accumulator entries)
-        // and written through LDS twice: row-major, then transposed, so both
-        // copies leave as whole 256-byte rows
-        uint32_t hp[2][2][4][2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
-                const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
-                const int4 y4 = *(const int4 *)(s_y + r4);
-                const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
-                const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int cc = tile_col<2>(nb);
-                    const int c = (int)n0 + cc;        // candidates < 2^31
-                    const bool col_ok = c < a.C;
-                    uint16_t h[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // padding rows and columns, and a void batch, give 0
-                        // (masked, not branched around: no divergence)
-                        const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
-                        const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
-                        const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
-                        const float d = __uint_as_float(__float_as_uint(dv) & keep);
-                        h[j] = bf16_rne(d);
-                    }
-                    hp[mb][nb][g][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-                    hp[mb][nb][g][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-                }
-            }
-        // row-major tile: lanes l and l ^ 1 hold adjacent columns, so they swap
-        // halves and each writes two rows of a column pair (4-byte writes):
-        // even lanes rows r4, r4 + 1 of columns cc, cc + 1, odd lanes rows
-        // r4 + 2, r4 + 3 of columns cc - 1, cc
-        const int odd = t & 1;
-        uint16_t *bp = bt + odd * (2 * kLdb - 1);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t x = hp[mb][nb][g][0], y = hp[mb][nb][g][1];   // rows r4, r4 + 1 | r4 + 2, r4 + 3
-                    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x : y), 0xB1, 0xF, 0xF, false);
-                    const uint32_t lo = odd ? o : x, hi = odd ? y : o;   // left and right column
-                    uint16_t *q = bp + tile_row<2>(mb, 4 * g) * kLdb + tile_col<2>(nb);
-                    *(uint32_t *)q = (lo & 0xffffu) | (hi << 16);
-                    *(uint32_t *)(q + kLdb) = (lo >> 16) | (hi & 0xffff0000u);
-                }
-        __syncthreads();
-        // row-major: 16 chunks of 16 B per row
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int rr = (t >> 4) + 16 * p, q = t & 15;
-            const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
-            *(u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8) = v;
-        }
-        __syncthreads();
-        // transposed: row cc of the LDS tile holds column cc of dz
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(uint2 *)(bt + tile_col<2>(nb) * kLdbT + tile_row<2>(mb, 4 * g)) =
-                        make_uint2(hp[mb][nb][g][0], hp[mb][nb][g][1]);
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int cr = (t >> 4) + 16 * p, q = t & 15;
-            const u32x4 v = *(const u32x4 *)(bt + cr * kLdbT + q * 8);
-            *(u32x4 *)(a.dzt + (n0 + cr) * a.Tq + m0 + q * 8) = v;
-        }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
         for (int mb = 0; mb < WM; ++mb)
@@ -880,6 +849,8 @@ __global__ void lse_kernel(const float2 *part, int64_t T, int nct, const int32_t
     const bool bad = h->void_batch != 0;
     lse[i] = bad ? NAN : l;
     loss[i] = (bad || !ok) ? NAN : l - zt[i];
+    if (i == 0)
+        h->z_T = (int32_t)T;   // the forward's logits (stored before this kernel) are T's
 }
 
 // dst[d][j] = element d of source row j for j < n, 0 for n <= j < (grid.x * 64);
@@ -1076,6 +1047,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.cand = cand;
     a.zt = reinterpret_cast<float *>(w + L.zt);
     a.part = reinterpret_cast<float2 *>(w + L.part);
+    a.zb = reinterpret_cast<float *>(w + L.zb);
     a.Tq = Tq;
     a.Cp = L.Cp;
     a.h = h;
@@ -1130,17 +1102,14 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.g = dloss;
     a.dz = dz;
     a.dzt = dzt;
+    a.zb = reinterpret_cast<float *>(w + L.zb);
     a.Tq = Tq;
     a.Cp = Cp;
     a.h = h;
 
-    a.A = xr;
-    a.B = wr;
-    a.K = kD;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = blocks(Cp, 128);
-    launch(SSM_PROF_DZ, true, true, gemm_kernel<EPI_DZ, 2, 2, kDzBK, kDzS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
-           dim3(256), s, a);
+    launch(SSM_PROF_DZ, true, true, dz_kernel, dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
 
     a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};
     a.B = Rows{wst, Cp, nullptr, kD, V};

@@ -19,6 +19,7 @@ FLAG_OVERFLOW = 0x2
 FLAG_BAD_PERM = 0x4
 FLAG_BAD_CAND = 0x8
 FLAG_BAD_SLOT = 0x10
+FLAG_NO_LOGITS = 0x20
 
 PROF_CAND = 0
 PROF_FWD = 1

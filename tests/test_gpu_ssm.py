@@ -108,6 +108,36 @@ def test_candidates_full_size_and_full_vocabulary():
         assert N.device_status(cfg, ws) == 0
 
 
+@pytest.mark.parametrize("case", ["no_forward", "other_T", "new_candidates"])
+def test_backward_needs_its_forward(case):
+    # dz comes from the logits the forward stored: a backward with no forward
+    # since the candidate set, or with another T, gives zero gradients and
+    # SSM_FLAG_NO_LOGITS; the workspace works again after a forward
+    N = S()
+    T, V, C = 400, V_SMALL, 500
+    tgt, X, W, perm, g = _inputs(8, T, V)
+    cfg, ws, cand, slot = _run_cand(N, V, C, T, tgt, perm)
+    Xd, Wd = _dev_bf16(X), _dev_bf16(W)
+    Tb = T
+    if case == "other_T":
+        N.loss_fwd(cfg, ws, Xd[:300], Wd, cand, slot[:300])
+        Tb = 200
+    elif case == "new_candidates":
+        N.loss_fwd(cfg, ws, Xd, Wd, cand, slot)
+        cand, slot = N.candidates(cfg, ws, _dev(tgt), _dev(perm))
+    lse = torch.zeros(Tb, device="cuda")
+    dW = torch.full((V, 768), 0.25, device="cuda")
+    dX = N.loss_bwd(cfg, ws, Xd[:Tb], Wd, cand, slot[:Tb], lse, _dev(g[:Tb]), dW)
+    assert torch.count_nonzero(dX) == 0 and bool((dW == 0.25).all())
+    assert N.device_status(cfg, ws, clear=True) == N.FLAG_NO_LOGITS
+    _, lse = N.loss_fwd(cfg, ws, Xd, Wd, cand, slot)
+    dX = N.loss_bwd(cfg, ws, Xd, Wd, cand, slot, lse, _dev(g), dW)
+    cand_o, slot_o, _, _ = orc.candidates(tgt, perm, V, C)
+    dX_o, _ = orc.loss_bwd(X, W, cand_o, slot_o, g)
+    assert np.abs(dX.cpu().numpy() - dX_o).max() <= 1e-2 * np.abs(dX_o).max()
+    assert N.device_status(cfg, ws) == 0
+
+
 @pytest.mark.parametrize("case", ["overflow", "bad_target", "bad_perm"])
 def test_void_batches(case):
     N = S()
