@@ -395,7 +395,11 @@ def main_ssm(args, torch):
         print(f"bench.py: sampled-softmax device flags {flags:#x} set", file=sys.stderr)
         sys.exit(1)
     flop = 2.0 * T * C * D   # one contraction over the batch and the candidate set
-    kflop = {"fwd": flop, "dz": flop, "dx": flop, "dw": flop}
+    kflop = {"fwd": flop, "dx": flop, "dw": flop}
+    # dz streams the forward's stored fp32 logits and writes dz twice in bf16
+    # (row-major and transposed), over the 128-padded batch and set
+    Tq, Cq = -(-T // 128) * 128, -(-C // 128) * 128
+    kbytes = {"dz": (4 + 2 + 2) * Tq * Cq}
     kernels = {}
     for name in SSM_GROUPS:
         ms_l = [a.elapsed_ms(b) for a, b in ev[name]]
@@ -406,6 +410,10 @@ def main_ssm(args, torch):
             tf = kflop[name] / (np.mean(ms_l) * 1e-3) / 1e12
             k.update({"flop_per_launch": kflop[name], "achieved_tflops": round(tf, 1),
                       "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        if name in kbytes:
+            gbs = kbytes[name] / (np.mean(ms_l) * 1e-3) / 1e9
+            k.update({"bytes_per_launch": kbytes[name], "achieved_gbs": round(gbs, 1),
+                      "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBPS, 4)})
         kernels[name] = k
     dom = max(kflop, key=lambda n: kernels[n]["ms_per_launch"])
     ms_step = el / args.steps * 1e3
@@ -425,8 +433,7 @@ def main_ssm(args, torch):
         "config": {"workload": f"sampled softmax: {T} positions x {C} candidates of a {V}-id vocabulary, "
                                f"dim {D}", "tokens_per_micro_step": T, "candidates": C, "vocab": V,
                    "dim": D},
-        # forward + backward contractions the method needs (the backward's
-        # recomputed logits are not counted)
+        # the three contractions the method needs (forward, dX, dW)
         "path_tflops": round(3 * flop / (ms_step * 1e-3) / 1e12, 1),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved_tflops"],
