@@ -8,14 +8,14 @@
 //             in the workspace); a per-position pass folds the tiles into
 //             lse and the loss.
 //   backward  a streaming pass over the stored z -> dz = g (exp(z - lse) -
-//             onehot), bf16, written row-major and transposed; dX = dz W_S;
-//             dW[S] += dz^T X.
+//             onehot), bf16, row-major; dX = dz W_S; dW[S] += dz^T X.
 //
-// Every contraction is C[m][n] = sum_k A[m][k] B[n][k] with both operands
-// k-contiguous in memory (the backward's transposed operands are written
-// first), so one kernel template serves all three: four wavefronts per
-// block, each owning WM x WN matrix-core tiles of 32 x 32, and a pipelined
-// main loop with direct global -> LDS loads.
+// Every contraction is C[m][n] = sum_k A[m][k] B[n][k]; B is k-contiguous in
+// memory (the backward's transposed X and W_S are written first), A too
+// except in dW, where A = dz^T is read k-major straight from dz through the
+// LDS transpose read.  One kernel template serves all three: four wavefronts
+// per block, each owning WM x WN matrix-core tiles of 32 x 32, and a
+// pipelined main loop with direct global -> LDS loads.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -33,7 +33,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 768;
 constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
 constexpr int kLdb = 128 + 16;  // bf16 per row of the dz epilogue's row-major tile (paired 4-byte writes conflict-free)
-constexpr int kLdbT = 128 + 8;  // bf16 per row of its transposed tile
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Per contraction: the k-step BK, the number NS of pipelined stages (two
 // blocks per CU), and the block tile, four wavefronts of WM x WN matrix-core
@@ -59,7 +58,7 @@ static_assert(sizeof(Hdr) == 256, "header is 256 bytes");
 
 struct Layout {
     int64_t Tp, Cp;   // padded maxima
-    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, dzt, zb, total;
+    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, zb, total;
 };
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -83,7 +82,6 @@ Layout layout(const ssm_config *c)
     L.xt = take(2ull * kD * L.Tp);
     L.wst = take(2ull * kD * L.Cp);
     L.dz = take(2ull * L.Tp * L.Cp);
-    L.dzt = take(2ull * L.Tp * L.Cp);
     L.zb = take(4ull * L.Tp * L.Cp);
     L.total = o;
     return L;
@@ -402,12 +400,26 @@ __device__ inline void barrier_nofence()
     asm volatile("" ::: "memory");
 }
 
-template <int WM, int WN, int BK, int S>
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// TA: A is stored k-major (A[m][k] at A.base[k A.ld + m], rows of A.base are
+// k); the stage then holds BK rows of BM m-values (row r's 16-byte chunk c at
+// position c ^ 4 (r & 3)) and the fragments come from gfx950's LDS transpose
+// read, ds_read_b64_tr_b16: within each 16 lanes, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes 4 j + i / 4, j = 0..3 (probed
+// on the GPU), so with lane p addressing row k0 + p / 4, column c0 + 4 (p % 4)
+// lane i gets rows k0 .. k0 + 3 of column c0 + i.
+template <int WM, int WN, int BK, int S, bool TA = false>
 __device__ inline void mainloop_wide(const Rows &A, const Rows &B, int64_t K, int64_t m0, int64_t n0,
                                      uint8_t *sm, f32x16 (&acc)[WM][WN], uint32_t *flags)
 {
     using WT = WideTile<WM, WN, BK, S>;
     constexpr int CH = WT::CH, RB = WT::RB, RPI = WT::RPI, SH = WT::SH, LA = WT::LA, LB = WT::LB;
+    constexpr int RBA = TA ? 2 * WT::BM : RB;       // bytes per LDS row of A
+    constexpr int RPIA = 1024 / RBA;                 // A rows one wavefront load covers
+    static_assert(!TA || WM == 2, "k-major A: 128 m-values per row (16 chunks)");
+    static_assert(!TA || BK / (4 * RPIA) == LA, "same loads per stage either way");
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = w >> 1, wn = w & 1;
@@ -416,19 +428,25 @@ __device__ inline void mainloop_wide(const Rows &A, const Rows &B, int64_t K, in
     const uint16_t *pa[LA], *pb[LB];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-        const int r = (4 * j + w) * RPI + lrow;
-        pa[j] = row_ptr(A, m0 + r, flags) + 8 * (lpos ^ ((r >> SH) & (CH - 1)));
+        if constexpr (TA) {
+            const int r = (4 * j + w) * RPIA + lane / 16, pos = lane % 16;   // k row, chunk position
+            pa[j] = A.base + r * A.ld + m0 + 8 * (pos ^ (4 * (r & 3)));
+        } else {
+            const int r = (4 * j + w) * RPI + lrow;
+            pa[j] = row_ptr(A, m0 + r, flags) + 8 * (lpos ^ ((r >> SH) & (CH - 1)));
+        }
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
         const int r = (4 * j + w) * RPI + lrow;
         pb[j] = row_ptr(B, n0 + r, flags) + 8 * (lpos ^ ((r >> SH) & (CH - 1)));
     }
+    const int64_t ka = TA ? A.ld : 1;   // elements per step of k in A
     auto issue = [&](int stage, int64_t k0) {
         uint8_t *ab = sm + stage * WT::STAGE, *bb = ab + WT::BM * RB;
 #pragma unroll
         for (int j = 0; j < LA; ++j)
-            lds_load16(pa[j] + k0, ab + (4 * j + w) * RPI * RB);
+            lds_load16(pa[j] + k0 * ka, ab + (4 * j + w) * RPIA * RBA);
 #pragma unroll
         for (int j = 0; j < LB; ++j)
             lds_load16(pb[j] + k0, bb + (4 * j + w) * RPI * RB);
@@ -453,16 +471,37 @@ __device__ inline void mainloop_wide(const Rows &A, const Rows &B, int64_t K, in
     // lane has the same swizzle
     const int ar = wm * WM * 32 + (lane & 31), br = wn * WN * 32 + (lane & 31), kq = lane >> 5;
     const int sa = (ar >> SH) & (CH - 1), sb = (br >> SH) & (CH - 1);
+    // k-major A: lane p = lane % 16 of group G = lane / 16 addresses row
+    // 16 kk + 8 (G / 2) + 4 h + p / 4 and column wm 64 + 32 mb + 16 (G % 2) +
+    // 4 (p % 4); the column's chunk has bit 2 = mb, so the swizzle is an XOR
+    const int tp = lane & 15, tg = lane >> 4;
+    const int ta_row = (8 * (tg >> 1) + (tp >> 2)) * RBA + 8 * (tp & 1);
+    const int ta_chunk = (8 * wm + 2 * (tg & 1) + ((tp >> 1) & 1)) ^ (4 * (tp >> 2));
     bf16x8 fa[2][WM], fb[2][WN];
+    // reads in the order the products use them: A fragment 0, the B
+    // fragments, then the other A fragments
     auto rd = [&](int stage, int kk, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
         const uint8_t *ab = sm + stage * WT::STAGE, *bb = ab + WT::BM * RB;
         const int c = 2 * kk + kq;
-#pragma unroll
-        for (int mb = 0; mb < WM; ++mb)
-            a[mb] = *(const bf16x8 *)(ab + (ar + 32 * mb) * RB + 16 * (c ^ sa));
+        auto rda = [&](int mb) {
+            if constexpr (TA) {
+                const uint8_t *q = ab + ta_row + 16 * kk * RBA + 16 * (ta_chunk ^ (4 * mb));
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)q);
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)(q + 4 * RBA));
+                a[mb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                a[mb] = *(const bf16x8 *)(ab + (ar + 32 * mb) * RB + 16 * (c ^ sa));
+            }
+        };
+        rda(0);
 #pragma unroll
         for (int nb = 0; nb < WN; ++nb)
             b[nb] = *(const bf16x8 *)(bb + (br + 32 * nb) * RB + 16 * (c ^ sb));
+#pragma unroll
+        for (int mb = 1; mb < WM; ++mb)
+            rda(mb);
     };
     auto mm = [&](int mb0, int mb1, const bf16x8 (&a)[WM], const bf16x8 (&b)[WN]) {
 #pragma unroll
@@ -481,12 +520,16 @@ __device__ inline void mainloop_wide(const Rows &A, const Rows &B, int64_t K, in
             rd(stage, kk, na, nb);
         mm(0, WM, a, b);
         if (more) {
+            constexpr int NR = (TA ? 2 : 1) * WM + WN, NM = WM * WN, NP = NR < NM ? NR : NM;
 #pragma unroll
-            for (int i = 0; i < WM + WN; ++i) {
+            for (int i = 0; i < NP; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix-core op
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, WM * WN - WM - WN, 0);
+            if constexpr (NM > NP)
+                __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+            if constexpr (NR > NP)
+                __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -538,7 +581,6 @@ struct GemmArgs {
     float2 *part;          // forward: per-tile (max, sum exp) [C / 128][T]
     float *zb;             // forward -> dz: fp32 logits, one 64 KB block per 128 x 128 tile
     uint16_t *dz;          // [Tq][Cp] bf16
-    uint16_t *dzt;         // [Cp][Tq] bf16
     int64_t Tq, Cp;
     uint32_t tiles_m, tiles_n;   // output tiles (block tile BM x 128)
     float *out;            // dX [T][768] or dW [V][768]
@@ -569,8 +611,8 @@ __device__ inline void store_logits(const GemmArgs &a, uint32_t mt, uint32_t nt,
 }
 
 // dz from the stored logits, one 128 x 128 tile per block:
-// dz = g (exp(z - lse) - onehot) rounded to bf16, written row-major [Tq][Cp]
-// and transposed [Cp][Tq].  Logits that the last forward did not store for
+// dz = g (exp(z - lse) - onehot) rounded to bf16, written row-major [Tq][Cp].
+// Logits that the last forward did not store for
 // this candidate set and T give zeros and SSM_FLAG_NO_LOGITS.
 __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
 {
@@ -599,96 +641,78 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
     const bool have = a.h->z_T == (int32_t)a.T;
     if (!have && blockIdx.x == 0 && t == 0)
         atomicOr(&a.h->flags, SSM_FLAG_NO_LOGITS);
-        uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
-        float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
-        float *s_g = s_l + 128;
-        int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
-        if (t < 128) {
-            const int64_t i = m0 + t;
-            const bool ok = have && i < a.T && a.h->void_batch == 0;
-            s_l[t] = ok ? a.lse[i] : 0.f;
-            s_g[t] = ok ? a.g[i] : 0.f;
-            s_y[t] = ok ? a.slot[i] : -1;
-        }
-        __syncthreads();
-        // dz of the tile as bf16, kept packed in registers (a lane holds 4
-        // consecutive rows of one column per group of 4 accumulator entries)
-        // and written through LDS twice: row-major, then transposed, so both
-        // copies leave as whole 256-byte rows
-        uint32_t hp[2][2][4][2];
+    uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
+    float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
+    float *s_g = s_l + 128;
+    int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
+    if (t < 128) {
+        const int64_t i = m0 + t;
+        const bool ok = have && i < a.T && a.h->void_batch == 0;
+        s_l[t] = ok ? a.lse[i] : 0.f;
+        s_g[t] = ok ? a.g[i] : 0.f;
+        s_y[t] = ok ? a.slot[i] : -1;
+    }
+    __syncthreads();
+    // dz of the tile as bf16, packed in registers (a lane holds 4
+    // consecutive rows of one column per group of 4 accumulator entries),
+    // then written through LDS so it leaves as whole 256-byte rows
+    uint32_t hp[2][2][4][2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
+            const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
+            const int4 y4 = *(const int4 *)(s_y + r4);
+            const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
+            const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int cc = tile_col<2>(nb);
+                const int c = (int)n0 + cc;        // candidates < 2^31
+                const bool col_ok = c < a.C;
+                uint16_t h[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // padding rows and columns, and a void batch, give 0
+                    // (masked, not branched around: no divergence)
+                    const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
+                    const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
+                    const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
+                    const float d = __uint_as_float(__float_as_uint(dv) & keep);
+                    h[j] = bf16_rne(d);
+                }
+                hp[mb][nb][g][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                hp[mb][nb][g][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            }
+        }
+    // row-major tile: lanes l and l ^ 1 hold adjacent columns, so they swap
+    // halves and each writes two rows of a column pair (4-byte writes):
+    // even lanes rows r4, r4 + 1 of columns cc, cc + 1, odd lanes rows
+    // r4 + 2, r4 + 3 of columns cc - 1, cc
+    const int odd = t & 1;
+    uint16_t *bp = bt + odd * (2 * kLdb - 1);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
-                const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
-                const int4 y4 = *(const int4 *)(s_y + r4);
-                const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
-                const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int cc = tile_col<2>(nb);
-                    const int c = (int)n0 + cc;        // candidates < 2^31
-                    const bool col_ok = c < a.C;
-                    uint16_t h[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        // padding rows and columns, and a void batch, give 0
-                        // (masked, not branched around: no divergence)
-                        const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
-                        const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
-                        const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
-                        const float d = __uint_as_float(__float_as_uint(dv) & keep);
-                        h[j] = bf16_rne(d);
-                    }
-                    hp[mb][nb][g][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-                    hp[mb][nb][g][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-                }
+                const uint32_t x = hp[mb][nb][g][0], y = hp[mb][nb][g][1];   // rows r4, r4 + 1 | r4 + 2, r4 + 3
+                const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x : y), 0xB1, 0xF, 0xF, false);
+                const uint32_t lo = odd ? o : x, hi = odd ? y : o;   // left and right column
+                uint16_t *q = bp + tile_row<2>(mb, 4 * g) * kLdb + tile_col<2>(nb);
+                *(uint32_t *)q = (lo & 0xffffu) | (hi << 16);
+                *(uint32_t *)(q + kLdb) = (lo >> 16) | (hi & 0xffff0000u);
             }
-        // row-major tile: lanes l and l ^ 1 hold adjacent columns, so they swap
-        // halves and each writes two rows of a column pair (4-byte writes):
-        // even lanes rows r4, r4 + 1 of columns cc, cc + 1, odd lanes rows
-        // r4 + 2, r4 + 3 of columns cc - 1, cc
-        const int odd = t & 1;
-        uint16_t *bp = bt + odd * (2 * kLdb - 1);
+    __syncthreads();
+    // row-major: 16 chunks of 16 B per row
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t x = hp[mb][nb][g][0], y = hp[mb][nb][g][1];   // rows r4, r4 + 1 | r4 + 2, r4 + 3
-                    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? x : y), 0xB1, 0xF, 0xF, false);
-                    const uint32_t lo = odd ? o : x, hi = odd ? y : o;   // left and right column
-                    uint16_t *q = bp + tile_row<2>(mb, 4 * g) * kLdb + tile_col<2>(nb);
-                    *(uint32_t *)q = (lo & 0xffffu) | (hi << 16);
-                    *(uint32_t *)(q + kLdb) = (lo >> 16) | (hi & 0xffff0000u);
-                }
-        __syncthreads();
-        // row-major: 16 chunks of 16 B per row
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int rr = (t >> 4) + 16 * p, q = t & 15;
-            const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
-            __builtin_nontemporal_store(v, (u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8));
-        }
-        __syncthreads();
-        // transposed: row cc of the LDS tile holds column cc of dz
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(uint2 *)(bt + tile_col<2>(nb) * kLdbT + tile_row<2>(mb, 4 * g)) =
-                        make_uint2(hp[mb][nb][g][0], hp[mb][nb][g][1]);
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int cr = (t >> 4) + 16 * p, q = t & 15;
-            const u32x4 v = *(const u32x4 *)(bt + cr * kLdbT + q * 8);
-            __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + (n0 + cr) * a.Tq + m0 + q * 8));
-        }
+    for (int p = 0; p < 8; ++p) {
+        const int rr = (t >> 4) + 16 * p, q = t & 15;
+        const u32x4 v = *(const u32x4 *)(bt + rr * kLdb + q * 8);
+        __builtin_nontemporal_store(v, (u32x4 *)(a.dz + (m0 + rr) * a.Cp + n0 + q * 8));
+    }
 }
 
 
@@ -715,7 +739,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         return;   // the whole block: no barrier is reached
     const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
     f32x16 acc[WM][WN];
-    mainloop_wide<WM, WN, BK, NS>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
+    mainloop_wide<WM, WN, BK, NS, EPI == EPI_DW>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
@@ -1082,7 +1106,6 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     uint16_t *xt = reinterpret_cast<uint16_t *>(w + L.xt);
     uint16_t *wst = reinterpret_cast<uint16_t *>(w + L.wst);
     uint16_t *dz = reinterpret_cast<uint16_t *>(w + L.dz);
-    uint16_t *dzt = reinterpret_cast<uint16_t *>(w + L.dzt);
     hipStream_t s = (hipStream_t)stream;
 
     const Rows xr{(const uint16_t *)X, kD, nullptr, (int32_t)T, V};
@@ -1101,7 +1124,6 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.lse = lse;
     a.g = dloss;
     a.dz = dz;
-    a.dzt = dzt;
     a.zb = reinterpret_cast<float *>(w + L.zb);
     a.Tq = Tq;
     a.Cp = Cp;
@@ -1120,7 +1142,7 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     launch(SSM_PROF_DX, true, true, gemm_kernel<EPI_DX, kDxWM, kDxWN, kDxBK, kDxS>,
            dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
 
-    a.A = Rows{dzt, Tq, nullptr, (int32_t)Cp, V};
+    a.A = Rows{dz, Cp, nullptr, (int32_t)Tq, V};   // k-major: rows of dz are positions
     a.B = Rows{xt, Tq, nullptr, kD, V};
     a.K = Tq;
     a.out = dW;
