@@ -41,6 +41,7 @@ constexpr int kTile = 128;      // T and C are padded to multiples of this
 constexpr int kFwdBK = 64, kFwdS = 2;                        // forward, 128 x 128
 constexpr int kDxWM = 2, kDxWN = 3, kDxBK = 64, kDxS = 2;    // dX, 128 x 192
 constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 192 or 128 x 128 by round fill
+constexpr int kMaxSplit = 4;                                 // dW: most parts of k
 
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
@@ -58,7 +59,7 @@ static_assert(sizeof(Hdr) == 256, "header is 256 bytes");
 
 struct Layout {
     int64_t Tp, Cp;   // padded maxima
-    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, zb, total;
+    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, zb, dwp, total;
 };
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -83,6 +84,7 @@ Layout layout(const ssm_config *c)
     L.wst = take(2ull * kD * L.Cp);
     L.dz = take(2ull * L.Tp * L.Cp);
     L.zb = take(4ull * L.Tp * L.Cp);
+    L.dwp = take(4ull * kMaxSplit * L.Cp * kD);
     L.total = o;
     return L;
 }
@@ -582,8 +584,10 @@ struct GemmArgs {
     float *zb;             // forward -> dz: fp32 logits, one 64 KB block per 128 x 128 tile
     uint16_t *dz;          // [Tq][Cp] bf16
     int64_t Tq, Cp;
-    uint32_t tiles_m, tiles_n;   // output tiles (block tile BM x 128)
+    uint32_t tiles_m, tiles_n;   // output tiles
     float *out;            // dX [T][768] or dW [V][768]
+    int32_t ksplit;        // dW: parts of k, each a block of its own (1: add into dW directly)
+    float *dwp;            // dW parts [ksplit][Cp][768] when ksplit > 1
     Hdr *h;
 };
 
@@ -735,11 +739,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     constexpr int BM = 64 * WM, BN = 64 * WN;
     __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WM, WN, BK, NS>()];
     uint32_t mt, nt;
-    if (!tile_of<true>(a.tiles_m, a.tiles_n, mt, nt))
+    // dW with k split: part p of k is M-tile row p of a taller grid, so the
+    // blocks of one group share their k range (and the rows of X^T they read)
+    const uint32_t parts = EPI == EPI_DW ? (uint32_t)a.ksplit : 1u;
+    if (!tile_of<true>(a.tiles_m * parts, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
+    Rows A = a.A, B = a.B;
+    int64_t K = a.K;
+    uint32_t part = 0;
+    if constexpr (EPI == EPI_DW) {
+        part = mt / a.tiles_m;
+        mt -= part * a.tiles_m;
+        const int64_t nk = a.K / BK, k0 = (int64_t)part * nk / parts * BK, k1 = (int64_t)(part + 1) * nk / parts * BK;
+        A.base += k0 * A.ld;   // k-major: rows of A are k
+        B.base += k0;
+        K = k1 - k0;
+    }
     const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
     f32x16 acc[WM][WN];
-    mainloop_wide<WM, WN, BK, NS, EPI == EPI_DW>(a.A, a.B, a.K, m0, n0, smem, acc, &a.h->flags);
+    mainloop_wide<WM, WN, BK, NS, EPI == EPI_DW>(A, B, K, m0, n0, smem, acc, &a.h->flags);
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
@@ -826,6 +844,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                         a.out[i * kD + n0 + tile_col<WN>(nb)] = acc[mb][nb][e];
                 }
             }
+    } else if (parts > 1) {   // EPI_DW, one part of k: plain stores, summed by dw_reduce_kernel
+        float *dwp = a.dwp + (int64_t)part * a.Cp * kD;
+#pragma unroll
+        for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t c = m0 + tile_row<WM>(mb, e);
+#pragma unroll
+                for (int nb = 0; nb < WN; ++nb)
+                    dwp[c * kD + n0 + tile_col<WN>(nb)] = acc[mb][nb][e];
+            }
     } else {   // EPI_DW
 #pragma unroll
         for (int mb = 0; mb < WM; ++mb)
@@ -844,6 +873,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                 }
             }
     }
+}
+
+// dW[cand[c]] += the parts of k in order (part 0 first): deterministic.
+__global__ void dw_reduce_kernel(const float *dwp, int parts, int64_t Cp, const int32_t *cand, int32_t C,
+                                 int32_t V, float *dW)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // float4 of [C][768]
+    if (i >= (int64_t)C * (kD / 4))
+        return;
+    const int64_t c = i / (kD / 4), q = i % (kD / 4);
+    const int32_t v = cand[c];
+    if ((uint32_t)v >= (uint32_t)V)
+        return;
+    const float4 *p = reinterpret_cast<const float4 *>(dwp) + c * (kD / 4) + q;
+    float4 s = p[0];
+    for (int k = 1; k < parts; ++k) {
+        const float4 x = p[k * Cp * (kD / 4)];
+        s.x += x.x;
+        s.y += x.y;
+        s.z += x.z;
+        s.w += x.w;
+    }
+    float4 *o = reinterpret_cast<float4 *>(dW + (int64_t)v * kD) + q;
+    float4 d = *o;
+    d.x += s.x;
+    d.y += s.y;
+    d.z += s.z;
+    d.w += s.w;
+    *o = d;
 }
 
 // Folds the per-tile sums of each position: lse = M + log sum_t s_t e^(m_t - M).
@@ -1147,21 +1205,35 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.K = Tq;
     a.out = dW;
     a.tiles_m = blocks(Cp, 128);
+    a.dwp = reinterpret_cast<float *>(w + L.dwp);
     // dW's blocks are few and long (k = T), so the last round of resident
-    // blocks (two per CU) decides much of its time: 128 x 192 tiles do about
-    // 1.25x the work per unit time of 128 x 128 ones (measured at equal
-    // fill), and the 128 x 128 form wins only where it fills its rounds that
-    // much better (10,240 candidates: 480 blocks in 512 slots)
-    const uint32_t nb2 = a.tiles_m * (kD / 128), nb3 = a.tiles_m * (kD / 192);
-    if (1.25 * round_fill(nb3, 2 * kCUs) >= round_fill(nb2, 2 * kCUs)) {
-        a.tiles_n = kD / 192;
-        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 3, kDwBK, kDwS>,
-               dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
-    } else {
-        a.tiles_n = kD / 128;
-        launch(SSM_PROF_DW, true, true, gemm_kernel<EPI_DW, 2, 2, kDwBK, kDwS>,
-               dim3(grid_blocks(a.tiles_m, a.tiles_n)), dim3(256), s, a);
-    }
+    // blocks (two per CU) decides much of its time.  Choose the tile and the
+    // number of parts of k by modelled time: 128 x 192 tiles do about 1.25x
+    // the work per unit time of 128 x 128 ones (measured at equal fill), a
+    // split costs its reduction (about 3 %), and the rounds' fill is known.
+    int wn = 2, split = 1;
+    double best = 0.0;
+    const int64_t nk = Tq / kDwBK;
+    for (int cwn = 2; cwn <= 3; ++cwn)
+        for (int p = 1; p <= kMaxSplit && p <= nk; ++p) {
+            const uint32_t nb = a.tiles_m * (uint32_t)(kD / (64 * cwn)) * (uint32_t)p;
+            const double score = (cwn == 3 ? 1.25 : 1.0) * round_fill(nb, 2 * kCUs) * (p > 1 ? 0.97 : 1.0);
+            if (score > best + 1e-9) {
+                best = score;
+                wn = cwn;
+                split = p;
+            }
+        }
+    a.ksplit = split;
+    a.tiles_n = kD / (64 * wn);
+    const dim3 grid(grid_blocks(a.tiles_m * (uint32_t)split, a.tiles_n));
+    if (wn == 3)
+        launch(SSM_PROF_DW, true, split == 1, gemm_kernel<EPI_DW, 2, 3, kDwBK, kDwS>, grid, dim3(256), s, a);
+    else
+        launch(SSM_PROF_DW, true, split == 1, gemm_kernel<EPI_DW, 2, 2, kDwBK, kDwS>, grid, dim3(256), s, a);
+    if (split > 1)
+        launch(SSM_PROF_DW, false, true, dw_reduce_kernel, dim3(blocks((int64_t)C * (kD / 4), 256)), dim3(256), s,
+               (const float *)a.dwp, split, Cp, cand, C, V, dW);
     return done(hipGetLastError());
 }
 
