@@ -88,9 +88,10 @@ int ssm_abi_version(void);
 const char *ssm_status_string(int status);
 
 /* Workspace size for cfg (host).  About 4 (T+128)(C+128) bytes for the
- * forward's fp32 logits, 2 (T+128)(C+128) for dz, plus 2 D (T + C + 256)
- * bytes of transposed operands and 8 T C/128 bytes of per-tile sums (about
- * 3 GB at T = 49,152, C = 10,240). */
+ * forward's fp32 logits, 2 (T+128)(C+128) for dz, 16 D (C+128) for dW's
+ * split parts, plus 2 D (T + C + 256) bytes of transposed operands and
+ * 8 T C/128 bytes of per-tile sums (about 3.1 GB at T = 49,152,
+ * C = 10,240). */
 int ssm_workspace_bytes(const ssm_config *cfg, uint64_t *bytes);
 
 /* Prepares a workspace (256-byte aligned, ws_bytes from ssm_workspace_bytes)
