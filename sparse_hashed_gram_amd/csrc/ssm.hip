@@ -359,8 +359,9 @@ __device__ inline bool tile_of(uint32_t nM, uint32_t nN, uint32_t &mt, uint32_t 
 // Pipelined form of the main loop: block tile (64 WM) x (64 WN), four
 // wavefronts of (32 WM) x (32 WN) (WM, WN > 2 let each operand fragment read
 // from LDS feed more matrix-core ops).  Direct global -> LDS loads into S
-// stages of BK; S - 1 stages are in flight while one is read, and one barrier
-// per k-step both publishes the stage that landed and frees the one read last.
+// stages of BK; all S start filling at once, S - 1 stay in flight while one is
+// read, and one barrier per k-step both publishes the stage that landed and
+// frees the one read last.
 // Rows are stored unpadded, BK / 8 chunks of 16 bytes each, chunk c of row r
 // at position c ^ ((r >> SH) & (CH - 1)), so the lanes of one ds_read_b128
 // (consecutive rows, one chunk) spread over the banks (the PMC bank-conflict
@@ -403,7 +404,6 @@ __device__ inline void barrier_nofence()
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 // TA: A is stored k-major (A[m][k] at A.base[k A.ld + m], rows of A.base are
 // k); the stage then holds BK rows of BM m-values (row r's 16-byte chunk c at
