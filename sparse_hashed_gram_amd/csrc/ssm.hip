@@ -31,7 +31,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
-constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
+constexpr int kLdt = 128 + 4;   // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
 constexpr int kLdb = 128 + 16;  // bf16 per row of the dz epilogue's row-major tile (paired 4-byte writes conflict-free)
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Per contraction: the k-step BK, the number NS of pipelined stages (two
@@ -724,7 +724,7 @@ template <int EPI, int WM, int WN, int BK, int NS>
 constexpr uint32_t smem_bytes()
 {
     constexpr uint32_t main = WideTile<WM, WN, BK, NS>::SMEM;
-    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 64 * 8) : main;
+    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 128 * 8) : main;
 }
 
 // One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile (the
@@ -765,31 +765,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         // layout (each store: 256 lanes x 16 bytes, contiguous; non-temporal:
         // 4 T C bytes would otherwise push the operands out of the caches)
         store_logits(a, mt, nt, acc);
-        // two halves of 64 rows.  The half's two wavefronts store their
-        // accumulators column-major (a lane's 4 consecutive rows of one column
-        // are one 16-byte store); wavefront q then folds columns 32q .. 32q + 32
-        // of every row of the half, a row per lane (reads of consecutive rows),
-        // and the four quarters meet in LDS
+        // all four wavefronts store their accumulators to LDS column-major (a
+        // lane's 4 consecutive rows of one column are one 16-byte store); then
+        // each thread folds two 32-column quarters of one row (reads of
+        // consecutive rows across a wavefront), and the quarters meet in LDS
         float *tile = reinterpret_cast<float *>(smem);                      // [128][kLdt]
-        float2 *pq = reinterpret_cast<float2 *>(smem + 128 * kLdt * 4);     // [4][64]
-        const int w = t >> 6, r = t & 63, q = w, wm = w >> 1;
-        const int64_t c0 = n0 + 32 * q;
-        const int64_t left = (int64_t)a.C - c0;
-        const int nv = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 32 ? 32 : (int)left));
-        for (int h = 0; h < 2; ++h) {
-            if (wm == h) {
+        float2 *pq = reinterpret_cast<float2 *>(smem + 128 * kLdt * 4);     // [4][128]
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                        for (int g = 0; g < 4; ++g)
-                            *(float4 *)(tile + tile_col<2>(nb) * kLdt + tile_row<2>(mb, 4 * g) - 64 * h) =
-                                make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
-                                            acc[mb][nb][4 * g + 3]);
-            }
-            __syncthreads();
-            const int64_t i = m0 + 64 * h + r;
+                for (int g = 0; g < 4; ++g)
+                    *(float4 *)(tile + tile_col<2>(nb) * kLdt + tile_row<2>(mb, 4 * g)) =
+                        make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                    acc[mb][nb][4 * g + 3]);
+        __syncthreads();
+        const int r = t & 127, hc = t >> 7;   // hc: wavefronts 0, 1 take quarters 0, 1; 2, 3 take 2, 3
+        const int64_t i = m0 + r;
+        const int64_t y = i < a.T ? a.slot[i] : -1;
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * hc + qq;
+            const int64_t c0 = n0 + 32 * q;
+            const int64_t left = (int64_t)a.C - c0;
+            const int nv = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 32 ? 32 : (int)left));
             const float *zc = tile + 32 * q * kLdt + r;   // column 32q + k at zc[k kLdt]
             float m = -INFINITY, s = 0.f;
             if (nv == 32) {
@@ -809,28 +809,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                 for (int k = 0; k < nv; ++k)
                     s += __expf(zc[k * kLdt] - m);
             }
-            if (i < a.T) {
-                const int64_t y = a.slot[i];
-                if (y >= c0 && y < c0 + nv)
-                    a.zt[i] = zc[(y - c0) * kLdt];
-            }
-            pq[q * 64 + r] = make_float2(m, s);
-            __syncthreads();
-            if (q == 0 && i < a.T) {
-                float M = -INFINITY;
+            if (y >= c0 && y < c0 + nv)
+                a.zt[i] = zc[(y - c0) * kLdt];
+            pq[q * 128 + r] = make_float2(m, s);
+        }
+        __syncthreads();
+        if (hc == 0 && i < a.T) {
+            float M = -INFINITY;
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    M = fmaxf(M, pq[k * 64 + r].x);
-                float S = 0.f;
+            for (int k = 0; k < 4; ++k)
+                M = fmaxf(M, pq[k * 128 + r].x);
+            float S = 0.f;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float2 o = pq[k * 64 + r];
-                    if (o.y > 0.f)
-                        S += o.y * __expf(o.x - M);
-                }
-                a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
+            for (int k = 0; k < 4; ++k) {
+                const float2 o = pq[k * 128 + r];
+                if (o.y > 0.f)
+                    S += o.y * __expf(o.x - M);
             }
-            __syncthreads();
+            a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
