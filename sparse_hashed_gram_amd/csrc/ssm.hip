@@ -332,18 +332,8 @@ __host__ __device__ inline uint32_t grid_blocks(uint32_t nM, uint32_t nN)
     return kXcds * ((nM * nN + kXcds - 1) / kXcds);
 }
 
-// The dz kernel keeps the plain order (M-tiles fastest): its two bf16 output
-// layouts were written faster that way (measured).
-template <bool GROUPED>
 __device__ inline bool tile_of(uint32_t nM, uint32_t nN, uint32_t &mt, uint32_t &nt)
 {
-    if (!GROUPED) {
-        if (blockIdx.x >= nM * nN)
-            return false;
-        mt = blockIdx.x % nM;
-        nt = blockIdx.x / nM;
-        return true;
-    }
     const uint32_t total = nM * nN, per = (total + kXcds - 1) / kXcds;
     const uint32_t tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
     if (tile >= total)
@@ -622,8 +612,12 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
 {
     __shared__ __align__(16) uint8_t smem[128 * kLdb * 2 + 3 * 128 * 4];
     uint32_t mt, nt;
-    if (!tile_of<false>(a.tiles_m, a.tiles_n, mt, nt))
+    // N-tiles fastest: consecutive blocks write neighbouring 256-byte pieces
+    // of the same dz rows (measured faster than M-tiles fastest or grouped)
+    if (blockIdx.x >= a.tiles_m * a.tiles_n)
         return;
+    mt = blockIdx.x / a.tiles_n;
+    nt = blockIdx.x % a.tiles_n;
     const int64_t m0 = (int64_t)mt * 128, n0 = (int64_t)nt * 128;
     const int t = threadIdx.x;
     f32x16 acc[2][2];
@@ -742,7 +736,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     // dW with k split: part p of k is M-tile row p of a taller grid, so the
     // blocks of one group share their k range (and the rows of X^T they read)
     const uint32_t parts = EPI == EPI_DW ? (uint32_t)a.ksplit : 1u;
-    if (!tile_of<true>(a.tiles_m * parts, a.tiles_n, mt, nt))
+    if (!tile_of(a.tiles_m * parts, a.tiles_n, mt, nt))
         return;   // the whole block: no barrier is reached
     Rows A = a.A, B = a.B;
     int64_t K = a.K;

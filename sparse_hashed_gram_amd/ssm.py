@@ -169,7 +169,11 @@ def loss_fwd(cfg: SsmConfig, ws: Workspace, X: torch.Tensor, W: torch.Tensor, ca
 def loss_bwd(cfg: SsmConfig, ws: Workspace, X: torch.Tensor, W: torch.Tensor, cand: torch.Tensor,
              slot: torch.Tensor, lse: torch.Tensor, dloss: torch.Tensor, dW: torch.Tensor,
              dX: torch.Tensor | None = None):
-    """dX (fp32 [T, 768], returned) and dW[cand] += ... in place (fp32 [V, 768])."""
+    """dX (fp32 [T, 768], returned) and dW[cand] += ... in place (fp32 [V, 768]).
+
+    Reads the logits the last loss_fwd on this workspace stored: call it after
+    that forward with the same X, W, cand, slot (else FLAG_NO_LOGITS and zero
+    gradients where the library can tell)."""
     T = X.shape[0]
     dX = dX if dX is not None else torch.empty((T, DIM), dtype=torch.float32, device=X.device)
     _check("ssm_loss_bwd", lib().ssm_loss_bwd(
