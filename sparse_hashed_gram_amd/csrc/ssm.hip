@@ -31,14 +31,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 768;
-constexpr int kLdt = 128 + 4;   // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
+constexpr int kLdt = 64 + 4;    // fp32 per column of the forward's epilogue tile (16-byte rows, conflict-free)
 constexpr int kLdb = 128 + 16;  // bf16 per row of the dz epilogue's row-major tile (paired 4-byte writes conflict-free)
 constexpr int kTile = 128;      // T and C are padded to multiples of this
 // Per contraction: the k-step BK, the number NS of pipelined stages (two
 // blocks per CU), and the block tile, four wavefronts of WM x WN matrix-core
 // tiles of 32 x 32.  Chosen by measurement on MI355X (49,152 positions x
 // 10,240 candidates x 768).
-constexpr int kFwdBK = 64, kFwdS = 2;                        // forward, 128 x 128
+constexpr int kFwdWN = 3, kFwdBK = 64, kFwdS = 2;            // forward, 128 x 64 WN
 constexpr int kDxWM = 2, kDxWN = 3, kDxBK = 64, kDxS = 2;    // dX, 128 x 192
 constexpr int kDwBK = 64, kDwS = 2;                          // dW, 128 x 192 or 128 x 128 by round fill
 constexpr int kMaxSplit = 4;                                 // dW: most parts of k
@@ -570,7 +570,7 @@ struct GemmArgs {
     const float *lse;      // [T]
     const float *g;        // [T]
     float *zt;             // forward: target logits [T]
-    float2 *part;          // forward: per-tile (max, sum exp) [C / 128][T]
+    float2 *part;          // forward: per-tile (max, sum exp) [column tiles][T]
     float *zb;             // forward -> dz: fp32 logits, one 64 KB block per 128 x 128 tile
     uint16_t *dz;          // [Tq][Cp] bf16
     int64_t Tq, Cp;
@@ -583,25 +583,33 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
-// Logits buffer: one block of 128 x 128 fp32 per tile (mt, nt), holding the
-// accumulators as the 256 threads of a block have them: entry 4 g + j of
-// matrix-core tile (mb, nb) of thread t at float4 ((2 mb + nb) 4 + g) 256 + t.
-__device__ inline f32x4 *logits_block(const GemmArgs &a, uint32_t mt, uint32_t nt)
+// Logits buffer, fragment-major: the 32 x 32 matrix-core tile of rows
+// 32 R .. and columns 32 Cb .. is 4 KB at float4 (R Cp/32 + Cb) 256, holding
+// the accumulators as a wavefront has them: entry 4 g + j of lane l at float4
+// g 64 + l.  So any block tiling can store or reload its fragments, each
+// access a contiguous 1 KB per wavefront.
+__device__ inline f32x4 *logits_frag(const GemmArgs &a, int64_t row0, int64_t col0)
 {
-    return reinterpret_cast<f32x4 *>(a.zb) + ((int64_t)mt * a.tiles_n + nt) * (128 * 128 / 4);
+    return reinterpret_cast<f32x4 *>(a.zb) + ((row0 >> 5) * (a.Cp >> 5) + (col0 >> 5)) * 256 + (threadIdx.x & 63);
 }
-__device__ inline void store_logits(const GemmArgs &a, uint32_t mt, uint32_t nt, const f32x16 (&acc)[2][2])
+template <int WM, int WN>
+__device__ inline void store_logits(const GemmArgs &a, int64_t m0, int64_t n0, const f32x16 (&acc)[WM][WN])
 {
-    f32x4 *zb = logits_block(a, mt, nt);
+    const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < WN; ++nb) {
+            const int64_t col0 = n0 + wn * WN * 32 + nb * 32;
+            if (col0 >= a.Cp)
+                continue;   // past the padded candidates (wavefront-uniform)
+            f32x4 *zb = logits_frag(a, m0 + wm * WM * 32 + mb * 32, col0);
 #pragma unroll
             for (int g = 0; g < 4; ++g)
                 __builtin_nontemporal_store(
                     f32x4{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]},
-                    zb + ((2 * mb + nb) * 4 + g) * 256 + threadIdx.x);
+                    zb + g * 64);
+        }
 }
 
 // dz from the stored logits, one 128 x 128 tile per block:
@@ -622,19 +630,21 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
     const int t = threadIdx.x;
     f32x16 acc[2][2];
     {
-        const f32x4 *zb = logits_block(a, mt, nt);
+        const int w = t >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb) {
+                const f32x4 *zb = logits_frag(a, m0 + wm * 64 + mb * 32, n0 + wn * 64 + nb * 32);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const f32x4 v = __builtin_nontemporal_load(zb + ((2 * mb + nb) * 4 + g) * 256 + t);
+                    const f32x4 v = __builtin_nontemporal_load(zb + g * 64);
                     acc[mb][nb][4 * g] = v[0];
                     acc[mb][nb][4 * g + 1] = v[1];
                     acc[mb][nb][4 * g + 2] = v[2];
                     acc[mb][nb][4 * g + 3] = v[3];
                 }
+            }
     }
     const bool have = a.h->z_T == (int32_t)a.T;
     if (!have && blockIdx.x == 0 && t == 0)
@@ -718,7 +728,7 @@ template <int EPI, int WM, int WN, int BK, int NS>
 constexpr uint32_t smem_bytes()
 {
     constexpr uint32_t main = WideTile<WM, WN, BK, NS>::SMEM;
-    return EPI == EPI_FWD ? cmax(main, 128 * kLdt * 4 + 4 * 128 * 8) : main;
+    return EPI == EPI_FWD ? cmax(main, 64 * WN * kLdt * 4 + 4 * 64 * 8) : main;
 }
 
 // One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile (the
@@ -728,7 +738,7 @@ template <int EPI, int WM, int WN, int BK, int NS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
     static_assert(EPI == EPI_FWD || EPI == EPI_DX || EPI == EPI_DW, "contraction epilogues");
-    static_assert(EPI != EPI_FWD || (WM == 2 && WN == 2), "the forward's epilogue takes 128 x 128 tiles");
+    static_assert(EPI != EPI_FWD || WM == 2, "the forward's epilogue takes 128-row tiles");
     static_assert(NS >= 2, "pipelined loop");
     constexpr int BM = 64 * WM, BN = 64 * WN;
     __shared__ __align__(16) uint8_t smem[smem_bytes<EPI, WM, WN, BK, NS>()];
@@ -755,47 +765,48 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
-        // the tile's fp32 logits for the dz kernel, in the accumulators' own
-        // layout (each store: 256 lanes x 16 bytes, contiguous; non-temporal:
-        // 4 T C bytes would otherwise push the operands out of the caches)
-        store_logits(a, mt, nt, acc);
-        // all four wavefronts store their accumulators to LDS column-major (a
-        // lane's 4 consecutive rows of one column are one 16-byte store); then
-        // each thread folds two 32-column quarters of one row (reads of
-        // consecutive rows across a wavefront), and the quarters meet in LDS
-        float *tile = reinterpret_cast<float *>(smem);                      // [128][kLdt]
-        float2 *pq = reinterpret_cast<float2 *>(smem + 128 * kLdt * 4);     // [4][128]
+        // the tile's fp32 logits for the dz kernel, fragment by fragment (each
+        // store: 64 lanes x 16 bytes, contiguous; non-temporal: 4 T C bytes
+        // would otherwise push the operands out of the caches)
+        store_logits<WM, WN>(a, m0, n0, acc);
+        // two halves of 64 rows.  The half's two wavefronts store their
+        // accumulators to LDS column-major (a lane's 4 consecutive rows of
+        // one column are one 16-byte store); wavefront q then folds columns
+        // q CW .. (q + 1) CW of every row of the half, a row per lane (reads
+        // of consecutive rows), and the four quarters meet in LDS
+        constexpr int CW = BN / 4;
+        float *tile = reinterpret_cast<float *>(smem);                      // [BN][kLdt]
+        float2 *pq = reinterpret_cast<float2 *>(smem + BN * kLdt * 4);      // [4][64]
+        const int w = t >> 6, r = t & 63, q = w, wm = w >> 1;
+        const int64_t c0 = n0 + CW * q;
+        const int64_t left = (int64_t)a.C - c0;
+        const int nv = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= CW ? CW : (int)left));
+        const float *zc = tile + CW * q * kLdt + r;   // column q CW + k at zc[k kLdt]
+        for (int h = 0; h < 2; ++h) {
+            if (wm == h) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(float4 *)(tile + tile_col<2>(nb) * kLdt + tile_row<2>(mb, 4 * g)) =
-                        make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
-                                    acc[mb][nb][4 * g + 3]);
-        __syncthreads();
-        const int r = t & 127, hc = t >> 7;   // hc: wavefronts 0, 1 take quarters 0, 1; 2, 3 take 2, 3
-        const int64_t i = m0 + r;
-        const int64_t y = i < a.T ? a.slot[i] : -1;
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int q = 2 * hc + qq;
-            const int64_t c0 = n0 + 32 * q;
-            const int64_t left = (int64_t)a.C - c0;
-            const int nv = __builtin_amdgcn_readfirstlane(left <= 0 ? 0 : (left >= 32 ? 32 : (int)left));
-            const float *zc = tile + 32 * q * kLdt + r;   // column 32q + k at zc[k kLdt]
+                        for (int g = 0; g < 4; ++g)
+                            *(float4 *)(tile + tile_col<WN>(nb) * kLdt + tile_row<WM>(mb, 4 * g) - 64 * h) =
+                                make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                            acc[mb][nb][4 * g + 3]);
+            }
+            __syncthreads();
+            const int64_t i = m0 + 64 * h + r;
             float m = -INFINITY, s = 0.f;
-            if (nv == 32) {
-                float v[32];
+            if (nv == CW) {
+                float v[CW];
 #pragma unroll
-                for (int k = 0; k < 32; ++k)
+                for (int k = 0; k < CW; ++k)
                     v[k] = zc[k * kLdt];
 #pragma unroll
-                for (int k = 0; k < 32; ++k)
+                for (int k = 0; k < CW; ++k)
                     m = fmaxf(m, v[k]);
 #pragma unroll
-                for (int k = 0; k < 32; ++k)
+                for (int k = 0; k < CW; ++k)
                     s += __expf(v[k] - m);
             } else if (nv > 0) {
                 for (int k = 0; k < nv; ++k)
@@ -803,24 +814,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
                 for (int k = 0; k < nv; ++k)
                     s += __expf(zc[k * kLdt] - m);
             }
-            if (y >= c0 && y < c0 + nv)
-                a.zt[i] = zc[(y - c0) * kLdt];
-            pq[q * 128 + r] = make_float2(m, s);
-        }
-        __syncthreads();
-        if (hc == 0 && i < a.T) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                M = fmaxf(M, pq[k * 128 + r].x);
-            float S = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float2 o = pq[k * 128 + r];
-                if (o.y > 0.f)
-                    S += o.y * __expf(o.x - M);
+            if (i < a.T) {
+                const int64_t y = a.slot[i];
+                if (y >= c0 && y < c0 + nv)
+                    a.zt[i] = zc[(y - c0) * kLdt];
             }
-            a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
+            pq[q * 64 + r] = make_float2(m, s);
+            __syncthreads();
+            if (q == 0 && i < a.T) {
+                float M = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    M = fmaxf(M, pq[k * 64 + r].x);
+                float S = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float2 o = pq[k * 64 + r];
+                    if (o.y > 0.f)
+                        S += o.y * __expf(o.x - M);
+                }
+                a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
+            }
+            __syncthreads();
         }
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
@@ -895,7 +910,8 @@ __global__ void dw_reduce_kernel(const float *dwp, int parts, int64_t Cp, const 
 }
 
 // Folds the per-tile sums of each position: lse = M + log sum_t s_t e^(m_t - M).
-// (Every tile has a finite maximum: its first column is a candidate.)
+// (Tile 0 has a finite maximum, its first column being a candidate; a later
+// tile wholly past C is (-inf, 0) and adds exp(-inf) * 0 = 0.)
 __global__ void lse_kernel(const float2 *part, int64_t T, int nct, const int32_t *slot, int32_t C,
                            const float *zt, float *loss, float *lse, Hdr *h)
 {
@@ -1107,7 +1123,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     Hdr *h = reinterpret_cast<Hdr *>(w + L.hdr);
     const int32_t V = cfg->vocab, C = cfg->candidates;
     const int64_t Tq = rup(T, kTile);
-    const int nct = (int)(L.Cp / kTile);
+    const int nct = (int)blocks(L.Cp, 64 * kFwdWN);   // column tiles of the forward
     GemmArgs a{};
     a.A = Rows{(const uint16_t *)X, kD, nullptr, (int32_t)T, V};
     a.B = Rows{(const uint16_t *)W, kD, cand, C, V};
@@ -1126,7 +1142,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     hipStream_t s = (hipStream_t)stream;
     a.tiles_m = blocks(Tq, 128);
     a.tiles_n = (uint32_t)nct;
-    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, 2, kFwdBK, kFwdS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
+    launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdWN, kFwdBK, kFwdS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
     launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
