@@ -39,7 +39,8 @@ ROW_BF16 = 768 * 2
 ROW_F32 = 768 * 4
 GROUPS = ("fwd", "sort", "reduce", "step", "stash")
 KERNEL_SRC = {"fwd": "ngram_fwd.hip", "sort": "ngram_reduce.hip", "reduce": "ngram_reduce.hip",
-              "step": "ngram_step.hip", "stash": "ngram_fwd.hip"}
+              "step": "ngram_step.hip", "stash": "ngram_fwd.hip",
+              "ssm_fwd": "ssm.hip", "ssm_dz": "ssm.hip", "ssm_dx": "ssm.hip", "ssm_dw": "ssm.hip"}
 
 
 def parse():
@@ -438,7 +439,8 @@ def main_ssm(args, torch):
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved_tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": kernels[dom]["frac_of_mfma_peak"], "traffic": None},
+                     "frac": kernels[dom]["frac_of_mfma_peak"],
+                     "traffic": pmc_traffic("ssm_" + dom, f"ssm_{T}x{C}", "ssm", "bf16")},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
