@@ -16,7 +16,9 @@ Prints one JSON line.  `value` is the window's tokens per second through the
 whole path with all inputs resident in HBM; per-kernel-group times come from
 HIP events recorded on the launch stream around each group inside the timed
 region; `roofline` reports the dominant group's algorithmic bytes per launch
-over its mean launch time against the 8 TB/s HBM3E peak; `cpu_baseline`
+(the bytes the method cannot avoid moving: each upstream gradient row read
+once, each touched row's table row and state read and written once, the row
+ids) over its mean launch time against the 8 TB/s HBM3E peak; `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -139,59 +141,64 @@ STATE = 8     # one (v, t_last) record per row
 
 
 def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_passes=3):
-    """Bytes each kernel group must move per window, listed per launch.  Per
-    unit: a token's forward reads two table rows and writes one output row
-    (plus its id); a reduced key reads its dY row; a stepped row reads and
-    writes its table row and its 8-byte state.
+    """Bytes each kernel group moves per window, listed per launch, two ways.
 
-    accumulate reduction, per micro-step: the bigram pass reads the dY row of
-      every key, the trigram pass those of keys whose row occurs more than
-      once in the micro-step (a singleton's row is written by the bigram
-      pass from the dY row it holds); per channel, a row new to the window
-      writes its window row, one already there reads and writes it;
-    fused reduction (last micro-step, or the whole window in burst modes):
-      the bigram pass reads the dY row of every key; the trigram pass reads
-      those of the keys whose row is not a singleton new to the window (the
-      others are stepped by the bigram pass from the dY row it holds); a row
-      already in the window reads its window row; every touched row reads and
-      writes its table row and its state;
-    step: per row left to it, window row read + table row read and written +
-      state read and written + slot id;
-    stash (burst): dY row read and written, token id, two indices, row code;
-    stash (burst by reference): token id, two indices, row code.
-    dY rows count dy_row bytes (3,072 fp32, 1,536 bf16); window rows are fp32."""
+    "min": what the method itself cannot avoid moving.  A token's forward
+      reads its two signed table rows and writes its output row (plus its
+      id).  A reduction reads every upstream gradient row it is given once
+      and the hashed row id of each position in each channel (4 B); a row it
+      steps reads and writes its table row and its 8-byte state; in spread
+      mode a micro-step's distinct rows also write (new to the window) or
+      read and write (already there) their fp32 window row, and the fused
+      last micro-step reads the window row of each row already there.  The
+      separate step reads the window row, table row, state and slot id of
+      each row left to it and writes the table row and state.
+    "kernel": the dY rows the kernels actually read.  The bigram pass reads
+      the dY row of every key; the trigram pass only those of keys whose
+      row is not a singleton new to the window (a singleton is stepped, or
+      stored into the window, by the bigram pass from the dY row it holds),
+      so the trigram rows that occur more than once are read twice.  The
+      other terms are as in "min".
+    stash (burst): dY row read and written (copying), token id, two indices,
+    row code.  dY rows count dy_row bytes (3,072 fp32, 1,536 bf16); window
+    rows are fp32."""
     steps, uwin, tsingle_win = stats
     A = len(steps)
     nch = len(uwin)   # tables in use: 2, or 1 for a token-indexed table
     fwd = T * ((nch + 1) * row_bytes + 4)
     table_state = 2 * row_bytes + 2 * STATE
     step_row = ROW_F32 + table_state + 4
+    ids = 4 * nch
     # sort: each radix pass reads and writes a (row, payload) pair per key of
     # every channel
-    out = {"fwd": [fwd] * A, "sort": [nch * T * 16 * radix_passes] * A}
+    mn = {"fwd": [fwd] * A, "sort": [nch * T * 16 * radix_passes] * A}
+    kn = {"fwd": [fwd] * A, "sort": [nch * T * 16 * radix_passes] * A}
     if mode in ("burst", "burst_ref"):
         n = A * T
         copy = 2 * dy_row if mode == "burst" else 0
-        out["stash"] = [T * (copy + 4 + 8 + 4)] * A
-        out["sort"] = [nch * n * 16 * radix_passes]
-        out["reduce"] = [(nch * n - tsingle_win) * dy_row + sum(uwin) * table_state]
-        out["step"] = [0]
-        return out
-    red = []
+        for d in (mn, kn):
+            d["stash"] = [T * (copy + 4 + 8 + 4)] * A
+            d["sort"] = [nch * n * 16 * radix_passes]
+            d["step"] = [0]
+        rows = sum(uwin) * table_state + n * ids
+        mn["reduce"] = [n * dy_row + rows]
+        kn["reduce"] = [(nch * n - tsingle_win) * dy_row + rows]
+        return {"min": mn, "kernel": kn}
+    red_m, red_k = [], []
     last = A - 1 if path == "fused" else A
     for m in range(last):
-        red.append(sum((T - single) * dy_row + new * ROW_F32 + (u - new) * 2 * ROW_F32
-                       for (u, new, _, single) in steps[m]))
+        win_rows = sum(new * ROW_F32 + (u - new) * 2 * ROW_F32 for (u, new, _, _) in steps[m])
+        red_m.append(T * dy_row + win_rows + T * ids)
+        red_k.append(sum((T - single) * dy_row for (_, _, _, single) in steps[m]) + win_rows + T * ids)
     fused_rows = 0
     if path == "fused":
-        b = 0
-        for (u, new, single_new, _) in steps[-1]:
-            b += (T - single_new) * dy_row + (u - new) * ROW_F32 + u * table_state
-            fused_rows += u
-        red.append(b)
-    out["reduce"] = red
-    out["step"] = [(sum(uwin) - fused_rows) * step_row]
-    return out
+        rows = sum((u - new) * ROW_F32 + u * table_state for (u, new, _, _) in steps[-1])
+        red_m.append(T * dy_row + rows + T * ids)
+        red_k.append(sum((T - single_new) * dy_row for (_, _, single_new, _) in steps[-1]) + rows + T * ids)
+        fused_rows = sum(u for (u, _, _, _) in steps[-1])
+    mn["reduce"], kn["reduce"] = red_m, red_k
+    mn["step"] = kn["step"] = [(sum(uwin) - fused_rows) * step_row]
+    return {"min": mn, "kernel": kn}
 
 
 def src_hash(name):
@@ -598,13 +605,19 @@ def main():
     passes = (rbits + 8) // 9   # the library's 9-bit radix digits
     bytes_ = [algorithmic_bytes(T, s, row_bytes, args.mode, args.path, dy_row, passes) for s in timed_stats]
     ms_all = {g_: [a.elapsed_ms(b) for a, b, _, _ in ev[g_]] for g_ in used}
-    # algorithmic bytes of each timed launch: launch m of the window's list
-    # (groups with one launch per window have a one-entry list)
-    by_all = {g_: [bytes_[win][g_][min(m, len(bytes_[win][g_]) - 1)] for _, _, win, m in ev[g_]] for g_ in used}
-    per_step = {g_: len(bytes_[0][g_]) for g_ in used}
+
+    def per_launch(kind):
+        # bytes of each timed launch: launch m of the window's list (groups
+        # with one launch per window have a one-entry list), then per group
+        # all bytes of its timed launches over their number
+        by = {g_: [bytes_[win][kind][g_][min(m, len(bytes_[win][kind][g_]) - 1)] for _, _, win, m in ev[g_]]
+              for g_ in used}
+        return {g_: float(np.sum(by[g_])) / len(ms_all[g_]) for g_ in used}
+
+    per_step = {g_: len(bytes_[0]["min"][g_]) for g_ in used}
     ms = {g_: float(np.mean(ms_all[g_])) for g_ in used}
-    # per group: all bytes of its timed launches over all their time
-    abytes = {g_: float(np.sum(by_all[g_])) / len(ms_all[g_]) for g_ in used}
+    abytes = per_launch("min")
+    kbytes = per_launch("kernel")
     upd_rows = float(np.mean([sum(s[1]) for s in timed_stats]))
     total_ms = {g_: ms[g_] * per_step[g_] for g_ in used}
     dom = max([g_ for g_ in ("fwd", "reduce", "step") if g_ in used], key=lambda g_: total_ms[g_])
@@ -628,6 +641,10 @@ def main():
                        "ms_per_step": round(total_ms[g_], 4),
                        "algorithmic_bytes_per_launch": int(abytes[g_]),
                        "achieved_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if kbytes[g_] != abytes[g_]:
+            kg = kbytes[g_] / (ms[g_] * 1e-3) / 1e9
+            kernels[g_].update({"kernel_read_bytes_per_launch": int(kbytes[g_]),
+                                "kernel_read_frac_of_hbm_peak": round(kg / HBM_PEAK_GBPS, 4)})
         if g_ == "fwd" and comp_fwd:
             cb = float(np.mean(comp_fwd))
             kernels[g_]["compulsory_bytes_per_launch"] = int(cb)
@@ -649,7 +666,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{w.dtype} table, {args.dy_dtype} dY, f32 sums",
         "data": "synthetic: Zipf token streams with EoS-aligned documents, N(0,1) upstream gradients",
         "config": {"workload": w.name, "table_rows": w.rows[0] + w.rows[1], "dim": 768,
                    "table_dtype": w.dtype, "tokens_per_micro_step": T, "accum_steps": A,

@@ -299,7 +299,7 @@ struct WsLayout {
     int64_t nrblk;          // radix tiles for nk keys
     int64_t nchunk;         // 64-key chunks for nk keys
     int64_t ngroup;         // groups of 64 chunks
-    int passes;             // radix passes (8 bits each)
+    int passes;             // radix passes (kRadixBits each)
     bool burst;             // micro-steps are kept and reduced at step time
     bool by_ref;            // ... and their dY is read where the caller keeps it
     int pos_bits;           // by_ref: dY row code = micro-step << pos_bits | position

@@ -10,7 +10,7 @@
 // and adds it to the window accumulator G[slot(r)].
 //
 // Pipeline per call, both channels in every launch (blockIdx.y = channel):
-//   1. LSD radix sort of (row, position|sign) pairs, 8-bit digits.  Each pass
+//   1. LSD radix sort of (row, position|sign) pairs, 9-bit digits.  Each pass
 //      is a per-tile LDS histogram, one digit-major scan, and a stable
 //      scatter: ranks within a tile come from wavefront ballots (64-lane
 //      match of the digit), the tile is reordered in LDS, then written out in
@@ -76,7 +76,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave
 
 // ------------------------------------------------------------ radix sort
 //
-// Tiles of 2048 keys (256 threads x 8).  Per pass: per-tile digit counts
+// Radix tiles of 256 threads x 8 keys (2,048), or x 16 (4,096) when a channel
+// has at least 2^20 keys to sort.  Per pass: per-tile digit counts
 // (hist[c][d][tile], digit-major), then one block per (digit, channel) turns
 // its row of tile counts into exclusive tile offsets and a digit total, then
 // the scatter adds the exclusive scan of the digit totals (done per block in

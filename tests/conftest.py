@@ -26,3 +26,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # the largest err / limit each parity test saw, per check (tests/helpers.py)
+    helpers = sys.modules.get("helpers")
+    if helpers is None or not getattr(helpers, "RATIOS", None):
+        return
+    tr = terminalreporter
+    tr.section("largest err/limit per parity test")
+    for test, d in sorted(helpers.RATIOS.items()):
+        tr.write_line(f"{test}: " + ", ".join(f"{k} {v:.3g}" for k, v in sorted(d.items())))

@@ -125,3 +125,57 @@ def test_window_export_is_the_per_id_gradient():
     np.testing.assert_array_equal(rows_g[order].cpu().numpy(), touched)
     helpers.assert_grad_close(G_g[order].cpu().numpy(), G, A)
     assert len(N.window_export(cfg, ws, 1, with_grad=False)[0]) == 0   # no second table
+
+
+def test_value_embeddings_bf16_at_the_bench_shape():
+    """The launch sequence bench.py --workload value times: the token-indexed
+    50,304 x 768 bf16 table, 393,216 tokens per micro-step, burst by
+    reference, three micro-steps kept and the last one reduced with the whole
+    window fused with the step; two windows.  Checked on sampled ids (the
+    hottest and random ones, fed to the oracle with every position of them):
+    v within tolerance, table rows within one bf16 ulp; every touched id's
+    t_last exact; untouched ids bitwise unchanged."""
+    N = ng()
+    w = workloads.VALUE
+    V_, T = w.rows[0], w.tokens_per_step
+    cfg = N.config(w.vocab, w.eos_id, (V_, 1), "bf16", max_tokens=T, mode="burst_ref", direct=True)
+    Wd = device_table(V_, "bf16", 77)
+    st = N.new_state(V_)
+    ws = N.Workspace(cfg)
+    rs = np.random.default_rng(2)
+    gen = torch.Generator(device="cuda")
+    for win in range(2):
+        toks = [synth.tokens(w, 4 * win + m) for m in range(4)]
+        gen.manual_seed(300 + win)
+        dys = [torch.randn((T, 768), generator=gen, device="cuda") for _ in range(4)]
+        ids = np.concatenate(toks).astype(np.int64)
+        u, cnt = np.unique(ids, return_counts=True)
+        sample = np.unique(np.concatenate([u[np.argsort(-cnt)[:8]], rs.choice(u, size=1000, replace=False)]))
+        pos = np.flatnonzero(np.isin(ids, sample))
+        dY = np.empty((len(pos), 768), np.float32)
+        for m in range(4):
+            sel = (pos // T) == m
+            dY[sel] = dys[m].index_select(0, torch.from_numpy(pos[sel] - m * T).cuda()).cpu().numpy()
+        plus = np.zeros(len(pos), np.uint8)
+        touched, G = oracle.window_grad(ids[pos], plus, dY)
+        _, A = oracle.window_grad(ids[pos], plus, np.abs(dY))
+        del dY
+        assert np.array_equal(touched, sample)
+        W0, v0, t0 = host_rows(Wd, sample), host_vec(N.state_v(st), sample), host_vec(N.state_t_last(st), sample)
+        cand = np.setdiff1d(np.arange(V_), u)
+        Wc = host_rows(Wd, cand)
+        tok_d = [to_dev(x) for x in toks]
+        for m in range(3):
+            N.embed_bwd_accum(cfg, ws, tok_d[m], dys[m])
+        t = win + 1
+        N.embed_bwd_step(cfg, ws, tok_d[3], dys[3], Wd, None, st, None, t, w.lr, w.beta2, w.eps)
+        torch.cuda.synchronize()
+        W_o, v_o, t_o = oracle.sparse_step(G, W0, v0, t0, t, w.lr, w.beta2, w.eps)
+        np.testing.assert_array_equal(host_vec(N.state_t_last(st), sample), t_o)
+        assert int((N.state_t_last(st) == t).sum()) == len(u)
+        helpers.assert_v_close(host_vec(N.state_v(st), sample), v_o, G=G, absbound=A, beta2=w.beta2)
+        helpers.assert_rows_close(host_rows(Wd, sample), W_o, W0, "bf16")
+        np.testing.assert_array_equal(host_rows(Wd, cand), Wc)
+        assert int(cnt.max()) > 100_000   # the hottest id spans thousands of chunks
+        del dys
+    assert N.device_status(cfg, ws) == 0

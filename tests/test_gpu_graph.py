@@ -5,13 +5,16 @@ its step number and learning rate in device memory (the _dev step entry
 points) -- is captured once and replayed for several windows, with new
 tokens, gradients and step parameters copied into the captured buffers
 between replays.  Every replay must equal the same window run eagerly through
-the host-scalar entry points, bitwise: the same kernels on the same inputs.
+the host-scalar entry points, bitwise: the same kernels on the same inputs,
+and every replayed window is also checked against the oracle (touched sets
+and t_last exact, v and W within tolerance, untouched rows unchanged).
 Eager work and synchronisations run between the replays."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import State, ng, to_dev, window_inputs
+from gpu_common import (State, check_step_against_oracle, ng, oracle_snapshots, to_dev, window_inputs,
+                        window_oracle)
 from sparse_hashed_gram_amd import synth, workloads
 
 pytestmark = pytest.mark.gpu
@@ -73,9 +76,11 @@ def test_graph_replay_equals_eager(mode, how):
             tok_s[m].copy_(toks[m])
             dy_s[m].copy_(dys[m])
         N.step_params(t, lr, w.beta2, w.eps, out=params)
+        snaps = oracle_snapshots(graph, window_oracle(cfg, toks_np, dys_np), np.random.default_rng(win))
         g.replay()
         outs = _window_eager(N, cfg, eager, ws_e, toks, dys, t, lr, w.beta2, w.eps, how)
         torch.cuda.synchronize()
+        check_step_against_oracle(graph, snaps, t, lr, w.beta2, w.eps, "f32")
         for m in range(A):
             assert torch.equal(out_s[m], outs[m]), f"window {win}: forward {m} differs"
         for c in range(2):

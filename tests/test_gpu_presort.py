@@ -7,13 +7,15 @@ the backward then only attaches the gradients.  The results must be bitwise
 those of the regular path (the same keys at the same stash positions, the
 same sort, the same sums), which the other GPU tests hold to the oracle.  A
 window that is not ready when it is reduced (keys without gradients, not
-sorted since its last keys) must be dropped without changing any row.
+sorted since its last keys) must be dropped without changing any row.  The
+windows taken ahead are also checked against the oracle directly.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_common import State, ng, to_dev, window_inputs
+from gpu_common import (State, check_step_against_oracle, ng, oracle_snapshots, to_dev, window_inputs,
+                        window_oracle)
 from sparse_hashed_gram_amd import synth, workloads
 
 pytestmark = pytest.mark.gpu
@@ -62,13 +64,14 @@ def test_keys_ahead_equal_the_regular_path(mode, presort, how):
         toks_np, dys_np = window_inputs(W, 4 * win)
         toks = [to_dev(x) for x in toks_np]
         dys = [to_dev(x) for x in dys_np]
+        snaps = oracle_snapshots(ahd, window_oracle(cfg_a, toks_np, dys_np), np.random.default_rng(win))
         _regular_window(N, cfg_r, reg, ws_r, toks, dys, win + 1, how)
         _ahead_window(N, cfg_a, ahd, ws_a, toks, dys, win + 1, how, 4, side)
         torch.cuda.synchronize()
         for c in range(2):
             assert torch.equal(reg.W[c], ahd.W[c]), (win, c)
             assert torch.equal(reg.st[c], ahd.st[c]), (win, c)
-        assert int((ahd.tl[0] == win + 1).sum()) > 0
+        check_step_against_oracle(ahd, snaps, win + 1, W.lr, W.beta2, W.eps, "f32")
     assert N.device_status(cfg_a, ws_a) == 0
 
 
@@ -84,11 +87,15 @@ def test_some_keys_ahead_ragged(mode):
     for win in range(3):
         toks = [to_dev(synth.tokens(W, 300 + 4 * win + m, Ts[m])) for m in range(4)]
         dys = [to_dev(synth.dY(W, 300 + 4 * win + m, Ts[m])) for m in range(4)]
+        toks_np = [synth.tokens(W, 300 + 4 * win + m, Ts[m]) for m in range(4)]
+        dys_np = [synth.dY(W, 300 + 4 * win + m, Ts[m]) for m in range(4)]
+        snaps = oracle_snapshots(ahd, window_oracle(cfg_r, toks_np, dys_np), np.random.default_rng(win))
         _regular_window(N, cfg_r, reg, ws_r, toks, dys, win + 1, "step")
         _ahead_window(N, cfg_r, ahd, ws_a, toks, dys, win + 1, "step", 2, side)
         torch.cuda.synchronize()
         for c in range(2):
             assert torch.equal(reg.W[c], ahd.W[c]) and torch.equal(reg.st[c], ahd.st[c])
+        check_step_against_oracle(ahd, snaps, win + 1, W.lr, W.beta2, W.eps, "f32")
     assert N.device_status(cfg_r, ws_a) == 0
 
 

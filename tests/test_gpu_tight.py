@@ -1,0 +1,117 @@
+"""The step held to the plain bound where the window gradient is exact.
+
+In a window where every touched row occurs at exactly one position, each
+row's window gradient is s dY of that position: no summation, so no
+implementation has any gradient error to carry into the step.  The step's
+results are then held to the bound with no propagation term: v within 1e-5
+relative, table rows within one ulp of the result plus 1e-5 of the update
+(fp32 tables), or one bf16 ulp (bf16 tables).  Lazy row-wise Adam with
+beta1 = 0 and one second moment per row, beta2 applied for the optimizer
+steps a row missed (the @classiclarryd post quoted on the airebao.com item).
+
+The token streams are drawn so that every bigram row and every trigram row
+of the window is hit once (tokens at colliding positions are redrawn until
+none collide); the second window draws new streams, so rows met again
+decay by beta2^(t - t_last).  All three modes and both step paths: the
+standalone step over an exported window, the step fused into the reduction
+(the last micro-step, or the whole burst window).
+"""
+import numpy as np
+import pytest
+import torch
+
+import helpers
+import oracle
+from gpu_common import State, device_table, dy_dev, host_rows, host_vec, ng, to_dev
+from sparse_hashed_gram_amd import synth, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def singleton_window(vocab, eos, rows, A, T, seed):
+    """A micro-steps of T tokens in which no bigram row and no trigram row of
+    the window occurs twice."""
+    rs = np.random.default_rng(seed)
+    toks = rs.integers(0, vocab, size=(A, T)).astype(np.int32)
+    for _ in range(10_000):
+        rr = [oracle.ngram_rows(toks[m], vocab, eos, rows) for m in range(A)]
+        dup = np.zeros(A * T, bool)
+        for c in range(2):
+            r = np.concatenate([x[2 * c] for x in rr])
+            _, first = np.unique(r, return_index=True)
+            d = np.ones(A * T, bool)
+            d[first] = False
+            dup |= d
+        if not dup.any():
+            return [toks[m].copy() for m in range(A)]
+        idx = np.flatnonzero(dup)
+        toks.reshape(-1)[idx] = rs.integers(0, vocab, size=len(idx))
+    raise RuntimeError("no collision-free window found")
+
+
+CASES = [("spread", "export"), ("spread", "fused_last"), ("burst", "export"), ("burst", "step"),
+         ("burst_ref", "export"), ("burst_ref", "step")]
+
+
+@pytest.mark.parametrize("table", ["tiny_f32", "shard_bf16"])
+@pytest.mark.parametrize("mode,how", CASES)
+def test_singleton_windows_tight_bound(mode, how, table):
+    N = ng()
+    w = workloads.TINY if table == "tiny_f32" else workloads.SHARD
+    dtype = "f32" if table == "tiny_f32" else "bf16"
+    T = 256 if table == "tiny_f32" else 49_152
+    cfg = N.config(w.vocab, w.eos_id, w.rows, dtype, max_tokens=T, mode=mode)
+    if dtype == "f32":
+        st = State(cfg, to_dev(synth.init_rows(w, 0, w.rows[0])), to_dev(synth.init_rows(w, 1, w.rows[1])))
+    else:
+        st = State(cfg, device_table(w.rows[0], "bf16", 71), device_table(w.rows[1], "bf16", 72))
+    ws = N.Workspace(cfg)
+    rs = np.random.default_rng(9)
+    for win in range(2):
+        toks = singleton_window(w.vocab, w.eos_id, w.rows, 4, T, 40 + win)
+        dys = [synth.dY(w, 100 + 4 * win + m, T) for m in range(4)]
+        rows = [helpers.oracle_rows(w, t, w.rows) for t in toks]
+        orc = []
+        for c in range(2):
+            r = np.concatenate([x[2 * c] for x in rows])
+            n = np.concatenate([x[2 * c + 1] for x in rows])
+            assert len(np.unique(r)) == len(r)
+            touched, G = oracle.window_grad(r, n, np.concatenate(dys))
+            order = np.argsort(r)
+            np.testing.assert_array_equal(G, np.where(n[order, None] == 1, -1.0, 1.0).astype(np.float32)
+                                          * np.concatenate(dys)[order])   # G = s dY exactly
+            cand = np.setdiff1d(rs.integers(0, w.rows[c], size=2048), touched)[:512]
+            orc.append(dict(touched=touched, G=G, W=host_rows(st.W[c], touched), v=host_vec(st.v[c], touched),
+                            tl=host_vec(st.tl[c], touched), cand=cand, Wc=host_rows(st.W[c], cand)))
+        keep = [dy_dev(d) for d in dys]
+        last = 3 if how == "fused_last" else 4
+        for m in range(last):
+            N.embed_bwd_accum(cfg, ws, to_dev(toks[m]), keep[m])
+        t = win + 1
+        if how == "export":
+            N.window_reduce(cfg, ws)
+            for c in range(2):   # the exported gradient is s dY exactly
+                r_g, G_g = N.window_export(cfg, ws, c)
+                order = torch.argsort(r_g)
+                np.testing.assert_array_equal(r_g[order].cpu().numpy(), orc[c]["touched"])
+                np.testing.assert_array_equal(G_g[order].cpu().numpy(), orc[c]["G"])
+            st.step(ws, t, w.lr, w.beta2, w.eps)
+        elif how == "fused_last":
+            st.bwd_step(ws, to_dev(toks[3]), keep[3], t, w.lr, w.beta2, w.eps)
+        else:
+            st.step(ws, t, w.lr, w.beta2, w.eps)
+        torch.cuda.synchronize()
+        for c in range(2):
+            o = orc[c]
+            W_o, v_o, t_o = oracle.sparse_step(o["G"], o["W"], o["v"], o["tl"], t, w.lr, w.beta2, w.eps)
+            np.testing.assert_array_equal(host_vec(st.tl[c], o["touched"]), t_o)
+            assert int((st.tl[c] == t).sum()) == len(o["touched"])
+            helpers.assert_v_close(host_vec(st.v[c], o["touched"]), v_o)
+            helpers.assert_rows_close(host_rows(st.W[c], o["touched"]), W_o, o["W"], dtype)
+            np.testing.assert_array_equal(host_rows(st.W[c], o["cand"]), o["Wc"])
+        if win == 1:   # rows met in both windows decayed by beta2^1
+            assert any(int((o["tl"] == 1).sum()) > 0 for o in orc)
+        del keep
+    assert N.device_status(cfg, ws) == 0
+    del st, ws
+    torch.cuda.empty_cache()

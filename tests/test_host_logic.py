@@ -93,41 +93,53 @@ TS = 2 * ROW + 16    # table row read + written, state read + written
 @pytest.mark.parametrize("dy_row", [3072, 1536])
 def test_bytes_burst_by_reference(dy_row):
     b = bench.algorithmic_bytes(T, STATS, ROW, "burst_ref", "fused", dy_row, radix_passes=3)
-    assert b["fwd"] == [T * (3 * ROW + 4)] * 2
-    assert b["stash"] == [T * 16] * 2              # token, two indices, row code
-    assert b["sort"] == [2 * 20 * 16 * 3]
-    # every bigram key and every trigram key but the window's singletons read
-    # their dY row; every distinct row of either channel is stepped once
-    assert b["reduce"] == [(40 - 12) * dy_row + 24 * TS]
-    assert b["step"] == [0]
+    mn, kn = b["min"], b["kernel"]
+    assert mn["fwd"] == kn["fwd"] == [T * (3 * ROW + 4)] * 2
+    assert mn["stash"] == [T * 16] * 2              # token, two indices, row code
+    assert mn["sort"] == [2 * 20 * 16 * 3]
+    # the method's minimum: every dY row once, both channels' row ids, every
+    # distinct row of either channel stepped once
+    assert mn["reduce"] == [20 * dy_row + 24 * TS + 20 * 8]
+    # the kernels: every bigram key and every trigram key but the window's
+    # singletons read their dY row
+    assert kn["reduce"] == [(40 - 12) * dy_row + 24 * TS + 20 * 8]
+    assert mn["step"] == kn["step"] == [0]
 
 
 def test_bytes_copying_burst_adds_the_dy_copy():
     b = bench.algorithmic_bytes(T, STATS, ROW, "burst", "fused", 3072, radix_passes=3)
-    assert b["stash"] == [T * (2 * 3072 + 16)] * 2
+    assert b["min"]["stash"] == b["kernel"]["stash"] == [T * (2 * 3072 + 16)] * 2
 
 
 def test_bytes_spread_fused_last():
     b = bench.algorithmic_bytes(T, STATS, ROW, "spread", "fused", 3072, radix_passes=2)
-    assert b["sort"] == [2 * T * 16 * 2] * 2
-    # micro-step 0 (accumulating): dY of every key but trigram singletons of
-    # the micro-step; new rows written (3 KB), rows already there read and
-    # written (6 KB)
-    m0 = (T - 0) * 3072 + 6 * 3072 + 0 + (T - 8) * 3072 + 9 * 3072 + 0
-    # micro-step 1 (fused with the step): dY of every key but trigram rows
-    # that are singletons new to the window; rows already in the window read
-    # their window row; every row it touches is stepped
-    m1 = (T - 0) * 3072 + 3 * 3072 + 5 * TS + (T - 5) * 3072 + 3 * 3072 + 10 * TS
-    assert b["reduce"] == [m0, m1]
+    mn, kn = b["min"], b["kernel"]
+    assert mn["sort"] == [2 * T * 16 * 2] * 2
+    # micro-step 0 (accumulating): new rows written (3 KB), rows already there
+    # read and written (6 KB); the method reads each dY row once, the kernels
+    # read it for every key but the micro-step's trigram singletons
+    win0 = 6 * 3072 + 0 + 9 * 3072 + 0
+    m0_min = T * 3072 + win0 + T * 8
+    m0_k = (T - 0) * 3072 + (T - 8) * 3072 + win0 + T * 8
+    # micro-step 1 (fused with the step): rows already in the window read
+    # their window row; every row it touches is stepped; the kernels read dY
+    # for every key but the trigram rows that are singletons new to the window
+    rows1 = 3 * 3072 + 5 * TS + 3 * 3072 + 10 * TS
+    m1_min = T * 3072 + rows1 + T * 8
+    m1_k = (T - 0) * 3072 + (T - 5) * 3072 + rows1 + T * 8
+    assert mn["reduce"] == [m0_min, m1_min]
+    assert kn["reduce"] == [m0_k, m1_k]
     # the separate step takes the window's other rows
-    assert b["step"] == [(24 - 15) * (3072 + TS + 4)]
+    assert mn["step"] == kn["step"] == [(24 - 15) * (3072 + TS + 4)]
 
 
 def test_bytes_spread_accumulate_then_step():
     b = bench.algorithmic_bytes(T, STATS, ROW, "spread", "accum", 3072, radix_passes=2)
-    m1 = (T - 0) * 3072 + 2 * 3072 + 3 * 6144 + (T - 6) * 3072 + 7 * 3072 + 3 * 6144
-    assert b["reduce"][1] == m1 and len(b["reduce"]) == 2
-    assert b["step"] == [24 * (3072 + TS + 4)]
+    win1 = 2 * 3072 + 3 * 6144 + 7 * 3072 + 3 * 6144
+    assert b["kernel"]["reduce"][1] == (T - 0) * 3072 + (T - 6) * 3072 + win1 + T * 8
+    assert b["min"]["reduce"][1] == T * 3072 + win1 + T * 8
+    assert len(b["min"]["reduce"]) == 2
+    assert b["min"]["step"] == [24 * (3072 + TS + 4)]
 
 
 def test_gpus_above_one_exit_with_a_message(capsys, monkeypatch):
