@@ -1,0 +1,355 @@
+// Host model of the indexing of the fused reduction + step (seg_step_kernel,
+// group_sum_kernel and fixup_kernel in ngram_reduce.hip), for bounds checks on
+// the CPU.  TEST INFRASTRUCTURE.
+//
+// Each 64-key chunk is planned and walked as the kernel's wavefront does,
+// with the wavefront's 64 lanes as arrays and its ballots, readlanes and
+// lane shuffles as loops.  Every address the kernel forms -- sorted keys,
+// payloads and head info, the singleton map, dY rows (micro-step base +
+// position), table rows and row state of both channels, window rows and
+// slot rows, partial rows, fix-up records, group sums -- is checked against
+// the extent of its buffer before it would be used.  The model also checks
+// what the indexing is for: every key is walked by exactly one wavefront,
+// every segment is completed exactly once (in its chunk, by the owner of a
+// one-chunk spill-over, or by the fix-up), every partial row and group sum
+// the fix-up reads was written, and every trigram singleton is stepped once.
+//
+// Build: g++ -O2 -std=c++17 -shared -fPIC seg_step_index.cpp (the test does).
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kChunk = 64;
+constexpr int kGroup = 64;
+constexpr int kFixThreads = 1024;
+constexpr uint32_t kNewHead = 0xFFFFFFFEu;
+constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
+
+struct Ctx {
+    // inputs
+    int64_t n;              // keys of this channel
+    const uint32_t *R, *V, *I;
+    int64_t nk;             // capacity of the sorted arrays (R, V, I extents)
+    const uint32_t *tinfo;  // singleton map (bigram pass only), code_cap entries
+    int64_t code_cap;
+    int pos_bits;           // dY row code = micro-step << pos_bits | position
+    int n_micro;            // micro-steps whose dY addresses are attached
+    const int64_t *Tm;      // positions of each micro-step
+    int64_t rows_c, rows_t; // rows of this channel's table and of the trigram table
+    int64_t wrows;          // window slots
+    int64_t nchunk, ngroup; // extents of the partial rows / fix-up records, group sums
+    int step_u;             // keys per batch
+    // results
+    std::vector<int> walked;        // per key: wavefronts that walked it
+    std::vector<int> completed;     // per key at a segment head: completions of the segment
+    std::vector<int> tstepped;      // per dY row code: trigram singleton steps
+    std::vector<int> partial_w;     // [nchunk][2]: partial rows written
+    std::vector<uint64_t> owners;   // fix-up records
+    int64_t violations = 0;
+    char first[256] = {0};
+    int64_t accesses = 0;
+};
+
+void bad(Ctx &x, const char *what, int64_t idx, int64_t ext, int64_t chunk)
+{
+    if (x.violations++ == 0)
+        snprintf(x.first, sizeof(x.first), "%s index %lld outside [0, %lld) in chunk %lld", what, (long long)idx,
+                 (long long)ext, (long long)chunk);
+}
+
+bool in(Ctx &x, const char *what, int64_t idx, int64_t ext, int64_t chunk)
+{
+    ++x.accesses;
+    if (idx < 0 || idx >= ext) {
+        bad(x, what, idx, ext, chunk);
+        return false;
+    }
+    return true;
+}
+
+uint32_t getR(Ctx &x, int64_t i, int64_t chunk)
+{
+    return in(x, "sorted row", i, x.nk, chunk) && in(x, "sorted row (count)", i, x.n, chunk) ? x.R[i] : 0u;
+}
+
+struct Plan {
+    uint32_t r0[kWave], v0[kWave], i0[kWave], v1[kWave];
+    uint64_t hm;
+    int nv, j0, jend, la;
+    bool first_cont, last_spills, owner_full;
+    uint32_t row_last;
+};
+
+int ctz64(uint64_t m) { return __builtin_ctzll(m); }
+int clz64(uint64_t m) { return __builtin_clzll(m); }
+
+bool plan(Ctx &x, int64_t chunk, Plan &p)
+{
+    const int64_t c0 = chunk * kChunk;
+    if (c0 >= x.n)
+        return false;
+    p.nv = (int)(x.n - c0 < kChunk ? x.n - c0 : kChunk);
+    bool head[kWave];
+    p.hm = 0;
+    for (int l = 0; l < kWave; ++l) {
+        const bool valid = l < p.nv;
+        p.r0[l] = valid ? getR(x, c0 + l, chunk) : 0xFFFFFFFFu;
+        p.v0[l] = valid && in(x, "sorted payload", c0 + l, x.nk, chunk) ? x.V[c0 + l] : 0u;
+    }
+    for (int l = 0; l < kWave; ++l) {
+        uint32_t prev = l > 0 ? p.r0[l - 1] : (c0 > 0 ? getR(x, c0 - 1, chunk) : 0xFFFFFFFFu);
+        head[l] = l < p.nv && p.r0[l] != prev;
+        if (head[l])
+            p.hm |= 1ull << l;
+    }
+    for (int l = 0; l < kWave; ++l)
+        p.i0[l] = head[l] && in(x, "head info", c0 + l, x.nk, chunk) ? x.I[c0 + l] : 0u;
+    p.row_last = p.r0[p.nv - 1];
+    const bool cont_after = p.nv == kChunk && c0 + kChunk < x.n && getR(x, c0 + kChunk, chunk) == p.row_last;
+    p.first_cont = !(p.hm & 1ull);
+    const int e0 = p.hm ? ctz64(p.hm) : p.nv;
+    bool skip_first = false;
+    if (p.first_cont) {
+        const uint32_t row0 = p.r0[0];
+        const bool piece0_cont = (e0 == p.nv) && cont_after;
+        const bool head_in_prev = (c0 == kChunk) || (getR(x, c0 - kChunk - 1, chunk) != row0);
+        skip_first = head_in_prev && !piece0_cont;
+    }
+    p.la = p.hm ? 63 - clz64(p.hm) : -1;
+    p.last_spills = p.hm && cont_after;
+    p.owner_full = false;
+    int extra = 0;
+    for (int l = 0; l < kWave; ++l)
+        p.v1[l] = 0;
+    if (p.last_spills) {
+        p.owner_full = !(c0 + 2 * kChunk < x.n && getR(x, c0 + 2 * kChunk, chunk) == p.row_last);
+        if (p.owner_full) {
+            for (int l = 0; l < kWave; ++l) {
+                const int64_t i1 = c0 + kChunk + l;
+                const bool ok1 = i1 < x.n;
+                const uint32_t r1 = ok1 ? getR(x, i1, chunk) : 0xFFFFFFFFu;
+                p.v1[l] = ok1 && in(x, "spill payload", i1, x.nk, chunk) ? x.V[i1] : 0u;
+                extra += (ok1 && r1 == p.row_last) ? 1 : 0;
+            }
+        }
+    }
+    p.j0 = skip_first ? e0 : 0;
+    p.jend = p.owner_full ? kChunk + extra : p.nv;
+    return true;
+}
+
+bool seg_ends(const Plan &p, int k)
+{
+    if (k >= kChunk - 1 && p.owner_full)
+        return k == p.jend - 1;
+    if (k == p.nv - 1)
+        return true;
+    return (k + 1 < kChunk) && ((p.hm >> (k + 1)) & 1ull);
+}
+
+// The readlane of lane j (< 128) of the pair (v0: lanes 0..63, v1: 64..127).
+uint32_t lane_val(Ctx &x, const uint32_t *v0, const uint32_t *v1, int j, int64_t chunk)
+{
+    if (j < 0 || j >= 2 * kWave) {
+        bad(x, "readlane", j, 2 * kWave, chunk);
+        return 0;
+    }
+    return j < kWave ? v0[j] : v1[j - kWave];
+}
+
+// The address checks of one dY row (by reference: the micro-step's own buffer).
+void dy_row(Ctx &x, uint32_t code, int64_t chunk)
+{
+    const int64_t m = (int64_t)(code >> x.pos_bits);
+    const int64_t pos = code & (uint32_t)((1ull << x.pos_bits) - 1u);
+    if (in(x, "dY micro-step (readlane of the dY base lanes)", m, kWave, chunk) &&
+        in(x, "dY micro-step attached", m, x.n_micro, chunk))
+        in(x, "dY position", pos, x.Tm[m], chunk);
+}
+
+void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
+{
+    Plan p;
+    if (!plan(x, chunk, p))
+        return;
+    const int64_t c0 = chunk * kChunk;
+    uint32_t t0[kWave], t1[kWave];
+    for (int l = 0; l < kWave; ++l) {
+        t0[l] = t1[l] = kNotSingle;
+        if (tsplit) {
+            if (l < p.nv && in(x, "singleton map", p.v0[l] & 0x7FFFFFFFu, x.code_cap, chunk))
+                t0[l] = x.tinfo[p.v0[l] & 0x7FFFFFFFu];
+            if (p.owner_full && kChunk + l < p.jend && in(x, "singleton map", p.v1[l] & 0x7FFFFFFFu, x.code_cap, chunk))
+                t1[l] = x.tinfo[p.v1[l] & 0x7FFFFFFFu];
+        }
+    }
+    uint64_t fin = (p.hm >> 1) | (1ull << (p.nv - 1));
+    if (p.first_cont && p.j0 == 0) {
+        const int e0 = p.hm ? ctz64(p.hm) : p.nv;
+        fin &= ~(1ull << (e0 - 1));
+    }
+    if (p.last_spills)
+        fin &= ~(1ull << 63);
+    int ps = p.j0;
+    for (int j = p.j0; j < p.jend; j += x.step_u) {
+        for (int u = 0; u < x.step_u; ++u) {
+            const int k = j + u;
+            if (k >= p.jend)
+                break;
+            const uint32_t v = lane_val(x, p.v0, p.v1, k, chunk);
+            dy_row(x, v & 0x7FFFFFFFu, chunk);
+            const int64_t key = c0 + k;   // keys past the chunk are the next chunk's (owned spill-over)
+            if (in(x, "walked key", key, x.n, chunk))
+                x.walked[key] += 1;
+            const bool ends_here = k < kChunk ? ((fin >> k) & 1ull) != 0 : (p.owner_full && k == p.jend - 1);
+            if (k < kChunk && k != p.j0 && ((p.hm >> k) & 1ull))
+                ps = k;
+            if (tsplit) {
+                const uint32_t tv = lane_val(x, t0, t1, k, chunk);
+                if (tv != kNotSingle) {
+                    const uint32_t tr = tv & 0x7FFFFFFFu;
+                    in(x, "trigram singleton table row", tr, x.rows_t, chunk);
+                    if (in(x, "singleton step count", v & 0x7FFFFFFFu, x.code_cap, chunk))
+                        x.tstepped[v & 0x7FFFFFFFu] += 1;
+                }
+            }
+            if (ends_here) {
+                const uint32_t row = k < kChunk ? lane_val(x, p.r0, p.r0, k, chunk) : p.row_last;
+                in(x, "table row", row, x.rows_c, chunk);
+                const uint32_t info = lane_val(x, p.i0, p.i0, ps, chunk);
+                if (info != kNewHead)
+                    in(x, "window slot", info, x.wrows, chunk);
+                const int64_t head = c0 + ps;
+                if (in(x, "segment head", head, x.n, chunk))
+                    x.completed[head] += 1;
+            } else if (seg_ends(p, k)) {
+                // flush_partial
+                if (ps == 0 && p.first_cont) {
+                    if (in(x, "partial row", chunk, x.nchunk, chunk))
+                        x.partial_w[2 * chunk] += 1;
+                } else {
+                    const uint32_t info = lane_val(x, p.i0, p.i0, ps, chunk);
+                    if (in(x, "partial row", chunk, x.nchunk, chunk))
+                        x.partial_w[2 * chunk + 1] += 1;
+                    if (in(x, "fix-up record", (int64_t)x.owners.size(), x.nchunk, chunk))
+                        x.owners.push_back((uint64_t)chunk | ((uint64_t)info << 32));
+                }
+            }
+        }
+    }
+}
+
+// group_sum_kernel: which groups of 64 chunks get a sum (partial rows 0 of
+// all their chunks read).
+void group_sums(Ctx &x, std::vector<int> &gw)
+{
+    const int64_t ng = (x.n > 0) ? ((x.n + kChunk - 1) / kChunk + kGroup - 1) / kGroup : 0;
+    for (int64_t g = 0; g < ng; ++g) {
+        const int64_t k0 = g * kGroup * kChunk, k1 = k0 + kGroup * kChunk;
+        if (g == 0 || k1 >= x.n)
+            continue;
+        if (getR(x, k0 - 1, -1) != getR(x, k1, -1))
+            continue;
+        for (int64_t c = g * kGroup; c < (g + 1) * kGroup; ++c)
+            if (in(x, "group member partial", c, x.nchunk, -1) && x.partial_w[2 * c] != 1)
+                bad(x, "group sum of an unwritten partial row (chunk)", c, x.nchunk, -1);
+        if (in(x, "group sum", g, x.ngroup, -1))
+            gw[g] = 1;
+    }
+}
+
+void fixup(Ctx &x, const std::vector<int> &gw)
+{
+    for (size_t k = 0; k < x.owners.size(); ++k) {
+        const int64_t chunk = (int64_t)(uint32_t)x.owners[k];
+        const uint32_t info = (uint32_t)(x.owners[k] >> 32);
+        const uint32_t row = getR(x, chunk * kChunk + kChunk - 1, chunk);
+        if (info != kNewHead)
+            in(x, "fix-up window slot", info, x.wrows, chunk);
+        in(x, "fix-up table row", row, x.rows_c, chunk);
+        int64_t m = 0;
+        for (int l = 0; l < kWave; ++l) {
+            const int64_t cc = chunk + 1 + l;
+            m += (cc * kChunk < x.n && getR(x, cc * kChunk, chunk) == row) ? 1 : 0;
+        }
+        if (m == kWave) {
+            for (;;) {
+                int cnt = 0;
+                for (int t = 0; t < kFixThreads; ++t) {
+                    const int64_t cc = chunk + 1 + m + t;
+                    cnt += (cc * kChunk < x.n && getR(x, cc * kChunk, chunk) == row) ? 1 : 0;
+                }
+                m += cnt;
+                if (cnt < kFixThreads)
+                    break;
+            }
+        }
+        const int64_t first = chunk + 1, last = chunk + m;
+        const int64_t g_lo = (first + kGroup - 1) / kGroup, g_hi = last / kGroup;
+        const int64_t ng = g_hi > g_lo ? g_hi - g_lo : 0;
+        const int64_t n_before = ng ? g_lo * kGroup - first : m;
+        const int64_t np = 1 + n_before + ng + (ng ? last - g_hi * kGroup + 1 : 0);
+        // the owner's tail piece, then the items in order
+        if (in(x, "fix-up tail piece", chunk, x.nchunk, chunk) && x.partial_w[2 * chunk + 1] != 1)
+            bad(x, "fix-up of an unwritten tail piece (chunk)", chunk, x.nchunk, chunk);
+        for (int64_t q = 1; q < np; ++q) {
+            if (q <= n_before || q > n_before + ng) {
+                const int64_t c = q <= n_before ? first + q - 1 : g_hi * kGroup + q - 1 - n_before - ng;
+                if (in(x, "fix-up head piece", c, x.nchunk, chunk) && x.partial_w[2 * c] != 1)
+                    bad(x, "fix-up of an unwritten head piece (chunk)", c, x.nchunk, chunk);
+            } else {
+                const int64_t g = g_lo + q - 1 - n_before;
+                if (in(x, "fix-up group sum", g, x.ngroup, chunk) && gw[g] != 1)
+                    bad(x, "fix-up of an unwritten group sum (group)", g, x.ngroup, chunk);
+            }
+        }
+        // the segment's head: the last head of the owner chunk
+        int64_t h = chunk * kChunk + kChunk - 1;
+        while (h > chunk * kChunk && x.R[h - 1] == row)
+            --h;
+        x.completed[h] += 1;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns the number of violations; `msg` (256 bytes) gets the first.  Fills
+// walked[n], completed[n] (at segment heads) and tstepped[code_cap].
+int64_t model_channel(int64_t n, const uint32_t *R, const uint32_t *V, const uint32_t *I, int64_t nk,
+                      const uint32_t *tinfo, int64_t code_cap, int pos_bits, int n_micro, const int64_t *Tm,
+                      int64_t rows_c, int64_t rows_t, int64_t wrows, int64_t nchunk, int64_t ngroup, int step_u,
+                      int32_t *walked, int32_t *completed, int32_t *tstepped, int64_t *accesses, char *msg)
+{
+    Ctx x;
+    x.n = n; x.R = R; x.V = V; x.I = I; x.nk = nk; x.tinfo = tinfo; x.code_cap = code_cap;
+    x.pos_bits = pos_bits; x.n_micro = n_micro; x.Tm = Tm; x.rows_c = rows_c; x.rows_t = rows_t;
+    x.wrows = wrows; x.nchunk = nchunk; x.ngroup = ngroup; x.step_u = step_u;
+    x.walked.assign(n, 0);
+    x.completed.assign(n, 0);
+    x.tstepped.assign(code_cap, 0);
+    x.partial_w.assign(2 * nchunk, 0);
+    const int64_t chunks = (n + kChunk - 1) / kChunk;
+    for (int64_t ch = 0; ch < chunks; ++ch)
+        walk_chunk(x, ch, tinfo != nullptr);
+    std::vector<int> gw(ngroup > 0 ? ngroup : 1, 0);
+    group_sums(x, gw);
+    fixup(x, gw);
+    for (int64_t i = 0; i < n; ++i) {
+        walked[i] = x.walked[i];
+        completed[i] = x.completed[i];
+    }
+    for (int64_t i = 0; i < code_cap; ++i)
+        tstepped[i] = x.tstepped[i];
+    *accesses = x.accesses;
+    memcpy(msg, x.first, sizeof(x.first));
+    return x.violations;
+}
+
+}  // extern "C"

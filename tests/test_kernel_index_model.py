@@ -1,0 +1,176 @@
+"""Bounds of the fused reduction's indexing, checked on the CPU.
+
+tests/kernel_model/seg_step_index.cpp walks the sorted keys of a burst
+window exactly as seg_step_kernel's wavefronts do (the chunk plan, the
+readlanes of keys 0..127, the dY row of each key from its micro-step and
+position, the singleton map, table rows and state, window slots, partial
+rows and fix-up records; then group_sum_kernel and fixup_kernel) and checks
+every index against the extent of its buffer in the workspace layout.  It
+also checks the bookkeeping the indexing serves: each key walked once, each
+segment completed once, each trigram singleton stepped once, and every
+partial row or group sum the fix-up reads written.
+
+The windows are those of the GPU tests: the full Zipf 1.1 window and the
+collision-stress window (4 x 393,216 positions, 42.3M rows per table), the
+ragged window (262,143 / 100,000 / 7 / 150,001 positions), one hot row over
+20,000 positions, and the token-indexed value-embedding window (hot ids of
+more than 64 chunks' worth of keys: the fix-up's block-wide scan).  The
+sorted keys, their payloads and the singleton map are built here the way the
+library defines them (stable sort by row; payload = micro-step << pos_bits |
+position with the sign in bit 31; a trigram row that occurs once in the
+window is a singleton), from the oracle's rows.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_hashed_gram_amd import synth, workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kernel_model", "seg_step_index.cpp")
+NEW_HEAD = 0xFFFFFFFE
+NOT_SINGLE = 0xFFFFFFFF
+
+
+@pytest.fixture(scope="module")
+def model(tmp_path_factory):
+    lib = str(tmp_path_factory.mktemp("model") / "libsegmodel.so")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", SRC, "-o", lib])
+    L = ctypes.CDLL(lib)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.model_channel.restype = i64
+    L.model_channel.argtypes = [i64, vp, vp, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp, i64, i64, i64,
+                                i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    return L
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _sorted_keys(rows, neg, codes):
+    order = np.argsort(rows, kind="stable")
+    R = rows[order].astype(np.uint32)
+    V = (codes[order].astype(np.uint64) | (neg[order].astype(np.uint64) << 31)).astype(np.uint32)
+    return R, V
+
+
+def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, step_u=2):
+    nchunk = (nk + 63) // 64
+    ngroup = (nchunk + 63) // 64
+    walked = np.zeros(max(n, 1), np.int32)
+    completed = np.zeros(max(n, 1), np.int32)
+    tstepped = np.zeros(code_cap, np.int32)
+    acc = ctypes.c_int64()
+    msg = ctypes.create_string_buffer(256)
+    Tm = np.ascontiguousarray(Tm, np.int64)
+    wrows = min(max(rows_c, rows_t), nk)
+    ext = np.zeros(nk, np.uint32)   # the arrays at their workspace extent (nk entries)
+    Rx, Vx, Ix = ext.copy(), ext.copy(), ext.copy()
+    Rx[:n], Vx[:n], Ix[:n] = R, V, I
+    viol = model.model_channel(n, _p(Rx), _p(Vx), _p(Ix), nk, _p(tinfo), code_cap, pos_bits, len(Tm), _p(Tm),
+                               rows_c, rows_t, wrows, nchunk, ngroup, step_u, _p(walked), _p(completed),
+                               _p(tstepped), ctypes.byref(acc), msg)
+    assert viol == 0, msg.value.decode()
+    assert acc.value > 0
+    return walked[:n], completed[:n], tstepped
+
+
+def _heads(R):
+    h = np.ones(len(R), bool)
+    h[1:] = R[1:] != R[:-1]
+    return h
+
+
+def _check_window(model, toks, rows, max_tokens, direct=False):
+    """Both channels of one burst-by-reference window, fused with the step."""
+    A = len(toks)
+    pos_bits = max(0, int(max_tokens - 1).bit_length())
+    code_cap = A << pos_bits
+    nk = A * max_tokens
+    codes, rb, nb, rt, nt = [], [], [], [], []
+    for m, tok in enumerate(toks):
+        codes.append((np.uint64(m) << np.uint64(pos_bits)) | np.arange(len(tok), dtype=np.uint64))
+        if direct:
+            rb.append(tok.astype(np.int64))
+            nb.append(np.zeros(len(tok), np.uint8))
+        else:
+            b, x, t, y, _ = oracle.ngram_rows(tok, workloads.VOCAB, workloads.EOS_ID, rows)
+            rb.append(b); nb.append(x); rt.append(t); nt.append(y)
+    codes = np.concatenate(codes)
+    n = len(codes)
+    Tm = [len(t) for t in toks]
+    Rb, Vb = _sorted_keys(np.concatenate(rb), np.concatenate(nb), codes)
+    Ib = np.where(_heads(Rb), NEW_HEAD, 0).astype(np.uint32)
+    tinfo = None
+    if not direct:
+        Rt, Vt = _sorted_keys(np.concatenate(rt), np.concatenate(nt), codes)
+        h = _heads(Rt)
+        ends = np.ones(n, bool)
+        ends[:-1] = Rt[1:] != Rt[:-1]
+        single = h & ends
+        tinfo = np.full(code_cap, NOT_SINGLE, np.uint32)
+        tinfo[Vt & 0x7FFFFFFF] = np.where(single, Rt | (Vt & 0x80000000), NOT_SINGLE).astype(np.uint32)
+    walked, completed, tstepped = _run(model, n, Rb, Vb, Ib, nk, tinfo, code_cap, pos_bits, Tm, rows[0],
+                                       rows[1] if not direct else 1)
+    assert (walked == 1).all(), np.flatnonzero(walked != 1)[:10]
+    np.testing.assert_array_equal(completed, _heads(Rb).astype(np.int32))
+    if direct:
+        return
+    # trigram singletons: stepped once each by the bigram pass, never walked again
+    sc = (Vt & 0x7FFFFFFF)[single]
+    assert (tstepped[sc] == 1).all() and int(tstepped.sum()) == int(single.sum())
+    # the split keeps the other trigram keys, in order, with their head info
+    keep = ~single
+    Rs, Vs = Rt[keep], Vt[keep]
+    Is = np.where(h[keep], NEW_HEAD, 0).astype(np.uint32)
+    w2, c2, _ = _run(model, len(Rs), Rs, Vs, Is, nk, None, code_cap, pos_bits, Tm, rows[1], rows[1])
+    assert (w2 == 1).all()
+    np.testing.assert_array_equal(c2, _heads(Rs).astype(np.int32))
+    # every trigram row completed exactly once over both passes
+    assert int(c2.sum()) + int(single.sum()) == int(h.sum())
+
+
+def test_full_window(model):
+    w = workloads.FULL
+    _check_window(model, [synth.tokens(w, m) for m in range(4)], w.rows, w.tokens_per_step)
+
+
+def test_collision_window(model):
+    w = workloads.COLLISION
+    _check_window(model, [synth.tokens(w, m) for m in range(4)], w.rows, w.tokens_per_step)
+
+
+def test_ragged_window(model):
+    w = workloads.FULL
+    Ts = [262_143, 100_000, 7, 150_001]
+    _check_window(model, [synth.tokens(w, 20 + m, Ts[m]) for m in range(4)], w.rows, max(Ts))
+
+
+@pytest.mark.parametrize("T", [65, 129, 4097, 20_000])
+def test_single_hot_row(model, T):
+    # one token repeated: every position hits the same bigram and trigram rows
+    # (after the first two), segments of thousands of keys over many chunks
+    toks = [np.full(T, 17, np.int32)]
+    _check_window(model, toks, (4096, 4096), T)
+
+
+def test_value_embedding_window(model):
+    w = workloads.VALUE
+    _check_window(model, [synth.tokens(w, m) for m in range(4)], (w.rows[0], 1), w.tokens_per_step, direct=True)
+
+
+def test_the_model_reports_an_index_past_its_buffer(model):
+    # the model itself: told that micro-step 0 has one position fewer than its
+    # keys name, it must report that key's dY row as out of bounds
+    tok = synth.tokens(workloads.TINY, 0, 300)
+    rb, nb, _, _, _ = oracle.ngram_rows(tok, workloads.VOCAB, workloads.EOS_ID, (4096, 4096))
+    codes = np.arange(300, dtype=np.uint64)
+    R, V = _sorted_keys(rb, nb, codes)
+    I = np.where(_heads(R), NEW_HEAD, 0).astype(np.uint32)
+    with pytest.raises(AssertionError, match="dY position"):
+        _run(model, 300, R, V, I, 300, None, 512, 9, [299], 4096, 4096)
