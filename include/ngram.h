@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 7
+#define NGRAM_ABI_VERSION 8
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -314,6 +314,35 @@ int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws,
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
                         uint32_t *rows, float *G, int64_t max_rows,
                         uint32_t *count, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one whole
+ * accumulation window reduced and stepped in a single call, with no caller
+ * workspace.  The same as, on a fresh workspace of cfg in burst-by-reference
+ * mode with accum_steps = n_micro and max_tokens = T, calling
+ * ngram_embed_bwd_accum for micro-steps 0 .. n_micro - 2 and
+ * ngram_embed_bwd_step for the last one (same kernels, same results).
+ * tokens: int32 [n_micro][T] (each micro-step starts without context, as in
+ * every other call); dY: [n_micro][T][768] of cfg->dy_dtype, 16-byte aligned,
+ * read in place while the call's kernels run; tables and row state as for
+ * ngram_sparse_step.  cfg's mode, accum_steps, max_tokens, window_rows and
+ * NGRAM_OPT_PRESORT are ignored; its tables, hash, dtypes and the other
+ * options apply.
+ * The window's workspace is a fixed 32 MiB array in the library's device
+ * code, one per GPU, held until the process ends; the call allocates
+ * nothing.  Limits: 1 <= n_micro <= 64 and n_micro * T <= 65,536 positions,
+ * else NGRAM_ESIZE (nothing enqueued); T = 0 does nothing.  The array is
+ * shared by every call on the same GPU and is re-initialised at each call:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  flags (device uint32, may be NULL): the
+ * call ORs its NGRAM_FLAG_* bits into it when its kernels end.  The current
+ * device must be the stream's device. */
+int ngram_window_step_noalloc(const ngram_config *cfg, const int32_t *tokens,
+                              const void *dY, int64_t T, int32_t n_micro,
+                              void *W_b, void *W_t, ngram_row_state *state_b,
+                              ngram_row_state *state_t, int32_t t, float lr,
+                              float beta2, float eps, uint32_t *flags,
+                              void *stream);
 
 /* Kernel groups for ngram_profile_events. */
 #define NGRAM_PROF_FWD 0    /* the forward gather-sum kernel              */

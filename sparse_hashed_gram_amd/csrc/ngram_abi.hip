@@ -8,6 +8,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ngram.h"
 #include "ngram_dev.hpp"
 
@@ -72,10 +74,15 @@ int check_cfg(const ngram_config *c)
     return NGRAM_OK;
 }
 
-WsLayout layout(const ngram_config *c)
+// one_shot: the layout of a whole burst window reduced and stepped in one
+// call on an empty window (ngram_window_step_noalloc): the slot maps, slot
+// rows and window accumulator, which only rows of an earlier reduce of the
+// window would use, take no memory.
+WsLayout layout(const ngram_config *c, bool one_shot = false)
 {
     WsLayout L;
     memset(&L, 0, sizeof(L));
+    L.one_shot = one_shot;
     L.burst = c->mode != NGRAM_MODE_SPREAD;
     L.by_ref = c->mode == NGRAM_MODE_BURST_REF;
     L.accum = c->accum_steps;
@@ -103,14 +110,14 @@ WsLayout layout(const ngram_config *c)
     o = up(o + sizeof(WsHeader));
     for (int k = 0; k < 2; ++k) {
         L.slot_map[k] = o;
-        o = up(o + sizeof(SlotEntry) * (uint64_t)c->rows[k]);
+        o = up(o + (one_shot ? 0 : sizeof(SlotEntry) * (uint64_t)c->rows[k]));
     }
     for (int k = 0; k < 2; ++k) {
         L.slot_rows[k] = o;
-        o = up(o + 4ull * (uint64_t)L.wrows);
+        o = up(o + (one_shot ? 0 : 4ull * (uint64_t)L.wrows));
     }
     L.gacc = o;
-    o = up(o + 4ull * 2 * (uint64_t)L.wrows * kDim);
+    o = up(o + (one_shot ? 0 : 4ull * 2 * (uint64_t)L.wrows * kDim));
     for (int k = 0; k < 2; ++k) {
         L.keys[k] = o;
         o = up(o + 4ull * 2 * (uint64_t)L.nk);
@@ -517,6 +524,105 @@ int ngram_window_export(const ngram_config *cfg, const void *ws, int channel, ui
     const WsLayout L = layout(cfg);
     return hip_status(launch_export(L, (const uint8_t *)ws, channel, rows, G, (uint32_t)max_rows, count,
                                     (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free window step
+//
+// For callers that cannot allocate device memory: the workspace of one whole
+// window lives in `scratch`, a fixed array in this library's device code.
+// Each GPU holds its own copy of the array at its own address; host code
+// never uses the array's name except to ask for that address
+// (hipGetSymbolAddress, once per device, kept in g_scratch).
+
+namespace {
+
+constexpr uint64_t kScratchBytes = 32ull << 20;
+constexpr int64_t kNoallocMaxPositions = 65536;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+uint8_t *g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call there; nullptr if HIP fails.
+uint8_t *scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch[dev] = static_cast<uint8_t *>(p);
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int ngram_window_step_noalloc(const ngram_config *cfg, const int32_t *tokens, const void *dY, int64_t T,
+                              int32_t n_micro, void *W_b, void *W_t, ngram_row_state *state_b,
+                              ngram_row_state *state_t, int32_t t, float lr, float beta2, float eps, uint32_t *flags,
+                              void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (T < 0 || n_micro < 1 || n_micro > kMaxMicro)
+        return NGRAM_ESIZE;
+    if ((int64_t)n_micro * T > kNoallocMaxPositions)
+        return NGRAM_ESIZE;
+    if (T > 0 && (!tokens || !dY))
+        return NGRAM_ENULL;
+    if (!aligned(tokens, 4) || !aligned(dY, 16))
+        return NGRAM_EALIGN;
+    const bool direct = (cfg->options & NGRAM_OPT_DIRECT) != 0;
+    if (!W_b || !state_b || (!direct && (!W_t || !state_t)))
+        return NGRAM_ENULL;
+    if (!aligned(W_b, 16) || !aligned(W_t, 16) || !aligned(state_b, 8) || !aligned(state_t, 8) ||
+        !aligned(flags, 4))
+        return NGRAM_EALIGN;
+    if ((rc = check_step_scalars(t, lr, beta2, eps)))
+        return rc;
+    if (T == 0)
+        return NGRAM_OK;   // an empty window touches no row
+    // the window as its own burst-by-reference configuration: n_micro
+    // micro-steps of T positions, reduced fused with the step
+    ngram_config c = *cfg;
+    c.mode = NGRAM_MODE_BURST_REF;
+    c.accum_steps = n_micro;
+    c.max_tokens = T;
+    c.window_rows = 0;
+    c.options &= ~NGRAM_OPT_PRESORT;
+    if ((rc = check_cfg(&c)))
+        return rc;
+    const WsLayout L = layout(&c, true);
+    if (L.total > kScratchBytes)
+        return NGRAM_ESIZE;
+    uint8_t *ws = scratch_ptr();
+    if (!ws)
+        return NGRAM_EHIP;
+    hipStream_t s = (hipStream_t)stream;
+    const HashParams hp = hash_params(&c);
+    const size_t dy_row = (size_t)L.dy_elt * kDim;
+    hipError_t e = launch_init(L, ws, s);
+    for (int m = 0; m < n_micro && e == hipSuccess; ++m)
+        e = launch_stash(L, ws, hp, tokens + (size_t)m * T, static_cast<const uint8_t *>(dY) + (size_t)m * T * dy_row,
+                         T, s);
+    if (e != hipSuccess)
+        return NGRAM_EHIP;
+    rc = burst_step(&c, L, ws, fuse_args(&c, W_b, W_t, state_b, state_t, t, lr, beta2, eps, nullptr), s);
+    if (rc == NGRAM_OK && flags)
+        rc = hip_status(launch_flags_export(L, ws, flags, s));
+    return rc;
 }
 
 int ngram_profile_events(int group, void *start_event, void *stop_event)

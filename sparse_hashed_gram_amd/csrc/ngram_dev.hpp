@@ -307,6 +307,10 @@ struct WsLayout {
     int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
     int nch;                // tables: 2 (bigram, trigram), or 1 (token-indexed)
+    bool one_shot;          // a whole burst window reduced and stepped in one call on an
+                            // empty window: no slot maps, slot rows or window
+                            // accumulator (their offsets name no memory and are
+                            // never dereferenced on that path)
 };
 
 // -------------------------------------------------------------- row step
@@ -463,6 +467,8 @@ hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s);
 hipError_t launch_step(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s);
 
 hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s);
+// ORs the workspace's sticky flags into the device word `out`.
+hipError_t launch_flags_export(const WsLayout &L, const uint8_t *ws, uint32_t *out, hipStream_t s);
 
 hipError_t launch_export(const WsLayout &L, const uint8_t *ws, int channel, uint32_t *rows,
                          float *G, uint32_t max_rows, uint32_t *count, hipStream_t s);

@@ -248,6 +248,11 @@ __global__ void stash_clear_kernel(WsHeader *__restrict__ hdr)
 
 __global__ void flags_clear_kernel(WsHeader *__restrict__ hdr) { hdr->flags = 0; }
 
+__global__ void flags_export_kernel(const WsHeader *__restrict__ hdr, uint32_t *__restrict__ out)
+{
+    *out |= hdr->flags;
+}
+
 __global__ void fill_u32_kernel(uint32_t *__restrict__ p, uint64_t n, uint32_t v)
 {
     for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -270,6 +275,8 @@ hipError_t launch_init(const WsLayout &L, uint8_t *ws, hipStream_t s)
     fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(hdr), sizeof(WsHeader) / 4, 0u);
     fill_u32_kernel<<<1, 1, 0, s>>>(&hdr->magic, 1, kMagic);
     fill_u32_kernel<<<1, 1, 0, s>>>(&hdr->epoch, 1, 1u);
+    if (L.one_shot)
+        return hipGetLastError();   // no slot maps
     for (int c = 0; c < 2; ++c)
         fill_u32_kernel<<<2048, 256, 0, s>>>(reinterpret_cast<uint32_t *>(ws + L.slot_map[c]),
                                              2 * (uint64_t)L.rows[c], 0u);
@@ -342,6 +349,12 @@ hipError_t launch_stash_clear(const WsLayout &L, uint8_t *ws, hipStream_t s)
 hipError_t launch_flags_clear(uint8_t *ws, const WsLayout &L, hipStream_t s)
 {
     flags_clear_kernel<<<1, 1, 0, s>>>(reinterpret_cast<WsHeader *>(ws + L.hdr));
+    return hipGetLastError();
+}
+
+hipError_t launch_flags_export(const WsLayout &L, const uint8_t *ws, uint32_t *out, hipStream_t s)
+{
+    flags_export_kernel<<<1, 1, 0, s>>>(reinterpret_cast<const WsHeader *>(ws + L.hdr), out);
     return hipGetLastError();
 }
 

@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
             "ngram_sparse_step_dev": ([cp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "ngram_embed_bwd_step_dev": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
+            "ngram_window_step_noalloc": ([cp, vp, vp, i64, i32, vp, vp, vp, vp, i32, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_float, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
             "ngram_profile_events": ([ctypes.c_int, vp, vp], ctypes.c_int),
         }
@@ -363,6 +365,27 @@ def embed_bwd_step_dev(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY
         ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), T,
         _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
         _dev(state_t, "state_t", torch.float32), _dev(params, "params"), _stream()))
+
+
+def window_step_noalloc(cfg: NgramConfig, tokens: torch.Tensor, dY: torch.Tensor, T: int, n_micro: int,
+                        W_b, W_t, state_b, state_t, t: int, lr: float, beta2: float, eps: float,
+                        flags: torch.Tensor | None = None):
+    """One whole window (tokens int32 [n_micro * T], dY [n_micro * T, 768])
+    reduced and stepped with no workspace (the library's fixed device array
+    serves as one).  flags: an optional int32 device word the call ORs its
+    device flags into."""
+    if tokens.numel() != n_micro * T or tuple(dY.shape) != (n_micro * T, DIM):
+        raise ValueError("tokens must hold n_micro * T ids and dY [n_micro * T, 768] rows")
+    dt = cfg.torch_dtype
+    _check_tables(cfg, W_b, W_t)
+    _check_state(cfg, state_b, state_t)
+    if flags is not None and (flags.numel() != 1 or flags.element_size() != 4):
+        raise ValueError("flags must be one 32-bit device word")
+    _check("ngram_window_step_noalloc", lib().ngram_window_step_noalloc(
+        ctypes.byref(cfg), _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), int(T),
+        int(n_micro), _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
+        _dev(state_t, "state_t", torch.float32), int(t), float(lr), float(beta2), float(eps),
+        _dev(flags, "flags"), _stream()))
 
 
 def window_export(cfg: NgramConfig, ws: Workspace, channel: int, with_grad: bool = True):

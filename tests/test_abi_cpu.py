@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 7
+    assert N.lib().ngram_abi_version() == 8
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -141,3 +141,30 @@ def test_host_rejections_enqueue_nothing(N):
     # bad config short-circuits everything
     c.dim = 7
     assert L.ngram_embed_fwd(cp, fake, fake, fake, 5, fake, None, None) == -3
+
+
+def test_noalloc_window_host_rejections(N):
+    # the allocation-free window step checks every size and pointer before
+    # any HIP call (sizes beyond its fixed array are refused, not truncated)
+    L = N.lib()
+    c = _good(N)
+    cp = ctypes.byref(c)
+    fake = ctypes.c_void_p(1 << 40)
+    tabs = [fake] * 4
+
+    def call(T, n, *rest, tok=fake, dy=fake, t=1, beta2=0.95, flags=None):
+        return L.ngram_window_step_noalloc(cp, tok, dy, T, n, *(rest or tabs), t, 0.01, beta2, 1e-8, flags,
+                                           None)
+
+    assert call(16_385, 4) == -4           # 65,540 positions: more than the array holds
+    assert call(65_537, 1) == -4
+    assert call(100, 0) == -4              # n_micro outside [1, 64]
+    assert call(100, 65) == -4
+    assert call(-1, 1) == -4
+    assert call(100, 4, tok=None) == -1
+    assert call(100, 4, dy=ctypes.c_void_p((1 << 40) + 8)) == -2
+    assert call(100, 4, fake, None, fake, fake) == -1      # W_t required for two tables
+    assert call(100, 4, flags=ctypes.c_void_p((1 << 40) + 2)) == -2
+    assert call(100, 4, t=0) == -5
+    assert call(100, 4, beta2=1.0) == -5
+    assert call(0, 4) == 0                 # an empty window: nothing to do, nothing enqueued
