@@ -41,8 +41,8 @@
  *     every buffer; the library never allocates, frees or synchronises in the
  *     hot calls (ngram_hash, ngram_embed_fwd, ngram_embed_bwd_accum,
  *     ngram_embed_bwd_step, ngram_window_keys, ngram_window_sort,
- *     ngram_window_reduce, ngram_sparse_step, ngram_window_export and the
- *     _dev step variants).  Those calls only enqueue work on `stream` (a
+ *     ngram_window_reduce, ngram_sparse_step, ngram_window_export,
+ *     ngram_touched_rows and the _dev step variants).  Those calls only enqueue work on `stream` (a
  *     hipStream_t; NULL = the null stream) and return; they are safe to
  *     capture in a HIP graph (with the _dev step variants, a replay can take
  *     a new step number and learning rate).
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 8
+#define NGRAM_ABI_VERSION 9
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -314,6 +314,22 @@ int ngram_embed_bwd_step_dev(const ngram_config *cfg, void *ws,
 int ngram_window_export(const ngram_config *cfg, const void *ws, int channel,
                         uint32_t *rows, float *G, int64_t max_rows,
                         uint32_t *count, void *stream);
+
+/* The distinct rows of one channel (0 bigram, 1 trigram) that the current
+ * window touches, in ascending order: the rows that receive this window's
+ * update and nothing else (the @classiclarryd post quoted on the airebao.com
+ * item: only the rows that receive updates are passed on and stepped).
+ * Valid after the window's last ngram_embed_bwd_accum (or ngram_window_keys)
+ * and before its step; it covers the rows already reduced into the window
+ * and, in the burst modes, those of every micro-step kept but not yet
+ * reduced.  rows: int32 [max_rows], device, 4-byte aligned; the first
+ * min(n, max_rows) rows are written.  count: int64, device, 8-byte aligned:
+ * n.  Sync-free (capture-safe); uses the workspace's touched-row bits (one bit
+ * per table row, 10.6 MB at 2 x 42.3M rows) and changes nothing else in it.
+ * A token-indexed table (NGRAM_OPT_DIRECT) has no channel 1: n = 0. */
+int ngram_touched_rows(const ngram_config *cfg, void *ws, int channel,
+                       int32_t *rows, int64_t max_rows, int64_t *count,
+                       void *stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): one whole

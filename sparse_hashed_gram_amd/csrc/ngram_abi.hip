@@ -159,6 +159,17 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
             o = up(o + (uint64_t)L.dy_elt * (uint64_t)L.nk * kDim);
         }
     }
+    // ngram_touched_rows: a bit per table row and the set bits per block of
+    // 8,192 words (none in the one-call window's layout)
+    uint64_t tw_max = 0;
+    for (int k = 0; k < 2; ++k) {
+        const uint64_t words = one_shot ? 0 : ((uint64_t)c->rows[k] + 31) / 32;
+        L.tbits[k] = o;
+        o = up(o + 4 * words);
+        tw_max = words > tw_max ? words : tw_max;
+    }
+    L.tblk = o;
+    o = up(o + 4 * ((tw_max + 8191) / 8192));
     L.total = o;
     return L;
 }
@@ -623,6 +634,27 @@ int ngram_window_step_noalloc(const ngram_config *cfg, const int32_t *tokens, co
     if (rc == NGRAM_OK && flags)
         rc = hip_status(launch_flags_export(L, ws, flags, s));
     return rc;
+}
+
+int ngram_touched_rows(const ngram_config *cfg, void *ws, int channel, int32_t *rows, int64_t max_rows,
+                       int64_t *count, void *stream)
+{
+    int rc = check_cfg(cfg);
+    if (rc)
+        return rc;
+    if (!ws || !count || (max_rows > 0 && !rows))
+        return NGRAM_ENULL;
+    if (channel != 0 && channel != 1)
+        return NGRAM_EARG;
+    if (max_rows < 0)
+        return NGRAM_ESIZE;
+    if (!aligned(ws, kAlign) || !aligned(rows, 4) || !aligned(count, 8))
+        return NGRAM_EALIGN;
+    const WsLayout L = layout(cfg);
+    if (channel >= L.nch)   // a token-indexed table has no second channel: no rows
+        return hip_status(launch_touched_none(count, (hipStream_t)stream));
+    return hip_status(launch_touched(L, (uint8_t *)ws, channel, rows, (uint64_t)max_rows, count,
+                                     (hipStream_t)stream));
 }
 
 int ngram_profile_events(int group, void *start_event, void *stop_event)

@@ -194,6 +194,43 @@ __device__ __forceinline__ void settle(T &x)
     asm volatile("" : "+v"(x));
 }
 
+// ---------------------------------------------------------------- scans
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d);
+        if (lane >= d)
+            v += o;
+    }
+    return v;
+}
+
+// Exclusive scan over a block of NT threads; *total (if given) gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave, uint32_t *total)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane == kWave - 1)
+        s_wave[w] = inc;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+        const uint32_t x = s_wave[i];
+        off += (i < w) ? x : 0u;
+        tot += x;
+    }
+    __syncthreads();
+    if (total)
+        *total = tot;
+    return off + inc - v;
+}
+
 // ------------------------------------------------------------ workspace
 //
 // One device allocation, carved by the host (WsLayout).  All mutable state
@@ -290,6 +327,8 @@ struct WsLayout {
     uint64_t stash_dy;      // dY dtype [nk][768] (burst, copying): the kept dY rows
     uint64_t dy_ptrs;       // const void * [64] (burst by reference): dY of each micro-step
     uint64_t mstep;         // MicroStep [64] (burst modes)
+    uint64_t tbits[2];      // uint32 [ceil(rows[c] / 32)]: touched-row bits (ngram_touched_rows)
+    uint64_t tblk;          // uint32 [ceil(words / 8192)]: set bits per block of words
     uint64_t total;
 
     int64_t rows[2];
@@ -472,5 +511,11 @@ hipError_t launch_flags_export(const WsLayout &L, const uint8_t *ws, uint32_t *o
 
 hipError_t launch_export(const WsLayout &L, const uint8_t *ws, int channel, uint32_t *rows,
                          float *G, uint32_t max_rows, uint32_t *count, hipStream_t s);
+
+// The window's distinct rows of channel c in ascending order (ngram_touched_rows).
+hipError_t launch_touched(const WsLayout &L, uint8_t *ws, int c, int32_t *rows, uint64_t max_rows, int64_t *count,
+                          hipStream_t s);
+// Writes a count of 0 (a channel with no table).
+hipError_t launch_touched_none(int64_t *count, hipStream_t s);
 
 }  // namespace ngram

@@ -39,41 +39,6 @@ __device__ __forceinline__ uint32_t count_of(const uint32_t *n_dev, uint32_t n_h
     return n_dev ? min(*n_dev, n_host) : n_host;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d);
-        if (lane >= d)
-            v += o;
-    }
-    return v;
-}
-
-// Exclusive scan over a block of NT threads; *total (if given) gets the sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave, uint32_t *total)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    const uint32_t inc = wave_incl_scan(v);
-    if (lane == kWave - 1)
-        s_wave[w] = inc;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / kWave; ++i) {
-        const uint32_t x = s_wave[i];
-        off += (i < w) ? x : 0u;
-        tot += x;
-    }
-    __syncthreads();
-    if (total)
-        *total = tot;
-    return off + inc - v;
-}
-
 // ------------------------------------------------------------ radix sort
 //
 // Radix tiles of 256 threads x 8 keys (2,048), or x 16 (4,096) when a channel

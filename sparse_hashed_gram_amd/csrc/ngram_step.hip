@@ -13,6 +13,8 @@
 // of a row share one 8-byte record, so the row's optimizer state costs one
 // small read and one small write; the window is emptied by advancing its
 // epoch afterwards, not by touching the slot map.
+#include <algorithm>
+
 #include "ngram_dev.hpp"
 
 #include "../../include/ngram.h"
@@ -193,7 +195,123 @@ __global__ void export_kernel(const WsHeader *__restrict__ hdr, int c, const uin
     }
 }
 
+// ------------------------------------------------------------ touched rows
+//
+// The distinct rows of one channel that the current window touches, in
+// ascending order: one bit per table row is set for every row the window
+// accumulator holds (its slot rows) and for every key kept in the burst
+// stash but not reduced yet, then the set bits are compacted in row order.
+// No sort: the bit array is the order.
+
+constexpr int kTouchThreads = 256;
+constexpr int kTouchWords = 32;   // consecutive bit words per thread
+constexpr int kTouchBlockWords = kTouchThreads * kTouchWords;
+
+__global__ void touched_clear_kernel(uint32_t *__restrict__ bits, uint64_t nwords)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        bits[i] = 0u;
+}
+
+// Grid-stride over the window's slot rows (the first n_slots of slot_rows)
+// and, in burst modes, the stash's packed indices of this channel (the first
+// n_stash); both counts are read here and bounded by the host's capacities.
+__global__ void touched_mark_kernel(const WsHeader *__restrict__ hdr, int c, const uint32_t *__restrict__ slot_rows,
+                                    uint32_t slot_cap, const uint32_t *__restrict__ sidx, uint32_t stash_cap,
+                                    uint32_t *__restrict__ bits)
+{
+    const uint32_t ns = min(hdr->n_slots[c], slot_cap);
+    const uint32_t nst = sidx ? min(hdr->n_stash, stash_cap) : 0u;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (uint64_t)ns + nst; i += stride) {
+        const uint32_t r = i < ns ? (slot_rows[i] & ~kSlotStepped) : (sidx[i - ns] & 0x7FFFFFFFu);
+        atomicOr(&bits[r >> 5], 1u << (r & 31u));
+    }
+}
+
+// Set bits per block of kTouchBlockWords words.
+__global__ __launch_bounds__(kTouchThreads) void touched_count_kernel(const uint32_t *__restrict__ bits,
+                                                                      uint64_t nwords, uint32_t *__restrict__ blk)
+{
+    __shared__ uint32_t s_wave[kTouchThreads / kWave];
+    const uint64_t w0 = (uint64_t)blockIdx.x * kTouchBlockWords + (uint64_t)threadIdx.x * kTouchWords;
+    uint32_t cnt = 0;
+    for (int j = 0; j < kTouchWords; ++j)
+        cnt += w0 + j < nwords ? (uint32_t)__popc(bits[w0 + j]) : 0u;
+    uint32_t total;
+    block_excl_scan<kTouchThreads>(cnt, s_wave, &total);
+    if (threadIdx.x == 0)
+        blk[blockIdx.x] = total;
+}
+
+// Writes the rows of the set bits in ascending order (the first max_rows of
+// them) and the number of touched rows to *count.
+__global__ __launch_bounds__(kTouchThreads) void touched_write_kernel(const uint32_t *__restrict__ bits,
+                                                                      uint64_t nwords,
+                                                                      const uint32_t *__restrict__ blk,
+                                                                      uint32_t nblk, int32_t *__restrict__ rows,
+                                                                      uint64_t max_rows, int64_t *__restrict__ count)
+{
+    __shared__ uint32_t s_wave[kTouchThreads / kWave];
+    const uint32_t b = blockIdx.x;
+    uint32_t part = 0, part_before = 0;
+    for (uint32_t k = threadIdx.x; k < nblk; k += kTouchThreads) {
+        const uint32_t x = blk[k];
+        part += x;
+        part_before += k < b ? x : 0u;
+    }
+    uint32_t before, all;
+    block_excl_scan<kTouchThreads>(part_before, s_wave, &before);
+    block_excl_scan<kTouchThreads>(part, s_wave, &all);
+    if (b == 0 && threadIdx.x == 0)
+        *count = (int64_t)all;
+    const uint64_t w0 = (uint64_t)b * kTouchBlockWords + (uint64_t)threadIdx.x * kTouchWords;
+    uint32_t cnt = 0;
+    for (int j = 0; j < kTouchWords; ++j)
+        cnt += w0 + j < nwords ? (uint32_t)__popc(bits[w0 + j]) : 0u;
+    uint64_t o = (uint64_t)before + block_excl_scan<kTouchThreads>(cnt, s_wave, nullptr);
+    for (int j = 0; j < kTouchWords && w0 + j < nwords; ++j) {
+        uint32_t m = bits[w0 + j];
+        while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1u;
+            if (o < max_rows)
+                rows[o] = (int32_t)(((w0 + j) << 5) + bit);
+            ++o;
+        }
+    }
+}
+
+__global__ void touched_none_kernel(int64_t *__restrict__ count) { *count = 0; }
+
 }  // namespace
+
+hipError_t launch_touched(const WsLayout &L, uint8_t *ws, int c, int32_t *rows, uint64_t max_rows, int64_t *count,
+                          hipStream_t s)
+{
+    const WsHeader *hdr = reinterpret_cast<const WsHeader *>(ws + L.hdr);
+    uint32_t *bits = reinterpret_cast<uint32_t *>(ws + L.tbits[c]);
+    uint32_t *blk = reinterpret_cast<uint32_t *>(ws + L.tblk);
+    const uint64_t nwords = ((uint64_t)L.rows[c] + 31) / 32;
+    const uint32_t nblk = (uint32_t)((nwords + kTouchBlockWords - 1) / kTouchBlockWords);
+    touched_clear_kernel<<<(unsigned)std::min<uint64_t>((nwords + 255) / 256, 4096), 256, 0, s>>>(bits, nwords);
+    const uint32_t slot_cap = (uint32_t)L.wrows;
+    const uint32_t stash_cap = L.burst ? (uint32_t)L.nk : 0u;
+    const uint32_t *sidx = L.burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) + (size_t)c * L.nk : nullptr;
+    const uint64_t items = (uint64_t)slot_cap + stash_cap;
+    touched_mark_kernel<<<(unsigned)std::min<uint64_t>((items + 255) / 256, 8192), 256, 0, s>>>(
+        hdr, c, reinterpret_cast<const uint32_t *>(ws + L.slot_rows[c]), slot_cap, sidx, stash_cap, bits);
+    touched_count_kernel<<<nblk, kTouchThreads, 0, s>>>(bits, nwords, blk);
+    touched_write_kernel<<<nblk, kTouchThreads, 0, s>>>(bits, nwords, blk, nblk, rows, max_rows, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_touched_none(int64_t *count, hipStream_t s)
+{
+    touched_none_kernel<<<1, 1, 0, s>>>(count);
+    return hipGetLastError();
+}
 
 hipError_t launch_step(const WsLayout &L, uint8_t *ws, const FuseArgs &f, hipStream_t s)
 {

@@ -136,6 +136,7 @@ def lib() -> ctypes.CDLL:
             "ngram_sparse_step_dev": ([cp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "ngram_embed_bwd_step_dev": ([cp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "ngram_window_export": ([cp, vp, ctypes.c_int, vp, vp, i64, vp, vp], ctypes.c_int),
+            "ngram_touched_rows": ([cp, vp, ctypes.c_int, vp, i64, vp, vp], ctypes.c_int),
             "ngram_window_step_noalloc": ([cp, vp, vp, i64, i32, vp, vp, vp, vp, i32, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, vp, vp], ctypes.c_int),
             "ngram_device_status": ([cp, vp, vp, ctypes.c_int, vp], ctypes.c_int),
@@ -365,6 +366,23 @@ def embed_bwd_step_dev(cfg: NgramConfig, ws: Workspace, tokens: torch.Tensor, dY
         ctypes.byref(cfg), ws.ptr, _dev(tokens, "tokens", torch.int32), _dev(dY, "dY", cfg.dy_torch_dtype), T,
         _dev(W_b, "W_b", dt), _dev(W_t, "W_t", dt), _dev(state_b, "state_b", torch.float32),
         _dev(state_t, "state_t", torch.float32), _dev(params, "params"), _stream()))
+
+
+def touched_rows(cfg: NgramConfig, ws: Workspace, channel: int, rows: torch.Tensor | None = None,
+                 count: torch.Tensor | None = None):
+    """The window's distinct rows of one channel, ascending, as (rows int32
+    [capacity], count int64 [1]) device tensors: no synchronisation (the first
+    count.item() entries are the rows).  capacity defaults to the window's
+    row capacity."""
+    dev = ws.tensor.device
+    if rows is None:
+        rows = torch.empty(cfg.window_capacity, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+    _check("ngram_touched_rows", lib().ngram_touched_rows(
+        ctypes.byref(cfg), ws.ptr, int(channel), _dev(rows, "rows", torch.int32), rows.numel(),
+        _dev(count, "count", torch.int64), _stream()))
+    return rows, count
 
 
 def window_step_noalloc(cfg: NgramConfig, tokens: torch.Tensor, dY: torch.Tensor, T: int, n_micro: int,

@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 8
+    assert N.lib().ngram_abi_version() == 9
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -135,6 +135,12 @@ def test_host_rejections_enqueue_nothing(N):
     assert L.ngram_sparse_step_dev(cp, *ok, None, None) == -1
     assert L.ngram_sparse_step_dev(cp, *ok, ctypes.c_void_p((1 << 40) + 4), None) == -2
     assert L.ngram_embed_bwd_step_dev(cp, fake, fake, fake, 5, *[fake] * 4, None, None) == -1
+    # touched-rows arguments
+    assert L.ngram_touched_rows(cp, fake, 2, fake, 10, fake, None) == -5
+    assert L.ngram_touched_rows(cp, fake, 0, fake, -1, fake, None) == -4
+    assert L.ngram_touched_rows(cp, fake, 0, None, 10, fake, None) == -1
+    assert L.ngram_touched_rows(cp, fake, 0, fake, 10, None, None) == -1
+    assert L.ngram_touched_rows(cp, fake, 0, fake, 10, ctypes.c_void_p((1 << 40) + 4), None) == -2
     # export arguments
     assert L.ngram_window_export(cp, fake, 2, fake, None, 10, fake, None) == -5
     assert L.ngram_window_export(cp, fake, 0, fake, None, -1, fake, None) == -4

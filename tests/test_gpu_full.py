@@ -4,6 +4,7 @@ configuration bench.py times.  The oracle cannot hold the whole table, so
 outputs are checked on samples it computes one by one:
 
 - forward: 4,096 sampled positions per micro-step, bit-exact;
+- the window's touched rows in ascending order (ngram_touched_rows), exact;
 - backward: the full touched set (exact), and the window gradient of sampled
   rows (random touched rows plus the hottest ones), fed to the oracle with
   exactly the entries hashed to those rows;
@@ -119,6 +120,14 @@ def _run_and_check_window(st, ws, toks, dy_seeds, rs, check_fwd=True, fused_last
             break
         N.embed_bwd_accum(cfg, ws, tok_d, dys[m])
     if not fused_last:
+        # the window's distinct rows, ascending, before any reduce in the
+        # burst modes (read from the stash) or after the spread reduces
+        for c in range(2):
+            got, cnt = N.touched_rows(cfg, ws, c)
+            want = np.unique(np.concatenate([p[2 * c] for p in per]))
+            assert int(cnt.item()) == len(want)
+            np.testing.assert_array_equal(got[:len(want)].cpu().numpy().astype(np.int64), want)
+            del got
         N.window_reduce(cfg, ws)
     snaps = []
     for c in range(2):

@@ -53,6 +53,8 @@ def test_graph_replay_equals_eager(mode, how):
     dy_s = [torch.zeros((T, 768), dtype=torch.float32, device="cuda") for _ in range(A)]
     out_s = [torch.empty((T, 768), dtype=torch.float32, device="cuda") for _ in range(A)]
     params = N.step_params(1, w.lr, w.beta2, w.eps)
+    trows = [torch.empty(A * T, dtype=torch.int32, device="cuda") for _ in range(2)]
+    tcount = [torch.empty(1, dtype=torch.int64, device="cuda") for _ in range(2)]
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
@@ -65,6 +67,8 @@ def test_graph_replay_equals_eager(mode, how):
             else:
                 N.embed_bwd_accum(cfg, ws_g, tok_s[m], dy_s[m])
         if how == "step":
+            for c in range(2):   # the window's rows, ascending, captured with the rest
+                N.touched_rows(cfg, ws_g, c, rows=trows[c], count=tcount[c])
             N.sparse_step_dev(cfg, ws_g, graph.W[0], graph.W[1], graph.st[0], graph.st[1], params)
 
     for win in range(3):
@@ -81,6 +85,11 @@ def test_graph_replay_equals_eager(mode, how):
         outs = _window_eager(N, cfg, eager, ws_e, toks, dys, t, lr, w.beta2, w.eps, how)
         torch.cuda.synchronize()
         check_step_against_oracle(graph, snaps, t, lr, w.beta2, w.eps, "f32")
+        if how == "step":
+            for c in range(2):
+                want = snaps[c]["touched"]
+                assert int(tcount[c].item()) == len(want)
+                np.testing.assert_array_equal(trows[c][:len(want)].cpu().numpy().astype(np.int64), want)
         for m in range(A):
             assert torch.equal(out_s[m], outs[m]), f"window {win}: forward {m} differs"
         for c in range(2):
