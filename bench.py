@@ -106,35 +106,67 @@ def device_table(torch, R, dtype, seed, chunk=1 << 21):
     return W
 
 
+def nested_keys(torch, rb, rt, known=None):
+    """Trigram keys the fused reduction's bigram pass completes (so the
+    trigram pass does not read their dY rows again): keys of trigram rows new
+    to the window (not in `known`) whose keys lie in one 2,048-key tile of the
+    trigram order and share one bigram row and one 64-key chunk of the
+    (bigram row, trigram row, position) order.  rb, rt: the rows of the
+    positions, in stream order."""
+    n = rb.numel()
+    if n == 0:
+        return 0
+    idx = torch.arange(n, device=rb.device)
+    ot = torch.sort(rt, stable=True).indices
+    obt = ot[torch.sort(rb[ot], stable=True).indices]
+    posb = torch.empty_like(obt)
+    posb[obt] = idx
+    Rt = rt[ot]
+    head = torch.ones(n, dtype=torch.bool, device=rb.device)
+    head[1:] = Rt[1:] != Rt[:-1]
+    end = torch.ones(n, dtype=torch.bool, device=rb.device)
+    end[:-1] = Rt[1:] != Rt[:-1]
+    hidx = torch.cummax(torch.where(head, idx, torch.zeros_like(idx)), 0).values
+    eidx = torch.flip(torch.cummin(torch.flip(torch.where(end, idx, torch.full_like(idx, n)), [0]), 0).values, [0])
+    seg = torch.cumsum(head.long(), 0) - 1
+    bkey = rb[ot] * (1 << 32) + (posb[ot] >> 6)
+    bad = torch.zeros(n, dtype=torch.bool, device=rb.device)
+    bad[1:] = (~head[1:]) & (bkey[1:] != bkey[:-1])
+    if known is not None:
+        bad |= head & torch.isin(Rt, known)
+    fail = torch.zeros(int(seg[-1]) + 1, dtype=torch.int32, device=rb.device)
+    fail.scatter_reduce_(0, seg, bad.int(), reduce="amax")
+    nested = ((hidx // 2048) == (eidx // 2048)) & (fail[seg] == 0)
+    return int(nested.sum())
+
+
 def window_stats(torch, N, cfg, toks):
     """From the library's own hash, per micro-step and table in use: distinct
-    rows, rows new to the window, and (trigram) rows that occur once in the
-    micro-step and are new to the window, and rows that occur once in it;
-    distinct rows of the whole window; trigram rows that occur once in the
-    whole window.  A token-indexed table has one channel."""
+    rows, rows new to the window, and (trigram) the keys the fused reduction
+    of that micro-step would complete in its bigram pass (nested_keys, rows
+    already in the window excluded), and the rows that occur once in it;
+    distinct rows of the whole window; the keys the window's fused reduction
+    completes in its bigram pass.  A token-indexed table has one channel."""
     nch = 1 if cfg.options & N.OPT_DIRECT else 2
     steps = []
     seen = [None] * nch
-    all_t = []
+    all_r = [[], []]
     for tok in toks:
         idx = N.hash(cfg, tok)
         per = []
+        rows = [(idx[c] & 0x7FFFFFFF).long() for c in range(nch)]
         for c in range(nch):
-            r = (idx[c] & 0x7FFFFFFF).long()
+            r = rows[c]
             u, cnt = torch.unique(r, return_counts=True)
             fresh = torch.ones_like(u, dtype=torch.bool) if seen[c] is None else ~torch.isin(u, seen[c])
-            single_new = int(((cnt == 1) & fresh).sum()) if c == 1 else 0
+            handled = nested_keys(torch, rows[0], r, seen[1]) if c == 1 else 0
             single = int((cnt == 1).sum()) if c == 1 else 0
-            per.append((int(u.numel()), int(fresh.sum()), single_new, single))
+            per.append((int(u.numel()), int(fresh.sum()), handled, single))
             seen[c] = u if seen[c] is None else torch.unique(torch.cat([seen[c], u]))
-            if c == 1:
-                all_t.append(r)
+            all_r[c].append(r)
         steps.append(per)
-    tsingle = 0
-    if all_t:
-        _, cnt = torch.unique(torch.cat(all_t), return_counts=True)
-        tsingle = int((cnt == 1).sum())
-    return steps, [int(s.numel()) for s in seen], tsingle
+    handled_win = nested_keys(torch, torch.cat(all_r[0]), torch.cat(all_r[1])) if nch == 2 else 0
+    return steps, [int(s.numel()) for s in seen], handled_win
 
 
 STATE = 8     # one (v, t_last) record per row
@@ -154,15 +186,17 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_pas
       separate step reads the window row, table row, state and slot id of
       each row left to it and writes the table row and state.
     "kernel": the dY rows the kernels actually read.  The bigram pass reads
-      the dY row of every key; the trigram pass only those of keys whose
-      row is not a singleton new to the window (a singleton is stepped, or
-      stored into the window, by the bigram pass from the dY row it holds),
-      so the trigram rows that occur more than once are read twice.  The
-      other terms are as in "min".
+      the dY row of every key.  The accumulating trigram pass reads those of
+      keys whose row is not a singleton of the micro-step (a singleton is
+      stored into the window by the bigram pass from the dY row it holds);
+      the fused trigram pass reads those of keys whose row the bigram pass
+      does not complete itself (nested_keys: singletons and nested runs new
+      to the window), so the other trigram rows are read twice.  The other
+      terms are as in "min".
     stash (burst): dY row read and written (copying), token id, two indices,
     row code.  dY rows count dy_row bytes (3,072 fp32, 1,536 bf16); window
     rows are fp32."""
-    steps, uwin, tsingle_win = stats
+    steps, uwin, handled_win = stats
     A = len(steps)
     nch = len(uwin)   # tables in use: 2, or 1 for a token-indexed table
     fwd = T * ((nch + 1) * row_bytes + 4)
@@ -182,7 +216,7 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_pas
             d["step"] = [0]
         rows = sum(uwin) * table_state + n * ids
         mn["reduce"] = [n * dy_row + rows]
-        kn["reduce"] = [(nch * n - tsingle_win) * dy_row + rows]
+        kn["reduce"] = [(nch * n - handled_win) * dy_row + rows]
         return {"min": mn, "kernel": kn}
     red_m, red_k = [], []
     last = A - 1 if path == "fused" else A
@@ -194,7 +228,7 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_pas
     if path == "fused":
         rows = sum((u - new) * ROW_F32 + u * table_state for (u, new, _, _) in steps[-1])
         red_m.append(T * dy_row + rows + T * ids)
-        red_k.append(sum((T - single_new) * dy_row for (_, _, single_new, _) in steps[-1]) + rows + T * ids)
+        red_k.append(sum((T - handled) * dy_row for (_, _, handled, _) in steps[-1]) + rows + T * ids)
         fused_rows = sum(u for (u, _, _, _) in steps[-1])
     mn["reduce"], kn["reduce"] = red_m, red_k
     mn["step"] = kn["step"] = [(sum(uwin) - fused_rows) * step_row]

@@ -144,6 +144,13 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
     L.code_cap = L.by_ref ? ((int64_t)L.accum << L.pos_bits) : L.nk;
     L.tinfo = o;
     o = up(o + 4ull * (uint64_t)L.code_cap);
+    L.nested = L.nch == 2 && c->rows[1] < (int64_t(1) << 30);
+    L.bidx = o;
+    o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
+    L.posb = o;
+    o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
+    L.tkept = o;
+    o = up(o + (L.nested ? (uint64_t)L.nk : 0));
     if (L.burst) {
         L.stash_idx = o;
         o = up(o + 4ull * 2 * (uint64_t)L.nk);

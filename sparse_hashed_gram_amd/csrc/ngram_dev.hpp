@@ -320,8 +320,14 @@ struct WsLayout {
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
     uint64_t gpart;         // fp32 [2][ngroup][768]: sums of 64-chunk groups inside one segment
-    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row's singleton
-                            // record (see the singleton split), else kNotSingle
+    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row's record
+                            // when the bigram pass completes that row (see the
+                            // singleton split and the nested trigram rows), else kNotSingle
+    uint64_t bidx;          // uint32 [code_cap]: per dY row code, its packed bigram index
+                            // (nested sort: the bigram keys are gathered in trigram order)
+    uint64_t posb;          // uint32 [code_cap]: per dY row code, its index in the
+                            // (bigram row, trigram row, position) order (nested sort)
+    uint64_t tkept;         // uint8 [nk]: per trigram-sorted key, kept for the trigram pass
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position
     uint64_t stash_dy;      // dY dtype [nk][768] (burst, copying): the kept dY rows
@@ -346,6 +352,9 @@ struct WsLayout {
     int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
     int nch;                // tables: 2 (bigram, trigram), or 1 (token-indexed)
+    bool nested;            // fused reductions sort the bigram keys by (bigram row,
+                            // trigram row) and complete nested trigram rows in the
+                            // bigram pass (two tables with rows[1] < 2^30)
     bool one_shot;          // a whole burst window reduced and stepped in one call on an
                             // empty window: no slot maps, slot rows or window
                             // accumulator (their offsets name no memory and are

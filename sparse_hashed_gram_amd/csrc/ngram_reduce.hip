@@ -52,11 +52,14 @@ __device__ __forceinline__ uint32_t count_of(const uint32_t *n_dev, uint32_t n_h
 // position i of the micro-step is hashed from the tokens.  Burst: every
 // position kept in the stash, whose packed indices were hashed when kept.
 // Also clears the fix-up record counts of the reduce that follows.
-template <bool FROM_STASH, int ITEMS>
+// NESTED: only the trigram keys are built here; each position's packed
+// bigram index goes to bidx[row code], from where the bigram keys are
+// gathered in trigram order once the trigram keys are sorted.
+template <bool FROM_STASH, int ITEMS, bool NESTED>
 __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     const int32_t *__restrict__ tok, const uint32_t *__restrict__ sidx, const uint32_t *__restrict__ spos,
     HashParams hp, uint32_t n_host, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals, int64_t nk,
-    uint32_t *__restrict__ hist, uint32_t nblk, WsHeader *__restrict__ hdr)
+    uint32_t *__restrict__ hist, uint32_t nblk, WsHeader *__restrict__ hdr, uint32_t *__restrict__ bidx)
 {
     __shared__ uint32_t h[2][kRadix];
     const int tid = threadIdx.x;
@@ -85,11 +88,15 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
             } else {
                 bad |= ngram_index(tok, i, hp, ib, it);
             }
-            keys[i] = ib & 0x7FFFFFFFu;
-            vals[i] = pos | (ib & 0x80000000u);
+            if (NESTED) {
+                bidx[pos] = ib;
+            } else {
+                keys[i] = ib & 0x7FFFFFFFu;
+                vals[i] = pos | (ib & 0x80000000u);
+                atomicAdd(&h[0][ib & (kRadix - 1)], 1u);
+            }
             keys[nk + i] = it & 0x7FFFFFFFu;
             vals[nk + i] = pos | (it & 0x80000000u);
-            atomicAdd(&h[0][ib & (kRadix - 1)], 1u);
             atomicAdd(&h[1][it & (kRadix - 1)], 1u);
         }
     }
@@ -97,18 +104,53 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
         atomicOr(&hdr->flags, NGRAM_FLAG_BAD_TOKEN);
     __syncthreads();
     for (int d = tid; d < kRadix; d += kSortThreads) {
-        hist[((size_t)0 * kRadix + d) * nblk + b] = h[0][d];
+        if (!NESTED)
+            hist[((size_t)0 * kRadix + d) * nblk + b] = h[0][d];
         hist[((size_t)1 * kRadix + d) * nblk + b] = h[1][d];
     }
+}
+
+// Nested sort: the bigram keys in the order of the sorted trigram keys (the
+// row code of each sorted trigram payload names its position's bigram
+// index), fused with the first bigram pass's digit counts.  A stable sort of
+// this sequence by bigram row gives the (bigram row, trigram row, position)
+// order.
+template <int ITEMS>
+__global__ __launch_bounds__(kSortThreads) void gather_bigram_kernel(
+    const uint32_t *__restrict__ vt, const uint32_t *__restrict__ bidx, const uint32_t *n_dev, uint32_t n_host,
+    uint32_t *__restrict__ keys0, uint32_t *__restrict__ vals0, uint32_t *__restrict__ hist, uint32_t nblk)
+{
+    __shared__ uint32_t h[kRadix];
+    const int tid = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t n = count_of(n_dev, n_host);
+    for (int d = tid; d < kRadix; d += kSortThreads)
+        h[d] = 0;
+    __syncthreads();
+    const uint32_t base = b * radix_tile(ITEMS);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t i = base + j * kSortThreads + tid;
+        if (i < n) {
+            const uint32_t code = vt[i] & 0x7FFFFFFFu;
+            const uint32_t ib = bidx[code];
+            keys0[i] = ib & 0x7FFFFFFFu;
+            vals0[i] = code | (ib & 0x80000000u);
+            atomicAdd(&h[ib & (kRadix - 1)], 1u);
+        }
+    }
+    __syncthreads();
+    for (int d = tid; d < kRadix; d += kSortThreads)
+        hist[(size_t)d * nblk + b] = h[d];
 }
 
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const uint32_t *__restrict__ keys, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
-    uint32_t *__restrict__ hist, uint32_t nblk)
+    uint32_t *__restrict__ hist, uint32_t nblk, int cbase)
 {
     __shared__ uint32_t h[kRadix];
-    const int c = blockIdx.y;
+    const int c = cbase + (int)blockIdx.y;
     const uint32_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const uint32_t n = count_of(n_dev, n_host);
@@ -131,10 +173,10 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
 // Block (d, c): exclusive scan of digit d's tile counts in place, total to
 // tot[c][d].  Each thread owns a contiguous run of tiles.
 __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__restrict__ hist, uint32_t nblk,
-                                                                   uint32_t *__restrict__ tot)
+                                                                   uint32_t *__restrict__ tot, int cbase)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
-    const int d = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+    const int d = blockIdx.x, c = cbase + (int)blockIdx.y, tid = threadIdx.x;
     uint32_t *row = hist + ((size_t)c * kRadix + d) * nblk;
     const uint32_t per = (nblk + kSortThreads - 1) / kSortThreads;
     const uint32_t lo = min(tid * per, nblk), hi = min(lo + per, nblk);
@@ -153,12 +195,14 @@ __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__r
 }
 
 // Stable scatter of one tile by the current digit.  Wave w owns the w-th
-// quarter of the tile's keys, processed 64 at a time in index order.
+// quarter of the tile's keys, processed 64 at a time in index order.  posb
+// (the nested sort's last bigram pass): each key's final index, by row code.
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
-    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk)
+    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk, int cbase,
+    uint32_t *__restrict__ posb)
 {
     constexpr int kPerWave = radix_tile(ITEMS) / (kSortThreads / kWave);
     __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
@@ -168,7 +212,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     __shared__ uint32_t s_v[radix_tile(ITEMS)];
     __shared__ uint32_t s_wave[kSortThreads / kWave];
 
-    const int c = blockIdx.y;
+    const int c = cbase + (int)blockIdx.y;
     const uint32_t b = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -269,8 +313,11 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
         const uint32_t k = s_k[p];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = s_glob[d] + (p - s_tile[d]);
+        const uint32_t v = s_v[p];
         ko[dst] = k;
-        vo[dst] = s_v[p];
+        vo[dst] = v;
+        if (posb)
+            posb[v & 0x7FFFFFFFu] = dst;
     }
 }
 
@@ -303,6 +350,9 @@ struct SlotArgs {
     uint32_t *split_rows;   // compacted trigram keys, payloads and head info
     uint32_t *split_vals;
     uint32_t *split_info;
+    bool nested;            // fused + nested sort: trigram rows nested in one bigram chunk
+    const uint32_t *posb;   // nested: index in the (bigram row, trigram row) order per row code
+    uint8_t *tkept;         // nested: per sorted trigram key, kept for the trigram pass
 };
 
 // Singleton split.  A trigram row that occurs at exactly one position of the
@@ -318,27 +368,81 @@ struct SlotArgs {
 //   kNotSingle otherwise.
 constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
 constexpr uint32_t kDropSingle = 0x3FFFFFFFu;   // slot field of all ones: never a slot
+// Nested trigram rows (fused reduction, nested sort).  The bigram keys are
+// sorted by (bigram row, trigram row, position).  Every position of a
+// trigram key has the same bigram key, so a trigram row whose positions all
+// have one bigram row lies in one bigram segment as one contiguous run; if
+// that run also lies inside one 64-key chunk of the bigram order (and the
+// row is new to the window), the one wavefront that walks it sums the run
+// from the dY rows it loads anyway and steps the row, and the trigram pass
+// skips its keys.  Its singleton-map record is row | neg << 31 | kMultiKey
+// (kMultiKey only when the run has more than one key).
+constexpr uint32_t kMultiKey = 0x40000000u;
+constexpr uint32_t kTrowMask = 0x3FFFFFFFu;
+
+// Inclusive running maximum over a block of NT threads; *excl (if given)
+// gets the maximum over the threads before this one (-1 for thread 0).
+template <int NT>
+__device__ __forceinline__ int block_incl_max(int v, int *s_wave, int *excl)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(v, d);
+        if (lane >= d)
+            v = max(v, o);
+    }
+    if (lane == kWave - 1)
+        s_wave[w] = v;
+    __syncthreads();
+    int before = -1;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i)
+        before = i < w ? max(before, s_wave[i]) : before;
+    __syncthreads();
+    const int prev_in_wave = __shfl_up(v, 1);
+    if (excl)
+        *excl = max(before, lane > 0 ? prev_in_wave : -1);
+    return max(before, v);
+}
 
 // Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
 // For the trigram channel it also counts, per tile, the keys the singleton
 // split keeps (split_kernel's layout).
+//
+// Nested sort, trigram channel: decides which trigram rows the bigram pass
+// completes.  A row qualifies if its keys lie in this tile of the trigram
+// order (its head here, its end here), it is new to the window, and all its
+// keys have the same bigram row and the same 64-key chunk of the bigram
+// order (compared key to key through posb and the sorted bigram keys).  Its
+// keys get their records in the singleton map and are dropped from the
+// trigram pass; every other key keeps kNotSingle and is kept.
 __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
+    __shared__ int s_iwave[kSortThreads / kWave];
+    __shared__ uint8_t s_fail[kSortTile];
     const int c = blockIdx.y;
     const uint32_t n = count_of(a.n_dev, a.n_host);
-    const uint32_t i0 = blockIdx.x * kSortTile + threadIdx.x * kSortItems;
+    const uint32_t tile0 = blockIdx.x * kSortTile;
+    const uint32_t i0 = tile0 + threadIdx.x * kSortItems;
     const uint32_t *R = a.rows + (size_t)c * a.nk;
+    const uint32_t *V = a.vals + (size_t)c * a.nk;
     const SlotEntry *sm = a.slot_map[c];
     uint32_t *info = a.seg_info + (size_t)c * a.nk;
     const uint32_t epoch = a.hdr->epoch;
     const bool empty = a.hdr->n_slots[c] == 0;   // the window holds no row yet: no lookups
+    const bool nest = a.nested && c == 1;
     uint32_t cnt = 0, kept = 0;
+    uint32_t headm = 0, knownm = 0, endm = 0;    // per item bits
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
         if (i < n) {
             const uint32_t r = R[i];
+            const bool end = i + 1 == n || R[i + 1] != r;
+            endm |= end ? 1u << j : 0u;
             bool single = false;
             if (i == 0 || R[i - 1] != r) {
                 bool known = false;
@@ -350,7 +454,9 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
                 }
                 info[i] = known ? slot : kNewHead;
                 cnt += known ? 0u : 1u;
-                single = (i + 1 == n || R[i + 1] != r) && !(a.fused && known);
+                single = end && !(a.fused && known);
+                headm |= 1u << j;
+                knownm |= known ? 1u << j : 0u;
             }
             kept += single ? 0u : 1u;
         }
@@ -359,6 +465,74 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
     block_excl_scan<kSortThreads>(cnt, s_wave, &total);
     if (threadIdx.x == 0)
         a.blk[(size_t)c * a.nblk + blockIdx.x] = total;
+    if (nest) {
+        // the tile-local head of each item's segment (-1: the segment began
+        // before this tile)
+        int last = -1;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            if (headm & (1u << j))
+                last = (int)(threadIdx.x * kSortItems + j);
+        int carry;
+        block_incl_max<kSortThreads>(last, s_iwave, &carry);
+        for (int j = threadIdx.x; j < kSortTile; j += kSortThreads)
+            s_fail[j] = 0;
+        __syncthreads();
+        // the (bigram row, trigram row) order index of every key of a segment
+        // with more than one key (and of the key before this thread's first
+        // item, if that item continues a segment), loaded together
+        uint32_t vq[kSortItems], pq[kSortItems];
+        uint32_t p_prev = 0;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t i = i0 + j;
+            vq[j] = i < n ? V[i] : 0u;
+            const bool multi = i < n && ((headm & endm) & (1u << j)) == 0;
+            pq[j] = multi ? a.posb[vq[j] & 0x7FFFFFFFu] : 0u;
+        }
+        if (i0 < n && !(headm & 1u) && carry >= 0)
+            p_prev = a.posb[V[i0 - 1] & 0x7FFFFFFFu];
+        int hl[kSortItems];
+        int run = carry;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t i = i0 + j;
+            if (headm & (1u << j))
+                run = (int)(threadIdx.x * kSortItems + j);
+            hl[j] = i < n ? run : -1;
+            if (i >= n || run < 0)
+                continue;
+            if (headm & (1u << j)) {
+                if (knownm & (1u << j))
+                    s_fail[run] = 1;   // the window already holds the row
+            } else {
+                // the same 64-key chunk of the bigram order as the key before,
+                // and the same bigram row (read from that chunk's sorted keys)
+                const uint32_t pa = j == 0 ? p_prev : pq[j - 1], pb = pq[j];
+                if ((pa >> 6) != (pb >> 6) || a.rows[pa] != a.rows[pb])
+                    s_fail[run] = 1;
+            }
+            if (j == kSortItems - 1 || i + 1 == n) {
+                // a segment running past the tile is not decided here
+                if (i + 1 < n && i + 1 == tile0 + kSortTile && R[i + 1] == R[i])
+                    s_fail[run] = 1;
+            }
+        }
+        __syncthreads();
+        kept = 0;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t i = i0 + j;
+            if (i >= n)
+                continue;
+            const bool nested = hl[j] >= 0 && !s_fail[hl[j]];
+            const uint32_t v = vq[j];
+            const bool single = (headm & (1u << j)) && (endm & (1u << j));
+            a.tinfo[v & 0x7FFFFFFFu] = nested ? (R[i] | (v & 0x80000000u) | (single ? 0u : kMultiKey)) : kNotSingle;
+            a.tkept[i] = nested ? 0 : 1;
+            kept += nested ? 0u : 1u;
+        }
+    }
     if (c == 1) {
         block_excl_scan<kSortThreads>(kept, s_wave, &total);
         if (threadIdx.x == 0)
@@ -406,20 +580,26 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
         if (i < n) {
-            const uint32_t r = R[i];
-            const uint32_t v = V[i];
-            uint32_t rec = kNotSingle;
-            if ((i == 0 || R[i - 1] != r) && (i + 1 == n || R[i + 1] != r)) {
-                const uint32_t in = info[i];
-                if (a.fused) {
-                    if (in == kNewHead)
-                        rec = r | (v & 0x80000000u);
-                } else {
-                    rec = in == kDropped ? kDropSingle : (in | ((v & 0x80000000u) >> 1));
+            bool kp;
+            if (a.nested) {
+                kp = a.tkept[i] != 0;   // the map records were written by mark_kernel
+            } else {
+                const uint32_t r = R[i];
+                const uint32_t v = V[i];
+                uint32_t rec = kNotSingle;
+                if ((i == 0 || R[i - 1] != r) && (i + 1 == n || R[i + 1] != r)) {
+                    const uint32_t in = info[i];
+                    if (a.fused) {
+                        if (in == kNewHead)
+                            rec = r | (v & 0x80000000u);
+                    } else {
+                        rec = in == kDropped ? kDropSingle : (in | ((v & 0x80000000u) >> 1));
+                    }
                 }
+                a.tinfo[v & 0x7FFFFFFFu] = rec;
+                kp = rec == kNotSingle;
             }
-            a.tinfo[v & 0x7FFFFFFFu] = rec;
-            if (rec == kNotSingle) {
+            if (kp) {
                 keep |= 1u << j;
                 ++cnt;
             }
@@ -528,6 +708,7 @@ struct RedArgs {
     int64_t ngroup;
     WsHeader *hdr;
     const uint32_t *tinfo;  // singleton map per dY row code
+    bool nested;            // the map also names nested trigram rows of several keys (kMultiKey)
     bool burst;             // the keys are the burst stash's: check the window is ready
     FuseArgs f;             // fused modes only
 };
@@ -955,9 +1136,16 @@ __device__ __forceinline__ float4 dy_quad_f32(uint2 x)
 // Three wavefronts per SIMD with two keys per batch (at most 168 VGPRs, no
 // spills) keep more loads in flight per CU than two wavefronts with four keys
 // per batch: 1.3 % faster with fp32 dY, 2-4 % with bf16 dY on the full table.
+// fp32 tables (wider row registers; small tables only) take two wavefronts
+// per SIMD, which leaves the compiler room without spilling.
+template <int ELT>
+constexpr int kStepWaves = ELT == 2 ? 3 : 2;
 template <int ELT, int DYE>
-__global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void seg_step_kernel(RedArgs a)
+__global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(kStepWaves<ELT>, kStepWaves<ELT>))) void seg_step_kernel(RedArgs a)
 {
+    // per wavefront: the running sum of the nested trigram run being walked
+    // (lane l holds elements 4l..4l+3 of each third, as in registers)
+    __shared__ float4 s_tacc[kRedThreads / kWave][kQ][kWave];
     const int c = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t chunk = (int64_t)blockIdx.x * (kRedThreads / kWave) + threadIdx.x / kWave;
@@ -1009,11 +1197,12 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
         WRow<ELT> w[kStepU], wt[kStepU];
         RowState st[kStepU], stt[kStepU];
         uint32_t row[kStepU], tv[kStepU];
-        bool ends_here[kStepU];
+        bool ends_here[kStepU], tlast[kStepU];
 #pragma unroll
         for (int u = 0; u < kStepU; ++u) {
             const int k = j + u;
             ends_here[u] = false;
+            tlast[u] = false;
             tv[u] = kNotSingle;
             if (k < p.jend) {
                 const uint32_t v = lane_val(p.v0, p.v1, k);
@@ -1031,9 +1220,19 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
                 if (tsplit) {
                     tv[u] = lane_val(t0, t1, k);
                     if (tv[u] != kNotSingle) {
-                        const uint32_t tr = tv[u] & 0x7FFFFFFFu;
-                        load_wrow<ELT>(wt[u], table_t + (uint64_t)tr * (kDim * ELT));
-                        stt[u] = ld_global_nt<RowState>(state_t + (uint64_t)tr * sizeof(RowState));
+                        // the key that completes its trigram row: a singleton, or
+                        // the last key of a nested run (the next key walked has
+                        // another record)
+                        tlast[u] = true;
+                        if (a.nested && (tv[u] & kMultiKey)) {
+                            const uint32_t nx = k + 1 < p.jend ? lane_val(t0, t1, k + 1) : kNotSingle;
+                            tlast[u] = nx == kNotSingle || ((nx ^ tv[u]) & kTrowMask) != 0;
+                        }
+                        if (tlast[u]) {
+                            const uint32_t tr = tv[u] & (a.nested ? kTrowMask : 0x7FFFFFFFu);
+                            load_wrow<ELT>(wt[u], table_t + (uint64_t)tr * (kDim * ELT));
+                            stt[u] = ld_global_nt<RowState>(state_t + (uint64_t)tr * sizeof(RowState));
+                        }
                     }
                 }
             }
@@ -1060,7 +1259,10 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
                 acc[q].z = fmaf(d.z, sgn, acc[q].z);
                 acc[q].w = fmaf(d.w, sgn, acc[q].w);
             }
-            if (tv[u] != kNotSingle) {   // the trigram singleton of this position: G = s_t dY
+            if (tv[u] != kNotSingle) {
+                // this position's trigram row is completed here: G = s_t dY for a
+                // singleton; a nested run adds s_t dY of its keys in order, the
+                // running sum kept in LDS between keys
                 const float ts = (tv[u] & 0x80000000u) ? -1.f : 1.f;
                 float4 g[kQ];
 #pragma unroll
@@ -1068,7 +1270,23 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(3, 
                     const float4 d = dy_quad_f32(x[u][q]);
                     g[q] = make_float4(ts * d.x, ts * d.y, ts * d.z, ts * d.w);
                 }
-                step_one<ELT>(g, wt[u], stt[u], tv[u] & 0x7FFFFFFFu, table_t, state_t, a, sp, sp_ok, lane);
+                const int wv = threadIdx.x / kWave;
+                if (a.nested && (tv[u] & kMultiKey)) {
+                    const uint32_t pv = k > p.j0 ? lane_val(t0, t1, k - 1) : kNotSingle;
+                    if (pv != kNotSingle && ((pv ^ tv[u]) & kTrowMask) == 0) {
+#pragma unroll
+                        for (int q = 0; q < kQ; ++q)
+                            g[q] = add4(s_tacc[wv][q][lane], g[q]);
+                    }
+                }
+                if (tlast[u]) {
+                    step_one<ELT>(g, wt[u], stt[u], tv[u] & (a.nested ? kTrowMask : 0x7FFFFFFFu), table_t, state_t,
+                                  a, sp, sp_ok, lane);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < kQ; ++q)
+                        s_tacc[wv][q][lane] = g[q];
+                }
             }
             if (ends_here[u]) {
                 const uint32_t info = (uint32_t)__builtin_amdgcn_readlane((int)p.i0, ps);
@@ -1352,7 +1570,36 @@ SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32
     sa.split_rows = spare_k + L.nk;
     sa.split_vals = spare_v + L.nk;
     sa.split_info = spare_k;
+    sa.nested = fused && L.nested;
+    sa.posb = reinterpret_cast<const uint32_t *>(ws + L.posb);
+    sa.tkept = reinterpret_cast<uint8_t *>(ws + L.tkept);
     return sa;
+}
+
+// The radix passes over the channels [cbase, cbase + nch) (the first pass's
+// digit counts already taken), from key buffer 0; posb, if set, gets each
+// key's final index (last pass).
+void radix_passes(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host, bool big, uint32_t nrb,
+                  int cbase, int nch, uint32_t *posb, hipStream_t s)
+{
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+    uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
+    int cur = 0;
+    for (int p = 0; p < L.passes; ++p) {
+        const int shift = p * kRadixBits;
+        uint32_t *kin = reinterpret_cast<uint32_t *>(ws + L.keys[cur]);
+        uint32_t *vin = reinterpret_cast<uint32_t *>(ws + L.vals[cur]);
+        uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
+        uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
+        if (p > 0)
+            (big ? radix_hist_kernel<kRadixItemsBig> : radix_hist_kernel<kRadixItemsSmall>)
+                <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nrb, cbase);
+        scan_digits_kernel<<<dim3(kRadix, nch), kSortThreads, 0, s>>>(hist, nrb, tot, cbase);
+        (big ? radix_scatter_kernel<kRadixItemsBig> : radix_scatter_kernel<kRadixItemsSmall>)
+            <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist, tot,
+                                                     nrb, cbase, p == L.passes - 1 ? posb : nullptr);
+        cur ^= 1;
+    }
 }
 
 // Keys, radix sort, segment heads, window slots (accumulating reduce only)
@@ -1364,36 +1611,41 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const bool burst = tok == nullptr;
     const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
+    const bool nested = fused && L.nested;
+    // (one channel per launch in the nested sort: 2,048-key tiles there were
+    // slower on the full window, 0.296 against 0.286 ms for the sort group)
     const bool big = n_host >= kRadixBigKeys;
     const uint32_t tile = radix_tile(big ? kRadixItemsBig : kRadixItemsSmall);
     const uint32_t nrb = (n_host + tile - 1) / tile;   // radix tiles
     const uint32_t nblk = (n_host + kSortTile - 1) / kSortTile;     // slot / split tiles
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
-    uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
     uint32_t *k0 = reinterpret_cast<uint32_t *>(ws + L.keys[0]);
     uint32_t *v0 = reinterpret_cast<uint32_t *>(ws + L.vals[0]);
 
-    launch_prof(NGRAM_PROF_SORT, true, false, burst ? (big ? keys_tile_kernel<true, kRadixItemsBig> : keys_tile_kernel<true, kRadixItemsSmall>)
-                      : (big ? keys_tile_kernel<false, kRadixItemsBig> : keys_tile_kernel<false, kRadixItemsSmall>),
-                dim3(nrb),
-                dim3(kSortThreads), 0, s, tok, burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) : nullptr,
+    uint32_t *bidx = reinterpret_cast<uint32_t *>(ws + L.bidx);
+    auto keys_k = nested ? (burst ? (big ? keys_tile_kernel<true, kRadixItemsBig, true>
+                                         : keys_tile_kernel<true, kRadixItemsSmall, true>)
+                                  : (big ? keys_tile_kernel<false, kRadixItemsBig, true>
+                                         : keys_tile_kernel<false, kRadixItemsSmall, true>))
+                         : (burst ? (big ? keys_tile_kernel<true, kRadixItemsBig, false>
+                                         : keys_tile_kernel<true, kRadixItemsSmall, false>)
+                                  : (big ? keys_tile_kernel<false, kRadixItemsBig, false>
+                                         : keys_tile_kernel<false, kRadixItemsSmall, false>));
+    launch_prof(NGRAM_PROF_SORT, true, false, keys_k, dim3(nrb), dim3(kSortThreads), 0, s, tok,
+                burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_idx) : nullptr,
                 burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
-                hist, nrb, hdr);
-    int cur = 0;
-    for (int p = 0; p < L.passes; ++p) {
-        const int shift = p * kRadixBits;
-        uint32_t *kin = reinterpret_cast<uint32_t *>(ws + L.keys[cur]);
-        uint32_t *vin = reinterpret_cast<uint32_t *>(ws + L.vals[cur]);
-        uint32_t *kout = reinterpret_cast<uint32_t *>(ws + L.keys[cur ^ 1]);
-        uint32_t *vout = reinterpret_cast<uint32_t *>(ws + L.vals[cur ^ 1]);
-        if (p > 0)
-            (big ? radix_hist_kernel<kRadixItemsBig> : radix_hist_kernel<kRadixItemsSmall>)
-                <<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nrb);
-        scan_digits_kernel<<<dim3(kRadix, L.nch), kSortThreads, 0, s>>>(hist, nrb, tot);
-        (big ? radix_scatter_kernel<kRadixItemsBig> : radix_scatter_kernel<kRadixItemsSmall>)
-            <<<dim3(nrb, L.nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist, tot,
-                                                       nrb);
-        cur ^= 1;
+                hist, nrb, hdr, bidx);
+    if (!nested) {
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, L.nch, nullptr, s);
+    } else {
+        // the trigram keys alone, then the bigram keys in trigram order (the
+        // same buffer 0 the trigram keys started from, their own half), then
+        // the bigram keys by row: (bigram row, trigram row, position)
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, nullptr, s);
+        const uint32_t *vt = reinterpret_cast<const uint32_t *>(ws + L.vals[L.passes & 1]) + L.nk;
+        (big ? gather_bigram_kernel<kRadixItemsBig> : gather_bigram_kernel<kRadixItemsSmall>)
+            <<<nrb, kSortThreads, 0, s>>>(vt, bidx, n_dev, n_host, k0, v0, hist, nrb);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, reinterpret_cast<uint32_t *>(ws + L.posb), s);
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
     // one table (token-indexed): no trigram channel, no singleton split
@@ -1430,6 +1682,7 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     ra.n_dev[1] = &hdr->n_multi;
     ra.n_host = n_host;
     ra.tinfo = L.nch == 2 ? sa.tinfo : nullptr;
+    ra.nested = sa.nested;
     ra.dY = burst && !L.by_ref ? ws + L.stash_dy : static_cast<const uint8_t *>(dY);
     ra.dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t *const *>(ws + L.dy_ptrs) : nullptr;
     ra.pos_bits = L.by_ref ? L.pos_bits : 31;

@@ -29,6 +29,8 @@ constexpr int kGroup = 64;
 constexpr int kFixThreads = 1024;
 constexpr uint32_t kNewHead = 0xFFFFFFFEu;
 constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
+constexpr uint32_t kMultiKey = 0x40000000u;
+constexpr uint32_t kTrowMask = 0x3FFFFFFFu;
 
 struct Ctx {
     // inputs
@@ -44,6 +46,7 @@ struct Ctx {
     int64_t wrows;          // window slots
     int64_t nchunk, ngroup; // extents of the partial rows / fix-up records, group sums
     int step_u;             // keys per batch
+    bool nested;            // the singleton map also names nested runs of several keys
     // results
     std::vector<int> walked;        // per key: wavefronts that walked it
     std::vector<int> completed;     // per key at a segment head: completions of the segment
@@ -212,10 +215,23 @@ void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
             if (tsplit) {
                 const uint32_t tv = lane_val(x, t0, t1, k, chunk);
                 if (tv != kNotSingle) {
-                    const uint32_t tr = tv & 0x7FFFFFFFu;
-                    in(x, "trigram singleton table row", tr, x.rows_t, chunk);
-                    if (in(x, "singleton step count", v & 0x7FFFFFFFu, x.code_cap, chunk))
-                        x.tstepped[v & 0x7FFFFFFFu] += 1;
+                    bool last = true;
+                    if (x.nested && (tv & kMultiKey)) {
+                        const uint32_t nx = k + 1 < p.jend ? lane_val(x, t0, t1, k + 1, chunk) : kNotSingle;
+                        last = nx == kNotSingle || ((nx ^ tv) & kTrowMask) != 0;
+                        const uint32_t pv = k > p.j0 ? lane_val(x, t0, t1, k - 1, chunk) : kNotSingle;
+                        const bool cont = pv != kNotSingle && ((pv ^ tv) & kTrowMask) == 0;
+                        // a run's keys are walked in one stretch: a key that continues
+                        // a run follows a key of the same run
+                        if (cont && !(pv & kMultiKey))
+                            bad(x, "nested run continuing a single key (key)", c0 + k, x.n, chunk);
+                    }
+                    if (last) {
+                        const uint32_t tr = tv & (x.nested ? kTrowMask : 0x7FFFFFFFu);
+                        in(x, "trigram table row (completed in the bigram pass)", tr, x.rows_t, chunk);
+                        if (in(x, "trigram step count", v & 0x7FFFFFFFu, x.code_cap, chunk))
+                            x.tstepped[v & 0x7FFFFFFFu] += 1;
+                    }
                 }
             }
             if (ends_here) {
@@ -325,9 +341,11 @@ extern "C" {
 int64_t model_channel(int64_t n, const uint32_t *R, const uint32_t *V, const uint32_t *I, int64_t nk,
                       const uint32_t *tinfo, int64_t code_cap, int pos_bits, int n_micro, const int64_t *Tm,
                       int64_t rows_c, int64_t rows_t, int64_t wrows, int64_t nchunk, int64_t ngroup, int step_u,
-                      int32_t *walked, int32_t *completed, int32_t *tstepped, int64_t *accesses, char *msg)
+                      int nested, int32_t *walked, int32_t *completed, int32_t *tstepped, int64_t *accesses,
+                      char *msg)
 {
     Ctx x;
+    x.nested = nested != 0;
     x.n = n; x.R = R; x.V = V; x.I = I; x.nk = nk; x.tinfo = tinfo; x.code_cap = code_cap;
     x.pos_bits = pos_bits; x.n_micro = n_micro; x.Tm = Tm; x.rows_c = rows_c; x.rows_t = rows_t;
     x.wrows = wrows; x.nchunk = nchunk; x.ngroup = ngroup; x.step_u = step_u;

@@ -44,7 +44,7 @@ def model(tmp_path_factory):
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.model_channel.restype = i64
     L.model_channel.argtypes = [i64, vp, vp, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp, i64, i64, i64,
-                                i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
+                                i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp]
     return L
 
 
@@ -59,7 +59,7 @@ def _sorted_keys(rows, neg, codes):
     return R, V
 
 
-def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, step_u=2):
+def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, step_u=2, nested=False):
     nchunk = (nk + 63) // 64
     ngroup = (nchunk + 63) // 64
     walked = np.zeros(max(n, 1), np.int32)
@@ -73,10 +73,10 @@ def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, s
     Rx, Vx, Ix = ext.copy(), ext.copy(), ext.copy()
     Rx[:n], Vx[:n], Ix[:n] = R, V, I
     viol = model.model_channel(n, _p(Rx), _p(Vx), _p(Ix), nk, _p(tinfo), code_cap, pos_bits, len(Tm), _p(Tm),
-                               rows_c, rows_t, wrows, nchunk, ngroup, step_u, _p(walked), _p(completed),
+                               rows_c, rows_t, wrows, nchunk, ngroup, step_u, int(nested), _p(walked), _p(completed),
                                _p(tstepped), ctypes.byref(acc), msg)
     assert viol == 0, msg.value.decode()
-    assert acc.value > 0
+    assert acc.value > 0 or n == 0
     return walked[:n], completed[:n], tstepped
 
 
@@ -86,8 +86,42 @@ def _heads(R):
     return h
 
 
+MULTI = 0x40000000
+TILE = 2048   # mark_kernel's tile of the trigram order
+
+
+def _nested_records(Rt, Vt, rb_of_code, posb_of_code, code_cap):
+    """mark_kernel's decision on an empty window: a trigram row is completed
+    by the bigram pass if its keys lie in one 2,048-key tile of the trigram
+    order and all have the same bigram row and 64-key chunk of the bigram
+    order.  Returns (singleton-map records per code, kept mask)."""
+    n = len(Rt)
+    idx = np.arange(n)
+    head = _heads(Rt)
+    end = np.ones(n, bool)
+    end[:-1] = Rt[1:] != Rt[:-1]
+    hidx = np.maximum.accumulate(np.where(head, idx, 0))
+    eidx = np.minimum.accumulate(np.where(end, idx, n)[::-1])[::-1]
+    seg = np.cumsum(head) - 1
+    code = (Vt & 0x7FFFFFFF).astype(np.int64)
+    bkey = rb_of_code[code].astype(np.int64) * (1 << 32) + (posb_of_code[code] >> 6)
+    mism = np.zeros(n, bool)
+    mism[1:] = (~head[1:]) & (bkey[1:] != bkey[:-1])
+    fail = np.zeros(int(seg[-1]) + 1 if n else 0, bool)
+    np.logical_or.at(fail, seg, mism)
+    nested = ((hidx // TILE) == (eidx // TILE)) & ~fail[seg]
+    single = head & end
+    rec = np.where(nested, Rt | (Vt & 0x80000000) | np.where(single, 0, MULTI), NOT_SINGLE).astype(np.uint32)
+    tinfo = np.full(code_cap, NOT_SINGLE, np.uint32)
+    tinfo[code] = rec
+    return tinfo, ~nested, nested, seg
+
+
 def _check_window(model, toks, rows, max_tokens, direct=False):
-    """Both channels of one burst-by-reference window, fused with the step."""
+    """Both channels of one burst-by-reference window, fused with the step:
+    the bigram keys in (bigram row, trigram row, position) order, the
+    trigram keys in (trigram row, position) order, nested trigram rows
+    completed by the bigram pass."""
     A = len(toks)
     pos_bits = max(0, int(max_tokens - 1).bit_length())
     code_cap = A << pos_bits
@@ -104,40 +138,53 @@ def _check_window(model, toks, rows, max_tokens, direct=False):
     codes = np.concatenate(codes)
     n = len(codes)
     Tm = [len(t) for t in toks]
-    Rb, Vb = _sorted_keys(np.concatenate(rb), np.concatenate(nb), codes)
+    rb, nb = np.concatenate(rb), np.concatenate(nb)
+    if direct:
+        Rb, Vb = _sorted_keys(rb, nb, codes)
+        Ib = np.where(_heads(Rb), NEW_HEAD, 0).astype(np.uint32)
+        walked, completed, _ = _run(model, n, Rb, Vb, Ib, nk, None, code_cap, pos_bits, Tm, rows[0], 1)
+        assert (walked == 1).all()
+        np.testing.assert_array_equal(completed, _heads(Rb).astype(np.int32))
+        return
+    rt, nt = np.concatenate(rt), np.concatenate(nt)
+    ot = np.argsort(rt, kind="stable")                    # trigram order
+    obt = ot[np.argsort(rb[ot], kind="stable")]           # (bigram row, trigram row, position)
+    Rb = rb[obt].astype(np.uint32)
+    Vb = (codes[obt] | (nb[obt].astype(np.uint64) << 31)).astype(np.uint32)
     Ib = np.where(_heads(Rb), NEW_HEAD, 0).astype(np.uint32)
-    tinfo = None
-    if not direct:
-        Rt, Vt = _sorted_keys(np.concatenate(rt), np.concatenate(nt), codes)
-        h = _heads(Rt)
-        ends = np.ones(n, bool)
-        ends[:-1] = Rt[1:] != Rt[:-1]
-        single = h & ends
-        tinfo = np.full(code_cap, NOT_SINGLE, np.uint32)
-        tinfo[Vt & 0x7FFFFFFF] = np.where(single, Rt | (Vt & 0x80000000), NOT_SINGLE).astype(np.uint32)
+    Rt = rt[ot].astype(np.uint32)
+    Vt = (codes[ot] | (nt[ot].astype(np.uint64) << 31)).astype(np.uint32)
+    rb_of_code = np.zeros(code_cap, np.int64)
+    rb_of_code[codes.astype(np.int64)] = rb
+    posb_of_code = np.zeros(code_cap, np.int64)
+    posb_of_code[codes[obt].astype(np.int64)] = np.arange(n)
+    tinfo, kept, nested, tseg = _nested_records(Rt, Vt, rb_of_code, posb_of_code, code_cap)
     walked, completed, tstepped = _run(model, n, Rb, Vb, Ib, nk, tinfo, code_cap, pos_bits, Tm, rows[0],
-                                       rows[1] if not direct else 1)
+                                       rows[1], nested=True)
     assert (walked == 1).all(), np.flatnonzero(walked != 1)[:10]
     np.testing.assert_array_equal(completed, _heads(Rb).astype(np.int32))
-    if direct:
-        return
-    # trigram singletons: stepped once each by the bigram pass, never walked again
-    sc = (Vt & 0x7FFFFFFF)[single]
-    assert (tstepped[sc] == 1).all() and int(tstepped.sum()) == int(single.sum())
-    # the split keeps the other trigram keys, in order, with their head info
-    keep = ~single
-    Rs, Vs = Rt[keep], Vt[keep]
-    Is = np.where(h[keep], NEW_HEAD, 0).astype(np.uint32)
+    # every nested trigram row is stepped exactly once by the bigram pass
+    # (at one of its keys), no other row is
+    per_row = np.bincount(tseg, weights=tstepped[(Vt & 0x7FFFFFFF).astype(np.int64)])
+    nested_seg = np.zeros(len(per_row), bool)
+    nested_seg[tseg[nested]] = True
+    np.testing.assert_array_equal(per_row, nested_seg.astype(float))
+    # the trigram pass walks the kept keys, in order, with their head info
+    h = _heads(Rt)
+    Rs, Vs = Rt[kept], Vt[kept]
+    Is = np.where(h[kept], NEW_HEAD, 0).astype(np.uint32)
     w2, c2, _ = _run(model, len(Rs), Rs, Vs, Is, nk, None, code_cap, pos_bits, Tm, rows[1], rows[1])
     assert (w2 == 1).all()
     np.testing.assert_array_equal(c2, _heads(Rs).astype(np.int32))
     # every trigram row completed exactly once over both passes
-    assert int(c2.sum()) + int(single.sum()) == int(h.sum())
+    assert int(c2.sum()) + int(nested_seg.sum()) == int(h.sum())
+    return int(kept.sum())
 
 
 def test_full_window(model):
     w = workloads.FULL
-    _check_window(model, [synth.tokens(w, m) for m in range(4)], w.rows, w.tokens_per_step)
+    kept = _check_window(model, [synth.tokens(w, m) for m in range(4)], w.rows, w.tokens_per_step)
+    assert kept < 200_000   # of 1,572,864 trigram keys, about 183K are left to the trigram pass
 
 
 def test_collision_window(model):
@@ -174,3 +221,16 @@ def test_the_model_reports_an_index_past_its_buffer(model):
     I = np.where(_heads(R), NEW_HEAD, 0).astype(np.uint32)
     with pytest.raises(AssertionError, match="dY position"):
         _run(model, 300, R, V, I, 300, None, 512, 9, [299], 4096, 4096)
+
+
+def test_the_model_reports_a_split_run(model):
+    # the model itself: a nested run whose keys are not adjacent in the walk
+    # (a single key of the same row in between) must be reported
+    R = np.array([5, 5, 5, 5], np.uint32)
+    V = np.arange(4, dtype=np.uint32)
+    I = np.array([NEW_HEAD, 0, 0, 0], np.uint32)
+    tinfo = np.full(8, NOT_SINGLE, np.uint32)
+    tinfo[[0, 2]] = 9 | MULTI
+    tinfo[1] = 9
+    with pytest.raises(AssertionError, match="nested run"):
+        _run(model, 4, R, V, I, 4, tinfo, 8, 3, [4], 16, 16, nested=True)
