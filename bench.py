@@ -110,17 +110,13 @@ def nested_keys(torch, rb, rt, known=None):
     """Trigram keys the fused reduction's bigram pass completes (so the
     trigram pass does not read their dY rows again): keys of trigram rows new
     to the window (not in `known`) whose keys lie in one 2,048-key tile of the
-    trigram order and share one bigram row and one 64-key chunk of the
-    (bigram row, trigram row, position) order.  rb, rt: the rows of the
+    trigram order and share one bigram row.  rb, rt: the rows of the
     positions, in stream order."""
     n = rb.numel()
     if n == 0:
         return 0
     idx = torch.arange(n, device=rb.device)
     ot = torch.sort(rt, stable=True).indices
-    obt = ot[torch.sort(rb[ot], stable=True).indices]
-    posb = torch.empty_like(obt)
-    posb[obt] = idx
     Rt = rt[ot]
     head = torch.ones(n, dtype=torch.bool, device=rb.device)
     head[1:] = Rt[1:] != Rt[:-1]
@@ -129,7 +125,7 @@ def nested_keys(torch, rb, rt, known=None):
     hidx = torch.cummax(torch.where(head, idx, torch.zeros_like(idx)), 0).values
     eidx = torch.flip(torch.cummin(torch.flip(torch.where(end, idx, torch.full_like(idx, n)), [0]), 0).values, [0])
     seg = torch.cumsum(head.long(), 0) - 1
-    bkey = rb[ot] * (1 << 32) + (posb[ot] >> 6)
+    bkey = rb[ot]
     bad = torch.zeros(n, dtype=torch.bool, device=rb.device)
     bad[1:] = (~head[1:]) & (bkey[1:] != bkey[:-1])
     if known is not None:

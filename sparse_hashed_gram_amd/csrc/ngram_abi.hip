@@ -144,11 +144,14 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
     L.code_cap = L.by_ref ? ((int64_t)L.accum << L.pos_bits) : L.nk;
     L.tinfo = o;
     o = up(o + 4ull * (uint64_t)L.code_cap);
-    L.nested = L.nch == 2 && c->rows[1] < (int64_t(1) << 30);
+    // nested trigram records keep four flag bits above the row
+    L.nested = L.nch == 2 && c->rows[1] <= (int64_t(1) << 28);
     L.bidx = o;
     o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
-    L.posb = o;
-    o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
+    L.tpart = o;
+    o = up(o + (L.nested ? 4ull * (uint64_t)L.nchunk * 2 * kDim : 0));
+    L.trec = o;
+    o = up(o + (L.nested ? 8ull * (uint64_t)L.nchunk : 0));
     L.tkept = o;
     o = up(o + (L.nested ? (uint64_t)L.nk : 0));
     if (L.burst) {

@@ -249,7 +249,8 @@ struct WsHeader {
     uint32_t n_keyed;      // burst modes: micro-steps whose keys are kept (>= n_micro)
     uint32_t sorted_n;     // burst modes: n_stash when the keys were last sorted
     uint32_t dropped;      // the window was found unready: its step changes no row
-    uint32_t pad[49];
+    uint32_t n_trun;       // fused reduction: nested trigram runs left to the fix-up
+    uint32_t pad[48];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
@@ -325,8 +326,11 @@ struct WsLayout {
                             // singleton split and the nested trigram rows), else kNotSingle
     uint64_t bidx;          // uint32 [code_cap]: per dY row code, its packed bigram index
                             // (nested sort: the bigram keys are gathered in trigram order)
-    uint64_t posb;          // uint32 [code_cap]: per dY row code, its index in the
-                            // (bigram row, trigram row, position) order (nested sort)
+    uint64_t tpart;         // fp32 [nchunk][2][768] (nested sort): pieces of nested trigram
+                            // runs that cross the end of a chunk's walk (slot 0: the piece
+                            // at the walk's start, slot 1: the piece at its end)
+    uint64_t trec;          // uint64 [nchunk] (nested sort): chunk | record << 32 of each run
+                            // whose first piece is in slot 1 of that chunk
     uint64_t tkept;         // uint8 [nk]: per trigram-sorted key, kept for the trigram pass
     uint64_t stash_idx;     // uint32 [2][nk] (burst): packed indices of kept positions
     uint64_t stash_pos;     // uint32 [nk] (burst): dY row code of each kept position

@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
     if (b == 0 && tid == 0) {
         hdr->n_owner[0] = 0;
         hdr->n_owner[1] = 0;
+        hdr->n_trun = 0;
     }
     for (int d = tid; d < kRadix; d += kSortThreads) {
         h[0][d] = 0;
@@ -195,14 +196,12 @@ __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__r
 }
 
 // Stable scatter of one tile by the current digit.  Wave w owns the w-th
-// quarter of the tile's keys, processed 64 at a time in index order.  posb
-// (the nested sort's last bigram pass): each key's final index, by row code.
+// quarter of the tile's keys, processed 64 at a time in index order.
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
-    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk, int cbase,
-    uint32_t *__restrict__ posb)
+    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk, int cbase)
 {
     constexpr int kPerWave = radix_tile(ITEMS) / (kSortThreads / kWave);
     __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
@@ -316,8 +315,6 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
         const uint32_t v = s_v[p];
         ko[dst] = k;
         vo[dst] = v;
-        if (posb)
-            posb[v & 0x7FFFFFFFu] = dst;
     }
 }
 
@@ -350,8 +347,8 @@ struct SlotArgs {
     uint32_t *split_rows;   // compacted trigram keys, payloads and head info
     uint32_t *split_vals;
     uint32_t *split_info;
-    bool nested;            // fused + nested sort: trigram rows nested in one bigram chunk
-    const uint32_t *posb;   // nested: index in the (bigram row, trigram row) order per row code
+    bool nested;            // fused + nested sort: trigram rows nested in one bigram segment
+    const uint32_t *bidx;   // nested: packed bigram index per row code
     uint8_t *tkept;         // nested: per sorted trigram key, kept for the trigram pass
 };
 
@@ -371,14 +368,20 @@ constexpr uint32_t kDropSingle = 0x3FFFFFFFu;   // slot field of all ones: never
 // Nested trigram rows (fused reduction, nested sort).  The bigram keys are
 // sorted by (bigram row, trigram row, position).  Every position of a
 // trigram key has the same bigram key, so a trigram row whose positions all
-// have one bigram row lies in one bigram segment as one contiguous run; if
-// that run also lies inside one 64-key chunk of the bigram order (and the
-// row is new to the window), the one wavefront that walks it sums the run
-// from the dY rows it loads anyway and steps the row, and the trigram pass
-// skips its keys.  Its singleton-map record is row | neg << 31 | kMultiKey
-// (kMultiKey only when the run has more than one key).
+// have one bigram row lies in one bigram segment as one contiguous run.  If
+// the row is new to the window, the bigram pass sums the run from the dY
+// rows it loads anyway and the trigram pass skips its keys: a run inside
+// one wavefront's walk is summed and stepped there; a run that crosses the
+// end of a walk (inside a bigram segment of many chunks) leaves one piece
+// per walk in tpart, and the fix-up adds the pieces in order and steps the
+// row.  The record is row | neg << 31, plus, for a run of several keys,
+// kMultiKey, and kRunHead / kRunTail on its first / last key.
 constexpr uint32_t kMultiKey = 0x40000000u;
-constexpr uint32_t kTrowMask = 0x3FFFFFFFu;
+constexpr uint32_t kRunHead = 0x20000000u;
+constexpr uint32_t kRunTail = 0x10000000u;
+constexpr uint32_t kTrowMask = 0x0FFFFFFFu;
+
+__device__ __forceinline__ bool is_run(uint32_t rec) { return rec != kNotSingle && (rec & kMultiKey) != 0u; }
 
 // Inclusive running maximum over a block of NT threads; *excl (if given)
 // gets the maximum over the threads before this one (-1 for thread 0).
@@ -414,10 +417,11 @@ __device__ __forceinline__ int block_incl_max(int v, int *s_wave, int *excl)
 // Nested sort, trigram channel: decides which trigram rows the bigram pass
 // completes.  A row qualifies if its keys lie in this tile of the trigram
 // order (its head here, its end here), it is new to the window, and all its
-// keys have the same bigram row and the same 64-key chunk of the bigram
-// order (compared key to key through posb and the sorted bigram keys).  Its
+// keys have the same bigram row (compared key to key through bidx).  Its
 // keys get their records in the singleton map and are dropped from the
-// trigram pass; every other key keeps kNotSingle and is kept.
+// trigram pass; every other key keeps kNotSingle and is kept.  The trigram
+// order lists a row's keys by position, as the bigram order lists the run,
+// so the segment's head and end are the run's first and last key.
 __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
 {
     __shared__ uint32_t s_wave[kSortThreads / kWave];
@@ -478,20 +482,20 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
         for (int j = threadIdx.x; j < kSortTile; j += kSortThreads)
             s_fail[j] = 0;
         __syncthreads();
-        // the (bigram row, trigram row) order index of every key of a segment
-        // with more than one key (and of the key before this thread's first
-        // item, if that item continues a segment), loaded together
-        uint32_t vq[kSortItems], pq[kSortItems];
-        uint32_t p_prev = 0;
+        // the bigram row of every key of a segment with more than one key
+        // (and of the key before this thread's first item, if that item
+        // continues a segment), loaded together
+        uint32_t vq[kSortItems], bq[kSortItems];
+        uint32_t b_prev = 0;
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t i = i0 + j;
             vq[j] = i < n ? V[i] : 0u;
             const bool multi = i < n && ((headm & endm) & (1u << j)) == 0;
-            pq[j] = multi ? a.posb[vq[j] & 0x7FFFFFFFu] : 0u;
+            bq[j] = multi ? a.bidx[vq[j] & 0x7FFFFFFFu] & 0x7FFFFFFFu : 0u;
         }
         if (i0 < n && !(headm & 1u) && carry >= 0)
-            p_prev = a.posb[V[i0 - 1] & 0x7FFFFFFFu];
+            b_prev = a.bidx[V[i0 - 1] & 0x7FFFFFFFu] & 0x7FFFFFFFu;
         int hl[kSortItems];
         int run = carry;
 #pragma unroll
@@ -505,12 +509,8 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
             if (headm & (1u << j)) {
                 if (knownm & (1u << j))
                     s_fail[run] = 1;   // the window already holds the row
-            } else {
-                // the same 64-key chunk of the bigram order as the key before,
-                // and the same bigram row (read from that chunk's sorted keys)
-                const uint32_t pa = j == 0 ? p_prev : pq[j - 1], pb = pq[j];
-                if ((pa >> 6) != (pb >> 6) || a.rows[pa] != a.rows[pb])
-                    s_fail[run] = 1;
+            } else if ((j == 0 ? b_prev : bq[j - 1]) != bq[j]) {
+                s_fail[run] = 1;   // another bigram row than the key before
             }
             if (j == kSortItems - 1 || i + 1 == n) {
                 // a segment running past the tile is not decided here
@@ -527,8 +527,9 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
                 continue;
             const bool nested = hl[j] >= 0 && !s_fail[hl[j]];
             const uint32_t v = vq[j];
-            const bool single = (headm & (1u << j)) && (endm & (1u << j));
-            a.tinfo[v & 0x7FFFFFFFu] = nested ? (R[i] | (v & 0x80000000u) | (single ? 0u : kMultiKey)) : kNotSingle;
+            const bool hd = (headm & (1u << j)) != 0, ed = (endm & (1u << j)) != 0;
+            const uint32_t run_bits = (hd && ed) ? 0u : (kMultiKey | (hd ? kRunHead : 0u) | (ed ? kRunTail : 0u));
+            a.tinfo[v & 0x7FFFFFFFu] = nested ? (R[i] | (v & 0x80000000u) | run_bits) : kNotSingle;
             a.tkept[i] = nested ? 0 : 1;
             kept += nested ? 0u : 1u;
         }
@@ -709,6 +710,8 @@ struct RedArgs {
     WsHeader *hdr;
     const uint32_t *tinfo;  // singleton map per dY row code
     bool nested;            // the map also names nested trigram rows of several keys (kMultiKey)
+    float *tpart;           // nested: [nchunk][2][768] pieces of runs that cross a walk's end
+    uint64_t *trec;         // nested: [nchunk] such runs, chunk of the first piece | record << 32
     bool burst;             // the keys are the burst stash's: check the window is ready
     FuseArgs f;             // fused modes only
 };
@@ -1163,6 +1166,16 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(kSt
         if (p.owner_full && kChunk + lane < p.jend)
             t1 = a.tinfo[p.v1 & 0x7FFFFFFFu];
     }
+    // nested runs: keys j0 .. kc_end continue a run from the walk before
+    // (the walk's first piece of that run, completed by the fix-up)
+    int kc_end = -1;
+    if (tsplit && a.nested && p.j0 < p.jend) {
+        const uint32_t tj = (uint32_t)__builtin_amdgcn_readlane((int)t0, p.j0);
+        if (is_run(tj) && !(tj & kRunHead)) {
+            const uint64_t tails = __ballot(is_run(t0) && (t0 & kRunTail)) & (~0ull << p.j0);
+            kc_end = tails ? (int)__builtin_ctzll(tails) : p.nv - 1;
+        }
+    }
     uint64_t lane_base = dy_lane_base(a, lane);
     settle_plan(p);
     settle(lane_base);
@@ -1221,13 +1234,8 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(kSt
                     tv[u] = lane_val(t0, t1, k);
                     if (tv[u] != kNotSingle) {
                         // the key that completes its trigram row: a singleton, or
-                        // the last key of a nested run (the next key walked has
-                        // another record)
-                        tlast[u] = true;
-                        if (a.nested && (tv[u] & kMultiKey)) {
-                            const uint32_t nx = k + 1 < p.jend ? lane_val(t0, t1, k + 1) : kNotSingle;
-                            tlast[u] = nx == kNotSingle || ((nx ^ tv[u]) & kTrowMask) != 0;
-                        }
+                        // the last key of a nested run that began in this walk
+                        tlast[u] = !(a.nested && (tv[u] & kMultiKey)) || (k > kc_end && (tv[u] & kRunTail));
                         if (tlast[u]) {
                             const uint32_t tr = tv[u] & (a.nested ? kTrowMask : 0x7FFFFFFFu);
                             load_wrow<ELT>(wt[u], table_t + (uint64_t)tr * (kDim * ELT));
@@ -1271,17 +1279,27 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(kSt
                     g[q] = make_float4(ts * d.x, ts * d.y, ts * d.z, ts * d.w);
                 }
                 const int wv = threadIdx.x / kWave;
-                if (a.nested && (tv[u] & kMultiKey)) {
-                    const uint32_t pv = k > p.j0 ? lane_val(t0, t1, k - 1) : kNotSingle;
-                    if (pv != kNotSingle && ((pv ^ tv[u]) & kTrowMask) == 0) {
+                const bool run = a.nested && (tv[u] & kMultiKey);
+                if (run && k != p.j0 && !(tv[u] & kRunHead)) {   // the key before is of the same run
 #pragma unroll
-                        for (int q = 0; q < kQ; ++q)
-                            g[q] = add4(s_tacc[wv][q][lane], g[q]);
-                    }
+                    for (int q = 0; q < kQ; ++q)
+                        g[q] = add4(s_tacc[wv][q][lane], g[q]);
                 }
                 if (tlast[u]) {
                     step_one<ELT>(g, wt[u], stt[u], tv[u] & (a.nested ? kTrowMask : 0x7FFFFFFFu), table_t, state_t,
                                   a, sp, sp_ok, lane);
+                } else if (run && (k == kc_end || k == p.jend - 1)) {
+                    // a piece of a run that crosses the walk's start (slot 0) or
+                    // end (slot 1); the fix-up adds the pieces and steps the row
+                    const int slot = k <= kc_end ? 0 : 1;
+                    const uint64_t dst = (uint64_t)a.tpart + ((uint64_t)chunk * 2 + slot) * (kDim * 4) + 16 * lane;
+#pragma unroll
+                    for (int q = 0; q < kQ; ++q)
+                        st_global<float4>(dst + q * (kWave * 16), g[q]);
+                    if (slot == 1 && lane == 0) {
+                        const uint32_t k2 = atomicAdd(&a.hdr->n_trun, 1u);
+                        a.trec[k2] = (uint64_t)chunk | ((uint64_t)tv[u] << 32);
+                    }
                 } else {
 #pragma unroll
                     for (int q = 0; q < kQ; ++q)
@@ -1534,6 +1552,71 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
         }
         __syncthreads();
     }
+    if constexpr (MODE != kAccum) {
+        // Nested trigram runs that crossed the end of a walk, one per
+        // wavefront: the piece in slot 1 of the run's first chunk, then slot
+        // 0 of each following chunk whose first key continues the run, added
+        // in order; then the row's step.
+        if (c == 1 && a.nested) {
+            constexpr int ELT = MODE == kFuseBf16 ? 2 : 4;
+            const uint32_t ntr = a.hdr->n_trun;
+            const int64_t n0 = count_of(a.n_dev[0], a.n_host);
+            const uint32_t *V0 = a.vals[0];
+            const uint64_t table_t = (uint64_t)a.f.w[1] + (uint64_t)ELT * 4 * lane;
+            const uint64_t state_t = (uint64_t)a.f.st[1];
+            const uint64_t P = (uint64_t)a.tpart + 16 * lane;
+            for (uint32_t r = blockIdx.x * kW + w; r < ntr; r += gridDim.x * kW) {
+                const uint64_t rec = a.trec[r];
+                const int64_t x = (int64_t)(uint32_t)rec;
+                const uint32_t tv = (uint32_t)(rec >> 32);
+                const uint32_t row = tv & kTrowMask;
+                WRow<ELT> wr;
+                load_wrow<ELT>(wr, table_t + (uint64_t)row * (kDim * ELT));
+                const RowState rst = ld_global_nt<RowState>(state_t + (uint64_t)row * sizeof(RowState));
+                // m = the following chunks whose first key continues the run
+                // (consecutive: the run's keys are contiguous), 64 probed at a time
+                int64_t m = 0;
+                for (;;) {
+                    const int64_t cc = x + 1 + m + lane;
+                    bool hit = false;
+                    if (cc * kChunk < n0) {
+                        const uint32_t t = a.tinfo[V0[cc * kChunk] & 0x7FFFFFFFu];
+                        hit = is_run(t) && !(t & kRunHead) && ((t ^ tv) & kTrowMask) == 0;
+                    }
+                    const uint64_t miss = ~__ballot(hit);
+                    const int lead = miss ? (int)__builtin_ctzll(miss) : kWave;
+                    m += lead;
+                    if (lead < kWave)
+                        break;
+                }
+                float4 g[kQ];
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    g[q] = ld_global<float4>(P + ((uint64_t)x * 2 + 1) * (kDim * 4) + q * (kWave * 16));
+                for (int64_t i = 1; i <= m; i += kRedU) {
+                    float4 y[kRedU][kQ];
+#pragma unroll
+                    for (int u = 0; u < kRedU; ++u) {
+                        if (i + u <= m) {
+#pragma unroll
+                            for (int q = 0; q < kQ; ++q)
+                                y[u][q] = ld_global<float4>(P + (uint64_t)(x + i + u) * 2 * (kDim * 4) +
+                                                            q * (kWave * 16));
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < kRedU; ++u) {
+                        if (i + u <= m) {
+#pragma unroll
+                            for (int q = 0; q < kQ; ++q)
+                                g[q] = add4(g[q], y[u][q]);
+                        }
+                    }
+                }
+                step_one<ELT>(g, wr, rst, row, table_t, state_t, a, sp, sp_ok, lane);
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -1571,16 +1654,15 @@ SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32
     sa.split_vals = spare_v + L.nk;
     sa.split_info = spare_k;
     sa.nested = fused && L.nested;
-    sa.posb = reinterpret_cast<const uint32_t *>(ws + L.posb);
+    sa.bidx = reinterpret_cast<const uint32_t *>(ws + L.bidx);
     sa.tkept = reinterpret_cast<uint8_t *>(ws + L.tkept);
     return sa;
 }
 
 // The radix passes over the channels [cbase, cbase + nch) (the first pass's
-// digit counts already taken), from key buffer 0; posb, if set, gets each
-// key's final index (last pass).
+// digit counts already taken), from key buffer 0.
 void radix_passes(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host, bool big, uint32_t nrb,
-                  int cbase, int nch, uint32_t *posb, hipStream_t s)
+                  int cbase, int nch, hipStream_t s)
 {
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
@@ -1597,7 +1679,7 @@ void radix_passes(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_
         scan_digits_kernel<<<dim3(kRadix, nch), kSortThreads, 0, s>>>(hist, nrb, tot, cbase);
         (big ? radix_scatter_kernel<kRadixItemsBig> : radix_scatter_kernel<kRadixItemsSmall>)
             <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist, tot,
-                                                     nrb, cbase, p == L.passes - 1 ? posb : nullptr);
+                                                     nrb, cbase);
         cur ^= 1;
     }
 }
@@ -1636,16 +1718,16 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
                 burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
                 hist, nrb, hdr, bidx);
     if (!nested) {
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, L.nch, nullptr, s);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, L.nch, s);
     } else {
         // the trigram keys alone, then the bigram keys in trigram order (the
         // same buffer 0 the trigram keys started from, their own half), then
         // the bigram keys by row: (bigram row, trigram row, position)
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, nullptr, s);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, s);
         const uint32_t *vt = reinterpret_cast<const uint32_t *>(ws + L.vals[L.passes & 1]) + L.nk;
         (big ? gather_bigram_kernel<kRadixItemsBig> : gather_bigram_kernel<kRadixItemsSmall>)
             <<<nrb, kSortThreads, 0, s>>>(vt, bidx, n_dev, n_host, k0, v0, hist, nrb);
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, reinterpret_cast<uint32_t *>(ws + L.posb), s);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, s);
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
     // one table (token-indexed): no trigram channel, no singleton split
@@ -1683,6 +1765,8 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     ra.n_host = n_host;
     ra.tinfo = L.nch == 2 ? sa.tinfo : nullptr;
     ra.nested = sa.nested;
+    ra.tpart = reinterpret_cast<float *>(ws + L.tpart);
+    ra.trec = reinterpret_cast<uint64_t *>(ws + L.trec);
     ra.dY = burst && !L.by_ref ? ws + L.stash_dy : static_cast<const uint8_t *>(dY);
     ra.dy_ptrs = L.by_ref ? reinterpret_cast<const uint8_t *const *>(ws + L.dy_ptrs) : nullptr;
     ra.pos_bits = L.by_ref ? L.pos_bits : 31;

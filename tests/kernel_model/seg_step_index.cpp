@@ -7,12 +7,14 @@
 // lane shuffles as loops.  Every address the kernel forms -- sorted keys,
 // payloads and head info, the singleton map, dY rows (micro-step base +
 // position), table rows and row state of both channels, window rows and
-// slot rows, partial rows, fix-up records, group sums -- is checked against
-// the extent of its buffer before it would be used.  The model also checks
-// what the indexing is for: every key is walked by exactly one wavefront,
-// every segment is completed exactly once (in its chunk, by the owner of a
-// one-chunk spill-over, or by the fix-up), every partial row and group sum
-// the fix-up reads was written, and every trigram singleton is stepped once.
+// slot rows, partial rows, fix-up records, group sums, nested trigram run
+// pieces and their records -- is checked against the extent of its buffer
+// before it would be used.  The model also checks what the indexing is for:
+// every key is walked by exactly one wavefront, every segment is completed
+// exactly once (in its chunk, by the owner of a one-chunk spill-over, or by
+// the fix-up), every partial row, group sum and run piece the fix-up reads
+// was written, every trigram row the bigram pass completes is stepped once,
+// and every key of such a row is in exactly one completed sum.
 //
 // Build: g++ -O2 -std=c++17 -shared -fPIC seg_step_index.cpp (the test does).
 #include <stdint.h>
@@ -30,7 +32,11 @@ constexpr int kFixThreads = 1024;
 constexpr uint32_t kNewHead = 0xFFFFFFFEu;
 constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
 constexpr uint32_t kMultiKey = 0x40000000u;
-constexpr uint32_t kTrowMask = 0x3FFFFFFFu;
+constexpr uint32_t kRunHead = 0x20000000u;
+constexpr uint32_t kRunTail = 0x10000000u;
+constexpr uint32_t kTrowMask = 0x0FFFFFFFu;
+
+bool is_run(uint32_t t) { return t != kNotSingle && (t & kMultiKey) != 0; }
 
 struct Ctx {
     // inputs
@@ -50,9 +56,13 @@ struct Ctx {
     // results
     std::vector<int> walked;        // per key: wavefronts that walked it
     std::vector<int> completed;     // per key at a segment head: completions of the segment
-    std::vector<int> tstepped;      // per dY row code: trigram singleton steps
+    std::vector<int> tstepped;      // per dY row code: trigram rows stepped at this key
+    std::vector<int> tsum;          // per dY row code: completed trigram sums holding this key
     std::vector<int> partial_w;     // [nchunk][2]: partial rows written
     std::vector<uint64_t> owners;   // fix-up records
+    std::vector<int> tpart_w;       // [nchunk][2]: nested run pieces written
+    std::vector<int64_t> tpart_lo, tpart_hi;   // [nchunk][2]: the piece's first and last key
+    std::vector<uint64_t> trec;     // nested run records
     int64_t violations = 0;
     char first[256] = {0};
     int64_t accesses = 0;
@@ -198,6 +208,22 @@ void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
     }
     if (p.last_spills)
         fin &= ~(1ull << 63);
+    // nested runs: keys j0 .. kc_end continue a run from the walk before
+    int kc_end = -1;
+    if (tsplit && x.nested && p.j0 < p.jend) {
+        uint32_t tj = 0;
+        if (in(x, "readlane of the walk's first record", p.j0, kWave, chunk))
+            tj = t0[p.j0];
+        if (is_run(tj) && !(tj & kRunHead)) {
+            uint64_t tails = 0;
+            for (int l = 0; l < kWave; ++l)
+                if (is_run(t0[l]) && (t0[l] & kRunTail))
+                    tails |= 1ull << l;
+            tails &= ~0ull << p.j0;
+            kc_end = tails ? ctz64(tails) : p.nv - 1;
+        }
+    }
+    int64_t piece_lo = -1;   // first key of the run piece being summed
     int ps = p.j0;
     for (int j = p.j0; j < p.jend; j += x.step_u) {
         for (int u = 0; u < x.step_u; ++u) {
@@ -215,22 +241,49 @@ void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
             if (tsplit) {
                 const uint32_t tv = lane_val(x, t0, t1, k, chunk);
                 if (tv != kNotSingle) {
-                    bool last = true;
-                    if (x.nested && (tv & kMultiKey)) {
-                        const uint32_t nx = k + 1 < p.jend ? lane_val(x, t0, t1, k + 1, chunk) : kNotSingle;
-                        last = nx == kNotSingle || ((nx ^ tv) & kTrowMask) != 0;
-                        const uint32_t pv = k > p.j0 ? lane_val(x, t0, t1, k - 1, chunk) : kNotSingle;
-                        const bool cont = pv != kNotSingle && ((pv ^ tv) & kTrowMask) == 0;
-                        // a run's keys are walked in one stretch: a key that continues
-                        // a run follows a key of the same run
-                        if (cont && !(pv & kMultiKey))
-                            bad(x, "nested run continuing a single key (key)", c0 + k, x.n, chunk);
+                    const bool run = x.nested && (tv & kMultiKey);
+                    const bool tlast = !run || (k > kc_end && (tv & kRunTail));
+                    const int64_t key = c0 + k;
+                    if (run && k != p.j0 && !(tv & kRunHead)) {
+                        // adds the running sum: the key before must be of the same run
+                        const uint32_t pv = lane_val(x, t0, t1, k - 1, chunk);
+                        if (!is_run(pv) || ((pv ^ tv) & kTrowMask) != 0 || piece_lo < 0)
+                            bad(x, "nested run continuing another record (key)", key, x.n, chunk);
+                    } else {
+                        piece_lo = key;
                     }
-                    if (last) {
+                    if (tlast) {
                         const uint32_t tr = tv & (x.nested ? kTrowMask : 0x7FFFFFFFu);
                         in(x, "trigram table row (completed in the bigram pass)", tr, x.rows_t, chunk);
+                        if (run) {
+                            // the run began in this walk: its first key carries kRunHead
+                            const uint32_t hv = x.tinfo[x.V[piece_lo] & 0x7FFFFFFFu];
+                            if (!(hv & kRunHead))
+                                bad(x, "nested run completed without its first key (key)", key, x.n, chunk);
+                        }
                         if (in(x, "trigram step count", v & 0x7FFFFFFFu, x.code_cap, chunk))
                             x.tstepped[v & 0x7FFFFFFFu] += 1;
+                        for (int64_t i = piece_lo; i <= key; ++i)
+                            if (in(x, "summed key", i, x.n, chunk))
+                                x.tsum[x.V[i] & 0x7FFFFFFFu] += 1;
+                        piece_lo = -1;
+                    } else if (run && (k == kc_end || k == p.jend - 1)) {
+                        const int slot = k <= kc_end ? 0 : 1;
+                        if (slot == 0 && piece_lo != c0 + p.j0)
+                            bad(x, "run piece of slot 0 not at the walk's start (key)", key, x.n, chunk);
+                        if (in(x, "run piece", chunk, x.nchunk, chunk)) {
+                            x.tpart_w[2 * chunk + slot] += 1;
+                            x.tpart_lo[2 * chunk + slot] = piece_lo;
+                            x.tpart_hi[2 * chunk + slot] = key;
+                        }
+                        if (slot == 1 && in(x, "run record", (int64_t)x.trec.size(), x.nchunk, chunk))
+                            x.trec.push_back((uint64_t)chunk | ((uint64_t)tv << 32));
+                        piece_lo = -1;
+                    } else if (run) {
+                        // the piece goes on: the next key walked is of the same run
+                        const uint32_t nx = k + 1 < p.jend ? lane_val(x, t0, t1, k + 1, chunk) : kNotSingle;
+                        if (!is_run(nx) || ((nx ^ tv) & kTrowMask) != 0 || (nx & kRunHead))
+                            bad(x, "nested run piece left open (key)", key, x.n, chunk);
                     }
                 }
             }
@@ -332,17 +385,75 @@ void fixup(Ctx &x, const std::vector<int> &gw)
     }
 }
 
+// The fix-up of nested trigram runs that crossed a walk's end: slot 1 of the
+// record's chunk, then slot 0 of each following chunk whose first key
+// continues the run (probed 64 chunks at a time, as the wavefront does).
+void trun_fixup(Ctx &x, int64_t n0, const uint32_t *V0)
+{
+    for (size_t r = 0; r < x.trec.size(); ++r) {
+        const int64_t c = (int64_t)(uint32_t)x.trec[r];
+        const uint32_t tv = (uint32_t)(x.trec[r] >> 32);
+        in(x, "run fix-up trigram row", tv & kTrowMask, x.rows_t, c);
+        int64_t m = 0;
+        for (;;) {
+            int lead = kWave;
+            for (int l = 0; l < kWave; ++l) {
+                const int64_t cc = c + 1 + m + l;
+                bool hit = false;
+                if (cc * kChunk < n0) {
+                    const uint32_t code = V0[cc * kChunk] & 0x7FFFFFFFu;
+                    if (in(x, "run fix-up probe record", code, x.code_cap, c)) {
+                        const uint32_t t = x.tinfo[code];
+                        hit = is_run(t) && !(t & kRunHead) && ((t ^ tv) & kTrowMask) == 0;
+                    }
+                }
+                if (!hit) {
+                    lead = l;
+                    break;
+                }
+            }
+            m += lead;
+            if (lead < kWave)
+                break;
+        }
+        if (!in(x, "run fix-up first piece", c, x.nchunk, c) || x.tpart_w[2 * c + 1] != 1) {
+            bad(x, "run fix-up of an unwritten first piece (chunk)", c, x.nchunk, c);
+            continue;
+        }
+        int64_t lo = x.tpart_lo[2 * c + 1], hi = x.tpart_hi[2 * c + 1];
+        bool ok = (x.tinfo[x.V[lo] & 0x7FFFFFFFu] & kRunHead) != 0;
+        for (int64_t i = 1; i <= m; ++i) {
+            const int64_t cc = c + i;
+            if (!in(x, "run fix-up piece", cc, x.nchunk, c) || x.tpart_w[2 * cc] != 1) {
+                bad(x, "run fix-up of an unwritten piece (chunk)", cc, x.nchunk, c);
+                ok = false;
+                break;
+            }
+            ok = ok && x.tpart_lo[2 * cc] == hi + 1;   // the pieces follow each other
+            hi = x.tpart_hi[2 * cc];
+        }
+        if (!ok || !(x.tinfo[x.V[hi] & 0x7FFFFFFFu] & kRunTail)) {
+            bad(x, "run fix-up pieces not one whole run (chunk)", c, x.nchunk, c);
+            continue;
+        }
+        x.tstepped[x.V[hi] & 0x7FFFFFFFu] += 1;
+        for (int64_t i = lo; i <= hi; ++i)
+            x.tsum[x.V[i] & 0x7FFFFFFFu] += 1;
+    }
+}
+
 }  // namespace
 
 extern "C" {
 
 // Returns the number of violations; `msg` (256 bytes) gets the first.  Fills
-// walked[n], completed[n] (at segment heads) and tstepped[code_cap].
+// walked[n], completed[n] (at segment heads), tstepped[code_cap] and
+// tsum[code_cap]; n_trec gets the number of nested run records.
 int64_t model_channel(int64_t n, const uint32_t *R, const uint32_t *V, const uint32_t *I, int64_t nk,
                       const uint32_t *tinfo, int64_t code_cap, int pos_bits, int n_micro, const int64_t *Tm,
                       int64_t rows_c, int64_t rows_t, int64_t wrows, int64_t nchunk, int64_t ngroup, int step_u,
-                      int nested, int32_t *walked, int32_t *completed, int32_t *tstepped, int64_t *accesses,
-                      char *msg)
+                      int nested, int32_t *walked, int32_t *completed, int32_t *tstepped, int32_t *tsum,
+                      int64_t *n_trec, int64_t *accesses, char *msg)
 {
     Ctx x;
     x.nested = nested != 0;
@@ -352,20 +463,28 @@ int64_t model_channel(int64_t n, const uint32_t *R, const uint32_t *V, const uin
     x.walked.assign(n, 0);
     x.completed.assign(n, 0);
     x.tstepped.assign(code_cap, 0);
+    x.tsum.assign(code_cap, 0);
     x.partial_w.assign(2 * nchunk, 0);
+    x.tpart_w.assign(2 * nchunk, 0);
+    x.tpart_lo.assign(2 * nchunk, -1);
+    x.tpart_hi.assign(2 * nchunk, -1);
     const int64_t chunks = (n + kChunk - 1) / kChunk;
     for (int64_t ch = 0; ch < chunks; ++ch)
         walk_chunk(x, ch, tinfo != nullptr);
     std::vector<int> gw(ngroup > 0 ? ngroup : 1, 0);
     group_sums(x, gw);
     fixup(x, gw);
+    trun_fixup(x, n, V);
     for (int64_t i = 0; i < n; ++i) {
         walked[i] = x.walked[i];
         completed[i] = x.completed[i];
     }
-    for (int64_t i = 0; i < code_cap; ++i)
+    for (int64_t i = 0; i < code_cap; ++i) {
         tstepped[i] = x.tstepped[i];
+        tsum[i] = x.tsum[i];
+    }
     *accesses = x.accesses;
+    *n_trec = (int64_t)x.trec.size();
     memcpy(msg, x.first, sizeof(x.first));
     return x.violations;
 }
