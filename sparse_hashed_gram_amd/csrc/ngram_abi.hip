@@ -148,6 +148,10 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
     L.nested = L.nch == 2 && c->rows[1] <= (int64_t(1) << 28);
     L.bidx = o;
     o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
+    for (int k = 0; k < 2; ++k) {
+        L.tix[k] = o;
+        o = up(o + (L.nested ? 4ull * (uint64_t)L.nk : 0));
+    }
     L.tpart = o;
     o = up(o + (L.nested ? 4ull * (uint64_t)L.nchunk * 2 * kDim : 0));
     L.trec = o;

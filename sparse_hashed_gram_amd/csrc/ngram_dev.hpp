@@ -321,9 +321,12 @@ struct WsLayout {
     uint64_t partial;       // fp32 [2][nchunk][2][768]
     uint64_t owners;        // uint64 [2][nchunk]
     uint64_t gpart;         // fp32 [2][ngroup][768]: sums of 64-chunk groups inside one segment
-    uint64_t tinfo;         // uint32 [code_cap]: per dY row code, its trigram row's record
-                            // when the bigram pass completes that row (see the
-                            // singleton split and the nested trigram rows), else kNotSingle
+    uint64_t tinfo;         // uint32 [code_cap]: per dY row code (nested sort: per index in
+                            // the trigram order), its trigram row's record when the bigram
+                            // pass completes that row (see the singleton split and the nested
+                            // trigram rows), else kNotSingle
+    uint64_t tix[2];        // uint32 [nk] each (nested sort): the bigram keys' indices in the
+                            // trigram order, carried through the bigram passes
     uint64_t bidx;          // uint32 [code_cap]: per dY row code, its packed bigram index
                             // (nested sort: the bigram keys are gathered in trigram order)
     uint64_t tpart;         // fp32 [nchunk][2][768] (nested sort): pieces of nested trigram

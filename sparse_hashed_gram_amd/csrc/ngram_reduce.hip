@@ -195,21 +195,29 @@ __global__ __launch_bounds__(kSortThreads) void scan_digits_kernel(uint32_t *__r
         tot[c * kRadix + d] = total;
 }
 
-// Stable scatter of one tile by the current digit.  Wave w owns the w-th
-// quarter of the tile's keys, processed 64 at a time in index order.
-template <int ITEMS>
-__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
+// Stable scatter of one tile of NT x ITEMS keys by the current digit.  Wave
+// w owns the w-th of the tile's NT / 64 equal parts, processed 64 keys at a
+// time in index order.  X3 (one channel): a third payload moves with the
+// keys, xin -> xout; a null xin stands for each key's index before the pass.
+template <int ITEMS, int NT, bool X3>
+__global__ __launch_bounds__(NT) void radix_scatter_kernel(
     const uint32_t *__restrict__ kin, const uint32_t *__restrict__ vin, uint32_t *__restrict__ kout,
     uint32_t *__restrict__ vout, int64_t nk, const uint32_t *n_dev, uint32_t n_host, int shift,
-    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk, int cbase)
+    const uint32_t *__restrict__ hist, const uint32_t *__restrict__ tot, uint32_t nblk, int cbase,
+    const uint32_t *__restrict__ xin, uint32_t *__restrict__ xout)
 {
-    constexpr int kPerWave = radix_tile(ITEMS) / (kSortThreads / kWave);
-    __shared__ uint32_t s_cnt[kSortThreads / kWave][kRadix];
+    constexpr int kTile = NT * ITEMS;
+    constexpr int kW = NT / kWave;
+    constexpr int kD = kRadix / NT;   // digits per thread in the per-digit loops
+    static_assert(kRadix % NT == 0, "digits are split evenly over the threads");
+    constexpr int kPerWave = kTile / kW;
+    __shared__ uint32_t s_cnt[kW][kRadix];
     __shared__ uint32_t s_tile[kRadix];
     __shared__ uint32_t s_glob[kRadix];
-    __shared__ uint32_t s_k[radix_tile(ITEMS)];
-    __shared__ uint32_t s_v[radix_tile(ITEMS)];
-    __shared__ uint32_t s_wave[kSortThreads / kWave];
+    __shared__ uint32_t s_k[kTile];
+    __shared__ uint32_t s_v[kTile];
+    __shared__ uint32_t s_x[X3 ? kTile : 1];
+    __shared__ uint32_t s_wave[kW];
 
     const int c = cbase + (int)blockIdx.y;
     const uint32_t b = blockIdx.x;
@@ -217,33 +225,33 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
     const uint32_t n = count_of(n_dev, n_host);
-    const uint32_t base = b * radix_tile(ITEMS);
+    const uint32_t base = b * kTile;
     if (base >= n)
         return;
     const uint32_t *ki = kin + (size_t)c * nk;
     const uint32_t *vi = vin + (size_t)c * nk;
 
-    for (int r = tid; r < (kSortThreads / kWave) * kRadix; r += kSortThreads)
+    for (int r = tid; r < kW * kRadix; r += NT)
         (&s_cnt[0][0])[r] = 0;
     {
-        // thread t owns digits t * kDpt .. t * kDpt + kDpt - 1
-        uint32_t v[kDpt], sum = 0;
+        // thread t owns digits t * kD .. t * kD + kD - 1
+        uint32_t v[kD], sum = 0;
 #pragma unroll
-        for (int j = 0; j < kDpt; ++j) {
-            v[j] = tot[c * kRadix + tid * kDpt + j];
+        for (int j = 0; j < kD; ++j) {
+            v[j] = tot[c * kRadix + tid * kD + j];
             sum += v[j];
         }
-        uint32_t run = block_excl_scan<kSortThreads>(sum, s_wave, nullptr);
+        uint32_t run = block_excl_scan<NT>(sum, s_wave, nullptr);
 #pragma unroll
-        for (int j = 0; j < kDpt; ++j) {
-            const int d = tid * kDpt + j;
+        for (int j = 0; j < kD; ++j) {
+            const int d = tid * kD + j;
             s_glob[d] = run + hist[((size_t)c * kRadix + d) * nblk + b];
             run += v[j];
         }
     }
     __syncthreads();
 
-    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
+    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS], x3[X3 ? ITEMS : 1];
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
@@ -251,6 +259,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
         const bool ok = i < n;
         key[j] = ok ? ki[i] : 0u;
         val[j] = ok ? vi[i] : 0u;
+        if constexpr (X3)
+            x3[j] = xin ? (ok ? xin[i] : 0u) : i;
     }
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
@@ -272,13 +282,13 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     {
         // per digit: exclusive offsets of the wavefronts' runs, then the
         // exclusive scan of the digit totals over the tile
-        uint32_t dtot[kDpt], sum = 0;
+        uint32_t dtot[kD], sum = 0;
 #pragma unroll
-        for (int j = 0; j < kDpt; ++j) {
-            const int d = tid * kDpt + j;
+        for (int j = 0; j < kD; ++j) {
+            const int d = tid * kD + j;
             uint32_t run = 0;
 #pragma unroll
-            for (int ww = 0; ww < kSortThreads / kWave; ++ww) {
+            for (int ww = 0; ww < kW; ++ww) {
                 const uint32_t x = s_cnt[ww][d];
                 s_cnt[ww][d] = run;
                 run += x;
@@ -286,10 +296,10 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
             dtot[j] = run;
             sum += run;
         }
-        uint32_t run = block_excl_scan<kSortThreads>(sum, s_wave, nullptr);
+        uint32_t run = block_excl_scan<NT>(sum, s_wave, nullptr);
 #pragma unroll
-        for (int j = 0; j < kDpt; ++j) {
-            s_tile[tid * kDpt + j] = run;
+        for (int j = 0; j < kD; ++j) {
+            s_tile[tid * kD + j] = run;
             run += dtot[j];
         }
     }
@@ -302,19 +312,23 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
             const uint32_t pos = s_tile[d] + s_cnt[w][d] + rank[j];
             s_k[pos] = key[j];
             s_v[pos] = val[j];
+            if constexpr (X3)
+                s_x[pos] = x3[j];
         }
     }
     __syncthreads();
     uint32_t *ko = kout + (size_t)c * nk;
     uint32_t *vo = vout + (size_t)c * nk;
-    const uint32_t nv = min((uint32_t)radix_tile(ITEMS), n - base);
-    for (uint32_t p = tid; p < nv; p += kSortThreads) {
+    const uint32_t nv = min((uint32_t)kTile, n - base);
+    for (uint32_t p = tid; p < nv; p += NT) {
         const uint32_t k = s_k[p];
         const uint32_t d = (k >> shift) & (kRadix - 1);
         const uint32_t dst = s_glob[d] + (p - s_tile[d]);
         const uint32_t v = s_v[p];
         ko[dst] = k;
         vo[dst] = v;
+        if constexpr (X3)
+            xout[dst] = s_x[p];
     }
 }
 
@@ -375,7 +389,10 @@ constexpr uint32_t kDropSingle = 0x3FFFFFFFu;   // slot field of all ones: never
 // end of a walk (inside a bigram segment of many chunks) leaves one piece
 // per walk in tpart, and the fix-up adds the pieces in order and steps the
 // row.  The record is row | neg << 31, plus, for a run of several keys,
-// kMultiKey, and kRunHead / kRunTail on its first / last key.
+// kMultiKey, and kRunHead / kRunTail on its first / last key.  With the
+// nested sort the map is indexed by the key's place in the trigram order
+// (mark_kernel writes it in that order, one contiguous store per key), and
+// the bigram sort carries that index along with each bigram key (tix).
 constexpr uint32_t kMultiKey = 0x40000000u;
 constexpr uint32_t kRunHead = 0x20000000u;
 constexpr uint32_t kRunTail = 0x10000000u;
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
             const uint32_t v = vq[j];
             const bool hd = (headm & (1u << j)) != 0, ed = (endm & (1u << j)) != 0;
             const uint32_t run_bits = (hd && ed) ? 0u : (kMultiKey | (hd ? kRunHead : 0u) | (ed ? kRunTail : 0u));
-            a.tinfo[v & 0x7FFFFFFFu] = nested ? (R[i] | (v & 0x80000000u) | run_bits) : kNotSingle;
+            a.tinfo[i] = nested ? (R[i] | (v & 0x80000000u) | run_bits) : kNotSingle;
             a.tkept[i] = nested ? 0 : 1;
             kept += nested ? 0u : 1u;
         }
@@ -710,6 +727,8 @@ struct RedArgs {
     WsHeader *hdr;
     const uint32_t *tinfo;  // singleton map per dY row code
     bool nested;            // the map also names nested trigram rows of several keys (kMultiKey)
+    const uint32_t *tix0;   // nested: per sorted bigram key, its index in the trigram order
+                            // (the singleton map's index); else the map is indexed by row code
     float *tpart;           // nested: [nchunk][2][768] pieces of runs that cross a walk's end
     uint64_t *trec;         // nested: [nchunk] such runs, chunk of the first piece | record << 32
     bool burst;             // the keys are the burst stash's: check the window is ready
@@ -1161,10 +1180,11 @@ __global__ __launch_bounds__(kRedThreads) __attribute__((amdgpu_waves_per_eu(kSt
     const bool tsplit = a.tinfo != nullptr && c == 0;
     uint32_t t0 = kNotSingle, t1 = kNotSingle;   // trigram singleton of keys lane, 64 + lane
     if (tsplit) {
+        const int64_t c0 = chunk * kChunk;
         if (lane < p.nv)
-            t0 = a.tinfo[p.v0 & 0x7FFFFFFFu];
+            t0 = a.tinfo[a.tix0 ? a.tix0[c0 + lane] : (p.v0 & 0x7FFFFFFFu)];
         if (p.owner_full && kChunk + lane < p.jend)
-            t1 = a.tinfo[p.v1 & 0x7FFFFFFFu];
+            t1 = a.tinfo[a.tix0 ? a.tix0[c0 + kChunk + lane] : (p.v1 & 0x7FFFFFFFu)];
     }
     // nested runs: keys j0 .. kc_end continue a run from the walk before
     // (the walk's first piece of that run, completed by the fix-up)
@@ -1561,7 +1581,6 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
             constexpr int ELT = MODE == kFuseBf16 ? 2 : 4;
             const uint32_t ntr = a.hdr->n_trun;
             const int64_t n0 = count_of(a.n_dev[0], a.n_host);
-            const uint32_t *V0 = a.vals[0];
             const uint64_t table_t = (uint64_t)a.f.w[1] + (uint64_t)ELT * 4 * lane;
             const uint64_t state_t = (uint64_t)a.f.st[1];
             const uint64_t P = (uint64_t)a.tpart + 16 * lane;
@@ -1580,7 +1599,7 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
                     const int64_t cc = x + 1 + m + lane;
                     bool hit = false;
                     if (cc * kChunk < n0) {
-                        const uint32_t t = a.tinfo[V0[cc * kChunk] & 0x7FFFFFFFu];
+                        const uint32_t t = a.tinfo[a.tix0[cc * kChunk]];
                         hit = is_run(t) && !(t & kRunHead) && ((t ^ tv) & kTrowMask) == 0;
                     }
                     const uint64_t miss = ~__ballot(hit);
@@ -1659,10 +1678,17 @@ SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32
     return sa;
 }
 
+// The scatter's block for the 4,096-key tiles of large sorts: 512 threads
+// of 8 keys (the full window's sort group 6 us faster than 256 threads of 16).
+constexpr int kScatterThreadsBig = 512, kScatterItemsBig = 8;
+static_assert(kScatterThreadsBig * kScatterItemsBig == radix_tile(kRadixItemsBig), "one tile per scatter block");
+
 // The radix passes over the channels [cbase, cbase + nch) (the first pass's
-// digit counts already taken), from key buffer 0.
+// digit counts already taken), from key buffer 0.  tix (one channel): each
+// key's index before the first pass is carried along, ping-ponging between
+// L.tix[0] and L.tix[1] (the last pass writes L.tix[passes & 1]).
 void radix_passes(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_t n_host, bool big, uint32_t nrb,
-                  int cbase, int nch, hipStream_t s)
+                  int cbase, int nch, bool tix, hipStream_t s)
 {
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     uint32_t *tot = reinterpret_cast<uint32_t *>(ws + L.tot);
@@ -1677,9 +1703,24 @@ void radix_passes(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32_
             (big ? radix_hist_kernel<kRadixItemsBig> : radix_hist_kernel<kRadixItemsSmall>)
                 <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, L.nk, n_dev, n_host, shift, hist, nrb, cbase);
         scan_digits_kernel<<<dim3(kRadix, nch), kSortThreads, 0, s>>>(hist, nrb, tot, cbase);
-        (big ? radix_scatter_kernel<kRadixItemsBig> : radix_scatter_kernel<kRadixItemsSmall>)
-            <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist, tot,
-                                                     nrb, cbase);
+        const uint32_t *xin = p == 0 ? nullptr : reinterpret_cast<const uint32_t *>(ws + L.tix[p & 1]);
+        uint32_t *xout = reinterpret_cast<uint32_t *>(ws + L.tix[(p + 1) & 1]);
+        if (big && tix)
+            radix_scatter_kernel<kScatterItemsBig, kScatterThreadsBig, true>
+                <<<dim3(nrb, nch), kScatterThreadsBig, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift,
+                                                               hist, tot, nrb, cbase, xin, xout);
+        else if (big)
+            radix_scatter_kernel<kScatterItemsBig, kScatterThreadsBig, false>
+                <<<dim3(nrb, nch), kScatterThreadsBig, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift,
+                                                               hist, tot, nrb, cbase, nullptr, nullptr);
+        else if (tix)
+            radix_scatter_kernel<kRadixItemsSmall, kSortThreads, true>
+                <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist,
+                                                         tot, nrb, cbase, xin, xout);
+        else
+            radix_scatter_kernel<kRadixItemsSmall, kSortThreads, false>
+                <<<dim3(nrb, nch), kSortThreads, 0, s>>>(kin, vin, kout, vout, L.nk, n_dev, n_host, shift, hist,
+                                                         tot, nrb, cbase, nullptr, nullptr);
         cur ^= 1;
     }
 }
@@ -1718,16 +1759,17 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
                 burst ? reinterpret_cast<const uint32_t *>(ws + L.stash_pos) : nullptr, hp, n_host, k0, v0, L.nk,
                 hist, nrb, hdr, bidx);
     if (!nested) {
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, L.nch, s);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, L.nch, false, s);
     } else {
         // the trigram keys alone, then the bigram keys in trigram order (the
         // same buffer 0 the trigram keys started from, their own half), then
-        // the bigram keys by row: (bigram row, trigram row, position)
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, s);
+        // the bigram keys by row: (bigram row, trigram row, position), each
+        // carrying its index in the trigram order
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, false, s);
         const uint32_t *vt = reinterpret_cast<const uint32_t *>(ws + L.vals[L.passes & 1]) + L.nk;
         (big ? gather_bigram_kernel<kRadixItemsBig> : gather_bigram_kernel<kRadixItemsSmall>)
             <<<nrb, kSortThreads, 0, s>>>(vt, bidx, n_dev, n_host, k0, v0, hist, nrb);
-        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, s);
+        radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, true, s);
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);
     // one table (token-indexed): no trigram channel, no singleton split
@@ -1765,6 +1807,7 @@ hipError_t reduce_part(const WsLayout &L, uint8_t *ws, uint32_t n_host, bool bur
     ra.n_host = n_host;
     ra.tinfo = L.nch == 2 ? sa.tinfo : nullptr;
     ra.nested = sa.nested;
+    ra.tix0 = sa.nested ? reinterpret_cast<const uint32_t *>(ws + L.tix[L.passes & 1]) : nullptr;
     ra.tpart = reinterpret_cast<float *>(ws + L.tpart);
     ra.trec = reinterpret_cast<uint64_t *>(ws + L.trec);
     ra.dY = burst && !L.by_ref ? ws + L.stash_dy : static_cast<const uint8_t *>(dY);

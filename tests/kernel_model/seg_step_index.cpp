@@ -45,6 +45,8 @@ struct Ctx {
     int64_t nk;             // capacity of the sorted arrays (R, V, I extents)
     const uint32_t *tinfo;  // singleton map (bigram pass only), code_cap entries
     int64_t code_cap;
+    const uint32_t *tix;    // nested sort: per sorted key, the map's index (trigram order);
+                            // null: the map is indexed by the key's row code
     int pos_bits;           // dY row code = micro-step << pos_bits | position
     int n_micro;            // micro-steps whose dY addresses are attached
     const int64_t *Tm;      // positions of each micro-step
@@ -88,6 +90,19 @@ bool in(Ctx &x, const char *what, int64_t idx, int64_t ext, int64_t chunk)
 uint32_t getR(Ctx &x, int64_t i, int64_t chunk)
 {
     return in(x, "sorted row", i, x.nk, chunk) && in(x, "sorted row (count)", i, x.n, chunk) ? x.R[i] : 0u;
+}
+
+// The singleton-map record of sorted key i (payload v), as the kernel reads
+// it: through tix in the nested sort, else by row code.
+uint32_t rec_of(Ctx &x, int64_t i, uint32_t v, int64_t chunk)
+{
+    int64_t m = v & 0x7FFFFFFFu;
+    if (x.tix) {
+        if (!in(x, "tix", i, x.nk, chunk) || !in(x, "tix (count)", i, x.n, chunk))
+            return kNotSingle;
+        m = x.tix[i];
+    }
+    return in(x, "singleton map", m, x.code_cap, chunk) ? x.tinfo[m] : kNotSingle;
 }
 
 struct Plan {
@@ -195,10 +210,10 @@ void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
     for (int l = 0; l < kWave; ++l) {
         t0[l] = t1[l] = kNotSingle;
         if (tsplit) {
-            if (l < p.nv && in(x, "singleton map", p.v0[l] & 0x7FFFFFFFu, x.code_cap, chunk))
-                t0[l] = x.tinfo[p.v0[l] & 0x7FFFFFFFu];
-            if (p.owner_full && kChunk + l < p.jend && in(x, "singleton map", p.v1[l] & 0x7FFFFFFFu, x.code_cap, chunk))
-                t1[l] = x.tinfo[p.v1[l] & 0x7FFFFFFFu];
+            if (l < p.nv)
+                t0[l] = rec_of(x, c0 + l, p.v0[l], chunk);
+            if (p.owner_full && kChunk + l < p.jend)
+                t1[l] = rec_of(x, c0 + kChunk + l, p.v1[l], chunk);
         }
     }
     uint64_t fin = (p.hm >> 1) | (1ull << (p.nv - 1));
@@ -257,7 +272,7 @@ void walk_chunk(Ctx &x, int64_t chunk, bool tsplit)
                         in(x, "trigram table row (completed in the bigram pass)", tr, x.rows_t, chunk);
                         if (run) {
                             // the run began in this walk: its first key carries kRunHead
-                            const uint32_t hv = x.tinfo[x.V[piece_lo] & 0x7FFFFFFFu];
+                            const uint32_t hv = rec_of(x, piece_lo, x.V[piece_lo], chunk);
                             if (!(hv & kRunHead))
                                 bad(x, "nested run completed without its first key (key)", key, x.n, chunk);
                         }
@@ -401,11 +416,8 @@ void trun_fixup(Ctx &x, int64_t n0, const uint32_t *V0)
                 const int64_t cc = c + 1 + m + l;
                 bool hit = false;
                 if (cc * kChunk < n0) {
-                    const uint32_t code = V0[cc * kChunk] & 0x7FFFFFFFu;
-                    if (in(x, "run fix-up probe record", code, x.code_cap, c)) {
-                        const uint32_t t = x.tinfo[code];
-                        hit = is_run(t) && !(t & kRunHead) && ((t ^ tv) & kTrowMask) == 0;
-                    }
+                    const uint32_t t = rec_of(x, cc * kChunk, V0[cc * kChunk], c);
+                    hit = is_run(t) && !(t & kRunHead) && ((t ^ tv) & kTrowMask) == 0;
                 }
                 if (!hit) {
                     lead = l;
@@ -421,7 +433,7 @@ void trun_fixup(Ctx &x, int64_t n0, const uint32_t *V0)
             continue;
         }
         int64_t lo = x.tpart_lo[2 * c + 1], hi = x.tpart_hi[2 * c + 1];
-        bool ok = (x.tinfo[x.V[lo] & 0x7FFFFFFFu] & kRunHead) != 0;
+        bool ok = (rec_of(x, lo, x.V[lo], c) & kRunHead) != 0;
         for (int64_t i = 1; i <= m; ++i) {
             const int64_t cc = c + i;
             if (!in(x, "run fix-up piece", cc, x.nchunk, c) || x.tpart_w[2 * cc] != 1) {
@@ -432,7 +444,7 @@ void trun_fixup(Ctx &x, int64_t n0, const uint32_t *V0)
             ok = ok && x.tpart_lo[2 * cc] == hi + 1;   // the pieces follow each other
             hi = x.tpart_hi[2 * cc];
         }
-        if (!ok || !(x.tinfo[x.V[hi] & 0x7FFFFFFFu] & kRunTail)) {
+        if (!ok || !(rec_of(x, hi, x.V[hi], c) & kRunTail)) {
             bad(x, "run fix-up pieces not one whole run (chunk)", c, x.nchunk, c);
             continue;
         }
@@ -450,14 +462,15 @@ extern "C" {
 // walked[n], completed[n] (at segment heads), tstepped[code_cap] and
 // tsum[code_cap]; n_trec gets the number of nested run records.
 int64_t model_channel(int64_t n, const uint32_t *R, const uint32_t *V, const uint32_t *I, int64_t nk,
-                      const uint32_t *tinfo, int64_t code_cap, int pos_bits, int n_micro, const int64_t *Tm,
+                      const uint32_t *tinfo, int64_t code_cap, const uint32_t *tix, int pos_bits, int n_micro,
+                      const int64_t *Tm,
                       int64_t rows_c, int64_t rows_t, int64_t wrows, int64_t nchunk, int64_t ngroup, int step_u,
                       int nested, int32_t *walked, int32_t *completed, int32_t *tstepped, int32_t *tsum,
                       int64_t *n_trec, int64_t *accesses, char *msg)
 {
     Ctx x;
     x.nested = nested != 0;
-    x.n = n; x.R = R; x.V = V; x.I = I; x.nk = nk; x.tinfo = tinfo; x.code_cap = code_cap;
+    x.n = n; x.R = R; x.V = V; x.I = I; x.nk = nk; x.tinfo = tinfo; x.code_cap = code_cap; x.tix = tix;
     x.pos_bits = pos_bits; x.n_micro = n_micro; x.Tm = Tm; x.rows_c = rows_c; x.rows_t = rows_t;
     x.wrows = wrows; x.nchunk = nchunk; x.ngroup = ngroup; x.step_u = step_u;
     x.walked.assign(n, 0);

@@ -45,7 +45,7 @@ def model(tmp_path_factory):
     L = ctypes.CDLL(lib)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.model_channel.restype = i64
-    L.model_channel.argtypes = [i64, vp, vp, vp, i64, vp, i64, ctypes.c_int, ctypes.c_int, vp, i64, i64, i64,
+    L.model_channel.argtypes = [i64, vp, vp, vp, i64, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp, i64, i64, i64,
                                 i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     return L
 
@@ -61,7 +61,7 @@ def _sorted_keys(rows, neg, codes):
     return R, V
 
 
-def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, step_u=2, nested=False):
+def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, step_u=2, nested=False, tix=None):
     nchunk = (nk + 63) // 64
     ngroup = (nchunk + 63) // 64
     walked = np.zeros(max(n, 1), np.int32)
@@ -76,7 +76,11 @@ def _run(model, n, R, V, I, nk, tinfo, code_cap, pos_bits, Tm, rows_c, rows_t, s
     ext = np.zeros(nk, np.uint32)   # the arrays at their workspace extent (nk entries)
     Rx, Vx, Ix = ext.copy(), ext.copy(), ext.copy()
     Rx[:n], Vx[:n], Ix[:n] = R, V, I
-    viol = model.model_channel(n, _p(Rx), _p(Vx), _p(Ix), nk, _p(tinfo), code_cap, pos_bits, len(Tm), _p(Tm),
+    Xx = None
+    if tix is not None:
+        Xx = ext.copy()
+        Xx[:n] = tix
+    viol = model.model_channel(n, _p(Rx), _p(Vx), _p(Ix), nk, _p(tinfo), code_cap, _p(Xx), pos_bits, len(Tm), _p(Tm),
                                rows_c, rows_t, wrows, nchunk, ngroup, step_u, int(nested), _p(walked), _p(completed),
                                _p(tstepped), _p(tsum), ctypes.byref(ntrec), ctypes.byref(acc), msg)
     assert viol == 0, msg.value.decode()
@@ -100,7 +104,8 @@ def _nested_records(Rt, Vt, rb_of_code, code_cap):
     by the bigram pass if its keys lie in one 2,048-key tile of the trigram
     order and all have the same bigram row.  Records: row | sign, and for a
     row of several keys MULTI with RUN_HEAD / RUN_TAIL on its first / last
-    key.  Returns (records per code, kept mask, nested mask, segment ids)."""
+    key; the map is indexed by the key's place in the trigram order.
+    Returns (records, kept mask, nested mask, segment ids)."""
     n = len(Rt)
     idx = np.arange(n)
     head = _heads(Rt)
@@ -120,7 +125,7 @@ def _nested_records(Rt, Vt, rb_of_code, code_cap):
     bits = np.where(single, 0, MULTI | np.where(head, RUN_HEAD, 0) | np.where(end, RUN_TAIL, 0))
     rec = np.where(nested, Rt | (Vt & 0x80000000) | bits, NOT_SINGLE).astype(np.uint32)
     tinfo = np.full(code_cap, NOT_SINGLE, np.uint32)
-    tinfo[code] = rec
+    tinfo[:n] = rec
     return tinfo, ~nested, nested, seg
 
 
@@ -164,8 +169,11 @@ def _check_window(model, toks, rows, max_tokens, direct=False):
     rb_of_code = np.zeros(code_cap, np.int64)
     rb_of_code[codes.astype(np.int64)] = rb
     tinfo, kept, nested, tseg = _nested_records(Rt, Vt, rb_of_code, code_cap)
+    inv_ot = np.empty(n, np.int64)
+    inv_ot[ot] = np.arange(n)
+    tix = inv_ot[obt].astype(np.uint32)   # each bigram key's place in the trigram order
     walked, completed, tstepped, tsum = _run(model, n, Rb, Vb, Ib, nk, tinfo, code_cap, pos_bits, Tm, rows[0],
-                                             rows[1], nested=True)
+                                             rows[1], nested=True, tix=tix)
     _check_window.n_trec = _run.n_trec
     assert (walked == 1).all(), np.flatnonzero(walked != 1)[:10]
     np.testing.assert_array_equal(completed, _heads(Rb).astype(np.int32))
