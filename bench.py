@@ -106,15 +106,25 @@ def device_table(torch, R, dtype, seed, chunk=1 << 21):
     return W
 
 
-def nested_keys(torch, rb, rt, known=None):
+NEST_MIN_KEYS = 1 << 20   # the library's nested sort: reductions of at least this many keys
+
+
+def nested_keys(torch, rb, rt, known=None, nest=True):
     """Trigram keys the fused reduction's bigram pass completes (so the
     trigram pass does not read their dY rows again): keys of trigram rows new
     to the window (not in `known`) whose keys lie in one 2,048-key tile of the
-    trigram order and share one bigram row.  rb, rt: the rows of the
+    trigram order and share one bigram row (nest), or that occur once (the
+    singleton split alone, without the nested sort).  rb, rt: the rows of the
     positions, in stream order."""
     n = rb.numel()
     if n == 0:
         return 0
+    if not nest:
+        u, inv, cnt = torch.unique(rt, return_inverse=True, return_counts=True)
+        single = cnt[inv] == 1
+        if known is not None:
+            single &= ~torch.isin(rt, known)
+        return int(single.sum())
     idx = torch.arange(n, device=rb.device)
     ot = torch.sort(rt, stable=True).indices
     Rt = rt[ot]
@@ -155,13 +165,18 @@ def window_stats(torch, N, cfg, toks):
             r = rows[c]
             u, cnt = torch.unique(r, return_counts=True)
             fresh = torch.ones_like(u, dtype=torch.bool) if seen[c] is None else ~torch.isin(u, seen[c])
-            handled = nested_keys(torch, rows[0], r, seen[1]) if c == 1 else 0
+            nest = bool(cfg.options & N.OPT_NEST_ALWAYS) or r.numel() >= NEST_MIN_KEYS
+            handled = nested_keys(torch, rows[0], r, seen[1], nest) if c == 1 else 0
             single = int((cnt == 1).sum()) if c == 1 else 0
             per.append((int(u.numel()), int(fresh.sum()), handled, single))
             seen[c] = u if seen[c] is None else torch.unique(torch.cat([seen[c], u]))
             all_r[c].append(r)
         steps.append(per)
-    handled_win = nested_keys(torch, torch.cat(all_r[0]), torch.cat(all_r[1])) if nch == 2 else 0
+    handled_win = 0
+    if nch == 2:
+        rb_w, rt_w = torch.cat(all_r[0]), torch.cat(all_r[1])
+        nest = bool(cfg.options & N.OPT_NEST_ALWAYS) or cfg.max_tokens * cfg.accum_steps >= NEST_MIN_KEYS
+        handled_win = nested_keys(torch, rb_w, rt_w, None, nest)
     return steps, [int(s.numel()) for s in seen], handled_win
 
 

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define NGRAM_ABI_VERSION 9
+#define NGRAM_ABI_VERSION 10
 
 /* dtypes of the tables (and of the forward output), and of the upstream
  * gradients dY */
@@ -135,6 +135,16 @@ extern "C" {
                                   be NULL).  The forward is out[i] =
                                   W_b[t[i]]; an id outside [0, vocab) is
                                   flagged and reads row 0                   */
+#define NGRAM_OPT_NEST_ALWAYS 0x8  /* fused reductions (the burst modes'
+                                  step, spread mode's fused last micro-
+                                  step) sort the bigram keys by (bigram
+                                  row, trigram row) and complete trigram
+                                  rows of several positions in the bigram
+                                  pass at any window size; without it only
+                                  reductions of at least 2^20 positions do
+                                  (a smaller one sorts faster than it would
+                                  gain).  Schedule only: the results are
+                                  the same within the stated tolerances     */
 
 typedef struct ngram_config {
     int32_t vocab;       /* V: token ids are valid in [0, V); 50304 in the

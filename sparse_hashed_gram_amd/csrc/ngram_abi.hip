@@ -58,7 +58,7 @@ int check_cfg(const ngram_config *c)
         return NGRAM_ECONFIG;
     if (c->dy_dtype != NGRAM_DTYPE_F32 && c->dy_dtype != NGRAM_DTYPE_BF16)
         return NGRAM_ECONFIG;
-    if ((c->options & ~(NGRAM_OPT_PRESORT | NGRAM_OPT_OUT_F32 | NGRAM_OPT_DIRECT)) != 0)
+    if ((c->options & ~(NGRAM_OPT_PRESORT | NGRAM_OPT_OUT_F32 | NGRAM_OPT_DIRECT | NGRAM_OPT_NEST_ALWAYS)) != 0)
         return NGRAM_ECONFIG;
     if ((c->options & NGRAM_OPT_DIRECT) && c->rows[0] < c->vocab)
         return NGRAM_ECONFIG;   // every token id needs its row
@@ -146,6 +146,7 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
     o = up(o + 4ull * (uint64_t)L.code_cap);
     // nested trigram records keep four flag bits above the row
     L.nested = L.nch == 2 && c->rows[1] <= (int64_t(1) << 28);
+    L.nest_always = (c->options & NGRAM_OPT_NEST_ALWAYS) != 0;
     L.bidx = o;
     o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
     for (int k = 0; k < 2; ++k) {

@@ -359,9 +359,10 @@ struct WsLayout {
     int64_t code_cap;       // dY row codes are below this
     int accum;              // micro-steps per window
     int nch;                // tables: 2 (bigram, trigram), or 1 (token-indexed)
-    bool nested;            // fused reductions sort the bigram keys by (bigram row,
-                            // trigram row) and complete nested trigram rows in the
-                            // bigram pass (two tables with rows[1] < 2^30)
+    bool nested;            // fused reductions of at least 2^20 keys sort the bigram keys
+                            // by (bigram row, trigram row) and complete nested trigram
+                            // rows in the bigram pass (two tables, rows[1] <= 2^28)
+    bool nest_always;       // ... and so do smaller ones (NGRAM_OPT_NEST_ALWAYS)
     bool one_shot;          // a whole burst window reduced and stepped in one call on an
                             // empty window: no slot maps, slot rows or window
                             // accumulator (their offsets name no memory and are

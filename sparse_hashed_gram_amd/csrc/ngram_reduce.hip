@@ -1642,6 +1642,18 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
 
 namespace {
 
+// Whether a reduction of up to n_host keys per table takes the nested sort.
+// Below 2^20 keys the second, serial sort (a few hundred tiles per pass at
+// most) costs more than the trigram rows it completes save: one shard's
+// window of 4 x 49,152 positions took 0.622 ms without it against 0.673 ms
+// with it, while the full window (4 x 393,216) took 3.44 ms with it against
+// 3.53 ms without, and the collision-stress window 2.75 against 3.10 ms.
+constexpr uint32_t kNestMinKeys = 1u << 20;
+bool nested_sort(const WsLayout &L, uint32_t n_host, bool fused)
+{
+    return fused && L.nested && (L.nest_always || n_host >= kNestMinKeys);
+}
+
 // The sorted arrays, the singleton split's outputs and the slot pointers of
 // one reduce.  The radix sort ping-pongs between the two key/payload buffers,
 // so after L.passes passes the sorted keys are in buffer passes % 2; the
@@ -1672,7 +1684,7 @@ SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32
     sa.split_rows = spare_k + L.nk;
     sa.split_vals = spare_v + L.nk;
     sa.split_info = spare_k;
-    sa.nested = fused && L.nested;
+    sa.nested = nested_sort(L, n_host, fused);
     sa.bidx = reinterpret_cast<const uint32_t *>(ws + L.bidx);
     sa.tkept = reinterpret_cast<uint8_t *>(ws + L.tkept);
     return sa;
@@ -1734,7 +1746,7 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.hdr);
     const bool burst = tok == nullptr;
     const uint32_t *n_dev = burst ? &hdr->n_stash : nullptr;
-    const bool nested = fused && L.nested;
+    const bool nested = nested_sort(L, n_host, fused);
     // (one channel per launch in the nested sort: 2,048-key tiles there were
     // slower on the full window, 0.296 against 0.286 ms for the sort group)
     const bool big = n_host >= kRadixBigKeys;

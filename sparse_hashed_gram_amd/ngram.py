@@ -22,6 +22,7 @@ MODE_BURST_REF = 2
 OPT_PRESORT = 0x1
 OPT_OUT_F32 = 0x2
 OPT_DIRECT = 0x4
+OPT_NEST_ALWAYS = 0x8
 _MODES = {"spread": MODE_SPREAD, "burst": MODE_BURST, "burst_ref": MODE_BURST_REF}
 
 FLAG_BAD_TOKEN = 0x1
@@ -80,9 +81,11 @@ class NgramConfig(ctypes.Structure):
 def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
            max_tokens: int = 1 << 16, accum_steps: int = 4, mode: str = "spread",
            window_rows: int = 0, dy_dtype: str = "f32", presort: bool = False,
-           out_f32: bool = False, direct: bool = False) -> NgramConfig:
+           out_f32: bool = False, direct: bool = False, nest_always: bool = False) -> NgramConfig:
     """direct: one table indexed by the token id (value embeddings); rows
-    is then (rows of that table, 1) and W_t / state_t may be None."""
+    is then (rows of that table, 1) and W_t / state_t may be None.
+    nest_always: fused reductions of any size complete trigram rows of
+    several positions in the bigram pass (NGRAM_OPT_NEST_ALWAYS)."""
     c = NgramConfig()
     c.vocab = vocab
     c.eos_id = eos_id
@@ -95,7 +98,8 @@ def config(vocab: int, eos_id: int, rows, dtype: str = "bf16", seeds=(1, 2),
     c.mode = _MODES[mode]
     c.window_rows = int(window_rows)
     c.dy_dtype = DTYPE_F32 if dy_dtype == "f32" else DTYPE_BF16
-    c.options = (OPT_PRESORT if presort else 0) | (OPT_OUT_F32 if out_f32 else 0) | (OPT_DIRECT if direct else 0)
+    c.options = ((OPT_PRESORT if presort else 0) | (OPT_OUT_F32 if out_f32 else 0) | (OPT_DIRECT if direct else 0)
+                 | (OPT_NEST_ALWAYS if nest_always else 0))
     return c
 
 

@@ -38,7 +38,7 @@ def test_config_struct_layout(N):
 
 
 def test_version_and_status_strings(N):
-    assert N.lib().ngram_abi_version() == 9
+    assert N.lib().ngram_abi_version() == 10
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert N.status_string(s) not in ("", "unknown status")
     assert N.status_string(-99) == "unknown status"
@@ -53,7 +53,7 @@ def _good(N, **kw):
 @pytest.mark.parametrize("field,value", [
     ("vocab", 0), ("eos_id", -1), ("eos_id", 50304), ("dim", 512), ("dtype", 2),
     ("max_tokens", 0), ("max_tokens", (1 << 28) + 1), ("accum_steps", 0), ("accum_steps", 65),
-    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("options", 8), ("options", 1)])
+    ("mode", 3), ("window_rows", -1), ("dy_dtype", 2), ("dy_dtype", -1), ("options", 16), ("options", 1)])
 def test_config_rejects(N, field, value):
     c = _good(N)
     setattr(c, field, value)

@@ -39,13 +39,14 @@ def _window_eager(N, cfg, st, ws, toks, dys, t, lr, beta2, eps, how):
     return outs
 
 
-@pytest.mark.parametrize("how", ["fused_last", "step"])
-@pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
-def test_graph_replay_equals_eager(mode, how):
+@pytest.mark.parametrize("mode,how,nest", [(m, h, False) for m in ("spread", "burst", "burst_ref")
+                                           for h in ("fused_last", "step")]
+                         + [("burst_ref", "step", True), ("spread", "fused_last", True)])
+def test_graph_replay_equals_eager(mode, how, nest):
     w = workloads.TINY
     N = ng()
     T, A = w.tokens_per_step, w.accum_steps
-    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T, mode=mode)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T, mode=mode, nest_always=nest)
     eager = _tiny_state(cfg, w)
     graph = eager.clone()
     ws_e, ws_g = N.Workspace(cfg), N.Workspace(cfg)

@@ -84,13 +84,15 @@ def _same_class(got, want):
 
 
 @pytest.mark.parametrize("dtype,dy_dtype", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
-@pytest.mark.parametrize("mode,how", [("spread", "export"), ("spread", "fused_last"), ("burst", "export"),
-                                      ("burst", "step"), ("burst", "fused_last"), ("burst_ref", "export"),
-                                      ("burst_ref", "step"), ("burst_ref", "fused_last")])
-def test_nonfinite_gradients_propagate(mode, how, dtype, dy_dtype):
+@pytest.mark.parametrize("mode,how,nest", [("spread", "export", False), ("spread", "fused_last", False),
+                                           ("burst", "export", False), ("burst", "step", False),
+                                           ("burst", "fused_last", False), ("burst_ref", "export", False),
+                                           ("burst_ref", "step", False), ("burst_ref", "fused_last", False),
+                                           ("burst_ref", "step", True), ("spread", "fused_last", True)])
+def test_nonfinite_gradients_propagate(mode, how, nest, dtype, dy_dtype):
     N = ng()
     cfg = N.config(W.vocab, W.eos_id, W.rows, dtype, max_tokens=W.tokens_per_step, mode=mode,
-                   dy_dtype=dy_dtype)
+                   dy_dtype=dy_dtype, nest_always=nest)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     st = State(cfg, to_dev(synth.init_rows(W, 0, W.rows[0])).to(tdt),
                to_dev(synth.init_rows(W, 1, W.rows[1])).to(tdt))

@@ -49,14 +49,16 @@ def _ahead_window(N, cfg, st, ws, toks, dys, t, how, n_ahead, side):
     _regular_window(N, cfg, st, ws, toks, dys, t, how)
 
 
+@pytest.mark.parametrize("nest", [False, True])
 @pytest.mark.parametrize("how", ["step", "fused_last"])
 @pytest.mark.parametrize("presort", [False, True])
 @pytest.mark.parametrize("mode", ["burst", "burst_ref"])
-def test_keys_ahead_equal_the_regular_path(mode, presort, how):
+def test_keys_ahead_equal_the_regular_path(mode, presort, how, nest):
     N = ng()
     T = W.tokens_per_step
-    cfg_r = N.config(W.vocab, W.eos_id, W.rows, "f32", max_tokens=T, mode=mode)
-    cfg_a = N.config(W.vocab, W.eos_id, W.rows, "f32", max_tokens=T, mode=mode, presort=presort)
+    cfg_r = N.config(W.vocab, W.eos_id, W.rows, "f32", max_tokens=T, mode=mode, nest_always=nest)
+    cfg_a = N.config(W.vocab, W.eos_id, W.rows, "f32", max_tokens=T, mode=mode, presort=presort,
+                     nest_always=nest)
     reg, ahd = _state(cfg_r), _state(cfg_a)
     ws_r, ws_a = N.Workspace(cfg_r), N.Workspace(cfg_a)
     side = torch.cuda.Stream()

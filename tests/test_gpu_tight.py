@@ -49,18 +49,19 @@ def singleton_window(vocab, eos, rows, A, T, seed):
     raise RuntimeError("no collision-free window found")
 
 
-CASES = [("spread", "export"), ("spread", "fused_last"), ("burst", "export"), ("burst", "step"),
-         ("burst_ref", "export"), ("burst_ref", "step")]
+CASES = [("spread", "export", False), ("spread", "fused_last", False), ("burst", "export", False),
+         ("burst", "step", False), ("burst_ref", "export", False), ("burst_ref", "step", False),
+         ("burst_ref", "step", True)]
 
 
 @pytest.mark.parametrize("table", ["tiny_f32", "shard_bf16"])
-@pytest.mark.parametrize("mode,how", CASES)
-def test_singleton_windows_tight_bound(mode, how, table):
+@pytest.mark.parametrize("mode,how,nest", CASES)
+def test_singleton_windows_tight_bound(mode, how, nest, table):
     N = ng()
     w = workloads.TINY if table == "tiny_f32" else workloads.SHARD
     dtype = "f32" if table == "tiny_f32" else "bf16"
     T = 256 if table == "tiny_f32" else 49_152
-    cfg = N.config(w.vocab, w.eos_id, w.rows, dtype, max_tokens=T, mode=mode)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, dtype, max_tokens=T, mode=mode, nest_always=nest)
     if dtype == "f32":
         st = State(cfg, to_dev(synth.init_rows(w, 0, w.rows[0])), to_dev(synth.init_rows(w, 1, w.rows[1])))
     else:

@@ -39,15 +39,17 @@ def test_tiny_workload_two_windows(mode):
     assert N.device_status(cfg, ws) == 0
 
 
+@pytest.mark.parametrize("nest", [False, True])
 @pytest.mark.parametrize("mode,how", [("spread", "fused_last"), ("burst", "step"),
                                       ("burst", "fused_last"), ("spread", "step"),
                                       ("burst_ref", "step"), ("burst_ref", "fused_last")])
-def test_tiny_workload_fused_step(mode, how):
+def test_tiny_workload_fused_step(mode, how, nest):
     # the step fused into the reduction: the last micro-step (spread) or the
-    # whole window (burst); gradients are checked through the step results
+    # whole window (burst); gradients are checked through the step results;
+    # nest: with the nested sort, which windows this small skip by default
     w = workloads.TINY
     N = ng()
-    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode=mode)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=w.tokens_per_step, mode=mode, nest_always=nest)
     st = _tiny_state(cfg, w)
     ws = N.Workspace(cfg)
     for win in range(w.steps // w.accum_steps):
@@ -56,14 +58,15 @@ def test_tiny_workload_fused_step(mode, how):
     assert N.device_status(cfg, ws) == 0
 
 
+@pytest.mark.parametrize("nest", [False, True])
 @pytest.mark.parametrize("how", ["fused_last", "step"])
 @pytest.mark.parametrize("mode", ["spread", "burst", "burst_ref"])
-def test_shard_workload_fused(mode, how):
+def test_shard_workload_fused(mode, how, nest):
     w = workloads.COLLISION
     N = ng()
     rows = workloads.SHARD.rows
     T = 49_152
-    cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=T, mode=mode)
+    cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=T, mode=mode, nest_always=nest)
     st = State(cfg, device_table(rows[0], "bf16", 61), device_table(rows[1], "bf16", 62))
     ws = N.Workspace(cfg)
     for win in range(2):
@@ -74,11 +77,12 @@ def test_shard_workload_fused(mode, how):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("nest", [False, True])
 @pytest.mark.parametrize("T", [65, 129, 20_000])
-def test_single_hot_row_fused(T):
+def test_single_hot_row_fused(T, nest):
     w = workloads.TINY
     N = ng()
-    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T)
+    cfg = N.config(w.vocab, w.eos_id, w.rows, "f32", max_tokens=T, nest_always=nest)
     st = _tiny_state(cfg, w)
     ws = N.Workspace(cfg)
     tok = np.full(T, 42, np.int32)
@@ -334,7 +338,8 @@ def test_radix_tile_size_does_not_change_results(mode):
     # burst windows sort 4 x max_tokens keys per channel: from 2^20 keys on
     # the radix kernels take 4,096-key tiles, below it 2,048-key tiles.  The
     # sort is stable either way, so a ragged window stepped through both
-    # configurations must give the same bits.
+    # configurations must give the same bits (both with the nested sort,
+    # which windows below 2^20 keys take only when asked to).
     N = ng()
     w = workloads.FULL
     rows = (1 << 20, 1 << 20)
@@ -343,7 +348,7 @@ def test_radix_tile_size_does_not_change_results(mode):
                for m, T in enumerate(Ts)] for win in range(2)]
     states = []
     for max_tokens in (262144, 262143):   # 4 x 262,144 = 2^20 keys; 4 x 262,143 just below
-        cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=max_tokens, mode=mode)
+        cfg = N.config(w.vocab, w.eos_id, rows, "bf16", max_tokens=max_tokens, mode=mode, nest_always=True)
         st = State(cfg, device_table(rows[0], "bf16", 41), device_table(rows[1], "bf16", 42))
         ws = N.Workspace(cfg)
         for win in range(2):

@@ -24,7 +24,7 @@ W = workloads.TINY
 def _regular(N, cfg0, st, toks, dys, n, T, t):
     cfg = N.config(cfg0.vocab, cfg0.eos_id, (cfg0.rows[0], cfg0.rows[1]),
                    "f32" if cfg0.dtype == N.DTYPE_F32 else "bf16", max_tokens=T, accum_steps=n,
-                   mode="burst_ref")
+                   mode="burst_ref", nest_always=bool(cfg0.options & N.OPT_NEST_ALWAYS))
     ws = N.Workspace(cfg)
     for m in range(n - 1):
         N.embed_bwd_accum(cfg, ws, toks[m], dys[m])
@@ -34,10 +34,12 @@ def _regular(N, cfg0, st, toks, dys, n, T, t):
     assert N.device_status(cfg, ws) == 0
 
 
+@pytest.mark.parametrize("nest", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_noalloc_window_equals_the_regular_path(dtype):
+def test_noalloc_window_equals_the_regular_path(dtype, nest):
+    # nest: the nested sort and its run pieces in the fixed array too
     N = ng()
-    cfg = N.config(W.vocab, W.eos_id, W.rows, dtype, max_tokens=2048)   # mode etc. are not used
+    cfg = N.config(W.vocab, W.eos_id, W.rows, dtype, max_tokens=2048, nest_always=nest)   # mode etc. are not used
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     reg = State(cfg, to_dev(synth.init_rows(W, 0, W.rows[0])).to(tdt),
                 to_dev(synth.init_rows(W, 1, W.rows[1])).to(tdt))
