@@ -1423,17 +1423,21 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
     constexpr int kW = kFixThreads / kWave;
     __shared__ float4 s_part[kW][kDim / 4];
     __shared__ float s_ss[kW];
-    const int c = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
-    const uint32_t nown = a.hdr->n_owner[c];
-    const uint32_t n = count_of(a.n_dev[c], a.n_host);
-    const uint32_t *R = a.rows[c];
-    const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
+    // the records of both channels are shared out over all blocks of the grid
+    const uint32_t blk = blockIdx.x + blockIdx.y * gridDim.x, nblk = gridDim.x * gridDim.y;
+    const uint32_t nown0 = a.hdr->n_owner[0];
+    const uint32_t nown_all = nown0 + (gridDim.y > 1 ? a.hdr->n_owner[1] : 0u);
     bool sp_ok = true;
     const StepParams sp = MODE == kAccum ? a.f.p : step_params(a.f.p, a.f.p_dev, sp_ok);
-    for (uint32_t k = blockIdx.x; k < nown; k += gridDim.x) {
+    for (uint32_t u = blk; u < nown_all; u += nblk) {
+        const int c = u < nown0 ? 0 : 1;
+        const uint32_t k = u - (c ? nown0 : 0u);
+        const uint32_t n = count_of(a.n_dev[c], a.n_host);
+        const uint32_t *R = a.rows[c];
+        const float4 *P = reinterpret_cast<const float4 *>(a.partial + (size_t)c * a.nchunk * 2 * kDim);
         const uint64_t rec = a.owners[(size_t)c * a.nchunk + k];
         const int64_t chunk = (int64_t)(uint32_t)rec;
         const uint32_t info = (uint32_t)(rec >> 32);
@@ -1574,17 +1578,17 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
     }
     if constexpr (MODE != kAccum) {
         // Nested trigram runs that crossed the end of a walk, one per
-        // wavefront: the piece in slot 1 of the run's first chunk, then slot
-        // 0 of each following chunk whose first key continues the run, added
-        // in order; then the row's step.
-        if (c == 1 && a.nested) {
+        // wavefront of the grid: the piece in slot 1 of the run's first
+        // chunk, then slot 0 of each following chunk whose first key
+        // continues the run, added in order; then the row's step.
+        if (a.nested) {
             constexpr int ELT = MODE == kFuseBf16 ? 2 : 4;
             const uint32_t ntr = a.hdr->n_trun;
             const int64_t n0 = count_of(a.n_dev[0], a.n_host);
             const uint64_t table_t = (uint64_t)a.f.w[1] + (uint64_t)ELT * 4 * lane;
             const uint64_t state_t = (uint64_t)a.f.st[1];
             const uint64_t P = (uint64_t)a.tpart + 16 * lane;
-            for (uint32_t r = blockIdx.x * kW + w; r < ntr; r += gridDim.x * kW) {
+            for (uint32_t r = blk * kW + w; r < ntr; r += nblk * kW) {
                 const uint64_t rec = a.trec[r];
                 const int64_t x = (int64_t)(uint32_t)rec;
                 const uint32_t tv = (uint32_t)(rec >> 32);
