@@ -178,55 +178,113 @@ __device__ inline int32_t block_scan(int32_t x, int32_t *wsum, int32_t *total)
 }
 
 // One block: ranks the present ids (ascending) into cand[0, n), then fills
-// cand[n, C) with absent ids in permutation order.
+// cand[n, C) with absent ids in permutation order.  Both are ranks of 0/1
+// flags, so ids (then permutation places) are taken 16,384 at a time: a
+// thread loads the flags of its 16 places of that span (round r, place
+// r 1,024 + t) all at once, each wavefront's ballot gives the rank inside
+// its 64 lanes, and one block scan over the (round, wavefront) counts in
+// place order gives every group's offset.
+constexpr int kSelRounds = 16;
+constexpr int kSelWaves = kSelectThreads / 64;
+constexpr int32_t kSelSpan = kSelRounds * kSelectThreads;
+
+__device__ inline int32_t rank_in_wave(uint64_t m)
+{
+    const int lane = threadIdx.x & 63;
+    return __popcll(m & ((1ull << lane) - 1ull));
+}
+
 __global__ __launch_bounds__(kSelectThreads) void cand_select_kernel(const int32_t *perm, int32_t V,
                                                                       int32_t C, int32_t *rank,
                                                                       const int32_t *cnt, int32_t *cand,
                                                                       Hdr *h)
 {
+    static_assert(kSelRounds * kSelWaves <= kSelectThreads, "at most one scanned count per thread");
+    constexpr int kCounts = kSelRounds * kSelWaves;
     __shared__ int32_t wsum[kSelectThreads / 64 + 1];
+    __shared__ int32_t s_off[kSelRounds * kSelWaves];
     __shared__ int32_t s_bad;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     if (t == 0)
         s_bad = 0;
     for (int32_t c = t; c < C; c += kSelectThreads)
         cand[c] = 0;   // in range whatever follows
     __syncthreads();
 
-    int32_t base = 0;
-    for (int32_t v0 = 0; v0 < V; v0 += kSelectThreads) {
-        const int32_t v = v0 + t;
-        const int32_t pres = v < V ? rank[v] : 0;
-        if (v < V && cnt[v] != 1)
+    // present ids, ascending
+    int32_t n = 0;
+    for (int32_t v0 = 0; v0 < V; v0 += kSelSpan) {
+        uint8_t f[kSelRounds];
+        bool bad = false;
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const int32_t v = v0 + r * kSelectThreads + t;
+            f[r] = v < V ? (uint8_t)rank[v] : 0;
+            bad |= v < V && cnt[v] != 1;
+        }
+        if (bad)
             s_bad = 1;
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const uint64_t m = __ballot(f[r] != 0);
+            if (lane == 0)
+                s_off[r * kSelWaves + w] = __popcll(m);
+        }
+        __syncthreads();
         int32_t tot;
-        const int32_t r = base + block_scan(pres, wsum, &tot);
-        if (v < V) {
-            rank[v] = pres ? r : -1;
-            if (pres && r < C)
-                cand[r] = v;
-        }
-        base += tot;
-    }
-    const int32_t n = base;
-    __syncthreads();   // ranks visible to the whole block
-    if (n < C) {
-        int32_t filled = 0;
-        for (int32_t j0 = 0; j0 < V && filled < C - n; j0 += kSelectThreads) {
-            const int32_t j = j0 + t;
-            int32_t p = -1;
-            if (j < V) {
-                p = perm[j];
-                if ((uint32_t)p >= (uint32_t)V)
-                    p = -1;
+        const int32_t off = block_scan(t < kCounts ? s_off[t] : 0, wsum, &tot);
+        if (t < kCounts)
+            s_off[t] = off;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const int32_t v = v0 + r * kSelectThreads + t;
+            const uint64_t m = __ballot(f[r] != 0);
+            const int32_t rk = n + s_off[r * kSelWaves + w] + rank_in_wave(m);
+            if (v < V) {
+                rank[v] = f[r] ? rk : -1;
+                if (f[r] && rk < C)
+                    cand[rk] = v;
             }
-            const int32_t absent = (p >= 0 && rank[p] < 0) ? 1 : 0;
-            int32_t tot;
-            const int32_t pos = filled + block_scan(absent, wsum, &tot);
-            if (absent && pos < C - n)
-                cand[n + pos] = p;
-            filled += tot;
         }
+        n += tot;
+        __syncthreads();   // s_off is reused
+    }
+    __syncthreads();   // ranks visible to the whole block
+    // absent ids in permutation order
+    int32_t filled = 0;
+    for (int32_t j0 = 0; j0 < V && n + filled < C; j0 += kSelSpan) {
+        int32_t p[kSelRounds];
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const int32_t j = j0 + r * kSelectThreads + t;
+            p[r] = j < V ? perm[j] : -1;
+        }
+        uint8_t f[kSelRounds];
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r)
+            f[r] = ((uint32_t)p[r] < (uint32_t)V && rank[p[r]] < 0) ? 1 : 0;
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const uint64_t m = __ballot(f[r] != 0);
+            if (lane == 0)
+                s_off[r * kSelWaves + w] = __popcll(m);
+        }
+        __syncthreads();
+        int32_t tot;
+        const int32_t off = block_scan(t < kCounts ? s_off[t] : 0, wsum, &tot);
+        if (t < kCounts)
+            s_off[t] = off;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+            const uint64_t m = __ballot(f[r] != 0);
+            const int32_t pos = filled + s_off[r * kSelWaves + w] + rank_in_wave(m);
+            if (f[r] && n + pos < C)
+                cand[n + pos] = p[r];
+        }
+        filled += tot;
+        __syncthreads();   // s_off is reused
     }
     if (t == 0) {
         h->n_present = (uint32_t)n;
@@ -912,23 +970,42 @@ __global__ void dw_reduce_kernel(const float *dwp, int parts, int64_t Cp, const 
 // Folds the per-tile sums of each position: lse = M + log sum_t s_t e^(m_t - M).
 // (Tile 0 has a finite maximum, its first column being a candidate; a later
 // tile wholly past C is (-inf, 0) and adds exp(-inf) * 0 = 0.)
+// Four adjacent lanes per position: lane q folds column tiles q, q + 4, ...
+// (one pass, rescaling the running sum whenever the running maximum grows),
+// then the four partial (max, sum) pairs meet by shuffles in a fixed order.
+constexpr int kLseLanes = 4;
 __global__ void lse_kernel(const float2 *part, int64_t T, int nct, const int32_t *slot, int32_t C,
                            const float *zt, float *loss, float *lse, Hdr *h)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= T)
-        return;
-    // one pass, rescaling the running sum whenever the running maximum grows
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = g / kLseLanes;
+    const int q = (int)(g % kLseLanes);
     float M = -INFINITY, S = 0.f;
-    for (int c = 0; c < nct; ++c) {
-        const float2 p = part[(int64_t)c * T + i];
-        if (p.x > M) {
-            S = S * expf(M - p.x) + p.y;
-            M = p.x;
-        } else {
-            S += p.y * expf(p.x - M);
+    if (i < T) {
+        for (int c = q; c < nct; c += kLseLanes) {
+            const float2 p = part[(int64_t)c * T + i];
+            if (p.y == 0.f)
+                continue;   // a column tile wholly past C: (-inf, 0)
+            if (p.x > M) {
+                S = S * expf(M - p.x) + p.y;
+                M = p.x;
+            } else {
+                S += p.y * expf(p.x - M);
+            }
         }
     }
+#pragma unroll
+    for (int d = 1; d < kLseLanes; d <<= 1) {
+        const float Mo = __shfl_xor(M, d, 64), So = __shfl_xor(S, d, 64);
+        // the lower lane's pair first, so both lanes compute the same bits
+        const bool low = (q & d) == 0;
+        const float Ma = low ? M : Mo, Sa = low ? S : So, Mb = low ? Mo : M, Sb = low ? So : S;
+        const float Mn = fmaxf(Ma, Mb);
+        S = (Sa != 0.f ? Sa * expf(Ma - Mn) : 0.f) + (Sb != 0.f ? Sb * expf(Mb - Mn) : 0.f);
+        M = Mn;
+    }
+    if (i >= T || q != 0)
+        return;
     const float l = M + logf(S);
     const int32_t y = slot[i];
     const bool ok = (uint32_t)y < (uint32_t)C;
@@ -1144,7 +1221,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.tiles_n = (uint32_t)nct;
     launch(SSM_PROF_FWD, true, true, gemm_kernel<EPI_FWD, 2, kFwdWN, kFwdBK, kFwdS>, dim3(grid_blocks(a.tiles_m, a.tiles_n)),
            dim3(256), s, a);
-    launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T, 256)), dim3(256), s,
+    launch(SSM_PROF_LSE, true, true, lse_kernel, dim3(blocks(T * kLseLanes, 256)), dim3(256), s,
            (const float2 *)a.part, T, nct, slot, C, (const float *)a.zt, loss, lse, h);
     return done(hipGetLastError());
 }

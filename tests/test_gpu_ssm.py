@@ -185,7 +185,10 @@ def _check_fwd(X, W, cand_o, slot_o, loss, lse, C, rows=None):
     assert np.all(np.abs(s_g - loss_o) <= tl + tz), np.max(np.abs(s_g - loss_o) / (tl + tz))
 
 
-@pytest.mark.parametrize("T,C", [(1, 1), (1, 300), (77, 128), (300, 1000), (1000, 1290), (2000, 2999)])
+# C in (128, 192]: the second 192-column tile lies wholly past C (its partial
+# sums are (-inf, 0) and the lse fold skips them)
+@pytest.mark.parametrize("T,C", [(1, 1), (1, 300), (77, 128), (77, 150), (130, 192), (300, 1000), (1000, 1290),
+                                 (2000, 2999)])
 def test_forward_matches_oracle(T, C):
     N = S()
     tgt, X, W, perm, _ = _inputs(100 + T, T, V_SMALL)
@@ -221,7 +224,7 @@ def _check_bwd(X, W, cand_o, slot_o, g, dX, dW, dW0, C):
     assert np.array_equal(got[rest], dW0[rest].astype(np.float64))   # untouched rows
 
 
-@pytest.mark.parametrize("T,C", [(1, 1), (5, 300), (77, 128), (300, 1000), (1000, 1290), (2000, 2999)])
+@pytest.mark.parametrize("T,C", [(1, 1), (5, 300), (77, 128), (77, 150), (300, 1000), (1000, 1290), (2000, 2999)])
 def test_backward_matches_oracle(T, C):
     N = S()
     tgt, X, W, perm, g = _inputs(200 + T, T, V_SMALL)
