@@ -45,7 +45,6 @@ constexpr int kMaxSplit = 4;                                 // dW: most parts o
 
 constexpr uint32_t kMagic = 0x53534d31u;
 constexpr uint64_t kAlign = 256;
-constexpr int kSelectThreads = 1024;
 
 struct Hdr {
     uint32_t magic;
@@ -59,7 +58,7 @@ static_assert(sizeof(Hdr) == 256, "header is 256 bytes");
 
 struct Layout {
     int64_t Tp, Cp;   // padded maxima
-    uint64_t hdr, rank, cnt, zt, part, xt, wst, dz, zb, dwp, total;
+    uint64_t hdr, rank, cnt, blk, absent, zt, part, xt, wst, dz, zb, dwp, total;
 };
 
 inline int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -78,6 +77,11 @@ Layout layout(const ssm_config *c)
     L.hdr = take(sizeof(Hdr));
     L.rank = take(4ull * c->vocab);
     L.cnt = take(4ull * c->vocab);
+    {
+        const uint64_t nbs = (c->vocab + 1023) / 1024;   // blocks of the candidate ranking
+        L.blk = take(4ull * 2 * nbs);
+        L.absent = take(4ull * 32 * nbs);
+    }
     L.zt = take(4ull * L.Tp);
     L.part = take(8ull * L.Tp * (L.Cp / kTile));
     L.xt = take(2ull * kD * L.Tp);
@@ -146,47 +150,14 @@ __global__ void cand_mark_kernel(const int32_t *tgt, int64_t T, const int32_t *p
     }
 }
 
-// Exclusive scan of one value per thread over the block; returns the
-// exclusive prefix and writes the block total to *total (all threads).
-__device__ inline int32_t block_scan(int32_t x, int32_t *wsum, int32_t *total)
-{
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int32_t v = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(v, d, 64);
-        if (lane >= d)
-            v += o;
-    }
-    if (lane == 63)
-        wsum[w] = v;
-    __syncthreads();
-    if (t == 0) {
-        int32_t s = 0;
-        for (int k = 0; k < kSelectThreads / 64; ++k) {
-            const int32_t e = wsum[k];
-            wsum[k] = s;
-            s += e;
-        }
-        wsum[kSelectThreads / 64] = s;
-    }
-    __syncthreads();
-    const int32_t r = wsum[w] + v - x;
-    *total = wsum[kSelectThreads / 64];
-    __syncthreads();
-    return r;
-}
-
-// One block: ranks the present ids (ascending) into cand[0, n), then fills
-// cand[n, C) with absent ids in permutation order.  Both are ranks of 0/1
-// flags, so ids (then permutation places) are taken 16,384 at a time: a
-// thread loads the flags of its 16 places of that span (round r, place
-// r 1,024 + t) all at once, each wavefront's ballot gives the rank inside
-// its 64 lanes, and one block scan over the (round, wavefront) counts in
-// place order gives every group's offset.
-constexpr int kSelRounds = 16;
-constexpr int kSelWaves = kSelectThreads / 64;
-constexpr int32_t kSelSpan = kSelRounds * kSelectThreads;
+// The candidate order, over blocks of 1,024 ids (and of 1,024 places of the
+// permutation): present ids ascending into cand[0, n), then absent ids in
+// permutation order into cand[n, C).  Both are ranks of 0/1 flags:
+// cand_count_kernel counts each block's flags (and keeps the absent flags
+// of its permutation places as bits), cand_rank_kernel adds the counts of
+// the blocks before its own and ranks its flags by wavefront ballots.
+constexpr int kSelBlock = 1024;
+constexpr int kSelWaves = kSelBlock / 64;
 
 __device__ inline int32_t rank_in_wave(uint64_t m)
 {
@@ -194,107 +165,103 @@ __device__ inline int32_t rank_in_wave(uint64_t m)
     return __popcll(m & ((1ull << lane) - 1ull));
 }
 
-__global__ __launch_bounds__(kSelectThreads) void cand_select_kernel(const int32_t *perm, int32_t V,
-                                                                      int32_t C, int32_t *rank,
-                                                                      const int32_t *cnt, int32_t *cand,
-                                                                      Hdr *h)
+// rank[] still holds the presence marks (0 / 1) here.  Also prefills cand
+// (in range whatever follows) and flags a permutation in which some id does
+// not occur exactly once.
+__global__ __launch_bounds__(kSelBlock) void cand_count_kernel(const int32_t *perm, int32_t V, int32_t C,
+                                                                const int32_t *rank, const int32_t *cnt,
+                                                                int32_t *cand, int32_t *blk, uint32_t *absent,
+                                                                int32_t nbs, Hdr *h)
 {
-    static_assert(kSelRounds * kSelWaves <= kSelectThreads, "at most one scanned count per thread");
-    constexpr int kCounts = kSelRounds * kSelWaves;
-    __shared__ int32_t wsum[kSelectThreads / 64 + 1];
-    __shared__ int32_t s_off[kSelRounds * kSelWaves];
-    __shared__ int32_t s_bad;
+    __shared__ int32_t s_c[2][kSelWaves];
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    if (t == 0)
-        s_bad = 0;
-    for (int32_t c = t; c < C; c += kSelectThreads)
-        cand[c] = 0;   // in range whatever follows
+    const int32_t b = blockIdx.x;
+    for (int64_t c = (int64_t)b * kSelBlock + t; c < C; c += (int64_t)gridDim.x * kSelBlock)
+        cand[c] = 0;
+    const int32_t v = b * kSelBlock + t;
+    const bool pres = v < V && rank[v] != 0;
+    if (v < V && cnt[v] != 1) {
+        atomicOr(&h->flags, SSM_FLAG_BAD_PERM);
+        atomicOr(&h->void_batch, 1u);
+    }
+    const int32_t p = v < V ? perm[v] : -1;
+    const bool ab = (uint32_t)p < (uint32_t)V && rank[p] == 0;
+    const uint64_t mp = __ballot(pres), ma = __ballot(ab);
+    if (lane == 0) {
+        s_c[0][w] = __popcll(mp);
+        s_c[1][w] = __popcll(ma);
+        absent[(int64_t)b * 2 * kSelWaves + 2 * w] = (uint32_t)ma;
+        absent[(int64_t)b * 2 * kSelWaves + 2 * w + 1] = (uint32_t)(ma >> 32);
+    }
     __syncthreads();
+    if (t < 2) {
+        int32_t sum = 0;
+        for (int k = 0; k < kSelWaves; ++k)
+            sum += s_c[t][k];
+        blk[(int64_t)t * nbs + b] = sum;
+    }
+}
 
-    // present ids, ascending
-    int32_t n = 0;
-    for (int32_t v0 = 0; v0 < V; v0 += kSelSpan) {
-        uint8_t f[kSelRounds];
-        bool bad = false;
-#pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const int32_t v = v0 + r * kSelectThreads + t;
-            f[r] = v < V ? (uint8_t)rank[v] : 0;
-            bad |= v < V && cnt[v] != 1;
-        }
-        if (bad)
-            s_bad = 1;
-#pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const uint64_t m = __ballot(f[r] != 0);
-            if (lane == 0)
-                s_off[r * kSelWaves + w] = __popcll(m);
-        }
-        __syncthreads();
-        int32_t tot;
-        const int32_t off = block_scan(t < kCounts ? s_off[t] : 0, wsum, &tot);
-        if (t < kCounts)
-            s_off[t] = off;
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const int32_t v = v0 + r * kSelectThreads + t;
-            const uint64_t m = __ballot(f[r] != 0);
-            const int32_t rk = n + s_off[r * kSelWaves + w] + rank_in_wave(m);
-            if (v < V) {
-                rank[v] = f[r] ? rk : -1;
-                if (f[r] && rk < C)
-                    cand[rk] = v;
-            }
-        }
-        n += tot;
-        __syncthreads();   // s_off is reused
+__global__ __launch_bounds__(kSelBlock) void cand_rank_kernel(const int32_t *perm, int32_t V, int32_t C,
+                                                               int32_t *rank, int32_t *cand, const int32_t *blk,
+                                                               const uint32_t *absent, int32_t nbs, Hdr *h)
+{
+    __shared__ int32_t s_red[4][kSelWaves];
+    __shared__ int32_t s_w[2][kSelWaves];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int32_t b = blockIdx.x;
+    // counts of the blocks before this one, and of all blocks
+    int32_t pre0 = 0, pre1 = 0, tot0 = 0, tot1 = 0;
+    for (int32_t k = t; k < nbs; k += kSelBlock) {
+        const int32_t c0 = blk[k], c1 = blk[(int64_t)nbs + k];
+        tot0 += c0;
+        tot1 += c1;
+        pre0 += k < b ? c0 : 0;
+        pre1 += k < b ? c1 : 0;
     }
-    __syncthreads();   // ranks visible to the whole block
-    // absent ids in permutation order
-    int32_t filled = 0;
-    for (int32_t j0 = 0; j0 < V && n + filled < C; j0 += kSelSpan) {
-        int32_t p[kSelRounds];
+    int32_t r4[4] = {pre0, pre1, tot0, tot1};
 #pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const int32_t j = j0 + r * kSelectThreads + t;
-            p[r] = j < V ? perm[j] : -1;
-        }
-        uint8_t f[kSelRounds];
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int r = 0; r < kSelRounds; ++r)
-            f[r] = ((uint32_t)p[r] < (uint32_t)V && rank[p[r]] < 0) ? 1 : 0;
-#pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const uint64_t m = __ballot(f[r] != 0);
-            if (lane == 0)
-                s_off[r * kSelWaves + w] = __popcll(m);
-        }
-        __syncthreads();
-        int32_t tot;
-        const int32_t off = block_scan(t < kCounts ? s_off[t] : 0, wsum, &tot);
-        if (t < kCounts)
-            s_off[t] = off;
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < kSelRounds; ++r) {
-            const uint64_t m = __ballot(f[r] != 0);
-            const int32_t pos = filled + s_off[r * kSelWaves + w] + rank_in_wave(m);
-            if (f[r] && n + pos < C)
-                cand[n + pos] = p[r];
-        }
-        filled += tot;
-        __syncthreads();   // s_off is reused
+        for (int d = 32; d >= 1; d >>= 1)
+            r4[q] += __shfl_xor(r4[q], d, 64);
+        if (lane == 0)
+            s_red[q][w] = r4[q];
     }
-    if (t == 0) {
+    const int32_t v = b * kSelBlock + t;
+    const bool pres = v < V && rank[v] != 0;
+    const uint64_t mp = __ballot(pres);
+    const uint64_t ma = (uint64_t)absent[(int64_t)b * 2 * kSelWaves + 2 * w] |
+                        ((uint64_t)absent[(int64_t)b * 2 * kSelWaves + 2 * w + 1] << 32);
+    const bool ab = (ma >> lane) & 1ull;
+    if (lane == 0) {
+        s_w[0][w] = __popcll(mp);
+        s_w[1][w] = __popcll(ma);
+    }
+    __syncthreads();
+    int32_t base[4] = {0, 0, 0, 0}, woff0 = 0, woff1 = 0;
+#pragma unroll
+    for (int k = 0; k < kSelWaves; ++k) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            base[q] += s_red[q][k];
+        woff0 += k < w ? s_w[0][k] : 0;
+        woff1 += k < w ? s_w[1][k] : 0;
+    }
+    const int32_t n = base[2];   // present ids in all
+    if (v < V) {
+        const int32_t r = base[0] + woff0 + rank_in_wave(mp);
+        rank[v] = pres ? r : -1;
+        if (pres && r < C)
+            cand[r] = v;
+        const int32_t pos = base[1] + woff1 + rank_in_wave(ma);
+        if (ab && n + pos < C)
+            cand[n + pos] = perm[v];
+    }
+    if (b == 0 && t == 0) {
         h->n_present = (uint32_t)n;
-        uint32_t f = 0;
-        if (n > C)
-            f |= SSM_FLAG_OVERFLOW;
-        if (s_bad)
-            f |= SSM_FLAG_BAD_PERM;
-        if (f) {
-            atomicOr(&h->flags, f);
+        if (n > C) {
+            atomicOr(&h->flags, SSM_FLAG_OVERFLOW);
             atomicOr(&h->void_batch, 1u);
         }
     }
@@ -1163,8 +1130,13 @@ int ssm_candidates(const ssm_config *cfg, void *ws, const int32_t *targets, int6
     launch(SSM_PROF_CAND, true, false, cand_clear_kernel, dim3(blocks(V, 256)), dim3(256), s, rank, cnt, V, h);
     launch(SSM_PROF_CAND, false, false, cand_mark_kernel, dim3(blocks(T > V ? T : V, 256)), dim3(256), s,
            targets, T, perm, V, rank, cnt, h);
-    launch(SSM_PROF_CAND, false, false, cand_select_kernel, dim3(1), dim3(kSelectThreads), s, perm, V, C,
-           rank, (const int32_t *)cnt, cand, h);
+    const int32_t nbs = (int32_t)blocks(V, kSelBlock);
+    int32_t *blk = reinterpret_cast<int32_t *>(w + L.blk);
+    uint32_t *absent = reinterpret_cast<uint32_t *>(w + L.absent);
+    launch(SSM_PROF_CAND, false, false, cand_count_kernel, dim3(nbs), dim3(kSelBlock), s, perm, V, C,
+           (const int32_t *)rank, (const int32_t *)cnt, cand, blk, absent, nbs, h);
+    launch(SSM_PROF_CAND, false, false, cand_rank_kernel, dim3(nbs), dim3(kSelBlock), s, perm, V, C, rank, cand,
+           (const int32_t *)blk, (const uint32_t *)absent, nbs, h);
     launch(SSM_PROF_CAND, false, true, cand_slot_kernel, dim3(blocks(T, 256)), dim3(256), s, targets, T, V,
            C, (const int32_t *)rank, slot);
     return done(hipGetLastError());
