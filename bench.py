@@ -246,10 +246,37 @@ def algorithmic_bytes(T, stats, row_bytes, mode, path, dy_row=768 * 4, radix_pas
     return {"min": mn, "kernel": kn}
 
 
+def code_text(src: str) -> str:
+    """A C++ source's code alone: comments dropped, runs of whitespace made
+    one space, so that a comment edit does not read as a kernel change.
+    String and character literals are kept as written."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def src_hash(name):
+    """Hash of a kernel source's code (comments and layout ignored): the key
+    of its PMC summaries."""
     p = os.path.join(ROOT, "sparse_hashed_gram_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(p, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def pmc_traffic(group, workload_key, mode, dy_dtype):

@@ -357,7 +357,7 @@ struct SlotArgs {
     uint32_t wrows;
     WsHeader *hdr;
     bool fused;             // the reduction is fused with the step
-    uint32_t *tinfo;        // singleton map, per dY row code
+    uint32_t *tinfo;        // singleton map: per dY row code, or (nested sort) per index in the trigram order
     uint32_t *split_rows;   // compacted trigram keys, payloads and head info
     uint32_t *split_vals;
     uint32_t *split_info;
@@ -725,7 +725,7 @@ struct RedArgs {
     float *gpart;           // [2][ngroup][768]: sums of groups of kGroup chunks inside one segment
     int64_t ngroup;
     WsHeader *hdr;
-    const uint32_t *tinfo;  // singleton map per dY row code
+    const uint32_t *tinfo;  // singleton map (see SlotArgs)
     bool nested;            // the map also names nested trigram rows of several keys (kMultiKey)
     const uint32_t *tix0;   // nested: per sorted bigram key, its index in the trigram order
                             // (the singleton map's index); else the map is indexed by row code
@@ -1130,8 +1130,8 @@ __device__ __forceinline__ void step_one(const float4 (&g)[kQ], const WRow<ELT> 
 
 // With the singleton split, the bigram pass (channel 0) also steps, for every
 // key it reads, the trigram row of that key's position when tinfo marks it a
-// singleton: its gradient is s_t dY of this very row of dY.  The trigram pass
-// then only walks the keys the split kept.
+// singleton (its gradient is s_t dY of this very row of dY) or the end of a
+// nested run; the trigram pass then only walks the keys the split kept.
 // Four consecutive dY elements of one lane: raw bits as loaded (16 bytes of
 // fp32 or 8 bytes of bf16), widened where they are used.
 template <int DYE>

@@ -148,3 +148,15 @@ def test_gpus_above_one_exit_with_a_message(capsys, monkeypatch):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_kernel_code_hash_ignores_comments_only():
+    # the PMC summaries are keyed by the kernel source's code: a comment or
+    # layout edit keeps the key, any change to the code itself does not
+    src = 'int f() { return 1; } // one\n/* block\n comment */ const char *s = "a // b";\n'
+    assert bench.code_text(src) == 'int f() { return 1; } const char *s = "a // b";'
+    assert bench.code_text(src.replace("// one", "// two")) == bench.code_text(src)
+    assert bench.code_text(src.replace("return 1", "return 2")) != bench.code_text(src)
+    assert bench.code_text("char c = '\\''; // x") == "char c = '\\'';"
+    h = bench.src_hash("ngram_reduce.hip")
+    assert len(h) == 16 and int(h, 16) >= 0
