@@ -149,6 +149,8 @@ WsLayout layout(const ngram_config *c, bool one_shot = false)
     L.nest_always = (c->options & NGRAM_OPT_NEST_ALWAYS) != 0;
     L.bidx = o;
     o = up(o + (L.nested ? 4ull * (uint64_t)L.code_cap : 0));
+    L.btro = o;
+    o = up(o + (L.nested ? 4ull * (uint64_t)L.nk : 0));
     for (int k = 0; k < 2; ++k) {
         L.tix[k] = o;
         o = up(o + (L.nested ? 4ull * (uint64_t)L.nk : 0));

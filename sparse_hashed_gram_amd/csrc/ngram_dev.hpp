@@ -329,6 +329,8 @@ struct WsLayout {
                             // trigram order, carried through the bigram passes
     uint64_t bidx;          // uint32 [code_cap]: per dY row code, its packed bigram index
                             // (nested sort: the bigram keys are gathered in trigram order)
+    uint64_t btro;          // uint32 [nk] (nested sort): the bigram row of each key in the
+                            // trigram order, as gathered for the bigram sort
     uint64_t tpart;         // fp32 [nchunk][2][768] (nested sort): pieces of nested trigram
                             // runs that cross the end of a chunk's walk (slot 0: the piece
                             // at the walk's start, slot 1: the piece at its end)

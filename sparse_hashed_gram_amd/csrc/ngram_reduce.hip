@@ -115,11 +115,13 @@ __global__ __launch_bounds__(kSortThreads) void keys_tile_kernel(
 // row code of each sorted trigram payload names its position's bigram
 // index), fused with the first bigram pass's digit counts.  A stable sort of
 // this sequence by bigram row gives the (bigram row, trigram row, position)
-// order.
+// order.  The rows are also kept in this order (btro), where mark_kernel
+// compares the bigram rows of consecutive trigram keys.
 template <int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void gather_bigram_kernel(
     const uint32_t *__restrict__ vt, const uint32_t *__restrict__ bidx, const uint32_t *n_dev, uint32_t n_host,
-    uint32_t *__restrict__ keys0, uint32_t *__restrict__ vals0, uint32_t *__restrict__ hist, uint32_t nblk)
+    uint32_t *__restrict__ keys0, uint32_t *__restrict__ vals0, uint32_t *__restrict__ hist, uint32_t nblk,
+    uint32_t *__restrict__ btro)
 {
     __shared__ uint32_t h[kRadix];
     const int tid = threadIdx.x;
@@ -136,6 +138,7 @@ __global__ __launch_bounds__(kSortThreads) void gather_bigram_kernel(
             const uint32_t code = vt[i] & 0x7FFFFFFFu;
             const uint32_t ib = bidx[code];
             keys0[i] = ib & 0x7FFFFFFFu;
+            btro[i] = ib & 0x7FFFFFFFu;
             vals0[i] = code | (ib & 0x80000000u);
             atomicAdd(&h[ib & (kRadix - 1)], 1u);
         }
@@ -362,7 +365,7 @@ struct SlotArgs {
     uint32_t *split_vals;
     uint32_t *split_info;
     bool nested;            // fused + nested sort: trigram rows nested in one bigram segment
-    const uint32_t *bidx;   // nested: packed bigram index per row code
+    const uint32_t *btro;   // nested: bigram row of each key in the trigram order
     uint8_t *tkept;         // nested: per sorted trigram key, kept for the trigram pass
 };
 
@@ -434,7 +437,7 @@ __device__ __forceinline__ int block_incl_max(int v, int *s_wave, int *excl)
 // Nested sort, trigram channel: decides which trigram rows the bigram pass
 // completes.  A row qualifies if its keys lie in this tile of the trigram
 // order (its head here, its end here), it is new to the window, and all its
-// keys have the same bigram row (compared key to key through bidx).  Its
+// keys have the same bigram row (compared key to key in btro).  Its
 // keys get their records in the singleton map and are dropped from the
 // trigram pass; every other key keeps kNotSingle and is kept.  The trigram
 // order lists a row's keys by position, as the bigram order lists the run,
@@ -509,10 +512,10 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
             const uint32_t i = i0 + j;
             vq[j] = i < n ? V[i] : 0u;
             const bool multi = i < n && ((headm & endm) & (1u << j)) == 0;
-            bq[j] = multi ? a.bidx[vq[j] & 0x7FFFFFFFu] & 0x7FFFFFFFu : 0u;
+            bq[j] = multi ? a.btro[i] : 0u;
         }
         if (i0 < n && !(headm & 1u) && carry >= 0)
-            b_prev = a.bidx[V[i0 - 1] & 0x7FFFFFFFu] & 0x7FFFFFFFu;
+            b_prev = a.btro[i0 - 1];
         int hl[kSortItems];
         int run = carry;
 #pragma unroll
@@ -1689,7 +1692,7 @@ SlotArgs slot_args(const WsLayout &L, uint8_t *ws, const uint32_t *n_dev, uint32
     sa.split_vals = spare_v + L.nk;
     sa.split_info = spare_k;
     sa.nested = nested_sort(L, n_host, fused);
-    sa.bidx = reinterpret_cast<const uint32_t *>(ws + L.bidx);
+    sa.btro = reinterpret_cast<const uint32_t *>(ws + L.btro);
     sa.tkept = reinterpret_cast<uint8_t *>(ws + L.tkept);
     return sa;
 }
@@ -1784,7 +1787,8 @@ void sort_part(const WsLayout &L, uint8_t *ws, const HashParams &hp, const int32
         radix_passes(L, ws, n_dev, n_host, big, nrb, 1, 1, false, s);
         const uint32_t *vt = reinterpret_cast<const uint32_t *>(ws + L.vals[L.passes & 1]) + L.nk;
         (big ? gather_bigram_kernel<kRadixItemsBig> : gather_bigram_kernel<kRadixItemsSmall>)
-            <<<nrb, kSortThreads, 0, s>>>(vt, bidx, n_dev, n_host, k0, v0, hist, nrb);
+            <<<nrb, kSortThreads, 0, s>>>(vt, bidx, n_dev, n_host, k0, v0, hist, nrb,
+                                          reinterpret_cast<uint32_t *>(ws + L.btro));
         radix_passes(L, ws, n_dev, n_host, big, nrb, 0, 1, true, s);
     }
     const SlotArgs sa = slot_args(L, ws, n_dev, n_host, fused);

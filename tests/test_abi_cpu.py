@@ -149,6 +149,23 @@ def test_host_rejections_enqueue_nothing(N):
     assert L.ngram_embed_fwd(cp, fake, fake, fake, 5, fake, None, None) == -3
 
 
+@pytest.mark.parametrize("n_micro,T", [(1, 65_536), (64, 1_024), (63, 1_025), (3, 16_385), (4, 16_384)])
+@pytest.mark.parametrize("dy_dtype", ["f32", "bf16"])
+def test_noalloc_largest_windows_fit(N, n_micro, T, dy_dtype):
+    # every window the allocation-free call accepts fits its fixed array:
+    # the largest ones (65,536 positions, or the widest dY-row codes) on the
+    # full-size tables with the nested sort pass every size check and reach
+    # the first HIP call, which fails here, where no GPU is visible
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake pointers: only where no GPU is visible")
+    c = _good(N, rows=(42_300_000, 42_300_000), dtype="bf16", max_tokens=T, dy_dtype=dy_dtype, nest_always=True)
+    fake = ctypes.c_void_p(1 << 40)
+    rc = N.lib().ngram_window_step_noalloc(ctypes.byref(c), fake, fake, T, n_micro, fake, fake, fake, fake, 1,
+                                           0.01, 0.95, 1e-8, None, None)
+    assert rc == -6
+
+
 def test_noalloc_window_host_rejections(N):
     # the allocation-free window step checks every size and pointer before
     # any HIP call (sizes beyond its fixed array are refused, not truncated)
