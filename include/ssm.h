@@ -24,7 +24,10 @@
  * fill order above; no bias, scale, cap or sampling correction on the logits;
  * a per-position upstream gradient g (1/T for a mean loss).  Precision: X and
  * W are bf16; the three contractions run on bf16 matrix cores with fp32
- * accumulation; dz is rounded to bf16 (nearest even) before the two backward
+ * accumulation; between the forward and the backward each logit is kept as
+ * exp(z - M) in fp16 (nearest even; M the largest logit of its row among
+ * the 192 candidates of its forward tile, so the kept value lies in (0, 1]);
+ * dz is rounded to bf16 (nearest even) before the two backward
  * contractions; lse, loss, dX and dW are fp32.
  *
  * Conventions: device pointers unless marked "host"; the caller owns every
@@ -87,10 +90,10 @@ typedef struct ssm_config {
 int ssm_abi_version(void);
 const char *ssm_status_string(int status);
 
-/* Workspace size for cfg (host).  About 4 (T+128)(C+128) bytes for the
- * forward's fp32 logits, 2 (T+128)(C+128) for dz, 16 D (C+128) for dW's
+/* Workspace size for cfg (host).  About 2 (T+128)(C+128) bytes for what the
+ * forward keeps of its logits, 2 (T+128)(C+128) for dz, 16 D (C+128) for dW's
  * split parts, plus 2 D (T + C + 256) bytes of transposed operands and
- * 8 T C/128 bytes of per-tile sums (about 3.1 GB at T = 49,152,
+ * 8 T C/128 bytes of per-tile sums (about 2.3 GB at T = 49,152,
  * C = 10,240). */
 int ssm_workspace_bytes(const ssm_config *cfg, uint64_t *bytes);
 
@@ -112,8 +115,9 @@ int ssm_candidates(const ssm_config *cfg, void *ws, const int32_t *targets, int6
 
 /* Forward: loss and lse (fp32 [T] each) of every position over the
  * candidate set.  X: bf16 [T][768]; W: bf16 [V][768] (the lm_head);
- * cand, slot as from ssm_candidates.  The fp32 logits stay in the workspace
- * for ssm_loss_bwd.  T = 0 enqueues nothing. */
+ * cand, slot as from ssm_candidates.  The logits, kept as fp16 exp(z - M)
+ * (see Precision above), stay in the workspace for ssm_loss_bwd.  T = 0
+ * enqueues nothing. */
 int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W,
                  const int32_t *cand, const int32_t *slot, int64_t T, float *loss,
                  float *lse, void *stream);

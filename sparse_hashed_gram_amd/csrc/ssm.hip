@@ -87,7 +87,7 @@ Layout layout(const ssm_config *c)
     L.xt = take(2ull * kD * L.Tp);
     L.wst = take(2ull * kD * L.Cp);
     L.dz = take(2ull * L.Tp * L.Cp);
-    L.zb = take(4ull * L.Tp * L.Cp);
+    L.zb = take(2ull * L.Tp * L.Cp);
     L.dwp = take(4ull * kMaxSplit * L.Cp * kD);
     L.total = o;
     return L;
@@ -596,7 +596,7 @@ struct GemmArgs {
     const float *g;        // [T]
     float *zt;             // forward: target logits [T]
     float2 *part;          // forward: per-tile (max, sum exp) [column tiles][T]
-    float *zb;             // forward -> dz: fp32 logits, one 64 KB block per 128 x 128 tile
+    uint16_t *zb;          // forward -> dz: fp16 exp(z - M) per logit, fragment-major (below)
     uint16_t *dz;          // [Tq][Cp] bf16
     int64_t Tq, Cp;
     uint32_t tiles_m, tiles_n;   // output tiles
@@ -608,42 +608,74 @@ struct GemmArgs {
 
 constexpr uint32_t cmax(uint32_t x, uint32_t y) { return x > y ? x : y; }
 
-// Logits buffer, fragment-major: the 32 x 32 matrix-core tile of rows
-// 32 R .. and columns 32 Cb .. is 4 KB at float4 (R Cp/32 + Cb) 256, holding
-// the accumulators as a wavefront has them: entry 4 g + j of lane l at float4
-// g 64 + l.  So any block tiling can store or reload its fragments, each
+// What the forward keeps of each logit z for the dz kernel: q = exp(z - M)
+// in fp16 (round to nearest), M the largest logit of its row among the
+// candidates of its forward column tile (the tile's per-row maximum, kept in
+// part).  q lies in (0, 1], where fp16 holds it to 2^-11 relative (2^-25
+// absolute below 2^-14); dz then needs only exp(M - lse) per row and tile.
+// Buffer, fragment-major: the 32 x 32 matrix-core tile of rows 32 R .. and
+// columns 32 Cb .. is 2 KB at 16-byte unit (R Cp/32 + Cb) 128, holding the
+// accumulators as a wavefront has them: entries 8 h .. 8 h + 7 of lane l in
+// unit h 64 + l.  So any block tiling can store or reload its fragments, each
 // access a contiguous 1 KB per wavefront.
-__device__ inline f32x4 *logits_frag(const GemmArgs &a, int64_t row0, int64_t col0)
+__device__ inline u32x4 *q_frag(const GemmArgs &a, int64_t row0, int64_t col0)
 {
-    return reinterpret_cast<f32x4 *>(a.zb) + ((row0 >> 5) * (a.Cp >> 5) + (col0 >> 5)) * 256 + (threadIdx.x & 63);
+    return reinterpret_cast<u32x4 *>(a.zb) + ((row0 >> 5) * (a.Cp >> 5) + (col0 >> 5)) * 128 + (threadIdx.x & 63);
 }
+__device__ inline uint32_t pack_f16(float lo, float hi)
+{
+    const _Float16 l = (_Float16)lo, h = (_Float16)hi;   // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+__device__ inline float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// q of the block tile's accumulators; s_M: each row's M, indexed by the row
+// in the tile.
 template <int WM, int WN>
-__device__ inline void store_logits(const GemmArgs &a, int64_t m0, int64_t n0, const f32x16 (&acc)[WM][WN])
+__device__ inline void store_q(const GemmArgs &a, int64_t m0, int64_t n0, const f32x16 (&acc)[WM][WN],
+                               const float *s_M)
 {
     const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
-    for (int mb = 0; mb < WM; ++mb)
+    for (int mb = 0; mb < WM; ++mb) {
+        float mr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 m4 = *(const float4 *)(s_M + tile_row<WM>(mb, 4 * g));   // 4 consecutive rows
+            mr[4 * g] = m4.x;
+            mr[4 * g + 1] = m4.y;
+            mr[4 * g + 2] = m4.z;
+            mr[4 * g + 3] = m4.w;
+        }
 #pragma unroll
         for (int nb = 0; nb < WN; ++nb) {
             const int64_t col0 = n0 + wn * WN * 32 + nb * 32;
             if (col0 >= a.Cp)
                 continue;   // past the padded candidates (wavefront-uniform)
-            f32x4 *zb = logits_frag(a, m0 + wm * WM * 32 + mb * 32, col0);
+            uint32_t v[8];
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                __builtin_nontemporal_store(
-                    f32x4{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]},
-                    zb + g * 64);
+            for (int e = 0; e < 8; ++e)
+                v[e] = pack_f16(__expf(acc[mb][nb][2 * e] - mr[2 * e]), __expf(acc[mb][nb][2 * e + 1] - mr[2 * e + 1]));
+            u32x4 *zb = q_frag(a, m0 + wm * WM * 32 + mb * 32, col0);
+            __builtin_nontemporal_store(u32x4{v[0], v[1], v[2], v[3]}, zb);
+            __builtin_nontemporal_store(u32x4{v[4], v[5], v[6], v[7]}, zb + 64);
         }
+    }
 }
 
-// dz from the stored logits, one 128 x 128 tile per block:
-// dz = g (exp(z - lse) - onehot) rounded to bf16, written row-major [Tq][Cp].
-// Logits that the last forward did not store for
-// this candidate set and T give zeros and SSM_FLAG_NO_LOGITS.
+// dz from what the forward stored, one 128 x 128 tile per block:
+// dz = g (q exp(M - lse) - onehot) rounded to bf16 (q exp(M - lse) is
+// exp(z - lse)), written row-major [Tq][Cp].  The tile's columns lie in at
+// most two column tiles of the forward (kFwdCols wide; a 32-column fragment
+// in one), whose M per row comes from part.  Values that the last forward
+// did not store for this candidate set and T give zeros and
+// SSM_FLAG_NO_LOGITS.
+constexpr int kFwdCols = 64 * kFwdWN;
+static_assert(kFwdCols % 32 == 0 && kFwdCols >= 128, "a fragment in one forward tile, a dz tile in two");
 __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
 {
-    __shared__ __align__(16) uint8_t smem[128 * kLdb * 2 + 3 * 128 * 4];
+    __shared__ __align__(16) uint8_t smem[128 * kLdb * 2 + 5 * 128 * 4];
     uint32_t mt, nt;
     // N-tiles fastest: consecutive blocks write neighbouring 256-byte pieces
     // of the same dz rows (measured faster than M-tiles fastest or grouped)
@@ -660,14 +692,14 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                const f32x4 *zb = logits_frag(a, m0 + wm * 64 + mb * 32, n0 + wn * 64 + nb * 32);
+                const u32x4 *zb = q_frag(a, m0 + wm * 64 + mb * 32, n0 + wn * 64 + nb * 32);
+                const u32x4 lo = __builtin_nontemporal_load(zb), hi = __builtin_nontemporal_load(zb + 64);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 v = __builtin_nontemporal_load(zb + g * 64);
-                    acc[mb][nb][4 * g] = v[0];
-                    acc[mb][nb][4 * g + 1] = v[1];
-                    acc[mb][nb][4 * g + 2] = v[2];
-                    acc[mb][nb][4 * g + 3] = v[3];
+                for (int e = 0; e < 4; ++e) {
+                    acc[mb][nb][2 * e] = f16_lo(lo[e]);
+                    acc[mb][nb][2 * e + 1] = f16_hi(lo[e]);
+                    acc[mb][nb][8 + 2 * e] = f16_lo(hi[e]);
+                    acc[mb][nb][8 + 2 * e + 1] = f16_hi(hi[e]);
                 }
             }
     }
@@ -675,15 +707,25 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
     if (!have && blockIdx.x == 0 && t == 0)
         atomicOr(&a.h->flags, SSM_FLAG_NO_LOGITS);
     uint16_t *bt = reinterpret_cast<uint16_t *>(smem);   // [128][kLdb] bf16
-    float *s_l = reinterpret_cast<float *>(smem + 128 * kLdb * 2);
-    float *s_g = s_l + 128;
+    float *s_f = reinterpret_cast<float *>(smem + 128 * kLdb * 2);   // [2][128]: exp(M - lse)
+    float *s_g = s_f + 2 * 128;
     int32_t *s_y = reinterpret_cast<int32_t *>(s_g + 128);
-    if (t < 128) {
-        const int64_t i = m0 + t;
+    const int64_t ft0 = n0 / kFwdCols;   // the first forward column tile of this tile
+    {
+        // thread t: row t % 128 of forward tile ft0 + t / 128 (the second
+        // only where the tile reaches into it)
+        const int r = t & 127, k = t >> 7;
+        const int64_t i = m0 + r;
         const bool ok = have && i < a.T && a.h->void_batch == 0;
-        s_l[t] = ok ? a.lse[i] : 0.f;
-        s_g[t] = ok ? a.g[i] : 0.f;
-        s_y[t] = ok ? a.slot[i] : -1;
+        const bool in = k == 0 || (ft0 + 1) * kFwdCols < n0 + 128;
+        float f = 0.f;
+        if (ok && in)
+            f = __expf(a.part[(ft0 + k) * a.T + i].x - a.lse[i]);
+        s_f[k * 128 + r] = f;
+        if (k == 0) {
+            s_g[r] = ok ? a.g[i] : 0.f;
+            s_y[r] = ok ? a.slot[i] : -1;
+        }
     }
     __syncthreads();
     // dz of the tile as bf16, packed in registers (a lane holds 4
@@ -695,21 +737,25 @@ __global__ __launch_bounds__(256) void dz_kernel(GemmArgs a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int r4 = tile_row<2>(mb, 4 * g);   // 4 consecutive rows, 16-byte aligned
-            const float4 l4 = *(const float4 *)(s_l + r4), g4 = *(const float4 *)(s_g + r4);
+            const float4 g4 = *(const float4 *)(s_g + r4);
             const int4 y4 = *(const int4 *)(s_y + r4);
-            const float lr[4] = {l4.x, l4.y, l4.z, l4.w}, gr[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float gr[4] = {g4.x, g4.y, g4.z, g4.w};
             const int yr[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 const int cc = tile_col<2>(nb);
                 const int c = (int)n0 + cc;        // candidates < 2^31
                 const bool col_ok = c < a.C;
+                // the fragment's forward tile (wavefront-uniform)
+                const int k = (int)((n0 + (cc & ~31)) / kFwdCols - ft0);
+                const float4 f4 = *(const float4 *)(s_f + k * 128 + r4);
+                const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
                 uint16_t h[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     // padding rows and columns, and a void batch, give 0
                     // (masked, not branched around: no divergence)
-                    const float p = __expf(acc[mb][nb][4 * g + j] - lr[j]);
+                    const float p = acc[mb][nb][4 * g + j] * fr[j];
                     const float dv = gr[j] * (p - (yr[j] == c ? 1.f : 0.f));
                     const uint32_t keep = col_ok && gr[j] != 0.f ? 0xffffffffu : 0u;
                     const float d = __uint_as_float(__float_as_uint(dv) & keep);
@@ -753,7 +799,7 @@ template <int EPI, int WM, int WN, int BK, int NS>
 constexpr uint32_t smem_bytes()
 {
     constexpr uint32_t main = WideTile<WM, WN, BK, NS>::SMEM;
-    return EPI == EPI_FWD ? cmax(main, 64 * WN * kLdt * 4 + 4 * 64 * 8) : main;
+    return EPI == EPI_FWD ? cmax(main, 64 * WN * kLdt * 4 + 4 * 64 * 8 + 64 * WM * 4) : main;
 }
 
 // One contraction C[m][n] = sum_k A[m][k] B[n][k] per block tile (the
@@ -790,10 +836,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int t = threadIdx.x;
 
     if constexpr (EPI == EPI_FWD) {
-        // the tile's fp32 logits for the dz kernel, fragment by fragment (each
-        // store: 64 lanes x 16 bytes, contiguous; non-temporal: 4 T C bytes
-        // would otherwise push the operands out of the caches)
-        store_logits<WM, WN>(a, m0, n0, acc);
         // two halves of 64 rows.  The half's two wavefronts store their
         // accumulators to LDS column-major (a lane's 4 consecutive rows of
         // one column are one 16-byte store); wavefront q then folds columns
@@ -802,6 +844,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         constexpr int CW = BN / 4;
         float *tile = reinterpret_cast<float *>(smem);                      // [BN][kLdt]
         float2 *pq = reinterpret_cast<float2 *>(smem + BN * kLdt * 4);      // [4][64]
+        float *s_M = reinterpret_cast<float *>(pq + 4 * 64);                // [BM]: each row's M
         const int w = t >> 6, r = t & 63, q = w, wm = w >> 1;
         const int64_t c0 = n0 + CW * q;
         const int64_t left = (int64_t)a.C - c0;
@@ -846,22 +889,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             }
             pq[q * 64 + r] = make_float2(m, s);
             __syncthreads();
-            if (q == 0 && i < a.T) {
+            if (q == 0) {
                 float M = -INFINITY;
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     M = fmaxf(M, pq[k * 64 + r].x);
-                float S = 0.f;
+                s_M[64 * h + r] = M;
+                if (i < a.T) {
+                    float S = 0.f;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float2 o = pq[k * 64 + r];
-                    if (o.y > 0.f)
-                        S += o.y * __expf(o.x - M);
+                    for (int k = 0; k < 4; ++k) {
+                        const float2 o = pq[k * 64 + r];
+                        if (o.y > 0.f)
+                            S += o.y * __expf(o.x - M);
+                    }
+                    a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
                 }
-                a.part[(int64_t)nt * a.T + i] = make_float2(M, S);
             }
             __syncthreads();
         }
+        // q = exp(z - M) for the dz kernel, fragment by fragment (each store:
+        // 64 lanes x 16 bytes, contiguous; non-temporal: 2 T C bytes would
+        // otherwise push the operands out of the caches)
+        store_q<WM, WN>(a, m0, n0, acc, s_M);
     } else if constexpr (EPI == EPI_DX) {
 #pragma unroll
         for (int mb = 0; mb < WM; ++mb)
@@ -1184,7 +1234,7 @@ int ssm_loss_fwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.cand = cand;
     a.zt = reinterpret_cast<float *>(w + L.zt);
     a.part = reinterpret_cast<float2 *>(w + L.part);
-    a.zb = reinterpret_cast<float *>(w + L.zb);
+    a.zb = reinterpret_cast<uint16_t *>(w + L.zb);
     a.Tq = Tq;
     a.Cp = L.Cp;
     a.h = h;
@@ -1237,7 +1287,8 @@ int ssm_loss_bwd(const ssm_config *cfg, void *ws, const void *X, const void *W, 
     a.lse = lse;
     a.g = dloss;
     a.dz = dz;
-    a.zb = reinterpret_cast<float *>(w + L.zb);
+    a.zb = reinterpret_cast<uint16_t *>(w + L.zb);
+    a.part = reinterpret_cast<float2 *>(w + L.part);
     a.Tq = Tq;
     a.Cp = Cp;
     a.h = h;

@@ -10,8 +10,14 @@ arithmetic of the HIP path and written out below:
 * lse: the largest logit error, plus the fp32 sums of exp over the tile and
   over the tiles (at most 66 + C/128 roundings of a positive sum) and the
   exp/log evaluations: (C/128 + 128) 2^-23 + 2^-22 |lse|;
-* dz = g (exp(z - lse) - onehot) is rounded to bf16 (2^-8 relative: an 8-bit significand) after an
-  fp32 evaluation whose error is g p (logit error + lse error + 2^-19);
+* between the forward and the backward each logit is kept as q = exp(z - M) in
+  fp16, M its row's maximum over the forward's column tile: q lies in (0, 1],
+  so the rounding is within 2^-11 relative (2^-25 absolute below 2^-14);
+* dz = g (q exp(M - lse) - onehot) is rounded to bf16 (2^-8 relative: an
+  8-bit significand) after an fp32 evaluation whose error is
+  g p (logit error + lse error + 2^-18 + 2^-11) + g 2^-25 (two fast exps of
+  arguments whose size matters only while p is not negligible, one product,
+  and q's rounding);
 * dX = dz W_S and dW = dz^T X: exact products of bf16 values summed in fp32
   over K = C (or T) padded to 128, so each entry is off by at most
   sum |d(dz)| |w| + K u sum |dz w|, with d(dz) the bound above.
@@ -75,7 +81,8 @@ def _dz_bound(X, W, cand, slot, g, lse_tol):
     _, lse = orc.loss_fwd(X, W, cand, slot)
     p = np.exp(z - lse[:, None])
     g = np.asarray(g, np.float64)[:, None]
-    e1 = np.abs(g) * p * (zerr + lse_tol[:, None] + 2.0 ** -19) + np.abs(g) * U   # fp32 evaluation
+    e1 = (np.abs(g) * p * (zerr + lse_tol[:, None] + 2.0 ** -18 + 2.0 ** -11)   # fp32 evaluation, fp16 q
+          + np.abs(g) * (U + 2.0 ** -25))
     return dz, e1 + 2.0 ** -8 * (np.abs(dz) + e1)                                  # then bf16 rounding
 
 

@@ -50,8 +50,8 @@ def test_config_rejects(S, field, value):
 def test_workspace_bytes_scale(S):
     small = S.workspace_bytes(S.config(50304, 1024, 1024))
     big = S.workspace_bytes(S.config(50304, 10240, 49152))
-    # the forward's fp32 logits and dz in bf16 dominate: 6 T C bytes
-    assert 6 * 49152 * 10240 < big < 6 * 49152 * 10240 * 1.1
+    # the forward's fp16 exp(z - M) and dz in bf16 dominate: 4 T C bytes
+    assert 4 * 49152 * 10240 < big < 4 * 49152 * 10240 * 1.15
     assert small < big
     assert S.workspace_bytes(S.config(50304, 10240, 49153)) > big   # T padded to 128
 
