@@ -28,7 +28,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kChunk = 64;
 constexpr int kGroup = 64;
-constexpr int kFixThreads = 1024;
+constexpr int kFixThreads = 512;
 constexpr uint32_t kNewHead = 0xFFFFFFFEu;
 constexpr uint32_t kNotSingle = 0xFFFFFFFFu;
 constexpr uint32_t kMultiKey = 0x40000000u;
