@@ -430,6 +430,37 @@ __device__ __forceinline__ int block_incl_max(int v, int *s_wave, int *excl)
     return max(before, v);
 }
 
+// A thread's kSortItems consecutive entries i0 .. i0 + kSortItems - 1 of p
+// (those below n; 0 past it): two 16-byte loads when all are below n and
+// p + i0 is 16-byte aligned (i0 is a multiple of kSortItems; a channel's
+// arrays start at c nk, which need not be), else one load each.
+__device__ __forceinline__ void load_items(const uint32_t *p, uint32_t i0, uint32_t n, uint32_t (&v)[kSortItems])
+{
+    static_assert(kSortItems == 8, "two 16-byte pieces");
+    if (i0 + kSortItems <= n && ((uintptr_t)(p + i0) & 15u) == 0) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(p + i0), y = *reinterpret_cast<const uint4 *>(p + i0 + 4);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            v[j] = i0 + j < n ? p[i0 + j] : 0u;
+    }
+}
+// The matching stores of the entries below n.
+__device__ __forceinline__ void store_items(uint32_t *p, uint32_t i0, uint32_t n, const uint32_t (&v)[kSortItems])
+{
+    if (i0 + kSortItems <= n && ((uintptr_t)(p + i0) & 15u) == 0) {
+        *reinterpret_cast<uint4 *>(p + i0) = make_uint4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<uint4 *>(p + i0 + 4) = make_uint4(v[4], v[5], v[6], v[7]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            if (i0 + j < n)
+                p[i0 + j] = v[j];
+    }
+}
+
 // Thread-contiguous items: thread t of tile b owns keys b*2048 + t*8 + [0, 8).
 // For the trigram channel it also counts, per tile, the keys the singleton
 // split keeps (split_kernel's layout).
@@ -460,15 +491,20 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
     const bool nest = a.nested && c == 1;
     uint32_t cnt = 0, kept = 0;
     uint32_t headm = 0, knownm = 0, endm = 0;    // per item bits
+    // the rows of the thread's items, and of the keys just before and after
+    uint32_t rq[kSortItems];
+    load_items(R, i0, n, rq);
+    const uint32_t r_before = i0 > 0 && i0 < n ? R[i0 - 1] : 0u;
+    const uint32_t r_after = i0 + kSortItems < n ? R[i0 + kSortItems] : 0u;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
         if (i < n) {
-            const uint32_t r = R[i];
-            const bool end = i + 1 == n || R[i + 1] != r;
+            const uint32_t r = rq[j];
+            const bool end = i + 1 == n || (j + 1 < kSortItems ? rq[j + 1] : r_after) != r;
             endm |= end ? 1u << j : 0u;
             bool single = false;
-            if (i == 0 || R[i - 1] != r) {
+            if (i == 0 || (j > 0 ? rq[j - 1] : r_before) != r) {
                 bool known = false;
                 uint32_t slot = 0;
                 if (!empty) {
@@ -502,18 +538,14 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
         for (int j = threadIdx.x; j < kSortTile; j += kSortThreads)
             s_fail[j] = 0;
         __syncthreads();
-        // the bigram row of every key of a segment with more than one key
-        // (and of the key before this thread's first item, if that item
-        // continues a segment), loaded together
+        // the payloads and bigram rows of the thread's items (the rows are
+        // compared only between keys of one segment of several keys), and
+        // the bigram row of the key before the first item if that item
+        // continues a segment
         uint32_t vq[kSortItems], bq[kSortItems];
         uint32_t b_prev = 0;
-#pragma unroll
-        for (int j = 0; j < kSortItems; ++j) {
-            const uint32_t i = i0 + j;
-            vq[j] = i < n ? V[i] : 0u;
-            const bool multi = i < n && ((headm & endm) & (1u << j)) == 0;
-            bq[j] = multi ? a.btro[i] : 0u;
-        }
+        load_items(V, i0, n, vq);
+        load_items(a.btro, i0, n, bq);
         if (i0 < n && !(headm & 1u) && carry >= 0)
             b_prev = a.btro[i0 - 1];
         int hl[kSortItems];
@@ -534,24 +566,33 @@ __global__ __launch_bounds__(kSortThreads) void mark_kernel(SlotArgs a)
             }
             if (j == kSortItems - 1 || i + 1 == n) {
                 // a segment running past the tile is not decided here
-                if (i + 1 < n && i + 1 == tile0 + kSortTile && R[i + 1] == R[i])
+                if (i + 1 < n && i + 1 == tile0 + kSortTile && r_after == rq[j])
                     s_fail[run] = 1;
             }
         }
         __syncthreads();
         kept = 0;
+        uint32_t rec[kSortItems];
+        uint32_t keep[2] = {0u, 0u};   // the kept flags, a byte per item
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t i = i0 + j;
-            if (i >= n)
-                continue;
-            const bool nested = hl[j] >= 0 && !s_fail[hl[j]];
+            const bool nested = i < n && hl[j] >= 0 && !s_fail[hl[j]];
             const uint32_t v = vq[j];
             const bool hd = (headm & (1u << j)) != 0, ed = (endm & (1u << j)) != 0;
             const uint32_t run_bits = (hd && ed) ? 0u : (kMultiKey | (hd ? kRunHead : 0u) | (ed ? kRunTail : 0u));
-            a.tinfo[i] = nested ? (R[i] | (v & 0x80000000u) | run_bits) : kNotSingle;
-            a.tkept[i] = nested ? 0 : 1;
-            kept += nested ? 0u : 1u;
+            rec[j] = nested ? (rq[j] | (v & 0x80000000u) | run_bits) : kNotSingle;
+            keep[j >> 2] |= nested ? 0u : 1u << (8 * (j & 3));
+            kept += i < n && !nested ? 1u : 0u;
+        }
+        store_items(a.tinfo, i0, n, rec);
+        if (i0 + kSortItems <= n) {   // i0 is a multiple of 8 and tkept 256-byte aligned
+            *reinterpret_cast<uint2 *>(a.tkept + i0) = make_uint2(keep[0], keep[1]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j)
+                if (i0 + j < n)
+                    a.tkept[i0 + j] = (uint8_t)((keep[j >> 2] >> (8 * (j & 3))) & 1u);
         }
     }
     if (c == 1) {
@@ -597,18 +638,47 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
     const uint32_t *V = a.vals + (size_t)c * a.nk;
     const uint32_t *info = a.seg_info + (size_t)c * a.nk;
     uint32_t keep = 0, cnt = 0;
+    uint32_t rq[kSortItems], vq[kSortItems];   // rows and payloads of the items
+    if (a.nested) {
+        // the map records and the kept flags (a byte per key) were written
+        // by mark_kernel
+        uint32_t k8[2] = {0u, 0u};
+        if (i0 + kSortItems <= n) {   // i0 is a multiple of 8 and tkept 256-byte aligned
+            const uint2 t = *reinterpret_cast<const uint2 *>(a.tkept + i0);
+            k8[0] = t.x;
+            k8[1] = t.y;
+        } else {
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const uint32_t i = i0 + j;
-        if (i < n) {
-            bool kp;
-            if (a.nested) {
-                kp = a.tkept[i] != 0;   // the map records were written by mark_kernel
-            } else {
-                const uint32_t r = R[i];
-                const uint32_t v = V[i];
+            for (int j = 0; j < kSortItems; ++j)
+                if (i0 + j < n)
+                    k8[j >> 2] |= (uint32_t)a.tkept[i0 + j] << (8 * (j & 3));
+        }
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            if ((k8[j >> 2] >> (8 * (j & 3))) & 0xFFu) {
+                keep |= 1u << j;
+                ++cnt;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            rq[j] = 0u;
+            vq[j] = 0u;
+        }
+    } else {
+        load_items(R, i0, n, rq);
+        load_items(V, i0, n, vq);
+        const uint32_t r_before = i0 > 0 && i0 < n ? R[i0 - 1] : 0u;
+        const uint32_t r_after = i0 + kSortItems < n ? R[i0 + kSortItems] : 0u;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t i = i0 + j;
+            if (i < n) {
+                const uint32_t r = rq[j];
+                const uint32_t v = vq[j];
                 uint32_t rec = kNotSingle;
-                if ((i == 0 || R[i - 1] != r) && (i + 1 == n || R[i + 1] != r)) {
+                if ((i == 0 || (j > 0 ? rq[j - 1] : r_before) != r) &&
+                    (i + 1 == n || (j + 1 < kSortItems ? rq[j + 1] : r_after) != r)) {
                     const uint32_t in = info[i];
                     if (a.fused) {
                         if (in == kNewHead)
@@ -618,11 +688,10 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
                     }
                 }
                 a.tinfo[v & 0x7FFFFFFFu] = rec;
-                kp = rec == kNotSingle;
-            }
-            if (kp) {
-                keep |= 1u << j;
-                ++cnt;
+                if (rec == kNotSingle) {
+                    keep |= 1u << j;
+                    ++cnt;
+                }
             }
         }
     }
@@ -631,8 +700,8 @@ __global__ __launch_bounds__(kSortThreads) void split_kernel(SlotArgs a)
     for (int j = 0; j < kSortItems; ++j) {
         if (keep & (1u << j)) {
             const uint32_t i = i0 + j;
-            a.split_rows[o] = R[i];
-            a.split_vals[o] = V[i];
+            a.split_rows[o] = a.nested ? R[i] : rq[j];
+            a.split_vals[o] = a.nested ? V[i] : vq[j];
             a.split_info[o] = info[i];
             ++o;
         }
