@@ -739,11 +739,15 @@ __global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
     const uint32_t i0 = b * kSortTile + tid * kSortItems;
     const uint32_t *R = a.rows + (size_t)c * a.nk;
     uint32_t *info = a.seg_info + (size_t)c * a.nk;
+    uint32_t rq[kSortItems], iq[kSortItems];   // rows and head info of the items
+    load_items(R, i0, n, rq);
+    load_items(info, i0, n, iq);
+    const uint32_t r_before = i0 > 0 && i0 < n ? R[i0 - 1] : 0u;
     uint32_t mask = 0, cnt = 0;
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t i = i0 + j;
-        if (i < n && (i == 0 || R[i - 1] != R[i]) && info[i] == kNewHead) {
+        if (i < n && (i == 0 || (j > 0 ? rq[j - 1] : r_before) != rq[j]) && iq[j] == kNewHead) {
             mask |= 1u << j;
             ++cnt;
         }
@@ -754,18 +758,19 @@ __global__ __launch_bounds__(kSortThreads) void assign_kernel(SlotArgs a)
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         if (mask & (1u << j)) {
-            const uint32_t i = i0 + j;
-            const uint32_t r = R[i];
+            const uint32_t r = rq[j];
             if (slot < a.wrows) {
                 sm[r] = SlotEntry{epoch, slot};
                 a.slot_rows[c][slot] = r;
-                info[i] = slot | 0x80000000u;
+                iq[j] = slot | 0x80000000u;
             } else {
-                info[i] = kDropped;   // window full: row dropped (flagged)
+                iq[j] = kDropped;   // window full: row dropped (flagged)
             }
             ++slot;
         }
     }
+    if (mask)   // the thread's items again, the new heads' info changed
+        store_items(info, i0, n, iq);
 }
 
 // ------------------------------------------------------ segment reduction
