@@ -1545,7 +1545,7 @@ __global__ __launch_bounds__(kFixThreads) void fixup_kernel(RedArgs a)
         // m = following chunks that start inside the segment (rows are
         // sorted, so they are consecutive): every wavefront probes the next
         // 64 chunk heads; a segment longer than that is scanned by the whole
-        // block, 1024 heads at a time
+        // block, kFixThreads heads at a time
         int64_t m = 0;
         {
             const int64_t cc = chunk + 1 + lane;
